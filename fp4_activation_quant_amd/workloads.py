@@ -1,0 +1,149 @@
+"""Seeded synthetic workloads for the fused add + Gemma RMSNorm + quant op.
+
+This module only draws inputs: it holds none of the op's arithmetic.  Tests,
+the benchmark and the smoke check all take their inputs from here, so every
+side sees the same tensors.  The per-workload quant scales depend on the
+op's output (amax of the normed activation); they are not computed here but
+read from ``tests/golden/workload_scales.json``, which a committed script
+writes from the CPU oracle.
+
+Recipe (all draws are fp32 on the CPU from ``torch.Generator().manual_seed``,
+scaled, then rounded to the activation dtype):
+
+* seeds: ``seed_base + stream``; stream 0 = x, 1 = residual, 2 = weight,
+  3 = outlier mask; the calibration draw of the decode sweep uses streams
+  10, 11 and 13 for x, residual and mask (same weight).
+* ``N(0, s)`` takes s as the standard deviation.
+* element outliers: elements with ``rand < p`` are multiplied by f before
+  rounding (x only); row outliers: rows with ``rand < p`` are multiplied by f
+  in both x and residual (row M//2 if the draw picks none).
+"""
+
+from dataclasses import dataclass, field
+import json
+import os
+
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SCALES_JSON = os.path.join(ROOT, "tests", "golden", "workload_scales.json")
+
+DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    H: int
+    dtype: str            # "bf16" | "fp16"
+    nvfp4: bool
+    has_residual: bool
+    write_y: bool
+    eps: float
+    x_std: float
+    r_std: float
+    w_dist: tuple         # ("normal", std) | ("uniform", lo, hi)
+    seed_base: int
+    scale_rule: str       # "fixed" | "fp8_amax" | "fp8_amax_calibration" | "nvfp4_amax"
+    fixed_scale: float = 0.0
+    elem_outliers: tuple = ()   # (p, factor) on x elements
+    row_outliers: tuple = ()    # (p, factor) on rows of x and residual
+    draw_M: int = 0             # rows drawn (>= M); 0 means M
+    tags: tuple = field(default=())
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+    @property
+    def rows_drawn(self):
+        return self.draw_M or self.M
+
+
+def _wl(**kw):
+    return Workload(**kw)
+
+
+_DECODE = dict(H=4096, dtype="bf16", nvfp4=False, has_residual=True, write_y=False, eps=1e-6,
+               x_std=1.0, r_std=2.0, w_dist=("normal", 0.1), seed_base=2000,
+               scale_rule="fp8_amax_calibration", elem_outliers=(0.01, 20.0), draw_M=256)
+_WIDE = dict(M=4096, H=5120, dtype="fp16", write_y=False, eps=1e-5, x_std=0.5, r_std=4.0,
+             w_dist=("uniform", -0.5, 0.5), seed_base=4000, row_outliers=(0.001, 100.0))
+
+WORKLOADS = {w.name: w for w in [
+    _wl(name="fp8_m16_h2048_bf16_y", M=16, H=2048, dtype="bf16", nvfp4=False, has_residual=True,
+        write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1), seed_base=1000,
+        scale_rule="fixed", fixed_scale=0.05),
+    *[_wl(name=f"fp8_decode_m{m}_h4096_bf16", M=m, **_DECODE) for m in (1, 8, 64, 256)],
+    _wl(name="nvfp4_prefill_m8192_h4096_bf16_y", M=8192, H=4096, dtype="bf16", nvfp4=True,
+        has_residual=True, write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1),
+        seed_base=3000, scale_rule="nvfp4_amax"),
+    _wl(name="fp8_res_m4096_h5120_fp16", nvfp4=False, has_residual=True, scale_rule="fp8_amax", **_WIDE),
+    _wl(name="fp8_nores_m4096_h5120_fp16", nvfp4=False, has_residual=False, scale_rule="fp8_amax", **_WIDE),
+    _wl(name="nvfp4_res_m4096_h5120_fp16", nvfp4=True, has_residual=True, scale_rule="nvfp4_amax", **_WIDE),
+    _wl(name="nvfp4_nores_m4096_h5120_fp16", nvfp4=True, has_residual=False, scale_rule="nvfp4_amax", **_WIDE),
+    _wl(name="nvfp4_m32768_h8192_bf16_y", M=32768, H=8192, dtype="bf16", nvfp4=True,
+        has_residual=True, write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1),
+        seed_base=5000, scale_rule="nvfp4_amax"),
+]}
+
+# The workload bench.py times by default: the largest one, bandwidth-bound.
+DEFAULT_BENCH = "nvfp4_m32768_h8192_bf16_y"
+
+
+def _gen(seed):
+    return torch.Generator().manual_seed(seed)
+
+
+def _draw(wl: Workload, rows: int, x_stream: int, r_stream: int, mask_stream: int):
+    H, dt = wl.H, wl.torch_dtype
+    x = torch.randn(rows, H, generator=_gen(wl.seed_base + x_stream)) * wl.x_std
+    r = torch.randn(rows, H, generator=_gen(wl.seed_base + r_stream)) * wl.r_std if wl.has_residual else None
+    if wl.elem_outliers:
+        p, f = wl.elem_outliers
+        mask = torch.rand(rows, H, generator=_gen(wl.seed_base + mask_stream)) < p
+        x = torch.where(mask, x * f, x)
+    if wl.row_outliers:
+        p, f = wl.row_outliers
+        rmask = torch.rand(rows, generator=_gen(wl.seed_base + mask_stream)) < p
+        if not bool(rmask.any()):
+            rmask[rows // 2] = True
+        x = torch.where(rmask[:, None], x * f, x)
+        if r is not None:
+            r = torch.where(rmask[:, None], r * f, r)
+    return x.to(dt), (r.to(dt) if r is not None else None)
+
+
+def make_weight(wl: Workload) -> torch.Tensor:
+    g = _gen(wl.seed_base + 2)
+    if wl.w_dist[0] == "normal":
+        w = torch.randn(wl.H, generator=g) * wl.w_dist[1]
+    else:
+        lo, hi = wl.w_dist[1], wl.w_dist[2]
+        w = torch.rand(wl.H, generator=g) * (hi - lo) + lo
+    return w.to(wl.torch_dtype)
+
+
+def make_inputs(wl: Workload):
+    """(x, residual or None, weight) as CPU tensors of the workload's dtype."""
+    x, r = _draw(wl, wl.rows_drawn, 0, 1, 3)
+    if wl.rows_drawn != wl.M:
+        x = x[: wl.M].contiguous()
+        r = r[: wl.M].contiguous() if r is not None else None
+    return x, r, make_weight(wl)
+
+
+def make_calibration_inputs(wl: Workload):
+    """The separate calibration draw of the decode sweep (same weight)."""
+    x, r = _draw(wl, wl.rows_drawn, 10, 11, 13)
+    return x, r, make_weight(wl)
+
+
+def load_scale(wl: Workload) -> float:
+    """The workload's fp32 quant scale: fixed, or read from the stored table."""
+    if wl.scale_rule == "fixed":
+        return float(torch.tensor(wl.fixed_scale, dtype=torch.float32))
+    with open(SCALES_JSON) as f:
+        table = json.load(f)
+    return float.fromhex(table[wl.name]["scale_hex"])

@@ -1,0 +1,232 @@
+"""The op as the unfused chain: add, Gemma RMSNorm, then a standalone quant.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Source: the ``fused_norm_quant`` page, ``gemma_add_rms_norm_quant`` (parameter
+list, returns, and the wrapper's assertions and output allocation), and the
+module docstring there: the fused kernel replaces the Gemma add-RMSNorm
+followed by a standalone static-FP8 or NVFP4 quant, computing the codes from
+the normed activation rounded to the activation dtype with the same scale
+arithmetic, so that the codes equal the unfused chain's.  The
+``fused_allreduce_norm_quant`` page (``fused_allreduce_gemma_rms_norm_quant``)
+states the same op behind an all-reduce, with fp32 accumulation
+(``fp32_acc=True``) and Gemma weight bias 1.
+
+All arrays of activation-dtype values are carried as their 16-bit patterns
+(uint16) with a ``Format`` (BF16 or FP16) saying which.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes):
+  * the norm reads the rounded sum h (the value written back to residual);
+  * eps is added to the mean square inside the square root;
+  * weight has x's dtype and the scale factor is (1 + w);
+  * y = RN_D(h * rstd * (1 + w)), evaluated here in fp64;
+  * FP8: q = E4M3FN_RNE(clamp(fl32(y / s), -448, 448));
+  * NVFP4 per 16-element block, all in fp32:
+        a = max|y|;  t = a / 6;  u = gs * t;  S = E4M3FN_RNE(min(u, 448));
+        o = gs / decode(S)  (0 when S decodes to 0);
+        c = E2M1_RNE(clamp(y * o, -6, 6));  byte = c[2k] | c[2k+1] << 4;
+  * scale bytes are stored at swizzle_128x4_offset(m, b); rows >= M of the
+    padded buffer are never written.
+"""
+
+import numpy as np
+
+from .formats import BF16, FP16, E4M3FN, E2M1, Format, bits_to_f64, f64_to_bits, encode, decode
+
+__all__ = [
+    "add_residual", "gemma_rms_norm", "quant_fp8_static", "quant_nvfp4",
+    "swizzle_128x4_offset", "block_scale_buffer_shape", "scatter_block_scales",
+    "gemma_add_rms_norm_quant",
+]
+
+NVFP4_BLOCK = 16      # elements per block scale ("16-element blocks")
+E2M1_MAX = 6.0
+E4M3_MAX = 448.0
+
+
+def _check_fmt(fmt: Format):
+    if fmt not in (BF16, FP16):
+        raise ValueError("activation dtype must be bf16 or fp16")
+
+
+def add_residual(x_bits, r_bits, fmt: Format) -> np.ndarray:
+    """h = RN_D(x + r): the residual after its in-place update.
+
+    ``residual``: "Updated in place to x + residual" (``fused_norm_quant``
+    page, parameter list).  The sum is taken in float64; when it is not exact
+    there, rounding twice (to float64, then to D) still gives the correctly
+    rounded sum because 53 >= 2p + 2 for p = 8 (bf16) and p = 11 (fp16).
+    """
+    _check_fmt(fmt)
+    x = bits_to_f64(x_bits, fmt)
+    r = bits_to_f64(r_bits, fmt)
+    return f64_to_bits(x + r, fmt)
+
+
+def gemma_rms_norm(h_bits, w_bits, eps: float, fmt: Format) -> np.ndarray:
+    """y = RN_D(h / sqrt(mean(h^2) + eps) * (1 + w)), one rounding, fp64.
+
+    ``weight``: the norm scales by (1 + weight) (``fused_norm_quant`` page,
+    parameter list; ``weight_bias=1.0 # GemmaRMSNorm-style`` on the
+    ``fused_allreduce_gemma_rms_norm`` page).  eps is the RMS-norm epsilon,
+    which the kernel receives as an fp32 scalar, so it is first rounded to
+    fp32 here.  Row-wise: ``h`` is (M, H), ``w`` is (H,).
+    """
+    _check_fmt(fmt)
+    h = bits_to_f64(h_bits, fmt)
+    w = bits_to_f64(w_bits, fmt)
+    if h.ndim != 2 or w.shape != (h.shape[1],):
+        raise ValueError("h must be (M, H) and w (H,)")
+    H = h.shape[1]
+    eps64 = float(np.float32(eps))
+    mean_sq = np.sum(h * h, axis=1) / H
+    rstd = 1.0 / np.sqrt(mean_sq + eps64)
+    y = (h * rstd[:, None]) * (1.0 + w)[None, :]
+    return f64_to_bits(y, fmt)
+
+
+def quant_fp8_static(y_bits, fmt: Format, scale: float) -> np.ndarray:
+    """Static per-tensor FP8: q = E4M3FN_RNE(clamp(fl32(y / scale), +-448)).
+
+    ``scale``: "FP8: the static per-tensor input scale" (``fused_norm_quant``
+    page, parameter list); the division by the scale is the reading of
+    "the same scale arithmetic as" the standalone static FP8 quant.  Values
+    beyond the E4M3FN range saturate to +-448.  Returns uint8 codes, same
+    shape as ``y_bits``.
+    """
+    _check_fmt(fmt)
+    y = bits_to_f64(y_bits, fmt).astype(np.float32)        # exact
+    s = np.float32(scale)
+    with np.errstate(over="ignore"):
+        v = y / s                                          # IEEE fp32 divide
+    v = np.minimum(np.maximum(v, np.float32(-E4M3_MAX)), np.float32(E4M3_MAX))
+    return encode(v.astype(np.float64), E4M3FN)
+
+
+def quant_nvfp4(y_bits, fmt: Format, global_scale: float):
+    """NVFP4: E2M1 codes with one E4M3FN scale per 16-element block.
+
+    ``scale``: "NVFP4: the global scale (input_global_scale_inv)"
+    (``fused_norm_quant`` page, parameter list; "NVFP4 global scale inverse"
+    on the ``fused_allreduce_norm_quant`` page) -- read as the multiplier gs
+    that maps a block's decode scale amax/6 into the E4M3 range.  E2M1
+    conversion is round-to-nearest-even with saturation
+    (``cvt.rn.satfinite.e2m1x2.f32`` in ``_cvt_e2m1x2``), and each byte holds
+    the even-index (lo) element in its low nibble ("lo in the low nibble").
+
+    Returns ``(q, S)``: q is (M, H/2) uint8 packed codes; S is the (M, H/16)
+    uint8 block-scale codes in row-major order (not yet swizzled).
+    """
+    _check_fmt(fmt)
+    y = bits_to_f64(y_bits, fmt).astype(np.float32)
+    M, H = y.shape
+    if H % NVFP4_BLOCK:
+        raise ValueError("H must be a multiple of 16")
+    gs = np.float32(global_scale)
+    blk = y.reshape(M, H // NVFP4_BLOCK, NVFP4_BLOCK)
+    a = np.max(np.abs(blk), axis=2)                                # exact
+    t = a / np.float32(E2M1_MAX)                                   # fp32
+    with np.errstate(over="ignore"):
+        u = gs * t                                                 # fp32
+    u = np.minimum(u, np.float32(E4M3_MAX))
+    S = encode(u.astype(np.float64), E4M3FN)
+    sigma = decode(S, E4M3FN).astype(np.float32)
+    o = np.zeros_like(sigma)
+    nz = sigma != 0
+    o[nz] = gs / sigma[nz]                                         # fp32
+    with np.errstate(over="ignore", invalid="ignore"):
+        v = blk * o[:, :, None]                                    # fp32
+    v = np.minimum(np.maximum(v, np.float32(-E2M1_MAX)), np.float32(E2M1_MAX))
+    c = encode(v.astype(np.float64), E2M1).astype(np.uint8).reshape(M, H)
+    q = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    return q, S.astype(np.uint8)
+
+
+def _round_up(a: int, b: int) -> int:
+    return (a + b - 1) // b * b
+
+
+def block_scale_buffer_shape(M: int, H: int):
+    """(round_up(M, 128), round_up(H / 16, 4)) bytes, as the wrapper allocates
+    it (``fused_norm_quant`` page, ``gemma_add_rms_norm_quant`` returns and
+    allocation)."""
+    return (_round_up(M, 128), _round_up(H // NVFP4_BLOCK, 4))
+
+
+def swizzle_128x4_offset(m, b, H: int):
+    """Byte offset of block scale (row m, block b) in the 128x4-tiled layout.
+
+    The pages name the layout ("swizzled 128x4 block scales", ``SWIZZLED_128x4``)
+    without spelling it out; this is the 128x4 tiling used for block-scaled
+    FP4 GEMM scale operands: 128-row x 4-block tiles of 512 contiguous bytes,
+    tiles in row-major order over (m // 128, b // 4), and inside a tile the
+    byte for (m, b) at (m % 32) * 16 + ((m % 128) // 32) * 4 + b % 4.
+    """
+    kp = _round_up(H // NVFP4_BLOCK, 4)
+    m = np.asarray(m, dtype=np.int64)
+    b = np.asarray(b, dtype=np.int64)
+    tile = (m // 128) * (kp // 4) + b // 4
+    return tile * 512 + (m % 32) * 16 + ((m % 128) // 32) * 4 + (b % 4)
+
+
+def scatter_block_scales(S, M: int, H: int, out: np.ndarray) -> np.ndarray:
+    """Write row-major scales S (M, H/16) into ``out`` (flat uint8 buffer of
+    prod(block_scale_buffer_shape) bytes) at their swizzled offsets.  Bytes
+    of rows >= M are left as they were ("rows >= M are left unwritten")."""
+    rows, cols = block_scale_buffer_shape(M, H)
+    if out.size != rows * cols:
+        raise ValueError("wrong block-scale buffer size")
+    nb = H // NVFP4_BLOCK
+    mm, bb = np.meshgrid(np.arange(M), np.arange(nb), indexing="ij")
+    out.reshape(-1)[swizzle_128x4_offset(mm, bb, H).reshape(-1)] = np.asarray(S, np.uint8).reshape(-1)
+    return out
+
+
+def gemma_add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale,
+                             nvfp4: bool, write_y: bool = False, fmt: Format = BF16,
+                             block_scale_fill: int = 0xA5):
+    """The whole op, as the unfused chain.
+
+    Arguments follow ``gemma_add_rms_norm_quant`` on the ``fused_norm_quant``
+    page, with x, residual (or None) and weight as 16-bit patterns of
+    ``fmt`` and ``scale`` a Python float (fp32 value).  Returns a dict:
+
+      residual : (M, H) uint16, x + residual (None when residual is None)
+      q        : FP8 (M, H) uint8 codes, or NVFP4 (M, H/2) uint8 packed codes
+      scales   : NVFP4 (M, H/16) row-major block-scale codes, else None
+      block_scale : NVFP4 swizzled buffer (flat uint8, unwritten bytes hold
+                 ``block_scale_fill``), else the scale value itself
+      y        : (M, H) uint16 normed activation (always computed; the op
+                 returns it only when write_y)
+    """
+    _check_fmt(fmt)
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    if x_bits.ndim != 2:
+        raise ValueError("x must be 2-D")
+    M, H = x_bits.shape
+    if residual_bits is not None:
+        h = add_residual(x_bits, residual_bits, fmt)
+    else:
+        h = x_bits
+    if nvfp4 and H % 64:
+        raise ValueError("NVFP4 needs H % 64 == 0")
+    out = {"residual": h if residual_bits is not None else None}
+    if M == 0:
+        y = np.zeros((0, H), np.uint16)
+    else:
+        y = gemma_rms_norm(h, weight_bits, eps, fmt)
+    out["y"] = y
+    if nvfp4:
+        if M:
+            q, S = quant_nvfp4(y, fmt, scale)
+        else:
+            q, S = np.zeros((0, H // 2), np.uint8), np.zeros((0, H // 16), np.uint8)
+        buf = np.full(int(np.prod(block_scale_buffer_shape(M, H))), block_scale_fill, np.uint8)
+        scatter_block_scales(S, M, H, buf)
+        out.update(q=q, scales=S, block_scale=buf)
+    else:
+        q = quant_fp8_static(y, fmt, scale) if M else np.zeros((0, H), np.uint8)
+        out.update(q=q, scales=None, block_scale=float(np.float32(scale)))
+    out["write_y"] = bool(write_y)
+    return out

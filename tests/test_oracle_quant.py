@@ -1,0 +1,210 @@
+"""Pins of the oracle's FP8 and NVFP4 quant steps and of the 128x4 scale
+layout: hand-derived worked examples, brute-force nearest-value searches,
+error bounds and invariants."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests.golden import read_fixture, num
+from tests.test_oracle_formats import _brute_nearest_even
+from tests.test_oracle_norm import to_bits, vals_to_bits
+
+
+def test_fp8_quant_cases():
+    cases = [[num(t) for t in v] for k, v in read_fixture("fp8_worked_examples.txt") if k == "quant_case"]
+    for y, s, code in cases:
+        q = O.quant_fp8_static(vals_to_bits([[y]], O.BF16), O.BF16, s)
+        assert int(q[0, 0]) == code, (y, s)
+
+
+@pytest.mark.parametrize("y,s,alt_code", [(0.0888671875, 7.0, 0x07), (0.087890625, 0.9, 0x1D)])
+def test_fp8_reciprocal_reading_differs(y, s, alt_code):
+    """y * fl32(1/s) gives a different code than y / s on the fixture's
+    example C cases, so the tests tell the two readings apart."""
+    yf, sf = np.float32(y), np.float32(s)
+    alt = O.encode(np.array([float(yf * (np.float32(1) / sf))]), O.E4M3FN)
+    assert int(alt[0]) == alt_code
+
+
+@pytest.mark.parametrize("fmt", [O.BF16, O.FP16])
+def test_fp8_error_bound_and_saturation(fmt):
+    """|decode(q) * s - y| <= ulp_E4M3(|y/s|)/2 * s (+ the fp32 division's
+    rounding) for |y/s| <= 448; beyond it q is +-448 with y's sign."""
+    g = torch.Generator().manual_seed(23)
+    y = (torch.randn(64, 512, generator=g) * torch.exp(torch.randn(64, 512, generator=g) * 2))
+    yb = to_bits(y.to(torch.bfloat16 if fmt is O.BF16 else torch.float16))
+    s = 0.0371
+    q = O.quant_fp8_static(yb, fmt, s)
+    yv = O.bits_to_f64(yb, fmt)
+    dq = O.decode(q, O.E4M3FN)
+    v = yv / float(np.float32(s))
+    sat = np.abs(v) > 448
+    assert np.all(np.abs(dq[sat]) == 448) and np.all(np.sign(dq[sat]) == np.sign(v[sat]))
+    a = np.abs(v[~sat])
+    _, e = np.frexp(np.where(a == 0, 1, a))
+    ulp = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)
+    err = np.abs(dq[~sat] - v[~sat])
+    assert np.all(err <= ulp / 2 + np.abs(v[~sat]) * 2.0 ** -23)
+
+
+def test_fp8_brute_force_nearest():
+    g = torch.Generator().manual_seed(29)
+    yb = to_bits((torch.randn(16, 4096, generator=g) * 4).to(torch.bfloat16))
+    s = np.float32(0.0123)
+    q = O.quant_fp8_static(yb, O.BF16, float(s))
+    v = O.bits_to_f64(yb, O.BF16).astype(np.float32) / s
+    v = np.clip(v, -448, 448).astype(np.float64).reshape(-1)
+    assert np.array_equal(q.reshape(-1).astype(np.int64), _brute_nearest_even(v, O.E4M3FN))
+
+
+def _nvfp4_fixture():
+    fx = read_fixture("nvfp4_worked_example.txt")
+    d = {}
+    for k, v in fx:
+        d.setdefault(k, []).extend(v)
+    return d
+
+
+def test_nvfp4_worked_example():
+    d = _nvfp4_fixture()
+    H = int(num(d["H"][0]))
+    w = [num(t) for t in d["w"]]
+    assert len(w) == H
+    x = vals_to_bits([[num(d["x"][0])] * H], O.BF16)
+    r = vals_to_bits([[num(d["residual"][0])] * H], O.BF16)
+    out = O.gemma_add_rms_norm_quant(x, r, vals_to_bits(w, O.BF16), num(d["eps"][0]),
+                                     num(d["gscale"][0]), nvfp4=True, write_y=True)
+    assert np.all(out["residual"] == num(d["residual_out"][0]))
+    assert np.array_equal(out["y"][0], vals_to_bits([num(t) for t in d["y"]], O.BF16))
+    assert [int(b) for b in out["q"][0]] == [num(t) for t in d["q"]]
+    assert [int(b) for b in out["scales"][0]] == [num(t) for t in d["scales"]]
+    buf = out["block_scale"]
+    assert buf.size == 128 * 4
+    assert [int(b) for b in buf[:4]] == [num(t) for t in d["scales"]]
+    assert np.all(buf[4:] == 0xA5)
+
+
+def _random_y(M, H, seed, fmt=O.BF16, spread=1.0):
+    g = torch.Generator().manual_seed(seed)
+    y = torch.randn(M, H, generator=g) * torch.exp(torch.randn(M, H // 16, 1, generator=g).expand(M, H // 16, 16).reshape(M, H) * spread)
+    return to_bits(y.to(torch.bfloat16 if fmt is O.BF16 else torch.float16))
+
+
+def test_nvfp4_brute_force_scale_and_codes():
+    """S is the E4M3 value nearest to gs * (a / 6) (fp32 ops), and each code is
+    the E2M1 value nearest to fl32(y * gs / decode(S)) -- both by exhaustive
+    search over the code tables."""
+    yb = _random_y(8, 1024, 31, spread=2.0)
+    gs = np.float32(37.5)
+    q, S = O.quant_nvfp4(yb, O.BF16, float(gs))
+    y = O.bits_to_f64(yb, O.BF16).astype(np.float32).reshape(8, 64, 16)
+    a = np.abs(y).max(axis=2)
+    u = np.minimum(gs * (a / np.float32(6)), np.float32(448))
+    assert np.array_equal(S.reshape(-1).astype(np.int64), _brute_nearest_even(u.reshape(-1).astype(np.float64), O.E4M3FN))
+    sig = O.decode(S, O.E4M3FN).astype(np.float32)
+    o = np.where(sig == 0, np.float32(0), gs / np.where(sig == 0, 1, sig)).astype(np.float32)
+    v = np.clip(y * o[:, :, None], -6, 6).astype(np.float64).reshape(-1)
+    codes = _brute_nearest_even(v, O.E2M1)
+    lo = q & 0xF
+    hi = q >> 4
+    unpacked = np.stack([lo, hi], axis=-1).reshape(-1).astype(np.int64)
+    assert np.array_equal(unpacked, codes)
+
+
+def test_nvfp4_nibble_order_lo_first():
+    """Byte k holds element 2k in its low nibble ("lo in the low nibble")."""
+    y = np.array([[1.0, 6.0] + [0.0] * 14 + [0.5, -6.0] + [0.0] * 14 + [0.0] * 32])
+    q, S = O.quant_nvfp4(vals_to_bits(y, O.BF16), O.BF16, 1.0)
+    assert int(q[0, 0]) == 0x72   # codes 2 (1.0) then 7 (6.0)
+    assert int(q[0, 8]) == 0xF1   # codes 1 (0.5) then 0xF (-6.0)
+
+
+def test_nvfp4_block_max_gets_top_code():
+    """With u = gs*a/6 in E4M3's normal range, rounding moves the block scale
+    by at most 2^-4 relative, so |a * o| is in [5.65, 6.4] and the block's
+    largest element always takes magnitude code 7 (6.0)."""
+    yb = _random_y(32, 2048, 37, spread=3.0)
+    gs = 448 * 6 / 50.0
+    q, S = O.quant_nvfp4(yb, O.BF16, gs)
+    y = O.bits_to_f64(yb, O.BF16).reshape(32, -1, 16)
+    a = np.abs(y).max(axis=2)
+    u = np.float32(gs) * (a.astype(np.float32) / np.float32(6))
+    normal = (u >= 2.0 ** -6) & (u <= 448)
+    codes = np.stack([q & 0xF, q >> 4], -1).reshape(32, -1, 16)
+    am = np.abs(y).argmax(axis=2)
+    top = np.take_along_axis(codes, am[:, :, None], 2)[:, :, 0] & 0x7
+    assert normal.mean() > 0.5
+    assert np.all(top[normal] == 7)
+
+
+def test_nvfp4_dequant_error_bound():
+    """Outside saturated blocks, |c * sigma / gs - y| <= half an E2M1 step at
+    |y * o| times sigma / gs (plus fp32 rounding of the scale product)."""
+    yb = _random_y(16, 1024, 41, spread=1.0)
+    gs = np.float32(448 * 6 / 30.0)
+    q, S = O.quant_nvfp4(yb, O.BF16, float(gs))
+    y = O.bits_to_f64(yb, O.BF16).reshape(16, -1, 16)
+    c = np.stack([q & 0xF, q >> 4], -1).reshape(16, -1, 16)
+    cv = O.decode(c, O.E2M1)
+    sig = O.decode(S, O.E4M3FN)
+    ok = sig > 0
+    deq = cv * (sig / float(gs))[:, :, None]
+    o = float(gs) / np.where(ok, sig, 1)
+    t = np.abs(y) * o[:, :, None]
+    step = np.where(t < 2, 0.5, np.where(t < 4, 1.0, 2.0))
+    bound = (step / 2) * (sig / float(gs))[:, :, None] * (1 + 2.0 ** -20) + np.abs(y) * 2.0 ** -22
+    unsat = (t <= 6)
+    m = ok[:, :, None] & unsat
+    assert m.mean() > 0.9
+    assert np.all(np.abs(deq - y)[m] <= bound[m])
+
+
+def test_nvfp4_zero_and_underflow_blocks():
+    y = np.zeros((1, 64))
+    y[0, 16:32] = [1e-6] + [0.0] * 15        # u = gs*a/6 underflows E4M3 -> S = 0
+    y[0, 32:48] = -1e-7
+    q, S = O.quant_nvfp4(vals_to_bits(y, O.BF16), O.BF16, 1.0)
+    assert list(S[0, :3]) == [0, 0, 0]
+    assert np.all(q[0, :8] == 0)
+    assert int(q[0, 8]) == 0x00
+    assert np.all(q[0, 16:24] == 0x88)        # negative values keep the sign bit
+
+
+def test_nvfp4_scale_saturation():
+    """u above 448 saturates S to 448 (0x7E); elements then saturate at 6."""
+    y = np.full((1, 64), 100.0)
+    y[0, 1] = 1.0
+    q, S = O.quant_nvfp4(vals_to_bits(y, O.BF16), O.BF16, 448.0)
+    assert np.all(S == 0x7E)
+    # o = 448/448 = 1: 100 -> 6 (code 7); 1.0 -> code 2
+    assert int(q[0, 0]) == 0x27 and np.all(q[0, 1:] == 0x77)
+
+
+def test_swizzle_fixture_offsets():
+    for k, v in read_fixture("swizzle_128x4_offsets.txt"):
+        H, m, b, off = (int(num(t)) for t in v)
+        assert int(O.swizzle_128x4_offset(m, b, H)) == off, (H, m, b)
+
+
+@pytest.mark.parametrize("M,H", [(1, 64), (127, 128), (128, 192), (129, 64), (300, 5120)])
+def test_swizzle_is_a_bijection_onto_the_padded_buffer(M, H):
+    R, C = O.block_scale_buffer_shape(M, H)
+    mm, bb = np.meshgrid(np.arange(R), np.arange(C), indexing="ij")
+    off = O.swizzle_128x4_offset(mm, bb, H).reshape(-1)
+    assert np.array_equal(np.sort(off), np.arange(R * C))
+
+
+def test_scatter_leaves_padding_rows_unwritten_and_unswizzles():
+    M, H = 130, 128
+    rng = np.random.default_rng(0)
+    S = rng.integers(0, 0x7E, (M, H // 16)).astype(np.uint8)
+    buf = np.full(int(np.prod(O.block_scale_buffer_shape(M, H))), 0xA5, np.uint8)
+    O.scatter_block_scales(S, M, H, buf)
+    R, C = O.block_scale_buffer_shape(M, H)
+    mm, bb = np.meshgrid(np.arange(R), np.arange(C), indexing="ij")
+    off = O.swizzle_128x4_offset(mm, bb, H)
+    back = buf[off]
+    assert np.array_equal(back[:M], S)
+    assert np.all(back[M:] == 0xA5)
