@@ -1,0 +1,207 @@
+"""Benchmark of the fused residual-add + Gemma RMSNorm + quant op on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one launch of the whole op (add, norm, y, quant, scale store) over
+one batch of the workload, inputs resident in HBM.  The in-place residual
+update is part of the op; to keep the residual bounded over many steps the
+activation alternates between x and -x from step to step (same work, same
+bytes).  Prints one JSON line:
+
+  value        whole-job effective HBM GB/s: algorithmic bytes per step x K /
+               wall time of the K steps (synchronised on both sides);
+  roofline     the kernel's average duration from HIP events recorded on the
+               launch stream, algorithmic bytes / that duration against the
+               8 TB/s HBM peak; traffic = measured HBM bytes per launch
+               (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel's
+               reading) from profiles/traffic.json when it was taken on the
+               current kernel source, else null;
+  cpu_baseline the CPU oracle timed on a bounded row sample of the same
+               workload on this host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective HBM GB/s (and % of peak) + tokens/s for add-RMSNorm+quant, 1 GPU"
+KERNEL_SRC = os.path.join(ROOT, "fp4_activation_quant_amd", "csrc", "gemma_norm_quant.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def algorithmic_bytes(wl):
+    """Bytes the op must move once: reads x, residual, weight, scale; writes
+    residual, y, codes and (NVFP4) one scale byte per 16 elements.  Padding
+    rows of the scale buffer are not written and not counted."""
+    MH = wl.M * wl.H
+    rd = 2 * MH + (2 * MH if wl.has_residual else 0) + 2 * wl.H + 4
+    wr = (2 * MH if wl.has_residual else 0) + (2 * MH if wl.write_y else 0)
+    wr += MH // 2 + MH // 16 if wl.nvfp4 else MH
+    return rd, wr
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kernel_name(wl):
+    return "fused_rows<{},{},{},{},{}>".format(
+        wl.dtype, "nvfp4" if wl.nvfp4 else "fp8", "res" if wl.has_residual else "nores",
+        "y" if wl.write_y else "noy", 1 if wl.H // 16 <= 1024 else 2)
+
+
+def measured_traffic(wl):
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f).get(wl.name)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("kernel_sha") != kernel_sha():
+        return None
+    return int(t["fetch_bytes"] + t["write_bytes"])
+
+
+def cpu_baseline(wl, x, r, w, scale, budget_s):
+    """The oracle as it is, on the first rows of the same inputs, until about
+    budget_s seconds of CPU work have run (at least 16 rows)."""
+    import numpy as np
+    import torch
+    import oracle as O
+
+    def b16(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    fmt = {"bf16": O.BF16, "fp16": O.FP16}[wl.dtype]
+    wb = b16(w)
+    chunk = max(1, min(wl.M, (1 << 20) // wl.H))
+    rows = 0
+    t0 = time.perf_counter()
+    while rows < wl.M:
+        n = min(chunk, wl.M - rows)
+        O.gemma_add_rms_norm_quant(b16(x[rows:rows + n]), b16(r[rows:rows + n]) if r is not None else None,
+                                   wb, wl.eps, scale, wl.nvfp4, wl.write_y, fmt)
+        rows += n
+        if time.perf_counter() - t0 >= budget_s and rows >= 16:
+            break
+    dt = time.perf_counter() - t0
+    rd, wr = algorithmic_bytes(wl)
+    per_row = (rd + wr - 2 * wl.H - 4) / wl.M
+    return {"value": round(per_row * rows / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "tokens_per_s": round(rows / dt, 1),
+            "sample": f"first {rows} of {wl.M} rows of {wl.name}, {dt:.1f} s, numpy single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the op is row-independent and this build has no "
+              "multi-GPU path (--gpus must be 1)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    from fp4_activation_quant_amd import _lib, ops
+    from fp4_activation_quant_amd.workloads import WORKLOADS, DEFAULT_BENCH, make_inputs, load_scale
+
+    _lib.lib()
+    wl = WORKLOADS[args.workload or DEFAULT_BENCH]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    x, r, w = make_inputs(wl)
+    scale = load_scale(wl)
+    xs = [x.to(dev), (-x).to(dev)]
+    rd = r.to(dev) if r is not None else None
+    wd = w.to(dev)
+    sd = torch.tensor([scale], dtype=torch.float32, device=dev)
+    M, H = wl.M, wl.H
+    if wl.nvfp4:
+        q = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+        bs = torch.empty((ops.round_up(M, 128), ops.round_up(H // 16, 4)), dtype=torch.uint8, device=dev)
+    else:
+        q = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
+        bs = None
+    y = torch.empty_like(xs[0]) if wl.write_y else None
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+
+    def launch(i):
+        ops.gemma_add_rms_norm_quant_out(xs[i & 1], rd, wd, wl.eps, sd, wl.nvfp4, q, bs, y)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            launch(i)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            launch(i)
+            ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_ms.sort()
+    avg_ms = sum(kern_ms) / len(kern_ms)
+    med_ms = kern_ms[len(kern_ms) // 2]
+
+    rbytes, wbytes = algorithmic_bytes(wl)
+    total = rbytes + wbytes
+    ms_per_step = wall * 1e3 / args.steps
+    value = total / (ms_per_step * 1e-3) / 1e9
+    achieved = total / (avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(wl)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": M, "H": H, "act_dtype": wl.dtype,
+                   "mode": "nvfp4" if wl.nvfp4 else "fp8_static", "residual": wl.has_residual,
+                   "write_y": wl.write_y, "bytes_per_step": total, "bytes_read": rbytes,
+                   "bytes_written": wbytes},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
+        "kernel_ms": {"avg": round(avg_ms, 5), "median": round(med_ms, 5),
+                      "min": round(kern_ms[0], 5), "max": round(kern_ms[-1], 5)},
+        "roofline": {"bound": "hbm", "kernel": kernel_name(wl), "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, x, r, w, scale, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

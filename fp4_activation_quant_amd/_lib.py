@@ -1,0 +1,76 @@
+"""ctypes binding of libgemma_norm_quant.so (include/gemma_norm_quant.h).
+
+Argument marshalling only: every step of the op runs in the HIP library.  The
+library is loaded from this package directory; there is no fallback.  Build
+it with ``python -m fp4_activation_quant_amd.build``.
+"""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemma_norm_quant.so")
+
+NQ_OK, NQ_EINVAL, NQ_EUNSUPPORTED, NQ_EHIP = 0, 1, 2, 3
+NQ_BF16, NQ_FP16 = 0, 1
+NQ_MODE_FP8_STATIC, NQ_MODE_NVFP4 = 0, 1
+EXPORTS = ("nq_gemma_add_rms_norm_quant", "nq_block_scale_bytes", "nq_status_string",
+           "nq_abi_version", "nq_convert_probe")
+
+_lib = None
+
+
+class NqError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {nq_status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(python -m fp4_activation_quant_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        L.nq_gemma_add_rms_norm_quant.argtypes = [vp, vp, vp, f32, vp, i64, i64, i32, i32, i32,
+                                                  vp, vp, vp, vp]
+        L.nq_gemma_add_rms_norm_quant.restype = i32
+        L.nq_block_scale_bytes.argtypes = [i64, i64]
+        L.nq_block_scale_bytes.restype = ctypes.c_size_t
+        L.nq_status_string.argtypes = [i32]
+        L.nq_status_string.restype = ctypes.c_char_p
+        L.nq_abi_version.argtypes = []
+        L.nq_abi_version.restype = i32
+        L.nq_convert_probe.argtypes = [i32, vp, i64, f32, vp, vp]
+        L.nq_convert_probe.restype = i32
+        _lib = L
+    return _lib
+
+
+def nq_gemma_add_rms_norm_quant(x, residual, weight, eps, scale, M, H, dtype, mode, write_y,
+                                q, block_scale, y, stream):
+    """Raw call with integer device addresses (0 for NULL); returns the status."""
+    return lib().nq_gemma_add_rms_norm_quant(x or None, residual or None, weight or None,
+                                             float(eps), scale or None, int(M), int(H), int(dtype),
+                                             int(mode), int(bool(write_y)), q or None,
+                                             block_scale or None, y or None, stream or None)
+
+
+def nq_block_scale_bytes(M, H):
+    return int(lib().nq_block_scale_bytes(int(M), int(H)))
+
+
+def nq_status_string(status):
+    return lib().nq_status_string(int(status)).decode()
+
+
+def nq_abi_version():
+    return int(lib().nq_abi_version())
+
+
+def nq_convert_probe(kind, inp, n, param, out, stream):
+    """Raw call: ``inp``/``out`` are device addresses (see the header)."""
+    return lib().nq_convert_probe(int(kind), inp or None, int(n), float(param), out or None,
+                                  stream or None)

@@ -1,0 +1,532 @@
+// Fused residual-add + Gemma RMSNorm + FP8 / NVFP4 activation quant for
+// MI355X (gfx950), behind the C ABI declared in include/gemma_norm_quant.h.
+//
+// The operation is `gemma_add_rms_norm_quant` on the `fused_norm_quant` page:
+// residual <- x + residual (rounded to x's dtype), y = h * rsqrt(mean(h^2) +
+// eps) * (1 + w) rounded to x's dtype, then static FP8 E4M3 codes of y/scale,
+// or NVFP4: E2M1 codes with one E4M3 scale per 16 elements in the 128x4-tiled
+// layout.  The page computes the codes from the rounded y so that they equal
+// the unfused chain; this file does the same.
+//
+// Design (memory-bound; no MFMA -- nothing here is a contraction):
+//  * One thread owns a "chunk" of 16 consecutive elements of a row: two
+//    128-bit loads per input tensor, two 128-bit stores per 16-bit output,
+//    one 128-bit (FP8) or 64-bit (NVFP4) code store.  A chunk is exactly one
+//    NVFP4 block, so the block amax needs no cross-lane step.
+//  * A workgroup owns a row at a time (round_up(H/16, 64) threads, up to
+//    1024, 1-2 chunks per thread, so H <= 32768 on this path) and strides
+//    over rows; the weight's (1 + w) lives in registers across rows.  Sum of squares: in-register fp32
+//    FMA chain, wavefront butterfly, one LDS slot per wave, one barrier per
+//    row (the LDS slots are double-buffered by row parity so no second
+//    barrier is needed).
+//  * The per-element quant arithmetic is IEEE fp32 (correctly rounded
+//    division, no contraction: the file is built with -ffp-contract=off) and
+//    the format conversions are the gfx950 hardware ones: v_cvt_pk_bf16_f32 /
+//    v_cvt_f16_f32 (RNE), v_cvt_pk_fp8_f32 (OCP E4M3, RNE) after an explicit
+//    clamp to +-448, v_cvt_scalef32_pk_fp4_f32 with unit scale after a clamp
+//    to +-6.  Their semantics are checked exhaustively against the CPU oracle
+//    through nq_convert_probe.
+//  * Shapes or pointers the vector path cannot take (H % 16 != 0, unaligned
+//    views) go to a scalar kernel with the same arithmetic.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "gemma_norm_quant.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kChunk = 16;        // elements per thread chunk == NVFP4 block
+constexpr int kWave = 64;
+constexpr int kMaxThreads = 1024;
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE2M1Max = 6.0f;
+
+// ----------------------------------------------------------------------------
+// Activation dtypes: unpack two values from a 32-bit word, pack two fp32
+// values with round-to-nearest-even.
+struct Bf16 {
+  static __device__ __forceinline__ float lo(uint32_t p) { return __uint_as_float(p << 16); }
+  static __device__ __forceinline__ float hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+};
+
+struct Fp16 {
+  static __device__ __forceinline__ float lo(uint32_t p) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t p) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+};
+
+// ----------------------------------------------------------------------------
+// Quant-side encoders (shared by the kernels and the probe).
+
+__device__ __forceinline__ float clampf(float v, float lim) {
+  return __builtin_amdgcn_fmed3f(v, -lim, lim);
+}
+
+// Four E4M3FN codes (saturating, RNE) packed little-endian into a word.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clampf(a, kE4M3Max), clampf(b, kE4M3Max), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clampf(c, kE4M3Max), clampf(d, kE4M3Max), w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint32_t e4m3_one(float a) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clampf(a, kE4M3Max), 0.0f, 0, false) & 0xffu;
+}
+
+// Eight E2M1 codes (saturating, RNE), element 2k in the low nibble of byte k.
+__device__ __forceinline__ uint32_t e2m1x8(const float *v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clampf(v[0], kE2M1Max), clampf(v[1], kE2M1Max), 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clampf(v[2], kE2M1Max), clampf(v[3], kE2M1Max), 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clampf(v[4], kE2M1Max), clampf(v[5], kE2M1Max), 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clampf(v[6], kE2M1Max), clampf(v[7], kE2M1Max), 1.0f, 3);
+  return w;
+}
+
+// NVFP4 block scale: S = E4M3(min(gs * (amax / 6), 448)).
+__device__ __forceinline__ uint32_t nvfp4_scale_code(float amax, float gs) {
+  const float t = amax / kE2M1Max;
+  const float u = fminf(gs * t, kE4M3Max);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false) & 0xffu;
+}
+
+// Element multiplier o = gs / decode(S), 0 for a zero scale.
+__device__ __forceinline__ float nvfp4_elem_scale(uint32_t s_code, float gs) {
+  const float sigma = __builtin_amdgcn_cvt_f32_fp8((int)s_code, 0);
+  return sigma == 0.0f ? 0.0f : gs / sigma;
+}
+
+// Byte offset of block scale (row m, block b) in the 128x4-tiled layout;
+// ktiles = round_up(H/16, 4) / 4.
+__device__ __forceinline__ size_t swz128x4(int64_t m, int b, int ktiles) {
+  return ((size_t)(m >> 7) * (size_t)ktiles + (size_t)(b >> 2)) * 512u + (size_t)(m & 31) * 16u +
+         (size_t)((m >> 5) & 3) * 4u + (size_t)(b & 3);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// ----------------------------------------------------------------------------
+// Vector kernel: one workgroup per row at a time, CPT chunks of 16 per thread.
+template <class D, bool NVFP4, bool HAS_RES, bool WRITE_Y, int CPT>
+__global__ void __launch_bounds__(kMaxThreads)
+fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__restrict__ w,
+           const float *__restrict__ scale_ptr, float eps, int64_t M, int nchunk,
+           uint8_t *__restrict__ q, uint8_t *__restrict__ bs, u32x4 *__restrict__ y, int ktiles) {
+  __shared__ float partial[2][kMaxThreads / kWave];
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int nwaves = nthr / kWave;
+  const float Hf = (float)(nchunk * kChunk);
+
+  // (1 + w) for this thread's chunks, kept for every row.
+  float g[CPT][kChunk];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = tid + c * nthr;
+    if (ch < nchunk) {
+      const u32x4 wa = w[2 * ch], wb = w[2 * ch + 1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        g[c][2 * k] = 1.0f + D::lo(wa[k]);
+        g[c][2 * k + 1] = 1.0f + D::hi(wa[k]);
+        g[c][8 + 2 * k] = 1.0f + D::lo(wb[k]);
+        g[c][8 + 2 * k + 1] = 1.0f + D::hi(wb[k]);
+      }
+    }
+  }
+  const float s = *scale_ptr;
+
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x, parity ^= 1) {
+    const size_t rbase = (size_t)row * (size_t)nchunk * 2;
+    uint32_t hb[CPT][8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * nthr;
+      if (ch < nchunk) {
+        const size_t i0 = rbase + 2 * (size_t)ch;
+        const u32x4 xa = __builtin_nontemporal_load(&x[i0]);
+        const u32x4 xb = __builtin_nontemporal_load(&x[i0 + 1]);
+        if constexpr (HAS_RES) {
+          const u32x4 ra = __builtin_nontemporal_load(&res[i0]);
+          const u32x4 rb = __builtin_nontemporal_load(&res[i0 + 1]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            hb[c][k] = D::pack(D::lo(xa[k]) + D::lo(ra[k]), D::hi(xa[k]) + D::hi(ra[k]));
+            hb[c][4 + k] = D::pack(D::lo(xb[k]) + D::lo(rb[k]), D::hi(xb[k]) + D::hi(rb[k]));
+          }
+          u32x4 oa = {hb[c][0], hb[c][1], hb[c][2], hb[c][3]};
+          u32x4 ob = {hb[c][4], hb[c][5], hb[c][6], hb[c][7]};
+          __builtin_nontemporal_store(oa, &res[i0]);
+          __builtin_nontemporal_store(ob, &res[i0 + 1]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            hb[c][k] = xa[k];
+            hb[c][4 + k] = xb[k];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float a = D::lo(hb[c][k]), b = D::hi(hb[c][k]);
+          ss = __builtin_fmaf(a, a, ss);
+          ss = __builtin_fmaf(b, b, ss);
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if ((tid & (kWave - 1)) == 0) partial[parity][tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+    for (int i = 0; i < nwaves; ++i) tot += partial[parity][i];
+    const float rstd = 1.0f / __builtin_sqrtf(tot / Hf + eps);
+
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * nthr;
+      if (ch < nchunk) {
+        float yv[kChunk];
+        uint32_t yb[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float a = (D::lo(hb[c][k]) * rstd) * g[c][2 * k];
+          const float b = (D::hi(hb[c][k]) * rstd) * g[c][2 * k + 1];
+          yb[k] = D::pack(a, b);
+          yv[2 * k] = D::lo(yb[k]);
+          yv[2 * k + 1] = D::hi(yb[k]);
+        }
+        const size_t i0 = rbase + 2 * (size_t)ch;
+        if constexpr (WRITE_Y) {
+          u32x4 oa = {yb[0], yb[1], yb[2], yb[3]};
+          u32x4 ob = {yb[4], yb[5], yb[6], yb[7]};
+          __builtin_nontemporal_store(oa, &y[i0]);
+          __builtin_nontemporal_store(ob, &y[i0 + 1]);
+        }
+        if constexpr (NVFP4) {
+          float amax = 0.0f;
+#pragma unroll
+          for (int k = 0; k < kChunk; ++k) amax = fmaxf(amax, fabsf(yv[k]));
+          const uint32_t sc = nvfp4_scale_code(amax, s);
+          const float o = nvfp4_elem_scale(sc, s);
+          float v[kChunk];
+#pragma unroll
+          for (int k = 0; k < kChunk; ++k) v[k] = yv[k] * o;
+          u32x2 packed = {e2m1x8(v), e2m1x8(v + 8)};
+          u32x2 *qp = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8) + ch;
+          __builtin_nontemporal_store(packed, qp);
+          bs[swz128x4(row, ch, ktiles)] = (uint8_t)sc;
+        } else {
+          float v[kChunk];
+#pragma unroll
+          for (int k = 0; k < kChunk; ++k) v[k] = yv[k] / s;
+          u32x4 packed = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7]),
+                          e4m3x4(v[8], v[9], v[10], v[11]), e4m3x4(v[12], v[13], v[14], v[15])};
+          u32x4 *qp = reinterpret_cast<u32x4 *>(q + (size_t)row * (size_t)nchunk * 16) + ch;
+          __builtin_nontemporal_store(packed, qp);
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Scalar kernel for any H and any alignment: same arithmetic, element loads.
+template <class D, bool NVFP4, bool HAS_RES, bool WRITE_Y>
+__global__ void __launch_bounds__(256)
+fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
+                  const uint16_t *__restrict__ w, const float *__restrict__ scale_ptr, float eps,
+                  int64_t M, int H, uint8_t *__restrict__ q, uint8_t *__restrict__ bs,
+                  uint16_t *__restrict__ y, int ktiles) {
+  __shared__ float partial[2][256 / kWave];
+  const int tid = threadIdx.x;
+  const int nwaves = blockDim.x / kWave;
+  const float s = *scale_ptr;
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x, parity ^= 1) {
+    const size_t rb = (size_t)row * (size_t)H;
+    float ss = 0.0f;
+    for (int j = tid; j < H; j += blockDim.x) {
+      uint32_t h = x[rb + j];
+      if constexpr (HAS_RES) {
+        h = D::pack(D::lo(h) + D::lo(res[rb + j]), 0.0f) & 0xffffu;
+        res[rb + j] = (uint16_t)h;
+      }
+      const float hf = D::lo(h);
+      ss = __builtin_fmaf(hf, hf, ss);
+    }
+    ss = wave_sum(ss);
+    if ((tid & (kWave - 1)) == 0) partial[parity][tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+    for (int i = 0; i < nwaves; ++i) tot += partial[parity][i];
+    const float rstd = 1.0f / __builtin_sqrtf(tot / (float)H + eps);
+    const uint16_t *hsrc = HAS_RES ? res : x;
+    if constexpr (NVFP4) {
+      // Blocks of 16 read h written by other threads before the barrier.
+      const int nb = H / kChunk;
+      for (int b = tid; b < nb; b += blockDim.x) {
+        float yv[kChunk];
+        for (int k = 0; k < kChunk; ++k) {
+          const int j = b * kChunk + k;
+          const float yy = (D::lo(hsrc[rb + j]) * rstd) * (1.0f + D::lo(w[j]));
+          const uint32_t yq = D::pack(yy, 0.0f) & 0xffffu;
+          if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
+          yv[k] = D::lo(yq);
+        }
+        float amax = 0.0f;
+        for (int k = 0; k < kChunk; ++k) amax = fmaxf(amax, fabsf(yv[k]));
+        const uint32_t sc = nvfp4_scale_code(amax, s);
+        const float o = nvfp4_elem_scale(sc, s);
+        float v[kChunk];
+        for (int k = 0; k < kChunk; ++k) v[k] = yv[k] * o;
+        const uint32_t p0 = e2m1x8(v), p1 = e2m1x8(v + 8);
+        uint8_t *qp = q + (size_t)row * (size_t)(H / 2) + (size_t)b * 8;
+        for (int k = 0; k < 4; ++k) {
+          qp[k] = (uint8_t)(p0 >> (8 * k));
+          qp[4 + k] = (uint8_t)(p1 >> (8 * k));
+        }
+        bs[swz128x4(row, b, ktiles)] = (uint8_t)sc;
+      }
+    } else {
+      for (int j = tid; j < H; j += blockDim.x) {
+        const float yy = (D::lo(hsrc[rb + j]) * rstd) * (1.0f + D::lo(w[j]));
+        const uint32_t yq = D::pack(yy, 0.0f) & 0xffffu;
+        if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
+        q[rb + j] = (uint8_t)e4m3_one(D::lo(yq) / s);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Conversion probe (diagnostics): the same device routines on bit patterns.
+__global__ void convert_probe(int kind, const uint32_t *__restrict__ in, int64_t n, float param,
+                              uint8_t *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t bits = in[i];
+  const float f = __uint_as_float(bits);
+  switch (kind) {
+    case 0: out[i] = (uint8_t)e4m3_one(f); break;
+    case 1: {
+      float v[8] = {f, 0, 0, 0, 0, 0, 0, 0};
+      out[i] = (uint8_t)(e2m1x8(v) & 0xfu);
+      break;
+    }
+    case 2: reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)(Bf16::pack(f, 0.0f) & 0xffffu); break;
+    case 3: reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)(Fp16::pack(f, 0.0f) & 0xffffu); break;
+    case 4: out[i] = (uint8_t)e4m3_one(Bf16::lo(bits & 0xffffu) / param); break;
+    case 5: out[i] = (uint8_t)e4m3_one(Fp16::lo(bits & 0xffffu) / param); break;
+    case 6: out[i] = (uint8_t)nvfp4_scale_code(f, param); break;
+    default: break;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Host side.
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static int cached[64] = {0};
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev >= 0 && dev < 64) cached[dev] = cus;
+  return cus;
+}
+
+// Rows in flight per CU for the persistent grid (tuning override:
+// GNQ_WG_PER_CU; 0 = one workgroup per row).
+int wg_per_cu_setting() {
+  static int v = -1;
+  if (v < 0) {
+    const char *e = getenv("GNQ_WG_PER_CU");
+    v = e ? atoi(e) : 8;
+    if (v < 0) v = 0;
+  }
+  return v;
+}
+
+template <class D, bool NV, bool RES, bool WY, int CPT>
+hipError_t launch_vec(dim3 grid, dim3 block, hipStream_t st, const void *x, void *res, const void *w,
+                      const float *scale, float eps, int64_t M, int nchunk, void *q, void *bs,
+                      void *y, int ktiles) {
+  hipLaunchKernelGGL((fused_rows<D, NV, RES, WY, CPT>), grid, block, 0, st,
+                     (const u32x4 *)x, (u32x4 *)res, (const u32x4 *)w, scale, eps, M, nchunk,
+                     (uint8_t *)q, (uint8_t *)bs, (u32x4 *)y, ktiles);
+  return hipGetLastError();
+}
+
+template <class D, bool NV, bool RES, bool WY>
+hipError_t dispatch_cpt(int cpt, dim3 grid, dim3 block, hipStream_t st, const void *x, void *res,
+                        const void *w, const float *scale, float eps, int64_t M, int nchunk,
+                        void *q, void *bs, void *y, int ktiles) {
+  if (cpt == 1)
+    return launch_vec<D, NV, RES, WY, 1>(grid, block, st, x, res, w, scale, eps, M, nchunk, q, bs, y, ktiles);
+  return launch_vec<D, NV, RES, WY, 2>(grid, block, st, x, res, w, scale, eps, M, nchunk, q, bs, y, ktiles);
+}
+
+template <class D, bool NV, bool RES, bool WY>
+hipError_t launch_scalar(dim3 grid, hipStream_t st, const void *x, void *res, const void *w,
+                         const float *scale, float eps, int64_t M, int H, void *q, void *bs,
+                         void *y, int ktiles) {
+  hipLaunchKernelGGL((fused_rows_scalar<D, NV, RES, WY>), grid, dim3(256), 0, st,
+                     (const uint16_t *)x, (uint16_t *)res, (const uint16_t *)w, scale, eps, M, H,
+                     (uint8_t *)q, (uint8_t *)bs, (uint16_t *)y, ktiles);
+  return hipGetLastError();
+}
+
+struct Args {
+  const void *x;
+  void *res;
+  const void *w;
+  const float *scale;
+  float eps;
+  int64_t M;
+  int64_t H;
+  void *q;
+  void *bs;
+  void *y;
+  hipStream_t st;
+};
+
+template <class D, bool NV, bool RES, bool WY>
+hipError_t run(const Args &a) {
+  const int ktiles = (int)(((a.H / kChunk) + 3) / 4);
+  const int cus = device_cus();
+  const int per_cu = wg_per_cu_setting();
+  auto aligned = [](const void *p, uintptr_t n) { return p == nullptr || ((uintptr_t)p % n) == 0; };
+  const bool vec = (a.H % kChunk == 0) && (a.H / kChunk) <= 2 * kMaxThreads && aligned(a.x, 16) &&
+                   aligned(a.res, 16) && aligned(a.w, 16) && aligned(a.y, 16) &&
+                   aligned(a.q, NV ? 8 : 16);
+  if (vec) {
+    const int nchunk = (int)(a.H / kChunk);
+    const int cpt = nchunk <= kMaxThreads ? 1 : 2;
+    const int per_thread = (nchunk + cpt - 1) / cpt;
+    const int threads = ((per_thread + kWave - 1) / kWave) * kWave;
+    int64_t g = a.M;
+    if (per_cu > 0) {
+      const int64_t cap = (int64_t)cus * per_cu;
+      if (g > cap) g = cap;
+    }
+    return dispatch_cpt<D, NV, RES, WY>(cpt, dim3((unsigned)g), dim3(threads), a.st, a.x, a.res,
+                                        a.w, a.scale, a.eps, a.M, nchunk, a.q, a.bs, a.y, ktiles);
+  }
+  int64_t g = a.M;
+  const int64_t cap = (int64_t)cus * 8;
+  if (g > cap) g = cap;
+  return launch_scalar<D, NV, RES, WY>(dim3((unsigned)g), a.st, a.x, a.res, a.w, a.scale, a.eps,
+                                       a.M, (int)a.H, a.q, a.bs, a.y, ktiles);
+}
+
+template <class D, bool NV>
+hipError_t run_res_y(const Args &a, bool res, bool wy) {
+  if (res) return wy ? run<D, NV, true, true>(a) : run<D, NV, true, false>(a);
+  return wy ? run<D, NV, false, true>(a) : run<D, NV, false, false>(a);
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x0 = (uintptr_t)a, x1 = x0 + na, y0 = (uintptr_t)b, y1 = y0 + nb;
+  return x0 < y1 && y0 < x1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nq_abi_version(void) { return NQ_ABI_VERSION; }
+
+const char *nq_status_string(int status) {
+  switch (status) {
+    case NQ_OK: return "ok";
+    case NQ_EINVAL: return "invalid argument";
+    case NQ_EUNSUPPORTED: return "unsupported shape or mode";
+    case NQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t nq_block_scale_bytes(int64_t M, int64_t H) {
+  if (M <= 0 || H < kChunk) return 0;
+  const int64_t rows = (M + 127) / 128 * 128;
+  const int64_t cols = ((H / kChunk) + 3) / 4 * 4;
+  return (size_t)rows * (size_t)cols;
+}
+
+nq_status nq_gemma_add_rms_norm_quant(const void *x, void *residual, const void *weight, float eps,
+                                      const float *scale, int64_t M, int64_t H, int dtype,
+                                      int mode, int write_y, void *q, void *block_scale, void *y,
+                                      void *stream) {
+  if (dtype != NQ_BF16 && dtype != NQ_FP16) return NQ_EINVAL;
+  if (mode != NQ_MODE_FP8_STATIC && mode != NQ_MODE_NVFP4) return NQ_EINVAL;
+  if (M < 0 || H <= 0 || H > (int64_t)1 << 30) return NQ_EINVAL;
+  if (!x || !weight || !scale || !q) return NQ_EINVAL;
+  const bool nv = mode == NQ_MODE_NVFP4;
+  if (nv && !block_scale) return NQ_EINVAL;
+  if (write_y && !y) return NQ_EINVAL;
+  if (nv && H % 64 != 0) return NQ_EUNSUPPORTED;
+  const size_t act = (size_t)M * (size_t)H * 2;
+  const size_t qbytes = nv ? (size_t)M * (size_t)(H / 2) : (size_t)M * (size_t)H;
+  const size_t bsbytes = nv ? nq_block_scale_bytes(M, H) : 0;
+  if (residual == x) return NQ_EINVAL;
+  if (overlaps(x, act, residual, act) || overlaps(q, qbytes, x, act) ||
+      overlaps(q, qbytes, residual, act) || (write_y && (overlaps(y, act, x, act) ||
+                                                          overlaps(y, act, residual, act) ||
+                                                          overlaps(y, act, q, qbytes))) ||
+      (nv && (overlaps(block_scale, bsbytes, x, act) || overlaps(block_scale, bsbytes, residual, act) ||
+              overlaps(block_scale, bsbytes, q, qbytes) ||
+              (write_y && overlaps(block_scale, bsbytes, y, act)))))
+    return NQ_EINVAL;
+  if (M == 0) return NQ_OK;
+
+  Args a{x, residual, weight, scale, eps, M, H, q, nv ? block_scale : nullptr,
+         write_y ? y : nullptr, (hipStream_t)stream};
+  hipError_t e;
+  const bool res = residual != nullptr, wy = write_y != 0;
+  if (dtype == NQ_BF16)
+    e = nv ? run_res_y<Bf16, true>(a, res, wy) : run_res_y<Bf16, false>(a, res, wy);
+  else
+    e = nv ? run_res_y<Fp16, true>(a, res, wy) : run_res_y<Fp16, false>(a, res, wy);
+  return e == hipSuccess ? NQ_OK : NQ_EHIP;
+}
+
+nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,
+                           void *stream) {
+  if (kind < 0 || kind > 6 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in)))
+    return NQ_EINVAL;
+  if (n == 0) return NQ_OK;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(convert_probe, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,
+                     kind, (const uint32_t *)in, n, param, (uint8_t *)out);
+  return hipGetLastError() == hipSuccess ? NQ_OK : NQ_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+/*
+ * gemma_norm_quant.h -- C ABI of the MI355X (gfx950) fused residual-add +
+ * Gemma RMSNorm + activation-quant library (libgemma_norm_quant.so).
+ *
+ * The operation is the one stated on the `fused_norm_quant` page
+ * (`gemma_add_rms_norm_quant(x, residual, weight, eps, scale, nvfp4,
+ * write_y)`, its parameter list, "Returns" list and wrapper source):
+ *
+ *   h        = x + residual, rounded to x's dtype and written back into
+ *              `residual` ("Updated in place to x + residual"); h = x when
+ *              residual is NULL, and nothing is written back then;
+ *   y        = h * rsqrt(mean(h^2) + eps) * (1 + weight), fp32 arithmetic,
+ *              rounded to x's dtype ("the norm scales by (1 + weight)"; the
+ *              quantized values are computed from this rounded y);
+ *   FP8      : q = E4M3FN(clamp(y / scale, -448, 448)), round to nearest even
+ *              (static per-tensor scale; the caller keeps `scale` as the
+ *              returned block scale);
+ *   NVFP4    : per 16-element block of a row, a = max|y|, S = E4M3FN(min(
+ *              scale * (a / 6), 448)), o = scale / S (0 if S == 0), codes
+ *              E2M1(clamp(y * o, -6, 6)) round to nearest even, two per byte
+ *              with the even-index element in the low nibble ("lo in the
+ *              low nibble", `_cvt_e2m1x2`); S is stored in the 128x4-tiled
+ *              layout (byte (m, b) at ((m/128)*(Kp/4) + b/4)*512 +
+ *              (m%32)*16 + ((m%128)/32)*4 + b%4, Kp = round_up(H/16, 4));
+ *              rows >= M of that buffer are never written.
+ *
+ * All pointers except `scale`'s owner are caller-owned device buffers on the
+ * current HIP device.  The library allocates nothing, keeps no pointer past
+ * the call and launches asynchronously on `stream` (a hipStream_t; NULL is
+ * the null stream).  On any error nothing is launched and nothing is
+ * written.  No C++ exception crosses this boundary.
+ */
+#ifndef GEMMA_NORM_QUANT_H
+#define GEMMA_NORM_QUANT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NQ_ABI_VERSION 1
+
+typedef enum {
+  NQ_OK = 0,
+  NQ_EINVAL = 1,        /* null required pointer, bad size, bad enum, aliasing */
+  NQ_EUNSUPPORTED = 2,  /* NVFP4 with H % 64 != 0 */
+  NQ_EHIP = 3           /* a HIP runtime call or the launch failed */
+} nq_status;
+
+typedef enum { NQ_BF16 = 0, NQ_FP16 = 1 } nq_dtype;
+
+typedef enum { NQ_MODE_FP8_STATIC = 0, NQ_MODE_NVFP4 = 1 } nq_mode;
+
+/*
+ * nq_gemma_add_rms_norm_quant -- the op above, one launch.
+ *
+ *   x          (M, H) dtype, row-major contiguous, read only.
+ *   residual   (M, H) dtype or NULL; updated in place to x + residual.
+ *              Must not be the same buffer as x.
+ *   weight     (H,) dtype; the norm scales by (1 + weight).
+ *   eps        RMS-norm epsilon (> 0; eps == 0 with an all-zero row gives
+ *              NaN, as the definition does).
+ *   scale      DEVICE pointer to one fp32: FP8 mode, the static per-tensor
+ *              scale (> 0); NVFP4 mode, the global scale (> 0) that maps a
+ *              block's amax/6 into E4M3's range (448*6/amax for a tensor
+ *              amax).  Non-finite values are outside the contract.
+ *   M, H       rows (tokens) >= 0 and hidden size >= 1.  M == 0 returns
+ *              NQ_OK without launching.  NVFP4 needs H % 64 == 0 (whole
+ *              4-column scale tiles, so no padded scale columns exist).
+ *   dtype      nq_dtype of x, residual, weight and y.
+ *   mode       nq_mode.
+ *   write_y    nonzero: also write y.
+ *   q          FP8: (M, H) bytes of E4M3FN codes.  NVFP4: (M, H/2) bytes of
+ *              packed E2M1 codes.
+ *   block_scale NVFP4: nq_block_scale_bytes(M, H) bytes, 128x4-tiled E4M3FN
+ *              block scales; bytes of rows >= M are left as they were.
+ *              FP8: ignored (may be NULL).
+ *   y          (M, H) dtype when write_y, else ignored (may be NULL).
+ *   stream     hipStream_t to launch on.
+ *
+ * Outputs must not overlap inputs or each other (residual is both).  Any
+ * alignment and any H are accepted; the fast path needs 16-byte aligned
+ * pointers and H % 16 == 0, other cases take a slower correct path.
+ */
+nq_status nq_gemma_add_rms_norm_quant(const void *x, void *residual, const void *weight,
+                                      float eps, const float *scale, int64_t M, int64_t H,
+                                      int dtype, int mode, int write_y, void *q,
+                                      void *block_scale, void *y, void *stream);
+
+/* Size in bytes of the NVFP4 block-scale buffer:
+ * round_up(M, 128) * round_up(H / 16, 4) (the wrapper's allocation on the
+ * `fused_norm_quant` page).  0 for M <= 0 or H < 16. */
+size_t nq_block_scale_bytes(int64_t M, int64_t H);
+
+/* Static description of a status code; never NULL. */
+const char *nq_status_string(int status);
+
+/* NQ_ABI_VERSION of the loaded library. */
+int nq_abi_version(void);
+
+/*
+ * nq_convert_probe -- diagnostic: runs the fused kernel's own device
+ * conversion routines on n 32-bit input patterns, so that tests can sweep
+ * them (every rounding tie and its neighbours, every 16-bit input) against
+ * an independent encoder.
+ *
+ *   in   device buffer of n uint32 patterns
+ *   kind 0: E4M3FN saturating encode of the fp32 pattern -> 1 byte each
+ *   kind 1: E2M1 saturating encode of the fp32 pattern   -> 1 byte each
+ *           (code in the low nibble)
+ *   kind 2: bf16 round-to-nearest-even of the fp32 pattern -> 2 bytes each
+ *   kind 3: fp16 round-to-nearest-even of the fp32 pattern -> 2 bytes each
+ *   kind 4: static FP8 quant of bf16 y = low 16 bits of the pattern with
+ *           scale `param` (the E4M3FN(y / scale) step) -> 1 byte each
+ *   kind 5: kind 4 for fp16 y
+ *   kind 6: NVFP4 block-scale code of amax = fp32 pattern with global scale
+ *           `param` -> 1 byte each
+ *   out  device buffer of n (kinds 0, 1, 4, 5, 6) or 2n (kinds 2, 3) bytes.
+ *   n    in [0, 2^31).
+ */
+nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMMA_NORM_QUANT_H */

@@ -1,0 +1,206 @@
+"""GPU-vs-oracle comparison shared by the GPU tests and the smoke check.
+
+The HIP op runs on device copies of CPU inputs, into output buffers that are
+pre-filled with a sentinel byte and followed by guard bytes, so that writes
+outside an output (or into the unwritten padding rows of the NVFP4 scale
+buffer) show up.  The oracle runs on a set of rows (all rows for small
+inputs, a seeded sample plus the first and the last 128-row tile for large
+ones); rows are independent, so a sampled row is compared exactly as in a
+full run.
+
+Acceptance, per element of the compared rows:
+  residual     bit-exact;
+  y            at most 1 unit in the last place of x's dtype;
+  codes        (FP8 element, NVFP4 block) bit-exact where the GPU's y equals
+               the oracle's y bit for bit, otherwise at most one code step,
+               with at most 1e-4 of all codes differing;
+  NVFP4 scales bit-exact in at least 99.99% of blocks (and wherever the
+               block's y matches);
+  quant step   the GPU's codes and scales equal the oracle's quant step
+               applied to the GPU's own y, bit for bit (needs the GPU's y);
+  padding      scale-buffer rows >= M and all guard bytes keep the sentinel.
+"""
+
+import numpy as np
+import torch
+
+import oracle as O
+from fp4_activation_quant_amd import ops
+
+FMT = {torch.bfloat16: O.BF16, torch.float16: O.FP16}
+SENTINEL = 0xA5
+GUARD = 4096
+CODE_DIFF_FRACTION = 1e-4
+SCALE_MATCH_FRACTION = 0.9999
+
+
+def bits16(t):
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _guarded(nbytes, dev):
+    return torch.full((nbytes + GUARD,), SENTINEL, dtype=torch.uint8, device=dev)
+
+
+def run_gpu(x, r, w, eps, scale, nvfp4, write_y, device="cuda", misalign=False):
+    """Run the HIP op once on device copies of CPU tensors.  Returns numpy
+    outputs and the guard/padding state.  ``misalign`` places x, residual and
+    y at a 2-byte offset (a non-16-byte-aligned view)."""
+    dev = torch.device(device)
+    M, H = x.shape
+    dt = x.dtype
+    off = 2 if misalign else 0
+    act = M * H * 2
+
+    def place(t):
+        buf = _guarded(act + off, dev)
+        v = buf[off:off + act].view(dt).view(M, H)
+        if t is not None:
+            v.copy_(t.to(dev))
+        return buf, v
+
+    xbuf, xd = place(x)
+    rbuf, rd = place(r) if r is not None else (None, None)
+    wd = w.to(dev).contiguous()
+    sd = torch.tensor([scale], dtype=torch.float32, device=dev)
+    qbytes = M * (H // 2) if nvfp4 else M * H
+    qbuf = _guarded(qbytes + off, dev)
+    qv = qbuf[off:off + qbytes]
+    qv = qv.view(M, H // 2) if nvfp4 else qv.view(torch.float8_e4m3fn).view(M, H)
+    bsn = ops.block_scale_bytes(M, H) if nvfp4 else 0
+    bsbuf = _guarded(bsn, dev) if nvfp4 else None
+    ybuf, yd = place(None) if write_y else (None, None)
+    ops.gemma_add_rms_norm_quant_out(xd, rd, wd, eps, sd, nvfp4, qv,
+                                     bsbuf[:bsn] if nvfp4 else None, yd)
+    torch.cuda.synchronize(dev)
+
+    def tail_ok(buf, n):
+        return bool((buf[off + n:].cpu() == SENTINEL).all()) and bool((buf[:off].cpu() == SENTINEL).all())
+
+    out = {
+        "M": M, "H": H, "nvfp4": nvfp4, "dtype": dt,
+        "x_unchanged": bool(torch.equal(xd.cpu(), x)),
+        "residual": bits16(rd) if rd is not None else None,
+        "y": bits16(yd) if yd is not None else None,
+        "q": qv.view(torch.uint8).cpu().numpy() if not nvfp4 else qv.cpu().numpy(),
+        "bs": bsbuf[:bsn].cpu().numpy() if nvfp4 else None,
+        "guards_ok": all([tail_ok(xbuf, act), tail_ok(qbuf, qbytes),
+                          rbuf is None or tail_ok(rbuf, act), ybuf is None or tail_ok(ybuf, act),
+                          bsbuf is None or bool((bsbuf[bsn:].cpu() == SENTINEL).all())]),
+    }
+    return out
+
+
+def sample_rows(M, max_full=512, n_random=192, extra=(), seed=0):
+    """All rows when M is small, else the first and last 128-row tiles, a
+    seeded random sample and ``extra`` rows."""
+    if M <= max_full:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    last0 = (M - 1) // 128 * 128
+    rows = np.concatenate([np.arange(128), np.arange(last0, M), rng.choice(M, n_random, replace=False),
+                           np.asarray(list(extra), dtype=np.int64)])
+    return np.unique(rows)
+
+
+def _ord16(b):
+    b = b.astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def _ord_code(c, sign_bit):
+    c = c.astype(np.int64)
+    return np.where(c & sign_bit, -(c & (sign_bit - 1)), c & (sign_bit - 1))
+
+
+def _unpack_e2m1(q):
+    return np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[0], -1)
+
+
+def gather_scales(bs_flat, rows, H):
+    nb = H // 16
+    mm, bb = np.meshgrid(rows, np.arange(nb), indexing="ij")
+    return bs_flat[O.swizzle_128x4_offset(mm, bb, H)]
+
+
+def compare(gpu, x, r, w, eps, scale, rows, y_gpu=None):
+    """Compare a GPU run with the oracle on ``rows``.  ``y_gpu`` (full (M, H)
+    uint16) is the GPU's y when the run itself did not write it."""
+    M, H, nvfp4 = gpu["M"], gpu["H"], gpu["nvfp4"]
+    fmt = FMT[x.dtype]
+    rows = np.asarray(rows, dtype=np.int64)
+    xb = bits16(x)[rows]
+    rb = bits16(r)[rows] if r is not None else None
+    ref = O.gemma_add_rms_norm_quant(xb, rb, bits16(w), eps, scale, nvfp4, True, fmt)
+    rep = {"rows": len(rows), "elements": len(rows) * H, "guards_ok": gpu["guards_ok"],
+           "x_unchanged": gpu["x_unchanged"]}
+    if r is not None:
+        rep["residual_mismatch"] = int(np.count_nonzero(gpu["residual"][rows] != ref["residual"]))
+    yg = gpu["y"] if gpu["y"] is not None else y_gpu
+    if yg is not None:
+        yg = yg[rows]
+        dy = np.abs(_ord16(yg) - _ord16(ref["y"]))
+        rep["y_max_ulp"] = int(dy.max()) if dy.size else 0
+        rep["y_diff_fraction"] = float(np.count_nonzero(dy) / max(dy.size, 1))
+        y_equal = dy == 0
+    else:
+        y_equal = None
+    if nvfp4:
+        cg = _unpack_e2m1(gpu["q"][rows])
+        cr = _unpack_e2m1(ref["q"])
+        step = np.abs(_ord_code(cg, 8) - _ord_code(cr, 8))
+        sg = gather_scales(gpu["bs"], rows, H)
+        sr = ref["scales"]
+        rep["scale_match_fraction"] = float(np.count_nonzero(sg == sr) / max(sr.size, 1))
+        if y_equal is not None:
+            blk_eq = y_equal.reshape(len(rows), -1, 16).all(axis=2)
+            rep["scale_mismatch_where_y_equal"] = int(np.count_nonzero((sg != sr) & blk_eq))
+            rep["code_mismatch_where_y_equal"] = int(np.count_nonzero(
+                (step != 0).reshape(len(rows), -1, 16).any(axis=2) & blk_eq))
+            q2, s2 = O.quant_nvfp4(yg, fmt, scale)
+            rep["requant_code_mismatch"] = int(np.count_nonzero(q2 != gpu["q"][rows]))
+            rep["requant_scale_mismatch"] = int(np.count_nonzero(s2 != sg))
+        # padding rows of the scale buffer keep the sentinel
+        R = O.block_scale_buffer_shape(M, H)[0]
+        if R > M:
+            pr = gather_scales(gpu["bs"], np.arange(M, R), H)
+            rep["padding_written"] = int(np.count_nonzero(pr != SENTINEL))
+        else:
+            rep["padding_written"] = 0
+    else:
+        cg = gpu["q"][rows]
+        cr = ref["q"]
+        step = np.abs(_ord_code(cg, 0x80) - _ord_code(cr, 0x80))
+        if y_equal is not None:
+            rep["code_mismatch_where_y_equal"] = int(np.count_nonzero((step != 0) & y_equal))
+            q2 = O.quant_fp8_static(yg, fmt, scale)
+            rep["requant_code_mismatch"] = int(np.count_nonzero(q2 != cg))
+    rep["code_max_step"] = int(step.max()) if step.size else 0
+    rep["code_diff_fraction"] = float(np.count_nonzero(step) / max(step.size, 1))
+    return rep
+
+
+def check(rep):
+    """Raise AssertionError listing every bar the report misses."""
+    bad = []
+    if not rep["guards_ok"]:
+        bad.append("wrote outside an output buffer")
+    if not rep["x_unchanged"]:
+        bad.append("x was modified")
+    if rep.get("residual_mismatch", 0):
+        bad.append(f"residual mismatches: {rep['residual_mismatch']}")
+    if rep.get("y_max_ulp", 0) > 1:
+        bad.append(f"y off by {rep['y_max_ulp']} ulp")
+    if rep["code_max_step"] > 1:
+        bad.append(f"code off by {rep['code_max_step']} steps")
+    if rep["code_diff_fraction"] > CODE_DIFF_FRACTION:
+        bad.append(f"code diff fraction {rep['code_diff_fraction']:.3g}")
+    for k in ("code_mismatch_where_y_equal", "scale_mismatch_where_y_equal",
+              "requant_code_mismatch", "requant_scale_mismatch", "padding_written"):
+        if rep.get(k, 0):
+            bad.append(f"{k}: {rep[k]}")
+    if "scale_match_fraction" in rep and rep["scale_match_fraction"] < SCALE_MATCH_FRACTION:
+        bad.append(f"scale match fraction {rep['scale_match_fraction']:.6f}")
+    if bad:
+        raise AssertionError("; ".join(bad) + f"  [{rep}]")
+    return rep

@@ -1,0 +1,103 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and its host-side logic (sizes, status strings, argument
+validation, the M == 0 early return) behaves as documented.  No call here
+reaches a kernel launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_activation_quant_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemma_norm_quant.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_is_built():
+    assert os.path.exists(_lib.LIB_PATH), "run python -m fp4_activation_quant_amd.build"
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert _lib.nq_abi_version() == 1
+    assert _lib.nq_status_string(0) == "ok"
+    for s in range(0, 6):
+        assert isinstance(_lib.nq_status_string(s), str)
+
+
+@pytest.mark.parametrize("M,H,want", [(1, 64, 512), (128, 64, 512), (129, 64, 1024),
+                                      (8192, 4096, 8192 * 256), (4096, 5120, 4096 * 320),
+                                      (32768, 8192, 32768 * 512), (1, 80, 128 * 8),
+                                      (0, 64, 0), (5, 8, 0)])
+def test_block_scale_bytes(M, H, want):
+    assert _lib.nq_block_scale_bytes(M, H) == want
+
+
+# Fake, never-dereferenced device addresses: every case below must be
+# rejected (or return early) on the host.
+X, R, W, S, Q, B, Y = (0x10000000 + i * 0x1000000 for i in range(7))
+
+
+def call(**over):
+    a = dict(x=X, r=R, w=W, eps=1e-6, s=S, M=4, H=128, dtype=0, mode=0, wy=0, q=Q, bs=B, y=Y)
+    a.update(over)
+    return _lib.nq_gemma_add_rms_norm_quant(a["x"], a["r"], a["w"], a["eps"], a["s"], a["M"],
+                                            a["H"], a["dtype"], a["mode"], a["wy"], a["q"],
+                                            a["bs"], a["y"], 0)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(x=0), _lib.NQ_EINVAL),
+    (dict(w=0), _lib.NQ_EINVAL),
+    (dict(s=0), _lib.NQ_EINVAL),
+    (dict(q=0), _lib.NQ_EINVAL),
+    (dict(M=-3), _lib.NQ_EINVAL),
+    (dict(H=0), _lib.NQ_EINVAL),
+    (dict(H=-5), _lib.NQ_EINVAL),
+    (dict(dtype=7), _lib.NQ_EINVAL),
+    (dict(mode=-1), _lib.NQ_EINVAL),
+    (dict(wy=1, y=0), _lib.NQ_EINVAL),
+    (dict(mode=1, bs=0), _lib.NQ_EINVAL),
+    (dict(mode=1, H=96), _lib.NQ_EUNSUPPORTED),
+    (dict(mode=1, H=32), _lib.NQ_EUNSUPPORTED),
+    (dict(r=X), _lib.NQ_EINVAL),
+    (dict(r=X + 256), _lib.NQ_EINVAL),
+    (dict(q=X + 100), _lib.NQ_EINVAL),
+    (dict(wy=1, y=R + 2), _lib.NQ_EINVAL),
+    (dict(mode=1, bs=Q + 10), _lib.NQ_EINVAL),
+    # M == 0: valid, returns before any launch
+    (dict(M=0), _lib.NQ_OK),
+    (dict(M=0, mode=1, wy=1), _lib.NQ_OK),
+    (dict(M=0, r=0), _lib.NQ_OK),
+])
+def test_validation(over, want):
+    assert call(**over) == want
+
+
+def test_probe_validation():
+    assert _lib.nq_convert_probe(9, 0x1000, 4, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
+    assert _lib.nq_convert_probe(0, 0x1000, -1, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
+    assert _lib.nq_convert_probe(0, 0, 4, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
+    assert _lib.nq_convert_probe(0, 0x1000, 0, 1.0, 0x2000, 0) == _lib.NQ_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

@@ -1,0 +1,101 @@
+"""The kernel's own device conversions (through nq_convert_probe) against the
+oracle's encoders: every rounding tie of every fp32 binade with its two
+neighbours plus random patterns for the format encoders, every 16-bit y for
+the static FP8 quant step, and tie-heavy amax values for the NVFP4 block
+scale."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_activation_quant_amd import _lib
+from tests.test_oracle_formats import _tie_heavy_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.lib()
+
+
+def probe(kind, patterns_u32, param=0.0):
+    dev = torch.device("cuda")
+    inp = torch.from_numpy(patterns_u32.astype(np.uint32).view(np.int32)).to(dev)
+    n = inp.numel()
+    width = 2 if kind in (2, 3) else 1
+    out = torch.full((n * width + 64,), 0xA5, dtype=torch.uint8, device=dev)
+    st = _lib.nq_convert_probe(kind, inp.data_ptr(), n, param, out.data_ptr(), 0)
+    assert st == _lib.NQ_OK
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[n * width:] == 0xA5)
+    o = o[: n * width]
+    return o.view(np.uint16) if width == 2 else o
+
+
+def _mismatch(got, want, inputs):
+    bad = np.nonzero(got != want)[0]
+    return bad.size, [(hex(int(inputs.view(np.uint32)[i])), hex(int(got[i])), hex(int(want[i]))) for i in bad[:6]]
+
+
+def test_e4m3_encoder():
+    v = _tie_heavy_f32(n_random=1_000_000)
+    got = probe(0, v.view(np.uint32))
+    want = O.encode(np.clip(v, -448, 448).astype(np.float64), O.E4M3FN)
+    n, ex = _mismatch(got, want, v)
+    assert n == 0, ex
+
+
+def test_e2m1_encoder():
+    v = _tie_heavy_f32(n_random=1_000_000)
+    got = probe(1, v.view(np.uint32))
+    want = O.encode(np.clip(v, -6, 6).astype(np.float64), O.E2M1)
+    n, ex = _mismatch(got, want, v)
+    assert n == 0, ex
+
+
+@pytest.mark.parametrize("kind,fmt", [(2, O.BF16), (3, O.FP16)])
+def test_half_rounding(kind, fmt):
+    v = _tie_heavy_f32(n_random=1_000_000)
+    got = probe(kind, v.view(np.uint32))
+    want = O.f64_to_bits(v.astype(np.float64), fmt)
+    n, ex = _mismatch(got, want, v)
+    assert n == 0, ex
+
+
+SCALES = [0.05, 7.0, 0.9, 1.0, 2.0 ** -20, 3.0e4, 0.0560825876891613, 0.01666259765625,
+          0.0157645083963871, 1.0 / 3.0, 0.0371]
+
+
+@pytest.mark.parametrize("kind,fmt", [(4, O.BF16), (5, O.FP16)])
+def test_fp8_quant_step_every_16bit_y(kind, fmt):
+    """All 65536 patterns of y (NaN/Inf excluded) for several scales,
+    including the workloads' calibrated ones."""
+    codes = np.arange(1 << 16, dtype=np.uint32)
+    yv = O.decode(codes, fmt)
+    ok = np.isfinite(yv)
+    codes = codes[ok]
+    rng = np.random.default_rng(3)
+    scales = SCALES + list(rng.uniform(1e-3, 10, 8))
+    for s in scales:
+        s32 = float(np.float32(s))
+        got = probe(kind, codes, s32)
+        want = O.quant_fp8_static(codes.astype(np.uint16)[None, :], fmt, s32)[0]
+        n, ex = _mismatch(got, want, codes)
+        assert n == 0, (s32, ex)
+
+
+@pytest.mark.parametrize("gs", [1.0, 441.1076965332031, 360.0879211425781, 1e5, 1.0 / 7.0])
+def test_nvfp4_block_scale_step(gs):
+    v = _tie_heavy_f32(exp_lo=-30, exp_hi=30, n_random=200_000)
+    v = np.abs(v)
+    got = probe(6, v.view(np.uint32), gs)
+    gs32 = np.float32(gs)
+    u = np.minimum(gs32 * (v / np.float32(6)), np.float32(448))
+    want = O.encode(u.astype(np.float64), O.E4M3FN)
+    n, ex = _mismatch(got, want, v)
+    assert n == 0, ex

@@ -1,0 +1,211 @@
+"""GPU parity: the HIP op against the CPU oracle, through the C ABI.
+
+Every workload runs at its full size in the launch configuration the
+benchmark uses; the oracle checks a row sample (rows are independent) and
+cheap whole-tensor properties cover the rest (residual == x + residual by
+torch's CPU add, guard bytes, untouched scale padding).  Edge cases cover
+ragged tiles, the scalar path (H % 16 != 0, unaligned views), both chunk
+counts per thread, residual=None, write_y off, special values, M == 0,
+determinism and argument errors.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_activation_quant_amd import _lib, ops
+from fp4_activation_quant_amd.workloads import WORKLOADS, make_inputs, load_scale
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.lib()  # the HIP library must be there: no fallback
+
+
+def _run_and_compare(x, r, w, eps, scale, nvfp4, write_y, rows=None, misalign=False):
+    r_in = r.clone() if r is not None else None
+    gpu = P.run_gpu(x, r_in, w, eps, scale, nvfp4, write_y, misalign=misalign)
+    y_gpu = None
+    if not write_y:
+        # The same kernel arithmetic with y written, for the quant-step check.
+        y_gpu = P.run_gpu(x, r.clone() if r is not None else None, w, eps, scale, nvfp4, True,
+                          misalign=misalign)["y"]
+    M = x.shape[0]
+    rows = P.sample_rows(M) if rows is None else rows
+    rep = P.compare(gpu, x, r, w, eps, scale, rows, y_gpu=y_gpu)
+    if r is not None:
+        rep["residual_full_mismatch"] = int(np.count_nonzero(gpu["residual"] != P.bits16(x + r)))
+        assert rep["residual_full_mismatch"] == 0
+    print(rep, flush=True)
+    return P.check(rep), gpu
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_parity(name):
+    wl = WORKLOADS[name]
+    print(f"workload {name}", flush=True)
+    x, r, w = make_inputs(wl)
+    extra = ()
+    if wl.row_outliers:
+        big = (x.float().abs().amax(dim=1) > 20).nonzero().flatten().tolist()
+        extra = big
+    rows = P.sample_rows(wl.M, extra=extra)
+    _run_and_compare(x, r, w, wl.eps, load_scale(wl), wl.nvfp4, wl.write_y, rows=rows)
+
+
+EDGE = [
+    # dtype, nvfp4, M, H, residual, write_y
+    (torch.bfloat16, False, 1, 64, True, True),
+    (torch.bfloat16, False, 127, 2048, True, True),
+    (torch.bfloat16, False, 129, 5120, False, False),
+    (torch.bfloat16, False, 300, 80, True, True),        # H % 16 != 0: scalar path
+    (torch.bfloat16, False, 65, 1000, True, False),      # scalar path
+    (torch.bfloat16, False, 3, 16384, True, True),       # 1024 threads
+    (torch.bfloat16, False, 5, 20480, True, True),       # 2 chunks per thread
+    (torch.float16, False, 257, 4096, True, True),
+    (torch.bfloat16, True, 1, 64, True, True),
+    (torch.bfloat16, True, 127, 128, True, True),
+    (torch.bfloat16, True, 129, 2048, True, False),
+    (torch.bfloat16, True, 257, 4096, False, True),
+    (torch.bfloat16, True, 130, 16384, True, True),
+    (torch.bfloat16, True, 3, 32768, True, True),        # 2 chunks per thread
+    (torch.float16, True, 200, 5120, True, True),
+    (torch.float16, True, 64, 192, False, False),
+]
+
+
+@pytest.mark.parametrize("dt,nvfp4,M,H,res,wy", EDGE)
+def test_edge_shapes(dt, nvfp4, M, H, res, wy):
+    print(f"edge {dt} nvfp4={nvfp4} M={M} H={H} res={res} write_y={wy}", flush=True)
+    g = torch.Generator().manual_seed(M * 7919 + H)
+    x = torch.randn(M, H, generator=g).to(dt)
+    r = (torch.randn(M, H, generator=g) * 2).to(dt) if res else None
+    w = (torch.randn(H, generator=g) * 0.2).to(dt)
+    scale = 0.03 if not nvfp4 else 448 * 6 / 5.0
+    _run_and_compare(x, r, w, 1e-6, scale, nvfp4, wy)
+
+
+@pytest.mark.parametrize("nvfp4", [False, True])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_unaligned_views_take_the_scalar_path(nvfp4, dt):
+    print(f"unaligned nvfp4={nvfp4} {dt}", flush=True)
+    g = torch.Generator().manual_seed(99)
+    M, H = 70, 256
+    x = torch.randn(M, H, generator=g).to(dt)
+    r = torch.randn(M, H, generator=g).to(dt)
+    w = (torch.randn(H, generator=g) * 0.2).to(dt)
+    _run_and_compare(x, r, w, 1e-6, 0.02 if not nvfp4 else 300.0, nvfp4, True, misalign=True)
+
+
+def _special_rows(H, dt):
+    rows = [
+        torch.zeros(H),                                   # zero row (eps > 0 -> y = 0)
+        torch.full((H,), 3.0),                            # constant row
+        torch.full((H,), -2.0 ** -10),                    # small constant
+        torch.linspace(-1000, 1000, H),                   # wide range
+        torch.where(torch.arange(H) % 2 == 0, 1e4, -1e-3),
+    ]
+    return torch.stack(rows).to(dt)
+
+
+@pytest.mark.parametrize("nvfp4", [False, True])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_special_values(nvfp4, dt):
+    print(f"special nvfp4={nvfp4} {dt}", flush=True)
+    H = 256
+    x = _special_rows(H, dt)
+    w = torch.linspace(-1.0, 1.0, H).to(dt)
+    w[::7] = -1.0                                          # 1 + w == 0 columns
+    # FP8: a tiny scale saturates most codes; NVFP4: a large global scale
+    # saturates the block scales.
+    for scale in ((1e-3, 0.5) if not nvfp4 else (1e5, 2.0)):
+        _run_and_compare(x, None, w, 1e-5, scale, nvfp4, True)
+        _run_and_compare(x, torch.flip(x, [0]).contiguous(), w, 1e-5, scale, nvfp4, True)
+
+
+def test_empty_batch_launches_nothing():
+    dev = torch.device("cuda")
+    for nvfp4 in (False, True):
+        x = torch.empty(0, 128, dtype=torch.bfloat16, device=dev)
+        w = torch.zeros(128, dtype=torch.bfloat16, device=dev)
+        s = torch.ones(1, dtype=torch.float32, device=dev)
+        q, bs, y = ops.gemma_add_rms_norm_quant(x, x.clone(), w, 1e-6, s, nvfp4, True)
+        assert q.shape[0] == 0 and y.shape == (0, 128)
+        # raw call with M = 0 on live buffers writes nothing
+        buf = torch.full((4096,), P.SENTINEL, dtype=torch.uint8, device=dev)
+        st = _lib.nq_gemma_add_rms_norm_quant(
+            buf.data_ptr(), buf.data_ptr() + 1024, w.data_ptr(), 1e-6, s.data_ptr(), 0, 128, 0,
+            int(nvfp4), 1, buf.data_ptr() + 2048, buf.data_ptr() + 3072, buf.data_ptr() + 3584, 0)
+        torch.cuda.synchronize()
+        assert st == _lib.NQ_OK and bool((buf == P.SENTINEL).all())
+
+
+def test_deterministic_across_runs():
+    wl = WORKLOADS["nvfp4_prefill_m8192_h4096_bf16_y"]
+    x, r, w = make_inputs(wl)
+    a = P.run_gpu(x, r.clone(), w, wl.eps, load_scale(wl), True, True)
+    b = P.run_gpu(x, r.clone(), w, wl.eps, load_scale(wl), True, True)
+    for k in ("residual", "y", "q", "bs"):
+        assert np.array_equal(a[k], b[k]), k
+    wl = WORKLOADS["fp8_res_m4096_h5120_fp16"]
+    x, r, w = make_inputs(wl)
+    a = P.run_gpu(x, r.clone(), w, wl.eps, load_scale(wl), False, True)
+    b = P.run_gpu(x, r.clone(), w, wl.eps, load_scale(wl), False, True)
+    for k in ("residual", "y", "q"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_invalid_arguments_write_nothing():
+    dev = torch.device("cuda")
+    M, H = 4, 128
+    buf = torch.full((1 << 16,), P.SENTINEL, dtype=torch.uint8, device=dev)
+    s = torch.ones(1, dtype=torch.float32, device=dev)
+    p = buf.data_ptr()
+    x, r, w, q, bs, y = p, p + 4096, p + 8192, p + 12288, p + 16384, p + 24576
+    call = _lib.nq_gemma_add_rms_norm_quant
+    cases = [
+        (dict(x=0), _lib.NQ_EINVAL),
+        (dict(w=0), _lib.NQ_EINVAL),
+        (dict(s=0), _lib.NQ_EINVAL),
+        (dict(q=0), _lib.NQ_EINVAL),
+        (dict(M=-1), _lib.NQ_EINVAL),
+        (dict(H=0), _lib.NQ_EINVAL),
+        (dict(dtype=2), _lib.NQ_EINVAL),
+        (dict(mode=2), _lib.NQ_EINVAL),
+        (dict(wy=1, y=0), _lib.NQ_EINVAL),
+        (dict(mode=1, bs=0), _lib.NQ_EINVAL),
+        (dict(mode=1, H=80), _lib.NQ_EUNSUPPORTED),
+        (dict(r=p), _lib.NQ_EINVAL),                 # residual aliases x
+        (dict(q=p + 4096 + 512), _lib.NQ_EINVAL),    # q overlaps residual
+    ]
+    for over, want in cases:
+        a = dict(x=x, r=r, w=w, s=s.data_ptr(), M=M, H=H, dtype=0, mode=0, wy=0, q=q, bs=bs, y=y)
+        a.update(over)
+        st = call(a["x"], a["r"], a["w"], 1e-6, a["s"], a["M"], a["H"], a["dtype"], a["mode"],
+                  a["wy"], a["q"], a["bs"], a["y"], 0)
+        assert st == want, (over, st)
+    torch.cuda.synchronize()
+    assert bool((buf == P.SENTINEL).all())
+
+
+def test_runs_on_the_callers_stream():
+    wl = WORKLOADS["fp8_m16_h2048_bf16_y"]
+    x, r, w = make_inputs(wl)
+    dev = torch.device("cuda")
+    s = torch.tensor([load_scale(wl)], dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    xd, rd, wd = x.to(dev), r.to(dev), w.to(dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        q, _, y = ops.gemma_add_rms_norm_quant(xd, rd, wd, wl.eps, s, False, True)
+    side.synchronize()
+    ref = O.gemma_add_rms_norm_quant(P.bits16(x), P.bits16(r), P.bits16(w), wl.eps, load_scale(wl),
+                                     False, True, O.BF16)
+    assert np.array_equal(P.bits16(rd), ref["residual"])
+    assert np.max(np.abs(P._ord16(P.bits16(y)) - P._ord16(ref["y"]))) <= 1
