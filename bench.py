@@ -55,7 +55,7 @@ def kernel_sha():
 def kernel_name(wl):
     return "fused_rows<{},{},{},{},{}>".format(
         wl.dtype, "nvfp4" if wl.nvfp4 else "fp8", "res" if wl.has_residual else "nores",
-        "y" if wl.write_y else "noy", 1 if wl.H // 16 <= 1024 else 2)
+        "y" if wl.write_y else "noy", 1 if wl.H <= 4096 else (2 if wl.H // 8 <= 2048 else 4))
 
 
 def measured_traffic(wl):
@@ -99,6 +99,26 @@ def cpu_baseline(wl, x, r, w, scale, budget_s):
             "sample": f"first {rows} of {wl.M} rows of {wl.name}, {dt:.1f} s, numpy single-threaded"}
 
 
+def copy_calibration(args):
+    """Known-size plain copy: each launch reads and writes MIB MiB."""
+    import torch
+    n = args.copy_calibration << 20
+    dev = torch.device("cuda:0")
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "steps": args.steps,
+                      "ms_per_copy": round(dt * 1e3, 5), "GBps": round(2 * n / dt / 1e9, 2)}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +127,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the op, time torch's device copy of MIB MiB (the plain "
+                         "copy kernel used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the op is row-independent and this build has no "
@@ -117,6 +140,8 @@ def main():
     from fp4_activation_quant_amd import _lib, ops
     from fp4_activation_quant_amd.workloads import WORKLOADS, DEFAULT_BENCH, make_inputs, load_scale
 
+    if args.copy_calibration:
+        return copy_calibration(args)
     _lib.lib()
     wl = WORKLOADS[args.workload or DEFAULT_BENCH]
     dev = torch.device("cuda:0")

@@ -9,16 +9,21 @@
 // the unfused chain; this file does the same.
 //
 // Design (memory-bound; no MFMA -- nothing here is a contraction):
-//  * One thread owns a "chunk" of 16 consecutive elements of a row: two
-//    128-bit loads per input tensor, two 128-bit stores per 16-bit output,
-//    one 128-bit (FP8) or 64-bit (NVFP4) code store.  A chunk is exactly one
-//    NVFP4 block, so the block amax needs no cross-lane step.
-//  * A workgroup owns a row at a time (round_up(H/16, 64) threads, up to
-//    1024, 1-2 chunks per thread, so H <= 32768 on this path) and strides
-//    over rows; the weight's (1 + w) lives in registers across rows.  Sum of squares: in-register fp32
-//    FMA chain, wavefront butterfly, one LDS slot per wave, one barrier per
-//    row (the LDS slots are double-buffered by row parity so no second
-//    barrier is needed).
+//  * One workgroup per row, grid = M (measured faster than a persistent grid
+//    on this chip: more independent rows in flight and no row loop).  A
+//    thread owns 8-element chunks (16 bytes) at chunk index tid, tid + nthr,
+//    ..., so every load and store instruction of a wave covers contiguous
+//    memory: 1 KB of x / residual / y, 512 B of FP8 codes, 256 B of FP4 codes.
+//    1, 2 or 4 chunks per thread (H <= 4096, <= 16384, <= 32768).
+//  * x and residual are streamed with non-temporal loads, all outputs with
+//    non-temporal stores; the weight is a plain (L2-cached) load.  All loads
+//    of a row are issued before the first wait.
+//  * Sum of squares: fp32 FMA chain per thread, DPP butterfly inside each
+//    16-lane row plus readlane across rows, one LDS slot per wave, one
+//    barrier per row.
+//  * An NVFP4 block (16 elements) is the chunk pair held by two adjacent
+//    lanes; the block amax is combined with a DPP lane swap and the even lane
+//    stores the block's scale byte at its 128x4-tiled offset.
 //  * The per-element quant arithmetic is IEEE fp32 (correctly rounded
 //    division, no contraction: the file is built with -ffp-contract=off) and
 //    the format conversions are the gfx950 hardware ones: v_cvt_pk_bf16_f32 /
@@ -26,12 +31,11 @@
 //    clamp to +-448, v_cvt_scalef32_pk_fp4_f32 with unit scale after a clamp
 //    to +-6.  Their semantics are checked exhaustively against the CPU oracle
 //    through nq_convert_probe.
-//  * Shapes or pointers the vector path cannot take (H % 16 != 0, unaligned
-//    views) go to a scalar kernel with the same arithmetic.
+//  * Shapes or pointers the vector path cannot take (H % 16 != 0, H > 32768,
+//    unaligned views) go to a scalar kernel with the same arithmetic.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "gemma_norm_quant.h"
 
@@ -43,7 +47,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kChunk = 16;        // elements per thread chunk == NVFP4 block
+constexpr int kVec = 8;           // elements per thread chunk (16 bytes)
+constexpr int kBlock = 16;        // elements per NVFP4 block scale
 constexpr int kWave = 64;
 constexpr int kMaxThreads = 1024;
 constexpr float kE4M3Max = 448.0f;
@@ -122,14 +127,37 @@ __device__ __forceinline__ size_t swz128x4(int64_t m, int b, int ktiles) {
          (size_t)((m >> 5) & 3) * 4u + (size_t)(b & 3);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, false));
+}
+
+// Value of the neighbouring lane (lane ^ 1): DPP quad_perm [1, 0, 3, 2].
+__device__ __forceinline__ float dpp_swap_adjacent(float v) { return dpp<0xB1>(v); }
+
+// Sum over the 64 lanes of a wave (all lanes active), returned to every lane:
+// DPP exchanges inside each 16-lane row (lane ^ 1, lane ^ 2, 8-lane mirror,
+// 16-lane mirror), then the four row totals via readlane.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  const int b = __builtin_bit_cast(int, v);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
 }
 
 // ----------------------------------------------------------------------------
-// Vector kernel: one workgroup per row at a time, CPT chunks of 16 per thread.
+// Vector kernel.  A workgroup normalises one row (grid = M; the row loop only
+// runs more than once if M exceeds the grid limit).  A chunk is 8 elements
+// (16 bytes of x's dtype); thread t owns chunks t, t + nthr, ... (CPT of
+// them), so each load/store instruction of a wave covers 1 KB of contiguous
+// 16-bit data.  An NVFP4 block is the chunk pair (2j, 2j+1), held by two
+// adjacent lanes of one wave; their amax is combined with a DPP lane swap.
 template <class D, bool NVFP4, bool HAS_RES, bool WRITE_Y, int CPT>
 __global__ void __launch_bounds__(kMaxThreads)
 fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__restrict__ w,
@@ -139,59 +167,45 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int nwaves = nthr / kWave;
-  const float Hf = (float)(nchunk * kChunk);
-
-  // (1 + w) for this thread's chunks, kept for every row.
-  float g[CPT][kChunk];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int ch = tid + c * nthr;
-    if (ch < nchunk) {
-      const u32x4 wa = w[2 * ch], wb = w[2 * ch + 1];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        g[c][2 * k] = 1.0f + D::lo(wa[k]);
-        g[c][2 * k + 1] = 1.0f + D::hi(wa[k]);
-        g[c][8 + 2 * k] = 1.0f + D::lo(wb[k]);
-        g[c][8 + 2 * k + 1] = 1.0f + D::hi(wb[k]);
-      }
-    }
-  }
-  const float s = *scale_ptr;
-
+  const float Hf = (float)(nchunk * kVec);
   int parity = 0;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x, parity ^= 1) {
-    const size_t rbase = (size_t)row * (size_t)nchunk * 2;
-    uint32_t hb[CPT][8];
+    const size_t rbase = (size_t)row * (size_t)nchunk;
+    // All loads first: x and residual stream from HBM (non-temporal), the
+    // weight comes from L2.
+    u32x4 xa[CPT], ra[CPT], wa[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * nthr;
+      if (ch < nchunk) {
+        xa[c] = __builtin_nontemporal_load(&x[rbase + ch]);
+        if constexpr (HAS_RES) ra[c] = __builtin_nontemporal_load(&res[rbase + ch]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * nthr;
+      if (ch < nchunk) wa[c] = w[ch];
+    }
+    // h = RN(x + r), written back; sum of squares of the rounded h.
+    uint32_t hb[CPT][4];
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * nthr;
       if (ch < nchunk) {
-        const size_t i0 = rbase + 2 * (size_t)ch;
-        const u32x4 xa = __builtin_nontemporal_load(&x[i0]);
-        const u32x4 xb = __builtin_nontemporal_load(&x[i0 + 1]);
         if constexpr (HAS_RES) {
-          const u32x4 ra = __builtin_nontemporal_load(&res[i0]);
-          const u32x4 rb = __builtin_nontemporal_load(&res[i0 + 1]);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            hb[c][k] = D::pack(D::lo(xa[k]) + D::lo(ra[k]), D::hi(xa[k]) + D::hi(ra[k]));
-            hb[c][4 + k] = D::pack(D::lo(xb[k]) + D::lo(rb[k]), D::hi(xb[k]) + D::hi(rb[k]));
-          }
-          u32x4 oa = {hb[c][0], hb[c][1], hb[c][2], hb[c][3]};
-          u32x4 ob = {hb[c][4], hb[c][5], hb[c][6], hb[c][7]};
-          __builtin_nontemporal_store(oa, &res[i0]);
-          __builtin_nontemporal_store(ob, &res[i0 + 1]);
+          for (int k = 0; k < 4; ++k)
+            hb[c][k] = D::pack(D::lo(xa[c][k]) + D::lo(ra[c][k]), D::hi(xa[c][k]) + D::hi(ra[c][k]));
+          const u32x4 o = {hb[c][0], hb[c][1], hb[c][2], hb[c][3]};
+          __builtin_nontemporal_store(o, &res[rbase + ch]);
         } else {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            hb[c][k] = xa[k];
-            hb[c][4 + k] = xb[k];
-          }
+          for (int k = 0; k < 4; ++k) hb[c][k] = xa[c][k];
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 4; ++k) {
           const float a = D::lo(hb[c][k]), b = D::hi(hb[c][k]);
           ss = __builtin_fmaf(a, a, ss);
           ss = __builtin_fmaf(b, b, ss);
@@ -204,48 +218,46 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
     float tot = 0.0f;
     for (int i = 0; i < nwaves; ++i) tot += partial[parity][i];
     const float rstd = 1.0f / __builtin_sqrtf(tot / Hf + eps);
+    const float s = *scale_ptr;
 
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * nthr;
       if (ch < nchunk) {
-        float yv[kChunk];
-        uint32_t yb[8];
+        // y = RN((h * rstd) * (1 + w)); the quant reads the rounded y.
+        float yv[kVec];
+        uint32_t yb[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float a = (D::lo(hb[c][k]) * rstd) * g[c][2 * k];
-          const float b = (D::hi(hb[c][k]) * rstd) * g[c][2 * k + 1];
+        for (int k = 0; k < 4; ++k) {
+          const float a = (D::lo(hb[c][k]) * rstd) * (1.0f + D::lo(wa[c][k]));
+          const float b = (D::hi(hb[c][k]) * rstd) * (1.0f + D::hi(wa[c][k]));
           yb[k] = D::pack(a, b);
           yv[2 * k] = D::lo(yb[k]);
           yv[2 * k + 1] = D::hi(yb[k]);
         }
-        const size_t i0 = rbase + 2 * (size_t)ch;
         if constexpr (WRITE_Y) {
-          u32x4 oa = {yb[0], yb[1], yb[2], yb[3]};
-          u32x4 ob = {yb[4], yb[5], yb[6], yb[7]};
-          __builtin_nontemporal_store(oa, &y[i0]);
-          __builtin_nontemporal_store(ob, &y[i0 + 1]);
+          const u32x4 o = {yb[0], yb[1], yb[2], yb[3]};
+          __builtin_nontemporal_store(o, &y[rbase + ch]);
         }
         if constexpr (NVFP4) {
           float amax = 0.0f;
 #pragma unroll
-          for (int k = 0; k < kChunk; ++k) amax = fmaxf(amax, fabsf(yv[k]));
+          for (int k = 0; k < kVec; ++k) amax = fmaxf(amax, fabsf(yv[k]));
+          amax = fmaxf(amax, dpp_swap_adjacent(amax));
           const uint32_t sc = nvfp4_scale_code(amax, s);
           const float o = nvfp4_elem_scale(sc, s);
-          float v[kChunk];
+          float v[kVec];
 #pragma unroll
-          for (int k = 0; k < kChunk; ++k) v[k] = yv[k] * o;
-          u32x2 packed = {e2m1x8(v), e2m1x8(v + 8)};
-          u32x2 *qp = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8) + ch;
-          __builtin_nontemporal_store(packed, qp);
-          bs[swz128x4(row, ch, ktiles)] = (uint8_t)sc;
+          for (int k = 0; k < kVec; ++k) v[k] = yv[k] * o;
+          uint32_t *qp = reinterpret_cast<uint32_t *>(q + (size_t)row * (size_t)nchunk * 4) + ch;
+          __builtin_nontemporal_store(e2m1x8(v), qp);
+          if ((ch & 1) == 0) bs[swz128x4(row, ch >> 1, ktiles)] = (uint8_t)sc;
         } else {
-          float v[kChunk];
+          float v[kVec];
 #pragma unroll
-          for (int k = 0; k < kChunk; ++k) v[k] = yv[k] / s;
-          u32x4 packed = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7]),
-                          e4m3x4(v[8], v[9], v[10], v[11]), e4m3x4(v[12], v[13], v[14], v[15])};
-          u32x4 *qp = reinterpret_cast<u32x4 *>(q + (size_t)row * (size_t)nchunk * 16) + ch;
+          for (int k = 0; k < kVec; ++k) v[k] = yv[k] / s;
+          const u32x2 packed = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
+          u32x2 *qp = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8) + ch;
           __builtin_nontemporal_store(packed, qp);
         }
       }
@@ -287,22 +299,22 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
     const uint16_t *hsrc = HAS_RES ? res : x;
     if constexpr (NVFP4) {
       // Blocks of 16 read h written by other threads before the barrier.
-      const int nb = H / kChunk;
+      const int nb = H / kBlock;
       for (int b = tid; b < nb; b += blockDim.x) {
-        float yv[kChunk];
-        for (int k = 0; k < kChunk; ++k) {
-          const int j = b * kChunk + k;
+        float yv[kBlock];
+        for (int k = 0; k < kBlock; ++k) {
+          const int j = b * kBlock + k;
           const float yy = (D::lo(hsrc[rb + j]) * rstd) * (1.0f + D::lo(w[j]));
           const uint32_t yq = D::pack(yy, 0.0f) & 0xffffu;
           if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
           yv[k] = D::lo(yq);
         }
         float amax = 0.0f;
-        for (int k = 0; k < kChunk; ++k) amax = fmaxf(amax, fabsf(yv[k]));
+        for (int k = 0; k < kBlock; ++k) amax = fmaxf(amax, fabsf(yv[k]));
         const uint32_t sc = nvfp4_scale_code(amax, s);
         const float o = nvfp4_elem_scale(sc, s);
-        float v[kChunk];
-        for (int k = 0; k < kChunk; ++k) v[k] = yv[k] * o;
+        float v[kBlock];
+        for (int k = 0; k < kBlock; ++k) v[k] = yv[k] * o;
         const uint32_t p0 = e2m1x8(v), p1 = e2m1x8(v + 8);
         uint8_t *qp = q + (size_t)row * (size_t)(H / 2) + (size_t)b * 8;
         for (int k = 0; k < 4; ++k) {
@@ -349,30 +361,6 @@ __global__ void convert_probe(int kind, const uint32_t *__restrict__ in, int64_t
 // ----------------------------------------------------------------------------
 // Host side.
 
-int device_cus() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  static int cached[64] = {0};
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  if (dev >= 0 && dev < 64) cached[dev] = cus;
-  return cus;
-}
-
-// Rows in flight per CU for the persistent grid (tuning override:
-// GNQ_WG_PER_CU; 0 = one workgroup per row).
-int wg_per_cu_setting() {
-  static int v = -1;
-  if (v < 0) {
-    const char *e = getenv("GNQ_WG_PER_CU");
-    v = e ? atoi(e) : 8;
-    if (v < 0) v = 0;
-  }
-  return v;
-}
-
 template <class D, bool NV, bool RES, bool WY, int CPT>
 hipError_t launch_vec(dim3 grid, dim3 block, hipStream_t st, const void *x, void *res, const void *w,
                       const float *scale, float eps, int64_t M, int nchunk, void *q, void *bs,
@@ -381,15 +369,6 @@ hipError_t launch_vec(dim3 grid, dim3 block, hipStream_t st, const void *x, void
                      (const u32x4 *)x, (u32x4 *)res, (const u32x4 *)w, scale, eps, M, nchunk,
                      (uint8_t *)q, (uint8_t *)bs, (u32x4 *)y, ktiles);
   return hipGetLastError();
-}
-
-template <class D, bool NV, bool RES, bool WY>
-hipError_t dispatch_cpt(int cpt, dim3 grid, dim3 block, hipStream_t st, const void *x, void *res,
-                        const void *w, const float *scale, float eps, int64_t M, int nchunk,
-                        void *q, void *bs, void *y, int ktiles) {
-  if (cpt == 1)
-    return launch_vec<D, NV, RES, WY, 1>(grid, block, st, x, res, w, scale, eps, M, nchunk, q, bs, y, ktiles);
-  return launch_vec<D, NV, RES, WY, 2>(grid, block, st, x, res, w, scale, eps, M, nchunk, q, bs, y, ktiles);
 }
 
 template <class D, bool NV, bool RES, bool WY>
@@ -416,33 +395,42 @@ struct Args {
   hipStream_t st;
 };
 
+constexpr int64_t kMaxGrid = ((int64_t)1 << 31) - 1;
+
+// Chunks per thread for the vector kernel: one 8-element chunk per thread up
+// to H = 4096 (short per-thread chains for latency), two up to H = 16384,
+// four up to H = 32768 (at most 1024 threads per workgroup).
+int chunks_per_thread(int64_t H) {
+  const int64_t nchunk = H / kVec;
+  if (H <= 4096) return 1;
+  if (nchunk <= 2 * kMaxThreads) return 2;
+  return 4;
+}
+
 template <class D, bool NV, bool RES, bool WY>
 hipError_t run(const Args &a) {
-  const int ktiles = (int)(((a.H / kChunk) + 3) / 4);
-  const int cus = device_cus();
-  const int per_cu = wg_per_cu_setting();
+  const int ktiles = (int)(((a.H / kBlock) + 3) / 4);
   auto aligned = [](const void *p, uintptr_t n) { return p == nullptr || ((uintptr_t)p % n) == 0; };
-  const bool vec = (a.H % kChunk == 0) && (a.H / kChunk) <= 2 * kMaxThreads && aligned(a.x, 16) &&
+  const bool vec = (a.H % kBlock == 0) && (a.H / kVec) <= 4 * kMaxThreads && aligned(a.x, 16) &&
                    aligned(a.res, 16) && aligned(a.w, 16) && aligned(a.y, 16) &&
-                   aligned(a.q, NV ? 8 : 16);
+                   aligned(a.q, NV ? 4 : 8);
+  const dim3 grid((unsigned)(a.M < kMaxGrid ? a.M : kMaxGrid));
   if (vec) {
-    const int nchunk = (int)(a.H / kChunk);
-    const int cpt = nchunk <= kMaxThreads ? 1 : 2;
+    const int nchunk = (int)(a.H / kVec);
+    const int cpt = chunks_per_thread(a.H);
     const int per_thread = (nchunk + cpt - 1) / cpt;
-    const int threads = ((per_thread + kWave - 1) / kWave) * kWave;
-    int64_t g = a.M;
-    if (per_cu > 0) {
-      const int64_t cap = (int64_t)cus * per_cu;
-      if (g > cap) g = cap;
-    }
-    return dispatch_cpt<D, NV, RES, WY>(cpt, dim3((unsigned)g), dim3(threads), a.st, a.x, a.res,
-                                        a.w, a.scale, a.eps, a.M, nchunk, a.q, a.bs, a.y, ktiles);
+    const dim3 block(((per_thread + kWave - 1) / kWave) * kWave);
+    if (cpt == 1)
+      return launch_vec<D, NV, RES, WY, 1>(grid, block, a.st, a.x, a.res, a.w, a.scale, a.eps, a.M,
+                                           nchunk, a.q, a.bs, a.y, ktiles);
+    if (cpt == 2)
+      return launch_vec<D, NV, RES, WY, 2>(grid, block, a.st, a.x, a.res, a.w, a.scale, a.eps, a.M,
+                                           nchunk, a.q, a.bs, a.y, ktiles);
+    return launch_vec<D, NV, RES, WY, 4>(grid, block, a.st, a.x, a.res, a.w, a.scale, a.eps, a.M,
+                                         nchunk, a.q, a.bs, a.y, ktiles);
   }
-  int64_t g = a.M;
-  const int64_t cap = (int64_t)cus * 8;
-  if (g > cap) g = cap;
-  return launch_scalar<D, NV, RES, WY>(dim3((unsigned)g), a.st, a.x, a.res, a.w, a.scale, a.eps,
-                                       a.M, (int)a.H, a.q, a.bs, a.y, ktiles);
+  return launch_scalar<D, NV, RES, WY>(grid, a.st, a.x, a.res, a.w, a.scale, a.eps, a.M, (int)a.H,
+                                       a.q, a.bs, a.y, ktiles);
 }
 
 template <class D, bool NV>
@@ -474,9 +462,9 @@ const char *nq_status_string(int status) {
 }
 
 size_t nq_block_scale_bytes(int64_t M, int64_t H) {
-  if (M <= 0 || H < kChunk) return 0;
+  if (M <= 0 || H < kBlock) return 0;
   const int64_t rows = (M + 127) / 128 * 128;
-  const int64_t cols = ((H / kChunk) + 3) / 4 * 4;
+  const int64_t cols = ((H / kBlock) + 3) / 4 * 4;
   return (size_t)rows * (size_t)cols;
 }
 

@@ -4,8 +4,8 @@ Every workload runs at its full size in the launch configuration the
 benchmark uses; the oracle checks a row sample (rows are independent) and
 cheap whole-tensor properties cover the rest (residual == x + residual by
 torch's CPU add, guard bytes, untouched scale padding).  Edge cases cover
-ragged tiles, the scalar path (H % 16 != 0, unaligned views), both chunk
-counts per thread, residual=None, write_y off, special values, M == 0,
+ragged tiles, the scalar path (H % 16 != 0, H > 32768, unaligned views),
+1, 2 and 4 chunks per thread, residual=None, write_y off, special values, M == 0,
 determinism and argument errors.
 """
 
@@ -66,15 +66,19 @@ EDGE = [
     (torch.bfloat16, False, 129, 5120, False, False),
     (torch.bfloat16, False, 300, 80, True, True),        # H % 16 != 0: scalar path
     (torch.bfloat16, False, 65, 1000, True, False),      # scalar path
-    (torch.bfloat16, False, 3, 16384, True, True),       # 1024 threads
-    (torch.bfloat16, False, 5, 20480, True, True),       # 2 chunks per thread
+    (torch.bfloat16, False, 3, 16384, True, True),       # 2 chunks x 1024 threads
+    (torch.bfloat16, False, 5, 20480, True, True),       # 4 chunks per thread
+    (torch.bfloat16, False, 9, 4112, True, True),        # ragged: some threads own 1 chunk
+    (torch.bfloat16, False, 33, 48, True, True),         # 6 chunks, one partial wave
+    (torch.bfloat16, False, 2, 40000, True, True),       # H > 32768: scalar path
     (torch.float16, False, 257, 4096, True, True),
     (torch.bfloat16, True, 1, 64, True, True),
     (torch.bfloat16, True, 127, 128, True, True),
     (torch.bfloat16, True, 129, 2048, True, False),
     (torch.bfloat16, True, 257, 4096, False, True),
     (torch.bfloat16, True, 130, 16384, True, True),
-    (torch.bfloat16, True, 3, 32768, True, True),        # 2 chunks per thread
+    (torch.bfloat16, True, 3, 32768, True, True),        # 4 chunks x 1024 threads
+    (torch.bfloat16, True, 17, 4160, True, True),        # ragged 2-chunk split
     (torch.float16, True, 200, 5120, True, True),
     (torch.float16, True, 64, 192, False, False),
 ]
