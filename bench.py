@@ -6,7 +6,10 @@ A step is one launch of the whole op (add, norm, y, quant, scale store) over
 one batch of the workload, inputs resident in HBM.  The in-place residual
 update is part of the op; to keep the residual bounded over many steps the
 activation alternates between x and -x from step to step (same work, same
-bytes).  Prints one JSON line:
+bytes).  Buffer sets (inputs and outputs) rotate from step to step so that at
+least 2 GiB of distinct data pass between two uses of a set, which keeps the
+256 MB Infinity Cache from serving a step out of the previous ones.  Prints
+one JSON line:
 
   value        whole-job effective HBM GB/s: algorithmic bytes per step x K /
                wall time of the K steps (synchronised on both sides);
@@ -31,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 2 << 30
 METRIC = "effective HBM GB/s (and % of peak) + tokens/s for add-RMSNorm+quant, 1 GPU"
 KERNEL_SRC = os.path.join(ROOT, "fp4_activation_quant_amd", "csrc", "gemma_norm_quant.hip")
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
@@ -127,6 +131,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K launches in one HIP graph and time its replay")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the op, time torch's device copy of MIB MiB (the plain "
                          "copy kernel used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -149,48 +155,83 @@ def main():
     print(f"# workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
     x, r, w = make_inputs(wl)
     scale = load_scale(wl)
-    xs = [x.to(dev), (-x).to(dev)]
-    rd = r.to(dev) if r is not None else None
+    M, H = wl.M, wl.H
+    rbytes, wbytes = algorithmic_bytes(wl)
+    total = rbytes + wbytes
+    # Buffer sets rotated across steps so that the data a step touches is not
+    # left in the 256 MB Infinity Cache by the previous steps: at least
+    # ROTATE_BYTES of distinct inputs/outputs per rotation (at most 64 sets).
+    n_sets = max(1, min(64, -(-ROTATE_BYTES // total)))
     wd = w.to(dev)
     sd = torch.tensor([scale], dtype=torch.float32, device=dev)
-    M, H = wl.M, wl.H
-    if wl.nvfp4:
-        q = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
-        bs = torch.empty((ops.round_up(M, 128), ops.round_up(H // 16, 4)), dtype=torch.uint8, device=dev)
-    else:
-        q = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
-        bs = None
-    y = torch.empty_like(xs[0]) if wl.write_y else None
+    xp_cpu, xn_cpu = x, -x
+    sets = []
+    for _ in range(n_sets):
+        st = {"x": [xp_cpu.to(dev), xn_cpu.to(dev)],
+              "r": r.to(dev) if r is not None else None,
+              "y": torch.empty((M, H), dtype=x.dtype, device=dev) if wl.write_y else None}
+        if wl.nvfp4:
+            st["q"] = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+            st["bs"] = torch.empty((ops.round_up(M, 128), ops.round_up(H // 16, 4)),
+                                   dtype=torch.uint8, device=dev)
+        else:
+            st["q"] = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
+            st["bs"] = None
+        sets.append(st)
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
     def launch(i):
-        ops.gemma_add_rms_norm_quant_out(xs[i & 1], rd, wd, wl.eps, sd, wl.nvfp4, q, bs, y)
+        # Set i % n_sets; the activation's sign flips each time a set comes
+        # round again, so the in-place residual stays bounded.
+        st = sets[i % n_sets]
+        xi = st["x"][(i // n_sets) & 1]
+        ops.gemma_add_rms_norm_quant_out(xi, st["r"], wd, wl.eps, sd, wl.nvfp4, st["q"], st["bs"],
+                                         st["y"])
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             launch(i)
     torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"# warmup done ({args.warmup} steps, {n_sets} buffer sets); timing {args.steps} steps"
+          f" ({'graph' if args.graph else 'eager'})", file=sys.stderr, flush=True)
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        for i in range(args.steps):
-            ev[i][0].record(stream)
-            launch(i)
-            ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    if args.graph:
+        # The K launches captured once as a HIP graph and replayed: launch
+        # overhead off the critical path.  Kernel time = event span / K.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                launch(args.warmup + i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_ms = [e0.elapsed_time(e1) / args.steps]
+    else:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                ev[i][0].record(stream)
+                launch(args.warmup + i)
+                ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_ms = [a.elapsed_time(b) for a, b in ev]
     kern_ms.sort()
     avg_ms = sum(kern_ms) / len(kern_ms)
     med_ms = kern_ms[len(kern_ms) // 2]
 
-    rbytes, wbytes = algorithmic_bytes(wl)
-    total = rbytes + wbytes
     ms_per_step = wall * 1e3 / args.steps
     value = total / (ms_per_step * 1e-3) / 1e9
     achieved = total / (avg_ms * 1e-3) / 1e9
@@ -214,6 +255,8 @@ def main():
                    "bytes_written": wbytes},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
+        "launch": "graph" if args.graph else "eager",
+        "buffer_sets": n_sets,
         "kernel_ms": {"avg": round(avg_ms, 5), "median": round(med_ms, 5),
                       "min": round(kern_ms[0], 5), "max": round(kern_ms[-1], 5)},
         "roofline": {"bound": "hbm", "kernel": kernel_name(wl), "achieved": round(achieved, 2),

@@ -97,14 +97,33 @@ __device__ __forceinline__ uint32_t e4m3_one(float a) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clampf(a, kE4M3Max), 0.0f, 0, false) & 0xffu;
 }
 
-// Eight E2M1 codes (saturating, RNE), element 2k in the low nibble of byte k.
+// Eight E2M1 codes, element 2k in the low nibble of byte k.  The gfx950
+// conversion rounds to nearest even and saturates out-of-range magnitudes
+// (including infinities) to 6 by itself, so no clamp precedes it; the
+// exhaustive probe tests check it against clamp-then-round.
 __device__ __forceinline__ uint32_t e2m1x8(const float *v) {
   uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clampf(v[0], kE2M1Max), clampf(v[1], kE2M1Max), 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clampf(v[2], kE2M1Max), clampf(v[3], kE2M1Max), 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clampf(v[4], kE2M1Max), clampf(v[5], kE2M1Max), 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clampf(v[6], kE2M1Max), clampf(v[7], kE2M1Max), 1.0f, 3);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
   return w;
+}
+
+// fl32(y / s), correctly rounded, from r = fl32(1 / s) (one IEEE division
+// per thread instead of one per element).  q0 = fl(y * r) lies within 1.5
+// ulp of y / s; a correction step q + (y - q*s) * r (FMA, one rounding)
+// brings it within 1 ulp, and from there one more step gives the correctly
+// rounded quotient (Markstein's theorem: reciprocal within half an ulp,
+// quotient within one ulp, exact remainder).  The remainder is exact for
+// |y| >= 2^-103, i.e. for every scale >= 2^-90 wherever the FP8 code is not
+// zero.  Quotients beyond +-1024 saturate to +-448 either way; clamping them
+// between steps keeps every intermediate finite.  The remainder is formed as
+// q*s - y and subtracted, so a zero quotient keeps the sign of y.
+__device__ __forceinline__ float div_by_scale(float y, float s, float r) {
+  float q = clampf(y * r, 1024.0f);
+  q = clampf(__builtin_fmaf(-__builtin_fmaf(q, s, -y), r, q), 1024.0f);
+  return __builtin_fmaf(-__builtin_fmaf(q, s, -y), r, q);
 }
 
 // NVFP4 block scale: S = E4M3(min(gs * (amax / 6), 448)).
@@ -164,42 +183,49 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
            const float *__restrict__ scale_ptr, float eps, int64_t M, int nchunk,
            uint8_t *__restrict__ q, uint8_t *__restrict__ bs, u32x4 *__restrict__ y, int ktiles) {
   __shared__ float partial[2][kMaxThreads / kWave];
-  const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
+  const unsigned tid = threadIdx.x;
+  const unsigned nthr = blockDim.x;
+  const unsigned nch = (unsigned)nchunk;
   const int nwaves = nthr / kWave;
   const float Hf = (float)(nchunk * kVec);
   int parity = 0;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x, parity ^= 1) {
     const size_t rbase = (size_t)row * (size_t)nchunk;
+    const u32x4 *__restrict__ xr = x + rbase;
+    u32x4 *__restrict__ rr = res + rbase;
+    u32x4 *__restrict__ yr = y + rbase;
     // All loads first: x and residual stream from HBM (non-temporal), the
-    // weight comes from L2.
+    // weight and the scale come from L2.  The scale's reciprocal is formed
+    // while the row loads are in flight.
     u32x4 xa[CPT], ra[CPT], wa[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * nthr;
-      if (ch < nchunk) {
-        xa[c] = __builtin_nontemporal_load(&x[rbase + ch]);
-        if constexpr (HAS_RES) ra[c] = __builtin_nontemporal_load(&res[rbase + ch]);
+      const unsigned ch = tid + c * nthr;
+      if (ch < nch) {
+        xa[c] = __builtin_nontemporal_load(&xr[ch]);
+        if constexpr (HAS_RES) ra[c] = __builtin_nontemporal_load(&rr[ch]);
       }
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * nthr;
-      if (ch < nchunk) wa[c] = w[ch];
+      const unsigned ch = tid + c * nthr;
+      if (ch < nch) wa[c] = w[ch];
     }
+    const float s = *scale_ptr;
+    const float r_s = NVFP4 ? 0.0f : 1.0f / s;
     // h = RN(x + r), written back; sum of squares of the rounded h.
     uint32_t hb[CPT][4];
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * nthr;
-      if (ch < nchunk) {
+      const unsigned ch = tid + c * nthr;
+      if (ch < nch) {
         if constexpr (HAS_RES) {
 #pragma unroll
           for (int k = 0; k < 4; ++k)
             hb[c][k] = D::pack(D::lo(xa[c][k]) + D::lo(ra[c][k]), D::hi(xa[c][k]) + D::hi(ra[c][k]));
           const u32x4 o = {hb[c][0], hb[c][1], hb[c][2], hb[c][3]};
-          __builtin_nontemporal_store(o, &res[rbase + ch]);
+          __builtin_nontemporal_store(o, &rr[ch]);
         } else {
 #pragma unroll
           for (int k = 0; k < 4; ++k) hb[c][k] = xa[c][k];
@@ -218,26 +244,27 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
     float tot = 0.0f;
     for (int i = 0; i < nwaves; ++i) tot += partial[parity][i];
     const float rstd = 1.0f / __builtin_sqrtf(tot / Hf + eps);
-    const float s = *scale_ptr;
 
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * nthr;
-      if (ch < nchunk) {
-        // y = RN((h * rstd) * (1 + w)); the quant reads the rounded y.
+      const unsigned ch = tid + c * nthr;
+      if (ch < nch) {
+        // y = RN(t * (1 + w)) with t = h * rstd, formed as fma(t, w, t): one
+        // rounding of the exact t * (1 + w).  The quant reads the rounded y.
         float yv[kVec];
         uint32_t yb[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float a = (D::lo(hb[c][k]) * rstd) * (1.0f + D::lo(wa[c][k]));
-          const float b = (D::hi(hb[c][k]) * rstd) * (1.0f + D::hi(wa[c][k]));
+          const float ta = D::lo(hb[c][k]) * rstd, tb = D::hi(hb[c][k]) * rstd;
+          const float a = __builtin_fmaf(ta, D::lo(wa[c][k]), ta);
+          const float b = __builtin_fmaf(tb, D::hi(wa[c][k]), tb);
           yb[k] = D::pack(a, b);
           yv[2 * k] = D::lo(yb[k]);
           yv[2 * k + 1] = D::hi(yb[k]);
         }
         if constexpr (WRITE_Y) {
           const u32x4 o = {yb[0], yb[1], yb[2], yb[3]};
-          __builtin_nontemporal_store(o, &y[rbase + ch]);
+          __builtin_nontemporal_store(o, &yr[ch]);
         }
         if constexpr (NVFP4) {
           float amax = 0.0f;
@@ -249,16 +276,16 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
           float v[kVec];
 #pragma unroll
           for (int k = 0; k < kVec; ++k) v[k] = yv[k] * o;
-          uint32_t *qp = reinterpret_cast<uint32_t *>(q + (size_t)row * (size_t)nchunk * 4) + ch;
-          __builtin_nontemporal_store(e2m1x8(v), qp);
+          uint32_t *qrow = reinterpret_cast<uint32_t *>(q + (size_t)row * (size_t)nchunk * 4);
+          __builtin_nontemporal_store(e2m1x8(v), &qrow[ch]);
           if ((ch & 1) == 0) bs[swz128x4(row, ch >> 1, ktiles)] = (uint8_t)sc;
         } else {
           float v[kVec];
 #pragma unroll
-          for (int k = 0; k < kVec; ++k) v[k] = yv[k] / s;
+          for (int k = 0; k < kVec; ++k) v[k] = div_by_scale(yv[k], s, r_s);
           const u32x2 packed = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
-          u32x2 *qp = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8) + ch;
-          __builtin_nontemporal_store(packed, qp);
+          u32x2 *qrow = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8);
+          __builtin_nontemporal_store(packed, &qrow[ch]);
         }
       }
     }
@@ -277,6 +304,7 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
   const int tid = threadIdx.x;
   const int nwaves = blockDim.x / kWave;
   const float s = *scale_ptr;
+  const float r_s = 1.0f / s;
   int parity = 0;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x, parity ^= 1) {
     const size_t rb = (size_t)row * (size_t)H;
@@ -304,7 +332,8 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
         float yv[kBlock];
         for (int k = 0; k < kBlock; ++k) {
           const int j = b * kBlock + k;
-          const float yy = (D::lo(hsrc[rb + j]) * rstd) * (1.0f + D::lo(w[j]));
+          const float t = D::lo(hsrc[rb + j]) * rstd;
+          const float yy = __builtin_fmaf(t, D::lo(w[j]), t);
           const uint32_t yq = D::pack(yy, 0.0f) & 0xffffu;
           if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
           yv[k] = D::lo(yq);
@@ -325,10 +354,11 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
       }
     } else {
       for (int j = tid; j < H; j += blockDim.x) {
-        const float yy = (D::lo(hsrc[rb + j]) * rstd) * (1.0f + D::lo(w[j]));
+        const float t = D::lo(hsrc[rb + j]) * rstd;
+          const float yy = __builtin_fmaf(t, D::lo(w[j]), t);
         const uint32_t yq = D::pack(yy, 0.0f) & 0xffffu;
         if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
-        q[rb + j] = (uint8_t)e4m3_one(D::lo(yq) / s);
+        q[rb + j] = (uint8_t)e4m3_one(div_by_scale(D::lo(yq), s, r_s));
       }
     }
   }
@@ -351,8 +381,8 @@ __global__ void convert_probe(int kind, const uint32_t *__restrict__ in, int64_t
     }
     case 2: reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)(Bf16::pack(f, 0.0f) & 0xffffu); break;
     case 3: reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)(Fp16::pack(f, 0.0f) & 0xffffu); break;
-    case 4: out[i] = (uint8_t)e4m3_one(Bf16::lo(bits & 0xffffu) / param); break;
-    case 5: out[i] = (uint8_t)e4m3_one(Fp16::lo(bits & 0xffffu) / param); break;
+    case 4: out[i] = (uint8_t)e4m3_one(div_by_scale(Bf16::lo(bits & 0xffffu), param, 1.0f / param)); break;
+    case 5: out[i] = (uint8_t)e4m3_one(div_by_scale(Fp16::lo(bits & 0xffffu), param, 1.0f / param)); break;
     case 6: out[i] = (uint8_t)nvfp4_scale_code(f, param); break;
     default: break;
   }

@@ -73,14 +73,16 @@ SCALES = [0.05, 7.0, 0.9, 1.0, 2.0 ** -20, 3.0e4, 0.0560825876891613, 0.01666259
 
 @pytest.mark.parametrize("kind,fmt", [(4, O.BF16), (5, O.FP16)])
 def test_fp8_quant_step_every_16bit_y(kind, fmt):
-    """All 65536 patterns of y (NaN/Inf excluded) for several scales,
-    including the workloads' calibrated ones."""
+    """All 65536 patterns of y (NaN/Inf excluded) for 75 scales, including the
+    workloads' calibrated ones."""
     codes = np.arange(1 << 16, dtype=np.uint32)
     yv = O.decode(codes, fmt)
     ok = np.isfinite(yv)
     codes = codes[ok]
     rng = np.random.default_rng(3)
-    scales = SCALES + list(rng.uniform(1e-3, 10, 8))
+    # plus random scales over 40 binades (the kernel divides with a
+    # reciprocal and two FMA corrections, exact for every scale >= 2^-90)
+    scales = SCALES + list(rng.uniform(1e-3, 10, 8)) + list(2.0 ** rng.uniform(-20, 20, 48))
     for s in scales:
         s32 = float(np.float32(s))
         got = probe(kind, codes, s32)
