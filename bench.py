@@ -1,6 +1,6 @@
 """Benchmark of the fused residual-add + Gemma RMSNorm + quant op on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--eager]
 
 A step is one launch of the whole op (add, norm, y, quant, scale store) over
 one batch of the workload, inputs resident in HBM.  The in-place residual
@@ -12,9 +12,12 @@ least 2 GiB of distinct data pass between two uses of a set, which keeps the
 one JSON line:
 
   value        whole-job effective HBM GB/s: algorithmic bytes per step x K /
-               wall time of the K steps (synchronised on both sides);
+               wall time of the K steps (synchronised on both sides).  The K
+               launches are captured once in a HIP graph and the timed region
+               is one replay of it (--eager: one Python launch per step);
   roofline     the kernel's average duration from HIP events recorded on the
-               launch stream, algorithmic bytes / that duration against the
+               launch stream around the timed region (graph: span / K; eager:
+               one event pair per launch), algorithmic bytes / that duration against the
                8 TB/s HBM peak; traffic = measured HBM bytes per launch
                (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel's
                reading) from profiles/traffic.json when it was taken on the
@@ -131,8 +134,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--graph", action="store_true",
-                    help="capture the K launches in one HIP graph and time its replay")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch step by step from Python instead of replaying the K launches "
+                         "captured in one HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the op, time torch's device copy of MIB MiB (the plain "
                          "copy kernel used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -194,9 +198,9 @@ def main():
             launch(i)
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps, {n_sets} buffer sets); timing {args.steps} steps"
-          f" ({'graph' if args.graph else 'eager'})", file=sys.stderr, flush=True)
+          f" ({'graph' if (not args.eager) else 'eager'})", file=sys.stderr, flush=True)
 
-    if args.graph:
+    if not args.eager:
         # The K launches captured once as a HIP graph and replayed: launch
         # overhead off the critical path.  Kernel time = event span / K.
         g = torch.cuda.CUDAGraph()
@@ -255,7 +259,7 @@ def main():
                    "bytes_written": wbytes},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
-        "launch": "graph" if args.graph else "eager",
+        "launch": "graph" if (not args.eager) else "eager",
         "buffer_sets": n_sets,
         "kernel_ms": {"avg": round(avg_ms, 5), "median": round(med_ms, 5),
                       "min": round(kern_ms[0], 5), "max": round(kern_ms[-1], 5)},

@@ -23,7 +23,9 @@
 //    barrier per row.
 //  * An NVFP4 block (16 elements) is the chunk pair held by two adjacent
 //    lanes; the block amax is combined with a DPP lane swap and the even lane
-//    stores the block's scale byte at its 128x4-tiled offset.
+//    stores the block's scale byte at its 128x4-tiled offset.  NVFP4 rows are
+//    assigned to workgroups so that each 128-row scale tile is written
+//    through a single XCD.
 //  * The per-element quant arithmetic is IEEE fp32 (correctly rounded
 //    division, no contraction: the file is built with -ffp-contract=off) and
 //    the format conversions are the gfx950 hardware ones: v_cvt_pk_bf16_f32 /
@@ -31,6 +33,8 @@
 //    clamp to +-448, v_cvt_scalef32_pk_fp4_f32 with unit scale after a clamp
 //    to +-6.  Their semantics are checked exhaustively against the CPU oracle
 //    through nq_convert_probe.
+//  * H <= 512: several rows per wavefront (fused_rows_small), reduced inside
+//    lane groups with DPP, no barrier.
 //  * Shapes or pointers the vector path cannot take (H % 16 != 0, H > 32768,
 //    unaligned views) go to a scalar kernel with the same arithmetic.
 
@@ -170,6 +174,18 @@ __device__ __forceinline__ float wave_sum(float v) {
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
 }
 
+// Workgroup -> row for NVFP4.  Workgroups are dispatched round-robin over the
+// 8 XCDs (workgroup b runs on XCD b % 8).  Inside every full span of 1024
+// rows, XCD x takes the whole 128-row tile x, so the 32 rows that share each
+// 128-byte line of the 128x4-tiled scales write it through one XCD's L2 and
+// the line reaches HBM once (measured: scale writes drop from ~2x to 1x,
+// 5% faster at M = 8192).  Rows of a ragged last span map to themselves.
+__device__ __forceinline__ int64_t nvfp4_row_of_block(int64_t b, int64_t M) {
+  if ((((b >> 10) + 1) << 10) > M) return b;
+  const int64_t lo = b & 1023;
+  return ((b >> 10) << 10) + ((lo & 7) << 7) + (lo >> 3);
+}
+
 // ----------------------------------------------------------------------------
 // Vector kernel.  A workgroup normalises one row (grid = M; the row loop only
 // runs more than once if M exceeds the grid limit).  A chunk is 8 elements
@@ -189,7 +205,8 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
   const int nwaves = nthr / kWave;
   const float Hf = (float)(nchunk * kVec);
   int parity = 0;
-  for (int64_t row = blockIdx.x; row < M; row += gridDim.x, parity ^= 1) {
+  for (int64_t blk = blockIdx.x; blk < M; blk += gridDim.x, parity ^= 1) {
+    const int64_t row = NVFP4 ? nvfp4_row_of_block(blk, M) : blk;
     const size_t rbase = (size_t)row * (size_t)nchunk;
     const u32x4 *__restrict__ xr = x + rbase;
     u32x4 *__restrict__ rr = res + rbase;
@@ -288,6 +305,111 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
           __builtin_nontemporal_store(packed, &qrow[ch]);
         }
       }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Small-H kernel (H <= 512): several rows per wavefront.  A row takes LPR
+// lanes (the power of two >= H/8, one 8-element chunk per lane), a wave holds
+// 64/LPR rows and a 256-thread workgroup 4 times as many.  The row sum of
+// squares is a DPP/shuffle reduction inside the LPR-lane group, so waves
+// never wait on each other: no LDS, no barrier.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LPR >= 2) v += dpp<0xB1>(v);    // lane ^ 1
+  if constexpr (LPR >= 4) v += dpp<0x4E>(v);    // lane ^ 2
+  if constexpr (LPR >= 8) v += dpp<0x141>(v);   // mirror inside 8 lanes
+  if constexpr (LPR >= 16) v += dpp<0x140>(v);  // mirror inside 16 lanes
+  if constexpr (LPR >= 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (LPR >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+constexpr int kSmallThreads = 256;
+
+template <class D, bool NVFP4, bool HAS_RES, bool WRITE_Y, int LPR>
+__global__ void __launch_bounds__(kSmallThreads)
+fused_rows_small(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__restrict__ w,
+                 const float *__restrict__ scale_ptr, float eps, int64_t M, int nchunk,
+                 uint8_t *__restrict__ q, uint8_t *__restrict__ bs, u32x4 *__restrict__ y,
+                 int ktiles) {
+  constexpr int kRowsPerWg = kSmallThreads / LPR;
+  const unsigned tid = threadIdx.x;
+  const unsigned ch = tid % LPR;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + tid / LPR;
+  const bool active = row < M && ch < (unsigned)nchunk;
+  const size_t rbase = (size_t)(row < M ? row : 0) * (size_t)nchunk;
+  u32x4 xa = {0, 0, 0, 0}, ra = {0, 0, 0, 0}, wa = {0, 0, 0, 0};
+  if (active) {
+    xa = __builtin_nontemporal_load(&x[rbase + ch]);
+    if constexpr (HAS_RES) ra = __builtin_nontemporal_load(&res[rbase + ch]);
+    wa = w[ch];
+  }
+  const float s = *scale_ptr;
+  const float r_s = NVFP4 ? 0.0f : 1.0f / s;
+  uint32_t hb[4];
+  float ss = 0.0f;
+  if constexpr (HAS_RES) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hb[k] = D::pack(D::lo(xa[k]) + D::lo(ra[k]), D::hi(xa[k]) + D::hi(ra[k]));
+    if (active) {
+      const u32x4 o = {hb[0], hb[1], hb[2], hb[3]};
+      __builtin_nontemporal_store(o, &res[rbase + ch]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hb[k] = xa[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = D::lo(hb[k]), b = D::hi(hb[k]);
+    ss = __builtin_fmaf(a, a, ss);
+    ss = __builtin_fmaf(b, b, ss);
+  }
+  ss = group_sum<LPR>(ss);
+  const float rstd = 1.0f / __builtin_sqrtf(ss / (float)(nchunk * kVec) + eps);
+  float yv[kVec];
+  uint32_t yb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float ta = D::lo(hb[k]) * rstd, tb = D::hi(hb[k]) * rstd;
+    yb[k] = D::pack(__builtin_fmaf(ta, D::lo(wa[k]), ta), __builtin_fmaf(tb, D::hi(wa[k]), tb));
+    yv[2 * k] = D::lo(yb[k]);
+    yv[2 * k + 1] = D::hi(yb[k]);
+  }
+  if constexpr (WRITE_Y) {
+    if (active) {
+      const u32x4 o = {yb[0], yb[1], yb[2], yb[3]};
+      __builtin_nontemporal_store(o, &y[rbase + ch]);
+    }
+  }
+  if constexpr (NVFP4) {
+    // H % 64 == 0, so a row's lanes pair up into whole blocks and inactive
+    // lanes pair only with inactive lanes.
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) amax = fmaxf(amax, fabsf(yv[k]));
+    amax = fmaxf(amax, dpp_swap_adjacent(amax));
+    const uint32_t sc = nvfp4_scale_code(amax, s);
+    const float o = nvfp4_elem_scale(sc, s);
+    float v[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) v[k] = yv[k] * o;
+    const uint32_t packed = e2m1x8(v);
+    if (active) {
+      uint32_t *qrow = reinterpret_cast<uint32_t *>(q + (size_t)row * (size_t)nchunk * 4);
+      __builtin_nontemporal_store(packed, &qrow[ch]);
+      if ((ch & 1) == 0) bs[swz128x4(row, ch >> 1, ktiles)] = (uint8_t)sc;
+    }
+  } else {
+    float v[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) v[k] = div_by_scale(yv[k], s, r_s);
+    const u32x2 packed = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
+    if (active) {
+      u32x2 *qrow = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8);
+      __builtin_nontemporal_store(packed, &qrow[ch]);
     }
   }
 }
@@ -401,6 +523,18 @@ hipError_t launch_vec(dim3 grid, dim3 block, hipStream_t st, const void *x, void
   return hipGetLastError();
 }
 
+template <class D, bool NV, bool RES, bool WY, int LPR>
+hipError_t launch_small(hipStream_t st, const void *x, void *res, const void *w,
+                        const float *scale, float eps, int64_t M, int nchunk, void *q, void *bs,
+                        void *y, int ktiles) {
+  constexpr int64_t rows_per_wg = kSmallThreads / LPR;
+  const int64_t blocks = (M + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL((fused_rows_small<D, NV, RES, WY, LPR>), dim3((unsigned)blocks),
+                     dim3(kSmallThreads), 0, st, (const u32x4 *)x, (u32x4 *)res, (const u32x4 *)w,
+                     scale, eps, M, nchunk, (uint8_t *)q, (uint8_t *)bs, (u32x4 *)y, ktiles);
+  return hipGetLastError();
+}
+
 template <class D, bool NV, bool RES, bool WY>
 hipError_t launch_scalar(dim3 grid, hipStream_t st, const void *x, void *res, const void *w,
                          const float *scale, float eps, int64_t M, int H, void *q, void *bs,
@@ -445,6 +579,21 @@ hipError_t run(const Args &a) {
                    aligned(a.res, 16) && aligned(a.w, 16) && aligned(a.y, 16) &&
                    aligned(a.q, NV ? 4 : 8);
   const dim3 grid((unsigned)(a.M < kMaxGrid ? a.M : kMaxGrid));
+  if (vec && a.H <= 512 && a.M <= kMaxGrid) {
+    // Several rows per wave; lanes per row = the power of two >= H/8.
+    const int nchunk = (int)(a.H / kVec);
+    if (nchunk <= 2)
+      return launch_small<D, NV, RES, WY, 2>(a.st, a.x, a.res, a.w, a.scale, a.eps, a.M, nchunk, a.q, a.bs, a.y, ktiles);
+    if (nchunk <= 4)
+      return launch_small<D, NV, RES, WY, 4>(a.st, a.x, a.res, a.w, a.scale, a.eps, a.M, nchunk, a.q, a.bs, a.y, ktiles);
+    if (nchunk <= 8)
+      return launch_small<D, NV, RES, WY, 8>(a.st, a.x, a.res, a.w, a.scale, a.eps, a.M, nchunk, a.q, a.bs, a.y, ktiles);
+    if (nchunk <= 16)
+      return launch_small<D, NV, RES, WY, 16>(a.st, a.x, a.res, a.w, a.scale, a.eps, a.M, nchunk, a.q, a.bs, a.y, ktiles);
+    if (nchunk <= 32)
+      return launch_small<D, NV, RES, WY, 32>(a.st, a.x, a.res, a.w, a.scale, a.eps, a.M, nchunk, a.q, a.bs, a.y, ktiles);
+    return launch_small<D, NV, RES, WY, 64>(a.st, a.x, a.res, a.w, a.scale, a.eps, a.M, nchunk, a.q, a.bs, a.y, ktiles);
+  }
   if (vec) {
     const int nchunk = (int)(a.H / kVec);
     const int cpt = chunks_per_thread(a.H);

@@ -5,7 +5,7 @@ benchmark uses; the oracle checks a row sample (rows are independent) and
 cheap whole-tensor properties cover the rest (residual == x + residual by
 torch's CPU add, guard bytes, untouched scale padding).  Edge cases cover
 ragged tiles, the scalar path (H % 16 != 0, H > 32768, unaligned views),
-1, 2 and 4 chunks per thread, residual=None, write_y off, special values, M == 0,
+1, 2 and 4 chunks per thread, several rows per wave (H <= 512), residual=None, write_y off, special values, M == 0,
 determinism and argument errors.
 """
 
@@ -79,8 +79,21 @@ EDGE = [
     (torch.bfloat16, True, 130, 16384, True, True),
     (torch.bfloat16, True, 3, 32768, True, True),        # 4 chunks x 1024 threads
     (torch.bfloat16, True, 17, 4160, True, True),        # ragged 2-chunk split
+    (torch.bfloat16, True, 2100, 256, True, True),       # XCD row map: 2 spans + ragged tail
+    (torch.float16, True, 3072, 64, False, True),        # XCD row map: exact spans
     (torch.float16, True, 200, 5120, True, True),
     (torch.float16, True, 64, 192, False, False),
+    # H <= 512: several rows per wave (lanes per row 2, 4, 8, 16, 32, 64)
+    (torch.bfloat16, False, 37, 16, True, True),
+    (torch.bfloat16, False, 300, 32, True, False),
+    (torch.float16, False, 1, 112, True, True),
+    (torch.bfloat16, False, 129, 256, False, True),
+    (torch.bfloat16, False, 65, 496, True, True),
+    (torch.float16, False, 1000, 512, True, False),
+    (torch.bfloat16, True, 37, 128, True, True),
+    (torch.float16, True, 1, 320, True, True),
+    (torch.bfloat16, True, 1000, 448, False, True),
+    (torch.bfloat16, True, 255, 512, True, False),
 ]
 
 
