@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 2 << 30
 METRIC = "effective HBM GB/s (and % of peak) + tokens/s for add-RMSNorm+quant, 1 GPU"
-KERNEL_SRC = os.path.join(ROOT, "fp4_activation_quant_amd", "csrc", "gemma_norm_quant.hip")
+KERNEL_SRC_DIR = os.path.join(ROOT, "fp4_activation_quant_amd", "csrc")
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -55,8 +55,15 @@ def algorithmic_bytes(wl):
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every kernel source file: traffic counters taken on other
+    sources are not reported."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_name(wl):
@@ -134,6 +141,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the unfused chain instead: add + norm (y to HBM), then the "
+                         "standalone quant kernel reading y back (same work, two launches)")
     ap.add_argument("--eager", action="store_true",
                     help="launch step by step from Python instead of replaying the K launches "
                          "captured in one HIP graph")
@@ -174,6 +184,8 @@ def main():
         st = {"x": [xp_cpu.to(dev), xn_cpu.to(dev)],
               "r": r.to(dev) if r is not None else None,
               "y": torch.empty((M, H), dtype=x.dtype, device=dev) if wl.write_y else None}
+        if args.unfused and not wl.write_y:
+            st["ytmp"] = torch.empty((M, H), dtype=x.dtype, device=dev)
         if wl.nvfp4:
             st["q"] = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
             st["bs"] = torch.empty((ops.round_up(M, 128), ops.round_up(H // 16, 4)),
@@ -190,6 +202,14 @@ def main():
         # round again, so the in-place residual stays bounded.
         st = sets[i % n_sets]
         xi = st["x"][(i // n_sets) & 1]
+        if args.unfused:
+            yi = st["y"] if st["y"] is not None else st["ytmp"]
+            ops.add_rms_norm_quant_out(xi, st["r"], wd, wl.eps, None, None, "gemma", None, None, yi)
+            if wl.nvfp4:
+                ops.quant_nvfp4(yi, sd, st["q"], st["bs"])
+            else:
+                ops.quant_fp8_static(yi, sd, st["q"])
+            return
         ops.gemma_add_rms_norm_quant_out(xi, st["r"], wd, wl.eps, sd, wl.nvfp4, st["q"], st["bs"],
                                          st["y"])
 
@@ -260,6 +280,7 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(M / (ms_per_step * 1e-3), 1),
         "launch": "graph" if (not args.eager) else "eager",
+        "path": "unfused (2 kernels)" if args.unfused else "fused",
         "buffer_sets": n_sets,
         "kernel_ms": {"avg": round(avg_ms, 5), "median": round(med_ms, 5),
                       "min": round(kern_ms[0], 5), "max": round(kern_ms[-1], 5)},

@@ -12,9 +12,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemma_no
 
 NQ_OK, NQ_EINVAL, NQ_EUNSUPPORTED, NQ_EHIP = 0, 1, 2, 3
 NQ_BF16, NQ_FP16 = 0, 1
-NQ_MODE_FP8_STATIC, NQ_MODE_NVFP4 = 0, 1
-EXPORTS = ("nq_gemma_add_rms_norm_quant", "nq_block_scale_bytes", "nq_status_string",
-           "nq_abi_version", "nq_convert_probe")
+NQ_MODE_FP8_STATIC, NQ_MODE_NVFP4, NQ_MODE_NONE = 0, 1, 2
+NQ_NORM_GEMMA, NQ_NORM_PLAIN = 0, 1
+EXPORTS = ("nq_gemma_add_rms_norm_quant", "nq_add_rms_norm_quant", "nq_quant_fp8_static",
+           "nq_quant_nvfp4", "nq_block_scale_bytes", "nq_status_string", "nq_abi_version",
+           "nq_convert_probe")
 
 _lib = None
 
@@ -37,6 +39,13 @@ def lib():
         L.nq_gemma_add_rms_norm_quant.argtypes = [vp, vp, vp, f32, vp, i64, i64, i32, i32, i32,
                                                   vp, vp, vp, vp]
         L.nq_gemma_add_rms_norm_quant.restype = i32
+        L.nq_add_rms_norm_quant.argtypes = [vp, vp, vp, f32, vp, i64, i64, i32, i32, i32, i32,
+                                            vp, vp, vp, vp]
+        L.nq_add_rms_norm_quant.restype = i32
+        L.nq_quant_fp8_static.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+        L.nq_quant_fp8_static.restype = i32
+        L.nq_quant_nvfp4.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
+        L.nq_quant_nvfp4.restype = i32
         L.nq_block_scale_bytes.argtypes = [i64, i64]
         L.nq_block_scale_bytes.restype = ctypes.c_size_t
         L.nq_status_string.argtypes = [i32]
@@ -56,6 +65,25 @@ def nq_gemma_add_rms_norm_quant(x, residual, weight, eps, scale, M, H, dtype, mo
                                              float(eps), scale or None, int(M), int(H), int(dtype),
                                              int(mode), int(bool(write_y)), q or None,
                                              block_scale or None, y or None, stream or None)
+
+
+def nq_add_rms_norm_quant(x, residual, weight, eps, scale, M, H, dtype, norm, mode, write_y,
+                          q, block_scale, y, stream):
+    """Raw call (integer device addresses, 0 for NULL); returns the status."""
+    return lib().nq_add_rms_norm_quant(x or None, residual or None, weight or None, float(eps),
+                                       scale or None, int(M), int(H), int(dtype), int(norm),
+                                       int(mode), int(bool(write_y)), q or None,
+                                       block_scale or None, y or None, stream or None)
+
+
+def nq_quant_fp8_static(y, scale, M, H, dtype, q, stream):
+    return lib().nq_quant_fp8_static(y or None, scale or None, int(M), int(H), int(dtype),
+                                     q or None, stream or None)
+
+
+def nq_quant_nvfp4(y, global_scale, M, H, dtype, q, block_scale, stream):
+    return lib().nq_quant_nvfp4(y or None, global_scale or None, int(M), int(H), int(dtype),
+                                q or None, block_scale or None, stream or None)
 
 
 def nq_block_scale_bytes(M, H):

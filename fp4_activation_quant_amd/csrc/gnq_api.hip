@@ -1,0 +1,168 @@
+// C ABI of the library (include/gemma_norm_quant.h): argument validation,
+// the M == 0 early return, dispatch to the per-(dtype, mode) kernels, and
+// the conversion probe.  The operation is `gemma_add_rms_norm_quant` on the
+// `fused_norm_quant` page; its assertions (2-D contiguous bf16/fp16 x,
+// residual of the same shape or None, weight of shape (H,), one fp32 scale,
+// H % 64 == 0 for NVFP4) become status codes here, and nothing is launched
+// or written when one fails.
+
+#include "gemma_norm_quant.h"
+#include "gnq_common.hpp"
+
+namespace gnq {
+namespace {
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x0 = (uintptr_t)a, x1 = x0 + na, y0 = (uintptr_t)b, y1 = y0 + nb;
+  return x0 < y1 && y0 < x1;
+}
+
+bool valid_dtype(int dtype) { return dtype == NQ_BF16 || dtype == NQ_FP16; }
+
+size_t block_scale_bytes(int64_t M, int64_t H) {
+  if (M <= 0 || H < kBlock) return 0;
+  const int64_t rows = (M + 127) / 128 * 128;
+  const int64_t cols = ((H / kBlock) + 3) / 4 * 4;
+  return (size_t)rows * (size_t)cols;
+}
+
+nq_status status_of(hipError_t e) { return e == hipSuccess ? NQ_OK : NQ_EHIP; }
+
+// Probe: the kernels' own device routines on arbitrary 32-bit patterns.
+__global__ void convert_probe(int kind, const uint32_t *__restrict__ in, int64_t n, float param,
+                              uint8_t *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t bits = in[i];
+  const float f = __uint_as_float(bits);
+  switch (kind) {
+    case 0: out[i] = (uint8_t)e4m3_one(f); break;
+    case 1: {
+      float v[8] = {f, 0, 0, 0, 0, 0, 0, 0};
+      out[i] = (uint8_t)(e2m1x8(v) & 0xfu);
+      break;
+    }
+    case 2: reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)(Bf16::pack(f, 0.0f) & 0xffffu); break;
+    case 3: reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)(Fp16::pack(f, 0.0f) & 0xffffu); break;
+    case 4: out[i] = (uint8_t)e4m3_one(div_by_scale(Bf16::lo(bits & 0xffffu), param, 1.0f / param)); break;
+    case 5: out[i] = (uint8_t)e4m3_one(div_by_scale(Fp16::lo(bits & 0xffffu), param, 1.0f / param)); break;
+    case 6: out[i] = (uint8_t)nvfp4_scale_code(f, param); break;
+    default: break;
+  }
+}
+
+}  // namespace
+}  // namespace gnq
+
+using namespace gnq;
+
+extern "C" {
+
+int nq_abi_version(void) { return NQ_ABI_VERSION; }
+
+const char *nq_status_string(int status) {
+  switch (status) {
+    case NQ_OK: return "ok";
+    case NQ_EINVAL: return "invalid argument";
+    case NQ_EUNSUPPORTED: return "unsupported shape or mode";
+    case NQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t nq_block_scale_bytes(int64_t M, int64_t H) { return block_scale_bytes(M, H); }
+
+nq_status nq_add_rms_norm_quant(const void *x, void *residual, const void *weight, float eps,
+                                const float *scale, int64_t M, int64_t H, int dtype, int norm,
+                                int mode, int write_y, void *q, void *block_scale, void *y,
+                                void *stream) {
+  if (!valid_dtype(dtype)) return NQ_EINVAL;
+  if (norm != NQ_NORM_GEMMA && norm != NQ_NORM_PLAIN) return NQ_EINVAL;
+  if (mode != NQ_MODE_FP8_STATIC && mode != NQ_MODE_NVFP4 && mode != NQ_MODE_NONE) return NQ_EINVAL;
+  if (M < 0 || H <= 0 || H > ((int64_t)1 << 30)) return NQ_EINVAL;
+  const bool nv = mode == NQ_MODE_NVFP4, none = mode == NQ_MODE_NONE;
+  if (!x || !weight) return NQ_EINVAL;
+  if (!none && (!scale || !q)) return NQ_EINVAL;
+  if (nv && !block_scale) return NQ_EINVAL;
+  if ((write_y || none) && !y) return NQ_EINVAL;
+  if (none && !write_y) return NQ_EINVAL;
+  if (nv && H % 64 != 0) return NQ_EUNSUPPORTED;
+  const size_t act = (size_t)M * (size_t)H * 2;
+  const size_t qbytes = none ? 0 : nv ? (size_t)M * (size_t)(H / 2) : (size_t)M * (size_t)H;
+  const size_t bsbytes = nv ? block_scale_bytes(M, H) : 0;
+  const void *yy = write_y ? y : nullptr;
+  const void *qq = none ? nullptr : q;
+  const void *bb = nv ? block_scale : nullptr;
+  if (residual == x) return NQ_EINVAL;
+  const void *bufs[5] = {x, residual, qq, yy, bb};
+  const size_t lens[5] = {act, act, qbytes, act, bsbytes};
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return NQ_EINVAL;
+  if (M == 0) return NQ_OK;
+
+  FusedArgs a{x, residual, weight, scale, eps, M, H, none ? nullptr : q, nv ? block_scale : nullptr,
+              (write_y || none) ? y : nullptr, norm == NQ_NORM_GEMMA, (hipStream_t)stream};
+  hipError_t e;
+  if (dtype == NQ_BF16)
+    e = nv ? fused_bf16_nvfp4(a) : none ? fused_bf16_none(a) : fused_bf16_fp8(a);
+  else
+    e = nv ? fused_fp16_nvfp4(a) : none ? fused_fp16_none(a) : fused_fp16_fp8(a);
+  return status_of(e);
+}
+
+nq_status nq_gemma_add_rms_norm_quant(const void *x, void *residual, const void *weight, float eps,
+                                      const float *scale, int64_t M, int64_t H, int dtype,
+                                      int mode, int write_y, void *q, void *block_scale, void *y,
+                                      void *stream) {
+  if (mode != NQ_MODE_FP8_STATIC && mode != NQ_MODE_NVFP4) return NQ_EINVAL;
+  return nq_add_rms_norm_quant(x, residual, weight, eps, scale, M, H, dtype, NQ_NORM_GEMMA, mode,
+                               write_y, q, block_scale, y, stream);
+}
+
+static nq_status quant_common(const void *y, const float *scale, int64_t M, int64_t H, int dtype,
+                              bool nv, void *q, void *block_scale, void *stream) {
+  if (!valid_dtype(dtype)) return NQ_EINVAL;
+  if (M < 0 || H <= 0 || H > ((int64_t)1 << 30)) return NQ_EINVAL;
+  if (!y || !scale || !q || (nv && !block_scale)) return NQ_EINVAL;
+  if (nv && H % kBlock != 0) return NQ_EUNSUPPORTED;
+  const size_t act = (size_t)M * (size_t)H * 2;
+  const size_t qbytes = nv ? (size_t)M * (size_t)(H / 2) : (size_t)M * (size_t)H;
+  const size_t bsbytes = nv ? block_scale_bytes(M, H) : 0;
+  if (overlaps(y, act, q, qbytes) || (nv && (overlaps(y, act, block_scale, bsbytes) ||
+                                             overlaps(q, qbytes, block_scale, bsbytes))))
+    return NQ_EINVAL;
+  if (M == 0) return NQ_OK;
+  QuantArgs a{y, scale, M, H, q, nv ? block_scale : nullptr, (hipStream_t)stream};
+  hipError_t e;
+  if (dtype == NQ_BF16)
+    e = nv ? quant_bf16_nvfp4(a) : quant_bf16_fp8(a);
+  else
+    e = nv ? quant_fp16_nvfp4(a) : quant_fp16_fp8(a);
+  return status_of(e);
+}
+
+nq_status nq_quant_fp8_static(const void *y, const float *scale, int64_t M, int64_t H, int dtype,
+                              void *q, void *stream) {
+  return quant_common(y, scale, M, H, dtype, false, q, nullptr, stream);
+}
+
+nq_status nq_quant_nvfp4(const void *y, const float *global_scale, int64_t M, int64_t H, int dtype,
+                         void *q, void *block_scale, void *stream) {
+  return quant_common(y, global_scale, M, H, dtype, true, q, block_scale, stream);
+}
+
+nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,
+                           void *stream) {
+  if (kind < 0 || kind > 6 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in)))
+    return NQ_EINVAL;
+  if (n == 0) return NQ_OK;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(convert_probe, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,
+                     kind, (const uint32_t *)in, n, param, (uint8_t *)out);
+  return status_of(hipGetLastError());
+}
+
+}  // extern "C"

@@ -1,0 +1,268 @@
+// Device building blocks shared by every kernel of the library: activation
+// dtypes, the FP8 / FP4 encoders, the correctly rounded division by the FP8
+// scale, the NVFP4 block-scale arithmetic, the 128x4 scale layout, DPP
+// reductions, and the host-side argument block.
+//
+// The operation is `gemma_add_rms_norm_quant` on the `fused_norm_quant` page
+// (and its unfused form: an add + Gemma RMSNorm kernel followed by a
+// standalone static-FP8 or NVFP4 quant, which the page says the fused kernel
+// matches code for code).  Format conversions are the gfx950 hardware
+// instructions; the per-element arithmetic is IEEE fp32 with no contraction
+// (the library is built with -ffp-contract=off and correctly rounded
+// divide/sqrt).  The probe entry point of the C ABI runs these routines on
+// arbitrary bit patterns so tests can check them exhaustively against the
+// CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gnq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kVec = 8;           // elements per thread chunk (16 bytes)
+constexpr int kBlock = 16;        // elements per NVFP4 block scale
+constexpr int kWave = 64;
+constexpr int kMaxThreads = 1024;
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE2M1Max = 6.0f;
+
+// Output modes (values of nq_mode).
+constexpr int kModeFp8 = 0;
+constexpr int kModeNvfp4 = 1;
+constexpr int kModeNone = 2;
+
+// ----------------------------------------------------------------------------
+// Activation dtypes: unpack two values from a 32-bit word, pack two fp32
+// values with round-to-nearest-even.
+struct Bf16 {
+  static __device__ __forceinline__ float lo(uint32_t p) { return __uint_as_float(p << 16); }
+  static __device__ __forceinline__ float hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+};
+
+struct Fp16 {
+  static __device__ __forceinline__ float lo(uint32_t p) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t p) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+};
+
+// ----------------------------------------------------------------------------
+// Quant-side encoders.
+
+__device__ __forceinline__ float clampf(float v, float lim) {
+  return __builtin_amdgcn_fmed3f(v, -lim, lim);
+}
+
+// Four E4M3FN codes packed little-endian into a word.  v_cvt_pk_fp8_f32
+// rounds to nearest even but does not saturate (465 -> NaN), hence the clamp.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clampf(a, kE4M3Max), clampf(b, kE4M3Max), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clampf(c, kE4M3Max), clampf(d, kE4M3Max), w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint32_t e4m3_one(float a) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clampf(a, kE4M3Max), 0.0f, 0, false) & 0xffu;
+}
+
+// Eight E2M1 codes, element 2k in the low nibble of byte k.  The gfx950
+// conversion rounds to nearest even and saturates out-of-range magnitudes
+// (including infinities) to 6 by itself, so no clamp precedes it; the
+// exhaustive probe tests check it against clamp-then-round.
+__device__ __forceinline__ uint32_t e2m1x8(const float *v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
+}
+
+// fl32(y / s), correctly rounded, from r = fl32(1 / s) (one IEEE division
+// per thread instead of one per element).  q0 = fl(y * r) lies within 1.5
+// ulp of y / s; a correction step q + (y - q*s) * r (FMA, one rounding)
+// brings it within 1 ulp, and from there one more step gives the correctly
+// rounded quotient (Markstein's theorem: reciprocal within half an ulp,
+// quotient within one ulp, exact remainder).  The remainder is exact for
+// |y| >= 2^-103, i.e. for every scale >= 2^-90 wherever the FP8 code is not
+// zero.  Quotients beyond +-1024 saturate to +-448 either way; clamping them
+// between steps keeps every intermediate finite.  The remainder is formed as
+// q*s - y and subtracted, so a zero quotient keeps the sign of y.
+__device__ __forceinline__ float div_by_scale(float y, float s, float r) {
+  float q = clampf(y * r, 1024.0f);
+  q = clampf(__builtin_fmaf(-__builtin_fmaf(q, s, -y), r, q), 1024.0f);
+  return __builtin_fmaf(-__builtin_fmaf(q, s, -y), r, q);
+}
+
+// NVFP4 block scale: S = E4M3(min(gs * (amax / 6), 448)).
+__device__ __forceinline__ uint32_t nvfp4_scale_code(float amax, float gs) {
+  const float t = amax / kE2M1Max;
+  const float u = fminf(gs * t, kE4M3Max);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false) & 0xffu;
+}
+
+// Element multiplier o = gs / decode(S), 0 for a zero scale.
+__device__ __forceinline__ float nvfp4_elem_scale(uint32_t s_code, float gs) {
+  const float sigma = __builtin_amdgcn_cvt_f32_fp8((int)s_code, 0);
+  return sigma == 0.0f ? 0.0f : gs / sigma;
+}
+
+// Byte offset of block scale (row m, block b) in the 128x4-tiled layout;
+// ktiles = round_up(H/16, 4) / 4.
+__device__ __forceinline__ size_t swz128x4(int64_t m, int b, int ktiles) {
+  return ((size_t)(m >> 7) * (size_t)ktiles + (size_t)(b >> 2)) * 512u + (size_t)(m & 31) * 16u +
+         (size_t)((m >> 5) & 3) * 4u + (size_t)(b & 3);
+}
+
+// Workgroup -> row for NVFP4.  Workgroups are dispatched round-robin over the
+// 8 XCDs (workgroup b runs on XCD b % 8).  Inside every full span of 1024
+// rows, XCD x takes the whole 128-row tile x, so the 32 rows that share each
+// 128-byte line of the 128x4-tiled scales write it through one XCD's L2 and
+// the line reaches HBM once (measured: scale writes drop from ~2x to 1x,
+// 5% faster at M = 8192).  Rows of a ragged last span map to themselves.
+__device__ __forceinline__ int64_t nvfp4_row_of_block(int64_t b, int64_t M) {
+  if ((((b >> 10) + 1) << 10) > M) return b;
+  const int64_t lo = b & 1023;
+  return ((b >> 10) << 10) + ((lo & 7) << 7) + (lo >> 3);
+}
+
+// ----------------------------------------------------------------------------
+// Cross-lane reductions.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, false));
+}
+
+// Value of the neighbouring lane (lane ^ 1): DPP quad_perm [1, 0, 3, 2].
+__device__ __forceinline__ float dpp_swap_adjacent(float v) { return dpp<0xB1>(v); }
+
+// Sum over the 64 lanes of a wave (all lanes active), returned to every lane:
+// DPP exchanges inside each 16-lane row (lane ^ 1, lane ^ 2, 8-lane mirror,
+// 16-lane mirror), then the four row totals via readlane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  const int b = __builtin_bit_cast(int, v);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+}
+
+// Sum over aligned groups of LPR lanes (LPR a power of two <= 64, all lanes
+// active), returned to every lane of the group.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LPR >= 2) v += dpp<0xB1>(v);    // lane ^ 1
+  if constexpr (LPR >= 4) v += dpp<0x4E>(v);    // lane ^ 2
+  if constexpr (LPR >= 8) v += dpp<0x141>(v);   // mirror inside 8 lanes
+  if constexpr (LPR >= 16) v += dpp<0x140>(v);  // mirror inside 16 lanes
+  if constexpr (LPR >= 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (LPR >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// ----------------------------------------------------------------------------
+// Gemma (1 + w) or plain (w) RMSNorm scaling of t = h * rstd, one rounding.
+// fma(t, w, t) is the correctly rounded t * (1 + w).
+template <bool GEMMA>
+__device__ __forceinline__ float norm_scale(float t, float w) {
+  if constexpr (GEMMA) return __builtin_fmaf(t, w, t);
+  return t * w;
+}
+
+// Quantize one 8-element chunk of y (already rounded to the activation dtype)
+// of row `row`, chunk `ch`, and store its codes (and, for NVFP4, from the
+// even lane of the pair, the block scale).  NVFP4 needs the neighbouring lane
+// to hold the other half of the 16-element block and to run this too.
+template <int MODE>
+__device__ __forceinline__ void quant_store_chunk(const float (&yv)[kVec], float s, float r_s,
+                                                  uint8_t *__restrict__ q, uint8_t *__restrict__ bs,
+                                                  int64_t row, unsigned ch, int nchunk, int ktiles) {
+  if constexpr (MODE == kModeNvfp4) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) amax = fmaxf(amax, fabsf(yv[k]));
+    amax = fmaxf(amax, dpp_swap_adjacent(amax));
+    const uint32_t sc = nvfp4_scale_code(amax, s);
+    const float o = nvfp4_elem_scale(sc, s);
+    float v[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) v[k] = yv[k] * o;
+    uint32_t *qrow = reinterpret_cast<uint32_t *>(q + (size_t)row * (size_t)nchunk * 4);
+    __builtin_nontemporal_store(e2m1x8(v), &qrow[ch]);
+    if ((ch & 1) == 0) bs[swz128x4(row, (int)(ch >> 1), ktiles)] = (uint8_t)sc;
+  } else if constexpr (MODE == kModeFp8) {
+    float v[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) v[k] = div_by_scale(yv[k], s, r_s);
+    const u32x2 packed = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
+    u32x2 *qrow = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8);
+    __builtin_nontemporal_store(packed, &qrow[ch]);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Host side.
+
+constexpr int64_t kMaxGrid = ((int64_t)1 << 31) - 1;
+
+struct FusedArgs {
+  const void *x;
+  void *res;        // nullptr: no residual
+  const void *w;
+  const float *scale;
+  float eps;
+  int64_t M;
+  int64_t H;
+  void *q;
+  void *bs;
+  void *y;          // nullptr: y not written
+  bool gemma;       // (1 + w) if true, w if false
+  hipStream_t st;
+};
+
+struct QuantArgs {
+  const void *y;
+  const float *scale;
+  int64_t M;
+  int64_t H;
+  void *q;
+  void *bs;
+  hipStream_t st;
+};
+
+// One translation unit per (dtype, mode) instantiates the fused kernels.
+hipError_t fused_bf16_fp8(const FusedArgs &a);
+hipError_t fused_bf16_nvfp4(const FusedArgs &a);
+hipError_t fused_bf16_none(const FusedArgs &a);
+hipError_t fused_fp16_fp8(const FusedArgs &a);
+hipError_t fused_fp16_nvfp4(const FusedArgs &a);
+hipError_t fused_fp16_none(const FusedArgs &a);
+hipError_t quant_bf16_fp8(const QuantArgs &a);
+hipError_t quant_bf16_nvfp4(const QuantArgs &a);
+hipError_t quant_fp16_fp8(const QuantArgs &a);
+hipError_t quant_fp16_nvfp4(const QuantArgs &a);
+
+}  // namespace gnq

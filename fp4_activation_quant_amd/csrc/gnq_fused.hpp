@@ -1,0 +1,344 @@
+// The fused kernels: residual add + (Gemma or plain) RMSNorm + FP8 / NVFP4 /
+// no quant, one launch.  Included by one translation unit per (dtype, mode)
+// (gnq_fused_<dtype>_<mode>.hip), which instantiates GNQ_FUSED_ENTRY.
+//
+// Design (memory-bound; no MFMA -- nothing here is a contraction):
+//  * fused_rows: one workgroup per row, grid = M (measured faster than a
+//    persistent grid on this chip: more independent rows in flight and no
+//    row loop).  A thread owns 8-element chunks (16 bytes) at chunk index
+//    tid, tid + nthr, ..., so every load and store instruction of a wave
+//    covers contiguous memory: 1 KB of x / residual / y, 512 B of FP8 codes,
+//    256 B of FP4 codes.  1, 2 or 4 chunks per thread (H <= 4096, <= 16384,
+//    <= 32768).  x and residual are streamed with non-temporal loads, all
+//    outputs with non-temporal stores; weight and scale are plain (L2-cached)
+//    loads.  All loads of a row are issued before the first wait.  Sum of
+//    squares: fp32 FMA chain per thread, DPP butterfly inside each 16-lane
+//    row plus readlane across rows, one LDS slot per wave, one barrier.
+//  * An NVFP4 block (16 elements) is the chunk pair held by two adjacent
+//    lanes; the block amax is combined with a DPP lane swap and the even lane
+//    stores the block's scale byte at its 128x4-tiled offset.  NVFP4 rows are
+//    assigned to workgroups so that each 128-row scale tile is written
+//    through a single XCD.
+//  * fused_rows_small: H <= 512, several rows per wavefront, reduced inside
+//    lane groups with DPP, no LDS and no barrier.
+//  * fused_rows_scalar: shapes or pointers the vector path cannot take
+//    (H % 16 != 0, H > 32768, unaligned views); same arithmetic.
+#pragma once
+
+#include "gnq_common.hpp"
+
+namespace gnq {
+
+template <class D, int MODE, bool HAS_RES, bool WRITE_Y, bool GEMMA, int CPT>
+__global__ void __launch_bounds__(kMaxThreads)
+fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__restrict__ w,
+           const float *__restrict__ scale_ptr, float eps, int64_t M, int nchunk,
+           uint8_t *__restrict__ q, uint8_t *__restrict__ bs, u32x4 *__restrict__ y, int ktiles) {
+  __shared__ float partial[2][kMaxThreads / kWave];
+  const unsigned tid = threadIdx.x;
+  const unsigned nthr = blockDim.x;
+  const unsigned nch = (unsigned)nchunk;
+  const int nwaves = nthr / kWave;
+  const float Hf = (float)(nchunk * kVec);
+  int parity = 0;
+  for (int64_t blk = blockIdx.x; blk < M; blk += gridDim.x, parity ^= 1) {
+    const int64_t row = MODE == kModeNvfp4 ? nvfp4_row_of_block(blk, M) : blk;
+    const size_t rbase = (size_t)row * (size_t)nchunk;
+    const u32x4 *__restrict__ xr = x + rbase;
+    u32x4 *__restrict__ rr = res + rbase;
+    u32x4 *__restrict__ yr = y + rbase;
+    // All loads first: x and residual stream from HBM (non-temporal), the
+    // weight and the scale come from L2.  The scale's reciprocal is formed
+    // while the row loads are in flight.
+    u32x4 xa[CPT], ra[CPT], wa[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const unsigned ch = tid + c * nthr;
+      if (ch < nch) {
+        xa[c] = __builtin_nontemporal_load(&xr[ch]);
+        if constexpr (HAS_RES) ra[c] = __builtin_nontemporal_load(&rr[ch]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const unsigned ch = tid + c * nthr;
+      if (ch < nch) wa[c] = w[ch];
+    }
+    const float s = MODE == kModeNone ? 1.0f : *scale_ptr;
+    const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+    // h = RN(x + r), written back; sum of squares of the rounded h.
+    uint32_t hb[CPT][4];
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const unsigned ch = tid + c * nthr;
+      if (ch < nch) {
+        if constexpr (HAS_RES) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            hb[c][k] = D::pack(D::lo(xa[c][k]) + D::lo(ra[c][k]), D::hi(xa[c][k]) + D::hi(ra[c][k]));
+          const u32x4 o = {hb[c][0], hb[c][1], hb[c][2], hb[c][3]};
+          __builtin_nontemporal_store(o, &rr[ch]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) hb[c][k] = xa[c][k];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float a = D::lo(hb[c][k]), b = D::hi(hb[c][k]);
+          ss = __builtin_fmaf(a, a, ss);
+          ss = __builtin_fmaf(b, b, ss);
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if ((tid & (kWave - 1)) == 0) partial[parity][tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+    for (int i = 0; i < nwaves; ++i) tot += partial[parity][i];
+    const float rstd = 1.0f / __builtin_sqrtf(tot / Hf + eps);
+
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const unsigned ch = tid + c * nthr;
+      if (ch < nch) {
+        // y = RN(t * (1 + w)) (Gemma) or RN(t * w), t = h * rstd; the quant
+        // reads the rounded y.
+        float yv[kVec];
+        uint32_t yb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float ta = D::lo(hb[c][k]) * rstd, tb = D::hi(hb[c][k]) * rstd;
+          yb[k] = D::pack(norm_scale<GEMMA>(ta, D::lo(wa[c][k])), norm_scale<GEMMA>(tb, D::hi(wa[c][k])));
+          yv[2 * k] = D::lo(yb[k]);
+          yv[2 * k + 1] = D::hi(yb[k]);
+        }
+        if constexpr (WRITE_Y) {
+          const u32x4 o = {yb[0], yb[1], yb[2], yb[3]};
+          __builtin_nontemporal_store(o, &yr[ch]);
+        }
+        quant_store_chunk<MODE>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles);
+      }
+    }
+  }
+}
+
+// Several rows per wavefront for H <= 512.  A row takes LPR lanes (the power
+// of two >= H/8, one 8-element chunk per lane), a wave holds 64/LPR rows and
+// a 256-thread workgroup 4 times as many.
+constexpr int kSmallThreads = 256;
+
+template <class D, int MODE, bool HAS_RES, bool WRITE_Y, bool GEMMA, int LPR>
+__global__ void __launch_bounds__(kSmallThreads)
+fused_rows_small(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__restrict__ w,
+                 const float *__restrict__ scale_ptr, float eps, int64_t M, int nchunk,
+                 uint8_t *__restrict__ q, uint8_t *__restrict__ bs, u32x4 *__restrict__ y,
+                 int ktiles) {
+  constexpr int kRowsPerWg = kSmallThreads / LPR;
+  const unsigned tid = threadIdx.x;
+  const unsigned ch = tid % LPR;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + tid / LPR;
+  const bool active = row < M && ch < (unsigned)nchunk;
+  const size_t rbase = (size_t)(row < M ? row : 0) * (size_t)nchunk;
+  u32x4 xa = {0, 0, 0, 0}, ra = {0, 0, 0, 0}, wa = {0, 0, 0, 0};
+  if (active) {
+    xa = __builtin_nontemporal_load(&x[rbase + ch]);
+    if constexpr (HAS_RES) ra = __builtin_nontemporal_load(&res[rbase + ch]);
+    wa = w[ch];
+  }
+  const float s = MODE == kModeNone ? 1.0f : *scale_ptr;
+  const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+  uint32_t hb[4];
+  float ss = 0.0f;
+  if constexpr (HAS_RES) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hb[k] = D::pack(D::lo(xa[k]) + D::lo(ra[k]), D::hi(xa[k]) + D::hi(ra[k]));
+    if (active) {
+      const u32x4 o = {hb[0], hb[1], hb[2], hb[3]};
+      __builtin_nontemporal_store(o, &res[rbase + ch]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hb[k] = xa[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = D::lo(hb[k]), b = D::hi(hb[k]);
+    ss = __builtin_fmaf(a, a, ss);
+    ss = __builtin_fmaf(b, b, ss);
+  }
+  ss = group_sum<LPR>(ss);
+  const float rstd = 1.0f / __builtin_sqrtf(ss / (float)(nchunk * kVec) + eps);
+  float yv[kVec];
+  uint32_t yb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float ta = D::lo(hb[k]) * rstd, tb = D::hi(hb[k]) * rstd;
+    yb[k] = D::pack(norm_scale<GEMMA>(ta, D::lo(wa[k])), norm_scale<GEMMA>(tb, D::hi(wa[k])));
+    yv[2 * k] = D::lo(yb[k]);
+    yv[2 * k + 1] = D::hi(yb[k]);
+  }
+  if constexpr (WRITE_Y) {
+    if (active) {
+      const u32x4 o = {yb[0], yb[1], yb[2], yb[3]};
+      __builtin_nontemporal_store(o, &y[rbase + ch]);
+    }
+  }
+  // NVFP4 has H % 64 == 0, so the lanes of a row pair up into whole blocks
+  // and an inactive lane pairs only with an inactive lane.
+  if (active) quant_store_chunk<MODE>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles);
+}
+
+// Any H and any alignment: element loads, same arithmetic.
+template <class D, int MODE, bool HAS_RES, bool WRITE_Y, bool GEMMA>
+__global__ void __launch_bounds__(256)
+fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
+                  const uint16_t *__restrict__ w, const float *__restrict__ scale_ptr, float eps,
+                  int64_t M, int H, uint8_t *__restrict__ q, uint8_t *__restrict__ bs,
+                  uint16_t *__restrict__ y, int ktiles) {
+  __shared__ float partial[2][256 / kWave];
+  const int tid = threadIdx.x;
+  const int nwaves = blockDim.x / kWave;
+  const float s = MODE == kModeNone ? 1.0f : *scale_ptr;
+  const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x, parity ^= 1) {
+    const size_t rb = (size_t)row * (size_t)H;
+    float ss = 0.0f;
+    for (int j = tid; j < H; j += blockDim.x) {
+      uint32_t h = x[rb + j];
+      if constexpr (HAS_RES) {
+        h = D::pack(D::lo(h) + D::lo(res[rb + j]), 0.0f) & 0xffffu;
+        res[rb + j] = (uint16_t)h;
+      }
+      const float hf = D::lo(h);
+      ss = __builtin_fmaf(hf, hf, ss);
+    }
+    ss = wave_sum(ss);
+    if ((tid & (kWave - 1)) == 0) partial[parity][tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+    for (int i = 0; i < nwaves; ++i) tot += partial[parity][i];
+    const float rstd = 1.0f / __builtin_sqrtf(tot / (float)H + eps);
+    // After the barrier every thread may read h written by the others.
+    const uint16_t *hsrc = HAS_RES ? res : x;
+    if constexpr (MODE == kModeNvfp4) {
+      const int nb = H / kBlock;
+      for (int b = tid; b < nb; b += blockDim.x) {
+        float yv[kBlock];
+        for (int k = 0; k < kBlock; ++k) {
+          const int j = b * kBlock + k;
+          const uint32_t yq =
+              D::pack(norm_scale<GEMMA>(D::lo(hsrc[rb + j]) * rstd, D::lo(w[j])), 0.0f) & 0xffffu;
+          if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
+          yv[k] = D::lo(yq);
+        }
+        float amax = 0.0f;
+        for (int k = 0; k < kBlock; ++k) amax = fmaxf(amax, fabsf(yv[k]));
+        const uint32_t sc = nvfp4_scale_code(amax, s);
+        const float o = nvfp4_elem_scale(sc, s);
+        float v[kBlock];
+        for (int k = 0; k < kBlock; ++k) v[k] = yv[k] * o;
+        const uint32_t p0 = e2m1x8(v), p1 = e2m1x8(v + 8);
+        uint8_t *qp = q + (size_t)row * (size_t)(H / 2) + (size_t)b * 8;
+        for (int k = 0; k < 4; ++k) {
+          qp[k] = (uint8_t)(p0 >> (8 * k));
+          qp[4 + k] = (uint8_t)(p1 >> (8 * k));
+        }
+        bs[swz128x4(row, b, ktiles)] = (uint8_t)sc;
+      }
+    } else {
+      for (int j = tid; j < H; j += blockDim.x) {
+        const uint32_t yq =
+            D::pack(norm_scale<GEMMA>(D::lo(hsrc[rb + j]) * rstd, D::lo(w[j])), 0.0f) & 0xffffu;
+        if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
+        if constexpr (MODE == kModeFp8) q[rb + j] = (uint8_t)e4m3_one(div_by_scale(D::lo(yq), s, r_s));
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Launch: pick the kernel and shape for (M, H, alignment).
+
+// Chunks per thread for fused_rows: one 8-element chunk per thread up to
+// H = 4096 (short per-thread chains for latency), two up to H = 16384, four
+// up to H = 32768 (at most 1024 threads per workgroup).
+inline int chunks_per_thread(int64_t H) {
+  const int64_t nchunk = H / kVec;
+  if (H <= 4096) return 1;
+  if (nchunk <= 2 * kMaxThreads) return 2;
+  return 4;
+}
+
+inline bool aligned_to(const void *p, uintptr_t n) { return p == nullptr || ((uintptr_t)p % n) == 0; }
+
+// Whether fused_rows / fused_rows_small can take the call.
+inline bool vector_path_ok(const FusedArgs &a, int mode) {
+  return (a.H % kBlock == 0) && (a.H / kVec) <= 4 * kMaxThreads && aligned_to(a.x, 16) &&
+         aligned_to(a.res, 16) && aligned_to(a.w, 16) && aligned_to(a.y, 16) &&
+         aligned_to(a.q, mode == kModeNvfp4 ? 4 : 8);
+}
+
+template <class D, int MODE, bool RES, bool WY, bool GEMMA>
+hipError_t run_fused(const FusedArgs &a) {
+  const int ktiles = (int)(((a.H / kBlock) + 3) / 4);
+  const dim3 grid((unsigned)(a.M < kMaxGrid ? a.M : kMaxGrid));
+  const u32x4 *x = (const u32x4 *)a.x;
+  u32x4 *res = (u32x4 *)a.res;
+  const u32x4 *w = (const u32x4 *)a.w;
+  u32x4 *y = (u32x4 *)a.y;
+  uint8_t *q = (uint8_t *)a.q, *bs = (uint8_t *)a.bs;
+  if (vector_path_ok(a, MODE)) {
+    const int nchunk = (int)(a.H / kVec);
+    if (a.H <= 512 && a.M <= kMaxGrid) {
+#define GNQ_SMALL(L)                                                                              \
+  hipLaunchKernelGGL((fused_rows_small<D, MODE, RES, WY, GEMMA, L>),                              \
+                     dim3((unsigned)((a.M + kSmallThreads / L - 1) / (kSmallThreads / L))),       \
+                     dim3(kSmallThreads), 0, a.st, x, res, w, a.scale, a.eps, a.M, nchunk, q, bs, \
+                     y, ktiles)
+      if (nchunk <= 2) GNQ_SMALL(2);
+      else if (nchunk <= 4) GNQ_SMALL(4);
+      else if (nchunk <= 8) GNQ_SMALL(8);
+      else if (nchunk <= 16) GNQ_SMALL(16);
+      else if (nchunk <= 32) GNQ_SMALL(32);
+      else GNQ_SMALL(64);
+#undef GNQ_SMALL
+      return hipGetLastError();
+    }
+    const int cpt = chunks_per_thread(a.H);
+    const int per_thread = (nchunk + cpt - 1) / cpt;
+    const dim3 block(((per_thread + kWave - 1) / kWave) * kWave);
+#define GNQ_VEC(C)                                                                          \
+  hipLaunchKernelGGL((fused_rows<D, MODE, RES, WY, GEMMA, C>), grid, block, 0, a.st, x, res, w, \
+                     a.scale, a.eps, a.M, nchunk, q, bs, y, ktiles)
+    if (cpt == 1) GNQ_VEC(1);
+    else if (cpt == 2) GNQ_VEC(2);
+    else GNQ_VEC(4);
+#undef GNQ_VEC
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((fused_rows_scalar<D, MODE, RES, WY, GEMMA>), grid, dim3(256), 0, a.st,
+                     (const uint16_t *)a.x, (uint16_t *)a.res, (const uint16_t *)a.w, a.scale,
+                     a.eps, a.M, (int)a.H, q, bs, (uint16_t *)a.y, ktiles);
+  return hipGetLastError();
+}
+
+template <class D, int MODE>
+hipError_t dispatch_fused(const FusedArgs &a) {
+  const bool res = a.res != nullptr, wy = a.y != nullptr;
+  if constexpr (MODE == kModeNone) {
+    // y is the only output in this mode.
+    if (a.gemma) return res ? run_fused<D, MODE, true, true, true>(a) : run_fused<D, MODE, false, true, true>(a);
+    return res ? run_fused<D, MODE, true, true, false>(a) : run_fused<D, MODE, false, true, false>(a);
+  } else {
+    if (a.gemma) {
+      if (res) return wy ? run_fused<D, MODE, true, true, true>(a) : run_fused<D, MODE, true, false, true>(a);
+      return wy ? run_fused<D, MODE, false, true, true>(a) : run_fused<D, MODE, false, false, true>(a);
+    }
+    if (res) return wy ? run_fused<D, MODE, true, true, false>(a) : run_fused<D, MODE, true, false, false>(a);
+    return wy ? run_fused<D, MODE, false, true, false>(a) : run_fused<D, MODE, false, false, false>(a);
+  }
+}
+
+}  // namespace gnq

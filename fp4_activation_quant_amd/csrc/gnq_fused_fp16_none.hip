@@ -1,0 +1,7 @@
+// Fused add + RMSNorm kernels for fp16 activations, none output (one
+// translation unit per dtype and mode so the library builds in parallel).
+#include "gnq_fused.hpp"
+
+namespace gnq {
+hipError_t fused_fp16_none(const FusedArgs &a) { return dispatch_fused<Fp16, kModeNone>(a); }
+}  // namespace gnq

@@ -57,19 +57,102 @@ def gemma_add_rms_norm_quant(x, residual, weight, eps, scale, nvfp4, write_y=Fal
     return q, block_scale, y
 
 
+def _ptr(t):
+    return t.data_ptr() if t is not None else 0
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
 def gemma_add_rms_norm_quant_out(x, residual, weight, eps, scale, nvfp4, q, block_scale, y):
     """Same op into caller-allocated outputs (no allocation, no checks beyond
     the library's own).  ``y`` None means write_y=False."""
     M, H = x.shape
     with torch.cuda.device(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
         st = _lib.nq_gemma_add_rms_norm_quant(
-            x.data_ptr(), residual.data_ptr() if residual is not None else 0, weight.data_ptr(),
-            eps, scale.data_ptr(), M, H, _DT[x.dtype],
-            _lib.NQ_MODE_NVFP4 if nvfp4 else _lib.NQ_MODE_FP8_STATIC, y is not None,
-            q.data_ptr(), block_scale.data_ptr() if block_scale is not None else 0,
-            y.data_ptr() if y is not None else 0, stream)
+            x.data_ptr(), _ptr(residual), weight.data_ptr(), eps, scale.data_ptr(), M, H,
+            _DT[x.dtype], _lib.NQ_MODE_NVFP4 if nvfp4 else _lib.NQ_MODE_FP8_STATIC, y is not None,
+            q.data_ptr(), _ptr(block_scale), _ptr(y), _stream(x.device))
     _check(st, "nq_gemma_add_rms_norm_quant")
+
+
+_MODES = {"fp8": _lib.NQ_MODE_FP8_STATIC, "nvfp4": _lib.NQ_MODE_NVFP4, None: _lib.NQ_MODE_NONE}
+_NORMS = {"gemma": _lib.NQ_NORM_GEMMA, "plain": _lib.NQ_NORM_PLAIN}
+
+
+def add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q, block_scale, y):
+    """The op with the norm ("gemma": 1 + w, "plain": w) and the output mode
+    ("fp8", "nvfp4" or None for add + norm alone) chosen, into
+    caller-allocated outputs."""
+    M, H = x.shape
+    with torch.cuda.device(x.device):
+        st = _lib.nq_add_rms_norm_quant(
+            x.data_ptr(), _ptr(residual), weight.data_ptr(), eps, _ptr(scale), M, H, _DT[x.dtype],
+            _NORMS[norm], _MODES[mode], y is not None, _ptr(q), _ptr(block_scale), _ptr(y),
+            _stream(x.device))
+    _check(st, "nq_add_rms_norm_quant")
+
+
+def add_rms_norm_quant(x, residual, weight, eps, scale, mode, norm="gemma", write_y=False):
+    """Allocating form of add_rms_norm_quant_out: returns (q, block_scale, y)
+    as gemma_add_rms_norm_quant does; mode None returns (None, None, y)."""
+    assert x.dim() == 2 and x.is_contiguous() and x.dtype in _DT and x.is_cuda
+    M, H = x.shape
+    if mode is None:
+        y = torch.empty_like(x)
+        if M:
+            add_rms_norm_quant_out(x, residual, weight, eps, None, None, norm, None, None, y)
+        return None, None, y
+    if mode == "nvfp4":
+        assert H % 64 == 0
+        q = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device)
+        block_scale = torch.empty((round_up(M, 128), round_up(H // 16, 4) // 4),
+                                  dtype=torch.int32, device=x.device).view(FP8_DTYPE)
+    else:
+        q = torch.empty((M, H), dtype=FP8_DTYPE, device=x.device)
+        block_scale = scale
+    y = torch.empty_like(x) if write_y else None
+    if M:
+        add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q,
+                               block_scale if mode == "nvfp4" else None, y)
+    return q, block_scale, y
+
+
+def gemma_add_rms_norm(x, residual, weight, eps):
+    """Add + Gemma RMSNorm without quant (residual updated in place); returns y."""
+    return add_rms_norm_quant(x, residual, weight, eps, None, None, "gemma", True)[2]
+
+
+def quant_fp8_static(y, scale, q=None):
+    """Standalone static FP8 quant of an activation: E4M3FN(y / scale)."""
+    assert y.dim() == 2 and y.is_contiguous() and y.dtype in _DT and y.is_cuda
+    M, H = y.shape
+    if q is None:
+        q = torch.empty((M, H), dtype=FP8_DTYPE, device=y.device)
+    if M:
+        with torch.cuda.device(y.device):
+            st = _lib.nq_quant_fp8_static(y.data_ptr(), scale.data_ptr(), M, H, _DT[y.dtype],
+                                          q.data_ptr(), _stream(y.device))
+        _check(st, "nq_quant_fp8_static")
+    return q
+
+
+def quant_nvfp4(y, global_scale, q=None, block_scale=None):
+    """Standalone NVFP4 quant: packed E2M1 codes and 128x4-tiled E4M3 scales."""
+    assert y.dim() == 2 and y.is_contiguous() and y.dtype in _DT and y.is_cuda
+    M, H = y.shape
+    if q is None:
+        q = torch.empty((M, H // 2), dtype=torch.uint8, device=y.device)
+    if block_scale is None:
+        block_scale = torch.empty((round_up(M, 128), round_up(H // 16, 4) // 4),
+                                  dtype=torch.int32, device=y.device).view(FP8_DTYPE)
+    if M:
+        with torch.cuda.device(y.device):
+            st = _lib.nq_quant_nvfp4(y.data_ptr(), global_scale.data_ptr(), M, H, _DT[y.dtype],
+                                     q.data_ptr(), block_scale.data_ptr(), _stream(y.device))
+        _check(st, "nq_quant_nvfp4")
+    return q, block_scale
 
 
 def block_scale_bytes(M, H):

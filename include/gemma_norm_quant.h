@@ -24,11 +24,15 @@
  *              (m%32)*16 + ((m%128)/32)*4 + b%4, Kp = round_up(H/16, 4));
  *              rows >= M of that buffer are never written.
  *
- * All pointers except `scale`'s owner are caller-owned device buffers on the
- * current HIP device.  The library allocates nothing, keeps no pointer past
- * the call and launches asynchronously on `stream` (a hipStream_t; NULL is
- * the null stream).  On any error nothing is launched and nothing is
- * written.  No C++ exception crosses this boundary.
+ * Around it the library also exports the op's variants and its unfused form:
+ * the same add + RMSNorm with a plain (w instead of 1 + w) norm and/or with
+ * no quant, and the standalone FP8 / NVFP4 quant of an activation.
+ *
+ * All pointers are caller-owned device buffers on the current HIP device.
+ * The library allocates nothing, keeps no pointer past the call and launches
+ * asynchronously on `stream` (a hipStream_t; NULL is the null stream).  On
+ * any error nothing is launched and nothing is written.  No C++ exception
+ * crosses this boundary.
  */
 #ifndef GEMMA_NORM_QUANT_H
 #define GEMMA_NORM_QUANT_H
@@ -40,18 +44,21 @@
 extern "C" {
 #endif
 
-#define NQ_ABI_VERSION 1
+#define NQ_ABI_VERSION 2
 
 typedef enum {
   NQ_OK = 0,
   NQ_EINVAL = 1,        /* null required pointer, bad size, bad enum, aliasing */
-  NQ_EUNSUPPORTED = 2,  /* NVFP4 with H % 64 != 0 */
+  NQ_EUNSUPPORTED = 2,  /* NVFP4 with H % 64 != 0 (or H % 16 != 0 for the standalone quant) */
   NQ_EHIP = 3           /* a HIP runtime call or the launch failed */
 } nq_status;
 
 typedef enum { NQ_BF16 = 0, NQ_FP16 = 1 } nq_dtype;
 
-typedef enum { NQ_MODE_FP8_STATIC = 0, NQ_MODE_NVFP4 = 1 } nq_mode;
+typedef enum { NQ_MODE_FP8_STATIC = 0, NQ_MODE_NVFP4 = 1, NQ_MODE_NONE = 2 } nq_mode;
+
+/* RMSNorm scaling: Gemma's (1 + weight), or plain weight. */
+typedef enum { NQ_NORM_GEMMA = 0, NQ_NORM_PLAIN = 1 } nq_norm;
 
 /*
  * nq_gemma_add_rms_norm_quant -- the op above, one launch.
@@ -88,6 +95,50 @@ nq_status nq_gemma_add_rms_norm_quant(const void *x, void *residual, const void 
                                       float eps, const float *scale, int64_t M, int64_t H,
                                       int dtype, int mode, int write_y, void *q,
                                       void *block_scale, void *y, void *stream);
+
+/*
+ * nq_add_rms_norm_quant -- the same op with the norm and the output chosen:
+ *
+ *   norm   NQ_NORM_GEMMA: y scales by (1 + weight), as above;
+ *          NQ_NORM_PLAIN: y scales by weight (plain RMSNorm, the
+ *          `rms_norm_static_fp8_quant` / `fused_add_rms_norm_static_fp8_quant`
+ *          semantics named on the PR conversation page).
+ *   mode   NQ_MODE_FP8_STATIC / NQ_MODE_NVFP4 as above, or NQ_MODE_NONE: no
+ *          quant, the op is add + RMSNorm alone (the tensor-parallel-size-1
+ *          path of `fused_allreduce_gemma_rms_norm`, "identical to the unfused
+ *          path"); then write_y must be nonzero and y non-NULL, and scale, q
+ *          and block_scale are ignored (may be NULL).
+ *
+ * Other arguments, layouts and errors as for nq_gemma_add_rms_norm_quant,
+ * which equals this call with norm = NQ_NORM_GEMMA.
+ */
+nq_status nq_add_rms_norm_quant(const void *x, void *residual, const void *weight, float eps,
+                                const float *scale, int64_t M, int64_t H, int dtype, int norm,
+                                int mode, int write_y, void *q, void *block_scale, void *y,
+                                void *stream);
+
+/*
+ * nq_quant_fp8_static / nq_quant_nvfp4 -- the standalone quant kernels of
+ * the unfused chain (the `fused_norm_quant` module docstring: the fused
+ * kernel replaces the Gemma add-RMSNorm followed by a standalone static FP8
+ * or NVFP4 quant, with the same scale arithmetic).  y is an (M, H)
+ * activation of `dtype`, row-major contiguous; the codes, block scales,
+ * rounding and layout are exactly the fused op's quant step.
+ *
+ *   nq_quant_fp8_static: scale = DEVICE pointer to the static per-tensor
+ *     scale; q = (M, H) E4M3FN bytes.  Any H >= 1.
+ *   nq_quant_nvfp4: global_scale = DEVICE pointer to the NVFP4 global scale;
+ *     q = (M, H/2) packed E2M1 bytes; block_scale = nq_block_scale_bytes(M, H)
+ *     bytes, 128x4-tiled, rows >= M left as they were.  H % 16 == 0
+ *     (NQ_EUNSUPPORTED otherwise); a partial last 4-column tile (H % 64 != 0)
+ *     keeps its unused columns untouched.
+ *
+ * M == 0 returns NQ_OK without launching.
+ */
+nq_status nq_quant_fp8_static(const void *y, const float *scale, int64_t M, int64_t H, int dtype,
+                              void *q, void *stream);
+nq_status nq_quant_nvfp4(const void *y, const float *global_scale, int64_t M, int64_t H, int dtype,
+                         void *q, void *block_scale, void *stream);
 
 /* Size in bytes of the NVFP4 block-scale buffer:
  * round_up(M, 128) * round_up(H / 16, 4) (the wrapper's allocation on the

@@ -28,7 +28,7 @@ from .formats import (  # noqa: F401
     bits_to_f64, f64_to_bits,
 )
 from .norm_quant import (  # noqa: F401
-    add_residual, gemma_rms_norm, quant_fp8_static, quant_nvfp4,
+    add_residual, gemma_rms_norm, rms_norm, quant_fp8_static, quant_nvfp4,
     swizzle_128x4_offset, block_scale_buffer_shape, scatter_block_scales,
-    gemma_add_rms_norm_quant,
+    gemma_add_rms_norm_quant, add_rms_norm_quant,
 )

@@ -35,9 +35,9 @@ import numpy as np
 from .formats import BF16, FP16, E4M3FN, E2M1, Format, bits_to_f64, f64_to_bits, encode, decode
 
 __all__ = [
-    "add_residual", "gemma_rms_norm", "quant_fp8_static", "quant_nvfp4",
+    "add_residual", "gemma_rms_norm", "rms_norm", "quant_fp8_static", "quant_nvfp4",
     "swizzle_128x4_offset", "block_scale_buffer_shape", "scatter_block_scales",
-    "gemma_add_rms_norm_quant",
+    "gemma_add_rms_norm_quant", "add_rms_norm_quant",
 ]
 
 NVFP4_BLOCK = 16      # elements per block scale ("16-element blocks")
@@ -73,6 +73,13 @@ def gemma_rms_norm(h_bits, w_bits, eps: float, fmt: Format) -> np.ndarray:
     which the kernel receives as an fp32 scalar, so it is first rounded to
     fp32 here.  Row-wise: ``h`` is (M, H), ``w`` is (H,).
     """
+    return rms_norm(h_bits, w_bits, eps, fmt, gemma=True)
+
+
+def rms_norm(h_bits, w_bits, eps: float, fmt: Format, gemma: bool) -> np.ndarray:
+    """RMSNorm scaled by (1 + w) (Gemma) or by w (plain RMSNorm, the norm of
+    the ``rms_norm_static_fp8_quant`` kernels named on the PR conversation
+    page, which "apply gamma * x_normed directly"); fp64, one rounding."""
     _check_fmt(fmt)
     h = bits_to_f64(h_bits, fmt)
     w = bits_to_f64(w_bits, fmt)
@@ -82,7 +89,7 @@ def gemma_rms_norm(h_bits, w_bits, eps: float, fmt: Format) -> np.ndarray:
     eps64 = float(np.float32(eps))
     mean_sq = np.sum(h * h, axis=1) / H
     rstd = 1.0 / np.sqrt(mean_sq + eps64)
-    y = (h * rstd[:, None]) * (1.0 + w)[None, :]
+    y = (h * rstd[:, None]) * ((1.0 + w) if gemma else w)[None, :]
     return f64_to_bits(y, fmt)
 
 
@@ -186,7 +193,18 @@ def scatter_block_scales(S, M: int, H: int, out: np.ndarray) -> np.ndarray:
 def gemma_add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale,
                              nvfp4: bool, write_y: bool = False, fmt: Format = BF16,
                              block_scale_fill: int = 0xA5):
-    """The whole op, as the unfused chain.
+    """The page's op (Gemma norm, FP8 or NVFP4); see add_rms_norm_quant."""
+    out = add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale,
+                             "nvfp4" if nvfp4 else "fp8", "gemma", fmt, block_scale_fill)
+    out["write_y"] = bool(write_y)
+    return out
+
+
+def add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale, mode, norm="gemma",
+                       fmt: Format = BF16, block_scale_fill: int = 0xA5):
+    """The whole op, as the unfused chain, with the norm ("gemma": 1 + w,
+    "plain": w) and the output ("fp8", "nvfp4", or None: add + norm only)
+    chosen.
 
     Arguments follow ``gemma_add_rms_norm_quant`` on the ``fused_norm_quant``
     page, with x, residual (or None) and weight as 16-bit patterns of
@@ -201,6 +219,8 @@ def gemma_add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale,
                  returns it only when write_y)
     """
     _check_fmt(fmt)
+    if mode not in ("fp8", "nvfp4", None) or norm not in ("gemma", "plain"):
+        raise ValueError("mode must be fp8, nvfp4 or None; norm gemma or plain")
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     if x_bits.ndim != 2:
         raise ValueError("x must be 2-D")
@@ -209,15 +229,18 @@ def gemma_add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale,
         h = add_residual(x_bits, residual_bits, fmt)
     else:
         h = x_bits
+    nvfp4 = mode == "nvfp4"
     if nvfp4 and H % 64:
         raise ValueError("NVFP4 needs H % 64 == 0")
     out = {"residual": h if residual_bits is not None else None}
     if M == 0:
         y = np.zeros((0, H), np.uint16)
     else:
-        y = gemma_rms_norm(h, weight_bits, eps, fmt)
+        y = rms_norm(h, weight_bits, eps, fmt, gemma=(norm == "gemma"))
     out["y"] = y
-    if nvfp4:
+    if mode is None:
+        out.update(q=None, scales=None, block_scale=None)
+    elif nvfp4:
         if M:
             q, S = quant_nvfp4(y, fmt, scale)
         else:
@@ -228,5 +251,4 @@ def gemma_add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale,
     else:
         q = quant_fp8_static(y, fmt, scale) if M else np.zeros((0, H), np.uint8)
         out.update(q=q, scales=None, block_scale=float(np.float32(scale)))
-    out["write_y"] = bool(write_y)
     return out

@@ -42,10 +42,16 @@ def _guarded(nbytes, dev):
     return torch.full((nbytes + GUARD,), SENTINEL, dtype=torch.uint8, device=dev)
 
 
-def run_gpu(x, r, w, eps, scale, nvfp4, write_y, device="cuda", misalign=False):
+def run_gpu(x, r, w, eps, scale, nvfp4, write_y, device="cuda", misalign=False, norm="gemma",
+            quant=True):
     """Run the HIP op once on device copies of CPU tensors.  Returns numpy
     outputs and the guard/padding state.  ``misalign`` places x, residual and
-    y at a 2-byte offset (a non-16-byte-aligned view)."""
+    y at a 2-byte offset (a non-16-byte-aligned view).  ``norm`` "plain"
+    scales by w instead of 1 + w; ``quant`` False runs add + norm alone (y is
+    then always written)."""
+    mode = ("nvfp4" if nvfp4 else "fp8") if quant else None
+    if not quant:
+        write_y, nvfp4 = True, False
     dev = torch.device(device)
     M, H = x.shape
     dt = x.dtype
@@ -63,26 +69,31 @@ def run_gpu(x, r, w, eps, scale, nvfp4, write_y, device="cuda", misalign=False):
     rbuf, rd = place(r) if r is not None else (None, None)
     wd = w.to(dev).contiguous()
     sd = torch.tensor([scale], dtype=torch.float32, device=dev)
-    qbytes = M * (H // 2) if nvfp4 else M * H
+    qbytes = (M * (H // 2) if nvfp4 else M * H) if quant else 0
     qbuf = _guarded(qbytes + off, dev)
     qv = qbuf[off:off + qbytes]
-    qv = qv.view(M, H // 2) if nvfp4 else qv.view(torch.float8_e4m3fn).view(M, H)
+    if quant:
+        qv = qv.view(M, H // 2) if nvfp4 else qv.view(torch.float8_e4m3fn).view(M, H)
     bsn = ops.block_scale_bytes(M, H) if nvfp4 else 0
     bsbuf = _guarded(bsn, dev) if nvfp4 else None
     ybuf, yd = place(None) if write_y else (None, None)
-    ops.gemma_add_rms_norm_quant_out(xd, rd, wd, eps, sd, nvfp4, qv,
-                                     bsbuf[:bsn] if nvfp4 else None, yd)
+    if norm == "gemma" and quant:
+        ops.gemma_add_rms_norm_quant_out(xd, rd, wd, eps, sd, nvfp4, qv,
+                                         bsbuf[:bsn] if nvfp4 else None, yd)
+    else:
+        ops.add_rms_norm_quant_out(xd, rd, wd, eps, sd if quant else None, mode, norm,
+                                   qv if quant else None, bsbuf[:bsn] if nvfp4 else None, yd)
     torch.cuda.synchronize(dev)
 
     def tail_ok(buf, n):
         return bool((buf[off + n:].cpu() == SENTINEL).all()) and bool((buf[:off].cpu() == SENTINEL).all())
 
     out = {
-        "M": M, "H": H, "nvfp4": nvfp4, "dtype": dt,
+        "M": M, "H": H, "nvfp4": nvfp4, "dtype": dt, "mode": mode, "norm": norm,
         "x_unchanged": bool(torch.equal(xd.cpu(), x)),
         "residual": bits16(rd) if rd is not None else None,
         "y": bits16(yd) if yd is not None else None,
-        "q": qv.view(torch.uint8).cpu().numpy() if not nvfp4 else qv.cpu().numpy(),
+        "q": (qv.view(torch.uint8).cpu().numpy() if not nvfp4 else qv.cpu().numpy()) if quant else None,
         "bs": bsbuf[:bsn].cpu().numpy() if nvfp4 else None,
         "guards_ok": all([tail_ok(xbuf, act), tail_ok(qbuf, qbytes),
                           rbuf is None or tail_ok(rbuf, act), ybuf is None or tail_ok(ybuf, act),
@@ -127,11 +138,12 @@ def compare(gpu, x, r, w, eps, scale, rows, y_gpu=None):
     """Compare a GPU run with the oracle on ``rows``.  ``y_gpu`` (full (M, H)
     uint16) is the GPU's y when the run itself did not write it."""
     M, H, nvfp4 = gpu["M"], gpu["H"], gpu["nvfp4"]
+    mode, norm = gpu.get("mode", "nvfp4" if nvfp4 else "fp8"), gpu.get("norm", "gemma")
     fmt = FMT[x.dtype]
     rows = np.asarray(rows, dtype=np.int64)
     xb = bits16(x)[rows]
     rb = bits16(r)[rows] if r is not None else None
-    ref = O.gemma_add_rms_norm_quant(xb, rb, bits16(w), eps, scale, nvfp4, True, fmt)
+    ref = O.add_rms_norm_quant(xb, rb, bits16(w), eps, scale, mode, norm, fmt)
     rep = {"rows": len(rows), "elements": len(rows) * H, "guards_ok": gpu["guards_ok"],
            "x_unchanged": gpu["x_unchanged"]}
     if r is not None:
@@ -145,6 +157,10 @@ def compare(gpu, x, r, w, eps, scale, rows, y_gpu=None):
         y_equal = dy == 0
     else:
         y_equal = None
+    if mode is None:
+        rep["code_max_step"] = 0
+        rep["code_diff_fraction"] = 0.0
+        return rep
     if nvfp4:
         cg = _unpack_e2m1(gpu["q"][rows])
         cr = _unpack_e2m1(ref["q"])

@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert _lib.nq_abi_version() == 1
+    assert _lib.nq_abi_version() == 2
     assert _lib.nq_status_string(0) == "ok"
     for s in range(0, 6):
         assert isinstance(_lib.nq_status_string(s), str)
@@ -87,6 +87,57 @@ def call(**over):
 ])
 def test_validation(over, want):
     assert call(**over) == want
+
+
+def call_ex(**over):
+    a = dict(x=X, r=R, w=W, eps=1e-6, s=S, M=4, H=128, dtype=0, norm=0, mode=0, wy=0, q=Q, bs=B, y=Y)
+    a.update(over)
+    return _lib.nq_add_rms_norm_quant(a["x"], a["r"], a["w"], a["eps"], a["s"], a["M"], a["H"],
+                                      a["dtype"], a["norm"], a["mode"], a["wy"], a["q"], a["bs"],
+                                      a["y"], 0)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(norm=2), _lib.NQ_EINVAL),
+    (dict(mode=3), _lib.NQ_EINVAL),
+    (dict(mode=2, wy=0), _lib.NQ_EINVAL),            # no-quant mode needs y
+    (dict(mode=2, wy=1, y=0), _lib.NQ_EINVAL),
+    (dict(mode=2, wy=1, y=X + 64), _lib.NQ_EINVAL),  # y overlaps x
+    (dict(mode=2, wy=1, s=0, q=0, bs=0, M=0), _lib.NQ_OK),   # scale/q ignored in no-quant mode
+    (dict(norm=1, mode=1, H=96), _lib.NQ_EUNSUPPORTED),
+    (dict(norm=1, M=0), _lib.NQ_OK),
+    (dict(x=0, norm=1), _lib.NQ_EINVAL),
+])
+def test_general_entry_validation(over, want):
+    assert call_ex(**over) == want
+
+
+def test_gemma_entry_rejects_no_quant_mode():
+    assert call(mode=2, wy=1, M=0) == _lib.NQ_EINVAL
+
+
+@pytest.mark.parametrize("nv,over,want", [
+    (False, dict(y=0), _lib.NQ_EINVAL),
+    (False, dict(s=0), _lib.NQ_EINVAL),
+    (False, dict(q=0), _lib.NQ_EINVAL),
+    (False, dict(dtype=5), _lib.NQ_EINVAL),
+    (False, dict(H=0), _lib.NQ_EINVAL),
+    (False, dict(q=X + 10), _lib.NQ_EINVAL),          # q overlaps y
+    (False, dict(M=0), _lib.NQ_OK),
+    (False, dict(H=7, M=0), _lib.NQ_OK),             # any H for FP8
+    (True, dict(bs=0), _lib.NQ_EINVAL),
+    (True, dict(H=24), _lib.NQ_EUNSUPPORTED),
+    (True, dict(H=48, M=0), _lib.NQ_OK),             # H % 16 == 0 suffices standalone
+    (True, dict(bs=Q + 4), _lib.NQ_EINVAL),
+])
+def test_standalone_quant_validation(nv, over, want):
+    a = dict(y=X, s=S, M=4, H=128, dtype=0, q=Q, bs=B)
+    a.update(over)
+    if nv:
+        st = _lib.nq_quant_nvfp4(a["y"], a["s"], a["M"], a["H"], a["dtype"], a["q"], a["bs"], 0)
+    else:
+        st = _lib.nq_quant_fp8_static(a["y"], a["s"], a["M"], a["H"], a["dtype"], a["q"], 0)
+    assert st == want
 
 
 def test_probe_validation():

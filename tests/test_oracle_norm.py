@@ -189,3 +189,47 @@ def test_empty_batch():
         assert out["q"].shape[0] == 0
         if nv:
             assert out["block_scale"].size == 0
+
+
+@pytest.mark.parametrize("fmt", [O.BF16, O.FP16])
+def test_plain_norm_matches_torch_rms_norm_with_weight(fmt):
+    """Plain RMSNorm (scale by w) against torch's rms_norm(weight=w) in
+    float64, with the same half-way-point allowance as above."""
+    M, H = 16, 768
+    g = torch.Generator().manual_seed(23)
+    h = (torch.randn(M, H, generator=g) * 2).to(TORCH[fmt])
+    w = (torch.randn(H, generator=g) * 0.5 + 1).to(TORCH[fmt])
+    ours = O.rms_norm(to_bits(h), to_bits(w), 1e-6, fmt, gemma=False)
+    ref64 = torch.nn.functional.rms_norm(h.double(), (H,), weight=w.double(), eps=float(np.float32(1e-6)))
+    ref = to_bits(ref64.to(TORCH[fmt]))
+    diff = ours != ref
+    assert not np.any(diff & ~_near_midpoint(ref64.numpy(), fmt))
+    assert diff.mean() < 1e-4
+
+
+def test_plain_norm_constant_rows_and_gemma_equivalence():
+    """Constant rows: plain y = RN(+-w).  And plain(w) == Gemma(w - 1) when
+    w - 1 is exact (w a multiple of 2^-7 in [0.5, 2))."""
+    H = 128
+    g = torch.Generator().manual_seed(29)
+    w = (torch.randint(64, 256, (H,), generator=g).double() / 128).to(torch.bfloat16)
+    sign = torch.where(torch.rand(3, H, generator=g) < 0.5, -1.0, 1.0).double()
+    h = (sign * 4.0).to(torch.bfloat16)
+    y = O.rms_norm(to_bits(h), to_bits(w), 0.0, O.BF16, gemma=False)
+    assert np.array_equal(y, to_bits((sign * w.double()).to(torch.bfloat16)))
+    hr = torch.randn(5, H, generator=g).to(torch.bfloat16)
+    wg = (w.double() - 1).to(torch.bfloat16)
+    assert torch.equal(wg.double() + 1, w.double())
+    assert np.array_equal(O.rms_norm(to_bits(hr), to_bits(w), 1e-6, O.BF16, gemma=False),
+                          O.rms_norm(to_bits(hr), to_bits(wg), 1e-6, O.BF16, gemma=True))
+
+
+def test_no_quant_mode_returns_residual_and_y_only():
+    g = torch.Generator().manual_seed(31)
+    x = torch.randn(4, 64, generator=g).to(torch.bfloat16)
+    r = torch.randn(4, 64, generator=g).to(torch.bfloat16)
+    w = (torch.randn(64, generator=g) * 0.1).to(torch.bfloat16)
+    out = O.add_rms_norm_quant(to_bits(x), to_bits(r), to_bits(w), 1e-6, None, None)
+    assert out["q"] is None and out["block_scale"] is None
+    ref = O.gemma_add_rms_norm_quant(to_bits(x), to_bits(r), to_bits(w), 1e-6, 0.1, False, True)
+    assert np.array_equal(out["y"], ref["y"]) and np.array_equal(out["residual"], ref["residual"])
