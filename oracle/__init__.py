@@ -10,6 +10,10 @@ The op is the one stated on the ``fused_norm_quant`` page
 that scales by ``(1 + weight)``; the normed activation rounded to x's dtype;
 then either static per-tensor FP8 E4M3 codes or NVFP4 (packed E2M1 codes with
 one E4M3 scale per 16-element block, stored in the 128x4-tiled scale layout).
+Its variants: a plain (w instead of 1 + w) norm, no quant, and MXFP8 (E4M3
+codes with one E8M0 power-of-two scale per 32-element block, the
+``allreduce_gemma_rms_norm_mxfp8`` variant on the
+``fused_allreduce_gemma_rms_norm`` page).
 The page says the fused kernel computes the same codes as the unfused chain
 (add+norm, then a standalone quant); the oracle is written as that chain.
 
@@ -25,10 +29,11 @@ Parity status per function is in each module's header.
 
 from .formats import (  # noqa: F401
     BF16, FP16, E4M3FN, E2M1, round_rne, encode, decode, decode_table,
-    bits_to_f64, f64_to_bits,
+    decode_e8m0, bits_to_f64, f64_to_bits,
 )
 from .norm_quant import (  # noqa: F401
     add_residual, gemma_rms_norm, rms_norm, quant_fp8_static, quant_nvfp4,
+    mxfp8_block_exponent, quant_mxfp8,
     swizzle_128x4_offset, block_scale_buffer_shape, scatter_block_scales,
     gemma_add_rms_norm_quant, add_rms_norm_quant,
 )

@@ -14,6 +14,11 @@ Formats used by the op:
   finite value 448.
 * E2M1 -- the NVFP4 element code (``_cvt_e2m1x2`` on the ``fused_norm_quant``
   page): bias 1, one mantissa bit, no Inf/NaN, largest value 6.
+* E8M0 -- the MXFP8 block-scale code (the scales, one per 32 values and
+  stored row by row, that ``allreduce_gemma_rms_norm_mxfp8`` returns on the
+  ``fused_allreduce_gemma_rms_norm`` page).  Read as the scale type of the OCP Microscaling (MX) formats: an
+  unsigned 8-bit exponent with bias 127 and nothing else, value
+  2**(code - 127); no sign, no zero, code 255 is NaN.
 
 Rounding (``round_rne``): the nearest value on the format's grid, ties to the
 value whose code has an even mantissa field (round-to-nearest-even), with
@@ -28,7 +33,8 @@ Parity: pinned by tests/test_oracle_formats.py -- decode tables against
 torch's CPU float8_e4m3fn/bfloat16/float16 casts, the E2M1 table against the
 golden list of its eight magnitudes, and every encoder against (a) torch's CPU
 casts and (b) a brute-force nearest-value search, over every tie and
-tie-neighbour of the fp32 inputs that matter plus random inputs.
+tie-neighbour of the fp32 inputs that matter plus random inputs; the E8M0
+table against torch's CPU float8_e8m0fnu.
 """
 
 from dataclasses import dataclass
@@ -84,6 +90,12 @@ def decode(codes, fmt: Format) -> np.ndarray:
     if fmt.fn_nan_only:
         mag = np.where((e == emax_field) & (m == (1 << fmt.man_bits) - 1), np.nan, mag)
     return np.where(s == 1, -mag, mag)
+
+
+def decode_e8m0(codes) -> np.ndarray:
+    """Value of each E8M0 code (float64): 2**(code - 127), NaN for 255."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    return np.where(c == 255, np.nan, np.ldexp(1.0, (c - 127).astype(np.int32)))
 
 
 def decode_table(fmt: Format) -> np.ndarray:

@@ -27,7 +27,12 @@ design notes):
         o = gs / decode(S)  (0 when S decodes to 0);
         c = E2M1_RNE(clamp(y * o, -6, 6));  byte = c[2k] | c[2k+1] << 4;
   * scale bytes are stored at swizzle_128x4_offset(m, b); rows >= M of the
-    padded buffer are never written.
+    padded buffer are never written;
+  * MXFP8 (the ``allreduce_gemma_rms_norm_mxfp8`` variant on the
+    ``fused_allreduce_gemma_rms_norm`` page, which gives only its outputs'
+    types and shapes) per 32-element block, with the OCP MX scale rule:
+        a = max|y|;  e = max(floor(log2 a) - 8, -127)  (-127 when a = 0);
+        scale code = e + 127 (E8M0);  q = E4M3FN_RNE(clamp(y * 2^-e, +-448)).
 """
 
 import numpy as np
@@ -36,6 +41,7 @@ from .formats import BF16, FP16, E4M3FN, E2M1, Format, bits_to_f64, f64_to_bits,
 
 __all__ = [
     "add_residual", "gemma_rms_norm", "rms_norm", "quant_fp8_static", "quant_nvfp4",
+    "mxfp8_block_exponent", "quant_mxfp8",
     "swizzle_128x4_offset", "block_scale_buffer_shape", "scatter_block_scales",
     "gemma_add_rms_norm_quant", "add_rms_norm_quant",
 ]
@@ -43,6 +49,9 @@ __all__ = [
 NVFP4_BLOCK = 16      # elements per block scale ("16-element blocks")
 E2M1_MAX = 6.0
 E4M3_MAX = 448.0
+MX_BLOCK = 32         # elements per MXFP8 scale (scales of shape [M, H // 32])
+MX_E4M3_EMAX = 8      # exponent of E4M3FN's largest normal, 448 = 1.75 * 2^8
+MX_SCALE_EMIN = -127  # smallest E8M0 exponent
 
 
 def _check_fmt(fmt: Format):
@@ -150,6 +159,51 @@ def quant_nvfp4(y_bits, fmt: Format, global_scale: float):
     return q, S.astype(np.uint8)
 
 
+def mxfp8_block_exponent(amax) -> np.ndarray:
+    """Shared exponent e of an MX block from its largest magnitude ``amax``.
+
+    The pages give the MXFP8 variant's output types and shapes only
+    (``allreduce_gemma_rms_norm_mxfp8``, ``fused_allreduce_gemma_rms_norm``
+    page: E4M3 values, one E8M0 scale per 32 values).  Read with the scale
+    rule of the OCP Microscaling formats: the block's scale is 2^e with
+    e = floor(log2(amax)) minus the exponent of the element format's largest
+    normal (8 for E4M3), so the block's largest value lands in [256, 512) on
+    the element grid.  e is clamped below at E8M0's smallest exponent -127,
+    which also covers an all-zero block.  Exact: frexp gives
+    amax = f * 2^k with f in [0.5, 1), so floor(log2(amax)) = k - 1.
+    """
+    a = np.asarray(amax, dtype=np.float64)
+    _, k = np.frexp(a)
+    e = np.where(a > 0, k.astype(np.int64) - 1 - MX_E4M3_EMAX, MX_SCALE_EMIN)
+    return np.maximum(e, MX_SCALE_EMIN).astype(np.int64)
+
+
+def quant_mxfp8(y_bits, fmt: Format):
+    """MXFP8: E4M3FN codes with one E8M0 scale per 32-element block.
+
+    Per block (``mxfp8_block_exponent`` for e): each element is y * 2^-e,
+    clamped to +-448 and rounded to nearest even E4M3FN; the block's scale
+    code is e + 127.  The scaling by a power of two is exact, so every
+    decision here is exact in any precision that holds y * 2^-e down to
+    E4M3's half-smallest step.  Values beyond 448 (blocks whose amax has a
+    scaled magnitude in [448, 512)) saturate, as the OCP conversion does.
+
+    Returns ``(q, S)``: q is (M, H) uint8 E4M3FN codes and S the (M, H/32)
+    uint8 E8M0 codes, both row-major.
+    """
+    _check_fmt(fmt)
+    y = bits_to_f64(y_bits, fmt)
+    M, H = y.shape
+    if H % MX_BLOCK:
+        raise ValueError("H must be a multiple of 32")
+    blk = y.reshape(M, H // MX_BLOCK, MX_BLOCK)
+    e = mxfp8_block_exponent(np.max(np.abs(blk), axis=2))
+    v = np.ldexp(blk, (-e)[:, :, None].astype(np.int32))            # exact
+    v = np.minimum(np.maximum(v, -E4M3_MAX), E4M3_MAX)
+    q = encode(v, E4M3FN).astype(np.uint8).reshape(M, H)
+    return q, (e + 127).astype(np.uint8)
+
+
 def _round_up(a: int, b: int) -> int:
     return (a + b - 1) // b * b
 
@@ -203,24 +257,28 @@ def gemma_add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale,
 def add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale, mode, norm="gemma",
                        fmt: Format = BF16, block_scale_fill: int = 0xA5):
     """The whole op, as the unfused chain, with the norm ("gemma": 1 + w,
-    "plain": w) and the output ("fp8", "nvfp4", or None: add + norm only)
-    chosen.
+    "plain": w) and the output ("fp8", "nvfp4", "mxfp8", or None: add + norm
+    only) chosen.
 
     Arguments follow ``gemma_add_rms_norm_quant`` on the ``fused_norm_quant``
     page, with x, residual (or None) and weight as 16-bit patterns of
     ``fmt`` and ``scale`` a Python float (fp32 value).  Returns a dict:
 
       residual : (M, H) uint16, x + residual (None when residual is None)
-      q        : FP8 (M, H) uint8 codes, or NVFP4 (M, H/2) uint8 packed codes
-      scales   : NVFP4 (M, H/16) row-major block-scale codes, else None
+      q        : FP8 / MXFP8 (M, H) uint8 codes, or NVFP4 (M, H/2) uint8
+                 packed codes
+      scales   : NVFP4 (M, H/16) row-major E4M3 block-scale codes, MXFP8
+                 (M, H/32) E8M0 codes, else None
       block_scale : NVFP4 swizzled buffer (flat uint8, unwritten bytes hold
-                 ``block_scale_fill``), else the scale value itself
+                 ``block_scale_fill``), MXFP8 the (M, H/32) scales (already
+                 row-major), FP8 the scale value itself (``scale`` is
+                 ignored for MXFP8)
       y        : (M, H) uint16 normed activation (always computed; the op
                  returns it only when write_y)
     """
     _check_fmt(fmt)
-    if mode not in ("fp8", "nvfp4", None) or norm not in ("gemma", "plain"):
-        raise ValueError("mode must be fp8, nvfp4 or None; norm gemma or plain")
+    if mode not in ("fp8", "nvfp4", "mxfp8", None) or norm not in ("gemma", "plain"):
+        raise ValueError("mode must be fp8, nvfp4, mxfp8 or None; norm gemma or plain")
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     if x_bits.ndim != 2:
         raise ValueError("x must be 2-D")
@@ -232,6 +290,8 @@ def add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale, mode, nor
     nvfp4 = mode == "nvfp4"
     if nvfp4 and H % 64:
         raise ValueError("NVFP4 needs H % 64 == 0")
+    if mode == "mxfp8" and H % MX_BLOCK:
+        raise ValueError("MXFP8 needs H % 32 == 0")
     out = {"residual": h if residual_bits is not None else None}
     if M == 0:
         y = np.zeros((0, H), np.uint16)
@@ -248,6 +308,12 @@ def add_rms_norm_quant(x_bits, residual_bits, weight_bits, eps, scale, mode, nor
         buf = np.full(int(np.prod(block_scale_buffer_shape(M, H))), block_scale_fill, np.uint8)
         scatter_block_scales(S, M, H, buf)
         out.update(q=q, scales=S, block_scale=buf)
+    elif mode == "mxfp8":
+        if M:
+            q, S = quant_mxfp8(y, fmt)
+        else:
+            q, S = np.zeros((0, H), np.uint8), np.zeros((0, H // MX_BLOCK), np.uint8)
+        out.update(q=q, scales=S, block_scale=S)
     else:
         q = quant_fp8_static(y, fmt, scale) if M else np.zeros((0, H), np.uint8)
         out.update(q=q, scales=None, block_scale=float(np.float32(scale)))

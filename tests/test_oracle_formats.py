@@ -47,6 +47,15 @@ def test_e4m3_decode_matches_torch():
     assert ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
 
 
+def test_e8m0_decode_matches_torch():
+    codes = np.arange(256, dtype=np.int64)
+    ours = O.decode_e8m0(codes)
+    ref = torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(ours, ref, equal_nan=True)
+    assert ours[127] == 1.0 and ours[0] == 2.0 ** -127 and ours[254] == 2.0 ** 127
+    assert np.isnan(ours[255])
+
+
 def test_e2m1_decode_matches_fixture():
     fx = dict((k, v) for k, v in read_fixture("e2m1_format.txt") if k == "values")
     vals = [num(t) for t in fx["values"]]

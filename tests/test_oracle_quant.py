@@ -208,3 +208,127 @@ def test_scatter_leaves_padding_rows_unwritten_and_unswizzles():
     back = buf[off]
     assert np.array_equal(back[:M], S)
     assert np.all(back[M:] == 0xA5)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8: E4M3FN codes with one E8M0 scale per 32-element block.
+
+def _expand(tokens):
+    out = []
+    for t in tokens:
+        v, _, n = t.partition("*")
+        out.extend([num(v)] * (int(n) if n else 1))
+    return out
+
+
+def _mxfp8_fixture():
+    fmt, blocks, e2e_w = O.BF16, [], []
+    for k, v in read_fixture("mxfp8_worked_examples.txt"):
+        if k == "dtype":
+            fmt = {"bf16": O.BF16, "fp16": O.FP16}[v[0]]
+        elif k == "block":
+            blocks.append({"fmt": fmt, "y": _expand(v)})
+        elif k in ("codes", "scale"):
+            blocks[-1][k] = _expand(v)
+        elif k == "e2e_w":
+            e2e_w.extend(_expand(v))
+    return blocks, e2e_w
+
+
+def test_mxfp8_worked_blocks():
+    blocks, _ = _mxfp8_fixture()
+    assert len(blocks) == 10
+    for i, b in enumerate(blocks):
+        assert len(b["y"]) == 32 and len(b["codes"]) == 32
+        yb = vals_to_bits([b["y"]], b["fmt"])
+        assert np.array_equal(O.bits_to_f64(yb, b["fmt"])[0], b["y"]), i   # inputs exact
+        q, S = O.quant_mxfp8(yb, b["fmt"])
+        assert list(q[0]) == b["codes"], (i, list(q[0]))
+        assert list(S[0]) == b["scale"], (i, list(S[0]))
+
+
+def test_mxfp8_worked_example_end_to_end():
+    blocks, w = _mxfp8_fixture()
+    H = 64
+    assert len(w) == H
+    x = vals_to_bits([[1.0] * H], O.BF16)
+    out = O.add_rms_norm_quant(x, x.copy(), vals_to_bits(w, O.BF16), 0.0, 1.0, "mxfp8")
+    assert np.all(out["residual"] == 0x4000)
+    assert list(O.bits_to_f64(out["y"], O.BF16)[0]) == blocks[0]["y"] + blocks[1]["y"]
+    assert list(out["q"][0]) == blocks[0]["codes"] + blocks[1]["codes"]
+    assert list(out["scales"][0]) == blocks[0]["scale"] + blocks[1]["scale"]
+    assert out["block_scale"] is out["scales"]
+
+
+def test_mxfp8_exponent_brute_force():
+    """e is the smallest integer >= -127 with amax < 512 * 2^e; for e > -127
+    also amax >= 256 * 2^e.  Checked by a linear search with exact ldexp
+    comparisons over every bf16 magnitude and every fp16 magnitude."""
+    import math
+    for fmt in (O.BF16, O.FP16):
+        codes = np.arange(0x8000, dtype=np.int64)
+        a = O.decode(codes, fmt)
+        a = a[np.isfinite(a)]
+        e = O.mxfp8_block_exponent(a)
+        for ai, ei in zip(a.tolist(), e.tolist()):
+            k = -127
+            while not ai < math.ldexp(512.0, k):
+                k += 1
+            assert ei == k, (ai, ei, k)
+            if ei > -127:
+                assert ai >= math.ldexp(256.0, ei)
+
+
+def test_mxfp8_codes_brute_force():
+    """Each code is the E4M3 value nearest to clamp(y / decode_e8m0(S)), ties
+    to the even code, found by exhaustive search over the code table; the
+    scale is divided out as a float64 quotient (exact for a power of two)."""
+    for fmt in (O.BF16, O.FP16):
+        yb = _random_y(8, 1024, 43, fmt=fmt, spread=3.0)
+        q, S = O.quant_mxfp8(yb, fmt)
+        assert S.shape == (8, 32) and q.shape == (8, 1024)
+        y = O.bits_to_f64(yb, fmt).reshape(8, 32, 32)
+        v = y / O.decode_e8m0(S)[:, :, None]
+        v = np.clip(v, -448, 448).reshape(-1)
+        assert np.array_equal(q.reshape(-1).astype(np.int64), _brute_nearest_even(v, O.E4M3FN))
+
+
+@pytest.mark.parametrize("fmt", [O.BF16, O.FP16])
+def test_mxfp8_dequant_error_bound(fmt):
+    """decode(q) * 2^e is within half an E4M3 step of y (relative 2^-4 in the
+    normal range, 2^-10 * 2^e below it) unless |y| >= 448 * 2^e, where it is
+    +-448 * 2^e with y's sign; the block's largest magnitude decodes to
+    [256, 448] * 2^e unless the scale is clamped."""
+    yb = _random_y(32, 2048, 47, fmt=fmt, spread=4.0)
+    q, S = O.quant_mxfp8(yb, fmt)
+    y = O.bits_to_f64(yb, fmt).reshape(32, -1, 32)
+    sc = O.decode_e8m0(S)[:, :, None]
+    dq = O.decode(q, O.E4M3FN).reshape(y.shape) * sc
+    sat = np.abs(y) >= 448 * sc
+    assert np.all(np.abs(dq[sat]) == (448 * sc * np.ones_like(y))[sat])
+    assert np.all(np.sign(dq[sat]) == np.sign(y[sat]))
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10 * sc)
+    assert np.all(np.abs(dq - y)[~sat] <= bound[~sat])
+    top = np.abs(dq).max(axis=2)
+    unclamped = S > 0
+    assert unclamped.mean() > 0.99
+    assert np.all((top >= 256 * sc[:, :, 0]) & (top <= 448 * sc[:, :, 0])
+                  | ~unclamped)
+    assert sat.mean() > 0.0        # the floor rule does saturate some blocks
+
+
+def test_mxfp8_signed_zero_and_shape_errors():
+    y = np.zeros((1, 32))
+    y[0, 1] = -0.0
+    y[0, 2] = 1.0
+    y[0, 3] = -2.0 ** -20             # rounds to -0 on the element grid
+    q, S = O.quant_mxfp8(vals_to_bits(y, O.BF16), O.BF16)
+    assert int(S[0, 0]) == 127 - 8 and list(q[0, :4]) == [0x00, 0x80, 0x78, 0x80]
+    with pytest.raises(ValueError):
+        O.quant_mxfp8(vals_to_bits(np.zeros((1, 48)), O.BF16), O.BF16)
+    with pytest.raises(ValueError):
+        O.add_rms_norm_quant(vals_to_bits(np.ones((1, 48)), O.BF16), None,
+                             vals_to_bits(np.zeros(48), O.BF16), 1e-6, 1.0, "mxfp8")
+    out = O.add_rms_norm_quant(np.zeros((0, 64), np.uint16), None, vals_to_bits(np.zeros(64), O.BF16),
+                               1e-6, 1.0, "mxfp8")
+    assert out["q"].shape == (0, 64) and out["scales"].shape == (0, 2)
