@@ -44,13 +44,14 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def algorithmic_bytes(wl):
-    """Bytes the op must move once: reads x, residual, weight, scale; writes
-    residual, y, codes and (NVFP4) one scale byte per 16 elements.  Padding
-    rows of the scale buffer are not written and not counted."""
+    """Bytes the op must move once: reads x, residual, weight and (FP8,
+    NVFP4) the scale; writes residual, y, codes and one scale byte per 16
+    (NVFP4) or 32 (MXFP8) elements.  Padding rows of the NVFP4 scale buffer
+    are not written and not counted."""
     MH = wl.M * wl.H
-    rd = 2 * MH + (2 * MH if wl.has_residual else 0) + 2 * wl.H + 4
+    rd = 2 * MH + (2 * MH if wl.has_residual else 0) + 2 * wl.H + (0 if wl.mode == "mxfp8" else 4)
     wr = (2 * MH if wl.has_residual else 0) + (2 * MH if wl.write_y else 0)
-    wr += MH // 2 + MH // 16 if wl.nvfp4 else MH
+    wr += {"nvfp4": MH // 2 + MH // 16, "mxfp8": MH + MH // 32, "fp8": MH}[wl.mode]
     return rd, wr
 
 
@@ -68,7 +69,7 @@ def kernel_sha():
 
 def kernel_name(wl):
     return "fused_rows<{},{},{},{},{}>".format(
-        wl.dtype, "nvfp4" if wl.nvfp4 else "fp8", "res" if wl.has_residual else "nores",
+        wl.dtype, wl.mode, "res" if wl.has_residual else "nores",
         "y" if wl.write_y else "noy", 1 if wl.H <= 4096 else (2 if wl.H // 8 <= 2048 else 4))
 
 
@@ -100,14 +101,14 @@ def cpu_baseline(wl, x, r, w, scale, budget_s):
     t0 = time.perf_counter()
     while rows < wl.M:
         n = min(chunk, wl.M - rows)
-        O.gemma_add_rms_norm_quant(b16(x[rows:rows + n]), b16(r[rows:rows + n]) if r is not None else None,
-                                   wb, wl.eps, scale, wl.nvfp4, wl.write_y, fmt)
+        O.add_rms_norm_quant(b16(x[rows:rows + n]), b16(r[rows:rows + n]) if r is not None else None,
+                             wb, wl.eps, scale, wl.mode, "gemma", fmt)
         rows += n
         if time.perf_counter() - t0 >= budget_s and rows >= 16:
             break
     dt = time.perf_counter() - t0
     rd, wr = algorithmic_bytes(wl)
-    per_row = (rd + wr - 2 * wl.H - 4) / wl.M
+    per_row = (rd + wr - 2 * wl.H - (0 if wl.mode == "mxfp8" else 4)) / wl.M
     return {"value": round(per_row * rows / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "tokens_per_s": round(rows / dt, 1),
             "sample": f"first {rows} of {wl.M} rows of {wl.name}, {dt:.1f} s, numpy single-threaded"}
@@ -190,6 +191,9 @@ def main():
             st["q"] = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
             st["bs"] = torch.empty((ops.round_up(M, 128), ops.round_up(H // 16, 4)),
                                    dtype=torch.uint8, device=dev)
+        elif wl.mode == "mxfp8":
+            st["q"] = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
+            st["bs"] = torch.empty((M, H // 32), dtype=torch.uint8, device=dev)
         else:
             st["q"] = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
             st["bs"] = None
@@ -207,8 +211,14 @@ def main():
             ops.add_rms_norm_quant_out(xi, st["r"], wd, wl.eps, None, None, "gemma", None, None, yi)
             if wl.nvfp4:
                 ops.quant_nvfp4(yi, sd, st["q"], st["bs"])
+            elif wl.mode == "mxfp8":
+                ops.quant_mxfp8(yi, st["q"], st["bs"])
             else:
                 ops.quant_fp8_static(yi, sd, st["q"])
+            return
+        if wl.mode == "mxfp8":
+            ops.add_rms_norm_quant_out(xi, st["r"], wd, wl.eps, None, "mxfp8", "gemma", st["q"],
+                                       st["bs"], st["y"])
             return
         ops.gemma_add_rms_norm_quant_out(xi, st["r"], wd, wl.eps, sd, wl.nvfp4, st["q"], st["bs"],
                                          st["y"])
@@ -274,7 +284,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "M": M, "H": H, "act_dtype": wl.dtype,
-                   "mode": "nvfp4" if wl.nvfp4 else "fp8_static", "residual": wl.has_residual,
+                   "mode": {"fp8": "fp8_static"}.get(wl.mode, wl.mode), "residual": wl.has_residual,
                    "write_y": wl.write_y, "bytes_per_step": total, "bytes_read": rbytes,
                    "bytes_written": wbytes},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

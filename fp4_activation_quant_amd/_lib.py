@@ -12,11 +12,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemma_no
 
 NQ_OK, NQ_EINVAL, NQ_EUNSUPPORTED, NQ_EHIP = 0, 1, 2, 3
 NQ_BF16, NQ_FP16 = 0, 1
-NQ_MODE_FP8_STATIC, NQ_MODE_NVFP4, NQ_MODE_NONE = 0, 1, 2
+NQ_MODE_FP8_STATIC, NQ_MODE_NVFP4, NQ_MODE_NONE, NQ_MODE_MXFP8 = 0, 1, 2, 3
 NQ_NORM_GEMMA, NQ_NORM_PLAIN = 0, 1
 EXPORTS = ("nq_gemma_add_rms_norm_quant", "nq_add_rms_norm_quant", "nq_quant_fp8_static",
-           "nq_quant_nvfp4", "nq_block_scale_bytes", "nq_status_string", "nq_abi_version",
-           "nq_convert_probe")
+           "nq_quant_nvfp4", "nq_quant_mxfp8", "nq_block_scale_bytes", "nq_status_string",
+           "nq_abi_version", "nq_convert_probe")
 
 _lib = None
 
@@ -46,6 +46,8 @@ def lib():
         L.nq_quant_fp8_static.restype = i32
         L.nq_quant_nvfp4.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
         L.nq_quant_nvfp4.restype = i32
+        L.nq_quant_mxfp8.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+        L.nq_quant_mxfp8.restype = i32
         L.nq_block_scale_bytes.argtypes = [i64, i64]
         L.nq_block_scale_bytes.restype = ctypes.c_size_t
         L.nq_status_string.argtypes = [i32]
@@ -84,6 +86,11 @@ def nq_quant_fp8_static(y, scale, M, H, dtype, q, stream):
 def nq_quant_nvfp4(y, global_scale, M, H, dtype, q, block_scale, stream):
     return lib().nq_quant_nvfp4(y or None, global_scale or None, int(M), int(H), int(dtype),
                                 q or None, block_scale or None, stream or None)
+
+
+def nq_quant_mxfp8(y, M, H, dtype, q, scales, stream):
+    return lib().nq_quant_mxfp8(y or None, int(M), int(H), int(dtype), q or None, scales or None,
+                                stream or None)
 
 
 def nq_block_scale_bytes(M, H):

@@ -4,7 +4,9 @@
 // `fused_norm_quant` page; its assertions (2-D contiguous bf16/fp16 x,
 // residual of the same shape or None, weight of shape (H,), one fp32 scale,
 // H % 64 == 0 for NVFP4) become status codes here, and nothing is launched
-// or written when one fails.
+// or written when one fails.  The MXFP8 mode is the variant
+// `allreduce_gemma_rms_norm_mxfp8` of the `fused_allreduce_gemma_rms_norm`
+// page without its all-reduce; it needs H % 32 == 0.
 
 #include "gemma_norm_quant.h"
 #include "gnq_common.hpp"
@@ -48,6 +50,8 @@ __global__ void convert_probe(int kind, const uint32_t *__restrict__ in, int64_t
     case 4: out[i] = (uint8_t)e4m3_one(div_by_scale(Bf16::lo(bits & 0xffffu), param, 1.0f / param)); break;
     case 5: out[i] = (uint8_t)e4m3_one(div_by_scale(Fp16::lo(bits & 0xffffu), param, 1.0f / param)); break;
     case 6: out[i] = (uint8_t)nvfp4_scale_code(f, param); break;
+    case 7: out[i] = (uint8_t)mx_scale_code(fabsf(f)); break;
+    case 8: out[i] = (uint8_t)e4m3_one(f * mx_elem_scale((uint32_t)param)); break;
     default: break;
   }
 }
@@ -79,21 +83,25 @@ nq_status nq_add_rms_norm_quant(const void *x, void *residual, const void *weigh
                                 void *stream) {
   if (!valid_dtype(dtype)) return NQ_EINVAL;
   if (norm != NQ_NORM_GEMMA && norm != NQ_NORM_PLAIN) return NQ_EINVAL;
-  if (mode != NQ_MODE_FP8_STATIC && mode != NQ_MODE_NVFP4 && mode != NQ_MODE_NONE) return NQ_EINVAL;
+  if (mode != NQ_MODE_FP8_STATIC && mode != NQ_MODE_NVFP4 && mode != NQ_MODE_NONE &&
+      mode != NQ_MODE_MXFP8)
+    return NQ_EINVAL;
   if (M < 0 || H <= 0 || H > ((int64_t)1 << 30)) return NQ_EINVAL;
-  const bool nv = mode == NQ_MODE_NVFP4, none = mode == NQ_MODE_NONE;
+  const bool nv = mode == NQ_MODE_NVFP4, none = mode == NQ_MODE_NONE, mx = mode == NQ_MODE_MXFP8;
   if (!x || !weight) return NQ_EINVAL;
-  if (!none && (!scale || !q)) return NQ_EINVAL;
-  if (nv && !block_scale) return NQ_EINVAL;
+  if (!none && !q) return NQ_EINVAL;
+  if ((mode == NQ_MODE_FP8_STATIC || nv) && !scale) return NQ_EINVAL;
+  if ((nv || mx) && !block_scale) return NQ_EINVAL;
   if ((write_y || none) && !y) return NQ_EINVAL;
   if (none && !write_y) return NQ_EINVAL;
   if (nv && H % 64 != 0) return NQ_EUNSUPPORTED;
+  if (mx && H % kMxBlock != 0) return NQ_EUNSUPPORTED;
   const size_t act = (size_t)M * (size_t)H * 2;
   const size_t qbytes = none ? 0 : nv ? (size_t)M * (size_t)(H / 2) : (size_t)M * (size_t)H;
-  const size_t bsbytes = nv ? block_scale_bytes(M, H) : 0;
+  const size_t bsbytes = nv ? block_scale_bytes(M, H) : mx ? (size_t)M * (size_t)(H / kMxBlock) : 0;
   const void *yy = write_y ? y : nullptr;
   const void *qq = none ? nullptr : q;
-  const void *bb = nv ? block_scale : nullptr;
+  const void *bb = (nv || mx) ? block_scale : nullptr;
   if (residual == x) return NQ_EINVAL;
   const void *bufs[5] = {x, residual, qq, yy, bb};
   const size_t lens[5] = {act, act, qbytes, act, bsbytes};
@@ -102,13 +110,26 @@ nq_status nq_add_rms_norm_quant(const void *x, void *residual, const void *weigh
       if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return NQ_EINVAL;
   if (M == 0) return NQ_OK;
 
-  FusedArgs a{x, residual, weight, scale, eps, M, H, none ? nullptr : q, nv ? block_scale : nullptr,
-              (write_y || none) ? y : nullptr, norm == NQ_NORM_GEMMA, (hipStream_t)stream};
+  FusedArgs a{x,
+              residual,
+              weight,
+              (nv || mode == NQ_MODE_FP8_STATIC) ? scale : nullptr,
+              eps,
+              M,
+              H,
+              none ? nullptr : q,
+              (nv || mx) ? block_scale : nullptr,
+              (write_y || none) ? y : nullptr,
+              norm == NQ_NORM_GEMMA,
+              (hipStream_t)stream};
+  const bool bf = dtype == NQ_BF16;
   hipError_t e;
-  if (dtype == NQ_BF16)
-    e = nv ? fused_bf16_nvfp4(a) : none ? fused_bf16_none(a) : fused_bf16_fp8(a);
-  else
-    e = nv ? fused_fp16_nvfp4(a) : none ? fused_fp16_none(a) : fused_fp16_fp8(a);
+  switch (mode) {
+    case NQ_MODE_NVFP4: e = bf ? fused_bf16_nvfp4(a) : fused_fp16_nvfp4(a); break;
+    case NQ_MODE_MXFP8: e = bf ? fused_bf16_mxfp8(a) : fused_fp16_mxfp8(a); break;
+    case NQ_MODE_NONE: e = bf ? fused_bf16_none(a) : fused_fp16_none(a); break;
+    default: e = bf ? fused_bf16_fp8(a) : fused_fp16_fp8(a); break;
+  }
   return status_of(e);
 }
 
@@ -122,40 +143,54 @@ nq_status nq_gemma_add_rms_norm_quant(const void *x, void *residual, const void 
 }
 
 static nq_status quant_common(const void *y, const float *scale, int64_t M, int64_t H, int dtype,
-                              bool nv, void *q, void *block_scale, void *stream) {
+                              int mode, void *q, void *block_scale, void *stream) {
+  const bool nv = mode == NQ_MODE_NVFP4, mx = mode == NQ_MODE_MXFP8;
   if (!valid_dtype(dtype)) return NQ_EINVAL;
   if (M < 0 || H <= 0 || H > ((int64_t)1 << 30)) return NQ_EINVAL;
-  if (!y || !scale || !q || (nv && !block_scale)) return NQ_EINVAL;
+  if (!y || !q || (!mx && !scale) || ((nv || mx) && !block_scale)) return NQ_EINVAL;
   if (nv && H % kBlock != 0) return NQ_EUNSUPPORTED;
+  if (mx && H % kMxBlock != 0) return NQ_EUNSUPPORTED;
   const size_t act = (size_t)M * (size_t)H * 2;
   const size_t qbytes = nv ? (size_t)M * (size_t)(H / 2) : (size_t)M * (size_t)H;
-  const size_t bsbytes = nv ? block_scale_bytes(M, H) : 0;
-  if (overlaps(y, act, q, qbytes) || (nv && (overlaps(y, act, block_scale, bsbytes) ||
-                                             overlaps(q, qbytes, block_scale, bsbytes))))
+  const size_t bsbytes = nv ? block_scale_bytes(M, H) : mx ? (size_t)M * (size_t)(H / kMxBlock) : 0;
+  if (overlaps(y, act, q, qbytes) || ((nv || mx) && (overlaps(y, act, block_scale, bsbytes) ||
+                                                     overlaps(q, qbytes, block_scale, bsbytes))))
     return NQ_EINVAL;
   if (M == 0) return NQ_OK;
-  QuantArgs a{y, scale, M, H, q, nv ? block_scale : nullptr, (hipStream_t)stream};
+  QuantArgs a{y, mx ? nullptr : scale, M, H, q, (nv || mx) ? block_scale : nullptr,
+              (hipStream_t)stream};
+  const bool bf = dtype == NQ_BF16;
   hipError_t e;
-  if (dtype == NQ_BF16)
-    e = nv ? quant_bf16_nvfp4(a) : quant_bf16_fp8(a);
+  if (nv)
+    e = bf ? quant_bf16_nvfp4(a) : quant_fp16_nvfp4(a);
+  else if (mx)
+    e = bf ? quant_bf16_mxfp8(a) : quant_fp16_mxfp8(a);
   else
-    e = nv ? quant_fp16_nvfp4(a) : quant_fp16_fp8(a);
+    e = bf ? quant_bf16_fp8(a) : quant_fp16_fp8(a);
   return status_of(e);
 }
 
 nq_status nq_quant_fp8_static(const void *y, const float *scale, int64_t M, int64_t H, int dtype,
                               void *q, void *stream) {
-  return quant_common(y, scale, M, H, dtype, false, q, nullptr, stream);
+  return quant_common(y, scale, M, H, dtype, NQ_MODE_FP8_STATIC, q, nullptr, stream);
 }
 
 nq_status nq_quant_nvfp4(const void *y, const float *global_scale, int64_t M, int64_t H, int dtype,
                          void *q, void *block_scale, void *stream) {
-  return quant_common(y, global_scale, M, H, dtype, true, q, block_scale, stream);
+  return quant_common(y, global_scale, M, H, dtype, NQ_MODE_NVFP4, q, block_scale, stream);
+}
+
+nq_status nq_quant_mxfp8(const void *y, int64_t M, int64_t H, int dtype, void *q, void *scales,
+                         void *stream) {
+  return quant_common(y, nullptr, M, H, dtype, NQ_MODE_MXFP8, q, scales, stream);
 }
 
 nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,
                            void *stream) {
-  if (kind < 0 || kind > 6 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in)))
+  if (kind < 0 || kind > 8 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in)))
+    return NQ_EINVAL;
+  // kind 8 takes an E8M0 code the kernels can produce (0..247) as param.
+  if (kind == 8 && !(param >= 0.0f && param <= 247.0f && param == (float)(int)param))
     return NQ_EINVAL;
   if (n == 0) return NQ_OK;
   const int threads = 256;

@@ -1,7 +1,7 @@
 // Device building blocks shared by every kernel of the library: activation
 // dtypes, the FP8 / FP4 encoders, the correctly rounded division by the FP8
-// scale, the NVFP4 block-scale arithmetic, the 128x4 scale layout, DPP
-// reductions, and the host-side argument block.
+// scale, the NVFP4 and MXFP8 block-scale arithmetic, the 128x4 scale layout,
+// DPP reductions, and the host-side argument block.
 //
 // The operation is `gemma_add_rms_norm_quant` on the `fused_norm_quant` page
 // (and its unfused form: an add + Gemma RMSNorm kernel followed by a
@@ -28,6 +28,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kVec = 8;           // elements per thread chunk (16 bytes)
 constexpr int kBlock = 16;        // elements per NVFP4 block scale
+constexpr int kMxBlock = 32;      // elements per MXFP8 (E8M0) block scale
 constexpr int kWave = 64;
 constexpr int kMaxThreads = 1024;
 constexpr float kE4M3Max = 448.0f;
@@ -37,6 +38,11 @@ constexpr float kE2M1Max = 6.0f;
 constexpr int kModeFp8 = 0;
 constexpr int kModeNvfp4 = 1;
 constexpr int kModeNone = 2;
+constexpr int kModeMxfp8 = 3;
+
+// Whether a mode reads the fp32 scale argument (MXFP8 derives its scales
+// from the data; no quant has none).
+constexpr bool mode_reads_scale(int mode) { return mode == kModeFp8 || mode == kModeNvfp4; }
 
 // ----------------------------------------------------------------------------
 // Activation dtypes: unpack two values from a 32-bit word, pack two fp32
@@ -124,6 +130,23 @@ __device__ __forceinline__ float nvfp4_elem_scale(uint32_t s_code, float gs) {
   return sigma == 0.0f ? 0.0f : gs / sigma;
 }
 
+// MXFP8 block scale: 2^e with e = floor(log2(amax)) - 8 (8 is the exponent
+// of E4M3's largest normal, 448 = 1.75 * 2^8) clamped below at -127, the OCP
+// MX scale rule.  The E8M0 code e + 127 is then the biased fp32 exponent of
+// amax minus 8, floored at 0 (a zero or subnormal amax gives 0).  amax >= 0;
+// the code is at most 247 for any bit pattern.
+__device__ __forceinline__ uint32_t mx_scale_code(float amax) {
+  const uint32_t be = __float_as_uint(amax) >> 23;
+  return be > 8u ? be - 8u : 0u;
+}
+
+// 2^-e for an E8M0 code <= 247: the fp32 with biased exponent 254 - code
+// (a normal number, 2^127 down to 2^-120).  Scaling y by it is exact unless
+// the product falls below 2^-126, which encodes to a signed zero either way.
+__device__ __forceinline__ float mx_elem_scale(uint32_t code) {
+  return __uint_as_float((254u - code) << 23);
+}
+
 // Byte offset of block scale (row m, block b) in the 128x4-tiled layout;
 // ktiles = round_up(H/16, 4) / 4.
 __device__ __forceinline__ size_t swz128x4(int64_t m, int b, int ktiles) {
@@ -185,17 +208,24 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // ----------------------------------------------------------------------------
 // Gemma (1 + w) or plain (w) RMSNorm scaling of t = h * rstd, one rounding.
-// fma(t, w, t) is the correctly rounded t * (1 + w).
+// fma(t, w, t) is the correctly rounded t * (1 + w).  Its exact zeros (t = 0
+// or w = -1) come out as +0 from the cancellation; the sign bit is therefore
+// taken from t * fl(1 + w), which carries the sign of the product
+// h * rstd * (1 + w) in every case (fl(1 + w) is +0 for w = -1 and has the
+// sign of 1 + w otherwise), so a zero y keeps the sign that product has.
 template <bool GEMMA>
 __device__ __forceinline__ float norm_scale(float t, float w) {
-  if constexpr (GEMMA) return __builtin_fmaf(t, w, t);
+  if constexpr (GEMMA) return __builtin_copysignf(__builtin_fmaf(t, w, t), t * (1.0f + w));
   return t * w;
 }
 
 // Quantize one 8-element chunk of y (already rounded to the activation dtype)
 // of row `row`, chunk `ch`, and store its codes (and, for NVFP4, from the
-// even lane of the pair, the block scale).  NVFP4 needs the neighbouring lane
-// to hold the other half of the 16-element block and to run this too.
+// even lane of the pair, the block scale; for MXFP8, from the first lane of
+// the quad, the E8M0 scale).  NVFP4 needs the neighbouring lane to hold the
+// other half of the 16-element block and to run this too; MXFP8 likewise
+// needs the aligned quad of lanes (4 x 8 = 32 elements) to hold chunks
+// 4k..4k+3 and all run it.
 template <int MODE>
 __device__ __forceinline__ void quant_store_chunk(const float (&yv)[kVec], float s, float r_s,
                                                   uint8_t *__restrict__ q, uint8_t *__restrict__ bs,
@@ -213,6 +243,21 @@ __device__ __forceinline__ void quant_store_chunk(const float (&yv)[kVec], float
     uint32_t *qrow = reinterpret_cast<uint32_t *>(q + (size_t)row * (size_t)nchunk * 4);
     __builtin_nontemporal_store(e2m1x8(v), &qrow[ch]);
     if ((ch & 1) == 0) bs[swz128x4(row, (int)(ch >> 1), ktiles)] = (uint8_t)sc;
+  } else if constexpr (MODE == kModeMxfp8) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) amax = fmaxf(amax, fabsf(yv[k]));
+    amax = fmaxf(amax, dpp<0xB1>(amax));   // lane ^ 1
+    amax = fmaxf(amax, dpp<0x4E>(amax));   // lane ^ 2
+    const uint32_t sc = mx_scale_code(amax);
+    const float o = mx_elem_scale(sc);
+    float v[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) v[k] = yv[k] * o;
+    const u32x2 packed = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
+    u32x2 *qrow = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8);
+    __builtin_nontemporal_store(packed, &qrow[ch]);
+    if ((ch & 3) == 0) bs[(size_t)row * (size_t)(nchunk >> 2) + (ch >> 2)] = (uint8_t)sc;
   } else if constexpr (MODE == kModeFp8) {
     float v[kVec];
 #pragma unroll
@@ -221,6 +266,21 @@ __device__ __forceinline__ void quant_store_chunk(const float (&yv)[kVec], float
     u32x2 *qrow = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8);
     __builtin_nontemporal_store(packed, &qrow[ch]);
   }
+}
+
+// MXFP8 quant of one whole 32-element block held by one thread (the scalar
+// kernels): codes to q[0..31] with byte stores (any alignment); returns the
+// E8M0 scale code.
+__device__ __forceinline__ uint32_t mx_block_store(const float (&yv)[kMxBlock], uint8_t *q) {
+  float amax = 0.0f;
+  for (int k = 0; k < kMxBlock; ++k) amax = fmaxf(amax, fabsf(yv[k]));
+  const uint32_t sc = mx_scale_code(amax);
+  const float o = mx_elem_scale(sc);
+  for (int k = 0; k < kMxBlock; k += 4) {
+    const uint32_t w = e4m3x4(yv[k] * o, yv[k + 1] * o, yv[k + 2] * o, yv[k + 3] * o);
+    for (int i = 0; i < 4; ++i) q[k + i] = (uint8_t)(w >> (8 * i));
+  }
+  return sc;
 }
 
 // ----------------------------------------------------------------------------
@@ -237,7 +297,7 @@ struct FusedArgs {
   int64_t M;
   int64_t H;
   void *q;
-  void *bs;
+  void *bs;         // NVFP4 128x4-tiled scales, MXFP8 (M, H/32) scales
   void *y;          // nullptr: y not written
   bool gemma;       // (1 + w) if true, w if false
   hipStream_t st;
@@ -260,9 +320,13 @@ hipError_t fused_bf16_none(const FusedArgs &a);
 hipError_t fused_fp16_fp8(const FusedArgs &a);
 hipError_t fused_fp16_nvfp4(const FusedArgs &a);
 hipError_t fused_fp16_none(const FusedArgs &a);
+hipError_t fused_bf16_mxfp8(const FusedArgs &a);
+hipError_t fused_fp16_mxfp8(const FusedArgs &a);
 hipError_t quant_bf16_fp8(const QuantArgs &a);
 hipError_t quant_bf16_nvfp4(const QuantArgs &a);
 hipError_t quant_fp16_fp8(const QuantArgs &a);
 hipError_t quant_fp16_nvfp4(const QuantArgs &a);
+hipError_t quant_bf16_mxfp8(const QuantArgs &a);
+hipError_t quant_fp16_mxfp8(const QuantArgs &a);
 
 }  // namespace gnq

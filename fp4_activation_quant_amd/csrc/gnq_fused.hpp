@@ -1,5 +1,5 @@
 // The fused kernels: residual add + (Gemma or plain) RMSNorm + FP8 / NVFP4 /
-// no quant, one launch.  Included by one translation unit per (dtype, mode)
+// MXFP8 / no quant, one launch.  Included by one translation unit per (dtype, mode)
 // (gnq_fused_<dtype>_<mode>.hip), which instantiates GNQ_FUSED_ENTRY.
 //
 // Design (memory-bound; no MFMA -- nothing here is a contraction):
@@ -19,10 +19,14 @@
 //    stores the block's scale byte at its 128x4-tiled offset.  NVFP4 rows are
 //    assigned to workgroups so that each 128-row scale tile is written
 //    through a single XCD.
+//  * An MXFP8 block (32 elements) is the chunk quad of four adjacent lanes
+//    (DPP quad permutations combine the amax); the quad's first lane stores
+//    the E8M0 scale byte, row-major.
 //  * fused_rows_small: H <= 512, several rows per wavefront, reduced inside
 //    lane groups with DPP, no LDS and no barrier.
 //  * fused_rows_scalar: shapes or pointers the vector path cannot take
-//    (H % 16 != 0, H > 32768, unaligned views); same arithmetic.
+//    (H % 16 != 0, H > 32768, unaligned views); same arithmetic, one thread
+//    per element (FP8, none) or per scale block (NVFP4, MXFP8).
 #pragma once
 
 #include "gnq_common.hpp"
@@ -64,7 +68,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
       const unsigned ch = tid + c * nthr;
       if (ch < nch) wa[c] = w[ch];
     }
-    const float s = MODE == kModeNone ? 1.0f : *scale_ptr;
+    const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
     const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
     // h = RN(x + r), written back; sum of squares of the rounded h.
     uint32_t hb[CPT][4];
@@ -146,7 +150,7 @@ fused_rows_small(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32
     if constexpr (HAS_RES) ra = __builtin_nontemporal_load(&res[rbase + ch]);
     wa = w[ch];
   }
-  const float s = MODE == kModeNone ? 1.0f : *scale_ptr;
+  const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
   const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
   uint32_t hb[4];
   float ss = 0.0f;
@@ -184,8 +188,9 @@ fused_rows_small(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32
       __builtin_nontemporal_store(o, &y[rbase + ch]);
     }
   }
-  // NVFP4 has H % 64 == 0, so the lanes of a row pair up into whole blocks
-  // and an inactive lane pairs only with an inactive lane.
+  // NVFP4 has H % 64 == 0 and MXFP8 H % 32 == 0, so the lanes of a row group
+  // into whole blocks (LPR >= 4 for MXFP8) and an inactive lane shares a
+  // block only with inactive lanes.
   if (active) quant_store_chunk<MODE>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles);
 }
 
@@ -199,7 +204,7 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
   __shared__ float partial[2][256 / kWave];
   const int tid = threadIdx.x;
   const int nwaves = blockDim.x / kWave;
-  const float s = MODE == kModeNone ? 1.0f : *scale_ptr;
+  const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
   const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
   int parity = 0;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x, parity ^= 1) {
@@ -246,6 +251,19 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
           qp[4 + k] = (uint8_t)(p1 >> (8 * k));
         }
         bs[swz128x4(row, b, ktiles)] = (uint8_t)sc;
+      }
+    } else if constexpr (MODE == kModeMxfp8) {
+      const int nb = H / kMxBlock;
+      for (int b = tid; b < nb; b += blockDim.x) {
+        float yv[kMxBlock];
+        for (int k = 0; k < kMxBlock; ++k) {
+          const int j = b * kMxBlock + k;
+          const uint32_t yq =
+              D::pack(norm_scale<GEMMA>(D::lo(hsrc[rb + j]) * rstd, D::lo(w[j])), 0.0f) & 0xffffu;
+          if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
+          yv[k] = D::lo(yq);
+        }
+        bs[(size_t)row * (size_t)nb + b] = (uint8_t)mx_block_store(yv, q + rb + (size_t)b * kMxBlock);
       }
     } else {
       for (int j = tid; j < H; j += blockDim.x) {

@@ -1,0 +1,7 @@
+// Fused add + RMSNorm kernels for fp16 activations, mxfp8 output (one
+// translation unit per dtype and mode so the library builds in parallel).
+#include "gnq_fused.hpp"
+
+namespace gnq {
+hipError_t fused_fp16_mxfp8(const FusedArgs &a) { return dispatch_fused<Fp16, kModeMxfp8>(a); }
+}  // namespace gnq

@@ -1,7 +1,8 @@
 // Standalone quant kernels: the second kernel of the unfused chain (an
 // activation already normalised and rounded to its dtype -> static FP8 codes,
-// or NVFP4 codes + 128x4-tiled E4M3 block scales), with the same arithmetic
-// and the same launch geometry as the fused kernels' quant step.
+// NVFP4 codes + 128x4-tiled E4M3 block scales, or MXFP8 codes + row-major
+// E8M0 scales), with the same arithmetic and the same launch geometry as the
+// fused kernels' quant step.
 #pragma once
 
 #include "gnq_common.hpp"
@@ -24,7 +25,7 @@ quant_rows(const u32x4 *__restrict__ y, const float *__restrict__ scale_ptr, int
       const unsigned ch = tid + c * nthr;
       if (ch < nch) ya[c] = __builtin_nontemporal_load(&yr[ch]);
     }
-    const float s = *scale_ptr;
+    const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
     const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -46,7 +47,7 @@ template <class D, int MODE>
 __global__ void __launch_bounds__(256)
 quant_rows_scalar(const uint16_t *__restrict__ y, const float *__restrict__ scale_ptr, int64_t M,
                   int H, uint8_t *__restrict__ q, uint8_t *__restrict__ bs, int ktiles) {
-  const float s = *scale_ptr;
+  const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
   const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
     const size_t rb = (size_t)row * (size_t)H;
@@ -70,6 +71,13 @@ quant_rows_scalar(const uint16_t *__restrict__ y, const float *__restrict__ scal
           qp[4 + k] = (uint8_t)(p1 >> (8 * k));
         }
         bs[swz128x4(row, b, ktiles)] = (uint8_t)sc;
+      }
+    } else if constexpr (MODE == kModeMxfp8) {
+      const int nb = H / kMxBlock;
+      for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+        float yv[kMxBlock];
+        for (int k = 0; k < kMxBlock; ++k) yv[k] = D::lo(y[rb + (size_t)b * kMxBlock + k]);
+        bs[(size_t)row * (size_t)nb + b] = (uint8_t)mx_block_store(yv, q + rb + (size_t)b * kMxBlock);
       }
     } else {
       for (int j = threadIdx.x; j < H; j += blockDim.x)

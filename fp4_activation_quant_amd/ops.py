@@ -9,6 +9,7 @@ from . import _lib
 
 _DT = {torch.bfloat16: _lib.NQ_BF16, torch.float16: _lib.NQ_FP16}
 FP8_DTYPE = torch.float8_e4m3fn
+E8M0_DTYPE = torch.float8_e8m0fnu
 
 
 def round_up(a, b):
@@ -77,14 +78,16 @@ def gemma_add_rms_norm_quant_out(x, residual, weight, eps, scale, nvfp4, q, bloc
     _check(st, "nq_gemma_add_rms_norm_quant")
 
 
-_MODES = {"fp8": _lib.NQ_MODE_FP8_STATIC, "nvfp4": _lib.NQ_MODE_NVFP4, None: _lib.NQ_MODE_NONE}
+_MODES = {"fp8": _lib.NQ_MODE_FP8_STATIC, "nvfp4": _lib.NQ_MODE_NVFP4, "mxfp8": _lib.NQ_MODE_MXFP8,
+          None: _lib.NQ_MODE_NONE}
 _NORMS = {"gemma": _lib.NQ_NORM_GEMMA, "plain": _lib.NQ_NORM_PLAIN}
 
 
 def add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q, block_scale, y):
     """The op with the norm ("gemma": 1 + w, "plain": w) and the output mode
-    ("fp8", "nvfp4" or None for add + norm alone) chosen, into
-    caller-allocated outputs."""
+    ("fp8", "nvfp4", "mxfp8" or None for add + norm alone) chosen, into
+    caller-allocated outputs.  MXFP8: ``block_scale`` is the (M, H // 32)
+    E8M0 scale buffer and ``scale`` is ignored (may be None)."""
     M, H = x.shape
     with torch.cuda.device(x.device):
         st = _lib.nq_add_rms_norm_quant(
@@ -96,7 +99,9 @@ def add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q, block
 
 def add_rms_norm_quant(x, residual, weight, eps, scale, mode, norm="gemma", write_y=False):
     """Allocating form of add_rms_norm_quant_out: returns (q, block_scale, y)
-    as gemma_add_rms_norm_quant does; mode None returns (None, None, y)."""
+    as gemma_add_rms_norm_quant does; mode None returns (None, None, y);
+    mode "mxfp8" returns E4M3 codes (M, H) and E8M0 scales (M, H // 32)
+    (torch.float8_e8m0fnu), both row-major."""
     assert x.dim() == 2 and x.is_contiguous() and x.dtype in _DT and x.is_cuda
     M, H = x.shape
     if mode is None:
@@ -109,14 +114,29 @@ def add_rms_norm_quant(x, residual, weight, eps, scale, mode, norm="gemma", writ
         q = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device)
         block_scale = torch.empty((round_up(M, 128), round_up(H // 16, 4) // 4),
                                   dtype=torch.int32, device=x.device).view(FP8_DTYPE)
+    elif mode == "mxfp8":
+        assert H % 32 == 0
+        q = torch.empty((M, H), dtype=FP8_DTYPE, device=x.device)
+        block_scale = torch.empty((M, H // 32), dtype=E8M0_DTYPE, device=x.device)
     else:
         q = torch.empty((M, H), dtype=FP8_DTYPE, device=x.device)
         block_scale = scale
     y = torch.empty_like(x) if write_y else None
     if M:
         add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q,
-                               block_scale if mode == "nvfp4" else None, y)
+                               block_scale if mode in ("nvfp4", "mxfp8") else None, y)
     return q, block_scale, y
+
+
+def gemma_add_rms_norm_mxfp8(x, residual, weight, eps, return_normed=False):
+    """Add + Gemma RMSNorm with an MXFP8 output, the single-GPU body of
+    ``allreduce_gemma_rms_norm_mxfp8`` (``fused_allreduce_gemma_rms_norm``
+    page).  Returns ``(x_q, x_scale, normed, residual)``: E4M3 codes (M, H),
+    E8M0 scales (M, H // 32), the normed rows when ``return_normed`` (else
+    None), and the residual (updated in place to x + residual; x itself when
+    residual is None)."""
+    q, s, y = add_rms_norm_quant(x, residual, weight, eps, None, "mxfp8", "gemma", return_normed)
+    return q, s, y, (residual if residual is not None else x)
 
 
 def gemma_add_rms_norm(x, residual, weight, eps):
@@ -153,6 +173,23 @@ def quant_nvfp4(y, global_scale, q=None, block_scale=None):
                                      q.data_ptr(), block_scale.data_ptr(), _stream(y.device))
         _check(st, "nq_quant_nvfp4")
     return q, block_scale
+
+
+def quant_mxfp8(y, q=None, scales=None):
+    """Standalone MXFP8 quant: E4M3 codes (M, H) and E8M0 scales (M, H // 32),
+    row-major."""
+    assert y.dim() == 2 and y.is_contiguous() and y.dtype in _DT and y.is_cuda
+    M, H = y.shape
+    if q is None:
+        q = torch.empty((M, H), dtype=FP8_DTYPE, device=y.device)
+    if scales is None:
+        scales = torch.empty((M, H // 32), dtype=E8M0_DTYPE, device=y.device)
+    if M:
+        with torch.cuda.device(y.device):
+            st = _lib.nq_quant_mxfp8(y.data_ptr(), M, H, _DT[y.dtype], q.data_ptr(),
+                                     scales.data_ptr(), _stream(y.device))
+        _check(st, "nq_quant_mxfp8")
+    return q, scales
 
 
 def block_scale_bytes(M, H):

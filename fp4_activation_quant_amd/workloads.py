@@ -37,7 +37,7 @@ class Workload:
     M: int
     H: int
     dtype: str            # "bf16" | "fp16"
-    nvfp4: bool
+    mode: str             # "fp8" (static) | "nvfp4" | "mxfp8"
     has_residual: bool
     write_y: bool
     eps: float
@@ -45,12 +45,16 @@ class Workload:
     r_std: float
     w_dist: tuple         # ("normal", std) | ("uniform", lo, hi)
     seed_base: int
-    scale_rule: str       # "fixed" | "fp8_amax" | "fp8_amax_calibration" | "nvfp4_amax"
+    scale_rule: str       # "fixed" | "fp8_amax" | "fp8_amax_calibration" | "nvfp4_amax" | "none"
     fixed_scale: float = 0.0
     elem_outliers: tuple = ()   # (p, factor) on x elements
     row_outliers: tuple = ()    # (p, factor) on rows of x and residual
     draw_M: int = 0             # rows drawn (>= M); 0 means M
     tags: tuple = field(default=())
+
+    @property
+    def nvfp4(self):
+        return self.mode == "nvfp4"
 
     @property
     def torch_dtype(self):
@@ -65,27 +69,35 @@ def _wl(**kw):
     return Workload(**kw)
 
 
-_DECODE = dict(H=4096, dtype="bf16", nvfp4=False, has_residual=True, write_y=False, eps=1e-6,
+_DECODE = dict(H=4096, dtype="bf16", mode="fp8", has_residual=True, write_y=False, eps=1e-6,
                x_std=1.0, r_std=2.0, w_dist=("normal", 0.1), seed_base=2000,
                scale_rule="fp8_amax_calibration", elem_outliers=(0.01, 20.0), draw_M=256)
 _WIDE = dict(M=4096, H=5120, dtype="fp16", write_y=False, eps=1e-5, x_std=0.5, r_std=4.0,
              w_dist=("uniform", -0.5, 0.5), seed_base=4000, row_outliers=(0.001, 100.0))
 
 WORKLOADS = {w.name: w for w in [
-    _wl(name="fp8_m16_h2048_bf16_y", M=16, H=2048, dtype="bf16", nvfp4=False, has_residual=True,
+    _wl(name="fp8_m16_h2048_bf16_y", M=16, H=2048, dtype="bf16", mode="fp8", has_residual=True,
         write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1), seed_base=1000,
         scale_rule="fixed", fixed_scale=0.05),
     *[_wl(name=f"fp8_decode_m{m}_h4096_bf16", M=m, **_DECODE) for m in (1, 8, 64, 256)],
-    _wl(name="nvfp4_prefill_m8192_h4096_bf16_y", M=8192, H=4096, dtype="bf16", nvfp4=True,
+    _wl(name="nvfp4_prefill_m8192_h4096_bf16_y", M=8192, H=4096, dtype="bf16", mode="nvfp4",
         has_residual=True, write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1),
         seed_base=3000, scale_rule="nvfp4_amax"),
-    _wl(name="fp8_res_m4096_h5120_fp16", nvfp4=False, has_residual=True, scale_rule="fp8_amax", **_WIDE),
-    _wl(name="fp8_nores_m4096_h5120_fp16", nvfp4=False, has_residual=False, scale_rule="fp8_amax", **_WIDE),
-    _wl(name="nvfp4_res_m4096_h5120_fp16", nvfp4=True, has_residual=True, scale_rule="nvfp4_amax", **_WIDE),
-    _wl(name="nvfp4_nores_m4096_h5120_fp16", nvfp4=True, has_residual=False, scale_rule="nvfp4_amax", **_WIDE),
-    _wl(name="nvfp4_m32768_h8192_bf16_y", M=32768, H=8192, dtype="bf16", nvfp4=True,
+    _wl(name="fp8_res_m4096_h5120_fp16", mode="fp8", has_residual=True, scale_rule="fp8_amax", **_WIDE),
+    _wl(name="fp8_nores_m4096_h5120_fp16", mode="fp8", has_residual=False, scale_rule="fp8_amax", **_WIDE),
+    _wl(name="nvfp4_res_m4096_h5120_fp16", mode="nvfp4", has_residual=True, scale_rule="nvfp4_amax", **_WIDE),
+    _wl(name="nvfp4_nores_m4096_h5120_fp16", mode="nvfp4", has_residual=False, scale_rule="nvfp4_amax", **_WIDE),
+    _wl(name="nvfp4_m32768_h8192_bf16_y", M=32768, H=8192, dtype="bf16", mode="nvfp4",
         has_residual=True, write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1),
         seed_base=5000, scale_rule="nvfp4_amax"),
+    # MXFP8 output (scales from the data, no scale argument) at the prefill
+    # and the largest shape.
+    _wl(name="mxfp8_prefill_m8192_h4096_bf16_y", M=8192, H=4096, dtype="bf16", mode="mxfp8",
+        has_residual=True, write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1),
+        seed_base=6000, scale_rule="none"),
+    _wl(name="mxfp8_m32768_h8192_bf16_y", M=32768, H=8192, dtype="bf16", mode="mxfp8",
+        has_residual=True, write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1),
+        seed_base=7000, scale_rule="none"),
 ]}
 
 # The workload bench.py times by default: the largest one, bandwidth-bound.
@@ -141,7 +153,10 @@ def make_calibration_inputs(wl: Workload):
 
 
 def load_scale(wl: Workload) -> float:
-    """The workload's fp32 quant scale: fixed, or read from the stored table."""
+    """The workload's fp32 quant scale: fixed, or read from the stored table
+    (1.0, unused, for MXFP8)."""
+    if wl.scale_rule == "none":
+        return 1.0
     if wl.scale_rule == "fixed":
         return float(torch.tensor(wl.fixed_scale, dtype=torch.float32))
     with open(SCALES_JSON) as f:

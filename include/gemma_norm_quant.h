@@ -25,8 +25,15 @@
  *              rows >= M of that buffer are never written.
  *
  * Around it the library also exports the op's variants and its unfused form:
- * the same add + RMSNorm with a plain (w instead of 1 + w) norm and/or with
- * no quant, and the standalone FP8 / NVFP4 quant of an activation.
+ * the same add + RMSNorm with a plain (w instead of 1 + w) norm, with no
+ * quant, or with an MXFP8 output (the `allreduce_gemma_rms_norm_mxfp8`
+ * variant on the `fused_allreduce_gemma_rms_norm` page, without its
+ * all-reduce), and the standalone FP8 / NVFP4 / MXFP8 quant of an
+ * activation.  MXFP8 takes the OCP Microscaling scale rule (the page gives
+ * only the outputs' types and shapes): per 32-element block of a row,
+ * a = max|y|, e = max(floor(log2 a) - 8, -127) (-127 for a = 0), E8M0 scale
+ * code e + 127, codes E4M3FN(clamp(y * 2^-e, -448, 448)) round to nearest
+ * even; codes (M, H) and scales (M, H/32) both row-major.
  *
  * All pointers are caller-owned device buffers on the current HIP device.
  * The library allocates nothing, keeps no pointer past the call and launches
@@ -44,18 +51,24 @@
 extern "C" {
 #endif
 
-#define NQ_ABI_VERSION 2
+#define NQ_ABI_VERSION 3
 
 typedef enum {
   NQ_OK = 0,
   NQ_EINVAL = 1,        /* null required pointer, bad size, bad enum, aliasing */
-  NQ_EUNSUPPORTED = 2,  /* NVFP4 with H % 64 != 0 (or H % 16 != 0 for the standalone quant) */
+  NQ_EUNSUPPORTED = 2,  /* NVFP4 with H % 64 != 0 (H % 16 != 0 for the standalone quant),
+                           MXFP8 with H % 32 != 0 */
   NQ_EHIP = 3           /* a HIP runtime call or the launch failed */
 } nq_status;
 
 typedef enum { NQ_BF16 = 0, NQ_FP16 = 1 } nq_dtype;
 
-typedef enum { NQ_MODE_FP8_STATIC = 0, NQ_MODE_NVFP4 = 1, NQ_MODE_NONE = 2 } nq_mode;
+typedef enum {
+  NQ_MODE_FP8_STATIC = 0,
+  NQ_MODE_NVFP4 = 1,
+  NQ_MODE_NONE = 2,
+  NQ_MODE_MXFP8 = 3
+} nq_mode;
 
 /* RMSNorm scaling: Gemma's (1 + weight), or plain weight. */
 typedef enum { NQ_NORM_GEMMA = 0, NQ_NORM_PLAIN = 1 } nq_norm;
@@ -107,7 +120,10 @@ nq_status nq_gemma_add_rms_norm_quant(const void *x, void *residual, const void 
  *          quant, the op is add + RMSNorm alone (the tensor-parallel-size-1
  *          path of `fused_allreduce_gemma_rms_norm`, "identical to the unfused
  *          path"); then write_y must be nonzero and y non-NULL, and scale, q
- *          and block_scale are ignored (may be NULL).
+ *          and block_scale are ignored (may be NULL);
+ *          or NQ_MODE_MXFP8: q = (M, H) bytes of E4M3FN codes, block_scale =
+ *          (M, H/32) bytes of E8M0 scale codes, both row-major; H % 32 == 0
+ *          (NQ_EUNSUPPORTED otherwise); scale is ignored (may be NULL).
  *
  * Other arguments, layouts and errors as for nq_gemma_add_rms_norm_quant,
  * which equals this call with norm = NQ_NORM_GEMMA.
@@ -140,6 +156,16 @@ nq_status nq_quant_fp8_static(const void *y, const float *scale, int64_t M, int6
 nq_status nq_quant_nvfp4(const void *y, const float *global_scale, int64_t M, int64_t H, int dtype,
                          void *q, void *block_scale, void *stream);
 
+/*
+ * nq_quant_mxfp8 -- standalone MXFP8 quant of an (M, H) activation y of
+ * `dtype` (row-major contiguous), exactly the MXFP8 step of
+ * nq_add_rms_norm_quant: q = (M, H) E4M3FN bytes, scales = (M, H/32) E8M0
+ * bytes, both row-major.  H % 32 == 0 (NQ_EUNSUPPORTED otherwise); M == 0
+ * returns NQ_OK without launching.
+ */
+nq_status nq_quant_mxfp8(const void *y, int64_t M, int64_t H, int dtype, void *q, void *scales,
+                         void *stream);
+
 /* Size in bytes of the NVFP4 block-scale buffer:
  * round_up(M, 128) * round_up(H / 16, 4) (the wrapper's allocation on the
  * `fused_norm_quant` page).  0 for M <= 0 or H < 16. */
@@ -168,7 +194,11 @@ int nq_abi_version(void);
  *   kind 5: kind 4 for fp16 y
  *   kind 6: NVFP4 block-scale code of amax = fp32 pattern with global scale
  *           `param` -> 1 byte each
- *   out  device buffer of n (kinds 0, 1, 4, 5, 6) or 2n (kinds 2, 3) bytes.
+ *   kind 7: MXFP8 E8M0 scale code of amax = |fp32 pattern| -> 1 byte each
+ *   kind 8: MXFP8 element code of the fp32 pattern in a block whose E8M0
+ *           scale code is `param` (an integer in [0, 247], else
+ *           NQ_EINVAL) -> 1 byte each
+ *   out  device buffer of n (kinds 0, 1, 4..8) or 2n (kinds 2, 3) bytes.
  *   n    in [0, 2^31).
  */
 nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,

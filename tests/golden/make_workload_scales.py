@@ -45,7 +45,7 @@ def main(names):
             table = json.load(f)
     for name in names:
         wl = WORKLOADS[name]
-        if wl.scale_rule == "fixed":
+        if wl.scale_rule in ("fixed", "none"):
             continue
         if wl.scale_rule == "fp8_amax_calibration":
             x, r, w = make_calibration_inputs(wl)

@@ -10,12 +10,14 @@ full run.
 
 Acceptance, per element of the compared rows:
   residual     bit-exact;
-  y            at most 1 unit in the last place of x's dtype;
-  codes        (FP8 element, NVFP4 block) bit-exact where the GPU's y equals
-               the oracle's y bit for bit, otherwise at most one code step,
-               with at most 1e-4 of all codes differing;
-  NVFP4 scales bit-exact in at least 99.99% of blocks (and wherever the
-               block's y matches);
+  y            at most 1 unit in the last place of x's dtype, and a zero y
+               with the oracle's sign;
+  codes        (FP8 element, NVFP4 / MXFP8 block) bit-exact (signed zeros
+               included) where the GPU's y equals the oracle's y bit for bit,
+               otherwise at most one code step (MXFP8: in blocks whose scale
+               matches), with at most 1e-4 of all codes differing;
+  NVFP4 / MXFP8 scales bit-exact in at least 99.99% of blocks (and wherever
+               the block's y matches);
   quant step   the GPU's codes and scales equal the oracle's quant step
                applied to the GPU's own y, bit for bit (needs the GPU's y);
   padding      scale-buffer rows >= M and all guard bytes keep the sentinel.
@@ -43,15 +45,18 @@ def _guarded(nbytes, dev):
 
 
 def run_gpu(x, r, w, eps, scale, nvfp4, write_y, device="cuda", misalign=False, norm="gemma",
-            quant=True):
+            quant=True, mxfp8=False):
     """Run the HIP op once on device copies of CPU tensors.  Returns numpy
     outputs and the guard/padding state.  ``misalign`` places x, residual and
     y at a 2-byte offset (a non-16-byte-aligned view).  ``norm`` "plain"
     scales by w instead of 1 + w; ``quant`` False runs add + norm alone (y is
-    then always written)."""
-    mode = ("nvfp4" if nvfp4 else "fp8") if quant else None
+    then always written); ``mxfp8`` selects the MXFP8 output (``nvfp4`` and
+    ``scale`` are then ignored and no scale pointer is passed)."""
+    mode = ("mxfp8" if mxfp8 else "nvfp4" if nvfp4 else "fp8") if quant else None
     if not quant:
-        write_y, nvfp4 = True, False
+        write_y = True
+    if mode != "nvfp4":
+        nvfp4 = False
     dev = torch.device(device)
     M, H = x.shape
     dt = x.dtype
@@ -74,15 +79,16 @@ def run_gpu(x, r, w, eps, scale, nvfp4, write_y, device="cuda", misalign=False, 
     qv = qbuf[off:off + qbytes]
     if quant:
         qv = qv.view(M, H // 2) if nvfp4 else qv.view(torch.float8_e4m3fn).view(M, H)
-    bsn = ops.block_scale_bytes(M, H) if nvfp4 else 0
-    bsbuf = _guarded(bsn, dev) if nvfp4 else None
+    bsn = ops.block_scale_bytes(M, H) if nvfp4 else M * (H // 32) if mode == "mxfp8" else 0
+    has_bs = mode in ("nvfp4", "mxfp8")
+    bsbuf = _guarded(bsn, dev) if has_bs else None
     ybuf, yd = place(None) if write_y else (None, None)
-    if norm == "gemma" and quant:
+    if norm == "gemma" and mode in ("fp8", "nvfp4"):
         ops.gemma_add_rms_norm_quant_out(xd, rd, wd, eps, sd, nvfp4, qv,
                                          bsbuf[:bsn] if nvfp4 else None, yd)
     else:
-        ops.add_rms_norm_quant_out(xd, rd, wd, eps, sd if quant else None, mode, norm,
-                                   qv if quant else None, bsbuf[:bsn] if nvfp4 else None, yd)
+        ops.add_rms_norm_quant_out(xd, rd, wd, eps, sd if mode in ("fp8", "nvfp4") else None, mode,
+                                   norm, qv if quant else None, bsbuf[:bsn] if has_bs else None, yd)
     torch.cuda.synchronize(dev)
 
     def tail_ok(buf, n):
@@ -94,7 +100,7 @@ def run_gpu(x, r, w, eps, scale, nvfp4, write_y, device="cuda", misalign=False, 
         "residual": bits16(rd) if rd is not None else None,
         "y": bits16(yd) if yd is not None else None,
         "q": (qv.view(torch.uint8).cpu().numpy() if not nvfp4 else qv.cpu().numpy()) if quant else None,
-        "bs": bsbuf[:bsn].cpu().numpy() if nvfp4 else None,
+        "bs": bsbuf[:bsn].cpu().numpy() if has_bs else None,
         "guards_ok": all([tail_ok(xbuf, act), tail_ok(qbuf, qbytes),
                           rbuf is None or tail_ok(rbuf, act), ybuf is None or tail_ok(ybuf, act),
                           bsbuf is None or bool((bsbuf[bsn:].cpu() == SENTINEL).all())]),
@@ -154,12 +160,34 @@ def compare(gpu, x, r, w, eps, scale, rows, y_gpu=None):
         dy = np.abs(_ord16(yg) - _ord16(ref["y"]))
         rep["y_max_ulp"] = int(dy.max()) if dy.size else 0
         rep["y_diff_fraction"] = float(np.count_nonzero(dy) / max(dy.size, 1))
-        y_equal = dy == 0
+        y_equal = yg == ref["y"]
+        # +0 and -0 are one ulp step apart in no ordering: count them apart
+        rep["y_zero_sign_mismatch"] = int(np.count_nonzero((dy == 0) & ~y_equal))
     else:
         y_equal = None
     if mode is None:
         rep["code_max_step"] = 0
         rep["code_diff_fraction"] = 0.0
+        return rep
+    if mode == "mxfp8":
+        cg = gpu["q"][rows]
+        cr = ref["q"]
+        sg = gpu["bs"].reshape(M, H // 32)[rows]
+        sr = ref["scales"]
+        rep["scale_match_fraction"] = float(np.count_nonzero(sg == sr) / max(sr.size, 1))
+        same_scale = np.repeat(sg == sr, 32, axis=1)
+        step = np.where(same_scale, np.abs(_ord_code(cg, 0x80) - _ord_code(cr, 0x80)), 0)
+        rep["codes_in_rescaled_blocks"] = int(np.count_nonzero(~same_scale))
+        if y_equal is not None:
+            blk_eq = y_equal.reshape(len(rows), -1, 32).all(axis=2)
+            rep["scale_mismatch_where_y_equal"] = int(np.count_nonzero((sg != sr) & blk_eq))
+            rep["code_mismatch_where_y_equal"] = int(np.count_nonzero(
+                (cg != cr).reshape(len(rows), -1, 32).any(axis=2) & blk_eq))
+            q2, s2 = O.quant_mxfp8(yg, fmt)
+            rep["requant_code_mismatch"] = int(np.count_nonzero(q2 != cg))
+            rep["requant_scale_mismatch"] = int(np.count_nonzero(s2 != sg))
+        rep["code_diff_fraction"] = float(np.count_nonzero(cg != cr) / max(cg.size, 1))
+        rep["code_max_step"] = int(step.max()) if step.size else 0
         return rep
     if nvfp4:
         cg = _unpack_e2m1(gpu["q"][rows])
@@ -172,7 +200,7 @@ def compare(gpu, x, r, w, eps, scale, rows, y_gpu=None):
             blk_eq = y_equal.reshape(len(rows), -1, 16).all(axis=2)
             rep["scale_mismatch_where_y_equal"] = int(np.count_nonzero((sg != sr) & blk_eq))
             rep["code_mismatch_where_y_equal"] = int(np.count_nonzero(
-                (step != 0).reshape(len(rows), -1, 16).any(axis=2) & blk_eq))
+                (cg != cr).reshape(len(rows), -1, 16).any(axis=2) & blk_eq))
             q2, s2 = O.quant_nvfp4(yg, fmt, scale)
             rep["requant_code_mismatch"] = int(np.count_nonzero(q2 != gpu["q"][rows]))
             rep["requant_scale_mismatch"] = int(np.count_nonzero(s2 != sg))
@@ -188,11 +216,11 @@ def compare(gpu, x, r, w, eps, scale, rows, y_gpu=None):
         cr = ref["q"]
         step = np.abs(_ord_code(cg, 0x80) - _ord_code(cr, 0x80))
         if y_equal is not None:
-            rep["code_mismatch_where_y_equal"] = int(np.count_nonzero((step != 0) & y_equal))
+            rep["code_mismatch_where_y_equal"] = int(np.count_nonzero((cg != cr) & y_equal))
             q2 = O.quant_fp8_static(yg, fmt, scale)
             rep["requant_code_mismatch"] = int(np.count_nonzero(q2 != cg))
     rep["code_max_step"] = int(step.max()) if step.size else 0
-    rep["code_diff_fraction"] = float(np.count_nonzero(step) / max(step.size, 1))
+    rep["code_diff_fraction"] = float(np.count_nonzero(cg != cr) / max(cg.size, 1))
     return rep
 
 
@@ -211,7 +239,7 @@ def check(rep):
         bad.append(f"code off by {rep['code_max_step']} steps")
     if rep["code_diff_fraction"] > CODE_DIFF_FRACTION:
         bad.append(f"code diff fraction {rep['code_diff_fraction']:.3g}")
-    for k in ("code_mismatch_where_y_equal", "scale_mismatch_where_y_equal",
+    for k in ("y_zero_sign_mismatch", "code_mismatch_where_y_equal", "scale_mismatch_where_y_equal",
               "requant_code_mismatch", "requant_scale_mismatch", "padding_written"):
         if rep.get(k, 0):
             bad.append(f"{k}: {rep[k]}")

@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert _lib.nq_abi_version() == 2
+    assert _lib.nq_abi_version() == 3
     assert _lib.nq_status_string(0) == "ok"
     for s in range(0, 6):
         assert isinstance(_lib.nq_status_string(s), str)
@@ -99,7 +99,16 @@ def call_ex(**over):
 
 @pytest.mark.parametrize("over,want", [
     (dict(norm=2), _lib.NQ_EINVAL),
-    (dict(mode=3), _lib.NQ_EINVAL),
+    (dict(mode=4), _lib.NQ_EINVAL),
+    (dict(mode=3, bs=0), _lib.NQ_EINVAL),             # MXFP8 needs its scale buffer
+    (dict(mode=3, q=0), _lib.NQ_EINVAL),
+    (dict(mode=3, H=48), _lib.NQ_EUNSUPPORTED),       # H % 32 != 0
+    (dict(mode=3, H=16, M=0), _lib.NQ_EUNSUPPORTED),
+    (dict(mode=3, bs=Q + 500), _lib.NQ_EINVAL),       # scales overlap the (M, H) codes
+    (dict(mode=3, bs=R + 8), _lib.NQ_EINVAL),         # scales overlap residual
+    (dict(mode=3, wy=1, y=B + 8), _lib.NQ_EINVAL),    # y overlaps the scales
+    (dict(mode=3, s=0, M=0), _lib.NQ_OK),             # scale ignored for MXFP8
+    (dict(mode=3, H=96, M=0, norm=1), _lib.NQ_OK),
     (dict(mode=2, wy=0), _lib.NQ_EINVAL),            # no-quant mode needs y
     (dict(mode=2, wy=1, y=0), _lib.NQ_EINVAL),
     (dict(mode=2, wy=1, y=X + 64), _lib.NQ_EINVAL),  # y overlaps x
@@ -112,8 +121,9 @@ def test_general_entry_validation(over, want):
     assert call_ex(**over) == want
 
 
-def test_gemma_entry_rejects_no_quant_mode():
+def test_gemma_entry_rejects_no_quant_and_mxfp8_modes():
     assert call(mode=2, wy=1, M=0) == _lib.NQ_EINVAL
+    assert call(mode=3, M=0) == _lib.NQ_EINVAL
 
 
 @pytest.mark.parametrize("nv,over,want", [
@@ -140,8 +150,28 @@ def test_standalone_quant_validation(nv, over, want):
     assert st == want
 
 
+@pytest.mark.parametrize("over,want", [
+    (dict(y=0), _lib.NQ_EINVAL),
+    (dict(q=0), _lib.NQ_EINVAL),
+    (dict(bs=0), _lib.NQ_EINVAL),
+    (dict(H=48), _lib.NQ_EUNSUPPORTED),
+    (dict(dtype=2), _lib.NQ_EINVAL),
+    (dict(bs=Q + 511), _lib.NQ_EINVAL),               # scales overlap the codes
+    (dict(q=X + 2), _lib.NQ_EINVAL),                  # codes overlap y
+    (dict(M=0), _lib.NQ_OK),
+    (dict(M=0, H=32), _lib.NQ_OK),
+])
+def test_standalone_mxfp8_validation(over, want):
+    a = dict(y=X, M=4, H=128, dtype=0, q=Q, bs=B)
+    a.update(over)
+    assert _lib.nq_quant_mxfp8(a["y"], a["M"], a["H"], a["dtype"], a["q"], a["bs"], 0) == want
+
+
 def test_probe_validation():
     assert _lib.nq_convert_probe(9, 0x1000, 4, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
+    for bad in (-1.0, 248.0, 12.5, float("nan"), float("inf")):
+        assert _lib.nq_convert_probe(8, 0x1000, 4, bad, 0x2000, 0) == _lib.NQ_EINVAL, bad
+    assert _lib.nq_convert_probe(8, 0x1000, 0, 247.0, 0x2000, 0) == _lib.NQ_OK
     assert _lib.nq_convert_probe(0, 0x1000, -1, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
     assert _lib.nq_convert_probe(0, 0, 4, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
     assert _lib.nq_convert_probe(0, 0x1000, 0, 1.0, 0x2000, 0) == _lib.NQ_OK

@@ -28,14 +28,14 @@ def _need_gpu():
     _lib.lib()  # the HIP library must be there: no fallback
 
 
-def _run_and_compare(x, r, w, eps, scale, nvfp4, write_y, rows=None, misalign=False):
+def _run_and_compare(x, r, w, eps, scale, nvfp4, write_y, rows=None, misalign=False, mxfp8=False):
     r_in = r.clone() if r is not None else None
-    gpu = P.run_gpu(x, r_in, w, eps, scale, nvfp4, write_y, misalign=misalign)
+    gpu = P.run_gpu(x, r_in, w, eps, scale, nvfp4, write_y, misalign=misalign, mxfp8=mxfp8)
     y_gpu = None
     if not write_y:
         # The same kernel arithmetic with y written, for the quant-step check.
         y_gpu = P.run_gpu(x, r.clone() if r is not None else None, w, eps, scale, nvfp4, True,
-                          misalign=misalign)["y"]
+                          misalign=misalign, mxfp8=mxfp8)["y"]
     M = x.shape[0]
     rows = P.sample_rows(M) if rows is None else rows
     rep = P.compare(gpu, x, r, w, eps, scale, rows, y_gpu=y_gpu)
@@ -56,7 +56,8 @@ def test_workload_parity(name):
         big = (x.float().abs().amax(dim=1) > 20).nonzero().flatten().tolist()
         extra = big
     rows = P.sample_rows(wl.M, extra=extra)
-    _run_and_compare(x, r, w, wl.eps, load_scale(wl), wl.nvfp4, wl.write_y, rows=rows)
+    _run_and_compare(x, r, w, wl.eps, load_scale(wl), wl.nvfp4, wl.write_y, rows=rows,
+                     mxfp8=wl.mode == "mxfp8")
 
 
 EDGE = [
