@@ -207,15 +207,14 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // ----------------------------------------------------------------------------
-// Gemma (1 + w) or plain (w) RMSNorm scaling of t = h * rstd, one rounding.
-// fma(t, w, t) is the correctly rounded t * (1 + w).  Its exact zeros (t = 0
-// or w = -1) come out as +0 from the cancellation; the sign bit is therefore
-// taken from t * fl(1 + w), which carries the sign of the product
-// h * rstd * (1 + w) in every case (fl(1 + w) is +0 for w = -1 and has the
-// sign of 1 + w otherwise), so a zero y keeps the sign that product has.
+// Gemma (1 + w) or plain (w) RMSNorm scaling of t = h * rstd in IEEE fp32:
+// t * fl(1 + w) (two fp32 roundings, then one to the activation dtype: within
+// one unit of that dtype of the exact value).  Plain IEEE products also give
+// every zero y the sign of h * rstd * (1 + w): fl(1 + w) is +0 for w = -1,
+// and t keeps the sign of h.
 template <bool GEMMA>
 __device__ __forceinline__ float norm_scale(float t, float w) {
-  if constexpr (GEMMA) return __builtin_copysignf(__builtin_fmaf(t, w, t), t * (1.0f + w));
+  if constexpr (GEMMA) return t * (1.0f + w);
   return t * w;
 }
 

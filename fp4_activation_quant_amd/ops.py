@@ -1,19 +1,28 @@
-"""PyTorch-facing wrapper of the fused op, mirroring ``gemma_add_rms_norm_quant``
-on the ``fused_norm_quant`` page: same arguments, same checks, same output
-allocation (PyTorch provides device memory and the stream; the HIP library
-does all the work)."""
+"""PyTorch-facing entry points of the HIP library.
+
+PyTorch supplies device memory and the current stream; every step of the op
+runs in the library (``_lib`` only marshals pointers).  The public call
+``gemma_add_rms_norm_quant`` keeps the interface of the op on the
+``fused_norm_quant`` page -- the same arguments, the same output tuple and
+output shapes -- so callers of that op can switch to it unchanged; the other
+functions expose the library's variants (plain norm, no quant, MXFP8) and
+the standalone quant kernels of the unfused chain.
+"""
 
 import torch
 
 from . import _lib
 
 _DT = {torch.bfloat16: _lib.NQ_BF16, torch.float16: _lib.NQ_FP16}
+_MODES = {"fp8": _lib.NQ_MODE_FP8_STATIC, "nvfp4": _lib.NQ_MODE_NVFP4, "mxfp8": _lib.NQ_MODE_MXFP8,
+          None: _lib.NQ_MODE_NONE}
+_NORMS = {"gemma": _lib.NQ_NORM_GEMMA, "plain": _lib.NQ_NORM_PLAIN}
 FP8_DTYPE = torch.float8_e4m3fn
 E8M0_DTYPE = torch.float8_e8m0fnu
 
 
 def round_up(a, b):
-    return (a + b - 1) // b * b
+    return -(-a // b) * b
 
 
 def _check(status, what):
@@ -21,73 +30,61 @@ def _check(status, what):
         raise _lib.NqError(status, what)
 
 
-def gemma_add_rms_norm_quant(x, residual, weight, eps, scale, nvfp4, write_y=False):
-    """Gemma RMSNorm of ``x (+ residual)`` quantized for the next linear.
-
-    x: (M, H) bf16/fp16, contiguous, read only.  residual: same shape or None;
-    updated in place to x + residual.  weight: (H,); the norm scales by
-    (1 + weight).  scale: fp32 tensor with one element -- FP8: the static
-    per-tensor input scale; NVFP4: the global scale.  Returns
-    ``(q, block_scale, y)``: FP8 codes (M, H) float8_e4m3fn, or packed E2M1
-    (M, H // 2) uint8; NVFP4 block scales (round_up(M, 128),
-    round_up(H // 16, 4)) float8_e4m3fn in the 128x4-tiled layout with rows
-    >= M left unwritten, or ``scale`` for FP8; and the normed activation in
-    x's dtype when ``write_y`` (else None).
-    """
-    assert x.dim() == 2 and x.is_contiguous()
-    assert x.dtype in (torch.bfloat16, torch.float16)
-    assert x.is_cuda
-    assert residual is None or (residual.shape == x.shape and residual.is_contiguous()
-                                and residual.dtype == x.dtype and residual.device == x.device)
-    assert weight.shape == (x.shape[1],) and weight.is_contiguous() and weight.dtype == x.dtype
-    assert scale.numel() == 1 and scale.dtype == torch.float32 and scale.device == x.device
-    M, H = x.shape
-    if nvfp4:
-        assert H % 64 == 0
-        q = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device)
-        block_scale = torch.empty((round_up(M, 128), round_up(H // 16, 4) // 4),
-                                  dtype=torch.int32, device=x.device).view(FP8_DTYPE)
-    else:
-        q = torch.empty((M, H), dtype=FP8_DTYPE, device=x.device)
-        block_scale = scale
-    y = torch.empty_like(x) if write_y else None
-    if M == 0:
-        return q, block_scale, y
-    gemma_add_rms_norm_quant_out(x, residual, weight, eps, scale, nvfp4, q,
-                                 block_scale if nvfp4 else None, y)
-    return q, block_scale, y
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
 
 
 def _ptr(t):
-    return t.data_ptr() if t is not None else 0
+    return 0 if t is None else t.data_ptr()
 
 
 def _stream(dev):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def gemma_add_rms_norm_quant_out(x, residual, weight, eps, scale, nvfp4, q, block_scale, y):
-    """Same op into caller-allocated outputs (no allocation, no checks beyond
-    the library's own).  ``y`` None means write_y=False."""
-    M, H = x.shape
-    with torch.cuda.device(x.device):
-        st = _lib.nq_gemma_add_rms_norm_quant(
-            x.data_ptr(), _ptr(residual), weight.data_ptr(), eps, scale.data_ptr(), M, H,
-            _DT[x.dtype], _lib.NQ_MODE_NVFP4 if nvfp4 else _lib.NQ_MODE_FP8_STATIC, y is not None,
-            q.data_ptr(), _ptr(block_scale), _ptr(y), _stream(x.device))
-    _check(st, "nq_gemma_add_rms_norm_quant")
+def _validate(x, residual, weight, scale):
+    _require(x.is_cuda and x.dim() == 2 and x.is_contiguous(), "x: contiguous 2-D device tensor")
+    _require(x.dtype in _DT, "x: bfloat16 or float16")
+    if residual is not None:
+        _require(residual.shape == x.shape and residual.dtype == x.dtype and
+                 residual.device == x.device and residual.is_contiguous(),
+                 "residual: contiguous, same shape, dtype and device as x")
+    _require(weight.shape == (x.shape[1],) and weight.dtype == x.dtype and weight.is_contiguous()
+             and weight.device == x.device, "weight: contiguous (H,) of x's dtype, on x's device")
+    if scale is not None:
+        _require(scale.numel() == 1 and scale.dtype == torch.float32 and scale.device == x.device,
+                 "scale: one float32 on x's device")
 
 
-_MODES = {"fp8": _lib.NQ_MODE_FP8_STATIC, "nvfp4": _lib.NQ_MODE_NVFP4, "mxfp8": _lib.NQ_MODE_MXFP8,
-          None: _lib.NQ_MODE_NONE}
-_NORMS = {"gemma": _lib.NQ_NORM_GEMMA, "plain": _lib.NQ_NORM_PLAIN}
+def _outputs(M, H, mode, dev, scale):
+    """(q, block_scale) buffers for an output mode; the FP8 "block scale" is
+    the caller's scale tensor itself."""
+    if mode == "nvfp4":
+        _require(H % 64 == 0, "NVFP4 needs H % 64 == 0")
+        q = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+        # 128x4-tiled E4M3 scales, rows padded to 128 and scale columns to 4;
+        # the padding rows are never written.
+        bs = torch.empty((round_up(M, 128), round_up(H // 16, 4)), dtype=torch.uint8,
+                         device=dev).view(FP8_DTYPE)
+        return q, bs
+    if mode == "mxfp8":
+        _require(H % 32 == 0, "MXFP8 needs H % 32 == 0")
+        return (torch.empty((M, H), dtype=FP8_DTYPE, device=dev),
+                torch.empty((M, H // 32), dtype=E8M0_DTYPE, device=dev))
+    return torch.empty((M, H), dtype=FP8_DTYPE, device=dev), scale
 
 
 def add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q, block_scale, y):
-    """The op with the norm ("gemma": 1 + w, "plain": w) and the output mode
-    ("fp8", "nvfp4", "mxfp8" or None for add + norm alone) chosen, into
-    caller-allocated outputs.  MXFP8: ``block_scale`` is the (M, H // 32)
-    E8M0 scale buffer and ``scale`` is ignored (may be None)."""
+    """One launch of the op into caller-allocated buffers; no allocation and
+    no checks beyond the library's own.
+
+    ``norm``: "gemma" (scale by 1 + w) or "plain" (by w).  ``mode``: "fp8"
+    (static per-tensor, ``scale`` = the dequant scale), "nvfp4" (``scale`` =
+    global scale, ``block_scale`` = the 128x4-tiled buffer), "mxfp8"
+    (``block_scale`` = (M, H // 32) E8M0 scales, ``scale`` ignored) or None
+    (add + norm only; ``y`` required).  ``y`` None: the normed activation is
+    not written."""
     M, H = x.shape
     with torch.cuda.device(x.device):
         st = _lib.nq_add_rms_norm_quant(
@@ -97,35 +94,61 @@ def add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q, block
     _check(st, "nq_add_rms_norm_quant")
 
 
+def gemma_add_rms_norm_quant_out(x, residual, weight, eps, scale, nvfp4, q, block_scale, y):
+    """The page's op (Gemma norm, FP8 or NVFP4) into caller-allocated buffers,
+    through the library's own entry point for it."""
+    M, H = x.shape
+    with torch.cuda.device(x.device):
+        st = _lib.nq_gemma_add_rms_norm_quant(
+            x.data_ptr(), _ptr(residual), weight.data_ptr(), eps, scale.data_ptr(), M, H,
+            _DT[x.dtype], _lib.NQ_MODE_NVFP4 if nvfp4 else _lib.NQ_MODE_FP8_STATIC, y is not None,
+            q.data_ptr(), _ptr(block_scale), _ptr(y), _stream(x.device))
+    _check(st, "nq_gemma_add_rms_norm_quant")
+
+
 def add_rms_norm_quant(x, residual, weight, eps, scale, mode, norm="gemma", write_y=False):
-    """Allocating form of add_rms_norm_quant_out: returns (q, block_scale, y)
-    as gemma_add_rms_norm_quant does; mode None returns (None, None, y);
-    mode "mxfp8" returns E4M3 codes (M, H) and E8M0 scales (M, H // 32)
-    (torch.float8_e8m0fnu), both row-major."""
-    assert x.dim() == 2 and x.is_contiguous() and x.dtype in _DT and x.is_cuda
+    """Allocating form of ``add_rms_norm_quant_out``.  Returns
+    ``(q, block_scale, y)``: codes, scales (FP8: ``scale`` itself), and the
+    normed activation when ``write_y`` (always for mode None, which returns
+    ``(None, None, y)``).  ``residual`` (or None) is updated in place."""
+    _validate(x, residual, weight, scale if mode in ("fp8", "nvfp4") else None)
     M, H = x.shape
     if mode is None:
         y = torch.empty_like(x)
         if M:
             add_rms_norm_quant_out(x, residual, weight, eps, None, None, norm, None, None, y)
         return None, None, y
-    if mode == "nvfp4":
-        assert H % 64 == 0
-        q = torch.empty((M, H // 2), dtype=torch.uint8, device=x.device)
-        block_scale = torch.empty((round_up(M, 128), round_up(H // 16, 4) // 4),
-                                  dtype=torch.int32, device=x.device).view(FP8_DTYPE)
-    elif mode == "mxfp8":
-        assert H % 32 == 0
-        q = torch.empty((M, H), dtype=FP8_DTYPE, device=x.device)
-        block_scale = torch.empty((M, H // 32), dtype=E8M0_DTYPE, device=x.device)
-    else:
-        q = torch.empty((M, H), dtype=FP8_DTYPE, device=x.device)
-        block_scale = scale
+    q, bs = _outputs(M, H, mode, x.device, scale)
     y = torch.empty_like(x) if write_y else None
     if M:
         add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q,
-                               block_scale if mode in ("nvfp4", "mxfp8") else None, y)
-    return q, block_scale, y
+                               bs if mode != "fp8" else None, y)
+    return q, bs, y
+
+
+def gemma_add_rms_norm_quant(x, residual, weight, eps, scale, nvfp4, write_y=False):
+    """Fused residual add + Gemma RMSNorm + input quant for the next linear.
+
+    ``x`` (M, H) bf16 or fp16 is only read.  ``residual`` (same shape and
+    dtype, or None) receives x + residual.  The norm multiplies by
+    (1 + ``weight``).  ``scale`` is one float32 on the device: the static
+    FP8 dequant scale, or with ``nvfp4`` the NVFP4 global scale.  Returns
+    ``(q, block_scale, y)``:
+
+    * FP8: q (M, H) float8_e4m3fn, block_scale = ``scale``;
+    * NVFP4 (H % 64 == 0): q (M, H // 2) uint8, two E2M1 codes per byte;
+      block_scale (round_up(M, 128), round_up(H // 16, 4)) float8_e4m3fn in
+      the 128x4-tiled layout, padding rows untouched;
+    * y: the normed activation in x's dtype when ``write_y``, else None.
+    """
+    _validate(x, residual, weight, scale)
+    M, H = x.shape
+    q, bs = _outputs(M, H, "nvfp4" if nvfp4 else "fp8", x.device, scale)
+    y = torch.empty_like(x) if write_y else None
+    if M:
+        gemma_add_rms_norm_quant_out(x, residual, weight, eps, scale, nvfp4, q,
+                                     bs if nvfp4 else None, y)
+    return q, bs, y
 
 
 def gemma_add_rms_norm_mxfp8(x, residual, weight, eps, return_normed=False):
@@ -144,9 +167,14 @@ def gemma_add_rms_norm(x, residual, weight, eps):
     return add_rms_norm_quant(x, residual, weight, eps, None, None, "gemma", True)[2]
 
 
+def _validate_y(y):
+    _require(y.is_cuda and y.dim() == 2 and y.is_contiguous() and y.dtype in _DT,
+             "y: contiguous 2-D bfloat16/float16 device tensor")
+
+
 def quant_fp8_static(y, scale, q=None):
     """Standalone static FP8 quant of an activation: E4M3FN(y / scale)."""
-    assert y.dim() == 2 and y.is_contiguous() and y.dtype in _DT and y.is_cuda
+    _validate_y(y)
     M, H = y.shape
     if q is None:
         q = torch.empty((M, H), dtype=FP8_DTYPE, device=y.device)
@@ -160,13 +188,13 @@ def quant_fp8_static(y, scale, q=None):
 
 def quant_nvfp4(y, global_scale, q=None, block_scale=None):
     """Standalone NVFP4 quant: packed E2M1 codes and 128x4-tiled E4M3 scales."""
-    assert y.dim() == 2 and y.is_contiguous() and y.dtype in _DT and y.is_cuda
+    _validate_y(y)
     M, H = y.shape
     if q is None:
         q = torch.empty((M, H // 2), dtype=torch.uint8, device=y.device)
     if block_scale is None:
-        block_scale = torch.empty((round_up(M, 128), round_up(H // 16, 4) // 4),
-                                  dtype=torch.int32, device=y.device).view(FP8_DTYPE)
+        block_scale = torch.empty((round_up(M, 128), round_up(H // 16, 4)), dtype=torch.uint8,
+                                  device=y.device).view(FP8_DTYPE)
     if M:
         with torch.cuda.device(y.device):
             st = _lib.nq_quant_nvfp4(y.data_ptr(), global_scale.data_ptr(), M, H, _DT[y.dtype],
@@ -178,7 +206,7 @@ def quant_nvfp4(y, global_scale, q=None, block_scale=None):
 def quant_mxfp8(y, q=None, scales=None):
     """Standalone MXFP8 quant: E4M3 codes (M, H) and E8M0 scales (M, H // 32),
     row-major."""
-    assert y.dim() == 2 and y.is_contiguous() and y.dtype in _DT and y.is_cuda
+    _validate_y(y)
     M, H = y.shape
     if q is None:
         q = torch.empty((M, H), dtype=FP8_DTYPE, device=y.device)

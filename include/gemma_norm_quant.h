@@ -2,24 +2,24 @@
  * gemma_norm_quant.h -- C ABI of the MI355X (gfx950) fused residual-add +
  * Gemma RMSNorm + activation-quant library (libgemma_norm_quant.so).
  *
- * The operation is the one stated on the `fused_norm_quant` page
- * (`gemma_add_rms_norm_quant(x, residual, weight, eps, scale, nvfp4,
- * write_y)`, its parameter list, "Returns" list and wrapper source):
+ * The operation is `gemma_add_rms_norm_quant` on the `fused_norm_quant`
+ * page (its argument list, return tuple and Python wrapper):
  *
- *   h        = x + residual, rounded to x's dtype and written back into
- *              `residual` ("Updated in place to x + residual"); h = x when
- *              residual is NULL, and nothing is written back then;
+ *   h        = x + residual, rounded to x's dtype and stored back into
+ *              `residual` (the residual stream is updated in place); h = x
+ *              when residual is NULL, and nothing is stored back then;
  *   y        = h * rsqrt(mean(h^2) + eps) * (1 + weight), fp32 arithmetic,
- *              rounded to x's dtype ("the norm scales by (1 + weight)"; the
- *              quantized values are computed from this rounded y);
+ *              rounded to x's dtype (Gemma's norm multiplies by one plus the
+ *              weight; the codes below are taken from this rounded y, as
+ *              the page's module docstring states);
  *   FP8      : q = E4M3FN(clamp(y / scale, -448, 448)), round to nearest even
  *              (static per-tensor scale; the caller keeps `scale` as the
  *              returned block scale);
  *   NVFP4    : per 16-element block of a row, a = max|y|, S = E4M3FN(min(
  *              scale * (a / 6), 448)), o = scale / S (0 if S == 0), codes
  *              E2M1(clamp(y * o, -6, 6)) round to nearest even, two per byte
- *              with the even-index element in the low nibble ("lo in the
- *              low nibble", `_cvt_e2m1x2`); S is stored in the 128x4-tiled
+ *              with the even-index element in the low nibble (the operand
+ *              order of the page's `_cvt_e2m1x2` helper); S is stored in the 128x4-tiled
  *              layout (byte (m, b) at ((m/128)*(Kp/4) + b/4)*512 +
  *              (m%32)*16 + ((m%128)/32)*4 + b%4, Kp = round_up(H/16, 4));
  *              rows >= M of that buffer are never written.
@@ -117,9 +117,10 @@ nq_status nq_gemma_add_rms_norm_quant(const void *x, void *residual, const void 
  *          `rms_norm_static_fp8_quant` / `fused_add_rms_norm_static_fp8_quant`
  *          semantics named on the PR conversation page).
  *   mode   NQ_MODE_FP8_STATIC / NQ_MODE_NVFP4 as above, or NQ_MODE_NONE: no
- *          quant, the op is add + RMSNorm alone (the tensor-parallel-size-1
- *          path of `fused_allreduce_gemma_rms_norm`, "identical to the unfused
- *          path"); then write_y must be nonzero and y non-NULL, and scale, q
+ *          quant, the op is add + RMSNorm alone (what
+ *          `fused_allreduce_gemma_rms_norm` reduces to at tensor-parallel
+ *          size 1, where it equals the unfused path); then write_y must be
+ *          nonzero and y non-NULL, and scale, q
  *          and block_scale are ignored (may be NULL);
  *          or NQ_MODE_MXFP8: q = (M, H) bytes of E4M3FN codes, block_scale =
  *          (M, H/32) bytes of E8M0 scale codes, both row-major; H % 32 == 0
@@ -135,9 +136,9 @@ nq_status nq_add_rms_norm_quant(const void *x, void *residual, const void *weigh
 
 /*
  * nq_quant_fp8_static / nq_quant_nvfp4 -- the standalone quant kernels of
- * the unfused chain (the `fused_norm_quant` module docstring: the fused
- * kernel replaces the Gemma add-RMSNorm followed by a standalone static FP8
- * or NVFP4 quant, with the same scale arithmetic).  y is an (M, H)
+ * the unfused chain that the `fused_norm_quant` module docstring says the
+ * fused kernel replaces (an add + Gemma RMSNorm kernel, then a separate
+ * static-FP8 or NVFP4 quant kernel using identical scale math).  y is an (M, H)
  * activation of `dtype`, row-major contiguous; the codes, block scales,
  * rounding and layout are exactly the fused op's quant step.
  *

@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Formats used by the op:
 
-* bf16 and fp16 -- the activation dtypes ("bf16/fp16 activation" in the
-  ``gemma_add_rms_norm_quant`` parameter list of the ``fused_norm_quant``
-  page).  IEEE-style: an all-ones exponent field is Inf/NaN.
+* bf16 and fp16 -- the activation dtypes (the ``x`` argument of
+  ``gemma_add_rms_norm_quant`` on the ``fused_norm_quant`` page may be
+  either).  IEEE-style: an all-ones exponent field is Inf/NaN.
 * E4M3FN -- the FP8 code of the static per-tensor mode and of the NVFP4 block
   scales (``FP8_DTYPE`` / ``current_platform.fp8_dtype()`` on the
   ``fused_norm_quant`` and ``fused_allreduce_norm_quant`` pages).  Read as the

@@ -46,7 +46,7 @@ __all__ = [
     "gemma_add_rms_norm_quant", "add_rms_norm_quant",
 ]
 
-NVFP4_BLOCK = 16      # elements per block scale ("16-element blocks")
+NVFP4_BLOCK = 16      # elements per NVFP4 block scale
 E2M1_MAX = 6.0
 E4M3_MAX = 448.0
 MX_BLOCK = 32         # elements per MXFP8 scale (scales of shape [M, H // 32])
@@ -62,8 +62,8 @@ def _check_fmt(fmt: Format):
 def add_residual(x_bits, r_bits, fmt: Format) -> np.ndarray:
     """h = RN_D(x + r): the residual after its in-place update.
 
-    ``residual``: "Updated in place to x + residual" (``fused_norm_quant``
-    page, parameter list).  The sum is taken in float64; when it is not exact
+    The ``residual`` argument of the op on the ``fused_norm_quant`` page is
+    overwritten with x + residual (parameter list there).  The sum is taken in float64; when it is not exact
     there, rounding twice (to float64, then to D) still gives the correctly
     rounded sum because 53 >= 2p + 2 for p = 8 (bf16) and p = 11 (fp16).
     """
@@ -88,7 +88,8 @@ def gemma_rms_norm(h_bits, w_bits, eps: float, fmt: Format) -> np.ndarray:
 def rms_norm(h_bits, w_bits, eps: float, fmt: Format, gemma: bool) -> np.ndarray:
     """RMSNorm scaled by (1 + w) (Gemma) or by w (plain RMSNorm, the norm of
     the ``rms_norm_static_fp8_quant`` kernels named on the PR conversation
-    page, which "apply gamma * x_normed directly"); fp64, one rounding."""
+    page, which multiply the normed value by the weight itself); fp64, one
+    rounding."""
     _check_fmt(fmt)
     h = bits_to_f64(h_bits, fmt)
     w = bits_to_f64(w_bits, fmt)
@@ -105,9 +106,10 @@ def rms_norm(h_bits, w_bits, eps: float, fmt: Format, gemma: bool) -> np.ndarray
 def quant_fp8_static(y_bits, fmt: Format, scale: float) -> np.ndarray:
     """Static per-tensor FP8: q = E4M3FN_RNE(clamp(fl32(y / scale), +-448)).
 
-    ``scale``: "FP8: the static per-tensor input scale" (``fused_norm_quant``
-    page, parameter list); the division by the scale is the reading of
-    "the same scale arithmetic as" the standalone static FP8 quant.  Values
+    ``scale`` is the static per-tensor input scale of the FP8 mode
+    (``fused_norm_quant`` page, parameter list).  The page says the fused
+    kernel uses the scale math of the standalone static FP8 quant; dividing
+    by the scale is the reading taken here.  Values
     beyond the E4M3FN range saturate to +-448.  Returns uint8 codes, same
     shape as ``y_bits``.
     """
@@ -123,13 +125,14 @@ def quant_fp8_static(y_bits, fmt: Format, scale: float) -> np.ndarray:
 def quant_nvfp4(y_bits, fmt: Format, global_scale: float):
     """NVFP4: E2M1 codes with one E4M3FN scale per 16-element block.
 
-    ``scale``: "NVFP4: the global scale (input_global_scale_inv)"
-    (``fused_norm_quant`` page, parameter list; "NVFP4 global scale inverse"
-    on the ``fused_allreduce_norm_quant`` page) -- read as the multiplier gs
-    that maps a block's decode scale amax/6 into the E4M3 range.  E2M1
-    conversion is round-to-nearest-even with saturation
-    (``cvt.rn.satfinite.e2m1x2.f32`` in ``_cvt_e2m1x2``), and each byte holds
-    the even-index (lo) element in its low nibble ("lo in the low nibble").
+    In NVFP4 mode ``scale`` is the global scale, passed as
+    ``input_global_scale_inv`` (``fused_norm_quant`` page, parameter list;
+    the ``fused_allreduce_norm_quant`` page calls it the inverse of the NVFP4
+    global scale) -- read as the multiplier gs that maps a block's decode
+    scale amax/6 into the E4M3 range.  E2M1 conversion is
+    round-to-nearest-even with saturation (the page's ``_cvt_e2m1x2`` helper
+    uses ``cvt.rn.satfinite.e2m1x2.f32``), and each byte holds the
+    even-index element in its low nibble (that helper's operand order).
 
     Returns ``(q, S)``: q is (M, H/2) uint8 packed codes; S is the (M, H/16)
     uint8 block-scale codes in row-major order (not yet swizzled).
@@ -218,8 +221,8 @@ def block_scale_buffer_shape(M: int, H: int):
 def swizzle_128x4_offset(m, b, H: int):
     """Byte offset of block scale (row m, block b) in the 128x4-tiled layout.
 
-    The pages name the layout ("swizzled 128x4 block scales", ``SWIZZLED_128x4``)
-    without spelling it out; this is the 128x4 tiling used for block-scaled
+    The pages name the layout (``SWIZZLED_128x4``, and the NVFP4 block scales
+    of the op are said to be swizzled 128x4) without spelling it out; this is the 128x4 tiling used for block-scaled
     FP4 GEMM scale operands: 128-row x 4-block tiles of 512 contiguous bytes,
     tiles in row-major order over (m // 128, b // 4), and inside a tile the
     byte for (m, b) at (m % 32) * 16 + ((m % 128) // 32) * 4 + b % 4.
@@ -234,7 +237,8 @@ def swizzle_128x4_offset(m, b, H: int):
 def scatter_block_scales(S, M: int, H: int, out: np.ndarray) -> np.ndarray:
     """Write row-major scales S (M, H/16) into ``out`` (flat uint8 buffer of
     prod(block_scale_buffer_shape) bytes) at their swizzled offsets.  Bytes
-    of rows >= M are left as they were ("rows >= M are left unwritten")."""
+    of rows >= M are left as they were (the op never writes its padding
+    rows)."""
     rows, cols = block_scale_buffer_shape(M, H)
     if out.size != rows * cols:
         raise ValueError("wrong block-scale buffer size")
