@@ -182,3 +182,19 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def test_torch_wrapper_rejects_bad_tensors_before_the_library():
+    """The torch-facing wrapper checks its arguments itself (ValueError) and
+    never reaches the library with host tensors or mismatched shapes."""
+    import torch
+    from fp4_activation_quant_amd import ops
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    w = torch.zeros(128, dtype=torch.bfloat16)
+    s = torch.ones(1, dtype=torch.float32)
+    with pytest.raises(ValueError, match="device"):
+        ops.gemma_add_rms_norm_quant(x, None, w, 1e-6, s, False)
+    with pytest.raises(ValueError, match="device"):
+        ops.add_rms_norm_quant(x, None, w, 1e-6, None, "mxfp8")
+    with pytest.raises(ValueError):
+        ops.quant_mxfp8(x)
