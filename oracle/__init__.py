@@ -13,7 +13,8 @@ one E4M3 scale per 16-element block, stored in the 128x4-tiled scale layout).
 Its variants: a plain (w instead of 1 + w) norm, no quant, and MXFP8 (E4M3
 codes with one E8M0 power-of-two scale per 32-element block, the
 ``allreduce_gemma_rms_norm_mxfp8`` variant on the
-``fused_allreduce_gemma_rms_norm`` page).
+``fused_allreduce_gemma_rms_norm`` page).  ``gemm.py`` is the consumer linear
+that reads the quantized activation (static FP8 or MXFP8) directly.
 The page says the fused kernel computes the same codes as the unfused chain
 (add+norm, then a standalone quant); the oracle is written as that chain.
 
@@ -36,4 +37,7 @@ from .norm_quant import (  # noqa: F401
     mxfp8_block_exponent, quant_mxfp8,
     swizzle_128x4_offset, block_scale_buffer_shape, scatter_block_scales,
     gemma_add_rms_norm_quant, add_rms_norm_quant,
+)
+from .gemm import (  # noqa: F401
+    dequant_fp8_static, dequant_mxfp8, gemm_f64, gemm_fp8_static, gemm_mxfp8,
 )
