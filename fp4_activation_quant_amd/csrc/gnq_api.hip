@@ -185,6 +185,40 @@ nq_status nq_quant_mxfp8(const void *y, int64_t M, int64_t H, int dtype, void *q
   return quant_common(y, nullptr, M, H, dtype, NQ_MODE_MXFP8, q, scales, stream);
 }
 
+static nq_status gemm_common(bool mx, const void *a, const void *sa, const float *a_scale,
+                             const void *b, const void *sb, const float *b_scale, int64_t M,
+                             int64_t N, int64_t K, void *out, void *stream) {
+  if (M < 0 || N < 0 || K <= 0 || M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30) ||
+      K > ((int64_t)1 << 24))
+    return NQ_EINVAL;
+  if (!a || !b || !out) return NQ_EINVAL;
+  if (mx ? (!sa || !sb) : (!a_scale || !b_scale)) return NQ_EINVAL;
+  if (K % kMxBlock != 0) return NQ_EUNSUPPORTED;
+  if (((uintptr_t)a | (uintptr_t)b) % 16 != 0) return NQ_EINVAL;
+  const size_t obytes = (size_t)M * (size_t)N * 2;
+  const size_t abytes = (size_t)M * (size_t)K, bbytes = (size_t)N * (size_t)K;
+  const size_t sab = mx ? (size_t)M * (size_t)(K / kMxBlock) : 4;
+  const size_t sbb = mx ? (size_t)N * (size_t)(K / kMxBlock) : 4;
+  const void *sap = mx ? sa : (const void *)a_scale, *sbp = mx ? sb : (const void *)b_scale;
+  if (overlaps(out, obytes, a, abytes) || overlaps(out, obytes, b, bbytes) ||
+      overlaps(out, obytes, sap, sab) || overlaps(out, obytes, sbp, sbb))
+    return NQ_EINVAL;
+  if (M == 0 || N == 0) return NQ_OK;
+  return status_of(gemm_fp8(mx, a, mx ? sa : nullptr, b, mx ? sb : nullptr, mx ? nullptr : a_scale,
+                            mx ? nullptr : b_scale, M, N, K, out, (hipStream_t)stream));
+}
+
+nq_status nq_gemm_mxfp8(const void *a, const void *a_scales, const void *b, const void *b_scales,
+                        int64_t M, int64_t N, int64_t K, void *out, void *stream) {
+  return gemm_common(true, a, a_scales, nullptr, b, b_scales, nullptr, M, N, K, out, stream);
+}
+
+nq_status nq_gemm_fp8_static(const void *a, const float *a_scale, const void *b,
+                             const float *b_scale, int64_t M, int64_t N, int64_t K, void *out,
+                             void *stream) {
+  return gemm_common(false, a, nullptr, a_scale, b, nullptr, b_scale, M, N, K, out, stream);
+}
+
 nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,
                            void *stream) {
   if (kind < 0 || kind > 8 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in)))

@@ -1,0 +1,195 @@
+// Consumer GEMM of the quantized activation: C[M, N] = dq(A) * dq(B)^T in
+// bf16, A the (M, K) activation codes the op wrote and B the (N, K) weight
+// codes in the same format, both K-contiguous (the pre-quantized input path
+// of the quantized linears on the PR conversation page).  Two formats:
+//  * MXFP8: E4M3 codes with row-major E8M0 scales (rows, K / 32), fed to the
+//    gfx950 block-scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) as they are;
+//  * static FP8: E4M3 codes with one fp32 scale per tensor: the same MFMA at
+//    unit block scale, the product of the two tensor scales applied to the
+//    fp32 accumulator.
+//
+// Operand layout of the MFMA (32 x 32 output, K = 64 per instruction,
+// measured on the chip with a one-wave probe): lane l supplies row (or
+// column) l % 32; its 32 bytes are two 16-byte halves, bytes 0..15 from the
+// first 32-element K block and bytes 16..31 from the second, lanes 0..31
+// holding the low 16 elements of each block and lanes 32..63 the high 16.
+// The scale operand of lane l is the E8M0 code of (row l % 32, block l / 32).
+// Accumulator register v of lane l is C[8 * (v / 4) + 4 * (l / 32) + v % 4]
+// [l % 32].
+//
+// Tiling: 256 threads (4 waves) per workgroup, a 256 x 256 output tile per
+// workgroup and 128 x 128 (4 x 4 MFMA tiles, 256 fp32 accumulators) per
+// wave; K advances 64 bytes per step through two LDS stages of 32 KB (A and
+// B tiles, 64-byte rows whose 16-byte chunks are XOR-swizzled by row to
+// spread LDS banks).  Global loads of step k + 1 are issued before the
+// MFMAs of step k.  Rows beyond M or N are clamped on load and masked on
+// store; a K tail of 32 (K % 64 == 32) loads zeros for the missing block.
+#include "gnq_common.hpp"
+
+namespace gnq {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kGemmThreads = 256;
+constexpr int kGemmTile = 256;                // output rows and columns per workgroup
+constexpr int kGemmWaveTile = 128;            // per wave
+constexpr int kGemmK = 64;                    // K bytes per step
+constexpr int kGemmOperandBytes = kGemmTile * kGemmK;     // 16 KB per operand per stage
+
+__device__ __forceinline__ int gemm_lds_off(int row, int chunk) {
+  return row * kGemmK + ((chunk ^ ((row >> 1) & 3)) << 4);
+}
+
+__device__ __forceinline__ i32x8 gemm_frag(const uint8_t *base, int row, int h) {
+  const u32x4 lo = *reinterpret_cast<const u32x4 *>(base + gemm_lds_off(row, h));
+  const u32x4 hi = *reinterpret_cast<const u32x4 *>(base + gemm_lds_off(row, 2 + h));
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <bool MX>
+__global__ void __launch_bounds__(kGemmThreads)
+gemm_fp8_tn(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
+            const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
+            const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N, int K,
+            uint16_t *__restrict__ C, int tiles_m, int tiles, int unit_scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kGemmOperandBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  // Workgroup b runs on XCD b % 8; give each XCD a contiguous range of
+  // tiles (consecutive tiles share a column of B) when the grid divides.
+  int b = blockIdx.x;
+  if ((tiles & 7) == 0) b = (b & 7) * (tiles >> 3) + (b >> 3);
+  const int tm = b % tiles_m, tn = b / tiles_m;
+  const int m0 = tm * kGemmTile, n0 = tn * kGemmTile;
+  const int wm = (wave >> 1) * kGemmWaveTile, wn = (wave & 1) * kGemmWaveTile;
+  const int ksteps = (K + kGemmK - 1) / kGemmK;
+  const int kblocks = K / 32;
+
+  // Global -> LDS staging: each thread moves 16-byte chunk c = tid % 4 of
+  // rows tid / 4 + 64 j (j = 0..3) of both operand tiles.
+  const int c = tid & 3;
+  const uint8_t *a_src[4], *b_src[4];
+  int st_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (tid >> 2) + 64 * j;
+    const int ar = min(m0 + row, M - 1), br = min(n0 + row, N - 1);
+    a_src[j] = A + (size_t)ar * (size_t)K + c * 16;
+    b_src[j] = B + (size_t)br * (size_t)K + c * 16;
+    st_off[j] = gemm_lds_off(row, c);
+  }
+  // Scale rows of this lane's four A and four B MFMA tiles.
+  size_t sa_row[4], sb_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sa_row[i] = (size_t)min(m0 + wm + 32 * i + r, M - 1) * (size_t)kblocks;
+    sb_row[i] = (size_t)min(n0 + wn + 32 * i + r, N - 1) * (size_t)kblocks;
+  }
+
+  u32x4 a_st[4], b_st[4];
+  int sa_cur[4], sb_cur[4], sa_nxt[4], sb_nxt[4];
+  auto gload = [&](int ks) {
+    const int kb = ks * kGemmK;
+    const bool in = kb + c * 16 < K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a_st[j] = in ? *reinterpret_cast<const u32x4 *>(a_src[j] + kb) : u32x4{0, 0, 0, 0};
+      b_st[j] = in ? *reinterpret_cast<const u32x4 *>(b_src[j] + kb) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto sload = [&](int ks, int (&sa)[4], int (&sb)[4]) {
+    const int blk = 2 * ks + h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (MX && blk < kblocks) {
+        sa[i] = SA[sa_row[i] + blk];
+        sb[i] = SB[sb_row[i] + blk];
+      } else {
+        sa[i] = unit_scale;
+        sb[i] = unit_scale;
+      }
+    }
+  };
+  auto stage_store = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4 *>(&lds[s][st_off[j]]) = a_st[j];
+      *reinterpret_cast<u32x4 *>(&lds[s][kGemmOperandBytes + st_off[j]]) = b_st[j];
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
+
+  gload(0);
+  sload(0, sa_cur, sb_cur);
+  stage_store(0);
+  __syncthreads();
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int cur = ks & 1;
+    const bool more = ks + 1 < ksteps;
+    if (more) {
+      gload(ks + 1);
+      sload(ks + 1, sa_nxt, sb_nxt);
+    }
+    const uint8_t *a_lds = lds[cur];
+    const uint8_t *b_lds = lds[cur] + kGemmOperandBytes;
+    i32x8 bf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = gemm_frag(b_lds, wn + 32 * j + r, h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const i32x8 af = gemm_frag(a_lds, wm + 32 * i + r, h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
+                                                                    sa_cur[i], 0, sb_cur[j]);
+    }
+    if (more) {
+      stage_store(cur ^ 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa_cur[i] = sa_nxt[i];
+        sb_cur[i] = sb_nxt[i];
+      }
+    }
+    __syncthreads();
+  }
+
+  const float s = MX ? 1.0f : (*a_scale) * (*b_scale);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn + 32 * j + r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row < M && col < N)
+          C[(size_t)row * (size_t)N + col] = (uint16_t)(Bf16::pack(acc[i][j][v] * s, 0.0f) & 0xffffu);
+      }
+    }
+}
+
+hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,
+                    const float *a_scale, const float *b_scale, int64_t M, int64_t N, int64_t K,
+                    void *c, hipStream_t st) {
+  const int tiles_m = (int)((M + kGemmTile - 1) / kGemmTile);
+  const int tiles_n = (int)((N + kGemmTile - 1) / kGemmTile);
+  const int tiles = tiles_m * tiles_n;
+  if (mx)
+    hipLaunchKernelGGL((gemm_fp8_tn<true>), dim3(tiles), dim3(kGemmThreads), 0, st, (const uint8_t *)a,
+                       (const uint8_t *)sa, (const uint8_t *)b, (const uint8_t *)sb, a_scale, b_scale,
+                       (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m, tiles, 127);
+  else
+    hipLaunchKernelGGL((gemm_fp8_tn<false>), dim3(tiles), dim3(kGemmThreads), 0, st, (const uint8_t *)a,
+                       (const uint8_t *)sa, (const uint8_t *)b, (const uint8_t *)sb, a_scale, b_scale,
+                       (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m, tiles, 127);
+  return hipGetLastError();
+}
+
+}  // namespace gnq

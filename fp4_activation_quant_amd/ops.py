@@ -220,5 +220,48 @@ def quant_mxfp8(y, q=None, scales=None):
     return q, scales
 
 
+def _validate_codes(q, name):
+    _require(q.is_cuda and q.dim() == 2 and q.is_contiguous() and q.element_size() == 1,
+             f"{name}: contiguous 2-D one-byte device tensor")
+
+
+def gemm_mxfp8(a, a_scales, b, b_scales, out=None):
+    """The consumer linear on an MXFP8 activation: out (M, N) bf16 =
+    dq(a) @ dq(b)^T, with a (M, K) / b (N, K) E4M3 codes and (rows, K // 32)
+    E8M0 scales, all row-major (the MXFP8 mode's outputs, and a weight in the
+    same format)."""
+    _validate_codes(a, "a")
+    _validate_codes(b, "b")
+    M, K = a.shape
+    N = b.shape[0]
+    _require(b.shape[1] == K and K % 32 == 0, "b: (N, K) with the same K; K % 32 == 0")
+    _require(a_scales.shape == (M, K // 32) and b_scales.shape == (N, K // 32),
+             "scales: (rows, K // 32)")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    with torch.cuda.device(a.device):
+        st = _lib.nq_gemm_mxfp8(a.data_ptr(), a_scales.data_ptr(), b.data_ptr(), b_scales.data_ptr(),
+                                M, N, K, out.data_ptr(), _stream(a.device))
+    _check(st, "nq_gemm_mxfp8")
+    return out
+
+
+def gemm_fp8_static(a, a_scale, b, b_scale, out=None):
+    """The consumer linear on a static-FP8 activation: out (M, N) bf16 =
+    (a * a_scale) @ (b * b_scale)^T, scales one float32 each on the device."""
+    _validate_codes(a, "a")
+    _validate_codes(b, "b")
+    M, K = a.shape
+    N = b.shape[0]
+    _require(b.shape[1] == K and K % 32 == 0, "b: (N, K) with the same K; K % 32 == 0")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    with torch.cuda.device(a.device):
+        st = _lib.nq_gemm_fp8_static(a.data_ptr(), a_scale.data_ptr(), b.data_ptr(), b_scale.data_ptr(),
+                                     M, N, K, out.data_ptr(), _stream(a.device))
+    _check(st, "nq_gemm_fp8_static")
+    return out
+
+
 def block_scale_bytes(M, H):
     return _lib.nq_block_scale_bytes(M, H)

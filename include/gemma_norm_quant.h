@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define NQ_ABI_VERSION 3
+#define NQ_ABI_VERSION 4
 
 typedef enum {
   NQ_OK = 0,
@@ -166,6 +166,37 @@ nq_status nq_quant_nvfp4(const void *y, const float *global_scale, int64_t M, in
  */
 nq_status nq_quant_mxfp8(const void *y, int64_t M, int64_t H, int dtype, void *q, void *scales,
                          void *stream);
+
+/*
+ * nq_gemm_mxfp8 / nq_gemm_fp8_static -- the consumer linear of the quantized
+ * activation: out[M, N] = dq(a) * dq(b)^T, rounded to bf16, where a is the
+ * (M, K) activation code matrix this library writes and b the (N, K) weight
+ * codes in the same format, both row-major (K-contiguous).  This is the
+ * pre-quantized input path of the quantized linears on the PR conversation
+ * page: the linear takes the activation already quantized instead of
+ * quantizing it again.
+ *
+ *   nq_gemm_mxfp8: a, b = E4M3FN codes; a_scales (M, K/32), b_scales
+ *     (N, K/32) = E8M0 codes, row-major (the MXFP8 mode's layout);
+ *     dq(x)[r, k] = E4M3(x[r, k]) * 2^(scale[r, k/32] - 127).
+ *   nq_gemm_fp8_static: a, b = E4M3FN codes; a_scale, b_scale = DEVICE
+ *     pointers to one fp32 each (the static FP8 mode's scale, and the
+ *     weight's); dq(x) = E4M3(x) * scale.
+ *   out: (M, N) bf16, row-major, round to nearest even of the fp32
+ *     accumulation; must not overlap any input.
+ *   M, N >= 0 (either 0: NQ_OK, nothing launched); K > 0 with K % 32 == 0
+ *     (NQ_EUNSUPPORTED otherwise); a and b 16-byte aligned (NQ_EINVAL
+ *     otherwise).
+ *
+ * Accumulation: the block-scaled MFMA of gfx950 in fp32 accumulators; the
+ * MFMA's internal sum of its 64 products is not an IEEE fp32 sum (measured
+ * relative error up to ~2^-12 of sum |a b| per instruction).
+ */
+nq_status nq_gemm_mxfp8(const void *a, const void *a_scales, const void *b, const void *b_scales,
+                        int64_t M, int64_t N, int64_t K, void *out, void *stream);
+nq_status nq_gemm_fp8_static(const void *a, const float *a_scale, const void *b,
+                             const float *b_scale, int64_t M, int64_t N, int64_t K, void *out,
+                             void *stream);
 
 /* Size in bytes of the NVFP4 block-scale buffer:
  * round_up(M, 128) * round_up(H / 16, 4) (the wrapper's allocation on the

@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert _lib.nq_abi_version() == 3
+    assert _lib.nq_abi_version() == 4
     assert _lib.nq_status_string(0) == "ok"
     for s in range(0, 6):
         assert isinstance(_lib.nq_status_string(s), str)
@@ -198,3 +198,26 @@ def test_torch_wrapper_rejects_bad_tensors_before_the_library():
         ops.add_rms_norm_quant(x, None, w, 1e-6, None, "mxfp8")
     with pytest.raises(ValueError):
         ops.quant_mxfp8(x)
+
+
+@pytest.mark.parametrize("mx", [True, False])
+@pytest.mark.parametrize("over,want", [
+    (dict(a=0), _lib.NQ_EINVAL),
+    (dict(b=0), _lib.NQ_EINVAL),
+    (dict(out=0), _lib.NQ_EINVAL),
+    (dict(sa=0), _lib.NQ_EINVAL),
+    (dict(sb=0), _lib.NQ_EINVAL),
+    (dict(K=0), _lib.NQ_EINVAL),
+    (dict(M=-1), _lib.NQ_EINVAL),
+    (dict(K=48), _lib.NQ_EUNSUPPORTED),
+    (dict(a=X + 8), _lib.NQ_EINVAL),                  # unaligned codes
+    (dict(out=X + 64), _lib.NQ_EINVAL),               # out overlaps a
+    (dict(out=Q + 4096), _lib.NQ_EINVAL),             # out overlaps b
+    (dict(M=0), _lib.NQ_OK),
+    (dict(N=0), _lib.NQ_OK),
+])
+def test_gemm_validation(mx, over, want):
+    a = dict(a=X, sa=S, b=Q, sb=B, M=4, N=8, K=4096, out=Y)
+    a.update(over)
+    fn = _lib.nq_gemm_mxfp8 if mx else _lib.nq_gemm_fp8_static
+    assert fn(a["a"], a["sa"], a["b"], a["sb"], a["M"], a["N"], a["K"], a["out"], 0) == want

@@ -1,0 +1,163 @@
+"""GPU parity of the consumer GEMM (nq_gemm_mxfp8, nq_gemm_fp8_static)
+against the oracle, through the C ABI.
+
+Bars:
+  * exact cases -- operands whose products and partial sums are exact in any
+    accumulator (a few significant bits, moderate scales): the bf16 output is
+    bit-identical to the oracle's rounding of the exact sum.  These pin the
+    operand layout, the K pairing and the per-block scales;
+  * general random codes and scales: |out - exact| <= 2^-8 |exact| (bf16
+    rounding of the accumulator) + 2^-10 * sum_k |a_k b_k| (the block-scaled
+    MFMA sums its 64 products with a relative error measured up to ~2^-12.8
+    of their absolute sum; fp32 accumulation across steps adds far less).
+Output guard bytes after the (M, N) result must keep their sentinel.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_activation_quant_amd import _lib, ops
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.lib()
+
+
+# E4M3 codes of small exact values: 0, +-0.5, +-1, +-1.5, +-2, +-3, +-4
+_SMALL = np.array([0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48,
+                   0xB0, 0xB8, 0xBC, 0xC0, 0xC4, 0xC8], np.uint8)
+
+
+def _finite_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape, dtype=np.int64)
+    return np.where((c & 0x7F) == 0x7F, c - 1, c).astype(np.uint8)
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _run(mx, aq, as_, bq, bs, M, N):
+    """GPU result as bf16 bits, with a guarded output buffer."""
+    out = torch.full((M * N * 2 + P.GUARD,), P.SENTINEL, dtype=torch.uint8, device="cuda")
+    o = out[:M * N * 2].view(torch.bfloat16).view(M, N)
+    if mx:
+        ops.gemm_mxfp8(_dev(aq), _dev(as_), _dev(bq), _dev(bs), out=o)
+    else:
+        ops.gemm_fp8_static(_dev(aq), torch.tensor([as_], dtype=torch.float32, device="cuda"),
+                            _dev(bq), torch.tensor([bs], dtype=torch.float32, device="cuda"), out=o)
+    torch.cuda.synchronize()
+    assert bool((out[M * N * 2:] == P.SENTINEL).all()), "wrote past the output"
+    return P.bits16(o)
+
+
+SHAPES = [(1, 8, 64), (5, 300, 96), (256, 256, 128), (300, 520, 1056), (513, 257, 2048),
+          (64, 1024, 4096), (1000, 40, 160)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_mxfp8_gemm_exact_cases(M, N, K):
+    print(f"gemm mx exact M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M * 7 + N * 11 + K)
+    aq = _SMALL[rng.integers(0, len(_SMALL), size=(M, K))]
+    bq = _SMALL[rng.integers(0, len(_SMALL), size=(N, K))]
+    # block scales 2^-1 .. 2^1: every product is a multiple of 2^-4 below 64,
+    # so all sums up to K = 4096 stay within 22 bits (exact in fp32)
+    as_ = rng.integers(126, 129, size=(M, K // 32)).astype(np.uint8)
+    bs = rng.integers(126, 129, size=(N, K // 32)).astype(np.uint8)
+    got = _run(True, aq, as_, bq, bs, M, N)
+    _, want = O.gemm_mxfp8(aq, as_, bq, bs)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, (bad[0][:5], bad[1][:5], got[bad][:5], want[bad][:5])
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES[:5])
+def test_fp8_static_gemm_exact_cases(M, N, K):
+    print(f"gemm static exact M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M * 5 + N * 3 + K)
+    aq = _SMALL[rng.integers(0, len(_SMALL), size=(M, K))]
+    bq = _SMALL[rng.integers(0, len(_SMALL), size=(N, K))]
+    got = _run(False, aq, 0.25, bq, 2.0, M, N)
+    _, want = O.gemm_fp8_static(aq, 0.25, bq, 2.0)
+    assert np.array_equal(got, want)
+
+
+def _tolerance_check(got_bits, exact, mag):
+    got = O.bits_to_f64(got_bits, O.BF16)
+    tol = 2.0 ** -8 * np.abs(exact) + 2.0 ** -10 * mag + 1e-300
+    err = np.abs(got - exact)
+    worst = float(np.max(err / tol))
+    print(f"  worst err / tol = {worst:.3f}", flush=True)
+    assert worst <= 1.0
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 300, 512), (256, 512, 4096), (129, 130, 1056)])
+def test_mxfp8_gemm_random(M, N, K):
+    print(f"gemm mx random M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M + N + K)
+    aq, bq = _finite_codes(rng, (M, K)), _finite_codes(rng, (N, K))
+    as_ = rng.integers(110, 140, size=(M, K // 32)).astype(np.uint8)
+    bs = rng.integers(110, 140, size=(N, K // 32)).astype(np.uint8)
+    got = _run(True, aq, as_, bq, bs, M, N)
+    exact, _ = O.gemm_mxfp8(aq, as_, bq, bs)
+    mag = O.gemm_f64(np.abs(O.dequant_mxfp8(aq, as_)), np.abs(O.dequant_mxfp8(bq, bs)))
+    _tolerance_check(got, exact, mag)
+
+
+def test_fp8_static_gemm_random():
+    rng = np.random.default_rng(17)
+    M, N, K = 200, 300, 2048
+    aq, bq = _finite_codes(rng, (M, K)), _finite_codes(rng, (N, K))
+    got = _run(False, aq, 0.0137, bq, 0.0021, M, N)
+    exact, _ = O.gemm_fp8_static(aq, 0.0137, bq, 0.0021)
+    mag = O.gemm_f64(np.abs(O.dequant_fp8_static(aq, 0.0137)), np.abs(O.dequant_fp8_static(bq, 0.0021)))
+    _tolerance_check(got, exact, mag)
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "fp8"])
+def test_gemm_consumes_the_ops_quantized_output(mode):
+    """The op's codes and scales go straight into the consumer linear; the
+    result matches the oracle GEMM of those same codes."""
+    print(f"gemm consumer {mode}", flush=True)
+    g = torch.Generator().manual_seed(23)
+    M, H, N = 300, 4096, 384
+    x = torch.randn(M, H, generator=g).to(torch.bfloat16).cuda()
+    r = torch.randn(M, H, generator=g).to(torch.bfloat16).cuda()
+    w = (torch.randn(H, generator=g) * 0.1).to(torch.bfloat16).cuda()
+    rng = np.random.default_rng(3)
+    wq = _finite_codes(rng, (N, H))
+    wq = np.where((wq & 0x78) > 0x50, wq & 0x87, wq).astype(np.uint8)   # keep |w| <= 16
+    if mode == "mxfp8":
+        ws = rng.integers(118, 124, size=(N, H // 32)).astype(np.uint8)
+        q, s, _ = ops.add_rms_norm_quant(x, r, w, 1e-6, None, "mxfp8")
+        out = ops.gemm_mxfp8(q, s, _dev(wq), _dev(ws))
+        aq, as_ = q.view(torch.uint8).cpu().numpy(), s.view(torch.uint8).cpu().numpy()
+        exact, _ = O.gemm_mxfp8(aq, as_, wq, ws)
+        mag = O.gemm_f64(np.abs(O.dequant_mxfp8(aq, as_)), np.abs(O.dequant_mxfp8(wq, ws)))
+    else:
+        sa = torch.tensor([0.02], dtype=torch.float32, device="cuda")
+        sw = torch.tensor([0.004], dtype=torch.float32, device="cuda")
+        q, _, _ = ops.gemma_add_rms_norm_quant(x, r, w, 1e-6, sa, False)
+        out = ops.gemm_fp8_static(q, sa, _dev(wq), sw)
+        aq = q.view(torch.uint8).cpu().numpy()
+        exact, _ = O.gemm_fp8_static(aq, 0.02, wq, 0.004)
+        mag = O.gemm_f64(np.abs(O.dequant_fp8_static(aq, 0.02)), np.abs(O.dequant_fp8_static(wq, 0.004)))
+    torch.cuda.synchronize()
+    _tolerance_check(P.bits16(out), exact, mag)
+
+
+def test_gemm_empty_writes_nothing():
+    buf = torch.full((1 << 16,), P.SENTINEL, dtype=torch.uint8, device="cuda")
+    p = buf.data_ptr()
+    st = _lib.nq_gemm_mxfp8(p, p + 8192, p + 16384, p + 24576, 0, 64, 64, p + 32768, 0)
+    st2 = _lib.nq_gemm_mxfp8(p, p + 8192, p + 16384, p + 24576, 64, 0, 64, p + 32768, 0)
+    torch.cuda.synchronize()
+    assert st == _lib.NQ_OK and st2 == _lib.NQ_OK and bool((buf == P.SENTINEL).all())
