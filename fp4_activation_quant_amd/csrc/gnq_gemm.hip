@@ -175,20 +175,170 @@ gemm_fp8_tn(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     }
 }
 
+// Direct-to-LDS pipeline (K % 128 == 0): global_load_lds_dwordx4 moves each
+// wave's 1 KB segments straight into LDS (lane l fills bytes 16 l .. 16 l +
+// 15 of the segment, so lane l fetches the global chunk that the swizzled
+// layout puts there); kGemmStages stages keep kGemmStages - 1 steps in
+// flight with no register staging.  For MXFP8 each stage also receives, by
+// 4-byte DMA, the four E8M0 codes of every row covering this step and the
+// next (blocks 4 (k / 2) .. 4 (k / 2) + 3), so the scales travel with the
+// data and the MFMA reads them from LDS.  One barrier per step: wait for this
+// step's own loads, barrier, then refill the stage every wave finished
+// reading in the previous step.
+constexpr int kGemmStages = 4;
+constexpr int kGemmScaleBytes = kGemmTile * 4;                       // per operand per stage
+constexpr int kGemmStageBytes = 2 * kGemmOperandBytes + 2 * kGemmScaleBytes;
+constexpr int kGemmDmaLds = kGemmStages * kGemmStageBytes;           // 136 KB
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <bool MX>
+__global__ void __launch_bounds__(kGemmThreads)
+gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
+                const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
+                const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N,
+                int K, uint16_t *__restrict__ C, int tiles_m, int tiles, int unit_scale) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  int b = blockIdx.x;
+  if ((tiles & 7) == 0) b = (b & 7) * (tiles >> 3) + (b >> 3);
+  const int tm = b % tiles_m, tn = b / tiles_m;
+  const int m0 = tm * kGemmTile, n0 = tn * kGemmTile;
+  const int wm = (wave >> 1) * kGemmWaveTile, wn = (wave & 1) * kGemmWaveTile;
+  const int ksteps = K / kGemmK;
+  const int kblocks = K / 32;
+
+  // Waves 0-1 fetch A, waves 2-3 fetch B: segment seg = 8 (wave % 2) + j of
+  // the operand tile holds rows 16 seg .. 16 seg + 15; lane l's slot is row
+  // 16 seg + l / 4, position l % 4, i.e. chunk (l % 4) ^ ((l / 8) % 4).
+  const bool fetch_b = wave >= 2;
+  const uint8_t *src = fetch_b ? B : A;
+  const int lim = fetch_b ? N - 1 : M - 1, base_row = fetch_b ? n0 : m0;
+  const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
+  const uint8_t *seg_src[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int seg = 8 * (wave & 1) + j;
+    seg_src[j] = src + (size_t)min(base_row + 16 * seg + (lane >> 2), lim) * (size_t)K + chunk * 16;
+  }
+  // Scale rows 64 (2 (wave % 2) + t) + lane of the operand, t = 0, 1.
+  const uint8_t *sc_src[2] = {nullptr, nullptr};
+  if (MX) {
+    const uint8_t *ssrc = fetch_b ? SB : SA;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      sc_src[t] = ssrc + (size_t)min(base_row + 64 * (2 * (wave & 1) + t) + lane, lim) * (size_t)kblocks;
+  }
+  auto issue = [&](int ks) {
+    uint8_t *st = smem + (ks % kGemmStages) * kGemmStageBytes;
+    uint8_t *dst = st + (fetch_b ? kGemmOperandBytes : 0) + (wave & 1) * 8 * 1024;
+    const int kb = ks * kGemmK;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) __builtin_amdgcn_global_load_lds(seg_src[j] + kb, dst + j * 1024, 16, 0, 0);
+    if (MX) {
+      uint8_t *sdst = st + 2 * kGemmOperandBytes + (fetch_b ? kGemmScaleBytes : 0) + (wave & 1) * 512;
+      const int so = 4 * (ks >> 1);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) __builtin_amdgcn_global_load_lds(sc_src[t] + so, sdst + t * 256, 4, 0, 0);
+    }
+  };
+  constexpr int kPer = MX ? 10 : 8;     // DMA instructions per wave per step
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
+
+#pragma unroll
+  for (int p = 0; p < kGemmStages - 1; ++p)
+    if (p < ksteps) issue(p);
+  for (int ks = 0; ks < ksteps; ++ks) {
+    if (ksteps - 1 - ks >= kGemmStages - 2) wait_vmcnt<kPer * (kGemmStages - 2)>();
+    else wait_vmcnt<0>();
+    // A plain barrier: the wait above already covers this step's loads of
+    // this wave, and every LDS read of the previous step has been consumed
+    // by its MFMAs.  (A fenced barrier would drain all DMA in flight.)
+    asm volatile("s_barrier" ::: "memory");
+    if (ks + kGemmStages - 1 < ksteps) issue(ks + kGemmStages - 1);
+    const uint8_t *st = smem + (ks % kGemmStages) * kGemmStageBytes;
+    const uint8_t *a_lds = st, *b_lds = st + kGemmOperandBytes;
+    const uint8_t *sa_lds = st + 2 * kGemmOperandBytes + (ks & 1) * 2 + h;
+    const uint8_t *sb_lds = sa_lds + kGemmScaleBytes;
+    int sa[4], sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = MX ? (int)sa_lds[(wm + 32 * i + r) * 4] : unit_scale;
+      sb[i] = MX ? (int)sb_lds[(wn + 32 * i + r) * 4] : unit_scale;
+    }
+    i32x8 bf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = gemm_frag(b_lds, wn + 32 * j + r, h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const i32x8 af = gemm_frag(a_lds, wm + 32 * i + r, h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
+                                                                    sa[i], 0, sb[j]);
+    }
+  }
+
+  const float s = MX ? 1.0f : (*a_scale) * (*b_scale);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn + 32 * j + r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row < M && col < N)
+          C[(size_t)row * (size_t)N + col] = (uint16_t)(Bf16::pack(acc[i][j][v] * s, 0.0f) & 0xffffu);
+      }
+    }
+}
+
 hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,
                     const float *a_scale, const float *b_scale, int64_t M, int64_t N, int64_t K,
                     void *c, hipStream_t st) {
   const int tiles_m = (int)((M + kGemmTile - 1) / kGemmTile);
   const int tiles_n = (int)((N + kGemmTile - 1) / kGemmTile);
   const int tiles = tiles_m * tiles_n;
+  const uint8_t *A = (const uint8_t *)a, *B = (const uint8_t *)b;
+  const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
+  const bool dma = K % (2 * kGemmK) == 0 && (!mx || ((uintptr_t)sa % 4 == 0 && (uintptr_t)sb % 4 == 0));
+  if (dma) {
+    static bool attr_set[2] = {false, false};
+    if (!attr_set[mx]) {
+      hipError_t e = mx ? hipFuncSetAttribute((const void *)gemm_fp8_tn_dma<true>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmDmaLds)
+                        : hipFuncSetAttribute((const void *)gemm_fp8_tn_dma<false>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmDmaLds);
+      if (e != hipSuccess) return e;
+      attr_set[mx] = true;
+    }
+    if (mx)
+      hipLaunchKernelGGL((gemm_fp8_tn_dma<true>), dim3(tiles), dim3(kGemmThreads), kGemmDmaLds, st, A,
+                         SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m,
+                         tiles, 127);
+    else
+      hipLaunchKernelGGL((gemm_fp8_tn_dma<false>), dim3(tiles), dim3(kGemmThreads), kGemmDmaLds, st, A,
+                         SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m,
+                         tiles, 127);
+    return hipGetLastError();
+  }
   if (mx)
-    hipLaunchKernelGGL((gemm_fp8_tn<true>), dim3(tiles), dim3(kGemmThreads), 0, st, (const uint8_t *)a,
-                       (const uint8_t *)sa, (const uint8_t *)b, (const uint8_t *)sb, a_scale, b_scale,
-                       (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m, tiles, 127);
+    hipLaunchKernelGGL((gemm_fp8_tn<true>), dim3(tiles), dim3(kGemmThreads), 0, st, A, SA, B, SB,
+                       a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m, tiles, 127);
   else
-    hipLaunchKernelGGL((gemm_fp8_tn<false>), dim3(tiles), dim3(kGemmThreads), 0, st, (const uint8_t *)a,
-                       (const uint8_t *)sa, (const uint8_t *)b, (const uint8_t *)sb, a_scale, b_scale,
-                       (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m, tiles, 127);
+    hipLaunchKernelGGL((gemm_fp8_tn<false>), dim3(tiles), dim3(kGemmThreads), 0, st, A, SA, B, SB,
+                       a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m, tiles, 127);
   return hipGetLastError();
 }
 
