@@ -74,7 +74,9 @@ def build(verbose=True, jobs=None) -> str:
                 if verbose and out.strip():
                     print(out)
         tmp_lib = LIB + ".tmp"
-        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib])
+        # -z defs: an unresolved symbol (e.g. a kernel template never
+        # instantiated) fails the link instead of the first call.
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp_lib])
         os.replace(tmp_lib, LIB)
     if verbose:
         print(f"built {LIB}", flush=True)

@@ -19,9 +19,9 @@
 //
 // Tiling: 256 threads (4 waves) per workgroup, a 256 x 256 output tile per
 // workgroup and 128 x 128 (4 x 4 MFMA tiles, 256 fp32 accumulators) per
-// wave; K advances 64 bytes per step through two LDS stages of 32 KB (A and
-// B tiles, 64-byte rows whose 16-byte chunks are XOR-swizzled by row to
-// spread LDS banks).  Global loads of step k + 1 are issued before the
+// wave; K advances 64 bytes per step through LDS stages (A and B tiles,
+// 64-byte rows whose 16-byte chunks are XOR-swizzled by row to spread LDS
+// banks).  Global loads of step k + 1 are issued before the
 // MFMAs of step k.  Rows beyond M or N are clamped on load and masked on
 // store; a K tail of 32 (K % 64 == 32) loads zeros for the missing block.
 #include "gnq_common.hpp"
@@ -37,8 +37,32 @@ constexpr int kGemmWaveTile = 128;            // per wave
 constexpr int kGemmK = 64;                    // K bytes per step
 constexpr int kGemmOperandBytes = kGemmTile * kGemmK;     // 16 KB per operand per stage
 
+// Chunk swizzle of a 64-byte LDS row: chunk c of row r sits at position
+// c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) % 4.  The 16-byte reads of 8 and of
+// 16 consecutive rows at one chunk then cover 128 and 256 distinct bytes
+// modulo 256 (no bank conflict with 32 or 64 four-byte banks; the plain
+// ((r >> 1) % 4) swizzle left a 2-way conflict, measured as 44% of LDS
+// cycles).
+__device__ __forceinline__ int gemm_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
 __device__ __forceinline__ int gemm_lds_off(int row, int chunk) {
-  return row * kGemmK + ((chunk ^ ((row >> 1) & 3)) << 4);
+  return row * kGemmK + ((chunk ^ gemm_swz(row)) << 4);
+}
+
+// Output tile of workgroup b: tiles are taken in groups of up to 16 tile
+// rows, column by column inside a group, so the workgroups resident at one
+// time (one per CU) cover about a 16 x 16 block of tiles: 16 row tiles of A
+// and 16 column tiles of B in flight (at K = 8192, 64 MB, inside the 256 MB
+// Infinity Cache) instead of all of A against two columns of B.
+constexpr int kGemmGroupRows = 16;
+
+__device__ __forceinline__ void gemm_tile_of_block(int b, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int per_group = kGemmGroupRows * tiles_n;
+  const int first = (b / per_group) * kGemmGroupRows;
+  const int rows = min(tiles_m - first, kGemmGroupRows);
+  const int p = b % per_group;
+  tm = first + p % rows;
+  tn = p / rows;
 }
 
 __device__ __forceinline__ i32x8 gemm_frag(const uint8_t *base, int row, int h) {
@@ -56,11 +80,8 @@ gemm_fp8_tn(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kGemmOperandBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, h = lane >> 5;
-  // Workgroup b runs on XCD b % 8; give each XCD a contiguous range of
-  // tiles (consecutive tiles share a column of B) when the grid divides.
-  int b = blockIdx.x;
-  if ((tiles & 7) == 0) b = (b & 7) * (tiles >> 3) + (b >> 3);
-  const int tm = b % tiles_m, tn = b / tiles_m;
+  int tm, tn;
+  gemm_tile_of_block(blockIdx.x, tiles_m, tiles / tiles_m, tm, tn);
   const int m0 = tm * kGemmTile, n0 = tn * kGemmTile;
   const int wm = (wave >> 1) * kGemmWaveTile, wn = (wave & 1) * kGemmWaveTile;
   const int ksteps = (K + kGemmK - 1) / kGemmK;
@@ -190,70 +211,88 @@ constexpr int kGemmScaleBytes = kGemmTile * 4;                       // per oper
 constexpr int kGemmStageBytes = 2 * kGemmOperandBytes + 2 * kGemmScaleBytes;
 constexpr int kGemmDmaLds = kGemmStages * kGemmStageBytes;           // 136 KB
 
+// Global -> LDS DMA of 16 or 4 bytes per lane (lane l writes lds + size * l).
+__device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const uint8_t *g, uint8_t *lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <bool MX>
-__global__ void __launch_bounds__(kGemmThreads)
+// NW waves per workgroup, each owning TM x TN MFMA tiles (32 x 32) of the
+// 256 x 256 workgroup tile; the 32 one-KB data segments and 8 scale segments
+// of a step are split evenly over the waves.
+template <bool MX, int NW, int TM, int TN>
+__global__ void __launch_bounds__(64 * NW)
 gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
                 const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
                 const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N,
                 int K, uint16_t *__restrict__ C, int tiles_m, int tiles, int unit_scale) {
+  static_assert((8 / TM) * (8 / TN) == NW, "waves must tile the 256 x 256 workgroup tile");
+  constexpr int kSegs = 32 / NW;        // data segments per wave per step
+  constexpr int kScaleSegs = 8 / NW;    // scale segments per wave per step
+  constexpr int kWavesN = 8 / TN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, h = lane >> 5;
-  int b = blockIdx.x;
-  if ((tiles & 7) == 0) b = (b & 7) * (tiles >> 3) + (b >> 3);
-  const int tm = b % tiles_m, tn = b / tiles_m;
+  int tm, tn;
+  gemm_tile_of_block(blockIdx.x, tiles_m, tiles / tiles_m, tm, tn);
   const int m0 = tm * kGemmTile, n0 = tn * kGemmTile;
-  const int wm = (wave >> 1) * kGemmWaveTile, wn = (wave & 1) * kGemmWaveTile;
+  const int wm = (wave / kWavesN) * 32 * TM, wn = (wave % kWavesN) * 32 * TN;
   const int ksteps = K / kGemmK;
   const int kblocks = K / 32;
 
-  // Waves 0-1 fetch A, waves 2-3 fetch B: segment seg = 8 (wave % 2) + j of
-  // the operand tile holds rows 16 seg .. 16 seg + 15; lane l's slot is row
-  // 16 seg + l / 4, position l % 4, i.e. chunk (l % 4) ^ ((l / 8) % 4).
-  const bool fetch_b = wave >= 2;
+  // Segment g = kSegs * wave + j of the step (g < 16: A, else B) holds rows
+  // 16 (g % 16) .. + 15 of its operand tile; lane l's slot is row
+  // 16 (g % 16) + l / 4, position l % 4, i.e. chunk (l % 4) ^ f(row).
+  const bool fetch_b = kSegs * wave >= 16;
   const uint8_t *src = fetch_b ? B : A;
   const int lim = fetch_b ? N - 1 : M - 1, base_row = fetch_b ? n0 : m0;
-  const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
-  const uint8_t *seg_src[8];
+  const int seg0 = (kSegs * wave) & 15;
+  const uint8_t *seg_src[kSegs];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int seg = 8 * (wave & 1) + j;
-    seg_src[j] = src + (size_t)min(base_row + 16 * seg + (lane >> 2), lim) * (size_t)K + chunk * 16;
+  for (int j = 0; j < kSegs; ++j) {
+    const int row = 16 * (seg0 + j) + (lane >> 2);
+    const int chunk = (lane & 3) ^ gemm_swz(row);
+    seg_src[j] = src + (size_t)min(base_row + row, lim) * (size_t)K + chunk * 16;
   }
-  // Scale rows 64 (2 (wave % 2) + t) + lane of the operand, t = 0, 1.
-  const uint8_t *sc_src[2] = {nullptr, nullptr};
-  if (MX) {
-    const uint8_t *ssrc = fetch_b ? SB : SA;
+  // Scale segment g = kScaleSegs * wave + t (g < 4: A) covers rows
+  // 64 (g % 4) + lane of its operand.
+  const bool sfetch_b = kScaleSegs * wave >= 4;
+  const int sseg0 = (kScaleSegs * wave) & 3;
+  const uint8_t *sc_src[kScaleSegs];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      sc_src[t] = ssrc + (size_t)min(base_row + 64 * (2 * (wave & 1) + t) + lane, lim) * (size_t)kblocks;
+  for (int t = 0; t < kScaleSegs; ++t) {
+    const int lim_s = sfetch_b ? N - 1 : M - 1, base_s = sfetch_b ? n0 : m0;
+    sc_src[t] = MX ? (sfetch_b ? SB : SA) + (size_t)min(base_s + 64 * (sseg0 + t) + lane, lim_s) * (size_t)kblocks
+                   : nullptr;
   }
   auto issue = [&](int ks) {
     uint8_t *st = smem + (ks % kGemmStages) * kGemmStageBytes;
-    uint8_t *dst = st + (fetch_b ? kGemmOperandBytes : 0) + (wave & 1) * 8 * 1024;
+    uint8_t *dst = st + (fetch_b ? kGemmOperandBytes : 0) + seg0 * 1024;
     const int kb = ks * kGemmK;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) __builtin_amdgcn_global_load_lds(seg_src[j] + kb, dst + j * 1024, 16, 0, 0);
+    for (int j = 0; j < kSegs; ++j) dma16(seg_src[j] + kb, dst + j * 1024);
     if (MX) {
-      uint8_t *sdst = st + 2 * kGemmOperandBytes + (fetch_b ? kGemmScaleBytes : 0) + (wave & 1) * 512;
+      uint8_t *sdst = st + 2 * kGemmOperandBytes + (sfetch_b ? kGemmScaleBytes : 0) + sseg0 * 256;
       const int so = 4 * (ks >> 1);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) __builtin_amdgcn_global_load_lds(sc_src[t] + so, sdst + t * 256, 4, 0, 0);
+      for (int t = 0; t < kScaleSegs; ++t) dma4(sc_src[t] + so, sdst + t * 256);
     }
   };
-  constexpr int kPer = MX ? 10 : 8;     // DMA instructions per wave per step
+  constexpr int kPer = kSegs + (MX ? kScaleSegs : 0);   // DMA instructions per wave per step
 
-  f32x16 acc[4][4];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{0};
 
 #pragma unroll
   for (int p = 0; p < kGemmStages - 1; ++p)
@@ -270,30 +309,33 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     const uint8_t *a_lds = st, *b_lds = st + kGemmOperandBytes;
     const uint8_t *sa_lds = st + 2 * kGemmOperandBytes + (ks & 1) * 2 + h;
     const uint8_t *sb_lds = sa_lds + kGemmScaleBytes;
-    int sa[4], sb[4];
+    int sa[TM], sb[TN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = MX ? (int)sa_lds[(wm + 32 * i + r) * 4] : unit_scale;
-      sb[i] = MX ? (int)sb_lds[(wn + 32 * i + r) * 4] : unit_scale;
-    }
-    i32x8 bf[4];
+    for (int i = 0; i < TM; ++i) sa[i] = MX ? (int)sa_lds[(wm + 32 * i + r) * 4] : unit_scale;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = gemm_frag(b_lds, wn + 32 * j + r, h);
+    for (int j = 0; j < TN; ++j) sb[j] = MX ? (int)sb_lds[(wn + 32 * j + r) * 4] : unit_scale;
+    // A fragments double-buffered: the reads for row tile i + 1 are issued
+    // before the MFMAs of row tile i, so LDS latency hides behind them.
+    i32x8 bf[TN], af[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const i32x8 af = gemm_frag(a_lds, wm + 32 * i + r, h);
+    for (int j = 0; j < TN; ++j) bf[j] = gemm_frag(b_lds, wn + 32 * j + r, h);
+    af[0] = gemm_frag(a_lds, wm + r, h);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
+    for (int i = 0; i < TM; ++i) {
+      if (i + 1 < TM) af[(i + 1) & 1] = gemm_frag(a_lds, wm + 32 * (i + 1) + r, h);
+      __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i & 1], bf[j], acc[i][j], 0, 0, 0,
                                                                     sa[i], 0, sb[j]);
     }
   }
 
   const float s = MX ? 1.0f : (*a_scale) * (*b_scale);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TN; ++j) {
       const int col = n0 + wn + 32 * j + r;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -303,6 +345,38 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
       }
     }
 }
+
+// Explicit instantiations: the kernels are referenced only from the launch
+// template below, and without these the device stubs were not emitted.
+#define GNQ_GEMM_DMA_INST(MX, NW, TM, TN)                                                        \
+  template __global__ void gemm_fp8_tn_dma<MX, NW, TM, TN>(                                      \
+      const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *, const float *,         \
+      const float *, int, int, int, uint16_t *, int, int, int);
+GNQ_GEMM_DMA_INST(true, 8, 4, 2)
+GNQ_GEMM_DMA_INST(false, 8, 4, 2)
+GNQ_GEMM_DMA_INST(true, 4, 4, 4)
+GNQ_GEMM_DMA_INST(false, 4, 4, 4)
+#undef GNQ_GEMM_DMA_INST
+
+template <bool MX, int NW, int TM, int TN>
+hipError_t launch_dma(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
+                      const float *a_scale, const float *b_scale, int M, int N, int K, uint16_t *C,
+                      int tiles_m, int tiles, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void *)gemm_fp8_tn_dma<MX, NW, TM, TN>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kGemmDmaLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemm_fp8_tn_dma<MX, NW, TM, TN>), dim3(tiles), dim3(64 * NW), kGemmDmaLds, st, A, SA,
+                     B, SB, a_scale, b_scale, M, N, K, C, tiles_m, tiles, 127);
+  return hipGetLastError();
+}
+
+#ifndef GNQ_GEMM_WAVES
+#define GNQ_GEMM_WAVES 8
+#endif
 
 hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,
                     const float *a_scale, const float *b_scale, int64_t M, int64_t N, int64_t K,
@@ -314,24 +388,17 @@ hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const
   const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
   const bool dma = K % (2 * kGemmK) == 0 && (!mx || ((uintptr_t)sa % 4 == 0 && (uintptr_t)sb % 4 == 0));
   if (dma) {
-    static bool attr_set[2] = {false, false};
-    if (!attr_set[mx]) {
-      hipError_t e = mx ? hipFuncSetAttribute((const void *)gemm_fp8_tn_dma<true>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmDmaLds)
-                        : hipFuncSetAttribute((const void *)gemm_fp8_tn_dma<false>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemmDmaLds);
-      if (e != hipSuccess) return e;
-      attr_set[mx] = true;
-    }
-    if (mx)
-      hipLaunchKernelGGL((gemm_fp8_tn_dma<true>), dim3(tiles), dim3(kGemmThreads), kGemmDmaLds, st, A,
-                         SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m,
-                         tiles, 127);
-    else
-      hipLaunchKernelGGL((gemm_fp8_tn_dma<false>), dim3(tiles), dim3(kGemmThreads), kGemmDmaLds, st, A,
-                         SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m,
-                         tiles, 127);
-    return hipGetLastError();
+#if GNQ_GEMM_WAVES == 8
+    return mx ? launch_dma<true, 8, 4, 2>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c,
+                                          tiles_m, tiles, st)
+              : launch_dma<false, 8, 4, 2>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
+                                           (uint16_t *)c, tiles_m, tiles, st);
+#else
+    return mx ? launch_dma<true, 4, 4, 4>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c,
+                                          tiles_m, tiles, st)
+              : launch_dma<false, 4, 4, 4>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
+                                           (uint16_t *)c, tiles_m, tiles, st);
+#endif
   }
   if (mx)
     hipLaunchKernelGGL((gemm_fp8_tn<true>), dim3(tiles), dim3(kGemmThreads), 0, st, A, SA, B, SB,
