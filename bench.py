@@ -134,6 +134,158 @@ def copy_calibration(args):
           flush=True)
 
 
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 MFMA
+
+
+def _time_graph(launch, steps, warmup, stream):
+    """Warm up, capture `steps` launches in one HIP graph, replay once;
+    returns (wall seconds, kernel ms per launch from events on `stream`)."""
+    import torch
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            launch(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            launch(warmup + i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, e0.elapsed_time(e1) / steps
+
+
+def gemm_cpu_baseline(gw, a, sa, b, sb, budget_s):
+    """The oracle GEMM (numpy float64 matmul, one BLAS thread) on the first
+    rows of the same operands, until about budget_s seconds."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    an, bn = a.numpy(), b.numpy()
+    rows, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while rows < gw.M:
+            n = min(64, gw.M - rows)
+            if gw.mode == "mxfp8":
+                O.gemm_mxfp8(an[rows:rows + n], sa[rows:rows + n].numpy(), bn, sb.numpy())
+            else:
+                O.gemm_fp8_static(an[rows:rows + n], gw.a_scale, bn, gw.b_scale)
+            rows += n
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * gw.N * gw.K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {rows} of {gw.M} rows x all {gw.N} columns of {gw.name}, {dt:.1f} s, "
+                      "numpy float64 matmul, one BLAS thread"}
+
+
+def gemm_main(args):
+    """The consumer GEMM: quantized activation x
+    quantized weight -> bf16, timed like the op (graph replay, buffer sets
+    rotated through >= 2 GiB)."""
+    import torch
+    from fp4_activation_quant_amd import _lib, ops
+    from fp4_activation_quant_amd.workloads import GEMM_WORKLOADS, make_gemm_inputs
+    _lib.lib()
+    gw = GEMM_WORKLOADS[args.gemm]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# gemm workload {gw.name}: generating inputs", file=sys.stderr, flush=True)
+    a, sa, b, sb = make_gemm_inputs(gw)
+    M, N, K = gw.M, gw.N, gw.K
+    mx = gw.mode == "mxfp8"
+    in_bytes = M * K + N * K + ((M + N) * (K // 32) if mx else 8)
+    out_bytes = 2 * M * N
+    n_sets = max(1, min(16, -(-ROTATE_BYTES // (in_bytes + out_bytes))))
+    sets = []
+    for _ in range(n_sets):
+        st = {"a": a.to(dev), "b": b.to(dev), "c": torch.empty((M, N), dtype=torch.bfloat16, device=dev)}
+        if mx:
+            st["sa"], st["sb"] = sa.to(dev), sb.to(dev)
+        else:
+            st["sa"] = torch.tensor([gw.a_scale], dtype=torch.float32, device=dev)
+            st["sb"] = torch.tensor([gw.b_scale], dtype=torch.float32, device=dev)
+        sets.append(st)
+
+    def launch(i):
+        st = sets[i % n_sets]
+        if mx:
+            ops.gemm_mxfp8(st["a"], st["sa"], st["b"], st["sb"], st["c"])
+        else:
+            ops.gemm_fp8_static(st["a"], st["sa"], st["b"], st["sb"], st["c"])
+
+    stream = torch.cuda.Stream(device=dev)
+    wall, kern_ms = _time_graph(launch, args.steps, args.warmup, stream)
+    flop = 2.0 * M * N * K
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = flop / (kern_ms * 1e-3) / 1e12
+    out = {
+        "metric": "consumer GEMM TFLOP/s (quantized activation x quantized weight -> bf16), 1 GPU",
+        "value": round(flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "e4m3" if not mx else "mxfp8 (e4m3 + e8m0)", "data": "synthetic",
+        "config": {"workload": gw.name, "M": M, "N": N, "K": K, "mode": gw.mode,
+                   "bytes_in": in_bytes, "bytes_out": out_bytes},
+        "launch": "graph", "buffer_sets": n_sets, "kernel_ms": round(kern_ms, 5),
+        "roofline": {"bound": "mfma", "kernel": "gemm_fp8_tn_dma" if K % 128 == 0 else "gemm_fp8_tn",
+                     "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    out["cpu_baseline"] = (None if args.no_cpu_baseline else
+                           gemm_cpu_baseline(gw, a, sa, b, sb, args.cpu_seconds))
+    print(json.dumps(out), flush=True)
+
+
+def chain_main(args):
+    """The op feeding the consumer GEMM, fused (add + norm + MXFP8 quant, then
+    the GEMM) against unfused (add + norm writing y, the standalone MXFP8
+    quant reading it back, then the GEMM): time per layer input."""
+    import torch
+    from fp4_activation_quant_amd import _lib, ops
+    from fp4_activation_quant_amd.workloads import WORKLOADS, GEMM_WORKLOADS, make_inputs, make_gemm_inputs
+    _lib.lib()
+    wl = WORKLOADS[args.chain]
+    gw = [g for g in GEMM_WORKLOADS.values() if g.mode == "mxfp8" and g.M == wl.M and g.K == wl.H][0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x, r, w = make_inputs(wl)
+    _, _, b, sb = make_gemm_inputs(gw)
+    M, H, N = wl.M, wl.H, gw.N
+    xd, wd, bd, sbd = x.to(dev), w.to(dev), b.to(dev), sb.to(dev)
+    xs = [xd, -xd]
+    rd = r.to(dev) if r is not None else None
+    q = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
+    s = torch.empty((M, H // 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, H), dtype=x.dtype, device=dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for path in ("fused", "unfused"):
+        def launch(i, path=path):
+            xi = xs[i & 1]
+            if path == "fused":
+                ops.add_rms_norm_quant_out(xi, rd, wd, wl.eps, None, "mxfp8", "gemma", q, s,
+                                           y if wl.write_y else None)
+            else:
+                ops.add_rms_norm_quant_out(xi, rd, wd, wl.eps, None, None, "gemma", None, None, y)
+                ops.quant_mxfp8(y, q, s)
+            ops.gemm_mxfp8(q, s, bd, sbd, c)
+        stream = torch.cuda.Stream(device=dev)
+        wall, kern_ms = _time_graph(launch, args.steps, args.warmup, stream)
+        res[path] = kern_ms
+    print(json.dumps({"metric": "norm + quant + consumer GEMM, us per layer input", "workload": wl.name,
+                      "gemm": gw.name, "fused_us": round(res["fused"] * 1e3, 2),
+                      "unfused_us": round(res["unfused"] * 1e3, 2),
+                      "speedup": round(res["unfused"] / res["fused"], 3)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +303,12 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the op, time torch's device copy of MIB MiB (the plain "
                          "copy kernel used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--gemm", default=None, metavar="GEMM_WORKLOAD",
+                    help="time the consumer GEMM of the quantized activation instead "
+                         "(gemm_mxfp8_m8192_n4096_k4096, ...)")
+    ap.add_argument("--chain", default=None, metavar="WORKLOAD",
+                    help="time the op (MXFP8 output) feeding the consumer GEMM, fused against "
+                         "the unfused chain, for a norm workload with a matching GEMM workload")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the op is row-independent and this build has no "
@@ -163,6 +321,10 @@ def main():
 
     if args.copy_calibration:
         return copy_calibration(args)
+    if args.gemm:
+        return gemm_main(args)
+    if args.chain:
+        return chain_main(args)
     _lib.lib()
     wl = WORKLOADS[args.workload or DEFAULT_BENCH]
     dev = torch.device("cuda:0")

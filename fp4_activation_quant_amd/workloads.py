@@ -162,3 +162,55 @@ def load_scale(wl: Workload) -> float:
     with open(SCALES_JSON) as f:
         table = json.load(f)
     return float.fromhex(table[wl.name]["scale_hex"])
+
+
+# ---------------------------------------------------------------------------
+# Consumer-GEMM workloads: the quantized activation of a norm workload's
+# shape (M tokens x K = H) against an (N, K) weight in the same format.
+# Codes are drawn directly as bytes (no quantization arithmetic here): sign
+# and mantissa uniform, E4M3 exponent field uniform in [lo, hi] (never the
+# NaN pattern); E8M0 block scales uniform in [s_lo, s_hi].
+
+@dataclass(frozen=True)
+class GemmWorkload:
+    name: str
+    mode: str             # "mxfp8" | "fp8"
+    M: int
+    N: int
+    K: int
+    seed_base: int
+    exp_range: tuple = (3, 11)          # activation codes: |v| in [2^-4, 2^4]
+    w_exp_range: tuple = (0, 7)         # weight codes: |v| below 2^1
+    scale_range: tuple = (118, 126)     # E8M0 codes of both operands
+    a_scale: float = 0.02               # static FP8 tensor scales
+    b_scale: float = 0.004
+
+
+GEMM_WORKLOADS = {g.name: g for g in [
+    GemmWorkload("gemm_mxfp8_m8192_n4096_k4096", "mxfp8", 8192, 4096, 4096, 8000),
+    GemmWorkload("gemm_fp8_m8192_n4096_k4096", "fp8", 8192, 4096, 4096, 8100),
+    GemmWorkload("gemm_mxfp8_m32768_n8192_k8192", "mxfp8", 32768, 8192, 8192, 8200),
+    GemmWorkload("gemm_mxfp8_m256_n4096_k4096", "mxfp8", 256, 4096, 4096, 8300),
+]}
+
+
+def _draw_codes(rows, cols, exp_range, gen):
+    lo, hi = exp_range
+    sign = torch.randint(0, 2, (rows, cols), generator=gen, dtype=torch.int32) << 7
+    ex = torch.randint(lo, hi + 1, (rows, cols), generator=gen, dtype=torch.int32)
+    man = torch.randint(0, 8, (rows, cols), generator=gen, dtype=torch.int32)
+    man = torch.where((ex == 15) & (man == 7), man - 1, man)        # no NaN code
+    return (sign | (ex << 3) | man).to(torch.uint8)
+
+
+def make_gemm_inputs(gw: GemmWorkload):
+    """(a codes (M, K), a scales (M, K/32) or None, b codes (N, K), b scales
+    (N, K/32) or None) as CPU uint8 tensors."""
+    a = _draw_codes(gw.M, gw.K, gw.exp_range, _gen(gw.seed_base))
+    b = _draw_codes(gw.N, gw.K, gw.w_exp_range, _gen(gw.seed_base + 1))
+    if gw.mode != "mxfp8":
+        return a, None, b, None
+    lo, hi = gw.scale_range
+    sa = torch.randint(lo, hi + 1, (gw.M, gw.K // 32), generator=_gen(gw.seed_base + 2), dtype=torch.int32)
+    sb = torch.randint(lo, hi + 1, (gw.N, gw.K // 32), generator=_gen(gw.seed_base + 3), dtype=torch.int32)
+    return a, sa.to(torch.uint8), b, sb.to(torch.uint8)

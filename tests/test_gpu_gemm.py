@@ -124,34 +124,43 @@ def test_fp8_static_gemm_random():
 
 @pytest.mark.parametrize("mode", ["mxfp8", "fp8"])
 def test_gemm_consumes_the_ops_quantized_output(mode):
-    """The op's codes and scales go straight into the consumer linear; the
-    result matches the oracle GEMM of those same codes."""
+    """The op's codes and scales go straight into the consumer linear.  The
+    oracle computes the op's codes from the seeded inputs and the GEMM of
+    those codes; on the GPU the op's own output feeds the GEMM.  Rows whose
+    GPU codes equal the oracle's (all but a few: y may differ by one unit
+    near a rounding tie) must match the oracle GEMM within the tolerance."""
     print(f"gemm consumer {mode}", flush=True)
     g = torch.Generator().manual_seed(23)
     M, H, N = 300, 4096, 384
-    x = torch.randn(M, H, generator=g).to(torch.bfloat16).cuda()
-    r = torch.randn(M, H, generator=g).to(torch.bfloat16).cuda()
-    w = (torch.randn(H, generator=g) * 0.1).to(torch.bfloat16).cuda()
+    x = torch.randn(M, H, generator=g).to(torch.bfloat16)
+    r = torch.randn(M, H, generator=g).to(torch.bfloat16)
+    w = (torch.randn(H, generator=g) * 0.1).to(torch.bfloat16)
     rng = np.random.default_rng(3)
     wq = _finite_codes(rng, (N, H))
     wq = np.where((wq & 0x78) > 0x50, wq & 0x87, wq).astype(np.uint8)   # keep |w| <= 16
+    xd, rd, wd = x.cuda(), r.cuda(), w.cuda()
     if mode == "mxfp8":
         ws = rng.integers(118, 124, size=(N, H // 32)).astype(np.uint8)
-        q, s, _ = ops.add_rms_norm_quant(x, r, w, 1e-6, None, "mxfp8")
+        ref = O.add_rms_norm_quant(P.bits16(x), P.bits16(r), P.bits16(w), 1e-6, 1.0, "mxfp8")
+        exact, _ = O.gemm_mxfp8(ref["q"], ref["scales"], wq, ws)
+        mag = O.gemm_f64(np.abs(O.dequant_mxfp8(ref["q"], ref["scales"])), np.abs(O.dequant_mxfp8(wq, ws)))
+        q, s, _ = ops.add_rms_norm_quant(xd, rd, wd, 1e-6, None, "mxfp8")
         out = ops.gemm_mxfp8(q, s, _dev(wq), _dev(ws))
-        aq, as_ = q.view(torch.uint8).cpu().numpy(), s.view(torch.uint8).cpu().numpy()
-        exact, _ = O.gemm_mxfp8(aq, as_, wq, ws)
-        mag = O.gemm_f64(np.abs(O.dequant_mxfp8(aq, as_)), np.abs(O.dequant_mxfp8(wq, ws)))
+        same = np.all(q.view(torch.uint8).cpu().numpy() == ref["q"], axis=1) & \
+            np.all(s.view(torch.uint8).cpu().numpy() == ref["scales"], axis=1)
     else:
+        ref = O.add_rms_norm_quant(P.bits16(x), P.bits16(r), P.bits16(w), 1e-6, 0.02, "fp8")
+        exact, _ = O.gemm_fp8_static(ref["q"], 0.02, wq, 0.004)
+        mag = O.gemm_f64(np.abs(O.dequant_fp8_static(ref["q"], 0.02)), np.abs(O.dequant_fp8_static(wq, 0.004)))
         sa = torch.tensor([0.02], dtype=torch.float32, device="cuda")
         sw = torch.tensor([0.004], dtype=torch.float32, device="cuda")
-        q, _, _ = ops.gemma_add_rms_norm_quant(x, r, w, 1e-6, sa, False)
+        q, _, _ = ops.gemma_add_rms_norm_quant(xd, rd, wd, 1e-6, sa, False)
         out = ops.gemm_fp8_static(q, sa, _dev(wq), sw)
-        aq = q.view(torch.uint8).cpu().numpy()
-        exact, _ = O.gemm_fp8_static(aq, 0.02, wq, 0.004)
-        mag = O.gemm_f64(np.abs(O.dequant_fp8_static(aq, 0.02)), np.abs(O.dequant_fp8_static(wq, 0.004)))
+        same = np.all(q.view(torch.uint8).cpu().numpy() == ref["q"], axis=1)
     torch.cuda.synchronize()
-    _tolerance_check(P.bits16(out), exact, mag)
+    print(f"  rows with the oracle's codes: {int(same.sum())} / {M}", flush=True)
+    assert same.mean() >= 0.95
+    _tolerance_check(P.bits16(out)[same], exact[same], mag[same])
 
 
 def test_gemm_empty_writes_nothing():
