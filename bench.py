@@ -280,10 +280,42 @@ def chain_main(args):
         stream = torch.cuda.Stream(device=dev)
         wall, kern_ms = _time_graph(launch, args.steps, args.warmup, stream)
         res[path] = kern_ms
-    print(json.dumps({"metric": "norm + quant + consumer GEMM, us per layer input", "workload": wl.name,
-                      "gemm": gw.name, "fused_us": round(res["fused"] * 1e3, 2),
-                      "unfused_us": round(res["unfused"] * 1e3, 2),
-                      "speedup": round(res["unfused"] / res["fused"], 3)}), flush=True)
+    # Row chunks on two streams: the op on chunk j + 1 runs beside the GEMM of
+    # chunk j (a memory-bound kernel next to a compute-bound one); every
+    # stream stays at the default priority.
+    ovl = max(1, args.overlap)
+    if ovl > 1 and M % ovl == 0:
+        rows = M // ovl
+        s_norm, s_gemm = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+        done = [torch.cuda.Event() for _ in range(ovl)]
+
+        def launch_ovl(i):
+            xi = xs[i & 1]
+            cur = torch.cuda.current_stream(dev)
+            s_norm.wait_stream(cur)             # fork from the launching (capturing) stream;
+            s_gemm.wait_stream(cur)             # the previous step joined it at its end
+            for j in range(ovl):
+                sl = slice(j * rows, (j + 1) * rows)
+                with torch.cuda.stream(s_norm):
+                    ops.add_rms_norm_quant_out(xi[sl], rd[sl] if rd is not None else None, wd, wl.eps, None,
+                                               "mxfp8", "gemma", q[sl], s[sl], y[sl] if wl.write_y else None)
+                    done[j].record(s_norm)
+                with torch.cuda.stream(s_gemm):
+                    s_gemm.wait_event(done[j])
+                    ops.gemm_mxfp8(q[sl], s[sl], bd, sbd, c[sl])
+            cur.wait_stream(s_gemm)
+            cur.wait_stream(s_norm)
+
+        stream = torch.cuda.Stream(device=dev)
+        wall, kern_ms = _time_graph(launch_ovl, args.steps, args.warmup, stream)
+        res["fused_overlap"] = kern_ms
+    line = {"metric": "norm + quant + consumer GEMM, us per layer input", "workload": wl.name,
+            "gemm": gw.name, "fused_us": round(res["fused"] * 1e3, 2),
+            "unfused_us": round(res["unfused"] * 1e3, 2),
+            "speedup": round(res["unfused"] / res["fused"], 3)}
+    if "fused_overlap" in res:
+        line.update(overlap_chunks=ovl, fused_overlap_us=round(res["fused_overlap"] * 1e3, 2))
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -309,6 +341,9 @@ def main():
     ap.add_argument("--chain", default=None, metavar="WORKLOAD",
                     help="time the op (MXFP8 output) feeding the consumer GEMM, fused against "
                          "the unfused chain, for a norm workload with a matching GEMM workload")
+    ap.add_argument("--overlap", type=int, default=1, metavar="CHUNKS",
+                    help="with --chain: also time the fused op and the GEMM on row chunks, the op "
+                         "of chunk j + 1 on a second stream beside the GEMM of chunk j")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the op is row-independent and this build has no "
