@@ -56,11 +56,12 @@ def algorithmic_bytes(wl):
 
 
 def kernel_sha():
-    """Hash of every kernel source file: traffic counters taken on other
-    sources are not reported."""
+    """Hash of the fused kernel's source files (the shared header, the fused
+    kernel template and its per-mode translation units): traffic counters
+    taken on other sources are not reported."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SRC_DIR)):
-        if name.endswith((".hip", ".hpp")):
+        if name == "gnq_common.hpp" or name.startswith("gnq_fused"):
             h.update(name.encode())
             with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
                 h.update(f.read())
