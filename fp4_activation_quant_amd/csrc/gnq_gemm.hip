@@ -378,6 +378,113 @@ hipError_t launch_dma(const uint8_t *A, const uint8_t *SA, const uint8_t *B, con
 #define GNQ_GEMM_WAVES 8
 #endif
 
+// Skinny GEMM for few activation rows (decode batches, M <= 64 per chunk):
+// the weight stream is the whole cost, so each workgroup owns 32 weight rows
+// (output columns) and one 64-row chunk of the activation, and its 8 waves
+// split K (wave w takes K steps w, w + 8, ...), loading their fragments
+// straight from global memory (the activation chunk stays in L2), kSkinnyUnroll
+// steps in flight per wave.  The 8 partial 64 x 32 fp32 tiles are summed
+// through LDS in a fixed order (deterministic), then rounded to bf16.
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyUnroll = 4;
+constexpr int kSkinnyRows = 64;                                      // activation rows per chunk
+constexpr int kSkinnyLds = kSkinnyWaves * 2 * 16 * 64 * 4;           // 64 KB of partials
+
+__device__ __forceinline__ i32x8 gemm_gfrag(const uint8_t *row_k) {
+  // lane's 32 bytes of one 64-byte K step: 16 at +16h and 16 at +32+16h
+  // (row_k already includes the +16h)
+  const u32x4 lo = *reinterpret_cast<const u32x4 *>(row_k);
+  const u32x4 hi = *reinterpret_cast<const u32x4 *>(row_k + 32);
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <bool MX>
+__global__ void __launch_bounds__(64 * kSkinnyWaves)
+gemm_fp8_skinny(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
+                const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
+                const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N, int K,
+                uint16_t *__restrict__ C, int unit_scale) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float *part = reinterpret_cast<float *>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int n0 = blockIdx.x * 32, m0 = blockIdx.y * kSkinnyRows;
+  const int ksteps = K / kGemmK, kblocks = K / 32;
+  const uint8_t *b_row = B + (size_t)min(n0 + r, N - 1) * (size_t)K + 16 * h;
+  const uint8_t *a_row0 = A + (size_t)min(m0 + r, M - 1) * (size_t)K + 16 * h;
+  const uint8_t *a_row1 = A + (size_t)min(m0 + 32 + r, M - 1) * (size_t)K + 16 * h;
+  const uint8_t *sb_row = MX ? SB + (size_t)min(n0 + r, N - 1) * (size_t)kblocks + h : nullptr;
+  const uint8_t *sa_row0 = MX ? SA + (size_t)min(m0 + r, M - 1) * (size_t)kblocks + h : nullptr;
+  const uint8_t *sa_row1 = MX ? SA + (size_t)min(m0 + 32 + r, M - 1) * (size_t)kblocks + h : nullptr;
+  const bool two = m0 + 32 < M;                    // second 32-row tile has rows
+
+  f32x16 acc0 = f32x16{0}, acc1 = f32x16{0};
+  for (int ks0 = wave; ks0 < ksteps; ks0 += kSkinnyUnroll * kSkinnyWaves) {
+    i32x8 bf[kSkinnyUnroll], af0[kSkinnyUnroll], af1[kSkinnyUnroll];
+    int sb[kSkinnyUnroll], sa0[kSkinnyUnroll], sa1[kSkinnyUnroll];
+    // all loads of the unrolled steps first (steps past the end load step
+    // ks0 again and are not used)
+#pragma unroll
+    for (int u = 0; u < kSkinnyUnroll; ++u) {
+      const int ks = ks0 + u * kSkinnyWaves < ksteps ? ks0 + u * kSkinnyWaves : ks0;
+      const size_t kb = (size_t)ks * kGemmK;
+      bf[u] = gemm_gfrag(b_row + kb);
+      af0[u] = gemm_gfrag(a_row0 + kb);
+      af1[u] = two ? gemm_gfrag(a_row1 + kb) : i32x8{0};
+      sb[u] = MX ? (int)sb_row[2 * ks] : unit_scale;
+      sa0[u] = MX ? (int)sa_row0[2 * ks] : unit_scale;
+      sa1[u] = MX ? (int)sa_row1[2 * ks] : unit_scale;
+    }
+#pragma unroll
+    for (int u = 0; u < kSkinnyUnroll; ++u) {
+      if (ks0 + u * kSkinnyWaves < ksteps) {
+        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af0[u], bf[u], acc0, 0, 0, 0, sa0[u], 0, sb[u]);
+        if (two)
+          acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af1[u], bf[u], acc1, 0, 0, 0, sa1[u], 0, sb[u]);
+      }
+    }
+  }
+  // partials: part[((wave * 2 + tile) * 16 + v) * 64 + lane]
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    part[((wave * 2 + 0) * 16 + v) * 64 + lane] = acc0[v];
+    part[((wave * 2 + 1) * 16 + v) * 64 + lane] = acc1[v];
+  }
+  __syncthreads();
+  const float s = MX ? 1.0f : (*a_scale) * (*b_scale);
+  for (int e = tid; e < 2 * 16 * 64; e += 64 * kSkinnyWaves) {
+    float sum = 0.0f;
+    for (int w = 0; w < kSkinnyWaves; ++w) sum += part[w * 2 * 16 * 64 + e];
+    const int tile = e / (16 * 64), v = (e / 64) % 16, l = e % 64;
+    const int row = m0 + 32 * tile + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+    const int col = n0 + (l & 31);
+    if (row < M && col < N)
+      C[(size_t)row * (size_t)N + col] = (uint16_t)(Bf16::pack(sum * s, 0.0f) & 0xffffu);
+  }
+}
+
+template __global__ void gemm_fp8_skinny<true>(const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *,
+                                               const float *, const float *, int, int, int, uint16_t *, int);
+template __global__ void gemm_fp8_skinny<false>(const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *,
+                                                const float *, const float *, int, int, int, uint16_t *, int);
+
+template <bool MX>
+hipError_t launch_skinny(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
+                         const float *a_scale, const float *b_scale, int M, int N, int K, uint16_t *C,
+                         hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void *)gemm_fp8_skinny<MX>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + kSkinnyRows - 1) / kSkinnyRows));
+  hipLaunchKernelGGL((gemm_fp8_skinny<MX>), grid, dim3(64 * kSkinnyWaves), kSkinnyLds, st, A, SA, B, SB,
+                     a_scale, b_scale, M, N, K, C, 127);
+  return hipGetLastError();
+}
+
 hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,
                     const float *a_scale, const float *b_scale, int64_t M, int64_t N, int64_t K,
                     void *c, hipStream_t st) {
@@ -386,6 +493,12 @@ hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const
   const int tiles = tiles_m * tiles_n;
   const uint8_t *A = (const uint8_t *)a, *B = (const uint8_t *)b;
   const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
+  // Few activation rows: the large tiles would leave most CUs idle (one
+  // workgroup per 256 output columns); the skinny kernel streams the weight
+  // with N / 32 x M / 64 workgroups.
+  if (M <= 256 && K % kGemmK == 0)
+    return mx ? launch_skinny<true>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st)
+              : launch_skinny<false>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st);
   const bool dma = K % (2 * kGemmK) == 0 && (!mx || ((uintptr_t)sa % 4 == 0 && (uintptr_t)sb % 4 == 0));
   if (dma) {
 #if GNQ_GEMM_WAVES == 8
