@@ -8,6 +8,8 @@
 // `allreduce_gemma_rms_norm_mxfp8` of the `fused_allreduce_gemma_rms_norm`
 // page without its all-reduce; it needs H % 32 == 0.
 
+#include <stdint.h>
+
 #include "gemma_norm_quant.h"
 #include "gnq_common.hpp"
 
@@ -96,6 +98,10 @@ nq_status nq_add_rms_norm_quant(const void *x, void *residual, const void *weigh
   if (none && !write_y) return NQ_EINVAL;
   if (nv && H % 64 != 0) return NQ_EUNSUPPORTED;
   if (mx && H % kMxBlock != 0) return NQ_EUNSUPPORTED;
+  // 16-bit elements need 2-byte alignment, the fp32 scale 4-byte.
+  if (((uintptr_t)x | (uintptr_t)residual | (uintptr_t)weight | (uintptr_t)((write_y || none) ? y : nullptr)) % 2 != 0)
+    return NQ_EINVAL;
+  if ((mode == NQ_MODE_FP8_STATIC || nv) && (uintptr_t)scale % 4 != 0) return NQ_EINVAL;
   const size_t act = (size_t)M * (size_t)H * 2;
   const size_t qbytes = none ? 0 : nv ? (size_t)M * (size_t)(H / 2) : (size_t)M * (size_t)H;
   const size_t bsbytes = nv ? block_scale_bytes(M, H) : mx ? (size_t)M * (size_t)(H / kMxBlock) : 0;
@@ -150,6 +156,7 @@ static nq_status quant_common(const void *y, const float *scale, int64_t M, int6
   if (!y || !q || (!mx && !scale) || ((nv || mx) && !block_scale)) return NQ_EINVAL;
   if (nv && H % kBlock != 0) return NQ_EUNSUPPORTED;
   if (mx && H % kMxBlock != 0) return NQ_EUNSUPPORTED;
+  if ((uintptr_t)y % 2 != 0 || (!mx && (uintptr_t)scale % 4 != 0)) return NQ_EINVAL;
   const size_t act = (size_t)M * (size_t)H * 2;
   const size_t qbytes = nv ? (size_t)M * (size_t)(H / 2) : (size_t)M * (size_t)H;
   const size_t bsbytes = nv ? block_scale_bytes(M, H) : mx ? (size_t)M * (size_t)(H / kMxBlock) : 0;
@@ -194,7 +201,10 @@ static nq_status gemm_common(bool mx, const void *a, const void *sa, const float
   if (!a || !b || !out) return NQ_EINVAL;
   if (mx ? (!sa || !sb) : (!a_scale || !b_scale)) return NQ_EINVAL;
   if (K % kMxBlock != 0) return NQ_EUNSUPPORTED;
-  if (((uintptr_t)a | (uintptr_t)b) % 16 != 0) return NQ_EINVAL;
+  if (((uintptr_t)a | (uintptr_t)b) % 16 != 0 || (uintptr_t)out % 2 != 0) return NQ_EINVAL;
+  if (!mx && ((uintptr_t)a_scale | (uintptr_t)b_scale) % 4 != 0) return NQ_EINVAL;
+  // one workgroup per 256 x 256 output tile: the count must fit a grid
+  if (((M + 255) / 256) * ((N + 255) / 256) > (int64_t)INT32_MAX) return NQ_EINVAL;
   const size_t obytes = (size_t)M * (size_t)N * 2;
   const size_t abytes = (size_t)M * (size_t)K, bbytes = (size_t)N * (size_t)K;
   const size_t sab = mx ? (size_t)M * (size_t)(K / kMxBlock) : 4;

@@ -24,6 +24,8 @@
 // banks).  Global loads of step k + 1 are issued before the
 // MFMAs of step k.  Rows beyond M or N are clamped on load and masked on
 // store; a K tail of 32 (K % 64 == 32) loads zeros for the missing block.
+#include <atomic>
+
 #include "gnq_common.hpp"
 
 namespace gnq {
@@ -346,6 +348,18 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     }
 }
 
+// Raise a kernel's dynamic-LDS limit once per device (bit d of `done`).
+inline hipError_t allow_dynamic_lds(const void *kernel, int bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 // Explicit instantiations: the kernels are referenced only from the launch
 // template below, and without these the device stubs were not emitted.
 #define GNQ_GEMM_DMA_INST(MX, NW, TM, TN)                                                        \
@@ -362,13 +376,9 @@ template <bool MX, int NW, int TM, int TN>
 hipError_t launch_dma(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
                       const float *a_scale, const float *b_scale, int M, int N, int K, uint16_t *C,
                       int tiles_m, int tiles, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void *)gemm_fp8_tn_dma<MX, NW, TM, TN>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kGemmDmaLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = allow_dynamic_lds((const void *)gemm_fp8_tn_dma<MX, NW, TM, TN>, kGemmDmaLds, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gemm_fp8_tn_dma<MX, NW, TM, TN>), dim3(tiles), dim3(64 * NW), kGemmDmaLds, st, A, SA,
                      B, SB, a_scale, b_scale, M, N, K, C, tiles_m, tiles, 127);
   return hipGetLastError();
@@ -472,13 +482,9 @@ template <bool MX>
 hipError_t launch_skinny(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
                          const float *a_scale, const float *b_scale, int M, int N, int K, uint16_t *C,
                          hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void *)gemm_fp8_skinny<MX>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = allow_dynamic_lds((const void *)gemm_fp8_skinny<MX>, kSkinnyLds, lds_set);
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + kSkinnyRows - 1) / kSkinnyRows));
   hipLaunchKernelGGL((gemm_fp8_skinny<MX>), grid, dim3(64 * kSkinnyWaves), kSkinnyLds, st, A, SA, B, SB,
                      a_scale, b_scale, M, N, K, C, 127);

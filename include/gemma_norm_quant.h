@@ -100,9 +100,10 @@ typedef enum { NQ_NORM_GEMMA = 0, NQ_NORM_PLAIN = 1 } nq_norm;
  *   y          (M, H) dtype when write_y, else ignored (may be NULL).
  *   stream     hipStream_t to launch on.
  *
- * Outputs must not overlap inputs or each other (residual is both).  Any
- * alignment and any H are accepted; the fast path needs 16-byte aligned
- * pointers and H % 16 == 0, other cases take a slower correct path.
+ * Outputs must not overlap inputs or each other (residual is both).
+ * x, residual, weight and y must be 2-byte aligned and scale 4-byte aligned
+ * (NQ_EINVAL otherwise); any H is accepted.  The fast path needs 16-byte
+ * aligned pointers and H % 16 == 0, other cases take a slower correct path.
  */
 nq_status nq_gemma_add_rms_norm_quant(const void *x, void *residual, const void *weight,
                                       float eps, const float *scale, int64_t M, int64_t H,
@@ -185,8 +186,8 @@ nq_status nq_quant_mxfp8(const void *y, int64_t M, int64_t H, int dtype, void *q
  *   out: (M, N) bf16, row-major, round to nearest even of the fp32
  *     accumulation; must not overlap any input.
  *   M, N >= 0 (either 0: NQ_OK, nothing launched); K > 0 with K % 32 == 0
- *     (NQ_EUNSUPPORTED otherwise); a and b 16-byte aligned (NQ_EINVAL
- *     otherwise).
+ *     (NQ_EUNSUPPORTED otherwise); a and b 16-byte aligned, out 2-byte
+ *     aligned, the static scales 4-byte aligned (NQ_EINVAL otherwise).
  *
  * Accumulation: the block-scaled MFMA of gfx950 in fp32 accumulators; the
  * MFMA's internal sum of its 64 products is not an IEEE fp32 sum (measured

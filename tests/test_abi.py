@@ -80,6 +80,10 @@ def call(**over):
     (dict(q=X + 100), _lib.NQ_EINVAL),
     (dict(wy=1, y=R + 2), _lib.NQ_EINVAL),
     (dict(mode=1, bs=Q + 10), _lib.NQ_EINVAL),
+    (dict(x=X + 1), _lib.NQ_EINVAL),                 # 16-bit data must be 2-byte aligned
+    (dict(w=W + 1), _lib.NQ_EINVAL),
+    (dict(wy=1, y=Y + 3), _lib.NQ_EINVAL),
+    (dict(s=S + 2), _lib.NQ_EINVAL),                 # fp32 scale must be 4-byte aligned
     # M == 0: valid, returns before any launch
     (dict(M=0), _lib.NQ_OK),
     (dict(M=0, mode=1, wy=1), _lib.NQ_OK),
@@ -213,6 +217,8 @@ def test_torch_wrapper_rejects_bad_tensors_before_the_library():
     (dict(a=X + 8), _lib.NQ_EINVAL),                  # unaligned codes
     (dict(out=X + 64), _lib.NQ_EINVAL),               # out overlaps a
     (dict(out=Q + 4096), _lib.NQ_EINVAL),             # out overlaps b
+    (dict(out=Y + 1), _lib.NQ_EINVAL),                # bf16 output must be 2-byte aligned
+    (dict(M=1 << 30, N=1 << 30, out=0x7F0000000000), _lib.NQ_EINVAL),  # tile count beyond a grid
     (dict(M=0), _lib.NQ_OK),
     (dict(N=0), _lib.NQ_OK),
 ])
