@@ -352,6 +352,9 @@ def main():
     ap.add_argument("--chain", default=None, metavar="WORKLOAD",
                     help="time the op (MXFP8 output) feeding the consumer GEMM, fused against "
                          "the unfused chain, for a norm workload with a matching GEMM workload")
+    ap.add_argument("--write-y", action="store_true",
+                    help="also write y for a workload whose default is write_y=False (the "
+                         "decode sweep with the normed output, 9H bytes per row)")
     ap.add_argument("--overlap", type=int, default=1, metavar="CHUNKS",
                     help="with --chain: also time the fused op and the GEMM on row chunks, the op "
                          "of chunk j + 1 on a second stream beside the GEMM of chunk j")
@@ -373,6 +376,9 @@ def main():
         return chain_main(args)
     _lib.lib()
     wl = WORKLOADS[args.workload or DEFAULT_BENCH]
+    if args.write_y and not wl.write_y:
+        import dataclasses
+        wl = dataclasses.replace(wl, write_y=True)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"# workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
