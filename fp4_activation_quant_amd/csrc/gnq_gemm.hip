@@ -202,16 +202,19 @@ gemm_fp8_tn(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
 // wave's 1 KB segments straight into LDS (lane l fills bytes 16 l .. 16 l +
 // 15 of the segment, so lane l fetches the global chunk that the swizzled
 // layout puts there); kGemmStages stages keep kGemmStages - 1 steps in
-// flight with no register staging.  For MXFP8 each stage also receives, by
-// 4-byte DMA, the four E8M0 codes of every row covering this step and the
-// next (blocks 4 (k / 2) .. 4 (k / 2) + 3), so the scales travel with the
-// data and the MFMA reads them from LDS.  One barrier per step: wait for this
+// flight with no register staging.  For MXFP8 the E8M0 codes arrive in
+// windows of 8 steps: one 16-byte DMA per row (blocks 16 j .. 16 j + 15 of
+// the row) into one of two LDS windows, issued a window ahead, so a row's
+// scale line is fetched once per 8 steps instead of once per step (4-byte
+// loads from 64 rows per instruction cost ~20% when issued every step).  One barrier per step: wait for this
 // step's own loads, barrier, then refill the stage every wave finished
 // reading in the previous step.
 constexpr int kGemmStages = 4;
-constexpr int kGemmScaleBytes = kGemmTile * 4;                       // per operand per stage
-constexpr int kGemmStageBytes = 2 * kGemmOperandBytes + 2 * kGemmScaleBytes;
-constexpr int kGemmDmaLds = kGemmStages * kGemmStageBytes;           // 136 KB
+constexpr int kGemmStageBytes = 2 * kGemmOperandBytes;               // 32 KB
+constexpr int kGemmScaleSteps = 8;                                   // K steps per scale window
+constexpr int kGemmScaleWin = kGemmTile * 2 * kGemmScaleSteps;       // 4 KB per operand
+constexpr int kGemmScaleOff = kGemmStages * kGemmStageBytes;         // two windows after the stages
+constexpr int kGemmDmaLds = kGemmScaleOff + 2 * 2 * kGemmScaleWin;   // 144 KB
 
 // Global -> LDS DMA of 16 or 4 bytes per lane (lane l writes lds + size * l).
 __device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *lds) {
@@ -281,14 +284,18 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     const int kb = ks * kGemmK;
 #pragma unroll
     for (int j = 0; j < kSegs; ++j) dma16(seg_src[j] + kb, dst + j * 1024);
-    if (MX) {
-      uint8_t *sdst = st + 2 * kGemmOperandBytes + (sfetch_b ? kGemmScaleBytes : 0) + sseg0 * 256;
-      const int so = 4 * (ks >> 1);
-#pragma unroll
-      for (int t = 0; t < kScaleSegs; ++t) dma4(sc_src[t] + so, sdst + t * 256);
-    }
   };
-  constexpr int kPer = kSegs + (MX ? kScaleSegs : 0);   // DMA instructions per wave per step
+  // Scale window w (steps 8 w .. 8 w + 7): segment t of this wave, 64 rows
+  // x 16 bytes, into window buffer w % 2.
+  auto issue_scales = [&](int w) {
+    uint8_t *sdst = smem + kGemmScaleOff + (w & 1) * 2 * kGemmScaleWin + (sfetch_b ? kGemmScaleWin : 0) +
+                    sseg0 * 1024;
+#pragma unroll
+    for (int t = 0; t < kScaleSegs; ++t) dma16(sc_src[t] + 16 * w, sdst + t * 1024);
+  };
+  // The wait below counts only data DMA of the later steps; a scale window
+  // issued in between only makes it stricter (loads complete in order).
+  constexpr int kPer = kSegs;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -296,6 +303,7 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{0};
 
+  if (MX) issue_scales(0);
 #pragma unroll
   for (int p = 0; p < kGemmStages - 1; ++p)
     if (p < ksteps) issue(p);
@@ -303,19 +311,23 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     if (ksteps - 1 - ks >= kGemmStages - 2) wait_vmcnt<kPer * (kGemmStages - 2)>();
     else wait_vmcnt<0>();
     // A plain barrier: the wait above already covers this step's loads of
-    // this wave, and every LDS read of the previous step has been consumed
-    // by its MFMAs.  (A fenced barrier would drain all DMA in flight.)
+    // this wave (and the scale window, issued before them), and every LDS
+    // read of the previous step has been consumed by its MFMAs.  (A fenced
+    // barrier would drain all DMA in flight.)
     asm volatile("s_barrier" ::: "memory");
     if (ks + kGemmStages - 1 < ksteps) issue(ks + kGemmStages - 1);
+    // the next window goes into the buffer the previous window's steps used
+    if (MX && ks % kGemmScaleSteps == 0 && ks + kGemmScaleSteps < ksteps) issue_scales(ks / kGemmScaleSteps + 1);
     const uint8_t *st = smem + (ks % kGemmStages) * kGemmStageBytes;
     const uint8_t *a_lds = st, *b_lds = st + kGemmOperandBytes;
-    const uint8_t *sa_lds = st + 2 * kGemmOperandBytes + (ks & 1) * 2 + h;
-    const uint8_t *sb_lds = sa_lds + kGemmScaleBytes;
+    const uint8_t *sa_lds = smem + kGemmScaleOff + ((ks / kGemmScaleSteps) & 1) * 2 * kGemmScaleWin +
+                            (ks % kGemmScaleSteps) * 2 + h;
+    const uint8_t *sb_lds = sa_lds + kGemmScaleWin;
     int sa[TM], sb[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] = MX ? (int)sa_lds[(wm + 32 * i + r) * 4] : unit_scale;
+    for (int i = 0; i < TM; ++i) sa[i] = MX ? (int)sa_lds[(wm + 32 * i + r) * 16] : unit_scale;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sb[j] = MX ? (int)sb_lds[(wn + 32 * j + r) * 4] : unit_scale;
+    for (int j = 0; j < TN; ++j) sb[j] = MX ? (int)sb_lds[(wn + 32 * j + r) * 16] : unit_scale;
     // A fragments double-buffered: the reads for row tile i + 1 are issued
     // before the MFMAs of row tile i, so LDS latency hides behind them.
     i32x8 bf[TN], af[2];
@@ -505,7 +517,9 @@ hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const
   if (M <= 256 && K % kGemmK == 0)
     return mx ? launch_skinny<true>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st)
               : launch_skinny<false>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-  const bool dma = K % (2 * kGemmK) == 0 && (!mx || ((uintptr_t)sa % 4 == 0 && (uintptr_t)sb % 4 == 0));
+  // DMA pipeline: K % 512 == 0 so a 16-byte scale window never crosses a
+  // row of (K / 32) codes, and 16-byte aligned scale rows.
+  const bool dma = K % 512 == 0 && (!mx || ((uintptr_t)sa % 16 == 0 && (uintptr_t)sb % 16 == 0));
   if (dma) {
 #if GNQ_GEMM_WAVES == 8
     return mx ? launch_dma<true, 8, 4, 2>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c,

@@ -59,8 +59,10 @@ def _run(mx, aq, as_, bq, bs, M, N):
     return P.bits16(o)
 
 
+# kernels: M <= 256 with K % 64 == 0 -> skinny; K % 512 == 0 -> LDS-DMA
+# pipeline; otherwise the register-staged kernel
 SHAPES = [(1, 8, 64), (5, 300, 96), (256, 256, 128), (300, 520, 1056), (513, 257, 2048),
-          (64, 1024, 4096), (1000, 40, 160)]
+          (64, 1024, 4096), (1000, 40, 160), (300, 600, 4096), (257, 1100, 1536)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -79,7 +81,7 @@ def test_mxfp8_gemm_exact_cases(M, N, K):
     assert bad[0].size == 0, (bad[0][:5], bad[1][:5], got[bad][:5], want[bad][:5])
 
 
-@pytest.mark.parametrize("M,N,K", SHAPES[:5])
+@pytest.mark.parametrize("M,N,K", SHAPES[:5] + SHAPES[7:])
 def test_fp8_static_gemm_exact_cases(M, N, K):
     print(f"gemm static exact M={M} N={N} K={K}", flush=True)
     rng = np.random.default_rng(M * 5 + N * 3 + K)
@@ -99,7 +101,8 @@ def _tolerance_check(got_bits, exact, mag):
     assert worst <= 1.0
 
 
-@pytest.mark.parametrize("M,N,K", [(37, 300, 512), (256, 512, 4096), (129, 130, 1056)])
+@pytest.mark.parametrize("M,N,K", [(37, 300, 512), (256, 512, 4096), (129, 130, 1056), (512, 384, 4096),
+                                   (300, 260, 160)])
 def test_mxfp8_gemm_random(M, N, K):
     print(f"gemm mx random M={M} N={N} K={K}", flush=True)
     rng = np.random.default_rng(M + N + K)
@@ -112,9 +115,9 @@ def test_mxfp8_gemm_random(M, N, K):
     _tolerance_check(got, exact, mag)
 
 
-def test_fp8_static_gemm_random():
+@pytest.mark.parametrize("M,N,K", [(200, 300, 2048), (600, 300, 2048)])
+def test_fp8_static_gemm_random(M, N, K):
     rng = np.random.default_rng(17)
-    M, N, K = 200, 300, 2048
     aq, bq = _finite_codes(rng, (M, K)), _finite_codes(rng, (N, K))
     got = _run(False, aq, 0.0137, bq, 0.0021, M, N)
     exact, _ = O.gemm_fp8_static(aq, 0.0137, bq, 0.0021)
