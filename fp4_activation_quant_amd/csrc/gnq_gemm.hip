@@ -21,9 +21,11 @@
 // workgroup and 128 x 128 (4 x 4 MFMA tiles, 256 fp32 accumulators) per
 // wave; K advances 64 bytes per step through LDS stages (A and B tiles,
 // 64-byte rows whose 16-byte chunks are XOR-swizzled by row to spread LDS
-// banks).  Global loads of step k + 1 are issued before the
-// MFMAs of step k.  Rows beyond M or N are clamped on load and masked on
-// store; a K tail of 32 (K % 64 == 32) loads zeros for the missing block.
+// banks).  For K % 512 == 0 the stages are filled by direct global->LDS
+// DMA three steps ahead and the fragment reads are pipelined one step ahead
+// of the MFMAs; other K use a register-staged two-stage kernel.  Rows beyond
+// M or N are clamped on load and masked on store; a K tail of 32
+// (K % 64 == 32) loads zeros for the missing block.
 #include <atomic>
 
 #include "gnq_common.hpp"
@@ -51,14 +53,20 @@ __device__ __forceinline__ int gemm_lds_off(int row, int chunk) {
   return row * kGemmK + ((chunk ^ gemm_swz(row)) << 4);
 }
 
-// Output tile of workgroup b: tiles are taken in groups of up to 16 tile
-// rows, column by column inside a group, so the workgroups resident at one
-// time (one per CU) cover about a 16 x 16 block of tiles: 16 row tiles of A
-// and 16 column tiles of B in flight (at K = 8192, 64 MB, inside the 256 MB
-// Infinity Cache) instead of all of A against two columns of B.
-constexpr int kGemmGroupRows = 16;
+// Output tile of workgroup b.  Workgroups are dealt to the 8 XCDs (each
+// with its own L2) round-robin, b % 8; when the tile count is a multiple of
+// 8 the tiles are renumbered so that XCD x works through the contiguous
+// range of tiles x T / 8 .. (x + 1) T / 8 - 1.  In that order tiles go in
+// groups of 4 tile rows, column by column, so the ~32 workgroups an XCD
+// holds at once cover 4 row tiles of A and 8 column tiles of B: 12 operand
+// tiles shared in its L2 instead of 18 (2 x 16) with plain groups of 16 rows
+// (measured ~4% faster at 32768 x 8192 x 8192).
+constexpr int kGemmGroupRows = 4;
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ void gemm_tile_of_block(int b, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int tiles = tiles_m * tiles_n;
+  if (tiles % kXcds == 0) b = (b % kXcds) * (tiles / kXcds) + b / kXcds;
   const int per_group = kGemmGroupRows * tiles_n;
   const int first = (b / per_group) * kGemmGroupRows;
   const int rows = min(tiles_m - first, kGemmGroupRows);
@@ -198,17 +206,15 @@ gemm_fp8_tn(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     }
 }
 
-// Direct-to-LDS pipeline (K % 128 == 0): global_load_lds_dwordx4 moves each
+// Direct-to-LDS pipeline (K % 512 == 0): global_load_lds_dwordx4 moves each
 // wave's 1 KB segments straight into LDS (lane l fills bytes 16 l .. 16 l +
 // 15 of the segment, so lane l fetches the global chunk that the swizzled
-// layout puts there); kGemmStages stages keep kGemmStages - 1 steps in
-// flight with no register staging.  For MXFP8 the E8M0 codes arrive in
-// windows of 8 steps: one 16-byte DMA per row (blocks 16 j .. 16 j + 15 of
-// the row) into one of two LDS windows, issued a window ahead, so a row's
-// scale line is fetched once per 8 steps instead of once per step (4-byte
-// loads from 64 rows per instruction cost ~20% when issued every step).  One barrier per step: wait for this
-// step's own loads, barrier, then refill the stage every wave finished
-// reading in the previous step.
+// layout puts there), with no register staging, into kGemmStages stages.
+// For MXFP8 the E8M0 codes arrive in windows of 8 steps: one 16-byte DMA per
+// row (blocks 16 j .. 16 j + 15 of the row) into one of two LDS windows,
+// issued a window ahead, so a row's scale line is fetched once per 8 steps
+// instead of once per step (4-byte loads from 64 rows per instruction cost
+// ~20% when issued every step).  One barrier per step.
 constexpr int kGemmStages = 4;
 constexpr int kGemmStageBytes = 2 * kGemmOperandBytes;               // 32 KB
 constexpr int kGemmScaleSteps = 8;                                   // K steps per scale window
@@ -232,19 +238,28 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // NW waves per workgroup, each owning TM x TN MFMA tiles (32 x 32) of the
 // 256 x 256 workgroup tile; the 32 one-KB data segments and 8 scale segments
-// of a step are split evenly over the waves.
+// of a step are split evenly over the waves.  The LDS reads are pipelined
+// across steps: the fragments and scale codes of step k + 1 are read into a
+// second register set while the MFMAs of step k run, so after the barrier a
+// wave goes straight to its MFMAs.  The barrier of step k certifies that
+// step k + 1's DMA has landed (each wave waits for its own segments first)
+// and that every wave has consumed the reads of step k - 1, whose stage the
+// DMA issued after it refills (two steps of DMA ahead of the reads).
 template <bool MX, int NW, int TM, int TN>
 __global__ void __launch_bounds__(64 * NW)
 gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
-                const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
-                const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N,
-                int K, uint16_t *__restrict__ C, int tiles_m, int tiles, int unit_scale) {
+                 const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
+                 const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N,
+                 int K, uint16_t *__restrict__ C, int tiles_m, int tiles, int unit_scale) {
   static_assert((8 / TM) * (8 / TN) == NW, "waves must tile the 256 x 256 workgroup tile");
-  constexpr int kSegs = 32 / NW;        // data segments per wave per step
-  constexpr int kScaleSegs = 8 / NW;    // scale segments per wave per step
+  static_assert(kGemmStages == 4, "the waits below assume four stages");
+  constexpr int kSegs = 32 / NW;
+  constexpr int kScaleSegs = 8 / NW;
   constexpr int kWavesN = 8 / TN;
+  constexpr int kMfma = TM * TN, kUnits = TM + TN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, h = lane >> 5;
   int tm, tn;
   gemm_tile_of_block(blockIdx.x, tiles_m, tiles / tiles_m, tm, tn);
@@ -253,9 +268,6 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
   const int ksteps = K / kGemmK;
   const int kblocks = K / 32;
 
-  // Segment g = kSegs * wave + j of the step (g < 16: A, else B) holds rows
-  // 16 (g % 16) .. + 15 of its operand tile; lane l's slot is row
-  // 16 (g % 16) + l / 4, position l % 4, i.e. chunk (l % 4) ^ f(row).
   const bool fetch_b = kSegs * wave >= 16;
   const uint8_t *src = fetch_b ? B : A;
   const int lim = fetch_b ? N - 1 : M - 1, base_row = fetch_b ? n0 : m0;
@@ -267,8 +279,6 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     const int chunk = (lane & 3) ^ gemm_swz(row);
     seg_src[j] = src + (size_t)min(base_row + row, lim) * (size_t)K + chunk * 16;
   }
-  // Scale segment g = kScaleSegs * wave + t (g < 4: A) covers rows
-  // 64 (g % 4) + lane of its operand.
   const bool sfetch_b = kScaleSegs * wave >= 4;
   const int sseg0 = (kScaleSegs * wave) & 3;
   const uint8_t *sc_src[kScaleSegs];
@@ -278,72 +288,125 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     sc_src[t] = MX ? (sfetch_b ? SB : SA) + (size_t)min(base_s + 64 * (sseg0 + t) + lane, lim_s) * (size_t)kblocks
                    : nullptr;
   }
-  auto issue = [&](int ks) {
-    uint8_t *st = smem + (ks % kGemmStages) * kGemmStageBytes;
-    uint8_t *dst = st + (fetch_b ? kGemmOperandBytes : 0) + seg0 * 1024;
-    const int kb = ks * kGemmK;
-#pragma unroll
-    for (int j = 0; j < kSegs; ++j) dma16(seg_src[j] + kb, dst + j * 1024);
+  // DMA of step `from` into the stage of step ks (from != ks only for the
+  // refetches past the last step), and of scale window `from` into the
+  // buffer of window w.
+  auto issue_seg = [&](int ks, int from, int j) {
+    uint8_t *dst = smem + (ks % kGemmStages) * kGemmStageBytes + (fetch_b ? kGemmOperandBytes : 0) + seg0 * 1024;
+    dma16(seg_src[j] + from * kGemmK, dst + j * 1024);
   };
-  // Scale window w (steps 8 w .. 8 w + 7): segment t of this wave, 64 rows
-  // x 16 bytes, into window buffer w % 2.
-  auto issue_scales = [&](int w) {
+  auto issue = [&](int ks, int from) {
+#pragma unroll
+    for (int j = 0; j < kSegs; ++j) issue_seg(ks, from, j);
+  };
+  auto issue_scales = [&](int w, int from) {
     uint8_t *sdst = smem + kGemmScaleOff + (w & 1) * 2 * kGemmScaleWin + (sfetch_b ? kGemmScaleWin : 0) +
                     sseg0 * 1024;
 #pragma unroll
-    for (int t = 0; t < kScaleSegs; ++t) dma16(sc_src[t] + 16 * w, sdst + t * 1024);
+    for (int t = 0; t < kScaleSegs; ++t) dma16(sc_src[t] + 16 * from, sdst + t * 1024);
   };
-  // The wait below counts only data DMA of the later steps; a scale window
-  // issued in between only makes it stricter (loads complete in order).
-  constexpr int kPer = kSegs;
+  const int chunks = ksteps / 8;
 
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{0};
-
-  if (MX) issue_scales(0);
+  i32x8 af[2][TM], bf[2][TN];
+  int sa[2][TM], sb[2][TN];
+  // LDS byte offsets of this lane's fragment rows, one per (stage pair,
+  // operand, 16-byte half).  The swizzle of rows wm + 32 i + r depends on r
+  // only, so tile, stage-in-pair and slot constants become immediate offsets
+  // of the reads; the offsets are hidden from the optimizer, which otherwise
+  // folds every constant into its own address register (one per read of the
+  // unrolled steps) and spills.
+  const int swz = gemm_swz(r);
+  uint32_t fbase[2][2][2];
 #pragma unroll
-  for (int p = 0; p < kGemmStages - 1; ++p)
-    if (p < ksteps) issue(p);
-  for (int ks = 0; ks < ksteps; ++ks) {
-    if (ksteps - 1 - ks >= kGemmStages - 2) wait_vmcnt<kPer * (kGemmStages - 2)>();
-    else wait_vmcnt<0>();
-    // A plain barrier: the wait above already covers this step's loads of
-    // this wave (and the scale window, issued before them), and every LDS
-    // read of the previous step has been consumed by its MFMAs.  (A fenced
-    // barrier would drain all DMA in flight.)
-    asm volatile("s_barrier" ::: "memory");
-    if (ks + kGemmStages - 1 < ksteps) issue(ks + kGemmStages - 1);
-    // the next window goes into the buffer the previous window's steps used
-    if (MX && ks % kGemmScaleSteps == 0 && ks + kGemmScaleSteps < ksteps) issue_scales(ks / kGemmScaleSteps + 1);
-    const uint8_t *st = smem + (ks % kGemmStages) * kGemmStageBytes;
-    const uint8_t *a_lds = st, *b_lds = st + kGemmOperandBytes;
-    const uint8_t *sa_lds = smem + kGemmScaleOff + ((ks / kGemmScaleSteps) & 1) * 2 * kGemmScaleWin +
-                            (ks % kGemmScaleSteps) * 2 + h;
-    const uint8_t *sb_lds = sa_lds + kGemmScaleWin;
-    int sa[TM], sb[TN];
+  for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] = MX ? (int)sa_lds[(wm + 32 * i + r) * 16] : unit_scale;
+    for (int op = 0; op < 2; ++op)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sb[j] = MX ? (int)sb_lds[(wn + 32 * j + r) * 16] : unit_scale;
-    // A fragments double-buffered: the reads for row tile i + 1 are issued
-    // before the MFMAs of row tile i, so LDS latency hides behind them.
-    i32x8 bf[TN], af[2];
+      for (int hh = 0; hh < 2; ++hh) {
+        fbase[sp][op][hh] = (uint32_t)(sp * 2 * kGemmStageBytes + op * kGemmOperandBytes +
+                                       ((op ? wn : wm) + r) * kGemmK + (((2 * hh + h) ^ swz) << 4));
+        asm volatile("" : "+v"(fbase[sp][op][hh]));
+      }
+  uint32_t sbase[2];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bf[j] = gemm_frag(b_lds, wn + 32 * j + r, h);
-    af[0] = gemm_frag(a_lds, wm + r, h);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (i + 1 < TM) af[(i + 1) & 1] = gemm_frag(a_lds, wm + 32 * (i + 1) + r, h);
-      __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i & 1], bf[j], acc[i][j], 0, 0, 0,
-                                                                    sa[i], 0, sb[j]);
-    }
+  for (int op = 0; op < 2; ++op) {
+    sbase[op] = (uint32_t)(kGemmScaleOff + op * kGemmScaleWin + ((op ? wn : wm) + r) * 16 + h);
+    asm volatile("" : "+v"(sbase[op]));
   }
+  // Read unit u of step ks into register set p: B tile u for u < TN, else
+  // A tile u - TN, each with its scale code (window buffer offset `wofs`).
+  auto read_unit = [&](int ks, int p, int u, uint32_t wofs) {
+    const int stg = ks % kGemmStages;
+    const int op = u < TN ? 1 : 0, t = u < TN ? u : u - TN;
+    const uint32_t imm = (uint32_t)((stg & 1) * kGemmStageBytes + t * 32 * kGemmK);
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(smem + fbase[stg >> 1][op][0] + imm);
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(smem + fbase[stg >> 1][op][1] + imm);
+    const i32x8 f = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    const int sc = MX ? (int)smem[sbase[op] + wofs + (ks % kGemmScaleSteps) * 2 + t * 32 * 16] : unit_scale;
+    if (op) {
+      bf[p][t] = f;
+      sb[p][t] = sc;
+    } else {
+      af[p][t] = f;
+      sa[p][t] = sc;
+    }
+  };
+
+  // One K step: MFMAs of step ks from register set ks % 2, interleaved with
+  // the reads of step ks + 1 into the other set.  The body has no branch (a
+  // branch let the compiler sink the MFMAs below later steps' reads): the
+  // last steps' DMA refetches the final step into stages no step reads
+  // again, and the last step's reads fetch a stale stage and scale slot
+  // (inside LDS) that nothing uses.
+  auto step = [&](int ks, int u8, int c) {
+    const int p = u8 & 1;
+    const uint32_t wofs = (uint32_t)((((ks + 1) / kGemmScaleSteps) & 1) * 2 * kGemmScaleWin);
+    // step ks + 1's segments of this wave: at most step ks + 2's (and a
+    // scale window issued after them) may still be in flight
+    wait_vmcnt<kSegs>();
+    asm volatile("s_barrier" ::: "memory");
+    const int nk = ks + kGemmStages - 1, from = min(nk, ksteps - 1);
+    // The DMA of step ks + 3 (each instruction holds the wave for many
+    // cycles) and the reads of step ks + 1 are spread between the MFMAs
+    // so that one is always queued.
+#pragma unroll
+    for (int q = 0; q < kMfma; ++q) {
+      const int i = q / TN, j = q % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[p][i], bf[p][j], acc[i][j], 0, 0, 0,
+                                                                  sa[p][i], 0, sb[p][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      // unit u of the next step is read after MFMA u * kMfma / kUnits,
+      // DMA segment g after MFMA g * kMfma / kSegs + kMfma / (2 kSegs)
+#pragma unroll
+      for (int u = 0; u < kUnits; ++u)
+        if ((u * kMfma) / kUnits == q) read_unit(ks + 1, p ^ 1, u, wofs);
+#pragma unroll
+      for (int g = 0; g < kSegs; ++g)
+        if ((g * kMfma) / kSegs + kMfma / (2 * kSegs) == q) issue_seg(nk, from, g);
+      if (MX && u8 == 0 && q == kMfma - 1) issue_scales(c + 1, min(c + 1, chunks - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ksteps % 8 == 0 (K % 512 == 0): steps run in chunks of 8, so stage,
+  // register set and scale slot are compile-time per step.
+  if (MX) issue_scales(0, 0);
+#pragma unroll
+  for (int p = 0; p < kGemmStages - 1; ++p) issue(p, p);
+  wait_vmcnt<kSegs * (kGemmStages - 2)>();
+  asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+  for (int u = 0; u < kUnits; ++u) read_unit(0, 0, u, 0);
+  for (int c = 0; c < chunks; ++c) {
+#pragma unroll
+    for (int u8 = 0; u8 < 8; ++u8) step(8 * c + u8, u8, c);
+  }
+  wait_vmcnt<0>();   // the refetches land before the workgroup's LDS is released
 
   const float s = MX ? 1.0f : (*a_scale) * (*b_scale);
 #pragma unroll
@@ -378,8 +441,6 @@ inline hipError_t allow_dynamic_lds(const void *kernel, int bytes, std::atomic<u
   template __global__ void gemm_fp8_tn_dma<MX, NW, TM, TN>(                                      \
       const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *, const float *,         \
       const float *, int, int, int, uint16_t *, int, int, int);
-GNQ_GEMM_DMA_INST(true, 8, 4, 2)
-GNQ_GEMM_DMA_INST(false, 8, 4, 2)
 GNQ_GEMM_DMA_INST(true, 4, 4, 4)
 GNQ_GEMM_DMA_INST(false, 4, 4, 4)
 #undef GNQ_GEMM_DMA_INST
@@ -396,9 +457,6 @@ hipError_t launch_dma(const uint8_t *A, const uint8_t *SA, const uint8_t *B, con
   return hipGetLastError();
 }
 
-#ifndef GNQ_GEMM_WAVES
-#define GNQ_GEMM_WAVES 8
-#endif
 
 // Skinny GEMM for few activation rows (decode batches, M <= 64 per chunk):
 // the weight stream is the whole cost, so each workgroup owns 32 weight rows
@@ -521,17 +579,10 @@ hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const
   // row of (K / 32) codes, and 16-byte aligned scale rows.
   const bool dma = K % 512 == 0 && (!mx || ((uintptr_t)sa % 16 == 0 && (uintptr_t)sb % 16 == 0));
   if (dma) {
-#if GNQ_GEMM_WAVES == 8
-    return mx ? launch_dma<true, 8, 4, 2>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c,
-                                          tiles_m, tiles, st)
-              : launch_dma<false, 8, 4, 2>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
-                                           (uint16_t *)c, tiles_m, tiles, st);
-#else
     return mx ? launch_dma<true, 4, 4, 4>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c,
                                           tiles_m, tiles, st)
               : launch_dma<false, 4, 4, 4>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
                                            (uint16_t *)c, tiles_m, tiles, st);
-#endif
   }
   if (mx)
     hipLaunchKernelGGL((gemm_fp8_tn<true>), dim3(tiles), dim3(kGemmThreads), 0, st, A, SA, B, SB,

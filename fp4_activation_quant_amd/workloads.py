@@ -190,6 +190,7 @@ GEMM_WORKLOADS = {g.name: g for g in [
     GemmWorkload("gemm_mxfp8_m8192_n4096_k4096", "mxfp8", 8192, 4096, 4096, 8000),
     GemmWorkload("gemm_fp8_m8192_n4096_k4096", "fp8", 8192, 4096, 4096, 8100),
     GemmWorkload("gemm_mxfp8_m32768_n8192_k8192", "mxfp8", 32768, 8192, 8192, 8200),
+    GemmWorkload("gemm_fp8_m32768_n8192_k8192", "fp8", 32768, 8192, 8192, 8500),
     GemmWorkload("gemm_mxfp8_m256_n4096_k4096", "mxfp8", 256, 4096, 4096, 8300),
     GemmWorkload("gemm_mxfp8_m64_n4096_k4096", "mxfp8", 64, 4096, 4096, 8400),
 ]}

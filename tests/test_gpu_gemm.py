@@ -60,9 +60,12 @@ def _run(mx, aq, as_, bq, bs, M, N):
 
 
 # kernels: M <= 256 with K % 64 == 0 -> skinny; K % 512 == 0 -> LDS-DMA
-# pipeline; otherwise the register-staged kernel
+# pipeline; otherwise the register-staged kernel.  (2000, 300, 1024) and
+# (1030, 1800, 512) have a multiple of 8 output tiles (the per-XCD tile
+# renumbering) with ragged edges; K = 512 is a single chunk of 8 steps.
 SHAPES = [(1, 8, 64), (5, 300, 96), (256, 256, 128), (300, 520, 1056), (513, 257, 2048),
-          (64, 1024, 4096), (1000, 40, 160), (300, 600, 4096), (257, 1100, 1536)]
+          (64, 1024, 4096), (1000, 40, 160), (300, 600, 4096), (257, 1100, 1536),
+          (2000, 300, 1024), (1030, 1800, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
