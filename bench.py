@@ -237,7 +237,8 @@ def gemm_main(args):
                 "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
-    kernel = ("gemm_fp8_skinny" if M <= 256 and K % 64 == 0 else
+    kernel = ("gemm_fp8_decode" if M <= 256 and K % 2048 == 0 and K <= 16384 else
+              "gemm_fp8_skinny" if M <= 256 and K % 64 == 0 else
               "gemm_fp8_tn_dma" if K % 512 == 0 else "gemm_fp8_tn")
     out = {
         "metric": "consumer GEMM TFLOP/s (quantized activation x quantized weight -> bf16), 1 GPU",

@@ -561,6 +561,180 @@ hipError_t launch_skinny(const uint8_t *A, const uint8_t *SA, const uint8_t *B, 
   return hipGetLastError();
 }
 
+// Decode-size GEMM (few activation rows, K % 2048 == 0, K <= 16384): a
+// workgroup owns an MT x NT output tile (MT activation rows, NT weight rows,
+// 8 to 32) and its 4 waves split K into contiguous quarters.  Each
+// wave streams its quarter through a private ring of S LDS stages of 128
+// K-bytes (two MFMA steps) by global_load_lds_dwordx4, eight lanes per
+// 128-byte line, so one instruction touches 8 cache lines; loading MFMA
+// fragments straight from global memory (lane l -> row l % 32) touches 32
+// lines per instruction and left the skinny kernel bound by the address
+// unit at ~16 GB/s per workgroup.  A wave needs no barrier: it waits only
+// for its own DMA.  The E8M0 codes of the wave's quarter (K / 128 bytes per
+// row) arrive by 16-byte DMA before the data.  Tiles narrower than the
+// 32 x 32 MFMA repeat their rows in the unused lanes (rows r % MT, r % NT),
+// whose outputs are dropped; narrow tiles give more workgroups for few rows.
+// The four partial tiles are summed through LDS in a fixed order.
+constexpr int kDecWaves = 4;
+constexpr int kDecStepK = 128;                                 // K bytes per stage (two MFMA steps)
+constexpr int kDecMaxK = 16384;
+constexpr int kDecDataBytes = 128 * 1024;                      // stage rings of the 4 waves
+
+__host__ __device__ constexpr int dec_lds_bytes(int K) { return kDecDataBytes + kDecWaves * (K / 2); }
+
+// Chunk swizzle of a 128-byte LDS row: chunk c of row r at slot c ^ g(r),
+// g(r) = (r / 2) % 8, so 16-byte reads of 16 consecutive rows at one chunk
+// hit 16 distinct slots modulo 256 bytes.
+__device__ __forceinline__ int dec_swz(int row) { return (row >> 1) & 7; }
+
+// Wait until at most `out` stages of PER loads each are in flight.
+template <int PER, int MAXO>
+__device__ __forceinline__ void dec_wait(int out) {
+  if constexpr (MAXO == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (out >= MAXO) wait_vmcnt<PER * MAXO>();
+    else dec_wait<PER, MAXO - 1>(out);
+  }
+}
+
+template <bool MX, int MT, int NT, int S>
+__global__ void __launch_bounds__(64 * kDecWaves)
+gemm_fp8_decode(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
+                const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
+                const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N, int K,
+                uint16_t *__restrict__ C, int unit_scale) {
+  constexpr int kBSeg = NT / 8, kASeg = MT / 8, kSeg = kBSeg + kASeg;   // 1 KB DMA segments per stage
+  constexpr int kStage = kSeg * 1024;
+  static_assert(kDecWaves * S * kStage <= kDecDataBytes, "stage rings exceed their LDS");
+  static_assert(NT + MT <= 64, "scale rows");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 31, h = lane >> 5;
+  const int n0 = blockIdx.x * NT, m0 = blockIdx.y * MT;
+  const int kq = K / kDecWaves;                 // this wave's K range: [wave kq, (wave + 1) kq)
+  const int J = kq / kDecStepK;                 // stages of the range (>= 4: K >= 2048)
+  const int kblocks = K / 32;
+  uint8_t *wl = smem + wave * S * kStage;
+
+  // DMA sources: segment i < kBSeg fills weight rows 8 i .. 8 i + 7 of a
+  // stage, the others activation rows 8 (i - kBSeg) ..; lane l takes row
+  // 8 i + l / 8 and fetches the global chunk (l % 8) ^ g(row), which lands
+  // in slot l % 8.
+  const uint8_t *src[kSeg];
+#pragma unroll
+  for (int i = 0; i < kSeg; ++i) {
+    const int q = 8 * (i < kBSeg ? i : i - kBSeg) + (lane >> 3);
+    const int c = (lane & 7) ^ dec_swz(q);
+    const size_t row = i < kBSeg ? (size_t)min(n0 + q, N - 1) : (size_t)min(m0 + q, M - 1);
+    src[i] = (i < kBSeg ? B : A) + row * (size_t)K + (size_t)wave * kq + c * 16;
+  }
+  auto issue = [&](int j) {
+    uint8_t *dst = wl + (j % S) * kStage;
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) dma16(src[i] + j * kDecStepK, dst + i * 1024);
+  };
+  // Scale codes of the wave's range: 16-byte piece t of scale row q (q < NT:
+  // weight row n0 + q, NT <= q < NT + MT: activation row m0 + q - NT; the
+  // remaining lanes repeat a weight row) at sc + t * 1024 + q * 16.
+  uint8_t *sc = smem + kDecDataBytes + wave * (K / 2);
+  if (MX) {
+    const int q = lane < NT + MT ? lane : 0;
+    const uint8_t *ssrc = q < NT ? SB + (size_t)min(n0 + q, N - 1) * kblocks
+                                 : SA + (size_t)min(m0 + q - NT, M - 1) * kblocks;
+    ssrc += wave * (kq / 32);
+    for (int t = 0; t < kq / 512; ++t) dma16(ssrc + 16 * t, sc + t * 1024);
+  }
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j)
+    if (j < J) issue(j);
+
+  f32x16 acc = f32x16{0};
+  const int rb = r % NT, ra = r % MT;
+  const int boff = rb * kDecStepK, aoff = kBSeg * 1024 + ra * kDecStepK;
+  const int gb = dec_swz(rb), ga = dec_swz(ra);
+  for (int j = 0; j < J; ++j) {
+    // stage j of this wave: the later stages already issued may stay in flight
+    dec_wait<kSeg, S - 2>(min(J - 1, j + S - 2) - j);
+    if (j + S - 1 < J) issue(j + S - 1);
+    const uint8_t *st = wl + (j % S) * kStage;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 b0 = *reinterpret_cast<const u32x4 *>(st + boff + (((4 * t + h) ^ gb) << 4));
+      const u32x4 b1 = *reinterpret_cast<const u32x4 *>(st + boff + (((4 * t + 2 + h) ^ gb) << 4));
+      const u32x4 a0 = *reinterpret_cast<const u32x4 *>(st + aoff + (((4 * t + h) ^ ga) << 4));
+      const u32x4 a1 = *reinterpret_cast<const u32x4 *>(st + aoff + (((4 * t + 2 + h) ^ ga) << 4));
+      const i32x8 bf = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+      const i32x8 af = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+      int sa = unit_scale, sb = unit_scale;
+      if (MX) {
+        const int blk = 4 * j + 2 * t + h;      // 32-element block within the wave's range
+        sb = sc[(blk >> 4) * 1024 + rb * 16 + (blk & 15)];
+        sa = sc[(blk >> 4) * 1024 + (NT + ra) * 16 + (blk & 15)];
+      }
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc, 0, 0, 0, sa, 0, sb);
+    }
+  }
+
+  // partials: red[(wave * 16 + v) * 64 + lane], over the (now idle) stages
+  __syncthreads();
+  float *red = reinterpret_cast<float *>(smem);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) red[(wave * 16 + v) * 64 + lane] = acc[v];
+  __syncthreads();
+  const float s = MX ? 1.0f : (*a_scale) * (*b_scale);
+#pragma unroll
+  for (int e = tid; e < 16 * 64; e += 64 * kDecWaves) {
+    const int v = e >> 6, l = e & 63;
+    const int tr = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3), tc = l & 31;
+    const int row = m0 + tr, col = n0 + tc;
+    if (tr < MT && tc < NT && row < M && col < N) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) sum += red[w * 16 * 64 + e];
+      C[(size_t)row * (size_t)N + col] = (uint16_t)(Bf16::pack(sum * s, 0.0f) & 0xffffu);
+    }
+  }
+}
+
+#define GNQ_GEMM_DEC_INST(MX, MT, NT, S)                                                          \
+  template __global__ void gemm_fp8_decode<MX, MT, NT, S>(                                        \
+      const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *, const float *,         \
+      const float *, int, int, int, uint16_t *, int);
+GNQ_GEMM_DEC_INST(true, 32, 16, 5)
+GNQ_GEMM_DEC_INST(false, 32, 16, 5)
+GNQ_GEMM_DEC_INST(true, 32, 32, 4)
+GNQ_GEMM_DEC_INST(false, 32, 32, 4)
+#undef GNQ_GEMM_DEC_INST
+
+template <bool MX, int MT, int NT, int S>
+hipError_t launch_decode_tile(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
+                              const float *a_scale, const float *b_scale, int M, int N, int K, uint16_t *C,
+                              hipStream_t st) {
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e =
+      allow_dynamic_lds((const void *)gemm_fp8_decode<MX, MT, NT, S>, dec_lds_bytes(kDecMaxK), lds_set);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((N + NT - 1) / NT), (unsigned)((M + MT - 1) / MT));
+  hipLaunchKernelGGL((gemm_fp8_decode<MX, MT, NT, S>), grid, dim3(64 * kDecWaves), dec_lds_bytes(K), st, A, SA,
+                     B, SB, a_scale, b_scale, M, N, K, C, 127);
+  return hipGetLastError();
+}
+
+// Tile: 32 x 32 unless that leaves fewer than 192 workgroups, then 32 x 16
+// (one ring each; 8-row tiles with deeper rings measured no faster: the
+// weight stream already runs at the HBM rate past a fixed ~3 us of launch,
+// first round trip and reduction).
+template <bool MX>
+hipError_t launch_decode(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
+                         const float *a_scale, const float *b_scale, int M, int N, int K, uint16_t *C,
+                         hipStream_t st) {
+  const long wide = (long)((N + 31) / 32) * ((M + 31) / 32);
+  if (wide < 192) return launch_decode_tile<MX, 32, 16, 5>(A, SA, B, SB, a_scale, b_scale, M, N, K, C, st);
+  return launch_decode_tile<MX, 32, 32, 4>(A, SA, B, SB, a_scale, b_scale, M, N, K, C, st);
+}
+
 hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,
                     const float *a_scale, const float *b_scale, int64_t M, int64_t N, int64_t K,
                     void *c, hipStream_t st) {
@@ -570,8 +744,11 @@ hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const
   const uint8_t *A = (const uint8_t *)a, *B = (const uint8_t *)b;
   const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
   // Few activation rows: the large tiles would leave most CUs idle (one
-  // workgroup per 256 output columns); the skinny kernel streams the weight
-  // with N / 32 x M / 64 workgroups.
+  // workgroup per 256 output columns); the decode kernel (or, for K it does
+  // not take, the skinny one) streams the weight with small tiles.
+  if (M <= 256 && K % 2048 == 0 && K <= kDecMaxK && (!mx || ((uintptr_t)sa % 16 == 0 && (uintptr_t)sb % 16 == 0)))
+    return mx ? launch_decode<true>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st)
+              : launch_decode<false>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st);
   if (M <= 256 && K % kGemmK == 0)
     return mx ? launch_skinny<true>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st)
               : launch_skinny<false>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st);

@@ -193,6 +193,8 @@ GEMM_WORKLOADS = {g.name: g for g in [
     GemmWorkload("gemm_fp8_m32768_n8192_k8192", "fp8", 32768, 8192, 8192, 8500),
     GemmWorkload("gemm_mxfp8_m256_n4096_k4096", "mxfp8", 256, 4096, 4096, 8300),
     GemmWorkload("gemm_mxfp8_m64_n4096_k4096", "mxfp8", 64, 4096, 4096, 8400),
+    GemmWorkload("gemm_mxfp8_m1_n4096_k4096", "mxfp8", 1, 4096, 4096, 8600),
+    GemmWorkload("gemm_fp8_m64_n4096_k4096", "fp8", 64, 4096, 4096, 8700),
 ]}
 
 
