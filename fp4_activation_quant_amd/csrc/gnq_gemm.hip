@@ -562,25 +562,31 @@ hipError_t launch_skinny(const uint8_t *A, const uint8_t *SA, const uint8_t *B, 
 }
 
 // Decode-size GEMM (few activation rows, K % 2048 == 0, K <= 16384): a
-// workgroup owns an MT x NT output tile (MT activation rows, NT weight rows,
-// 8 to 32) and its 4 waves split K into contiguous quarters.  Each
-// wave streams its quarter through a private ring of S LDS stages of 128
-// K-bytes (two MFMA steps) by global_load_lds_dwordx4, eight lanes per
-// 128-byte line, so one instruction touches 8 cache lines; loading MFMA
-// fragments straight from global memory (lane l -> row l % 32) touches 32
-// lines per instruction and left the skinny kernel bound by the address
-// unit at ~16 GB/s per workgroup.  A wave needs no barrier: it waits only
-// for its own DMA.  The E8M0 codes of the wave's quarter (K / 128 bytes per
-// row) arrive by 16-byte DMA before the data.  Tiles narrower than the
-// 32 x 32 MFMA repeat their rows in the unused lanes (rows r % MT, r % NT),
-// whose outputs are dropped; narrow tiles give more workgroups for few rows.
-// The four partial tiles are summed through LDS in a fixed order.
-constexpr int kDecWaves = 4;
+// workgroup owns an MT x NT output tile (MT activation rows, NT weight rows)
+// and its NW waves split K into contiguous ranges.  Each wave streams its
+// range through a private ring of S LDS stages of 128 K-bytes (two MFMA
+// steps) by global_load_lds_dwordx4, eight lanes per 128-byte line, so one
+// instruction touches 8 cache lines; loading MFMA fragments straight from
+// global memory (lane l -> row l % 32) touches 32 lines per instruction and
+// left the skinny kernel bound by the address unit at ~16 GB/s per
+// workgroup.  A wave needs no barrier: it waits only for its own DMA.  The
+// E8M0 codes of the wave's range (K / 32 / NW bytes per row) arrive by
+// 16-byte DMA before the data.  A tile narrower than the 32 x 32 MFMA
+// repeats its rows in the unused lanes (rows r % MT, r % NT), whose outputs
+// are dropped: narrow tiles give more workgroups for few rows, wide ones
+// fewer re-reads of both operands.  The NW partial tiles are summed through
+// LDS in a fixed order.
 constexpr int kDecStepK = 128;                                 // K bytes per stage (two MFMA steps)
 constexpr int kDecMaxK = 16384;
-constexpr int kDecDataBytes = 128 * 1024;                      // stage rings of the 4 waves
+constexpr int kDecDataBytes = 128 * 1024;                      // stage rings of the waves
+constexpr int kDecLdsMax = 160 * 1024;
 
-__host__ __device__ constexpr int dec_lds_bytes(int K) { return kDecDataBytes + kDecWaves * (K / 2); }
+// scale rows (weight then activation) per 16-byte piece: 64 per DMA part
+__host__ __device__ constexpr int dec_scale_parts(int MT, int NT) { return (MT + NT + 63) / 64; }
+// 16-byte pieces per row per wave: K / NW / 512; one KB per part per piece
+__host__ __device__ constexpr int dec_lds_bytes(int K, int MT, int NT) {
+  return kDecDataBytes + 2 * K * dec_scale_parts(MT, NT);
+}
 
 // Chunk swizzle of a 128-byte LDS row: chunk c of row r at slot c ^ g(r),
 // g(r) = (r / 2) % 8, so 16-byte reads of 16 consecutive rows at one chunk
@@ -598,23 +604,26 @@ __device__ __forceinline__ void dec_wait(int out) {
   }
 }
 
-template <bool MX, int MT, int NT, int S>
-__global__ void __launch_bounds__(64 * kDecWaves)
+template <bool MX, int NW, int MT, int NT, int S>
+__global__ void __launch_bounds__(64 * NW)
 gemm_fp8_decode(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
                 const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
                 const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N, int K,
                 uint16_t *__restrict__ C, int unit_scale) {
   constexpr int kBSeg = NT / 8, kASeg = MT / 8, kSeg = kBSeg + kASeg;   // 1 KB DMA segments per stage
   constexpr int kStage = kSeg * 1024;
-  static_assert(kDecWaves * S * kStage <= kDecDataBytes, "stage rings exceed their LDS");
-  static_assert(NT + MT <= 64, "scale rows");
+  constexpr int kTM = MT >= 32 ? MT / 32 : 1, kTN = NT >= 32 ? NT / 32 : 1;   // MFMA tiles
+  constexpr int kParts = dec_scale_parts(MT, NT);
+  static_assert(NW * S * kStage <= kDecDataBytes, "stage rings exceed their LDS");
+  static_assert(NW * kTM * kTN * 16 * 64 * 4 <= kDecDataBytes, "partials exceed the ring LDS");
+  static_assert(kSeg * (S - 2) < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, h = lane >> 5;
   const int n0 = blockIdx.x * NT, m0 = blockIdx.y * MT;
-  const int kq = K / kDecWaves;                 // this wave's K range: [wave kq, (wave + 1) kq)
-  const int J = kq / kDecStepK;                 // stages of the range (>= 4: K >= 2048)
+  const int kq = K / NW;                        // this wave's K range: [wave kq, (wave + 1) kq)
+  const int J = kq / kDecStepK;                 // stages of the range
   const int kblocks = K / 32;
   uint8_t *wl = smem + wave * S * kStage;
 
@@ -636,24 +645,44 @@ gemm_fp8_decode(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     for (int i = 0; i < kSeg; ++i) dma16(src[i] + j * kDecStepK, dst + i * 1024);
   };
   // Scale codes of the wave's range: 16-byte piece t of scale row q (q < NT:
-  // weight row n0 + q, NT <= q < NT + MT: activation row m0 + q - NT; the
-  // remaining lanes repeat a weight row) at sc + t * 1024 + q * 16.
-  uint8_t *sc = smem + kDecDataBytes + wave * (K / 2);
+  // weight row n0 + q, NT <= q < NT + MT: activation row m0 + q - NT; lanes
+  // past the last row repeat a weight row) at sc + (t kParts + q / 64) KB +
+  // (q % 64) * 16.
+  const int pieces = kq / 512;
+  uint8_t *sc = smem + kDecDataBytes + wave * pieces * kParts * 1024;
   if (MX) {
-    const int q = lane < NT + MT ? lane : 0;
-    const uint8_t *ssrc = q < NT ? SB + (size_t)min(n0 + q, N - 1) * kblocks
-                                 : SA + (size_t)min(m0 + q - NT, M - 1) * kblocks;
-    ssrc += wave * (kq / 32);
-    for (int t = 0; t < kq / 512; ++t) dma16(ssrc + 16 * t, sc + t * 1024);
+#pragma unroll
+    for (int u = 0; u < kParts; ++u) {
+      const int q = 64 * u + lane < NT + MT ? 64 * u + lane : 0;
+      const uint8_t *ssrc = q < NT ? SB + (size_t)min(n0 + q, N - 1) * kblocks
+                                   : SA + (size_t)min(m0 + q - NT, M - 1) * kblocks;
+      ssrc += wave * (kq / 32);
+      for (int t = 0; t < pieces; ++t) dma16(ssrc + 16 * t, sc + (t * kParts + u) * 1024);
+    }
   }
 #pragma unroll
   for (int j = 0; j < S - 1; ++j)
     if (j < J) issue(j);
 
-  f32x16 acc = f32x16{0};
-  const int rb = r % NT, ra = r % MT;
-  const int boff = rb * kDecStepK, aoff = kBSeg * 1024 + ra * kDecStepK;
-  const int gb = dec_swz(rb), ga = dec_swz(ra);
+  f32x16 acc[kTM][kTN];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) acc[i][j] = f32x16{0};
+  int brow[kTN], arow[kTM];
+#pragma unroll
+  for (int j = 0; j < kTN; ++j) brow[j] = NT >= 32 ? 32 * j + r : r % NT;
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) arow[i] = MT >= 32 ? 32 * i + r : r % MT;
+  auto frag = [&](const uint8_t *base, int row, int t) {
+    const int g = dec_swz(row);
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(base + row * kDecStepK + (((4 * t + h) ^ g) << 4));
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(base + row * kDecStepK + (((4 * t + 2 + h) ^ g) << 4));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto code = [&](int q, int blk) {
+    return (int)sc[((blk >> 4) * kParts + (q >> 6)) * 1024 + (q & 63) * 16 + (blk & 15)];
+  };
   for (int j = 0; j < J; ++j) {
     // stage j of this wave: the later stages already issued may stay in flight
     dec_wait<kSeg, S - 2>(min(J - 1, j + S - 2) - j);
@@ -661,78 +690,97 @@ gemm_fp8_decode(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     const uint8_t *st = wl + (j % S) * kStage;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const u32x4 b0 = *reinterpret_cast<const u32x4 *>(st + boff + (((4 * t + h) ^ gb) << 4));
-      const u32x4 b1 = *reinterpret_cast<const u32x4 *>(st + boff + (((4 * t + 2 + h) ^ gb) << 4));
-      const u32x4 a0 = *reinterpret_cast<const u32x4 *>(st + aoff + (((4 * t + h) ^ ga) << 4));
-      const u32x4 a1 = *reinterpret_cast<const u32x4 *>(st + aoff + (((4 * t + 2 + h) ^ ga) << 4));
-      const i32x8 bf = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-      const i32x8 af = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-      int sa = unit_scale, sb = unit_scale;
-      if (MX) {
-        const int blk = 4 * j + 2 * t + h;      // 32-element block within the wave's range
-        sb = sc[(blk >> 4) * 1024 + rb * 16 + (blk & 15)];
-        sa = sc[(blk >> 4) * 1024 + (NT + ra) * 16 + (blk & 15)];
+      const int blk = 4 * j + 2 * t + h;        // 32-element block within the wave's range
+      i32x8 bf[kTN], af[kTM];
+      int sb[kTN], sa[kTM];
+#pragma unroll
+      for (int jj = 0; jj < kTN; ++jj) {
+        bf[jj] = frag(st, brow[jj], t);
+        sb[jj] = MX ? code(brow[jj], blk) : unit_scale;
       }
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc, 0, 0, 0, sa, 0, sb);
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        af[i] = frag(st + kBSeg * 1024, arow[i], t);
+        sa[i] = MX ? code(NT + arow[i], blk) : unit_scale;
+      }
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < kTN; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[jj], acc[i][jj], 0, 0, 0, sa[i],
+                                                                       0, sb[jj]);
     }
   }
 
-  // partials: red[(wave * 16 + v) * 64 + lane], over the (now idle) stages
+  // partials: red[((wave * kTM + i) * kTN + j) * 1024 + v * 64 + lane] over
+  // the (now idle) stage rings
   __syncthreads();
   float *red = reinterpret_cast<float *>(smem);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) red[(wave * 16 + v) * 64 + lane] = acc[v];
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < kTN; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[((wave * kTM + i) * kTN + jj) * 1024 + v * 64 + lane] = acc[i][jj][v];
   __syncthreads();
   const float s = MX ? 1.0f : (*a_scale) * (*b_scale);
-#pragma unroll
-  for (int e = tid; e < 16 * 64; e += 64 * kDecWaves) {
-    const int v = e >> 6, l = e & 63;
-    const int tr = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3), tc = l & 31;
+  constexpr int kOut = kTM * kTN * 1024;
+  for (int e = tid; e < kOut; e += 64 * NW) {
+    const int tile = e >> 10, v = (e >> 6) & 15, l = e & 63;
+    const int tr = 32 * (tile / kTN) + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+    const int tc = 32 * (tile % kTN) + (l & 31);
     const int row = m0 + tr, col = n0 + tc;
     if (tr < MT && tc < NT && row < M && col < N) {
       float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) sum += red[w * 16 * 64 + e];
+      for (int w = 0; w < NW; ++w) sum += red[w * kOut + e];
       C[(size_t)row * (size_t)N + col] = (uint16_t)(Bf16::pack(sum * s, 0.0f) & 0xffffu);
     }
   }
 }
 
-#define GNQ_GEMM_DEC_INST(MX, MT, NT, S)                                                          \
-  template __global__ void gemm_fp8_decode<MX, MT, NT, S>(                                        \
+#define GNQ_GEMM_DEC_INST(MX, NW, MT, NT, S)                                                      \
+  template __global__ void gemm_fp8_decode<MX, NW, MT, NT, S>(                                    \
       const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *, const float *,         \
       const float *, int, int, int, uint16_t *, int);
-GNQ_GEMM_DEC_INST(true, 32, 16, 5)
-GNQ_GEMM_DEC_INST(false, 32, 16, 5)
-GNQ_GEMM_DEC_INST(true, 32, 32, 4)
-GNQ_GEMM_DEC_INST(false, 32, 32, 4)
+GNQ_GEMM_DEC_INST(true, 4, 32, 16, 5)
+GNQ_GEMM_DEC_INST(false, 4, 32, 16, 5)
+GNQ_GEMM_DEC_INST(true, 4, 32, 32, 4)
+GNQ_GEMM_DEC_INST(false, 4, 32, 32, 4)
+GNQ_GEMM_DEC_INST(true, 2, 64, 64, 4)
+GNQ_GEMM_DEC_INST(false, 2, 64, 64, 4)
 #undef GNQ_GEMM_DEC_INST
 
-template <bool MX, int MT, int NT, int S>
+template <bool MX, int NW, int MT, int NT, int S>
 hipError_t launch_decode_tile(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
                               const float *a_scale, const float *b_scale, int M, int N, int K, uint16_t *C,
                               hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e =
-      allow_dynamic_lds((const void *)gemm_fp8_decode<MX, MT, NT, S>, dec_lds_bytes(kDecMaxK), lds_set);
+  const hipError_t e = allow_dynamic_lds((const void *)gemm_fp8_decode<MX, NW, MT, NT, S>, kDecLdsMax, lds_set);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((N + NT - 1) / NT), (unsigned)((M + MT - 1) / MT));
-  hipLaunchKernelGGL((gemm_fp8_decode<MX, MT, NT, S>), grid, dim3(64 * kDecWaves), dec_lds_bytes(K), st, A, SA,
-                     B, SB, a_scale, b_scale, M, N, K, C, 127);
+  hipLaunchKernelGGL((gemm_fp8_decode<MX, NW, MT, NT, S>), grid, dim3(64 * NW), dec_lds_bytes(K, MT, NT), st, A,
+                     SA, B, SB, a_scale, b_scale, M, N, K, C, 127);
   return hipGetLastError();
 }
 
-// Tile: 32 x 32 unless that leaves fewer than 192 workgroups, then 32 x 16
-// (one ring each; 8-row tiles with deeper rings measured no faster: the
-// weight stream already runs at the HBM rate past a fixed ~3 us of launch,
-// first round trip and reduction).
+// Tile choice (measured on 4096- and 8192-wide weights, K 4096 and 8192):
+// 64 x 64 with 2 waves when that still gives >= 256 workgroups (M = 256:
+// 20-30% faster than 32 x 32, which re-reads both operands twice as often;
+// it needs K <= 8192 for its scale slab); else 32 x 32 unless that leaves
+// fewer than 192 workgroups, then 32 x 16.  8-row tiles with deeper rings
+// measured no faster for one row: the weight stream already runs at the HBM
+// rate past a fixed ~3 us of launch, first round trip and reduction.
 template <bool MX>
 hipError_t launch_decode(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
                          const float *a_scale, const float *b_scale, int M, int N, int K, uint16_t *C,
                          hipStream_t st) {
-  const long wide = (long)((N + 31) / 32) * ((M + 31) / 32);
-  if (wide < 192) return launch_decode_tile<MX, 32, 16, 5>(A, SA, B, SB, a_scale, b_scale, M, N, K, C, st);
-  return launch_decode_tile<MX, 32, 32, 4>(A, SA, B, SB, a_scale, b_scale, M, N, K, C, st);
+  const long wide = (long)((N + 63) / 64) * ((M + 63) / 64);
+  if (K <= 8192 && wide >= 256)
+    return launch_decode_tile<MX, 2, 64, 64, 4>(A, SA, B, SB, a_scale, b_scale, M, N, K, C, st);
+  const long mid = (long)((N + 31) / 32) * ((M + 31) / 32);
+  if (mid < 192) return launch_decode_tile<MX, 4, 32, 16, 5>(A, SA, B, SB, a_scale, b_scale, M, N, K, C, st);
+  return launch_decode_tile<MX, 4, 32, 32, 4>(A, SA, B, SB, a_scale, b_scale, M, N, K, C, st);
 }
 
 hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,

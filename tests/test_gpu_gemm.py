@@ -64,14 +64,15 @@ def _run(mx, aq, as_, bq, bs, M, N):
 # pipeline; otherwise the register-staged kernel.  (2000, 300, 1024) and
 # (1030, 1800, 512) have a multiple of 8 output tiles (the per-XCD tile
 # renumbering) with ragged edges; K = 512 is a single chunk of 8 steps.
-# The decode shapes cover both of its tiles (32 x 16 when 32 x 32 tiles
-# would number fewer than 192, else 32 x 32) with ragged edges, and K from
-# 2048 (four stages per wave) to 16384 (the largest scale slab).
+# The decode shapes cover each of its tiles (64 x 64 when those number
+# >= 256 and K <= 8192, else 32 x 16 when 32 x 32 tiles would number fewer
+# than 192, else 32 x 32) with ragged edges, and K from 2048 (four stages
+# per wave) to 16384 (the largest scale slab).
 SHAPES = [(1, 8, 64), (5, 300, 96), (256, 256, 128), (300, 520, 1056), (513, 257, 2048),
           (64, 1024, 4096), (1000, 40, 160), (300, 600, 4096), (257, 1100, 1536),
           (2000, 300, 1024), (1030, 1800, 512),
           (1, 4096, 2048), (33, 300, 2048), (7, 1000, 6144), (250, 130, 8192), (3, 64, 16384),
-          (20, 200, 2048), (9, 50, 4096), (70, 2100, 2048)]
+          (20, 200, 2048), (9, 50, 4096), (70, 2100, 2048), (200, 5000, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -111,7 +112,8 @@ def _tolerance_check(got_bits, exact, mag):
 
 
 @pytest.mark.parametrize("M,N,K", [(37, 300, 512), (256, 512, 4096), (129, 130, 1056), (512, 384, 4096),
-                                   (300, 260, 160), (17, 96, 16384), (1, 333, 4096), (100, 2000, 4096)])
+                                   (300, 260, 160), (17, 96, 16384), (1, 333, 4096), (100, 2000, 4096),
+                                   (250, 4100, 4096)])
 def test_mxfp8_gemm_random(M, N, K):
     print(f"gemm mx random M={M} N={N} K={K}", flush=True)
     rng = np.random.default_rng(M + N + K)
