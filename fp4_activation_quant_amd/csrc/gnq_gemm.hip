@@ -222,12 +222,9 @@ constexpr int kGemmScaleWin = kGemmTile * 2 * kGemmScaleSteps;       // 4 KB per
 constexpr int kGemmScaleOff = kGemmStages * kGemmStageBytes;         // two windows after the stages
 constexpr int kGemmDmaLds = kGemmScaleOff + 2 * 2 * kGemmScaleWin;   // 144 KB
 
-// Global -> LDS DMA of 16 or 4 bytes per lane (lane l writes lds + size * l).
+// Global -> LDS DMA of 16 bytes per lane (lane l writes lds + 16 l).
 __device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const uint8_t *g, uint8_t *lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
 }
 
 template <int N>
@@ -248,9 +245,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <bool MX, int NW, int TM, int TN>
 __global__ void __launch_bounds__(64 * NW)
 gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
-                 const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
-                 const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N,
-                 int K, uint16_t *__restrict__ C, int tiles_m, int tiles, int unit_scale) {
+                const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
+                const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N,
+                int K, uint16_t *__restrict__ C, int tiles_m, int tiles, int unit_scale) {
   static_assert((8 / TM) * (8 / TN) == NW, "waves must tile the 256 x 256 workgroup tile");
   static_assert(kGemmStages == 4, "the waits below assume four stages");
   constexpr int kSegs = 32 / NW;
