@@ -39,5 +39,5 @@ from .norm_quant import (  # noqa: F401
     gemma_add_rms_norm_quant, add_rms_norm_quant,
 )
 from .gemm import (  # noqa: F401
-    dequant_fp8_static, dequant_mxfp8, gemm_f64, gemm_fp8_static, gemm_mxfp8,
+    dequant_fp8_static, dequant_mxfp8, dequant_nvfp4, gemm_f64, gemm_fp8_static, gemm_mxfp8, gemm_nvfp4,
 )

@@ -104,3 +104,99 @@ def test_bad_scale_shapes_raise():
         O.dequant_mxfp8(np.zeros((2, 48), np.uint8), np.zeros((2, 1), np.uint8))
     with pytest.raises(ValueError):
         O.dequant_mxfp8(np.zeros((2, 64), np.uint8), np.zeros((2, 3), np.uint8))
+
+
+# ---- NVFP4 consumer -------------------------------------------------------
+
+_E2M1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+
+
+def _frac_e2m1(c):
+    return (-1 if c & 8 else 1) * _E2M1[c & 7]
+
+
+def _nvfp4_operand(rng, rows, K, scale_codes):
+    """Random packed E2M1 codes and a 128x4-tiled scale buffer whose block
+    scales are drawn from ``scale_codes``; also returns the row-major scale
+    codes."""
+    q = rng.integers(0, 256, size=(rows, K // 2), dtype=np.int64).astype(np.uint8)
+    S = np.asarray(scale_codes, np.uint8)[rng.integers(0, len(scale_codes), size=(rows, K // 16))]
+    buf = np.zeros(int(np.prod(O.block_scale_buffer_shape(rows, K))), np.uint8)
+    O.scatter_block_scales(S, rows, K, buf)
+    return q, S, buf
+
+
+def test_nvfp4_gemm_exact_rational():
+    rng = np.random.default_rng(7)
+    M, N, K = 3, 5, 128
+    codes = [0x30, 0x38, 0x39, 0x3C, 0x44, 0x2A, 0x51]          # 0.5, 1, 1.125, 1.5, 3, 0.3125, 36
+    aq, aS, abuf = _nvfp4_operand(rng, M, K, codes)
+    bq, bS, bbuf = _nvfp4_operand(rng, N, K, codes)
+    ga, gb = 2.5, 0.75
+    exact, bits = O.gemm_nvfp4(aq, abuf, ga, bq, bbuf, gb, M, N, K)
+    for m in range(M):
+        for n in range(N):
+            ref = Fraction(0)
+            for k in range(K):
+                ca = (int(aq[m, k // 2]) >> (4 * (k % 2))) & 15
+                cb = (int(bq[n, k // 2]) >> (4 * (k % 2))) & 15
+                ref += _frac_e2m1(ca) * _frac_e4m3(aS[m, k // 16]) * _frac_e2m1(cb) * _frac_e4m3(bS[n, k // 16])
+            ref /= Fraction(ga) * Fraction(gb)
+            assert abs(exact[m, n] - float(ref)) <= 1e-14 * max(1.0, abs(float(ref)))
+    assert bits.dtype == np.uint16 and bits.shape == (M, N)
+
+
+def test_nvfp4_element_order_and_scale_placement():
+    """Byte j of a row holds element 2 j in its low nibble; the scale of
+    (row m, block b) sits at the 128x4-tiled offset, checked at hand-computed
+    offsets of a 130-row, 8-block (K = 128) buffer."""
+    M, K = 130, 128
+    # a: row 33 has a single 1.0 (code 2) at element 81 (byte 40, high nibble),
+    # row 129 a single 1.0 at element 32 (byte 16, low nibble); b: all ones.
+    aq = np.zeros((M, K // 2), np.uint8)
+    aq[33, 40] = 0x20
+    aq[129, 16] = 0x02
+    abuf = np.zeros(256 * 8, np.uint8)
+    # element 81 is in block 5 of row 33: tile 1 (rows 0..127, blocks 4..7),
+    # 512 + (33 % 32) * 16 + (33 // 32) * 4 + 5 % 4 = 533
+    abuf[533] = 0x40                                   # 2.0
+    # element 32 is in block 2 of row 129: tile 2, 1024 + 1 * 16 + 0 + 2 = 1042
+    abuf[1042] = 0x48                                  # 4.0
+    bq = np.full((1, K // 2), 0x22, np.uint8)          # every element 1.0
+    bbuf = np.full(128 * 8, 0x38, np.uint8)            # every scale 1.0
+    exact, _ = O.gemm_nvfp4(aq, abuf, 1.0, bq, bbuf, 1.0, M, 1, K)
+    want = np.zeros((M, 1))
+    want[33, 0] = 2.0
+    want[129, 0] = 4.0
+    assert np.array_equal(exact, want)
+    # moving row 33's code to the low nibble (element 80) keeps block 5
+    aq[33, 40] = 0x02
+    assert O.gemm_nvfp4(aq, abuf, 1.0, bq, bbuf, 1.0, M, 1, K)[0][33, 0] == 2.0
+    # a B operand that is zero except element 81 selects the high nibble
+    bq2 = np.zeros((1, K // 2), np.uint8)
+    bq2[0, 40] = 0x20
+    aq[33, 40] = 0x20
+    assert O.gemm_nvfp4(aq, abuf, 1.0, bq2, bbuf, 1.0, M, 1, K)[0][33, 0] == 2.0
+    aq[33, 40] = 0x02
+    assert O.gemm_nvfp4(aq, abuf, 1.0, bq2, bbuf, 1.0, M, 1, K)[0][33, 0] == 0.0
+
+
+def test_nvfp4_closed_form_and_global_scale_law():
+    M, N, K = 2, 3, 256
+    aq = np.full((M, K // 2), 0x22, np.uint8)          # 1.0 everywhere
+    bq = np.full((N, K // 2), 0x33, np.uint8)          # 1.5 everywhere
+    abuf = np.full(128 * 16, 0x38, np.uint8)           # scale 1.0
+    bbuf = np.full(128 * 16, 0x40, np.uint8)           # scale 2.0
+    exact, bits = O.gemm_nvfp4(aq, abuf, 1.0, bq, bbuf, 1.0, M, N, K)
+    assert np.all(exact == K * 1.0 * 3.0)
+    assert np.all(O.bits_to_f64(bits, O.BF16) == 768.0)
+    half, _ = O.gemm_nvfp4(aq, abuf, 2.0, bq, bbuf, 1.0, M, N, K)
+    third, _ = O.gemm_nvfp4(aq, abuf, 1.0, bq, bbuf, 3.0, M, N, K)
+    assert np.all(half == exact / 2) and np.allclose(third, exact / 3, rtol=1e-15)
+
+
+def test_nvfp4_gemm_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        O.dequant_nvfp4(np.zeros((2, 40), np.uint8), np.zeros(128 * 8, np.uint8), 1.0, 2, 80)
+    with pytest.raises(ValueError):
+        O.dequant_nvfp4(np.zeros((2, 32), np.uint8), np.zeros(128 * 8, np.uint8), 1.0, 2, 128)
