@@ -136,6 +136,7 @@ def copy_calibration(args):
 
 
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 MFMA
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
 def _time_graph(launch, steps, warmup, stream):
@@ -172,6 +173,16 @@ def gemm_cpu_baseline(gw, a, sa, b, sb, budget_s):
     rows, t0 = 0, time.perf_counter()
     with threadpool_limits(1):
         while rows < gw.M:
+            if gw.mode == "nvfp4":
+                # 128-row chunks: a chunk's block scales are one contiguous
+                # slab of the 128x4-tiled buffer (128 x K/16 bytes)
+                n = min(128, gw.M - rows)
+                slab = sa.numpy()[rows * (gw.K // 16):(rows + 128) * (gw.K // 16)]
+                O.gemm_nvfp4(an[rows:rows + n], slab, gw.a_gs, bn, sb.numpy(), gw.b_gs, n, gw.N, gw.K)
+                rows += n
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+                continue
             n = min(64, gw.M - rows)
             if gw.mode == "mxfp8":
                 O.gemm_mxfp8(an[rows:rows + n], sa[rows:rows + n].numpy(), bn, sb.numpy())
@@ -202,14 +213,21 @@ def gemm_main(args):
     a, sa, b, sb = make_gemm_inputs(gw)
     M, N, K = gw.M, gw.N, gw.K
     mx = gw.mode == "mxfp8"
-    in_bytes = M * K + N * K + ((M + N) * (K // 32) if mx else 8)
+    nv = gw.mode == "nvfp4"
+    if nv:
+        in_bytes = (M + N) * (K // 2) + sa.numel() + sb.numel() + 8
+    else:
+        in_bytes = M * K + N * K + ((M + N) * (K // 32) if mx else 8)
     out_bytes = 2 * M * N
     n_sets = max(1, min(16, -(-ROTATE_BYTES // (in_bytes + out_bytes))))
     sets = []
     for _ in range(n_sets):
         st = {"a": a.to(dev), "b": b.to(dev), "c": torch.empty((M, N), dtype=torch.bfloat16, device=dev)}
-        if mx:
+        if mx or nv:
             st["sa"], st["sb"] = sa.to(dev), sb.to(dev)
+            if nv:
+                st["ga"] = torch.tensor([gw.a_gs], dtype=torch.float32, device=dev)
+                st["gb"] = torch.tensor([gw.b_gs], dtype=torch.float32, device=dev)
         else:
             st["sa"] = torch.tensor([gw.a_scale], dtype=torch.float32, device=dev)
             st["sb"] = torch.tensor([gw.b_scale], dtype=torch.float32, device=dev)
@@ -217,7 +235,9 @@ def gemm_main(args):
 
     def launch(i):
         st = sets[i % n_sets]
-        if mx:
+        if nv:
+            ops.gemm_nvfp4(st["a"], st["sa"], st["ga"], st["b"], st["sb"], st["gb"], st["c"])
+        elif mx:
             ops.gemm_mxfp8(st["a"], st["sa"], st["b"], st["sb"], st["c"])
         else:
             ops.gemm_fp8_static(st["a"], st["sa"], st["b"], st["sb"], st["c"])
@@ -228,16 +248,19 @@ def gemm_main(args):
     ms_per_step = wall * 1e3 / args.steps
     # Bound: whichever of the MFMA time at peak and the HBM time of the
     # operands and output at peak is longer (few activation rows: HBM).
-    hbm_bound = (in_bytes + out_bytes) / (HBM_PEAK_GBS * 1e9) > flop / (MFMA_FP8_PEAK_TFLOPS * 1e12)
+    # the NVFP4 consumer runs the bf16 MFMA on exactly dequantized operands
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if nv else MFMA_FP8_PEAK_TFLOPS
+    hbm_bound = (in_bytes + out_bytes) / (HBM_PEAK_GBS * 1e9) > flop / (mfma_peak * 1e12)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round((in_bytes + out_bytes) / (kern_ms * 1e-3) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
         roof = {"bound": "mfma", "achieved": round(flop / (kern_ms * 1e-3) / 1e12, 1),
-                "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
+                "peak": mfma_peak, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
-    kernel = ("gemm_fp8_decode" if M <= 256 and K % 2048 == 0 and K <= 16384 else
+    kernel = ("gemm_nvfp4_k" if nv else
+              "gemm_fp8_decode" if M <= 256 and K % 2048 == 0 and K <= 16384 else
               "gemm_fp8_skinny" if M <= 256 and K % 64 == 0 else
               "gemm_fp8_tn_dma" if K % 512 == 0 else "gemm_fp8_tn")
     out = {
@@ -245,13 +268,15 @@ def gemm_main(args):
         "value": round(flop / (ms_per_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "e4m3" if not mx else "mxfp8 (e4m3 + e8m0)", "data": "synthetic",
+        "vs_baseline": None,
+        "dtype": ("nvfp4 (e2m1 + e4m3 block scales; bf16 MFMA)" if nv else
+                  "mxfp8 (e4m3 + e8m0)" if mx else "e4m3"), "data": "synthetic",
         "config": {"workload": gw.name, "M": M, "N": N, "K": K, "mode": gw.mode,
                    "bytes_in": in_bytes, "bytes_out": out_bytes},
         "launch": "graph", "buffer_sets": n_sets, "kernel_ms": round(kern_ms, 5),
         "roofline": dict(kernel=kernel, **roof),
     }
-    if not args.no_library:
+    if not args.no_library and not nv:
         out["library"] = library_gemm(sets[0], mx, M, N, K, args.steps, args.warmup, stream)
     out["cpu_baseline"] = (None if args.no_cpu_baseline else
                            gemm_cpu_baseline(gw, a, sa, b, sb, args.cpu_seconds))

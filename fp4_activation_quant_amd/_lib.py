@@ -15,7 +15,7 @@ NQ_BF16, NQ_FP16 = 0, 1
 NQ_MODE_FP8_STATIC, NQ_MODE_NVFP4, NQ_MODE_NONE, NQ_MODE_MXFP8 = 0, 1, 2, 3
 NQ_NORM_GEMMA, NQ_NORM_PLAIN = 0, 1
 EXPORTS = ("nq_gemma_add_rms_norm_quant", "nq_add_rms_norm_quant", "nq_quant_fp8_static",
-           "nq_quant_nvfp4", "nq_quant_mxfp8", "nq_gemm_mxfp8", "nq_gemm_fp8_static",
+           "nq_quant_nvfp4", "nq_quant_mxfp8", "nq_gemm_mxfp8", "nq_gemm_fp8_static", "nq_gemm_nvfp4",
            "nq_block_scale_bytes", "nq_status_string", "nq_abi_version", "nq_convert_probe")
 
 _lib = None
@@ -52,6 +52,8 @@ def lib():
         L.nq_gemm_mxfp8.restype = i32
         L.nq_gemm_fp8_static.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp]
         L.nq_gemm_fp8_static.restype = i32
+        L.nq_gemm_nvfp4.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp]
+        L.nq_gemm_nvfp4.restype = i32
         L.nq_block_scale_bytes.argtypes = [i64, i64]
         L.nq_block_scale_bytes.restype = ctypes.c_size_t
         L.nq_status_string.argtypes = [i32]
@@ -105,6 +107,11 @@ def nq_gemm_mxfp8(a, a_scales, b, b_scales, M, N, K, out, stream):
 def nq_gemm_fp8_static(a, a_scale, b, b_scale, M, N, K, out, stream):
     return lib().nq_gemm_fp8_static(a or None, a_scale or None, b or None, b_scale or None, int(M),
                                     int(N), int(K), out or None, stream or None)
+
+
+def nq_gemm_nvfp4(a, a_scales, a_gs, b, b_scales, b_gs, M, N, K, out, stream):
+    return lib().nq_gemm_nvfp4(a or None, a_scales or None, a_gs or None, b or None, b_scales or None,
+                               b_gs or None, int(M), int(N), int(K), out or None, stream or None)
 
 
 def nq_block_scale_bytes(M, H):

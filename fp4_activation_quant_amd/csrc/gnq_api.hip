@@ -229,6 +229,29 @@ nq_status nq_gemm_fp8_static(const void *a, const float *a_scale, const void *b,
   return gemm_common(false, a, nullptr, a_scale, b, nullptr, b_scale, M, N, K, out, stream);
 }
 
+nq_status nq_gemm_nvfp4(const void *a, const void *a_scales, const float *a_gs, const void *b,
+                        const void *b_scales, const float *b_gs, int64_t M, int64_t N, int64_t K, void *out,
+                        void *stream) {
+  if (M < 0 || N < 0 || K <= 0 || M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30) ||
+      K > ((int64_t)1 << 24))
+    return NQ_EINVAL;
+  if (!a || !b || !a_scales || !b_scales || !a_gs || !b_gs || !out) return NQ_EINVAL;
+  if (K % 256 != 0) return NQ_EUNSUPPORTED;
+  if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)a_scales | (uintptr_t)b_scales) % 16 != 0 ||
+      (uintptr_t)out % 2 != 0 || ((uintptr_t)a_gs | (uintptr_t)b_gs) % 4 != 0)
+    return NQ_EINVAL;
+  // one workgroup per 32 x 32 (or larger) output tile: the count must fit a grid
+  if (((M + 31) / 32) * ((N + 31) / 32) > (int64_t)INT32_MAX) return NQ_EINVAL;
+  const size_t obytes = (size_t)M * (size_t)N * 2;
+  if (overlaps(out, obytes, a, (size_t)M * (size_t)(K / 2)) || overlaps(out, obytes, b, (size_t)N * (size_t)(K / 2)) ||
+      overlaps(out, obytes, a_scales, block_scale_bytes(M, K)) ||
+      overlaps(out, obytes, b_scales, block_scale_bytes(N, K)) || overlaps(out, obytes, a_gs, 4) ||
+      overlaps(out, obytes, b_gs, 4))
+    return NQ_EINVAL;
+  if (M == 0 || N == 0) return NQ_OK;
+  return status_of(gemm_nvfp4(a, a_scales, a_gs, b, b_scales, b_gs, M, N, K, out, (hipStream_t)stream));
+}
+
 nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,
                            void *stream) {
   if (kind < 0 || kind > 8 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in)))

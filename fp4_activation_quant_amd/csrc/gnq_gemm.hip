@@ -780,6 +780,222 @@ hipError_t launch_decode(const uint8_t *A, const uint8_t *SA, const uint8_t *B, 
   return launch_decode_tile<MX, 4, 32, 32, 4>(A, SA, B, SB, a_scale, b_scale, M, N, K, C, st);
 }
 
+// NVFP4 consumer: C[M, N] = dq(A) dq(B)^T in bf16 for the op's NVFP4 output
+// as it stands (E2M1 codes, element 2 j in the low nibble of byte j; E4M3
+// block scales per 16 elements in the 128x4-tiled buffer; dq = code x scale
+// / gs).  The block-scaled MFMA takes only power-of-two (E8M0) scales, and a
+// code times an E4M3 scale has up to 5 significant bits (not exact in any
+// 8-bit format), so the operands are dequantized exactly to bf16 (8
+// significant bits) in registers and fed to the bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16; its operand and accumulator layout, measured
+// with a one-wave probe, match the block-scaled one's for rows and outputs);
+// 1 / (gs_a gs_b) is applied to the fp32 sum.  The hardware's scaled
+// E2M1 -> bf16 conversion uses only the exponent of its scale (probe), so
+// the conversion is by hand: magnitudes -> the E4M3 byte of the same value
+// by a byte permute on a table, E4M3 -> fp32 by the hardware convert, times
+// the decoded block scale (exact), upper 16 bits (exact).
+//
+// Structure of the decode kernel: a workgroup owns an MT x NT tile, its NW
+// waves split K into contiguous ranges, each streaming its range through a
+// private ring of S LDS stages (64 K-elements: 32 code bytes per row and the
+// 512-byte scale chunk of the 128-row scale tile) by 16-byte DMA, with no
+// barrier; the partial tiles are summed through LDS in a fixed order.
+// A lane's 16 K-elements per half stage are one whole block (lanes 0..31
+// block 2 j, lanes 32..63 block 2 j + 1), read as 8 bytes; every element is
+// scaled by its own block's scale before the MFMA, so the MFMA's pairing of
+// K positions need not follow the blocks.  Code rows are 32 bytes; their
+// 16-byte halves are swapped on every other group of 8 rows (g(q) =
+// (q / 8) % 2) to halve the LDS bank conflicts of those reads.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+constexpr int kFp4StepK = 64;                       // K elements per stage
+constexpr int kFp4StepBytes = kFp4StepK / 2;        // code bytes per row per stage
+constexpr int kFp4ScaleChunk = 512;                 // 128 rows x 4 blocks of scales
+
+__device__ __forceinline__ int fp4_swz(int row) { return (row >> 3) & 1; }
+
+// 8 E2M1 codes (element 2 j in the low nibble of byte j) times their block
+// scale `sig`, as 8 bf16 (exact).
+__device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w, float sig) {
+  constexpr uint32_t kLutLo = 0x3C383000u, kLutHi = 0x4C484440u;   // E4M3 of 0, .5, 1, 1.5 | 2, 3, 4, 6
+  const uint32_t ev = __builtin_amdgcn_perm(kLutHi, kLutLo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
+  const uint32_t od = __builtin_amdgcn_perm(kLutHi, kLutLo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
+  const f32x2 e01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, false);   // elements 0, 2
+  const f32x2 e23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, true);    // elements 4, 6
+  const f32x2 o01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, false);   // elements 1, 3
+  const f32x2 o23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, true);    // elements 5, 7
+  const float v[8] = {e01[0] * sig, o01[0] * sig, e01[1] * sig, o01[1] * sig,
+                      e23[0] * sig, o23[0] * sig, e23[1] * sig, o23[1] * sig};
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    out[j] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, v[2 * j + 1]), __builtin_bit_cast(uint32_t, v[2 * j]),
+                                   0x07060302u);
+  return __builtin_bit_cast(bf16x8, out);
+}
+
+template <int NW, int MT, int NT, int S>
+__global__ void __launch_bounds__(64 * NW)
+gemm_nvfp4_k(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ a_gs,
+             const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB, const float *__restrict__ b_gs,
+             int M, int N, int K, uint16_t *__restrict__ C, int tiles_n) {
+  constexpr int kBSeg = NT / 32, kASeg = MT / 32, kCSeg = kBSeg + kASeg;   // 1 KB code segments
+  constexpr int kCodeB = NT * kFp4StepBytes, kCodeA = MT * kFp4StepBytes;
+  constexpr int kStage = kCodeB + kCodeA + 2 * kFp4ScaleChunk;
+  constexpr int kTM = MT / 32, kTN = NT / 32;
+  static_assert(MT % 32 == 0 && NT % 32 == 0 && 128 % MT == 0 && 128 % NT == 0, "tiles inside one scale tile");
+  static_assert(NW * S * kStage <= kDecDataBytes, "stage rings exceed their LDS");
+  static_assert(NW * kTM * kTN * 4096 <= kDecDataBytes, "partials exceed the LDS");
+  static_assert((kCSeg + 1) * (S - 2) < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 31, h = lane >> 5;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int m0 = tm * MT, n0 = tn * NT;
+  const int ksteps = K / kFp4StepK;             // stages over all of K
+  const int J = ksteps / NW;                    // this wave's stages: wave J .. (wave + 1) J - 1
+  const size_t rowb = (size_t)K / 2;
+  uint8_t *wl = smem + wave * S * kStage;
+
+  // Code segment i (< kBSeg: weight rows 32 i .., else activation rows):
+  // lane l takes row 32 i + l / 2 and fetches the global half (l % 2) ^ g(row),
+  // landing at half l % 2 of the row's 32 LDS bytes.
+  const uint8_t *src[kCSeg];
+#pragma unroll
+  for (int i = 0; i < kCSeg; ++i) {
+    const int q = 32 * (i < kBSeg ? i : i - kBSeg) + (lane >> 1);
+    const size_t row = i < kBSeg ? (size_t)min(n0 + q, N - 1) : (size_t)min(m0 + q, M - 1);
+    src[i] = (i < kBSeg ? B : A) + row * rowb + (size_t)wave * J * kFp4StepBytes + 16 * ((lane & 1) ^ fp4_swz(q));
+  }
+  // Scale chunk of stage j: lanes 0..31 the weight's 512 bytes, 32..63 the
+  // activation's, each 16 bytes.
+  const uint8_t *ssrc = lane < 32 ? SB + ((size_t)(n0 / 128) * ksteps + (size_t)wave * J) * kFp4ScaleChunk + 16 * lane
+                                  : SA + ((size_t)(m0 / 128) * ksteps + (size_t)wave * J) * kFp4ScaleChunk + 16 * (lane - 32);
+  auto issue = [&](int j) {
+    uint8_t *dst = wl + (j % S) * kStage;
+#pragma unroll
+    for (int i = 0; i < kCSeg; ++i)
+      dma16(src[i] + (size_t)j * kFp4StepBytes, dst + (i < kBSeg ? i * 1024 : kCodeB + (i - kBSeg) * 1024));
+    dma16(ssrc + (size_t)j * kFp4ScaleChunk, dst + kCodeB + kCodeA);
+  };
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j)
+    if (j < J) issue(j);
+
+  f32x16 acc[kTM][kTN];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < kTN; ++jj) acc[i][jj] = f32x16{0};
+  // rows of this lane's fragments inside the tile and inside the 128-row scale tile
+  const int bq0 = r, aq0 = r;
+  const int bs0 = n0 % 128, as0 = m0 % 128;
+  for (int j = 0; j < J; ++j) {
+    dec_wait<kCSeg + 1, S - 2>(min(J - 1, j + S - 2) - j);
+    if (j + S - 1 < J) issue(j + S - 1);
+    const uint8_t *st = wl + (j % S) * kStage;
+    const uint8_t *sch = st + kCodeB + kCodeA;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {                 // half stage: blocks 2 p (lanes 0..31), 2 p + 1 (32..63)
+      const int blk = 2 * p + h;
+      bf16x8 bf[kTN][2], af[kTM][2];
+#pragma unroll
+      for (int jj = 0; jj < kTN; ++jj) {
+        const int q = 32 * jj + bq0, qs = bs0 + q;
+        const uint2 w = *reinterpret_cast<const uint2 *>(st + q * kFp4StepBytes + 16 * (p ^ fp4_swz(q)) + 8 * h);
+        const float sig = __builtin_amdgcn_cvt_f32_fp8((int)sch[(qs & 31) * 16 + (qs >> 5) * 4 + blk], 0);
+        bf[jj][0] = fp4x8_bf16(w.x, sig);
+        bf[jj][1] = fp4x8_bf16(w.y, sig);
+      }
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        const int q = 32 * i + aq0, qs = as0 + q;
+        const uint2 w = *reinterpret_cast<const uint2 *>(st + kCodeB + q * kFp4StepBytes + 16 * (p ^ fp4_swz(q)) + 8 * h);
+        const float sig =
+            __builtin_amdgcn_cvt_f32_fp8((int)sch[kFp4ScaleChunk + (qs & 31) * 16 + (qs >> 5) * 4 + blk], 0);
+        af[i][0] = fp4x8_bf16(w.x, sig);
+        af[i][1] = fp4x8_bf16(w.y, sig);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < kTN; ++jj)
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][e], bf[jj][e], acc[i][jj], 0, 0, 0);
+    }
+  }
+
+  __syncthreads();
+  float *red = reinterpret_cast<float *>(smem);
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < kTN; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[((wave * kTM + i) * kTN + jj) * 1024 + v * 64 + lane] = acc[i][jj][v];
+  __syncthreads();
+  const float s = 1.0f / ((*a_gs) * (*b_gs));
+  constexpr int kOut = kTM * kTN * 1024;
+  for (int e = tid; e < kOut; e += 64 * NW) {
+    const int tile = e >> 10, v = (e >> 6) & 15, l = e & 63;
+    const int row = m0 + 32 * (tile / kTN) + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+    const int col = n0 + 32 * (tile % kTN) + (l & 31);
+    if (row < M && col < N) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += red[w * kOut + e];
+      C[(size_t)row * (size_t)N + col] = (uint16_t)(Bf16::pack(sum * s, 0.0f) & 0xffffu);
+    }
+  }
+}
+
+#define GNQ_GEMM_FP4_INST(NW, MT, NT, S)                                                          \
+  template __global__ void gemm_nvfp4_k<NW, MT, NT, S>(const uint8_t *, const uint8_t *, const float *, \
+                                                        const uint8_t *, const uint8_t *, const float *, int, \
+                                                        int, int, uint16_t *, int);
+GNQ_GEMM_FP4_INST(4, 32, 32, 8)
+GNQ_GEMM_FP4_INST(8, 32, 32, 4)
+GNQ_GEMM_FP4_INST(4, 64, 64, 3)
+#undef GNQ_GEMM_FP4_INST
+
+template <int NW, int MT, int NT, int S>
+hipError_t launch_nvfp4(const uint8_t *A, const uint8_t *SA, const float *a_gs, const uint8_t *B,
+                        const uint8_t *SB, const float *b_gs, int M, int N, int K, uint16_t *C, hipStream_t st) {
+  static std::atomic<uint64_t> lds_set{0};
+  // the stage rings, or the partial tiles summed over them at the end
+  constexpr int ring = NW * S * (NT * kFp4StepBytes + MT * kFp4StepBytes + 2 * kFp4ScaleChunk);
+  constexpr int part = NW * (MT / 32) * (NT / 32) * 4096;
+  constexpr int lds = ring > part ? ring : part;
+  const hipError_t e = allow_dynamic_lds((const void *)gemm_nvfp4_k<NW, MT, NT, S>, lds, lds_set);
+  if (e != hipSuccess) return e;
+  const int tiles_n = (N + NT - 1) / NT;
+  const long tiles = (long)((M + MT - 1) / MT) * tiles_n;
+  hipLaunchKernelGGL((gemm_nvfp4_k<NW, MT, NT, S>), dim3((unsigned)tiles), dim3(64 * NW), lds, st, A, SA, a_gs, B,
+                     SB, b_gs, M, N, K, C, tiles_n);
+  return hipGetLastError();
+}
+
+// Caller guarantees K % 256 == 0, 0 < M, N, and that the 32 x 32 tile count
+// fits a grid.  Tiles: 32 x 32 up to 256 rows, else 64 x 64 with 3 stages
+// (64 KB of LDS: two workgroups per CU hide each other's LDS and
+// conversion latency; 6 stages and one workgroup per CU ran 1.7x slower).
+hipError_t gemm_nvfp4(const void *a, const void *sa, const float *a_gs, const void *b, const void *sb,
+                      const float *b_gs, int64_t M, int64_t N, int64_t K, void *c, hipStream_t st) {
+  const uint8_t *A = (const uint8_t *)a, *B = (const uint8_t *)b;
+  const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
+#ifdef GNQ_FP4_TILE
+  return launch_nvfp4<GNQ_FP4_TILE>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+#endif
+  // up to 256 rows: 32 x 32 tiles (enough workgroups), 8 waves when K allows
+  if (M <= 256 && K % 512 == 0)
+    return launch_nvfp4<8, 32, 32, 4>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+  if (M <= 256)
+    return launch_nvfp4<4, 32, 32, 8>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+  return launch_nvfp4<4, 64, 64, 3>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+}
+
 hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,
                     const float *a_scale, const float *b_scale, int64_t M, int64_t N, int64_t K,
                     void *c, hipStream_t st) {

@@ -263,5 +263,31 @@ def gemm_fp8_static(a, a_scale, b, b_scale, out=None):
     return out
 
 
+def gemm_nvfp4(a, a_block_scale, a_global_scale, b, b_block_scale, b_global_scale, out=None):
+    """The consumer linear on an NVFP4 activation: out (M, N) bf16 =
+    dq(a) @ dq(b)^T, with a (M, K // 2) / b (N, K // 2) packed E2M1 codes,
+    their 128x4-tiled E4M3 block-scale buffers (the NVFP4 mode's outputs, and
+    a weight in the same format) and one float32 global scale each on the
+    device (dq = code * block scale / global scale)."""
+    _validate_codes(a, "a")
+    _validate_codes(b, "b")
+    M, K = a.shape[0], 2 * a.shape[1]
+    N = b.shape[0]
+    _require(b.shape[1] == K // 2 and K % 256 == 0, "b: (N, K // 2) with the same K; K % 256 == 0")
+    for name, bs, rows in (("a_block_scale", a_block_scale, M), ("b_block_scale", b_block_scale, N)):
+        _require(bs.is_cuda and bs.is_contiguous() and bs.numel() * bs.element_size() >= _lib.nq_block_scale_bytes(rows, K),
+                 f"{name}: contiguous device buffer of block_scale_bytes(rows, K) bytes")
+    for name, g in (("a_global_scale", a_global_scale), ("b_global_scale", b_global_scale)):
+        _require(g.is_cuda and g.dtype == torch.float32 and g.numel() >= 1, f"{name}: float32 device tensor")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    with torch.cuda.device(a.device):
+        st = _lib.nq_gemm_nvfp4(a.data_ptr(), a_block_scale.data_ptr(), a_global_scale.data_ptr(), b.data_ptr(),
+                                b_block_scale.data_ptr(), b_global_scale.data_ptr(), M, N, K, out.data_ptr(),
+                                _stream(a.device))
+    _check(st, "nq_gemm_nvfp4")
+    return out
+
+
 def block_scale_bytes(M, H):
     return _lib.nq_block_scale_bytes(M, H)

@@ -174,7 +174,7 @@ def load_scale(wl: Workload) -> float:
 @dataclass(frozen=True)
 class GemmWorkload:
     name: str
-    mode: str             # "mxfp8" | "fp8"
+    mode: str             # "mxfp8" | "fp8" | "nvfp4"
     M: int
     N: int
     K: int
@@ -184,6 +184,9 @@ class GemmWorkload:
     scale_range: tuple = (118, 126)     # E8M0 codes of both operands
     a_scale: float = 0.02               # static FP8 tensor scales
     b_scale: float = 0.004
+    fp4_scale_range: tuple = (0x30, 0x60)   # NVFP4 E4M3 block-scale codes (0.5 .. 32)
+    a_gs: float = 300.0                 # NVFP4 global scales
+    b_gs: float = 150.0
 
 
 GEMM_WORKLOADS = {g.name: g for g in [
@@ -195,6 +198,9 @@ GEMM_WORKLOADS = {g.name: g for g in [
     GemmWorkload("gemm_mxfp8_m64_n4096_k4096", "mxfp8", 64, 4096, 4096, 8400),
     GemmWorkload("gemm_mxfp8_m1_n4096_k4096", "mxfp8", 1, 4096, 4096, 8600),
     GemmWorkload("gemm_fp8_m64_n4096_k4096", "fp8", 64, 4096, 4096, 8700),
+    GemmWorkload("gemm_nvfp4_m8192_n4096_k4096", "nvfp4", 8192, 4096, 4096, 8800),
+    GemmWorkload("gemm_nvfp4_m64_n4096_k4096", "nvfp4", 64, 4096, 4096, 8900),
+    GemmWorkload("gemm_nvfp4_m1_n4096_k4096", "nvfp4", 1, 4096, 4096, 9000),
 ]}
 
 
@@ -207,9 +213,25 @@ def _draw_codes(rows, cols, exp_range, gen):
     return (sign | (ex << 3) | man).to(torch.uint8)
 
 
+def _nvfp4_scale_buffer(rows, K, code_range, gen):
+    """A 128x4-tiled block-scale buffer (round_up(rows, 128) x K/16 bytes, the
+    op's layout) filled with E4M3 codes in code_range (padding rows too)."""
+    lo, hi = code_range
+    n = (rows + 127) // 128 * 128 * (K // 16)
+    return torch.randint(lo, hi + 1, (n,), generator=gen, dtype=torch.int32).to(torch.uint8)
+
+
 def make_gemm_inputs(gw: GemmWorkload):
-    """(a codes (M, K), a scales (M, K/32) or None, b codes (N, K), b scales
-    (N, K/32) or None) as CPU uint8 tensors."""
+    """(a codes, a scales or None, b codes, b scales or None) as CPU uint8
+    tensors: FP8 codes (rows, K) with E8M0 scales (rows, K/32) for MXFP8;
+    for NVFP4 packed random E2M1 codes (rows, K/2) with flat 128x4-tiled
+    E4M3 scale buffers."""
+    if gw.mode == "nvfp4":
+        a = torch.randint(0, 256, (gw.M, gw.K // 2), generator=_gen(gw.seed_base), dtype=torch.int32)
+        b = torch.randint(0, 256, (gw.N, gw.K // 2), generator=_gen(gw.seed_base + 1), dtype=torch.int32)
+        sa = _nvfp4_scale_buffer(gw.M, gw.K, gw.fp4_scale_range, _gen(gw.seed_base + 2))
+        sb = _nvfp4_scale_buffer(gw.N, gw.K, gw.fp4_scale_range, _gen(gw.seed_base + 3))
+        return a.to(torch.uint8), sa, b.to(torch.uint8), sb
     a = _draw_codes(gw.M, gw.K, gw.exp_range, _gen(gw.seed_base))
     b = _draw_codes(gw.N, gw.K, gw.w_exp_range, _gen(gw.seed_base + 1))
     if gw.mode != "mxfp8":

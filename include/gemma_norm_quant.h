@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define NQ_ABI_VERSION 4
+#define NQ_ABI_VERSION 5
 
 typedef enum {
   NQ_OK = 0,
@@ -198,6 +198,30 @@ nq_status nq_gemm_mxfp8(const void *a, const void *a_scales, const void *b, cons
 nq_status nq_gemm_fp8_static(const void *a, const float *a_scale, const void *b,
                              const float *b_scale, int64_t M, int64_t N, int64_t K, void *out,
                              void *stream);
+
+/*
+ * nq_gemm_nvfp4 -- the consumer linear of the NVFP4 output: out[M, N] =
+ * dq(a) * dq(b)^T rounded to bf16, a the (M, K/2) packed E2M1 codes this
+ * library writes (element 2j in the low nibble of byte j) and b the weight's
+ * (N, K/2) codes in the same format; a_scales / b_scales the 128x4-tiled
+ * E4M3FN block-scale buffers of nq_block_scale_bytes(M, K) /
+ * nq_block_scale_bytes(N, K) bytes (the NVFP4 mode's layout: one scale per
+ * 16 elements); a_gs / b_gs DEVICE pointers to the fp32 global scale each
+ * operand was quantized with (the op's `scale` in NVFP4 mode).
+ *   dq(x)[r, k] = E2M1(code) * E4M3(scale[r, k/16]) / gs.
+ * The products are exact in fp32 (each dequantized value fits bf16); the
+ * sum is accumulated in fp32 and multiplied by 1 / (gs_a gs_b) before the
+ * rounding to bf16.  Scale bytes of rows >= M (>= N) are read (they share
+ * 512-byte tiles with real rows) but only reach outputs that are not
+ * written.
+ *   M, N >= 0 (either 0: NQ_OK, nothing launched); K > 0 with K % 256 == 0
+ *   (NQ_EUNSUPPORTED otherwise); a, b and both scale buffers 16-byte
+ *   aligned, out 2-byte aligned, a_gs and b_gs 4-byte aligned, out
+ *   overlapping no input (NQ_EINVAL otherwise).
+ */
+nq_status nq_gemm_nvfp4(const void *a, const void *a_scales, const float *a_gs, const void *b,
+                        const void *b_scales, const float *b_gs, int64_t M, int64_t N, int64_t K, void *out,
+                        void *stream);
 
 /* Size in bytes of the NVFP4 block-scale buffer:
  * round_up(M, 128) * round_up(H / 16, 4) (the wrapper's allocation on the

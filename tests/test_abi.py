@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert _lib.nq_abi_version() == 4
+    assert _lib.nq_abi_version() == 5
     assert _lib.nq_status_string(0) == "ok"
     for s in range(0, 6):
         assert isinstance(_lib.nq_status_string(s), str)
@@ -227,3 +227,29 @@ def test_gemm_validation(mx, over, want):
     a.update(over)
     fn = _lib.nq_gemm_mxfp8 if mx else _lib.nq_gemm_fp8_static
     assert fn(a["a"], a["sa"], a["b"], a["sb"], a["M"], a["N"], a["K"], a["out"], 0) == want
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(a=0), _lib.NQ_EINVAL),
+    (dict(b=0), _lib.NQ_EINVAL),
+    (dict(sa=0), _lib.NQ_EINVAL),
+    (dict(sb=0), _lib.NQ_EINVAL),
+    (dict(ga=0), _lib.NQ_EINVAL),
+    (dict(gb=0), _lib.NQ_EINVAL),
+    (dict(out=0), _lib.NQ_EINVAL),
+    (dict(K=0), _lib.NQ_EINVAL),
+    (dict(N=-1), _lib.NQ_EINVAL),
+    (dict(K=192), _lib.NQ_EUNSUPPORTED),               # K % 256 != 0
+    (dict(sa=S + 8), _lib.NQ_EINVAL),                 # scale buffer not 16-byte aligned
+    (dict(ga=S + 2), _lib.NQ_EINVAL),                 # global scale not 4-byte aligned
+    (dict(out=X + 64), _lib.NQ_EINVAL),               # out overlaps a
+    (dict(out=Y + 1), _lib.NQ_EINVAL),
+    (dict(M=1 << 30, N=1 << 30, out=0x7F0000000000), _lib.NQ_EINVAL),  # tile count beyond a grid
+    (dict(M=0), _lib.NQ_OK),
+    (dict(N=0), _lib.NQ_OK),
+])
+def test_gemm_nvfp4_validation(over, want):
+    a = dict(a=X, sa=S, ga=B, b=Q, sb=B + 4096, gb=B + 64, M=4, N=8, K=4096, out=Y)
+    a.update(over)
+    assert _lib.nq_gemm_nvfp4(a["a"], a["sa"], a["ga"], a["b"], a["sb"], a["gb"], a["M"], a["N"], a["K"],
+                              a["out"], 0) == want

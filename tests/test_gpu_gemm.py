@@ -184,3 +184,108 @@ def test_gemm_empty_writes_nothing():
     st2 = _lib.nq_gemm_mxfp8(p, p + 8192, p + 16384, p + 24576, 64, 0, 64, p + 32768, 0)
     torch.cuda.synchronize()
     assert st == _lib.NQ_OK and st2 == _lib.NQ_OK and bool((buf == P.SENTINEL).all())
+
+
+# ---- NVFP4 consumer (nq_gemm_nvfp4) ----------------------------------------
+
+def _nvfp4_operand(rng, rows, K, nibbles, scale_codes):
+    """Packed E2M1 codes drawn from `nibbles` and a 128x4-tiled scale buffer
+    with block scales from `scale_codes`; the padding rows' bytes are random
+    junk (the kernel reads them beside real rows but must not use them)."""
+    nib = np.asarray(nibbles, np.uint8)[rng.integers(0, len(nibbles), size=(rows, K))]
+    q = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    S = np.asarray(scale_codes, np.uint8)[rng.integers(0, len(scale_codes), size=(rows, K // 16))]
+    buf = rng.integers(0, 0x7F, size=int(np.prod(O.block_scale_buffer_shape(rows, K))), dtype=np.int64).astype(np.uint8)
+    O.scatter_block_scales(S, rows, K, buf)
+    return q, buf
+
+
+def _run_nvfp4(aq, abuf, ga, bq, bbuf, gb, M, N):
+    out = torch.full((M * N * 2 + P.GUARD,), P.SENTINEL, dtype=torch.uint8, device="cuda")
+    o = out[:M * N * 2].view(torch.bfloat16).view(M, N)
+    f32 = lambda v: torch.tensor([v], dtype=torch.float32, device="cuda")
+    ops.gemm_nvfp4(_dev(aq), _dev(abuf), f32(ga), _dev(bq), _dev(bbuf), f32(gb), out=o)
+    torch.cuda.synchronize()
+    assert bool((out[M * N * 2:] == P.SENTINEL).all()), "wrote past the output"
+    return P.bits16(o)
+
+
+# 32 x 32 tiles up to 256 rows (8 waves when K % 512 == 0, else 4), 64 x 64
+# beyond; shapes cross 128-row scale tiles and have ragged edges; K from
+# 256 (one stage per wave) up
+NVFP4_SHAPES = [(1, 8, 256), (5, 300, 512), (32, 64, 1024), (33, 100, 256), (200, 130, 2048),
+                (130, 257, 768), (64, 1000, 1024), (300, 200, 512), (257, 70, 768)]
+
+
+@pytest.mark.parametrize("M,N,K", NVFP4_SHAPES)
+@pytest.mark.parametrize("gs", [(1.0, 1.0), (2.0, 0.5)])
+def test_nvfp4_gemm_exact_cases(M, N, K, gs):
+    """Codes within +-2 and block scales 0.5 .. 1.5 (non-powers of two
+    included): every partial sum is a multiple of 2^-8 below 2^24 units, so
+    any fp32 summation order is exact, and with power-of-two global scales
+    the bf16 result is bit-identical to the oracle's rounding."""
+    print(f"gemm nvfp4 exact M={M} N={N} K={K} gs={gs}", flush=True)
+    rng = np.random.default_rng(M * 13 + N * 7 + K)
+    nib = [0, 1, 2, 3, 4, 9, 10, 11, 12]
+    sc = [0x30, 0x38, 0x39, 0x3C]
+    aq, abuf = _nvfp4_operand(rng, M, K, nib, sc)
+    bq, bbuf = _nvfp4_operand(rng, N, K, nib, sc)
+    got = _run_nvfp4(aq, abuf, gs[0], bq, bbuf, gs[1], M, N)
+    _, want = O.gemm_nvfp4(aq, abuf, gs[0], bq, bbuf, gs[1], M, N, K)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, (bad[0][:5], bad[1][:5], got[bad][:5], want[bad][:5])
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 96, 4096), (300, 520, 2048), (1, 333, 8192), (256, 512, 4096)])
+def test_nvfp4_gemm_random(M, N, K):
+    print(f"gemm nvfp4 random M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M + 3 * N + K)
+    sc = [c for c in range(0x18, 0x60)]                 # E4M3 block scales 2^-4 .. 2^5
+    aq, abuf = _nvfp4_operand(rng, M, K, list(range(16)), sc)
+    bq, bbuf = _nvfp4_operand(rng, N, K, list(range(16)), sc)
+    ga, gb = 2.7, 0.37
+    got = _run_nvfp4(aq, abuf, ga, bq, bbuf, gb, M, N)
+    exact, _ = O.gemm_nvfp4(aq, abuf, ga, bq, bbuf, gb, M, N, K)
+    mag = O.gemm_f64(np.abs(O.dequant_nvfp4(aq, abuf, ga, M, K)), np.abs(O.dequant_nvfp4(bq, bbuf, gb, N, K)))
+    _tolerance_check(got, exact, mag)
+
+
+def test_nvfp4_gemm_consumes_the_ops_output():
+    """The op's NVFP4 codes, block scales and global scale go straight into
+    the consumer; rows whose GPU codes and scales equal the oracle's must
+    match the oracle GEMM of the oracle's own output within the tolerance."""
+    print("gemm nvfp4 consumer", flush=True)
+    g = torch.Generator().manual_seed(29)
+    M, H, N = 300, 4096, 384
+    x = torch.randn(M, H, generator=g).to(torch.bfloat16)
+    r = torch.randn(M, H, generator=g).to(torch.bfloat16)
+    w = (torch.randn(H, generator=g) * 0.1).to(torch.bfloat16)
+    gs = 448.0 * 6.0 / 9.0
+    rng = np.random.default_rng(4)
+    bq, bbuf = _nvfp4_operand(rng, N, H, list(range(16)), list(range(0x20, 0x48)))
+    gb = 1.5
+    ref = O.add_rms_norm_quant(P.bits16(x), P.bits16(r), P.bits16(w), 1e-6, gs, "nvfp4")
+    abuf = np.asarray(ref["block_scale"], np.uint8).reshape(-1)
+    exact, _ = O.gemm_nvfp4(ref["q"], abuf, gs, bq, bbuf, gb, M, N, H)
+    mag = O.gemm_f64(np.abs(O.dequant_nvfp4(ref["q"], abuf, gs, M, H)), np.abs(O.dequant_nvfp4(bq, bbuf, gb, N, H)))
+    sd = torch.tensor([gs], dtype=torch.float32, device="cuda")
+    q, bs, _ = ops.gemma_add_rms_norm_quant(x.cuda(), r.cuda(), w.cuda(), 1e-6, sd, True)
+    out = ops.gemm_nvfp4(q, bs, sd, _dev(bq), _dev(bbuf), torch.tensor([gb], dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    qn = q.view(torch.uint8).cpu().numpy()
+    bsn = bs.view(torch.uint8).cpu().numpy().reshape(-1)
+    rows = np.arange(M)[:, None]
+    offs = O.swizzle_128x4_offset(rows, np.arange(H // 16)[None, :], H)
+    same = np.all(qn == ref["q"], axis=1) & np.all(bsn[offs] == abuf[offs], axis=1)
+    print(f"  rows with the oracle's codes and scales: {int(same.sum())} / {M}", flush=True)
+    assert same.mean() >= 0.95
+    _tolerance_check(P.bits16(out)[same], exact[same], mag[same])
+
+
+def test_nvfp4_gemm_empty_writes_nothing():
+    buf = torch.full((1 << 16,), P.SENTINEL, dtype=torch.uint8, device="cuda")
+    p = buf.data_ptr()
+    st = _lib.nq_gemm_nvfp4(p, p + 8192, p + 16384, p + 24576, p + 32768, p + 16388, 0, 64, 256, p + 40960, 0)
+    st2 = _lib.nq_gemm_nvfp4(p, p + 8192, p + 16384, p + 24576, p + 32768, p + 16388, 64, 0, 256, p + 40960, 0)
+    torch.cuda.synchronize()
+    assert st == _lib.NQ_OK and st2 == _lib.NQ_OK and bool((buf == P.SENTINEL).all())
