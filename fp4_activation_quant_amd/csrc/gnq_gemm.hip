@@ -1,12 +1,14 @@
 // Consumer GEMM of the quantized activation: C[M, N] = dq(A) * dq(B)^T in
 // bf16, A the (M, K) activation codes the op wrote and B the (N, K) weight
 // codes in the same format, both K-contiguous (the pre-quantized input path
-// of the quantized linears on the PR conversation page).  Two formats:
+// of the quantized linears on the PR conversation page).  Three formats:
 //  * MXFP8: E4M3 codes with row-major E8M0 scales (rows, K / 32), fed to the
 //    gfx950 block-scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) as they are;
 //  * static FP8: E4M3 codes with one fp32 scale per tensor: the same MFMA at
 //    unit block scale, the product of the two tensor scales applied to the
-//    fp32 accumulator.
+//    fp32 accumulator;
+//  * NVFP4: packed E2M1 codes with 128x4-tiled E4M3 block scales, dequantized
+//    exactly to bf16 in registers for the bf16 MFMA (gemm_nvfp4 below).
 //
 // Operand layout of the MFMA (32 x 32 output, K = 64 per instruction,
 // measured on the chip with a one-wave probe): lane l supplies row (or
