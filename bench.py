@@ -305,15 +305,19 @@ def library_gemm(st, mx, M, N, K, steps, warmup, stream):
 
 
 def chain_main(args):
-    """The op feeding the consumer GEMM, fused (add + norm + MXFP8 quant, then
-    the GEMM) against unfused (add + norm writing y, the standalone MXFP8
-    quant reading it back, then the GEMM): time per layer input."""
+    """The op feeding the consumer GEMM, fused (add + norm + MXFP8 or NVFP4
+    quant, then the GEMM) against unfused (add + norm writing y, the
+    standalone quant reading it back, then the GEMM): time per layer input."""
     import torch
     from fp4_activation_quant_amd import _lib, ops
-    from fp4_activation_quant_amd.workloads import WORKLOADS, GEMM_WORKLOADS, make_inputs, make_gemm_inputs
+    from fp4_activation_quant_amd.workloads import (WORKLOADS, GEMM_WORKLOADS, make_inputs, make_gemm_inputs,
+                                                     load_scale)
     _lib.lib()
     wl = WORKLOADS[args.chain]
-    gw = [g for g in GEMM_WORKLOADS.values() if g.mode == "mxfp8" and g.M == wl.M and g.K == wl.H][0]
+    if wl.mode not in ("mxfp8", "nvfp4"):
+        raise SystemExit("--chain takes an MXFP8 or NVFP4 workload")
+    nv = wl.mode == "nvfp4"
+    gw = [g for g in GEMM_WORKLOADS.values() if g.mode == wl.mode and g.M == wl.M and g.K == wl.H][0]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x, r, w = make_inputs(wl)
@@ -322,14 +326,29 @@ def chain_main(args):
     xd, wd, bd, sbd = x.to(dev), w.to(dev), b.to(dev), sb.to(dev)
     xs = [xd, -xd]
     rd = r.to(dev) if r is not None else None
-    q = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
-    s = torch.empty((M, H // 32), dtype=torch.uint8, device=dev)
     y = torch.empty((M, H), dtype=x.dtype, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if nv:
+        q = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((ops.round_up(M, 128), ops.round_up(H // 16, 4)), dtype=torch.uint8, device=dev)
+        gsd = torch.tensor([load_scale(wl)], dtype=torch.float32, device=dev)
+        gbd = torch.tensor([gw.b_gs], dtype=torch.float32, device=dev)
+    else:
+        q = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
+        s = torch.empty((M, H // 32), dtype=torch.uint8, device=dev)
     res = {}
     for path in ("fused", "unfused"):
         def launch(i, path=path):
             xi = xs[i & 1]
+            if nv:
+                if path == "fused":
+                    ops.add_rms_norm_quant_out(xi, rd, wd, wl.eps, gsd, "nvfp4", "gemma", q, s,
+                                               y if wl.write_y else None)
+                else:
+                    ops.add_rms_norm_quant_out(xi, rd, wd, wl.eps, None, None, "gemma", None, None, y)
+                    ops.quant_nvfp4(y, gsd, q, s)
+                ops.gemm_nvfp4(q, s, gsd, bd, sbd, gbd, c)
+                return
             if path == "fused":
                 ops.add_rms_norm_quant_out(xi, rd, wd, wl.eps, None, "mxfp8", "gemma", q, s,
                                            y if wl.write_y else None)
@@ -344,7 +363,7 @@ def chain_main(args):
     # chunk j (a memory-bound kernel next to a compute-bound one); every
     # stream stays at the default priority.
     ovl = max(1, args.overlap)
-    if ovl > 1 and M % ovl == 0:
+    if ovl > 1 and M % ovl == 0 and not nv:
         rows = M // ovl
         s_norm, s_gemm = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
         done = [torch.cuda.Event() for _ in range(ovl)]
