@@ -962,6 +962,157 @@ GNQ_GEMM_FP4_INST(8, 32, 32, 4)
 GNQ_GEMM_FP4_INST(4, 64, 64, 3)
 #undef GNQ_GEMM_FP4_INST
 
+// Many rows: 256 x 256 workgroup tiles (4 waves of 128 x 128, 16 MFMA tiles
+// each), operands staged in shared LDS stages of 64 K-elements by 16-byte
+// DMA (codes of 256 + 256 rows and the four 512-byte scale tiles of their
+// two 128-row groups), one barrier per stage.  Each converted fragment feeds
+// 4 MFMAs instead of 2 in a 64 x 64 tile, halving the dequantization per
+// MFMA.  Scale tiles past the last 128-row group (a partial 256-row tile)
+// are not read: the last group's tile stands in, for rows whose outputs are
+// dropped.
+constexpr int kFp4BigRows = 256;
+constexpr int kFp4BigStages = 6;
+constexpr int kFp4BigCode = kFp4BigRows * kFp4StepBytes;                 // 8 KB per operand
+constexpr int kFp4BigStage = 2 * kFp4BigCode + 4 * kFp4ScaleChunk;       // + A lo/hi, B lo/hi scale tiles
+constexpr int kFp4BigLds = kFp4BigStages * kFp4BigStage;                 // 108 KB
+
+__global__ void __launch_bounds__(256)
+gemm_nvfp4_big(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ a_gs,
+               const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB, const float *__restrict__ b_gs,
+               int M, int N, int K, uint16_t *__restrict__ C, int tiles_m, int tiles) {
+  constexpr int kPer = 5;                               // DMA instructions per wave per stage
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 31, h = lane >> 5;
+  int tm, tn;
+  gemm_tile_of_block(blockIdx.x, tiles_m, tiles / tiles_m, tm, tn);
+  const int m0 = tm * kFp4BigRows, n0 = tn * kFp4BigRows;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int ksteps = K / kFp4StepK;
+  const size_t rowb = (size_t)K / 2;
+
+  // Code segments: wave w fetches 1 KB segments 4 w .. 4 w + 3 of the
+  // stage's 16 (0..7: A rows 32 i .., 8..15: B rows); lane l takes row
+  // 32 i + l / 2, global half (l % 2) ^ g(row) into half l % 2.
+  const uint8_t *src[4];
+  int dsto[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int seg = 4 * wave + t;
+    const bool isb = seg >= 8;
+    const int q = 32 * (seg & 7) + (lane >> 1);
+    const size_t row = isb ? (size_t)min(n0 + q, N - 1) : (size_t)min(m0 + q, M - 1);
+    src[t] = (isb ? B : A) + row * rowb + 16 * ((lane & 1) ^ fp4_swz(q));
+    dsto[t] = (isb ? kFp4BigCode : 0) + (seg & 7) * 1024;
+  }
+  // Scale tiles: wave w fetches tile w (0, 1: A's two 128-row groups; 2, 3:
+  // B's) with lanes 0..31, 16 bytes each.
+  const bool sb_ = wave >= 2;
+  const int groups = sb_ ? (N + 127) / 128 : (M + 127) / 128;
+  const int grp = min((sb_ ? n0 : m0) / 128 + (wave & 1), groups - 1);
+  const uint8_t *ssrc = (sb_ ? SB : SA) + (size_t)grp * ksteps * kFp4ScaleChunk + 16 * (lane & 31);
+  const int sdst = 2 * kFp4BigCode + wave * kFp4ScaleChunk;
+  auto issue = [&](int ks, int from) {
+    uint8_t *st = smem + (ks % kFp4BigStages) * kFp4BigStage;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(src[t] + (size_t)from * kFp4StepBytes, st + dsto[t]);
+    if (lane < 32) dma16(ssrc + (size_t)from * kFp4ScaleChunk, st + sdst);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
+
+  // Half stage (ks, p): blocks 2 p (lanes 0..31) and 2 p + 1 (32..63) of
+  // stage ks.  Its 8 fragments (4 A, 4 B rows of this lane) are read as 8
+  // code bytes + 1 scale byte each, then dequantized into bf16 (two bf16x8
+  // per fragment, one per MFMA) in register set `set`.
+  uint2 raw[8];
+  float sig[8];
+  bf16x8 fr[2][8][2];
+  auto read_half = [&](int ks, int p) {
+    const uint8_t *st = smem + (ks % kFp4BigStages) * kFp4BigStage;
+    const int blk = 2 * p + h;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const bool isb = f >= 4;
+      const int q = (isb ? wn : wm) + 32 * (f & 3) + r, qs = q & 127;
+      raw[f] = *reinterpret_cast<const uint2 *>(st + (isb ? kFp4BigCode : 0) + q * kFp4StepBytes +
+                                                16 * (p ^ fp4_swz(q)) + 8 * h);
+      sig[f] = __builtin_amdgcn_cvt_f32_fp8(
+          (int)st[2 * kFp4BigCode + ((isb ? 2 : 0) + (q >> 7)) * kFp4ScaleChunk + (qs & 31) * 16 + (qs >> 5) * 4 + blk],
+          0);
+    }
+  };
+  auto convert = [&](int set, int u) {            // conversion unit u: fragment u / 2, half u % 2
+    const int f = u >> 1;
+    fr[set][f][u & 1] = fp4x8_bf16((u & 1) ? raw[f].y : raw[f].x, sig[f]);
+  };
+  // MFMAs of register set `set`, with the 16 conversion units of the next
+  // half stage (into the other set) between them, one after every second
+  // MFMA, so the VALU dequantization runs beside the MFMA pipe.
+  auto half = [&](int set, int nks, int np) {
+    read_half(nks, np);
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const int e = q >> 4, i = (q >> 2) & 3, j = q & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[set][i][e], fr[set][4 + j][e], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q & 1) convert(set ^ 1, q >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < kFp4BigStages - 1; ++j) issue(j, min(j, ksteps - 1));
+  wait_vmcnt<kPer * (kFp4BigStages - 2)>();
+  asm volatile("s_barrier" ::: "memory");
+  read_half(0, 0);
+#pragma unroll
+  for (int u = 0; u < 16; ++u) convert(0, u);
+  for (int ks = 0; ks < ksteps; ++ks) {
+    // stage ks + 1 (converted during this step) of this wave has landed;
+    // refetches past the end keep the count uniform.  A plain barrier (a
+    // fenced one would drain all DMA in flight): every read of stage ks - 1
+    // happened before it.
+    wait_vmcnt<kPer * (kFp4BigStages - 3)>();
+    asm volatile("s_barrier" ::: "memory");
+    issue(ks + kFp4BigStages - 1, min(ks + kFp4BigStages - 1, ksteps - 1));
+    half(0, ks, 1);          // MFMAs of (ks, 0), conversion of (ks, 1)
+    half(1, ks + 1, 0);      // MFMAs of (ks, 1), conversion of (ks + 1, 0)
+  }
+  wait_vmcnt<0>();   // the refetches land before the workgroup's LDS is released
+
+  const float s = 1.0f / ((*a_gs) * (*b_gs));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn + 32 * j + r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row < M && col < N)
+          C[(size_t)row * (size_t)N + col] = (uint16_t)(Bf16::pack(acc[i][j][v] * s, 0.0f) & 0xffffu);
+      }
+    }
+}
+
+hipError_t launch_nvfp4_big(const uint8_t *A, const uint8_t *SA, const float *a_gs, const uint8_t *B,
+                            const uint8_t *SB, const float *b_gs, int M, int N, int K, uint16_t *C, hipStream_t st) {
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = allow_dynamic_lds((const void *)gemm_nvfp4_big, kFp4BigLds, lds_set);
+  if (e != hipSuccess) return e;
+  const int tiles_m = (M + kFp4BigRows - 1) / kFp4BigRows, tiles_n = (N + kFp4BigRows - 1) / kFp4BigRows;
+  const int tiles = tiles_m * tiles_n;
+  hipLaunchKernelGGL(gemm_nvfp4_big, dim3((unsigned)tiles), dim3(256), kFp4BigLds, st, A, SA, a_gs, B, SB, b_gs, M,
+                     N, K, C, tiles_m, tiles);
+  return hipGetLastError();
+}
+
 template <int NW, int MT, int NT, int S>
 hipError_t launch_nvfp4(const uint8_t *A, const uint8_t *SA, const float *a_gs, const uint8_t *B,
                         const uint8_t *SB, const float *b_gs, int M, int N, int K, uint16_t *C, hipStream_t st) {
@@ -980,9 +1131,10 @@ hipError_t launch_nvfp4(const uint8_t *A, const uint8_t *SA, const float *a_gs, 
 }
 
 // Caller guarantees K % 256 == 0, 0 < M, N, and that the 32 x 32 tile count
-// fits a grid.  Tiles: 32 x 32 up to 256 rows, else 64 x 64 with 3 stages
-// (64 KB of LDS: two workgroups per CU hide each other's LDS and
-// conversion latency; 6 stages and one workgroup per CU ran 1.7x slower).
+// fits a grid.  32 x 32 tiles up to 256 rows, else the 256 x 256 kernel
+// (measured 1.24x faster than 64 x 64 tiles with per-wave K ranges; those
+// ran 1.7x faster with 3 stages and two workgroups per CU than with 6 and
+// one).
 hipError_t gemm_nvfp4(const void *a, const void *sa, const float *a_gs, const void *b, const void *sb,
                       const float *b_gs, int64_t M, int64_t N, int64_t K, void *c, hipStream_t st) {
   const uint8_t *A = (const uint8_t *)a, *B = (const uint8_t *)b;
@@ -995,7 +1147,11 @@ hipError_t gemm_nvfp4(const void *a, const void *sa, const float *a_gs, const vo
     return launch_nvfp4<8, 32, 32, 4>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
   if (M <= 256)
     return launch_nvfp4<4, 32, 32, 8>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+#ifdef GNQ_FP4_SMALL_TILES
   return launch_nvfp4<4, 64, 64, 3>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+#else
+  return launch_nvfp4_big(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+#endif
 }
 
 hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,

@@ -210,11 +210,13 @@ def _run_nvfp4(aq, abuf, ga, bq, bbuf, gb, M, N):
     return P.bits16(o)
 
 
-# 32 x 32 tiles up to 256 rows (8 waves when K % 512 == 0, else 4), 64 x 64
-# beyond; shapes cross 128-row scale tiles and have ragged edges; K from
-# 256 (one stage per wave) up
+# 32 x 32 tiles up to 256 rows (8 waves when K % 512 == 0, else 4), 256 x 256
+# beyond; shapes cross 128-row scale tiles and have ragged edges (a partial
+# 256-row tile with and without its second 128-row group); K from 256 (one
+# stage per wave; fewer stages than the large kernel's ring) up
 NVFP4_SHAPES = [(1, 8, 256), (5, 300, 512), (32, 64, 1024), (33, 100, 256), (200, 130, 2048),
-                (130, 257, 768), (64, 1000, 1024), (300, 200, 512), (257, 70, 768)]
+                (130, 257, 768), (64, 1000, 1024), (300, 200, 512), (257, 70, 768), (600, 520, 1024),
+                (520, 700, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", NVFP4_SHAPES)
