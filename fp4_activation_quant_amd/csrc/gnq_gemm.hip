@@ -959,7 +959,6 @@ gemm_nvfp4_k(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
                                                         int, int, uint16_t *, int);
 GNQ_GEMM_FP4_INST(4, 32, 32, 8)
 GNQ_GEMM_FP4_INST(8, 32, 32, 4)
-GNQ_GEMM_FP4_INST(4, 64, 64, 3)
 #undef GNQ_GEMM_FP4_INST
 
 // Many rows: 256 x 256 workgroup tiles (4 waves of 128 x 128, 16 MFMA tiles
@@ -1139,19 +1138,12 @@ hipError_t gemm_nvfp4(const void *a, const void *sa, const float *a_gs, const vo
                       const float *b_gs, int64_t M, int64_t N, int64_t K, void *c, hipStream_t st) {
   const uint8_t *A = (const uint8_t *)a, *B = (const uint8_t *)b;
   const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
-#ifdef GNQ_FP4_TILE
-  return launch_nvfp4<GNQ_FP4_TILE>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-#endif
   // up to 256 rows: 32 x 32 tiles (enough workgroups), 8 waves when K allows
   if (M <= 256 && K % 512 == 0)
     return launch_nvfp4<8, 32, 32, 4>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
   if (M <= 256)
     return launch_nvfp4<4, 32, 32, 8>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-#ifdef GNQ_FP4_SMALL_TILES
-  return launch_nvfp4<4, 64, 64, 3>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-#else
   return launch_nvfp4_big(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-#endif
 }
 
 hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,
