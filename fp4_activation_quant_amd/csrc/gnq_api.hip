@@ -12,6 +12,7 @@
 
 #include "gemma_norm_quant.h"
 #include "gnq_common.hpp"
+#include "gnq_gemm.hpp"
 
 namespace gnq {
 namespace {

@@ -327,11 +327,5 @@ hipError_t quant_fp16_fp8(const QuantArgs &a);
 hipError_t quant_fp16_nvfp4(const QuantArgs &a);
 hipError_t quant_bf16_mxfp8(const QuantArgs &a);
 hipError_t quant_fp16_mxfp8(const QuantArgs &a);
-// Consumer GEMM of the quantized activation (gnq_gemm.hip).
-hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,
-                    const float *a_scale, const float *b_scale, int64_t M, int64_t N, int64_t K,
-                    void *c, hipStream_t st);
-hipError_t gemm_nvfp4(const void *a, const void *sa, const float *a_gs, const void *b, const void *sb,
-                      const float *b_gs, int64_t M, int64_t N, int64_t K, void *c, hipStream_t st);
 
 }  // namespace gnq

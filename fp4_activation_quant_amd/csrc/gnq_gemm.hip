@@ -31,6 +31,7 @@
 #include <atomic>
 
 #include "gnq_common.hpp"
+#include "gnq_gemm.hpp"
 
 namespace gnq {
 
