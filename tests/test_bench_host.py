@@ -1,0 +1,55 @@
+"""Host logic of bench.py without a GPU: the algorithmic byte count that the
+roofline's `achieved` divides by, and the refusal of a multi-GPU run."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from fp4_activation_quant_amd.workloads import WORKLOADS  # noqa: E402
+
+# Bytes per call, worked out by hand from the op's traffic: read x (2 bytes
+# per element) and the residual (2), write the residual back (2), y (2) when
+# it is written, and the codes (FP8: 1 byte per element; NVFP4: 1/2 plus one
+# scale byte per 16 elements); once per call the weight (2 H) and the
+# 4-byte scale.  E.g. M = 16, H = 2048, FP8 with residual and y:
+# 16 * 2048 * 9 + 2 * 2048 + 4 = 299012.
+EXPECTED = {
+    "fp8_m16_h2048_bf16_y": 299_012,
+    "fp8_decode_m1_h4096_bf16": 36_868,
+    "fp8_decode_m8_h4096_bf16": 237_572,
+    "fp8_decode_m64_h4096_bf16": 1_843_204,
+    "fp8_decode_m256_h4096_bf16": 7_348_228,
+    "nvfp4_prefill_m8192_h4096_bf16_y": 287_318_020,
+    "fp8_res_m4096_h5120_fp16": 146_810_884,
+    "fp8_nores_m4096_h5120_fp16": 62_924_804,
+    "nvfp4_res_m4096_h5120_fp16": 137_635_844,
+    "nvfp4_nores_m4096_h5120_fp16": 53_749_764,
+    "nvfp4_m32768_h8192_bf16_y": 2_298_494_980,
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXPECTED))
+def test_algorithmic_bytes(name):
+    rd, wr = bench.algorithmic_bytes(WORKLOADS[name])
+    assert rd + wr == EXPECTED[name]
+
+
+def test_mxfp8_bytes_have_no_scale_read_and_one_code_byte_per_element():
+    wl = WORKLOADS["mxfp8_m32768_h8192_bf16_y"]
+    rd, wr = bench.algorithmic_bytes(wl)
+    MH = wl.M * wl.H
+    assert rd == 4 * MH + 2 * wl.H                       # x, residual, weight; no scale
+    assert wr == 2 * MH + 2 * MH + MH + MH // 32         # residual, y, codes, E8M0 scales
+
+
+def test_multi_gpu_run_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
