@@ -136,7 +136,7 @@ def copy_calibration(args):
 
 
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 MFMA
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA
 
 
 def _time_graph(launch, steps, warmup, stream):
@@ -248,7 +248,7 @@ def gemm_main(args):
     ms_per_step = wall * 1e3 / args.steps
     # Bound: whichever of the MFMA time at peak and the HBM time of the
     # operands and output at peak is longer (few activation rows: HBM).
-    # the NVFP4 consumer runs the bf16 MFMA on exactly dequantized operands
+    # the NVFP4 consumer runs the fp16 MFMA on exactly dequantized operands
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if nv else MFMA_FP8_PEAK_TFLOPS
     hbm_bound = (in_bytes + out_bytes) / (HBM_PEAK_GBS * 1e9) > flop / (mfma_peak * 1e12)
     if hbm_bound:
@@ -269,7 +269,7 @@ def gemm_main(args):
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("nvfp4 (e2m1 + e4m3 block scales; bf16 MFMA)" if nv else
+        "dtype": ("nvfp4 (e2m1 + e4m3 block scales; fp16 MFMA)" if nv else
                   "mxfp8 (e4m3 + e8m0)" if mx else "e4m3"), "data": "synthetic",
         "config": {"workload": gw.name, "M": M, "N": N, "K": K, "mode": gw.mode,
                    "bytes_in": in_bytes, "bytes_out": out_bytes},

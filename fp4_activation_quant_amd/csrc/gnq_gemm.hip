@@ -8,7 +8,7 @@
 //    unit block scale, the product of the two tensor scales applied to the
 //    fp32 accumulator;
 //  * NVFP4: packed E2M1 codes with 128x4-tiled E4M3 block scales, dequantized
-//    exactly to bf16 in registers for the bf16 MFMA (gemm_nvfp4 below).
+//    exactly to fp16 in registers for the fp16 MFMA (gemm_nvfp4 below).
 //
 // Operand layout of the MFMA (32 x 32 output, K = 64 per instruction,
 // measured on the chip with a one-wave probe): lane l supplies row (or
@@ -788,15 +788,15 @@ hipError_t launch_decode(const uint8_t *A, const uint8_t *SA, const uint8_t *B, 
 // block scales per 16 elements in the 128x4-tiled buffer; dq = code x scale
 // / gs).  The block-scaled MFMA takes only power-of-two (E8M0) scales, and a
 // code times an E4M3 scale has up to 5 significant bits (not exact in any
-// 8-bit format), so the operands are dequantized exactly to bf16 (8
-// significant bits) in registers and fed to the bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16; its operand and accumulator layout, measured
-// with a one-wave probe, match the block-scaled one's for rows and outputs);
-// 1 / (gs_a gs_b) is applied to the fp32 sum.  The hardware's scaled
-// E2M1 -> bf16 conversion uses only the exponent of its scale (probe), so
-// the conversion is by hand: magnitudes -> the E4M3 byte of the same value
-// by a byte permute on a table, E4M3 -> fp32 by the hardware convert, times
-// the decoded block scale (exact), upper 16 bits (exact).
+// 8-bit format), so the operands are dequantized exactly to fp16 (11
+// significant bits; every such product lies in fp16's normal range) in
+// registers and fed to the fp16 MFMA (v_mfma_f32_32x32x16_f16; its operand
+// and accumulator layout, measured with a one-wave probe, match the
+// block-scaled one's for rows and outputs); 1 / (gs_a gs_b) is applied to
+// the fp32 sum.  The hardware's scaled E2M1 -> fp16 conversion applies only
+// the exponent of its scale (probe), so a block scale is split into a power
+// of two for the conversion and a 3-bit significand applied by one packed
+// fp16 multiply per two elements (fp4x8_f16 below).
 //
 // Structure of the decode kernel: a workgroup owns an MT x NT tile, its NW
 // waves split K into contiguous ranges, each streaming its range through a
@@ -809,8 +809,8 @@ hipError_t launch_decode(const uint8_t *A, const uint8_t *SA, const uint8_t *B, 
 // K positions need not follow the blocks.  Code rows are 32 bytes; their
 // 16-byte halves are swapped on every other group of 8 rows (g(q) =
 // (q / 8) % 2) to halve the LDS bank conflicts of those reads.
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 constexpr int kFp4StepK = 64;                       // K elements per stage
 constexpr int kFp4StepBytes = kFp4StepK / 2;        // code bytes per row per stage
 constexpr int kFp4ScaleChunk = 512;                 // 128 rows x 4 blocks of scales
@@ -818,23 +818,32 @@ constexpr int kFp4ScaleChunk = 512;                 // 128 rows x 4 blocks of sc
 __device__ __forceinline__ int fp4_swz(int row) { return (row >> 3) & 1; }
 
 // 8 E2M1 codes (element 2 j in the low nibble of byte j) times their block
-// scale `sig`, as 8 bf16 (exact).
-__device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w, float sig) {
-  constexpr uint32_t kLutLo = 0x3C383000u, kLutHi = 0x4C484440u;   // E4M3 of 0, .5, 1, 1.5 | 2, 3, 4, 6
-  const uint32_t ev = __builtin_amdgcn_perm(kLutHi, kLutLo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
-  const uint32_t od = __builtin_amdgcn_perm(kLutHi, kLutLo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
-  const f32x2 e01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, false);   // elements 0, 2
-  const f32x2 e23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, true);    // elements 4, 6
-  const f32x2 o01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, false);   // elements 1, 3
-  const f32x2 o23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, true);    // elements 5, 7
-  const float v[8] = {e01[0] * sig, o01[0] * sig, e01[1] * sig, o01[1] * sig,
-                      e23[0] * sig, o23[0] * sig, e23[1] * sig, o23[1] * sig};
-  u32x4 out;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    out[j] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, v[2 * j + 1]), __builtin_bit_cast(uint32_t, v[2 * j]),
-                                   0x07060302u);
-  return __builtin_bit_cast(bf16x8, out);
+// scale, as 8 fp16 (exact: a code times an E4M3 scale has at most 5
+// significant bits and lies within fp16's normal range).  The hardware's
+// packed FP4 -> fp16 conversion (v_cvt_scalef32_pk_f16_fp4; operand byte j
+// gives elements 2 j, 2 j + 1, low nibble first) applies only the exponent
+// of its fp32 scale operand (probed: 1.125, 1.5 and 1.875 act as 1, 3 as 2,
+// 2^-9 and 448 as 2^-9 and 256), so it is passed `sig` for the power of two
+// and the packed fp16 multiply by `mant` supplies the significand
+// (fp4_block_scale).  Intermediates stay normal: code x 2^E lies in
+// [2^-9, 3072] for E4M3 scales.
+__device__ __forceinline__ f16x8 fp4x8_f16(uint32_t w, float sig, f16x2 mant) {
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sig, 0) * mant;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sig, 1) * mant;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sig, 2) * mant;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sig, 3) * mant;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Splits a block scale v (the fp32 value of its E4M3 byte) as v = M 2^E,
+// M = frexp mantissa in [0.5, 1) with v's sign: `mant` = M as a packed fp16
+// pair (exact, 3 significant bits) and `sig` = 2 |v|, whose exponent field is
+// E.  A zero scale gives M = 0 and a NaN scale M = NaN, so the products come
+// out as the plain multiply gives them.
+__device__ __forceinline__ void fp4_block_scale(float v, float &sig, f16x2 &mant) {
+  sig = __builtin_fabsf(v) + __builtin_fabsf(v);
+  const _Float16 mh = (_Float16)__builtin_amdgcn_frexp_mantf(v);
+  mant = f16x2{mh, mh};
 }
 
 template <int NW, int MT, int NT, int S>
@@ -902,23 +911,27 @@ gemm_nvfp4_k(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
 #pragma unroll
     for (int p = 0; p < 2; ++p) {                 // half stage: blocks 2 p (lanes 0..31), 2 p + 1 (32..63)
       const int blk = 2 * p + h;
-      bf16x8 bf[kTN][2], af[kTM][2];
+      f16x8 bf[kTN][2], af[kTM][2];
 #pragma unroll
       for (int jj = 0; jj < kTN; ++jj) {
         const int q = 32 * jj + bq0, qs = bs0 + q;
         const uint2 w = *reinterpret_cast<const uint2 *>(st + q * kFp4StepBytes + 16 * (p ^ fp4_swz(q)) + 8 * h);
-        const float sig = __builtin_amdgcn_cvt_f32_fp8((int)sch[(qs & 31) * 16 + (qs >> 5) * 4 + blk], 0);
-        bf[jj][0] = fp4x8_bf16(w.x, sig);
-        bf[jj][1] = fp4x8_bf16(w.y, sig);
+        float sig;
+        f16x2 mant;
+        fp4_block_scale(__builtin_amdgcn_cvt_f32_fp8((int)sch[(qs & 31) * 16 + (qs >> 5) * 4 + blk], 0), sig, mant);
+        bf[jj][0] = fp4x8_f16(w.x, sig, mant);
+        bf[jj][1] = fp4x8_f16(w.y, sig, mant);
       }
 #pragma unroll
       for (int i = 0; i < kTM; ++i) {
         const int q = 32 * i + aq0, qs = as0 + q;
         const uint2 w = *reinterpret_cast<const uint2 *>(st + kCodeB + q * kFp4StepBytes + 16 * (p ^ fp4_swz(q)) + 8 * h);
-        const float sig =
-            __builtin_amdgcn_cvt_f32_fp8((int)sch[kFp4ScaleChunk + (qs & 31) * 16 + (qs >> 5) * 4 + blk], 0);
-        af[i][0] = fp4x8_bf16(w.x, sig);
-        af[i][1] = fp4x8_bf16(w.y, sig);
+        float sig;
+        f16x2 mant;
+        fp4_block_scale(__builtin_amdgcn_cvt_f32_fp8((int)sch[kFp4ScaleChunk + (qs & 31) * 16 + (qs >> 5) * 4 + blk], 0),
+                        sig, mant);
+        af[i][0] = fp4x8_f16(w.x, sig, mant);
+        af[i][1] = fp4x8_f16(w.y, sig, mant);
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e)
@@ -926,7 +939,7 @@ gemm_nvfp4_k(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
         for (int i = 0; i < kTM; ++i)
 #pragma unroll
           for (int jj = 0; jj < kTN; ++jj)
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][e], bf[jj][e], acc[i][jj], 0, 0, 0);
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i][e], bf[jj][e], acc[i][jj], 0, 0, 0);
     }
   }
 
@@ -1026,63 +1039,87 @@ gemm_nvfp4_big(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, co
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
 
-  // Half stage (ks, p): blocks 2 p (lanes 0..31) and 2 p + 1 (32..63) of
-  // stage ks.  Its 8 fragments (4 A, 4 B rows of this lane) are read as 8
-  // code bytes + 1 scale byte each, then dequantized into bf16 (two bf16x8
-  // per fragment, one per MFMA) in register set `set`.
-  uint2 raw[8];
-  float sig[8];
-  bf16x8 fr[2][8][2];
-  auto read_half = [&](int ks, int p) {
+  // K pairing: lanes of half h (lanes 32 h .. 32 h + 31) take global chunk h
+  // of a row's 64-element step, blocks 2 h and 2 h + 1; half stage p feeds
+  // block 2 h + p to the 32 MFMAs (two of K 16 per tile) of that half.  A
+  // step's fragments -- 8 rows (4 of A, 4 of B) of 16 code bytes and the two
+  // scale bytes of those blocks -- are read into one of two buffers during
+  // the half stage before their first conversion, so the LDS latency runs
+  // beside the MFMAs.  Within a 32-row slice the lane's offsets are the same for every
+  // fragment (the chunk swizzle depends on the row's bits 3 only).
+  const int lane_code = r * kFp4StepBytes + 16 * (h ^ fp4_swz(r));
+  const int lane_scale = r * 16 + 2 * h;
+  uint4 raw[2][8];
+  uint32_t scw[2][8];
+  f16x8 fr[2][8][2];
+  // Read item t of step ks into buffer `buf`: fragment t / 2, its codes
+  // (t even) or its scale bytes (t odd).
+  auto read_item = [&](int buf, int ks, int t) {
     const uint8_t *st = smem + (ks % kFp4BigStages) * kFp4BigStage;
-    const int blk = 2 * p + h;
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const bool isb = f >= 4;
-      const int q = (isb ? wn : wm) + 32 * (f & 3) + r, qs = q & 127;
-      raw[f] = *reinterpret_cast<const uint2 *>(st + (isb ? kFp4BigCode : 0) + q * kFp4StepBytes +
-                                                16 * (p ^ fp4_swz(q)) + 8 * h);
-      sig[f] = __builtin_amdgcn_cvt_f32_fp8(
-          (int)st[2 * kFp4BigCode + ((isb ? 2 : 0) + (q >> 7)) * kFp4ScaleChunk + (qs & 31) * 16 + (qs >> 5) * 4 + blk],
-          0);
-    }
+    const int f = t >> 1;
+    const bool isb = f >= 4;
+    const int q0 = (isb ? wn : wm) + 32 * (f & 3);
+    if ((t & 1) == 0)
+      raw[buf][f] = *reinterpret_cast<const uint4 *>(st + (isb ? kFp4BigCode : 0) + q0 * kFp4StepBytes + lane_code);
+    else
+      scw[buf][f] = *reinterpret_cast<const uint16_t *>(st + 2 * kFp4BigCode +
+                                                        ((isb ? 2 : 0) + (q0 >> 7)) * kFp4ScaleChunk + (f & 3) * 4 +
+                                                        lane_scale);
   };
-  auto convert = [&](int set, int u) {            // conversion unit u: fragment u / 2, half u % 2
+  // Conversion unit u of half stage p from buffer `buf`: fragment u / 2,
+  // MFMA half u % 2 (8 elements), into register set `set`.
+  float sig;
+  f16x2 mant;
+  auto convert = [&](int set, int buf, int p, int u) {
     const int f = u >> 1;
-    fr[set][f][u & 1] = fp4x8_bf16((u & 1) ? raw[f].y : raw[f].x, sig[f]);
+    if ((u & 1) == 0)
+      fp4_block_scale(p ? __builtin_amdgcn_cvt_f32_fp8((int)scw[buf][f], 1) : __builtin_amdgcn_cvt_f32_fp8((int)scw[buf][f], 0),
+                      sig, mant);
+    const uint32_t w = p ? ((u & 1) ? raw[buf][f].w : raw[buf][f].z) : ((u & 1) ? raw[buf][f].y : raw[buf][f].x);
+    fr[set][f][u & 1] = fp4x8_f16(w, sig, mant);
   };
   // MFMAs of register set `set`, with the 16 conversion units of the next
-  // half stage (into the other set) between them, one after every second
-  // MFMA, so the VALU dequantization runs beside the MFMA pipe.
-  auto half = [&](int set, int nks, int np) {
-    read_half(nks, np);
+  // half stage (buffer `buf`, half `np`, into the other set) between them,
+  // one after every second MFMA, so the VALU dequantization runs beside the
+  // MFMA pipe; with `rd`, the 16 read items of step `rks` into buffer `rbuf`
+  // go between the others, spread so that the four waves' LDS reads do not
+  // arrive as one burst.
+  auto half = [&](int set, int buf, int np, bool rd, int rbuf, int rks) {
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
       const int e = q >> 4, i = (q >> 2) & 3, j = q & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[set][i][e], fr[set][4 + j][e], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[set][i][e], fr[set][4 + j][e], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (q & 1) convert(set ^ 1, q >> 1);
+      if (q & 1)
+        convert(set ^ 1, buf, np, q >> 1);
+      else if (rd)
+        read_item(rbuf, rks, q >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // Step ks from buffer `cur`; step ks + 1 (landed, per the wait) is read
+  // into buffer `nxt` during the first half.  A plain barrier (a fenced one would drain all DMA in
+  // flight): every read of stage ks - 1 happened before it, so its slot can
+  // be refilled; refetches past the end keep the DMA count uniform.
+  auto step = [&](int ks, int cur, int nxt) {
+    wait_vmcnt<kPer * (kFp4BigStages - 3)>();
+    asm volatile("s_barrier" ::: "memory");
+    issue(ks + kFp4BigStages - 1, min(ks + kFp4BigStages - 1, ksteps - 1));
+    half(0, cur, 1, true, nxt, ks + 1);   // MFMAs of (ks, 0), conversion of (ks, 1), reads of ks + 1
+    half(1, nxt, 0, false, 0, 0);         // MFMAs of (ks, 1), conversion of (ks + 1, 0)
   };
 
 #pragma unroll
   for (int j = 0; j < kFp4BigStages - 1; ++j) issue(j, min(j, ksteps - 1));
   wait_vmcnt<kPer * (kFp4BigStages - 2)>();
   asm volatile("s_barrier" ::: "memory");
-  read_half(0, 0);
 #pragma unroll
-  for (int u = 0; u < 16; ++u) convert(0, u);
-  for (int ks = 0; ks < ksteps; ++ks) {
-    // stage ks + 1 (converted during this step) of this wave has landed;
-    // refetches past the end keep the count uniform.  A plain barrier (a
-    // fenced one would drain all DMA in flight): every read of stage ks - 1
-    // happened before it.
-    wait_vmcnt<kPer * (kFp4BigStages - 3)>();
-    asm volatile("s_barrier" ::: "memory");
-    issue(ks + kFp4BigStages - 1, min(ks + kFp4BigStages - 1, ksteps - 1));
-    half(0, ks, 1);          // MFMAs of (ks, 0), conversion of (ks, 1)
-    half(1, ks + 1, 0);      // MFMAs of (ks, 1), conversion of (ks + 1, 0)
+  for (int t = 0; t < 16; ++t) read_item(0, 0, t);
+#pragma unroll
+  for (int u = 0; u < 16; ++u) convert(0, 0, 0, u);
+  for (int ks = 0; ks < ksteps; ks += 2) {   // ksteps is even (K % 256 == 0)
+    step(ks, 0, 1);
+    step(ks + 1, 1, 0);
   }
   wait_vmcnt<0>();   // the refetches land before the workgroup's LDS is released
 
