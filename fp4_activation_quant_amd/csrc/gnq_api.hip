@@ -237,7 +237,7 @@ nq_status nq_gemm_nvfp4(const void *a, const void *a_scales, const float *a_gs, 
       K > ((int64_t)1 << 24))
     return NQ_EINVAL;
   if (!a || !b || !a_scales || !b_scales || !a_gs || !b_gs || !out) return NQ_EINVAL;
-  if (K % 256 != 0) return NQ_EUNSUPPORTED;
+  if (K % 64 != 0) return NQ_EUNSUPPORTED;
   if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)a_scales | (uintptr_t)b_scales) % 16 != 0 ||
       (uintptr_t)out % 2 != 0 || ((uintptr_t)a_gs | (uintptr_t)b_gs) % 4 != 0)
     return NQ_EINVAL;

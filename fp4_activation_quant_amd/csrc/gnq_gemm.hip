@@ -866,7 +866,9 @@ gemm_nvfp4_k(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   const int m0 = tm * MT, n0 = tn * NT;
   const int ksteps = K / kFp4StepK;             // stages over all of K
-  const int J = ksteps / NW;                    // this wave's stages: wave J .. (wave + 1) J - 1
+  // this wave's stages: j0 .. j0 + J - 1 (an even split; J may be 0)
+  const int j0 = (wave * ksteps) / NW;
+  const int J = ((wave + 1) * ksteps) / NW - j0;
   const size_t rowb = (size_t)K / 2;
   uint8_t *wl = smem + wave * S * kStage;
 
@@ -878,12 +880,12 @@ gemm_nvfp4_k(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
   for (int i = 0; i < kCSeg; ++i) {
     const int q = 32 * (i < kBSeg ? i : i - kBSeg) + (lane >> 1);
     const size_t row = i < kBSeg ? (size_t)min(n0 + q, N - 1) : (size_t)min(m0 + q, M - 1);
-    src[i] = (i < kBSeg ? B : A) + row * rowb + (size_t)wave * J * kFp4StepBytes + 16 * ((lane & 1) ^ fp4_swz(q));
+    src[i] = (i < kBSeg ? B : A) + row * rowb + (size_t)j0 * kFp4StepBytes + 16 * ((lane & 1) ^ fp4_swz(q));
   }
   // Scale chunk of stage j: lanes 0..31 the weight's 512 bytes, 32..63 the
   // activation's, each 16 bytes.
-  const uint8_t *ssrc = lane < 32 ? SB + ((size_t)(n0 / 128) * ksteps + (size_t)wave * J) * kFp4ScaleChunk + 16 * lane
-                                  : SA + ((size_t)(m0 / 128) * ksteps + (size_t)wave * J) * kFp4ScaleChunk + 16 * (lane - 32);
+  const uint8_t *ssrc = lane < 32 ? SB + ((size_t)(n0 / 128) * ksteps + (size_t)j0) * kFp4ScaleChunk + 16 * lane
+                                  : SA + ((size_t)(m0 / 128) * ksteps + (size_t)j0) * kFp4ScaleChunk + 16 * (lane - 32);
   auto issue = [&](int j) {
     uint8_t *dst = wl + (j % S) * kStage;
 #pragma unroll
@@ -1117,10 +1119,12 @@ gemm_nvfp4_big(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, co
   for (int t = 0; t < 16; ++t) read_item(0, 0, t);
 #pragma unroll
   for (int u = 0; u < 16; ++u) convert(0, 0, 0, u);
-  for (int ks = 0; ks < ksteps; ks += 2) {   // ksteps is even (K % 256 == 0)
+  int ks = 0;
+  for (; ks + 1 < ksteps; ks += 2) {
     step(ks, 0, 1);
     step(ks + 1, 1, 0);
   }
+  if (ks < ksteps) step(ks, 0, 1);             // odd step count
   wait_vmcnt<0>();   // the refetches land before the workgroup's LDS is released
 
   const float s = 1.0f / ((*a_gs) * (*b_gs));
@@ -1167,7 +1171,7 @@ hipError_t launch_nvfp4(const uint8_t *A, const uint8_t *SA, const float *a_gs, 
   return hipGetLastError();
 }
 
-// Caller guarantees K % 256 == 0, 0 < M, N, and that the 32 x 32 tile count
+// Caller guarantees K % 64 == 0, 0 < M, N, and that the 32 x 32 tile count
 // fits a grid.  32 x 32 tiles up to 256 rows, else the 256 x 256 kernel
 // (measured 1.24x faster than 64 x 64 tiles with per-wave K ranges; those
 // ran 1.7x faster with 3 stages and two workgroups per CU than with 6 and
@@ -1176,7 +1180,8 @@ hipError_t gemm_nvfp4(const void *a, const void *sa, const float *a_gs, const vo
                       const float *b_gs, int64_t M, int64_t N, int64_t K, void *c, hipStream_t st) {
   const uint8_t *A = (const uint8_t *)a, *B = (const uint8_t *)b;
   const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
-  // up to 256 rows: 32 x 32 tiles (enough workgroups), 8 waves when K allows
+  // up to 256 rows: 32 x 32 tiles (enough workgroups); 8 waves splitting K
+  // when it divides into 8 equal ranges, else 4 (ranges may differ by a stage)
   if (M <= 256 && K % 512 == 0)
     return launch_nvfp4<8, 32, 32, 4>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
   if (M <= 256)

@@ -273,7 +273,7 @@ def gemm_nvfp4(a, a_block_scale, a_global_scale, b, b_block_scale, b_global_scal
     _validate_codes(b, "b")
     M, K = a.shape[0], 2 * a.shape[1]
     N = b.shape[0]
-    _require(b.shape[1] == K // 2 and K % 256 == 0, "b: (N, K // 2) with the same K; K % 256 == 0")
+    _require(b.shape[1] == K // 2 and K % 64 == 0, "b: (N, K // 2) with the same K; K % 64 == 0")
     for name, bs, rows in (("a_block_scale", a_block_scale, M), ("b_block_scale", b_block_scale, N)):
         _require(bs.is_cuda and bs.is_contiguous() and bs.numel() * bs.element_size() >= _lib.nq_block_scale_bytes(rows, K),
                  f"{name}: contiguous device buffer of block_scale_bytes(rows, K) bytes")

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define NQ_ABI_VERSION 5
+#define NQ_ABI_VERSION 6
 
 typedef enum {
   NQ_OK = 0,
@@ -209,12 +209,13 @@ nq_status nq_gemm_fp8_static(const void *a, const float *a_scale, const void *b,
  * 16 elements); a_gs / b_gs DEVICE pointers to the fp32 global scale each
  * operand was quantized with (the op's `scale` in NVFP4 mode).
  *   dq(x)[r, k] = E2M1(code) * E4M3(scale[r, k/16]) / gs.
- * The products are exact in fp32 (each dequantized value fits bf16); the
+ * The products are exact in fp32 (each dequantized value has at most 5
+ * significant bits and lies in [2^-10, 2688] in magnitude, or is 0); the
  * sum is accumulated in fp32 and multiplied by 1 / (gs_a gs_b) before the
  * rounding to bf16.  Scale bytes of rows >= M (>= N) are read (they share
  * 512-byte tiles with real rows) but only reach outputs that are not
  * written.
- *   M, N >= 0 (either 0: NQ_OK, nothing launched); K > 0 with K % 256 == 0
+ *   M, N >= 0 (either 0: NQ_OK, nothing launched); K > 0 with K % 64 == 0
  *   (NQ_EUNSUPPORTED otherwise); a, b and both scale buffers 16-byte
  *   aligned, out 2-byte aligned, a_gs and b_gs 4-byte aligned, out
  *   overlapping no input (NQ_EINVAL otherwise).

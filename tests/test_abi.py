@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert _lib.nq_abi_version() == 5
+    assert _lib.nq_abi_version() == 6
     assert _lib.nq_status_string(0) == "ok"
     for s in range(0, 6):
         assert isinstance(_lib.nq_status_string(s), str)
@@ -239,7 +239,7 @@ def test_gemm_validation(mx, over, want):
     (dict(out=0), _lib.NQ_EINVAL),
     (dict(K=0), _lib.NQ_EINVAL),
     (dict(N=-1), _lib.NQ_EINVAL),
-    (dict(K=192), _lib.NQ_EUNSUPPORTED),               # K % 256 != 0
+    (dict(K=96), _lib.NQ_EUNSUPPORTED),                # K % 64 != 0
     (dict(sa=S + 8), _lib.NQ_EINVAL),                 # scale buffer not 16-byte aligned
     (dict(ga=S + 2), _lib.NQ_EINVAL),                 # global scale not 4-byte aligned
     (dict(out=X + 64), _lib.NQ_EINVAL),               # out overlaps a

@@ -214,9 +214,12 @@ def _run_nvfp4(aq, abuf, ga, bq, bbuf, gb, M, N):
 # beyond; shapes cross 128-row scale tiles and have ragged edges (a partial
 # 256-row tile with and without its second 128-row group); K from 256 (one
 # stage per wave; fewer stages than the large kernel's ring) up
+# K % 256 != 0 included: 64-element steps split unevenly over the small
+# kernel's waves (some with none) and odd step counts in the large one.
 NVFP4_SHAPES = [(1, 8, 256), (5, 300, 512), (32, 64, 1024), (33, 100, 256), (200, 130, 2048),
                 (130, 257, 768), (64, 1000, 1024), (300, 200, 512), (257, 70, 768), (600, 520, 1024),
-                (520, 700, 256)]
+                (520, 700, 256), (1, 40, 64), (17, 96, 448), (64, 200, 1152), (260, 33, 64),
+                (300, 260, 320), (257, 130, 1152)]
 
 
 @pytest.mark.parametrize("M,N,K", NVFP4_SHAPES)
@@ -238,7 +241,8 @@ def test_nvfp4_gemm_exact_cases(M, N, K, gs):
     assert bad[0].size == 0, (bad[0][:5], bad[1][:5], got[bad][:5], want[bad][:5])
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 96, 4096), (300, 520, 2048), (1, 333, 8192), (256, 512, 4096)])
+@pytest.mark.parametrize("M,N,K", [(17, 96, 4096), (300, 520, 2048), (1, 333, 8192), (256, 512, 4096),
+                                   (300, 520, 2880), (8, 300, 2880)])
 def test_nvfp4_gemm_random(M, N, K):
     print(f"gemm nvfp4 random M={M} N={N} K={K}", flush=True)
     rng = np.random.default_rng(M + 3 * N + K)
@@ -252,13 +256,13 @@ def test_nvfp4_gemm_random(M, N, K):
     _tolerance_check(got, exact, mag)
 
 
-def test_nvfp4_gemm_consumes_the_ops_output():
+@pytest.mark.parametrize("M,H,N", [(300, 4096, 384), (40, 1152, 200)])
+def test_nvfp4_gemm_consumes_the_ops_output(M, H, N):
     """The op's NVFP4 codes, block scales and global scale go straight into
     the consumer; rows whose GPU codes and scales equal the oracle's must
     match the oracle GEMM of the oracle's own output within the tolerance."""
-    print("gemm nvfp4 consumer", flush=True)
+    print(f"gemm nvfp4 consumer M={M} H={H} N={N}", flush=True)
     g = torch.Generator().manual_seed(29)
-    M, H, N = 300, 4096, 384
     x = torch.randn(M, H, generator=g).to(torch.bfloat16)
     r = torch.randn(M, H, generator=g).to(torch.bfloat16)
     w = (torch.randn(H, generator=g) * 0.1).to(torch.bfloat16)
