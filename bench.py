@@ -259,7 +259,8 @@ def gemm_main(args):
                 "peak": mfma_peak, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
-    kernel = (("gemm_nvfp4_big" if M > 256 else "gemm_nvfp4_k") if nv else
+    kernel = (("gemm_nvfp4_gemv" if M <= 8 and M * (K // 32) * 80 <= 128 * 1024 else
+               "gemm_nvfp4_big" if M > 256 else "gemm_nvfp4_k") if nv else
               "gemm_fp8_decode" if M <= 256 and K % 2048 == 0 and K <= 16384 else
               "gemm_fp8_skinny" if M <= 256 and K % 64 == 0 else
               "gemm_fp8_tn_dma" if K % 512 == 0 else "gemm_fp8_tn")

@@ -846,6 +846,14 @@ __device__ __forceinline__ void fp4_block_scale(float v, float &sig, f16x2 &mant
   mant = f16x2{mh, mh};
 }
 
+// Workgroup b runs on XCD b % 8: give each XCD a contiguous range of the
+// n workgroups' tiles, so the workgroups that share a 128-row scale tile
+// share one L2 (a bijection on 0 .. n - 1).
+__device__ __forceinline__ int xcd_contiguous(int b, int n) {
+  const int q = n / kXcds, r = n % kXcds, x = b % kXcds;
+  return x * q + min(x, r) + b / kXcds;
+}
+
 template <int NW, int MT, int NT, int S>
 __global__ void __launch_bounds__(64 * NW)
 gemm_nvfp4_k(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ a_gs,
@@ -863,7 +871,8 @@ gemm_nvfp4_k(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, h = lane >> 5;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int bt = xcd_contiguous(blockIdx.x, gridDim.x);   // consecutive weight tiles on one XCD
+  const int tm = bt / tiles_n, tn = bt % tiles_n;
   const int m0 = tm * MT, n0 = tn * NT;
   const int ksteps = K / kFp4StepK;             // stages over all of K
   // this wave's stages: j0 .. j0 + J - 1 (an even split; J may be 0)
@@ -1171,6 +1180,146 @@ hipError_t launch_nvfp4(const uint8_t *A, const uint8_t *SA, const float *a_gs, 
   return hipGetLastError();
 }
 
+// Few activation rows (M <= 8): a dot-product kernel, since 32-row MFMA
+// tiles would dequantize a mostly padded activation tile for every weight
+// tile.  The workgroup first dequantizes the activation once into LDS as
+// fp16 (row m, 32-element chunk ci at (m * K / 32 + ci) * 80 bytes: the
+// 16-byte pad puts the chunks that 16 consecutive lanes read on distinct
+// banks).  Its 8 waves own 16 weight rows, two per wave (lanes 0..31 and
+// 32..63); lane c of a row takes the row's 16-byte code chunks c, c + 32, ...
+// (32 elements: blocks 2 ci and 2 ci + 1, their two scale bytes adjacent in
+// the tiled buffer), loaded four ahead of their use; the row blocks are laid
+// out contiguously per XCD (xcd_contiguous).  A block's 16 codes are
+// converted at the power of two of its scale (fp4_block_scale), dotted with
+// each activation row by v_dot2_f32_f16 into a block sum (exact products,
+// fp32 sums), and the block's significand multiplies that sum into the row's
+// accumulator.  The 32 lanes' sums of a row meet in a butterfly.
+constexpr int kGemvRows = 16;             // weight rows per workgroup
+constexpr int kGemvChunk = 80;            // LDS bytes per 32-element activation chunk
+constexpr int kGemvMaxLds = 128 * 1024;
+constexpr int kGemvGroup = 4;             // weight chunks per lane in flight
+
+__device__ __forceinline__ size_t nvfp4_scale_offset(int row, int blk, int kp4) {
+  // byte of (row, 16-element block) in the 128x4-tiled buffer, kp4 = K / 64
+  return ((size_t)(row >> 7) * kp4 + (blk >> 2)) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (blk & 3);
+}
+
+template <int MR>
+__global__ void __launch_bounds__(512)
+gemm_nvfp4_gemv(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, const float *__restrict__ a_gs,
+                const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB, const float *__restrict__ b_gs,
+                int M, int N, int K, uint16_t *__restrict__ C) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = K / 32, kp4 = K / 64;
+  const int c = lane & 31;
+  const int row = xcd_contiguous(blockIdx.x, gridDim.x) * kGemvRows + 2 * wave + (lane >> 5);
+  const int rowc = min(row, N - 1);
+  const uint8_t *brow = B + (size_t)rowc * (size_t)(K / 2);
+
+  uint4 code[2][kGemvGroup];
+  uint32_t scw[2][kGemvGroup];
+  // chunks c + 32 (g + j) of group g; past the row's end the last chunk is
+  // refetched (in bounds) and its contribution skipped
+  auto load = [&](int buf, int g) {
+#pragma unroll
+    for (int j = 0; j < kGemvGroup; ++j) {
+      const int ci = min(c + 32 * (g + j), nch - 1);
+      code[buf][j] = *reinterpret_cast<const uint4 *>(brow + (size_t)ci * 16);
+      scw[buf][j] = *reinterpret_cast<const uint16_t *>(SB + nvfp4_scale_offset(rowc, 2 * ci, kp4));
+    }
+  };
+  load(0, 0);
+
+  // the activation, dequantized (code x block scale; 1 / gs comes last)
+  const int units = M * (K / 8);
+  for (int u = tid; u < units; u += 512) {
+    const int m = u / (K / 8), k = (u - m * (K / 8)) * 8;
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(A + (size_t)m * (size_t)(K / 2) + k / 2);
+    float sig;
+    f16x2 mant;
+    fp4_block_scale(__builtin_amdgcn_cvt_f32_fp8((int)SA[nvfp4_scale_offset(m, k / 16, kp4)], 0), sig, mant);
+    *reinterpret_cast<f16x8 *>(smem + ((size_t)m * nch + k / 32) * kGemvChunk + (k % 32) * 2) =
+        fp4x8_f16(w, sig, mant);
+  }
+  __syncthreads();
+
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+  const int groups = (nch + 31) / 32;          // chunk groups of 32 per row, kGemvGroup at a time
+  for (int g = 0; g < groups; g += 2 * kGemvGroup) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int gg = g + half * kGemvGroup;
+      if (gg >= groups) break;
+      if (gg + kGemvGroup < groups) load(half ^ 1, gg + kGemvGroup);
+#pragma unroll
+      for (int j = 0; j < kGemvGroup; ++j) {
+        const int ci = c + 32 * (gg + j);
+        if (ci >= nch) continue;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const float v = blk ? __builtin_amdgcn_cvt_f32_fp8((int)scw[half][j], 1)
+                              : __builtin_amdgcn_cvt_f32_fp8((int)scw[half][j], 0);
+          const float sig = __builtin_fabsf(v) + __builtin_fabsf(v);
+          const float mant = __builtin_amdgcn_frexp_mantf(v);
+          const uint32_t w0 = blk ? code[half][j].z : code[half][j].x;
+          const uint32_t w1 = blk ? code[half][j].w : code[half][j].y;
+          f16x2 bp[8];
+          bp[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, sig, 0);
+          bp[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, sig, 1);
+          bp[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, sig, 2);
+          bp[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, sig, 3);
+          bp[4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, sig, 0);
+          bp[5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, sig, 1);
+          bp[6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, sig, 2);
+          bp[7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, sig, 3);
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            if (m >= M) break;
+            const uint8_t *ap = smem + ((size_t)m * nch + ci) * kGemvChunk + blk * 32;
+            const uint4 a0 = *reinterpret_cast<const uint4 *>(ap);
+            const uint4 a1 = *reinterpret_cast<const uint4 *>(ap + 16);
+            float t = 0.0f;
+            t = __builtin_amdgcn_fdot2(bp[0], __builtin_bit_cast(f16x2, a0.x), t, false);
+            t = __builtin_amdgcn_fdot2(bp[1], __builtin_bit_cast(f16x2, a0.y), t, false);
+            t = __builtin_amdgcn_fdot2(bp[2], __builtin_bit_cast(f16x2, a0.z), t, false);
+            t = __builtin_amdgcn_fdot2(bp[3], __builtin_bit_cast(f16x2, a0.w), t, false);
+            t = __builtin_amdgcn_fdot2(bp[4], __builtin_bit_cast(f16x2, a1.x), t, false);
+            t = __builtin_amdgcn_fdot2(bp[5], __builtin_bit_cast(f16x2, a1.y), t, false);
+            t = __builtin_amdgcn_fdot2(bp[6], __builtin_bit_cast(f16x2, a1.z), t, false);
+            t = __builtin_amdgcn_fdot2(bp[7], __builtin_bit_cast(f16x2, a1.w), t, false);
+            acc[m] = __builtin_fmaf(t, mant, acc[m]);
+          }
+        }
+      }
+    }
+  }
+
+  const float s = 1.0f / ((*a_gs) * (*b_gs));
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    if (m >= M) break;
+    float v = acc[m];
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (c == 0 && row < N) C[(size_t)m * (size_t)N + row] = (uint16_t)(Bf16::pack(v * s, 0.0f) & 0xffffu);
+  }
+}
+
+template <int MR>
+hipError_t launch_nvfp4_gemv(const uint8_t *A, const uint8_t *SA, const float *a_gs, const uint8_t *B,
+                             const uint8_t *SB, const float *b_gs, int M, int N, int K, uint16_t *C, hipStream_t st) {
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = allow_dynamic_lds((const void *)gemm_nvfp4_gemv<MR>, kGemvMaxLds, lds_set);
+  if (e != hipSuccess) return e;
+  const int lds = M * (K / 32) * kGemvChunk;
+  hipLaunchKernelGGL((gemm_nvfp4_gemv<MR>), dim3((unsigned)((N + kGemvRows - 1) / kGemvRows)), dim3(512), lds, st,
+                     A, SA, a_gs, B, SB, b_gs, M, N, K, C);
+  return hipGetLastError();
+}
+
 // Caller guarantees K % 64 == 0, 0 < M, N, and that the 32 x 32 tile count
 // fits a grid.  32 x 32 tiles up to 256 rows, else the 256 x 256 kernel
 // (measured 1.24x faster than 64 x 64 tiles with per-wave K ranges; those
@@ -1180,6 +1329,13 @@ hipError_t gemm_nvfp4(const void *a, const void *sa, const float *a_gs, const vo
                       const float *b_gs, int64_t M, int64_t N, int64_t K, void *c, hipStream_t st) {
   const uint8_t *A = (const uint8_t *)a, *B = (const uint8_t *)b;
   const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
+  // up to 8 rows whose dequantized activation fits the LDS: dot products
+  if (M <= 8 && M * (K / 32) * (int64_t)kGemvChunk <= kGemvMaxLds) {
+    if (M == 1) return launch_nvfp4_gemv<1>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+    if (M == 2) return launch_nvfp4_gemv<2>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+    if (M <= 4) return launch_nvfp4_gemv<4>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+    return launch_nvfp4_gemv<8>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+  }
   // up to 256 rows: 32 x 32 tiles (enough workgroups); 8 waves splitting K
   // when it divides into 8 equal ranges, else 4 (ranges may differ by a stage)
   if (M <= 256 && K % 512 == 0)
