@@ -172,12 +172,34 @@ def _validate_y(y):
              "y: contiguous 2-D bfloat16/float16 device tensor")
 
 
+def _buf(t, name, dev, shape=None, nbytes=None, itemsize=None, dtype=None):
+    """A caller-supplied tensor the library reads or writes by pointer:
+    contiguous, on ``dev``, and of the stated shape / size / element type."""
+    _require(isinstance(t, torch.Tensor) and t.is_cuda and t.device == dev and t.is_contiguous(),
+             f"{name}: contiguous tensor on {dev}")
+    if shape is not None:
+        _require(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(shape)}, got {tuple(t.shape)}")
+    if nbytes is not None:
+        _require(t.numel() * t.element_size() >= nbytes, f"{name}: at least {nbytes} bytes")
+    if itemsize is not None:
+        _require(t.element_size() == itemsize, f"{name}: {itemsize}-byte elements")
+    if dtype is not None:
+        _require(t.dtype == dtype, f"{name}: {dtype}")
+
+
+def _scalar(t, name, dev):
+    _buf(t, name, dev, dtype=torch.float32)
+    _require(t.numel() == 1, f"{name}: one float32")
+
+
 def quant_fp8_static(y, scale, q=None):
     """Standalone static FP8 quant of an activation: E4M3FN(y / scale)."""
     _validate_y(y)
     M, H = y.shape
+    _scalar(scale, "scale", y.device)
     if q is None:
         q = torch.empty((M, H), dtype=FP8_DTYPE, device=y.device)
+    _buf(q, "q", y.device, shape=(M, H), itemsize=1)
     if M:
         with torch.cuda.device(y.device):
             st = _lib.nq_quant_fp8_static(y.data_ptr(), scale.data_ptr(), M, H, _DT[y.dtype],
@@ -190,11 +212,15 @@ def quant_nvfp4(y, global_scale, q=None, block_scale=None):
     """Standalone NVFP4 quant: packed E2M1 codes and 128x4-tiled E4M3 scales."""
     _validate_y(y)
     M, H = y.shape
+    _require(H % 16 == 0, "the standalone NVFP4 quant needs H % 16 == 0")
+    _scalar(global_scale, "global_scale", y.device)
     if q is None:
         q = torch.empty((M, H // 2), dtype=torch.uint8, device=y.device)
     if block_scale is None:
         block_scale = torch.empty((round_up(M, 128), round_up(H // 16, 4)), dtype=torch.uint8,
                                   device=y.device).view(FP8_DTYPE)
+    _buf(q, "q", y.device, shape=(M, H // 2), itemsize=1)
+    _buf(block_scale, "block_scale", y.device, nbytes=_lib.nq_block_scale_bytes(M, H))
     if M:
         with torch.cuda.device(y.device):
             st = _lib.nq_quant_nvfp4(y.data_ptr(), global_scale.data_ptr(), M, H, _DT[y.dtype],
@@ -208,10 +234,13 @@ def quant_mxfp8(y, q=None, scales=None):
     row-major."""
     _validate_y(y)
     M, H = y.shape
+    _require(H % 32 == 0, "MXFP8 needs H % 32 == 0")
     if q is None:
         q = torch.empty((M, H), dtype=FP8_DTYPE, device=y.device)
     if scales is None:
         scales = torch.empty((M, H // 32), dtype=E8M0_DTYPE, device=y.device)
+    _buf(q, "q", y.device, shape=(M, H), itemsize=1)
+    _buf(scales, "scales", y.device, shape=(M, H // 32), itemsize=1)
     if M:
         with torch.cuda.device(y.device):
             st = _lib.nq_quant_mxfp8(y.data_ptr(), M, H, _DT[y.dtype], q.data_ptr(),
@@ -220,9 +249,17 @@ def quant_mxfp8(y, q=None, scales=None):
     return q, scales
 
 
-def _validate_codes(q, name):
+def _validate_codes(q, name, dev=None):
     _require(q.is_cuda and q.dim() == 2 and q.is_contiguous() and q.element_size() == 1,
              f"{name}: contiguous 2-D one-byte device tensor")
+    _require(dev is None or q.device == dev, f"{name}: on {dev}")
+
+
+def _gemm_out(out, M, N, dev):
+    if out is None:
+        return torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _buf(out, "out", dev, shape=(M, N), dtype=torch.bfloat16)
+    return out
 
 
 def gemm_mxfp8(a, a_scales, b, b_scales, out=None):
@@ -231,14 +268,13 @@ def gemm_mxfp8(a, a_scales, b, b_scales, out=None):
     E8M0 scales, all row-major (the MXFP8 mode's outputs, and a weight in the
     same format)."""
     _validate_codes(a, "a")
-    _validate_codes(b, "b")
+    _validate_codes(b, "b", a.device)
     M, K = a.shape
     N = b.shape[0]
     _require(b.shape[1] == K and K % 32 == 0, "b: (N, K) with the same K; K % 32 == 0")
-    _require(a_scales.shape == (M, K // 32) and b_scales.shape == (N, K // 32),
-             "scales: (rows, K // 32)")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _buf(a_scales, "a_scales", a.device, shape=(M, K // 32), itemsize=1)
+    _buf(b_scales, "b_scales", a.device, shape=(N, K // 32), itemsize=1)
+    out = _gemm_out(out, M, N, a.device)
     with torch.cuda.device(a.device):
         st = _lib.nq_gemm_mxfp8(a.data_ptr(), a_scales.data_ptr(), b.data_ptr(), b_scales.data_ptr(),
                                 M, N, K, out.data_ptr(), _stream(a.device))
@@ -250,12 +286,13 @@ def gemm_fp8_static(a, a_scale, b, b_scale, out=None):
     """The consumer linear on a static-FP8 activation: out (M, N) bf16 =
     (a * a_scale) @ (b * b_scale)^T, scales one float32 each on the device."""
     _validate_codes(a, "a")
-    _validate_codes(b, "b")
+    _validate_codes(b, "b", a.device)
     M, K = a.shape
     N = b.shape[0]
     _require(b.shape[1] == K and K % 32 == 0, "b: (N, K) with the same K; K % 32 == 0")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _scalar(a_scale, "a_scale", a.device)
+    _scalar(b_scale, "b_scale", a.device)
+    out = _gemm_out(out, M, N, a.device)
     with torch.cuda.device(a.device):
         st = _lib.nq_gemm_fp8_static(a.data_ptr(), a_scale.data_ptr(), b.data_ptr(), b_scale.data_ptr(),
                                      M, N, K, out.data_ptr(), _stream(a.device))
@@ -270,17 +307,15 @@ def gemm_nvfp4(a, a_block_scale, a_global_scale, b, b_block_scale, b_global_scal
     a weight in the same format) and one float32 global scale each on the
     device (dq = code * block scale / global scale)."""
     _validate_codes(a, "a")
-    _validate_codes(b, "b")
+    _validate_codes(b, "b", a.device)
     M, K = a.shape[0], 2 * a.shape[1]
     N = b.shape[0]
     _require(b.shape[1] == K // 2 and K % 64 == 0, "b: (N, K // 2) with the same K; K % 64 == 0")
-    for name, bs, rows in (("a_block_scale", a_block_scale, M), ("b_block_scale", b_block_scale, N)):
-        _require(bs.is_cuda and bs.is_contiguous() and bs.numel() * bs.element_size() >= _lib.nq_block_scale_bytes(rows, K),
-                 f"{name}: contiguous device buffer of block_scale_bytes(rows, K) bytes")
-    for name, g in (("a_global_scale", a_global_scale), ("b_global_scale", b_global_scale)):
-        _require(g.is_cuda and g.dtype == torch.float32 and g.numel() >= 1, f"{name}: float32 device tensor")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _buf(a_block_scale, "a_block_scale", a.device, nbytes=_lib.nq_block_scale_bytes(M, K))
+    _buf(b_block_scale, "b_block_scale", a.device, nbytes=_lib.nq_block_scale_bytes(N, K))
+    _scalar(a_global_scale, "a_global_scale", a.device)
+    _scalar(b_global_scale, "b_global_scale", a.device)
+    out = _gemm_out(out, M, N, a.device)
     with torch.cuda.device(a.device):
         st = _lib.nq_gemm_nvfp4(a.data_ptr(), a_block_scale.data_ptr(), a_global_scale.data_ptr(), b.data_ptr(),
                                 b_block_scale.data_ptr(), b_global_scale.data_ptr(), M, N, K, out.data_ptr(),

@@ -298,3 +298,54 @@ def test_nvfp4_gemm_empty_writes_nothing():
     st2 = _lib.nq_gemm_nvfp4(p, p + 8192, p + 16384, p + 24576, p + 32768, p + 16388, 64, 0, 256, p + 40960, 0)
     torch.cuda.synchronize()
     assert st == _lib.NQ_OK and st2 == _lib.NQ_OK and bool((buf == P.SENTINEL).all())
+
+
+def test_wrappers_reject_bad_buffers():
+    """Every tensor the wrappers hand to the library by pointer is checked
+    first (device, contiguity, shape / size, element type): these raise
+    before anything is launched."""
+    dev = torch.device("cuda")
+    M, N, K = 4, 64, 256
+    a = torch.zeros(M, K, dtype=torch.uint8, device=dev)
+    b = torch.zeros(N, K, dtype=torch.uint8, device=dev)
+    sa = torch.zeros(M, K // 32, dtype=torch.uint8, device=dev)
+    sb = torch.zeros(N, K // 32, dtype=torch.uint8, device=dev)
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    bad_out = [torch.empty(M, N + 1, dtype=torch.bfloat16, device=dev),          # shape
+               torch.empty(M, N, dtype=torch.float16, device=dev),                # dtype
+               torch.empty(N, M, dtype=torch.bfloat16, device=dev).t(),          # not contiguous
+               torch.empty(M, N, dtype=torch.bfloat16)]                           # host memory
+    for o in bad_out:
+        with pytest.raises(ValueError, match="out"):
+            ops.gemm_mxfp8(a, sa, b, sb, out=o)
+        with pytest.raises(ValueError, match="out"):
+            ops.gemm_fp8_static(a, one, b, one, out=o)
+    with pytest.raises(ValueError, match="a_scales"):
+        ops.gemm_mxfp8(a, sa.cpu(), b, sb)
+    with pytest.raises(ValueError, match="b_scales"):
+        ops.gemm_mxfp8(a, sa, b, sb[:, :-1].contiguous())
+    with pytest.raises(ValueError, match="a_scale"):
+        ops.gemm_fp8_static(a, one.cpu(), b, one)
+    with pytest.raises(ValueError, match="b_scale"):
+        ops.gemm_fp8_static(a, one, b, torch.ones(2, dtype=torch.float32, device=dev))
+    a4 = torch.zeros(M, K // 2, dtype=torch.uint8, device=dev)
+    b4 = torch.zeros(N, K // 2, dtype=torch.uint8, device=dev)
+    sa4 = torch.zeros(ops.block_scale_bytes(M, K), dtype=torch.uint8, device=dev)
+    sb4 = torch.zeros(ops.block_scale_bytes(N, K), dtype=torch.uint8, device=dev)
+    with pytest.raises(ValueError, match="b_block_scale"):
+        ops.gemm_nvfp4(a4, sa4, one, b4, sb4[:-1], one)
+    with pytest.raises(ValueError, match="a_global_scale"):
+        ops.gemm_nvfp4(a4, sa4, one.double(), b4, sb4, one)
+    with pytest.raises(ValueError, match="out"):
+        ops.gemm_nvfp4(a4, sa4, one, b4, sb4, one, out=torch.empty(M, N - 1, dtype=torch.bfloat16, device=dev))
+    y = torch.zeros(M, K, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError, match="scale"):
+        ops.quant_fp8_static(y, one.cpu())
+    with pytest.raises(ValueError, match="q"):
+        ops.quant_fp8_static(y, one, q=torch.empty(M, K - 1, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError, match="block_scale"):
+        ops.quant_nvfp4(y, one, block_scale=torch.empty(8, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError, match="global_scale"):
+        ops.quant_nvfp4(y, torch.ones(1, dtype=torch.float16, device=dev))
+    with pytest.raises(ValueError, match="scales"):
+        ops.quant_mxfp8(y, scales=torch.empty(M, K // 32 + 1, dtype=torch.uint8, device=dev))
