@@ -68,10 +68,18 @@ def kernel_sha():
     return h.hexdigest()[:16]
 
 
+def chunks_per_thread(H):
+    """The fused kernel's 8-element chunks per thread (its launcher's rule)."""
+    nchunk = H // 8
+    if H <= 4096 or (nchunk <= 1024 and nchunk % 256 == 0):
+        return 1
+    return 2 if nchunk <= 2048 else 4
+
+
 def kernel_name(wl):
     return "fused_rows<{},{},{},{},{}>".format(
         wl.dtype, wl.mode, "res" if wl.has_residual else "nores",
-        "y" if wl.write_y else "noy", 1 if wl.H <= 4096 else (2 if wl.H // 8 <= 2048 else 4))
+        "y" if wl.write_y else "noy", chunks_per_thread(wl.H))
 
 
 def measured_traffic(wl):

@@ -8,8 +8,9 @@
 //    row loop).  A thread owns 8-element chunks (16 bytes) at chunk index
 //    tid, tid + nthr, ..., so every load and store instruction of a wave
 //    covers contiguous memory: 1 KB of x / residual / y, 512 B of FP8 codes,
-//    256 B of FP4 codes.  1, 2 or 4 chunks per thread (H <= 4096, <= 16384,
-//    <= 32768).  x and residual are streamed with non-temporal loads, all
+//    256 B of FP4 codes.  1, 2 or 4 chunks per thread (chunks_per_thread:
+//    one up to H = 4096 and at H = 6144, 8192; else two up to 16384, four up
+//    to 32768).  x and residual are streamed with non-temporal loads, all
 //    outputs with non-temporal stores; weight and scale are plain (L2-cached)
 //    loads.  All loads of a row are issued before the first wait.  Sum of
 //    squares: fp32 FMA chain per thread, DPP butterfly inside each 16-lane
@@ -280,11 +281,16 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
 // Launch: pick the kernel and shape for (M, H, alignment).
 
 // Chunks per thread for fused_rows: one 8-element chunk per thread up to
-// H = 4096 (short per-thread chains for latency), two up to H = 16384, four
-// up to H = 32768 (at most 1024 threads per workgroup).
+// H = 4096 (short per-thread chains for latency), and beyond wherever that
+// gives a workgroup of whole 4-wave groups within 1024 threads (H = 6144,
+// 8192: its waves spread evenly over the 4 SIMDs; measured 1-3.5% faster
+// than two chunks at H = 8192, while the 10-wave workgroups of H = 5120 ran
+// 3-22% slower than 5-wave ones with two chunks); otherwise two up to
+// H = 16384, four up to H = 32768.
 inline int chunks_per_thread(int64_t H) {
   const int64_t nchunk = H / kVec;
   if (H <= 4096) return 1;
+  if (nchunk <= kMaxThreads && nchunk % (4 * kWave) == 0) return 1;
   if (nchunk <= 2 * kMaxThreads) return 2;
   return 4;
 }

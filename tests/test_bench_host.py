@@ -53,3 +53,14 @@ def test_multi_gpu_run_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+@pytest.mark.parametrize("H,cpt", [(16, 1), (2048, 1), (4096, 1), (5120, 2), (6144, 1), (8192, 1),
+                                   (8320, 2), (16384, 2), (16512, 4), (32768, 4)])
+def test_kernel_name_follows_the_launchers_chunk_rule(H, cpt):
+    """One 8-element chunk per thread up to H = 4096 and wherever that makes
+    a workgroup of whole 4-wave groups within 1024 threads; else two up to
+    H = 16384, four beyond (the fused launcher's chunks_per_thread)."""
+    assert bench.chunks_per_thread(H) == cpt
+    assert bench.kernel_name(WORKLOADS["nvfp4_m32768_h8192_bf16_y"]).endswith(",1>")
+    assert bench.kernel_name(WORKLOADS["fp8_nores_m4096_h5120_fp16"]).endswith(",2>")
