@@ -439,8 +439,8 @@ def main():
                          "of chunk j + 1 on a second stream beside the GEMM of chunk j")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the op is row-independent and this build has no "
-              "multi-GPU path (--gpus must be 1)", file=sys.stderr, flush=True)
+        print("bench.py measures one GPU only: the op is row-independent, and its rows would "
+              "split across GPUs with no exchange (--gpus must be 1)", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import torch
