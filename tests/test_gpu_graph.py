@@ -68,3 +68,50 @@ def test_graph_replays_match_eager(name):
             assert torch.equal(rg, re), rep
         if bsg is not None:
             assert torch.equal(bsg, bse), rep
+
+
+@pytest.mark.parametrize("fmt,M,H,N", [("nvfp4", 4, 1024, 320), ("nvfp4", 40, 1152, 200),
+                                       ("nvfp4", 300, 1024, 384), ("mxfp8", 300, 1024, 384)])
+def test_graph_op_and_consumer_gemm_replays_match_eager(fmt, M, H, N):
+    """The op and its consumer GEMM captured together (the NVFP4 dot-product,
+    small-tile and large-tile kernels, and the MXFP8 one): every replay, with
+    eager resets and synchronisations between, gives the eager result bit for
+    bit."""
+    print(f"graph chain {fmt} M={M} H={H} N={N}", flush=True)
+    dev = torch.device("cuda")
+    g = torch.Generator().manual_seed(M + H + N)
+    x = torch.randn(M, H, generator=g).to(torch.bfloat16).to(dev)
+    r0 = torch.randn(M, H, generator=g).to(torch.bfloat16).to(dev)
+    w = (torch.randn(H, generator=g) * 0.1).to(torch.bfloat16).to(dev)
+    W = torch.randn(N, H, generator=g).to(torch.bfloat16).to(dev)
+    gs = torch.tensor([448.0 * 6.0 / 9.0], dtype=torch.float32, device=dev)
+    if fmt == "nvfp4":
+        wq, wbs = ops.quant_nvfp4(W, gs)
+    else:
+        wq, wbs = ops.quant_mxfp8(W)
+
+    def chain(r):
+        if fmt == "nvfp4":
+            q, bs, _ = ops.gemma_add_rms_norm_quant(x, r, w, 1e-6, gs, True)
+            return ops.gemm_nvfp4(q, bs, gs, wq, wbs, gs)
+        q, s, _, _ = ops.gemma_add_rms_norm_mxfp8(x, r, w, 1e-6)
+        return ops.gemm_mxfp8(q, s, wq, wbs)
+
+    re = r0.clone()
+    oute = chain(re)
+    torch.cuda.synchronize()
+
+    rg = r0.clone()
+    st = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=st):
+        outg = chain(rg)
+    for rep in range(3):
+        rg.copy_(r0)
+        outg.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outg, oute), rep
+        assert torch.equal(rg, re), rep
