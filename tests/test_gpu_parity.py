@@ -83,6 +83,8 @@ EDGE = [
     (torch.bfloat16, True, 2100, 256, True, True),       # XCD row map: 2 spans + ragged tail
     (torch.float16, True, 3072, 64, False, True),        # XCD row map: exact spans
     (torch.float16, True, 200, 5120, True, True),
+    (torch.bfloat16, True, 45, 6144, True, True),        # one chunk per thread, 12 waves
+    (torch.float16, False, 33, 8192, False, True),       # one chunk per thread, 16 waves
     (torch.float16, True, 64, 192, False, False),
     # H <= 512: several rows per wave (lanes per row 2, 4, 8, 16, 32, 64)
     (torch.bfloat16, False, 37, 16, True, True),
