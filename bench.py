@@ -76,6 +76,24 @@ def chunks_per_thread(H):
     return 2 if nchunk <= 2048 else 4
 
 
+def nvfp4_kernel(M, N, K):
+    """The NVFP4 consumer kernel the library's dispatch picks for (M, N, K)."""
+    if M <= 8 and M * (K // 32) * 80 <= 128 * 1024:
+        return "gemm_nvfp4_gemv"
+
+    def tiles(mt, nt):
+        return -(-M // mt) * -(-N // nt)
+    if M > 256 and tiles(256, 256) >= 128:
+        return "gemm_nvfp4_big"
+    if M >= 128 and tiles(128, 64) >= 192:
+        return "gemm_nvfp4_k<4,128,64,4>"
+    if M >= 64 and tiles(64, 64) >= 192:
+        return "gemm_nvfp4_k<8,64,64,3>"
+    if M >= 64 and tiles(64, 32) >= 192:
+        return "gemm_nvfp4_k<8,64,32,4>"
+    return "gemm_nvfp4_k<8,32,32,4>" if K % 512 == 0 else "gemm_nvfp4_k<4,32,32,8>"
+
+
 def kernel_name(wl):
     return "fused_rows<{},{},{},{},{}>".format(
         wl.dtype, wl.mode, "res" if wl.has_residual else "nores",
@@ -267,8 +285,7 @@ def gemm_main(args):
                 "peak": mfma_peak, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
-    kernel = (("gemm_nvfp4_gemv" if M <= 8 and M * (K // 32) * 80 <= 128 * 1024 else
-               "gemm_nvfp4_big" if M > 256 else "gemm_nvfp4_k") if nv else
+    kernel = (nvfp4_kernel(M, N, K) if nv else
               "gemm_fp8_decode" if M <= 256 and K % 2048 == 0 and K <= 16384 else
               "gemm_fp8_skinny" if M <= 256 and K % 64 == 0 else
               "gemm_fp8_tn_dma" if K % 512 == 0 else "gemm_fp8_tn")

@@ -984,6 +984,9 @@ gemm_nvfp4_k(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA, cons
                                                         int, int, uint16_t *, int);
 GNQ_GEMM_FP4_INST(4, 32, 32, 8)
 GNQ_GEMM_FP4_INST(8, 32, 32, 4)
+GNQ_GEMM_FP4_INST(8, 64, 32, 4)
+GNQ_GEMM_FP4_INST(8, 64, 64, 3)
+GNQ_GEMM_FP4_INST(4, 128, 64, 4)
 #undef GNQ_GEMM_FP4_INST
 
 // Many rows: 256 x 256 workgroup tiles (4 waves of 128 x 128, 16 MFMA tiles
@@ -1321,28 +1324,40 @@ hipError_t launch_nvfp4_gemv(const uint8_t *A, const uint8_t *SA, const float *a
 }
 
 // Caller guarantees K % 64 == 0, 0 < M, N, and that the 32 x 32 tile count
-// fits a grid.  32 x 32 tiles up to 256 rows, else the 256 x 256 kernel
-// (measured 1.24x faster than 64 x 64 tiles with per-wave K ranges; those
-// ran 1.7x faster with 3 stages and two workgroups per CU than with 6 and
-// one).
+// fits a grid.  Tile choice (measured at N = 4096 and 8192, K = 4096): a
+// workgroup round costs about the same whatever its tile, so the largest
+// tile that still gives enough workgroups wins.  Up to 8 rows the
+// dot-product kernel; beyond 256 rows the 256 x 256 kernel once it has 128
+// workgroups (at N = 4096 it took 108 us at M = 300 to 1024 with 32-64
+// workgroups, against 31-67 us on 128 x 64 tiles); else the first of
+// 128 x 64, 64 x 64, 64 x 32 tiles giving 192 workgroups (M = 200: 64 x 64
+// 19.4 us, 32 x 32 35.3 us); else 32 x 32 tiles.
 hipError_t gemm_nvfp4(const void *a, const void *sa, const float *a_gs, const void *b, const void *sb,
                       const float *b_gs, int64_t M, int64_t N, int64_t K, void *c, hipStream_t st) {
   const uint8_t *A = (const uint8_t *)a, *B = (const uint8_t *)b;
   const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
+  uint16_t *C = (uint16_t *)c;
+  const int m = (int)M, n = (int)N, k = (int)K;
   // up to 8 rows whose dequantized activation fits the LDS: dot products
   if (M <= 8 && M * (K / 32) * (int64_t)kGemvChunk <= kGemvMaxLds) {
-    if (M == 1) return launch_nvfp4_gemv<1>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-    if (M == 2) return launch_nvfp4_gemv<2>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-    if (M <= 4) return launch_nvfp4_gemv<4>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-    return launch_nvfp4_gemv<8>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+    if (M == 1) return launch_nvfp4_gemv<1>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
+    if (M == 2) return launch_nvfp4_gemv<2>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
+    if (M <= 4) return launch_nvfp4_gemv<4>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
+    return launch_nvfp4_gemv<8>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
   }
-  // up to 256 rows: 32 x 32 tiles (enough workgroups); 8 waves splitting K
-  // when it divides into 8 equal ranges, else 4 (ranges may differ by a stage)
-  if (M <= 256 && K % 512 == 0)
-    return launch_nvfp4<8, 32, 32, 4>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-  if (M <= 256)
-    return launch_nvfp4<4, 32, 32, 8>(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-  return launch_nvfp4_big(A, SA, a_gs, B, SB, b_gs, (int)M, (int)N, (int)K, (uint16_t *)c, st);
+  auto tiles = [&](int64_t mt, int64_t nt) { return ((M + mt - 1) / mt) * ((N + nt - 1) / nt); };
+  if (M > 256 && tiles(kFp4BigRows, kFp4BigRows) >= 128)
+    return launch_nvfp4_big(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
+  if (M >= 128 && tiles(128, 64) >= 192)
+    return launch_nvfp4<4, 128, 64, 4>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
+  if (M >= 64 && tiles(64, 64) >= 192)
+    return launch_nvfp4<8, 64, 64, 3>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
+  if (M >= 64 && tiles(64, 32) >= 192)
+    return launch_nvfp4<8, 64, 32, 4>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
+  // 32 x 32 tiles; 8 waves splitting K when it divides into 8 equal ranges,
+  // else 4 (ranges may differ by a stage)
+  if (K % 512 == 0) return launch_nvfp4<8, 32, 32, 4>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
+  return launch_nvfp4<4, 32, 32, 8>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
 }
 
 hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,

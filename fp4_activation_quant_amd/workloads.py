@@ -201,6 +201,8 @@ GEMM_WORKLOADS = {g.name: g for g in [
     GemmWorkload("gemm_nvfp4_m8192_n4096_k4096", "nvfp4", 8192, 4096, 4096, 8800),
     GemmWorkload("gemm_nvfp4_m64_n4096_k4096", "nvfp4", 64, 4096, 4096, 8900),
     GemmWorkload("gemm_nvfp4_m1_n4096_k4096", "nvfp4", 1, 4096, 4096, 9000),
+    GemmWorkload("gemm_nvfp4_m256_n4096_k4096", "nvfp4", 256, 4096, 4096, 9100),
+    GemmWorkload("gemm_nvfp4_m1024_n4096_k4096", "nvfp4", 1024, 4096, 4096, 9200),
 ]}
 
 

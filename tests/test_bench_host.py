@@ -64,3 +64,15 @@ def test_kernel_name_follows_the_launchers_chunk_rule(H, cpt):
     assert bench.chunks_per_thread(H) == cpt
     assert bench.kernel_name(WORKLOADS["nvfp4_m32768_h8192_bf16_y"]).endswith(",1>")
     assert bench.kernel_name(WORKLOADS["fp8_nores_m4096_h5120_fp16"]).endswith(",2>")
+
+
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (1, 4096, 4096, "gemm_nvfp4_gemv"), (8, 50, 8192, "gemm_nvfp4_k<8,32,32,4>"),
+    (64, 4096, 4096, "gemm_nvfp4_k<8,32,32,4>"), (128, 4096, 4096, "gemm_nvfp4_k<8,64,32,4>"),
+    (256, 4096, 4096, "gemm_nvfp4_k<8,64,64,3>"), (1024, 4096, 4096, "gemm_nvfp4_k<4,128,64,4>"),
+    (2048, 4096, 4096, "gemm_nvfp4_big"), (8192, 4096, 4096, "gemm_nvfp4_big"),
+    (300, 200, 448, "gemm_nvfp4_k<4,32,32,8>")])
+def test_nvfp4_kernel_follows_the_dispatch(M, N, K, kernel):
+    """The bench names the NVFP4 consumer kernel the library's tile choice
+    picks (largest tile with enough workgroups)."""
+    assert bench.nvfp4_kernel(M, N, K) == kernel

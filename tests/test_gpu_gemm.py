@@ -217,12 +217,16 @@ def _run_nvfp4(aq, abuf, ga, bq, bbuf, gb, M, N):
 # K % 256 != 0 included: 64-element steps split unevenly over the small
 # kernel's waves (some with none) and odd step counts in the large one;
 # M <= 8 takes the dot-product kernel (each of its row counts 1, 2, 4, 8),
-# except M = 8 at K = 8192, whose fp16 activation exceeds its LDS.
+# except M = 8 at K = 8192, whose fp16 activation exceeds its LDS; the tile
+# choice puts (2100, 4096) on 256 x 256 tiles, (300, 4096) and (257, 4160)
+# on 128 x 64, (200, 3072) on 64 x 64, (100, 3100) and (520, 700) on 64 x 32
+# and the rest on 32 x 32.
 NVFP4_SHAPES = [(1, 8, 256), (5, 300, 512), (32, 64, 1024), (33, 100, 256), (200, 130, 2048),
                 (130, 257, 768), (64, 1000, 1024), (300, 200, 512), (257, 70, 768), (600, 520, 1024),
                 (520, 700, 256), (1, 40, 64), (17, 96, 448), (64, 200, 1152), (260, 33, 64),
                 (300, 260, 320), (257, 130, 1152), (2, 70, 320), (3, 130, 1152), (4, 17, 64),
-                (8, 50, 8192), (1, 2000, 3072)]
+                (8, 50, 8192), (1, 2000, 3072), (2100, 4096, 128), (300, 4096, 256), (257, 4160, 192),
+                (200, 3072, 320), (100, 3100, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", NVFP4_SHAPES)
@@ -245,7 +249,8 @@ def test_nvfp4_gemm_exact_cases(M, N, K, gs):
 
 
 @pytest.mark.parametrize("M,N,K", [(17, 96, 4096), (300, 520, 2048), (1, 333, 8192), (256, 512, 4096),
-                                   (300, 520, 2880), (8, 300, 2880), (2, 1000, 4096), (4, 64, 16384)])
+                                   (300, 520, 2880), (8, 300, 2880), (2, 1000, 4096), (4, 64, 16384),
+                                   (2100, 4096, 256), (300, 4096, 512), (200, 3072, 512), (100, 3100, 512)])
 def test_nvfp4_gemm_random(M, N, K):
     print(f"gemm nvfp4 random M={M} N={N} K={K}", flush=True)
     rng = np.random.default_rng(M + 3 * N + K)

@@ -71,10 +71,11 @@ def test_graph_replays_match_eager(name):
 
 
 @pytest.mark.parametrize("fmt,M,H,N", [("nvfp4", 4, 1024, 320), ("nvfp4", 40, 1152, 200),
-                                       ("nvfp4", 300, 1024, 384), ("mxfp8", 300, 1024, 384)])
+                                       ("nvfp4", 300, 1024, 384), ("nvfp4", 300, 1024, 4096),
+                                       ("nvfp4", 2100, 256, 4096), ("mxfp8", 300, 1024, 384)])
 def test_graph_op_and_consumer_gemm_replays_match_eager(fmt, M, H, N):
     """The op and its consumer GEMM captured together (the NVFP4 dot-product,
-    small-tile and large-tile kernels, and the MXFP8 one): every replay, with
+    32 x 32, 128 x 64 and 256 x 256 tile kernels, and the MXFP8 one): every replay, with
     eager resets and synchronisations between, gives the eager result bit for
     bit."""
     print(f"graph chain {fmt} M={M} H={H} N={N}", flush=True)
