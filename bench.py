@@ -76,6 +76,23 @@ def chunks_per_thread(H):
     return 2 if nchunk <= 2048 else 4
 
 
+def fp8_kernel(M, N, K):
+    """The FP8 / MXFP8 consumer kernel the library's dispatch picks (16-byte
+    aligned scales assumed)."""
+    dma = K % 512 == 0
+    t256 = -(-M // 256) * -(-N // 256)
+    t128 = -(-M // 128) * -(-N // 128)
+    if dma and t256 >= 128:
+        return "gemm_fp8_tn_dma<256>"
+    if dma and (M > 256 or t128 >= 128):
+        return "gemm_fp8_tn_dma<128>"
+    if M <= 256 and K % 2048 == 0 and K <= 16384:
+        return "gemm_fp8_decode"
+    if M <= 256 and K % 64 == 0:
+        return "gemm_fp8_skinny"
+    return "gemm_fp8_tn"
+
+
 def nvfp4_kernel(M, N, K):
     """The NVFP4 consumer kernel the library's dispatch picks for (M, N, K)."""
     if M <= 8 and M * (K // 32) * 80 <= 128 * 1024:
@@ -285,10 +302,7 @@ def gemm_main(args):
                 "peak": mfma_peak, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
-    kernel = (nvfp4_kernel(M, N, K) if nv else
-              "gemm_fp8_decode" if M <= 256 and K % 2048 == 0 and K <= 16384 else
-              "gemm_fp8_skinny" if M <= 256 and K % 64 == 0 else
-              "gemm_fp8_tn_dma" if K % 512 == 0 else "gemm_fp8_tn")
+    kernel = nvfp4_kernel(M, N, K) if nv else fp8_kernel(M, N, K)
     out = {
         "metric": "consumer GEMM TFLOP/s (quantized activation x quantized weight -> bf16), 1 GPU",
         "value": round(flop / (ms_per_step * 1e-3) / 1e12, 2),

@@ -219,11 +219,15 @@ gemm_fp8_tn(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
 // instead of once per step (4-byte loads from 64 rows per instruction cost
 // ~20% when issued every step).  One barrier per step.
 constexpr int kGemmStages = 4;
-constexpr int kGemmStageBytes = 2 * kGemmOperandBytes;               // 32 KB
 constexpr int kGemmScaleSteps = 8;                                   // K steps per scale window
-constexpr int kGemmScaleWin = kGemmTile * 2 * kGemmScaleSteps;       // 4 KB per operand
-constexpr int kGemmScaleOff = kGemmStages * kGemmStageBytes;         // two windows after the stages
-constexpr int kGemmDmaLds = kGemmScaleOff + 2 * 2 * kGemmScaleWin;   // 144 KB
+// LDS layout for a T x T workgroup tile: kGemmStages stages of both
+// operands' T rows x kGemmK bytes, then two scale windows of T rows x 16
+// bytes per operand (T = 256: 128 KB + 16 KB; T = 128: 64 KB + 8 KB).
+__host__ __device__ constexpr int dma_operand_bytes(int T) { return T * kGemmK; }
+__host__ __device__ constexpr int dma_stage_bytes(int T) { return 2 * dma_operand_bytes(T); }
+__host__ __device__ constexpr int dma_scale_win(int T) { return T * 2 * kGemmScaleSteps; }
+__host__ __device__ constexpr int dma_scale_off(int T) { return kGemmStages * dma_stage_bytes(T); }
+__host__ __device__ constexpr int dma_lds_bytes(int T) { return dma_scale_off(T) + 2 * 2 * dma_scale_win(T); }
 
 // Global -> LDS DMA of 16 bytes per lane (lane l writes lds + 16 l).
 __device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *lds) {
@@ -237,25 +241,30 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // NW waves per workgroup, each owning TM x TN MFMA tiles (32 x 32) of the
-// 256 x 256 workgroup tile; the 32 one-KB data segments and 8 scale segments
-// of a step are split evenly over the waves.  The LDS reads are pipelined
+// T x T workgroup tile; the T / 8 one-KB data segments (16 rows each, T / 16
+// per operand) and T / 32 scale segments (64 rows each) of a step are split
+// evenly over the waves.  The LDS reads are pipelined
 // across steps: the fragments and scale codes of step k + 1 are read into a
 // second register set while the MFMAs of step k run, so after the barrier a
 // wave goes straight to its MFMAs.  The barrier of step k certifies that
 // step k + 1's DMA has landed (each wave waits for its own segments first)
 // and that every wave has consumed the reads of step k - 1, whose stage the
 // DMA issued after it refills (two steps of DMA ahead of the reads).
-template <bool MX, int NW, int TM, int TN>
+template <bool MX, int NW, int TM, int TN, int T>
 __global__ void __launch_bounds__(64 * NW)
 gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
                 const uint8_t *__restrict__ B, const uint8_t *__restrict__ SB,
                 const float *__restrict__ a_scale, const float *__restrict__ b_scale, int M, int N,
                 int K, uint16_t *__restrict__ C, int tiles_m, int tiles, int unit_scale) {
-  static_assert((8 / TM) * (8 / TN) == NW, "waves must tile the 256 x 256 workgroup tile");
+  static_assert(T == 128 || T == 256, "workgroup tile");
+  static_assert((T / 32 / TM) * (T / 32 / TN) == NW, "waves must tile the T x T workgroup tile");
   static_assert(kGemmStages == 4, "the waits below assume four stages");
-  constexpr int kSegs = 32 / NW;
-  constexpr int kScaleSegs = 8 / NW;
-  constexpr int kWavesN = 8 / TN;
+  static_assert((T / 8) % NW == 0 && (T / 32) % NW == 0, "segments split evenly over the waves");
+  constexpr int kSegs = T / 8 / NW;
+  constexpr int kScaleSegs = T / 32 / NW;
+  constexpr int kWavesN = T / 32 / TN;
+  constexpr int kOperandBytes = dma_operand_bytes(T), kStageBytes = dma_stage_bytes(T);
+  constexpr int kScaleWin = dma_scale_win(T), kScaleOff = dma_scale_off(T);
   constexpr int kMfma = TM * TN, kUnits = TM + TN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -263,15 +272,15 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
   const int r = lane & 31, h = lane >> 5;
   int tm, tn;
   gemm_tile_of_block(blockIdx.x, tiles_m, tiles / tiles_m, tm, tn);
-  const int m0 = tm * kGemmTile, n0 = tn * kGemmTile;
+  const int m0 = tm * T, n0 = tn * T;
   const int wm = (wave / kWavesN) * 32 * TM, wn = (wave % kWavesN) * 32 * TN;
   const int ksteps = K / kGemmK;
   const int kblocks = K / 32;
 
-  const bool fetch_b = kSegs * wave >= 16;
+  const bool fetch_b = kSegs * wave >= T / 16;
   const uint8_t *src = fetch_b ? B : A;
   const int lim = fetch_b ? N - 1 : M - 1, base_row = fetch_b ? n0 : m0;
-  const int seg0 = (kSegs * wave) & 15;
+  const int seg0 = (kSegs * wave) % (T / 16);
   const uint8_t *seg_src[kSegs];
 #pragma unroll
   for (int j = 0; j < kSegs; ++j) {
@@ -279,8 +288,8 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     const int chunk = (lane & 3) ^ gemm_swz(row);
     seg_src[j] = src + (size_t)min(base_row + row, lim) * (size_t)K + chunk * 16;
   }
-  const bool sfetch_b = kScaleSegs * wave >= 4;
-  const int sseg0 = (kScaleSegs * wave) & 3;
+  const bool sfetch_b = kScaleSegs * wave >= T / 64;
+  const int sseg0 = (kScaleSegs * wave) % (T / 64);
   const uint8_t *sc_src[kScaleSegs];
 #pragma unroll
   for (int t = 0; t < kScaleSegs; ++t) {
@@ -292,7 +301,7 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
   // refetches past the last step), and of scale window `from` into the
   // buffer of window w.
   auto issue_seg = [&](int ks, int from, int j) {
-    uint8_t *dst = smem + (ks % kGemmStages) * kGemmStageBytes + (fetch_b ? kGemmOperandBytes : 0) + seg0 * 1024;
+    uint8_t *dst = smem + (ks % kGemmStages) * kStageBytes + (fetch_b ? kOperandBytes : 0) + seg0 * 1024;
     dma16(seg_src[j] + from * kGemmK, dst + j * 1024);
   };
   auto issue = [&](int ks, int from) {
@@ -300,7 +309,7 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     for (int j = 0; j < kSegs; ++j) issue_seg(ks, from, j);
   };
   auto issue_scales = [&](int w, int from) {
-    uint8_t *sdst = smem + kGemmScaleOff + (w & 1) * 2 * kGemmScaleWin + (sfetch_b ? kGemmScaleWin : 0) +
+    uint8_t *sdst = smem + kScaleOff + (w & 1) * 2 * kScaleWin + (sfetch_b ? kScaleWin : 0) +
                     sseg0 * 1024;
 #pragma unroll
     for (int t = 0; t < kScaleSegs; ++t) dma16(sc_src[t] + 16 * from, sdst + t * 1024);
@@ -328,14 +337,14 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     for (int op = 0; op < 2; ++op)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        fbase[sp][op][hh] = (uint32_t)(sp * 2 * kGemmStageBytes + op * kGemmOperandBytes +
+        fbase[sp][op][hh] = (uint32_t)(sp * 2 * kStageBytes + op * kOperandBytes +
                                        ((op ? wn : wm) + r) * kGemmK + (((2 * hh + h) ^ swz) << 4));
         asm volatile("" : "+v"(fbase[sp][op][hh]));
       }
   uint32_t sbase[2];
 #pragma unroll
   for (int op = 0; op < 2; ++op) {
-    sbase[op] = (uint32_t)(kGemmScaleOff + op * kGemmScaleWin + ((op ? wn : wm) + r) * 16 + h);
+    sbase[op] = (uint32_t)(kScaleOff + op * kScaleWin + ((op ? wn : wm) + r) * 16 + h);
     asm volatile("" : "+v"(sbase[op]));
   }
   // Read unit u of step ks into register set p: B tile u for u < TN, else
@@ -343,7 +352,7 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
   auto read_unit = [&](int ks, int p, int u, uint32_t wofs) {
     const int stg = ks % kGemmStages;
     const int op = u < TN ? 1 : 0, t = u < TN ? u : u - TN;
-    const uint32_t imm = (uint32_t)((stg & 1) * kGemmStageBytes + t * 32 * kGemmK);
+    const uint32_t imm = (uint32_t)((stg & 1) * kStageBytes + t * 32 * kGemmK);
     const u32x4 lo = *reinterpret_cast<const u32x4 *>(smem + fbase[stg >> 1][op][0] + imm);
     const u32x4 hi = *reinterpret_cast<const u32x4 *>(smem + fbase[stg >> 1][op][1] + imm);
     const i32x8 f = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -365,7 +374,7 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
   // (inside LDS) that nothing uses.
   auto step = [&](int ks, int u8, int c) {
     const int p = u8 & 1;
-    const uint32_t wofs = (uint32_t)((((ks + 1) / kGemmScaleSteps) & 1) * 2 * kGemmScaleWin);
+    const uint32_t wofs = (uint32_t)((((ks + 1) / kGemmScaleSteps) & 1) * 2 * kScaleWin);
     // step ks + 1's segments of this wave: at most step ks + 2's (and a
     // scale window issued after them) may still be in flight
     wait_vmcnt<kSegs>();
@@ -437,22 +446,26 @@ inline hipError_t allow_dynamic_lds(const void *kernel, int bytes, std::atomic<u
 
 // Explicit instantiations: the kernels are referenced only from the launch
 // template below, and without these the device stubs were not emitted.
-#define GNQ_GEMM_DMA_INST(MX, NW, TM, TN)                                                        \
-  template __global__ void gemm_fp8_tn_dma<MX, NW, TM, TN>(                                      \
+#define GNQ_GEMM_DMA_INST(MX, NW, TM, TN, T)                                                     \
+  template __global__ void gemm_fp8_tn_dma<MX, NW, TM, TN, T>(                                   \
       const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *, const float *,         \
       const float *, int, int, int, uint16_t *, int, int, int);
-GNQ_GEMM_DMA_INST(true, 4, 4, 4)
-GNQ_GEMM_DMA_INST(false, 4, 4, 4)
+GNQ_GEMM_DMA_INST(true, 4, 4, 4, 256)
+GNQ_GEMM_DMA_INST(false, 4, 4, 4, 256)
+GNQ_GEMM_DMA_INST(true, 4, 2, 2, 128)
+GNQ_GEMM_DMA_INST(false, 4, 2, 2, 128)
 #undef GNQ_GEMM_DMA_INST
 
-template <bool MX, int NW, int TM, int TN>
+template <bool MX, int NW, int TM, int TN, int T>
 hipError_t launch_dma(const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
                       const float *a_scale, const float *b_scale, int M, int N, int K, uint16_t *C,
-                      int tiles_m, int tiles, hipStream_t st) {
+                      hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = allow_dynamic_lds((const void *)gemm_fp8_tn_dma<MX, NW, TM, TN>, kGemmDmaLds, lds_set);
+  constexpr int lds = dma_lds_bytes(T);
+  const hipError_t e = allow_dynamic_lds((const void *)gemm_fp8_tn_dma<MX, NW, TM, TN, T>, lds, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_fp8_tn_dma<MX, NW, TM, TN>), dim3(tiles), dim3(64 * NW), kGemmDmaLds, st, A, SA,
+  const int tiles_m = (M + T - 1) / T, tiles = tiles_m * ((N + T - 1) / T);
+  hipLaunchKernelGGL((gemm_fp8_tn_dma<MX, NW, TM, TN, T>), dim3(tiles), dim3(64 * NW), lds, st, A, SA,
                      B, SB, a_scale, b_scale, M, N, K, C, tiles_m, tiles, 127);
   return hipGetLastError();
 }
@@ -1363,29 +1376,39 @@ hipError_t gemm_nvfp4(const void *a, const void *sa, const float *a_gs, const vo
 hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const void *sb,
                     const float *a_scale, const float *b_scale, int64_t M, int64_t N, int64_t K,
                     void *c, hipStream_t st) {
-  const int tiles_m = (int)((M + kGemmTile - 1) / kGemmTile);
-  const int tiles_n = (int)((N + kGemmTile - 1) / kGemmTile);
-  const int tiles = tiles_m * tiles_n;
   const uint8_t *A = (const uint8_t *)a, *B = (const uint8_t *)b;
   const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
-  // Few activation rows: the large tiles would leave most CUs idle (one
-  // workgroup per 256 output columns); the decode kernel (or, for K it does
-  // not take, the skinny one) streams the weight with small tiles.
+  // Tile choice (measured at N = 4096 and 8192, K = 4096): a workgroup's
+  // 256 x 256 tile keeps one CU busy ~40 us, so with fewer than 128 such
+  // workgroups the 128 x 128 tiles (four times as many, two workgroups per
+  // CU) win: M = 300, 512, 1024 at N = 4096 took 41, 43, 46 us on 256 x 256
+  // and 19, 21, 26 us on 128 x 128 (MXFP8); at 128 workgroups they tie.  Up
+  // to 256 rows the decode kernel's small tiles stream the weight faster,
+  // unless 128 x 128 tiles already number 128 (M = 192, N = 8192: 28.8 us
+  // against 21.2 us).  The DMA pipeline needs K % 512 == 0 (a 16-byte scale
+  // window never crosses a row of K / 32 codes) and 16-byte aligned scales.
+  const bool dma = K % 512 == 0 && (!mx || ((uintptr_t)sa % 16 == 0 && (uintptr_t)sb % 16 == 0));
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256), t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (dma && t256 >= 128)
+    return mx ? launch_dma<true, 4, 4, 4, 256>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
+                                               (uint16_t *)c, st)
+              : launch_dma<false, 4, 4, 4, 256>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
+                                                (uint16_t *)c, st);
+  if (dma && (M > 256 || t128 >= 128))
+    return mx ? launch_dma<true, 4, 2, 2, 128>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
+                                               (uint16_t *)c, st)
+              : launch_dma<false, 4, 2, 2, 128>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
+                                                (uint16_t *)c, st);
+  // Few activation rows: the decode kernel (or, for K it does not take, the
+  // skinny one) streams the weight with small tiles.
   if (M <= 256 && K % 2048 == 0 && K <= kDecMaxK && (!mx || ((uintptr_t)sa % 16 == 0 && (uintptr_t)sb % 16 == 0)))
     return mx ? launch_decode<true>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st)
               : launch_decode<false>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st);
   if (M <= 256 && K % kGemmK == 0)
     return mx ? launch_skinny<true>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st)
               : launch_skinny<false>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st);
-  // DMA pipeline: K % 512 == 0 so a 16-byte scale window never crosses a
-  // row of (K / 32) codes, and 16-byte aligned scale rows.
-  const bool dma = K % 512 == 0 && (!mx || ((uintptr_t)sa % 16 == 0 && (uintptr_t)sb % 16 == 0));
-  if (dma) {
-    return mx ? launch_dma<true, 4, 4, 4>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c,
-                                          tiles_m, tiles, st)
-              : launch_dma<false, 4, 4, 4>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
-                                           (uint16_t *)c, tiles_m, tiles, st);
-  }
+  const int tiles_m = (int)((M + kGemmTile - 1) / kGemmTile);
+  const int tiles = tiles_m * (int)((N + kGemmTile - 1) / kGemmTile);
   if (mx)
     hipLaunchKernelGGL((gemm_fp8_tn<true>), dim3(tiles), dim3(kGemmThreads), 0, st, A, SA, B, SB,
                        a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m, tiles, 127);

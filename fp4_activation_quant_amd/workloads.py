@@ -198,6 +198,9 @@ GEMM_WORKLOADS = {g.name: g for g in [
     GemmWorkload("gemm_mxfp8_m64_n4096_k4096", "mxfp8", 64, 4096, 4096, 8400),
     GemmWorkload("gemm_mxfp8_m1_n4096_k4096", "mxfp8", 1, 4096, 4096, 8600),
     GemmWorkload("gemm_fp8_m64_n4096_k4096", "fp8", 64, 4096, 4096, 8700),
+    GemmWorkload("gemm_mxfp8_m512_n4096_k4096", "mxfp8", 512, 4096, 4096, 9300),
+    GemmWorkload("gemm_mxfp8_m1024_n4096_k4096", "mxfp8", 1024, 4096, 4096, 9400),
+    GemmWorkload("gemm_fp8_m1024_n4096_k4096", "fp8", 1024, 4096, 4096, 9500),
     GemmWorkload("gemm_nvfp4_m8192_n4096_k4096", "nvfp4", 8192, 4096, 4096, 8800),
     GemmWorkload("gemm_nvfp4_m64_n4096_k4096", "nvfp4", 64, 4096, 4096, 8900),
     GemmWorkload("gemm_nvfp4_m1_n4096_k4096", "nvfp4", 1, 4096, 4096, 9000),

@@ -76,3 +76,16 @@ def test_nvfp4_kernel_follows_the_dispatch(M, N, K, kernel):
     """The bench names the NVFP4 consumer kernel the library's tile choice
     picks (largest tile with enough workgroups)."""
     assert bench.nvfp4_kernel(M, N, K) == kernel
+
+
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (1, 4096, 4096, "gemm_fp8_decode"), (256, 4096, 4096, "gemm_fp8_decode"),
+    (192, 8192, 4096, "gemm_fp8_tn_dma<128>"), (300, 4096, 4096, "gemm_fp8_tn_dma<128>"),
+    (1024, 4096, 4096, "gemm_fp8_tn_dma<128>"), (2048, 4096, 4096, "gemm_fp8_tn_dma<256>"),
+    (8192, 4096, 4096, "gemm_fp8_tn_dma<256>"), (300, 520, 1056, "gemm_fp8_tn"),
+    (33, 300, 1536, "gemm_fp8_skinny")])
+def test_fp8_kernel_follows_the_dispatch(M, N, K, kernel):
+    """The bench names the FP8 / MXFP8 consumer kernel the library's tile
+    choice picks (256 x 256 once 128 workgroups, else 128 x 128 past 256 rows
+    or at 128 workgroups, else the decode-size kernels)."""
+    assert bench.fp8_kernel(M, N, K) == kernel

@@ -72,7 +72,12 @@ SHAPES = [(1, 8, 64), (5, 300, 96), (256, 256, 128), (300, 520, 1056), (513, 257
           (64, 1024, 4096), (1000, 40, 160), (300, 600, 4096), (257, 1100, 1536),
           (2000, 300, 1024), (1030, 1800, 512),
           (1, 4096, 2048), (33, 300, 2048), (7, 1000, 6144), (250, 130, 8192), (3, 64, 16384),
-          (20, 200, 2048), (9, 50, 4096), (70, 2100, 2048), (200, 5000, 2048)]
+          (20, 200, 2048), (9, 50, 4096), (70, 2100, 2048), (200, 5000, 2048),
+          (2100, 4096, 512), (200, 16384, 512)]
+# Tile paths: K % 512 != 0 beyond 256 rows -> register-staged 256 x 256
+# kernel ((300, 520, 1056), (1000, 40, 160)); (2100, 4096) -> 144 workgroups
+# of 256 x 256; the other M > 256 shapes and (200, 16384) -> 128 x 128;
+# M <= 256 otherwise -> decode or skinny kernels.
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -113,7 +118,7 @@ def _tolerance_check(got_bits, exact, mag):
 
 @pytest.mark.parametrize("M,N,K", [(37, 300, 512), (256, 512, 4096), (129, 130, 1056), (512, 384, 4096),
                                    (300, 260, 160), (17, 96, 16384), (1, 333, 4096), (100, 2000, 4096),
-                                   (250, 4100, 4096)])
+                                   (250, 4100, 4096), (2100, 4096, 1024), (1030, 1800, 1024)])
 def test_mxfp8_gemm_random(M, N, K):
     print(f"gemm mx random M={M} N={N} K={K}", flush=True)
     rng = np.random.default_rng(M + N + K)
@@ -126,7 +131,7 @@ def test_mxfp8_gemm_random(M, N, K):
     _tolerance_check(got, exact, mag)
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 300, 2048), (600, 300, 2048)])
+@pytest.mark.parametrize("M,N,K", [(200, 300, 2048), (600, 300, 2048), (2100, 4096, 512), (200, 16384, 512)])
 def test_fp8_static_gemm_random(M, N, K):
     rng = np.random.default_rng(17)
     aq, bq = _finite_codes(rng, (M, K)), _finite_codes(rng, (N, K))
