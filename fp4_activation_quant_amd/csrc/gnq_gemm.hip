@@ -19,15 +19,22 @@
 // Accumulator register v of lane l is C[8 * (v / 4) + 4 * (l / 32) + v % 4]
 // [l % 32].
 //
-// Tiling: 256 threads (4 waves) per workgroup, a 256 x 256 output tile per
-// workgroup and 128 x 128 (4 x 4 MFMA tiles, 256 fp32 accumulators) per
-// wave; K advances 64 bytes per step through LDS stages (A and B tiles,
-// 64-byte rows whose 16-byte chunks are XOR-swizzled by row to spread LDS
-// banks).  For K % 512 == 0 the stages are filled by direct global->LDS
-// DMA three steps ahead and the fragment reads are pipelined one step ahead
-// of the MFMAs; other K use a register-staged two-stage kernel.  Rows beyond
-// M or N are clamped on load and masked on store; a K tail of 32
-// (K % 64 == 32) loads zeros for the missing block.
+// Kernels (the dispatchers gemm_fp8 and gemm_nvfp4 at the end pick one by
+// shape and workgroup count):
+//  * gemm_fp8_tn_dma<.., T>: FP8 / MXFP8 for K % 512 == 0 on T x T
+//    workgroup tiles (T = 256: 4 waves of 128 x 128, 256 fp32 accumulators
+//    each; T = 128: 4 waves of 64 x 64), K advancing 64 bytes per step
+//    through LDS stages filled by direct global->LDS DMA three steps ahead,
+//    fragment reads pipelined one step ahead of the MFMAs;
+//  * gemm_fp8_tn: the register-staged two-stage kernel on 256 x 256 tiles
+//    for other K;
+//  * gemm_fp8_decode, gemm_fp8_skinny: up to 256 rows, small tiles whose
+//    waves split K (the weight stream is the cost);
+//  * gemm_nvfp4_gemv (up to 8 rows), gemm_nvfp4_k (32- to 128-row tiles,
+//    waves splitting K) and gemm_nvfp4_big (256 x 256): NVFP4.
+// LDS rows of 64 bytes have their 16-byte chunks XOR-swizzled by row to
+// spread LDS banks.  Rows beyond M or N are clamped on load and masked on
+// store; a K tail of 32 (K % 64 == 32) loads zeros for the missing block.
 #include <atomic>
 
 #include "gnq_common.hpp"
