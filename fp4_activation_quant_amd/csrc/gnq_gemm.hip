@@ -22,8 +22,9 @@
 // Kernels (the dispatchers gemm_fp8 and gemm_nvfp4 at the end pick one by
 // shape and workgroup count):
 //  * gemm_fp8_tn_dma<.., T>: FP8 / MXFP8 for K % 512 == 0 on T x T
-//    workgroup tiles (T = 256: 4 waves of 128 x 128, 256 fp32 accumulators
-//    each; T = 128: 4 waves of 64 x 64), K advancing 64 bytes per step
+//    workgroup tiles (T = 256: 8 waves of 64 x 128, two per SIMD, measured
+//    ~9% faster at 8192 x 4096 x 4096 than 4 waves of 128 x 128; T = 128:
+//    4 waves of 64 x 64), K advancing 64 bytes per step
 //    through LDS stages filled by direct global->LDS DMA three steps ahead,
 //    fragment reads pipelined one step ahead of the MFMAs;
 //  * gemm_fp8_tn: the register-staged two-stage kernel on 256 x 256 tiles
@@ -457,8 +458,8 @@ inline hipError_t allow_dynamic_lds(const void *kernel, int bytes, std::atomic<u
   template __global__ void gemm_fp8_tn_dma<MX, NW, TM, TN, T>(                                   \
       const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *, const float *,         \
       const float *, int, int, int, uint16_t *, int, int, int);
-GNQ_GEMM_DMA_INST(true, 4, 4, 4, 256)
-GNQ_GEMM_DMA_INST(false, 4, 4, 4, 256)
+GNQ_GEMM_DMA_INST(true, 8, 2, 4, 256)
+GNQ_GEMM_DMA_INST(false, 8, 2, 4, 256)
 GNQ_GEMM_DMA_INST(true, 4, 2, 2, 128)
 GNQ_GEMM_DMA_INST(false, 4, 2, 2, 128)
 #undef GNQ_GEMM_DMA_INST
@@ -1397,9 +1398,9 @@ hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const
   const bool dma = K % 512 == 0 && (!mx || ((uintptr_t)sa % 16 == 0 && (uintptr_t)sb % 16 == 0));
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256), t128 = ((M + 127) / 128) * ((N + 127) / 128);
   if (dma && t256 >= 128)
-    return mx ? launch_dma<true, 4, 4, 4, 256>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
+    return mx ? launch_dma<true, 8, 2, 4, 256>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
                                                (uint16_t *)c, st)
-              : launch_dma<false, 4, 4, 4, 256>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
+              : launch_dma<false, 8, 2, 4, 256>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
                                                 (uint16_t *)c, st);
   if (dma && (M > 256 || t128 >= 128))
     return mx ? launch_dma<true, 4, 2, 2, 128>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K,
