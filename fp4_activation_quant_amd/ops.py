@@ -75,9 +75,26 @@ def _outputs(M, H, mode, dev, scale):
     return torch.empty((M, H), dtype=FP8_DTYPE, device=dev), scale
 
 
+def _validate_out(x, mode, q, block_scale, y):
+    """Caller-supplied outputs: on x's device, contiguous, large enough, of
+    one-byte (codes, scales) or x's (y) elements; alignment is the library's
+    business (unaligned views take its scalar path)."""
+    M, H = x.shape
+    dev = x.device
+    if mode is not None:
+        _buf(q, "q", dev, nbytes=M * (H // 2) if mode == "nvfp4" else M * H, itemsize=1)
+    if mode == "nvfp4":
+        _buf(block_scale, "block_scale", dev, nbytes=_lib.nq_block_scale_bytes(M, H))
+    elif mode == "mxfp8":
+        _buf(block_scale, "block_scale", dev, nbytes=M * (H // 32), itemsize=1)
+    if y is not None:
+        _buf(y, "y", dev, nbytes=M * H * x.element_size(), dtype=x.dtype)
+
+
 def add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q, block_scale, y):
-    """One launch of the op into caller-allocated buffers; no allocation and
-    no checks beyond the library's own.
+    """One launch of the op into caller-allocated buffers; no allocation.
+    Every tensor is checked (device, contiguity, size, element type) before
+    its pointer goes to the library.
 
     ``norm``: "gemma" (scale by 1 + w) or "plain" (by w).  ``mode``: "fp8"
     (static per-tensor, ``scale`` = the dequant scale), "nvfp4" (``scale`` =
@@ -85,6 +102,8 @@ def add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q, block
     (``block_scale`` = (M, H // 32) E8M0 scales, ``scale`` ignored) or None
     (add + norm only; ``y`` required).  ``y`` None: the normed activation is
     not written."""
+    _validate(x, residual, weight, scale if mode in ("fp8", "nvfp4") else None)
+    _validate_out(x, mode, q, block_scale, y)
     M, H = x.shape
     with torch.cuda.device(x.device):
         st = _lib.nq_add_rms_norm_quant(
@@ -96,7 +115,10 @@ def add_rms_norm_quant_out(x, residual, weight, eps, scale, mode, norm, q, block
 
 def gemma_add_rms_norm_quant_out(x, residual, weight, eps, scale, nvfp4, q, block_scale, y):
     """The page's op (Gemma norm, FP8 or NVFP4) into caller-allocated buffers,
-    through the library's own entry point for it."""
+    through the library's own entry point for it (same checks as
+    ``add_rms_norm_quant_out``)."""
+    _validate(x, residual, weight, scale)
+    _validate_out(x, "nvfp4" if nvfp4 else "fp8", q, block_scale, y)
     M, H = x.shape
     with torch.cuda.device(x.device):
         st = _lib.nq_gemma_add_rms_norm_quant(

@@ -359,3 +359,27 @@ def test_wrappers_reject_bad_buffers():
         ops.quant_nvfp4(y, torch.ones(1, dtype=torch.float16, device=dev))
     with pytest.raises(ValueError, match="scales"):
         ops.quant_mxfp8(y, scales=torch.empty(M, K // 32 + 1, dtype=torch.uint8, device=dev))
+
+
+def test_op_out_forms_reject_bad_buffers():
+    """The caller-buffer forms of the op check their tensors too."""
+    dev = torch.device("cuda")
+    M, H = 4, 256
+    x = torch.zeros(M, H, dtype=torch.bfloat16, device=dev)
+    w = torch.zeros(H, dtype=torch.bfloat16, device=dev)
+    s = torch.ones(1, dtype=torch.float32, device=dev)
+    q = torch.empty(M, H // 2, dtype=torch.uint8, device=dev)
+    bs = torch.empty(ops.block_scale_bytes(M, H), dtype=torch.uint8, device=dev)
+    with pytest.raises(ValueError, match="block_scale"):
+        ops.gemma_add_rms_norm_quant_out(x, None, w, 1e-6, s, True, q, bs[:-1], None)
+    with pytest.raises(ValueError, match="q"):
+        ops.gemma_add_rms_norm_quant_out(x, None, w, 1e-6, s, True, q.cpu(), bs, None)
+    with pytest.raises(ValueError, match="y"):
+        ops.gemma_add_rms_norm_quant_out(x, None, w, 1e-6, s, True, q, bs,
+                                         torch.empty(M, H, dtype=torch.float16, device=dev))
+    with pytest.raises(ValueError, match="scale"):
+        ops.gemma_add_rms_norm_quant_out(x, None, w, 1e-6, s.cpu(), True, q, bs, None)
+    with pytest.raises(ValueError, match="block_scale"):
+        ops.add_rms_norm_quant_out(x, None, w, 1e-6, None, "mxfp8", "gemma",
+                                   torch.empty(M, H, dtype=torch.uint8, device=dev),
+                                   torch.empty(M, H // 32 - 1, dtype=torch.uint8, device=dev), None)
