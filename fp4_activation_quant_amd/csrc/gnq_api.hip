@@ -89,7 +89,8 @@ nq_status nq_add_rms_norm_quant(const void *x, void *residual, const void *weigh
   if (mode != NQ_MODE_FP8_STATIC && mode != NQ_MODE_NVFP4 && mode != NQ_MODE_NONE &&
       mode != NQ_MODE_MXFP8)
     return NQ_EINVAL;
-  if (M < 0 || H <= 0 || H > ((int64_t)1 << 30)) return NQ_EINVAL;
+  // H <= 2^30 and M * H <= 2^60: every byte count below fits 64 bits
+  if (M < 0 || H <= 0 || H > ((int64_t)1 << 30) || M > ((int64_t)1 << 60) / H) return NQ_EINVAL;
   const bool nv = mode == NQ_MODE_NVFP4, none = mode == NQ_MODE_NONE, mx = mode == NQ_MODE_MXFP8;
   if (!x || !weight) return NQ_EINVAL;
   if (!none && !q) return NQ_EINVAL;
@@ -153,7 +154,8 @@ static nq_status quant_common(const void *y, const float *scale, int64_t M, int6
                               int mode, void *q, void *block_scale, void *stream) {
   const bool nv = mode == NQ_MODE_NVFP4, mx = mode == NQ_MODE_MXFP8;
   if (!valid_dtype(dtype)) return NQ_EINVAL;
-  if (M < 0 || H <= 0 || H > ((int64_t)1 << 30)) return NQ_EINVAL;
+  // H <= 2^30 and M * H <= 2^60: every byte count below fits 64 bits
+  if (M < 0 || H <= 0 || H > ((int64_t)1 << 30) || M > ((int64_t)1 << 60) / H) return NQ_EINVAL;
   if (!y || !q || (!mx && !scale) || ((nv || mx) && !block_scale)) return NQ_EINVAL;
   if (nv && H % kBlock != 0) return NQ_EUNSUPPORTED;
   if (mx && H % kMxBlock != 0) return NQ_EUNSUPPORTED;

@@ -86,7 +86,8 @@ typedef enum { NQ_NORM_GEMMA = 0, NQ_NORM_PLAIN = 1 } nq_norm;
  *              scale (> 0); NVFP4 mode, the global scale (> 0) that maps a
  *              block's amax/6 into E4M3's range (448*6/amax for a tensor
  *              amax).  Non-finite values are outside the contract.
- *   M, H       rows (tokens) >= 0 and hidden size >= 1.  M == 0 returns
+ *   M, H       rows (tokens) >= 0 and hidden size 1 .. 2^30, with
+ *              M * H <= 2^60 (NQ_EINVAL otherwise).  M == 0 returns
  *              NQ_OK without launching.  NVFP4 needs H % 64 == 0 (whole
  *              4-column scale tiles, so no padded scale columns exist).
  *   dtype      nq_dtype of x, residual, weight and y.

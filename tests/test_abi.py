@@ -69,6 +69,8 @@ def call(**over):
     (dict(M=-3), _lib.NQ_EINVAL),
     (dict(H=0), _lib.NQ_EINVAL),
     (dict(H=-5), _lib.NQ_EINVAL),
+    (dict(H=(1 << 30) + 64), _lib.NQ_EINVAL),          # H beyond 2^30
+    (dict(M=(1 << 60) // 128 + 1), _lib.NQ_EINVAL),    # M * H beyond 2^60 (H = 128)
     (dict(dtype=7), _lib.NQ_EINVAL),
     (dict(mode=-1), _lib.NQ_EINVAL),
     (dict(wy=1, y=0), _lib.NQ_EINVAL),
@@ -139,6 +141,7 @@ def test_gemma_entry_rejects_no_quant_and_mxfp8_modes():
     (False, dict(q=X + 10), _lib.NQ_EINVAL),          # q overlaps y
     (False, dict(M=0), _lib.NQ_OK),
     (False, dict(H=7, M=0), _lib.NQ_OK),             # any H for FP8
+    (False, dict(M=1 << 59), _lib.NQ_EINVAL),        # M * H beyond 2^60
     (True, dict(bs=0), _lib.NQ_EINVAL),
     (True, dict(H=24), _lib.NQ_EUNSUPPORTED),
     (True, dict(H=48, M=0), _lib.NQ_OK),             # H % 16 == 0 suffices standalone
