@@ -79,6 +79,7 @@ EDGE = [
     (torch.bfloat16, True, 257, 4096, False, True),
     (torch.bfloat16, True, 130, 16384, True, True),
     (torch.bfloat16, True, 3, 32768, True, True),        # 4 chunks x 1024 threads
+    (torch.float16, True, 3, 32832, True, True),         # NVFP4 beyond 32768: scalar path
     (torch.bfloat16, True, 17, 4160, True, True),        # ragged 2-chunk split
     (torch.bfloat16, True, 2100, 256, True, True),       # XCD row map: 2 spans + ragged tail
     (torch.float16, True, 3072, 64, False, True),        # XCD row map: exact spans
