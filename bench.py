@@ -95,7 +95,7 @@ def fp8_kernel(M, N, K):
 
 def nvfp4_kernel(M, N, K):
     """The NVFP4 consumer kernel the library's dispatch picks for (M, N, K)."""
-    if M <= 8 and M * (K // 32) * 80 <= 128 * 1024:
+    if M <= 8 and M * N <= 12288 and M * (K // 32) * 80 <= 128 * 1024:
         return "gemm_nvfp4_gemv"
 
     def tiles(mt, nt):

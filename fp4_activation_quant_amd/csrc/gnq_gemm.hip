@@ -31,7 +31,7 @@
 //    for other K;
 //  * gemm_fp8_decode, gemm_fp8_skinny: up to 256 rows, small tiles whose
 //    waves split K (the weight stream is the cost);
-//  * gemm_nvfp4_gemv (up to 8 rows), gemm_nvfp4_k (32- to 128-row tiles,
+//  * gemm_nvfp4_gemv (a few rows, narrow weight), gemm_nvfp4_k (32- to 128-row tiles,
 //    waves splitting K) and gemm_nvfp4_big (256 x 256): NVFP4.
 // LDS rows of 64 bytes have their 16-byte chunks XOR-swizzled by row to
 // spread LDS banks.  Rows beyond M or N are clamped on load and masked on
@@ -1204,7 +1204,7 @@ hipError_t launch_nvfp4(const uint8_t *A, const uint8_t *SA, const float *a_gs, 
   return hipGetLastError();
 }
 
-// Few activation rows (M <= 8): a dot-product kernel, since 32-row MFMA
+// Few activation rows (up to 8): a dot-product kernel, since 32-row MFMA
 // tiles would dequantize a mostly padded activation tile for every weight
 // tile.  The workgroup first dequantizes the activation once into LDS as
 // fp16 (row m, 32-element chunk ci at (m * K / 32 + ci) * 80 bytes: the
@@ -1347,8 +1347,8 @@ hipError_t launch_nvfp4_gemv(const uint8_t *A, const uint8_t *SA, const float *a
 // Caller guarantees K % 64 == 0, 0 < M, N, and that the 32 x 32 tile count
 // fits a grid.  Tile choice (measured at N = 4096 and 8192, K = 4096): a
 // workgroup round costs about the same whatever its tile, so the largest
-// tile that still gives enough workgroups wins.  Up to 8 rows the
-// dot-product kernel; beyond 256 rows the 256 x 256 kernel once it has 128
+// tile that still gives enough workgroups wins.  For a few rows against a
+// narrow weight (M <= 8, M N <= 12288) the dot-product kernel; beyond 256 rows the 256 x 256 kernel once it has 128
 // workgroups (at N = 4096 it took 108 us at M = 300 to 1024 with 32-64
 // workgroups, against 31-67 us on 128 x 64 tiles); else the first of
 // 128 x 64, 64 x 64, 64 x 32 tiles giving 192 workgroups (M = 200: 64 x 64
@@ -1359,8 +1359,12 @@ hipError_t gemm_nvfp4(const void *a, const void *sa, const float *a_gs, const vo
   const uint8_t *SA = (const uint8_t *)sa, *SB = (const uint8_t *)sb;
   uint16_t *C = (uint16_t *)c;
   const int m = (int)M, n = (int)N, k = (int)K;
-  // up to 8 rows whose dequantized activation fits the LDS: dot products
-  if (M <= 8 && M * (K / 32) * (int64_t)kGemvChunk <= kGemvMaxLds) {
+  // dot products while their work (M N dot products per K) stays below the
+  // MFMA kernel's fixed cost: measured at N = K = 4096 they win up to
+  // M = 3 (6.6 against 7.2 us) and lose from M = 4 (7.7 against 7.2, 12.3
+  // against 7.3 at M = 8); at N = 8192 they tie at M = 2; the activation
+  // must fit the LDS
+  if (M <= 8 && M * N <= 12288 && M * (K / 32) * (int64_t)kGemvChunk <= kGemvMaxLds) {
     if (M == 1) return launch_nvfp4_gemv<1>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
     if (M == 2) return launch_nvfp4_gemv<2>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);
     if (M <= 4) return launch_nvfp4_gemv<4>(A, SA, a_gs, B, SB, b_gs, m, n, k, C, st);

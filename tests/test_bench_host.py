@@ -67,7 +67,9 @@ def test_kernel_name_follows_the_launchers_chunk_rule(H, cpt):
 
 
 @pytest.mark.parametrize("M,N,K,kernel", [
-    (1, 4096, 4096, "gemm_nvfp4_gemv"), (8, 50, 8192, "gemm_nvfp4_k<8,32,32,4>"),
+    (1, 4096, 4096, "gemm_nvfp4_gemv"), (3, 4096, 4096, "gemm_nvfp4_gemv"),
+    (4, 4096, 4096, "gemm_nvfp4_k<8,32,32,4>"), (2, 8192, 4096, "gemm_nvfp4_k<8,32,32,4>"),
+    (8, 300, 2880, "gemm_nvfp4_gemv"), (8, 50, 8192, "gemm_nvfp4_k<8,32,32,4>"),
     (64, 4096, 4096, "gemm_nvfp4_k<8,32,32,4>"), (128, 4096, 4096, "gemm_nvfp4_k<8,64,32,4>"),
     (256, 4096, 4096, "gemm_nvfp4_k<8,64,64,3>"), (1024, 4096, 4096, "gemm_nvfp4_k<4,128,64,4>"),
     (2048, 4096, 4096, "gemm_nvfp4_big"), (8192, 4096, 4096, "gemm_nvfp4_big"),

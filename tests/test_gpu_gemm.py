@@ -221,8 +221,10 @@ def _run_nvfp4(aq, abuf, ga, bq, bbuf, gb, M, N):
 # stage per wave; fewer stages than the large kernel's ring) up
 # K % 256 != 0 included: 64-element steps split unevenly over the small
 # kernel's waves (some with none) and odd step counts in the large one;
-# M <= 8 takes the dot-product kernel (each of its row counts 1, 2, 4, 8),
-# except M = 8 at K = 8192, whose fp16 activation exceeds its LDS; the tile
+# M <= 8 with M N <= 12288 takes the dot-product kernel (each of its row
+# counts 1, 2, 4, 8; (3, 4096, 256) sits on the bound), except M = 8 at
+# K = 8192, whose fp16 activation exceeds its LDS; (2, 6200, 512) and
+# (4, 4100, 320) lie just past the bound, on the 32 x 32 tiles; the tile
 # choice puts (2100, 4096) on 256 x 256 tiles, (300, 4096) and (257, 4160)
 # on 128 x 64, (200, 3072) on 64 x 64, (100, 3100) and (520, 700) on 64 x 32
 # and the rest on 32 x 32.
@@ -231,7 +233,7 @@ NVFP4_SHAPES = [(1, 8, 256), (5, 300, 512), (32, 64, 1024), (33, 100, 256), (200
                 (520, 700, 256), (1, 40, 64), (17, 96, 448), (64, 200, 1152), (260, 33, 64),
                 (300, 260, 320), (257, 130, 1152), (2, 70, 320), (3, 130, 1152), (4, 17, 64),
                 (8, 50, 8192), (1, 2000, 3072), (2100, 4096, 128), (300, 4096, 256), (257, 4160, 192),
-                (200, 3072, 320), (100, 3100, 256)]
+                (200, 3072, 320), (100, 3100, 256), (3, 4096, 256), (2, 6200, 512), (4, 4100, 320)]
 
 
 @pytest.mark.parametrize("M,N,K", NVFP4_SHAPES)
