@@ -111,10 +111,17 @@ def nvfp4_kernel(M, N, K):
     return "gemm_nvfp4_k<8,32,32,4>" if K % 512 == 0 else "gemm_nvfp4_k<4,32,32,8>"
 
 
+def prefetch_rows(M, H):
+    """Whether the fused kernel loops 1024 workgroups over the rows, loading
+    the next row early (its launcher's rule)."""
+    return 4096 < H < 6144 and 2048 <= M <= 16384
+
+
 def kernel_name(wl):
-    return "fused_rows<{},{},{},{},{}>".format(
+    return "fused_rows<{},{},{},{},{}{}>".format(
         wl.dtype, wl.mode, "res" if wl.has_residual else "nores",
-        "y" if wl.write_y else "noy", chunks_per_thread(wl.H))
+        "y" if wl.write_y else "noy", chunks_per_thread(wl.H),
+        ",prefetch" if prefetch_rows(wl.M, wl.H) else "")
 
 
 def measured_traffic(wl):

@@ -3,9 +3,12 @@
 // (gnq_fused_<dtype>_<mode>.hip), which instantiates GNQ_FUSED_ENTRY.
 //
 // Design (memory-bound; no MFMA -- nothing here is a contraction):
-//  * fused_rows: one workgroup per row, grid = M (measured faster than a
-//    persistent grid on this chip: more independent rows in flight and no
-//    row loop).  A thread owns 8-element chunks (16 bytes) at chunk index
+//  * fused_rows: one workgroup per row, grid = M (at 32768 x 8192 a grid of
+//    512 to 2048 looping workgroups took 426-461 us against 380).  The
+//    exception (PF): rows of 4096 < H < 6144 (5- or 6-wave workgroups) at
+//    2048 <= M <= 16384 run on 1024 workgroups that loop over rows and issue
+//    the next row's loads before the current row's reduction, 5-15% faster
+//    at M = 2048 ... 8192 (H = 5120) and 1-6% at 16384.  A thread owns 8-element chunks (16 bytes) at chunk index
 //    tid, tid + nthr, ..., so every load and store instruction of a wave
 //    covers contiguous memory: 1 KB of x / residual / y, 512 B of FP8 codes,
 //    256 B of FP4 codes.  1, 2 or 4 chunks per thread (chunks_per_thread:
@@ -34,7 +37,7 @@
 
 namespace gnq {
 
-template <class D, int MODE, bool HAS_RES, bool WRITE_Y, bool GEMMA, int CPT>
+template <class D, int MODE, bool HAS_RES, bool WRITE_Y, bool GEMMA, int CPT, bool PF>
 __global__ void __launch_bounds__(kMaxThreads)
 fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__restrict__ w,
            const float *__restrict__ scale_ptr, float eps, int64_t M, int nchunk,
@@ -45,32 +48,37 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
   const unsigned nch = (unsigned)nchunk;
   const int nwaves = nthr / kWave;
   const float Hf = (float)(nchunk * kVec);
-  int parity = 0;
-  for (int64_t blk = blockIdx.x; blk < M; blk += gridDim.x, parity ^= 1) {
-    const int64_t row = MODE == kModeNvfp4 ? nvfp4_row_of_block(blk, M) : blk;
-    const size_t rbase = (size_t)row * (size_t)nchunk;
-    const u32x4 *__restrict__ xr = x + rbase;
-    u32x4 *__restrict__ rr = res + rbase;
-    u32x4 *__restrict__ yr = y + rbase;
-    // All loads first: x and residual stream from HBM (non-temporal), the
-    // weight and the scale come from L2.  The scale's reciprocal is formed
-    // while the row loads are in flight.
-    u32x4 xa[CPT], ra[CPT], wa[CPT];
+  // The row loads: x and residual stream from HBM (non-temporal).
+  u32x4 xa[CPT], ra[CPT], wa[CPT];
+  auto load_row = [&](int64_t b) {
+    const int64_t rw = MODE == kModeNvfp4 ? nvfp4_row_of_block(b, M) : b;
+    const size_t rb = (size_t)rw * (size_t)nchunk;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const unsigned ch = tid + c * nthr;
       if (ch < nch) {
-        xa[c] = __builtin_nontemporal_load(&xr[ch]);
-        if constexpr (HAS_RES) ra[c] = __builtin_nontemporal_load(&rr[ch]);
+        xa[c] = __builtin_nontemporal_load(&x[rb + ch]);
+        if constexpr (HAS_RES) ra[c] = __builtin_nontemporal_load(&res[rb + ch]);
       }
     }
+  };
+  int64_t blk = blockIdx.x;
+  if (blk < M) load_row(blk);
+  // The weight and the scale come from L2, once per workgroup; the scale's
+  // reciprocal is formed while the first row's loads are in flight.
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const unsigned ch = tid + c * nthr;
-      if (ch < nch) wa[c] = w[ch];
-    }
-    const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
-    const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+  for (int c = 0; c < CPT; ++c) {
+    const unsigned ch = tid + c * nthr;
+    if (ch < nch) wa[c] = w[ch];
+  }
+  const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
+  const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+  int parity = 0;
+  for (; blk < M; blk += gridDim.x, parity ^= 1) {
+    const int64_t row = MODE == kModeNvfp4 ? nvfp4_row_of_block(blk, M) : blk;
+    const size_t rbase = (size_t)row * (size_t)nchunk;
+    u32x4 *__restrict__ rr = res + rbase;
+    u32x4 *__restrict__ yr = y + rbase;
     // h = RN(x + r), written back; sum of squares of the rounded h.
     uint32_t hb[CPT][4];
     float ss = 0.0f;
@@ -96,6 +104,10 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
         }
       }
     }
+    // x and residual are dead once h is formed: with PF the next row's loads
+    // go out now, behind this row's reduction and stores.
+    if constexpr (PF)
+      if (blk + gridDim.x < M) load_row(blk + gridDim.x);
     ss = wave_sum(ss);
     if ((tid & (kWave - 1)) == 0) partial[parity][tid / kWave] = ss;
     __syncthreads();
@@ -125,6 +137,8 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
         quant_store_chunk<MODE>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles);
       }
     }
+    if constexpr (!PF)
+      if (blk + gridDim.x < M) load_row(blk + gridDim.x);
   }
 }
 
@@ -297,6 +311,16 @@ inline int chunks_per_thread(int64_t H) {
 
 inline bool aligned_to(const void *p, uintptr_t n) { return p == nullptr || ((uintptr_t)p % n) == 0; }
 
+// Whether fused_rows runs as 1024 workgroups looping over rows with the next
+// row's loads issued early (PF): rows of 4096 < H < 6144 (two chunks per
+// thread, 5- or 6-wave workgroups) at 2048 <= M <= 16384, where it measured
+// faster than one workgroup per row.  A multiple of 8 workgroups keeps each
+// workgroup's NVFP4 rows on its own XCD.
+constexpr int kPrefetchGrid = 1024;
+inline bool prefetch_rows(int64_t M, int64_t H) {
+  return H > 4096 && H < 6144 && M >= 2048 && M <= 16384;
+}
+
 // Whether fused_rows / fused_rows_small can take the call.
 inline bool vector_path_ok(const FusedArgs &a, int mode) {
   return (a.H % kBlock == 0) && (a.H / kVec) <= 4 * kMaxThreads && aligned_to(a.x, 16) &&
@@ -333,12 +357,13 @@ hipError_t run_fused(const FusedArgs &a) {
     const int cpt = chunks_per_thread(a.H);
     const int per_thread = (nchunk + cpt - 1) / cpt;
     const dim3 block(((per_thread + kWave - 1) / kWave) * kWave);
-#define GNQ_VEC(C)                                                                          \
-  hipLaunchKernelGGL((fused_rows<D, MODE, RES, WY, GEMMA, C>), grid, block, 0, a.st, x, res, w, \
+#define GNQ_VEC(C, P, G)                                                                       \
+  hipLaunchKernelGGL((fused_rows<D, MODE, RES, WY, GEMMA, C, P>), G, block, 0, a.st, x, res, w, \
                      a.scale, a.eps, a.M, nchunk, q, bs, y, ktiles)
-    if (cpt == 1) GNQ_VEC(1);
-    else if (cpt == 2) GNQ_VEC(2);
-    else GNQ_VEC(4);
+    if (cpt == 1) GNQ_VEC(1, false, grid);
+    else if (cpt == 2 && prefetch_rows(a.M, a.H)) GNQ_VEC(2, true, dim3(kPrefetchGrid));
+    else if (cpt == 2) GNQ_VEC(2, false, grid);
+    else GNQ_VEC(4, false, grid);
 #undef GNQ_VEC
     return hipGetLastError();
   }

@@ -63,7 +63,20 @@ def test_kernel_name_follows_the_launchers_chunk_rule(H, cpt):
     H = 16384, four beyond (the fused launcher's chunks_per_thread)."""
     assert bench.chunks_per_thread(H) == cpt
     assert bench.kernel_name(WORKLOADS["nvfp4_m32768_h8192_bf16_y"]).endswith(",1>")
-    assert bench.kernel_name(WORKLOADS["fp8_nores_m4096_h5120_fp16"]).endswith(",2>")
+    assert bench.kernel_name(WORKLOADS["fp8_nores_m4096_h5120_fp16"]).endswith(",2,prefetch>")
+    assert bench.kernel_name(WORKLOADS["fp8_decode_m256_h4096_bf16"]).endswith(",1>")
+
+
+@pytest.mark.parametrize("M,H,pf", [(4096, 5120, True), (2048, 4160, True), (16384, 6080, True),
+                                    (2047, 5120, False), (16385, 5120, False), (4096, 4096, False),
+                                    (4096, 6144, False), (32768, 8192, False), (1, 5120, False)])
+def test_prefetch_rule(M, H, pf):
+    """Rows of 4096 < H < 6144 at 2048 <= M <= 16384 take the looping
+    prefetch launch (the fused launcher's prefetch_rows), always with two
+    chunks per thread."""
+    assert bench.prefetch_rows(M, H) == pf
+    if pf:
+        assert bench.chunks_per_thread(H) == 2
 
 
 @pytest.mark.parametrize("M,N,K,kernel", [

@@ -5,7 +5,9 @@ benchmark uses; the oracle checks a row sample (rows are independent) and
 cheap whole-tensor properties cover the rest (residual == x + residual by
 torch's CPU add, guard bytes, untouched scale padding).  Edge cases cover
 ragged tiles, the scalar path (H % 16 != 0, H > 32768, unaligned views),
-1, 2 and 4 chunks per thread, several rows per wave (H <= 512), residual=None, write_y off, special values, M == 0,
+1, 2 and 4 chunks per thread, the looping launch with early loads (4096 < H
+< 6144 at 2048 <= M <= 16384), several rows per wave (H <= 512),
+residual=None, write_y off, special values, M == 0,
 determinism and argument errors.
 """
 
@@ -84,6 +86,8 @@ EDGE = [
     (torch.bfloat16, True, 2100, 256, True, True),       # XCD row map: 2 spans + ragged tail
     (torch.float16, True, 3072, 64, False, True),        # XCD row map: exact spans
     (torch.float16, True, 200, 5120, True, True),
+    (torch.float16, True, 2100, 5120, True, True),       # row loop with prefetch, ragged
+    (torch.bfloat16, False, 3000, 4160, False, False),   # row loop with prefetch
     (torch.bfloat16, True, 45, 6144, True, True),        # one chunk per thread, 12 waves
     (torch.float16, False, 33, 8192, False, True),       # one chunk per thread, 16 waves
     (torch.float16, True, 64, 192, False, False),
@@ -110,6 +114,42 @@ def test_edge_shapes(dt, nvfp4, M, H, res, wy):
     w = (torch.randn(H, generator=g) * 0.2).to(dt)
     scale = 0.03 if not nvfp4 else 448 * 6 / 5.0
     _run_and_compare(x, r, w, 1e-6, scale, nvfp4, wy)
+
+
+PREFETCH = [
+    # dtype, nvfp4, M, H, residual, write_y: rows of 4096 < H < 6144 at
+    # 2048 <= M <= 16384 loop 1024 workgroups over the rows
+    (torch.float16, True, 2100, 5120, True, True),
+    (torch.bfloat16, False, 3000, 4160, False, False),
+    (torch.float16, True, 4096, 6080, False, False),
+    (torch.bfloat16, True, 16384, 5120, True, False),
+]
+
+
+@pytest.mark.parametrize("dt,nvfp4,M,H,res,wy", PREFETCH)
+def test_row_loop_matches_one_workgroup_per_row(dt, nvfp4, M, H, res, wy):
+    """Rows are independent, so every byte the looping launch writes (the
+    whole residual, y, codes and scale buffer) must equal that of 1024-row
+    slices, which launch one workgroup per row; sampled rows of both launch
+    forms are checked against the oracle by the other tests."""
+    print(f"prefetch loop {dt} nvfp4={nvfp4} M={M} H={H} res={res} write_y={wy}", flush=True)
+    g = torch.Generator().manual_seed(M * 31 + H)
+    x = torch.randn(M, H, generator=g).to(dt)
+    r = (torch.randn(M, H, generator=g) * 2).to(dt) if res else None
+    w = (torch.randn(H, generator=g) * 0.2).to(dt)
+    scale = 0.03 if not nvfp4 else 448 * 6 / 5.0
+    full = P.run_gpu(x, r.clone() if res else None, w, 1e-6, scale, nvfp4, wy)
+    assert full["guards_ok"]
+    tile_row = ops.block_scale_bytes(128, H)      # bytes of one 128-row band of scale tiles
+    for a in range(0, M, 1024):
+        b = min(M, a + 1024)
+        part = P.run_gpu(x[a:b], r[a:b].clone() if res else None, w, 1e-6, scale, nvfp4, wy)
+        for k in ("residual", "y", "q"):
+            if full[k] is not None:
+                assert np.array_equal(full[k][a:b], part[k]), (k, a)
+        if nvfp4:
+            o = a // 128 * tile_row
+            assert np.array_equal(full["bs"][o:o + part["bs"].size], part["bs"]), a
 
 
 @pytest.mark.parametrize("nvfp4", [False, True])
