@@ -104,3 +104,19 @@ def test_fp8_kernel_follows_the_dispatch(M, N, K, kernel):
     choice picks (256 x 256 once 128 workgroups, else 128 x 128 past 256 rows
     or at 128 workgroups, else the decode-size kernels)."""
     assert bench.fp8_kernel(M, N, K) == kernel
+
+
+def test_cpu_baseline_single_and_all_threads(monkeypatch):
+    """Both CPU-baseline legs run the oracle on a prefix of the rows: the
+    single-threaded one and the one over every host thread (OMP_NUM_THREADS
+    caps the count)."""
+    from fp4_activation_quant_amd.workloads import make_inputs, load_scale
+    monkeypatch.setenv("OMP_NUM_THREADS", "2")
+    assert bench.host_threads() <= 2
+    wl = WORKLOADS["fp8_m16_h2048_bf16_y"]
+    x, r, w = make_inputs(wl)
+    out = bench.cpu_baseline(wl, x, r, w, load_scale(wl), 0.05)
+    assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
+    if bench.host_threads() > 1:
+        par = out["all_threads"]
+        assert par["cores"] == 2 and par["value"] > 0 and par["unit"] == "GB/s"
