@@ -30,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -57,15 +58,24 @@ def algorithmic_bytes(wl):
 
 def kernel_sha():
     """Hash of the fused kernel's source files (the shared header, the fused
-    kernel template and its per-mode translation units): traffic counters
-    taken on other sources are not reported."""
+    kernel template and its per-mode translation units) with comments and
+    blank space removed: traffic counters taken on other code are not
+    reported, while a comment edit keeps them."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SRC_DIR)):
         if name == "gnq_common.hpp" or name.startswith("gnq_fused"):
             h.update(name.encode())
-            with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(KERNEL_SRC_DIR, name), encoding="utf-8") as f:
+                h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
+
+
+def _code_only(src):
+    """C++ source without its comments, one space for each run of blank space
+    (the sources hold no string literal with a comment marker in it)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
 
 
 def chunks_per_thread(H):

@@ -7,9 +7,10 @@
 //    512 to 2048 looping workgroups took 426-461 us against 380).  The
 //    exception (PF): rows of 4096 < H < 6144 (5- or 6-wave workgroups) at
 //    2048 <= M <= 16384 run on 1024 workgroups that loop over rows and issue
-//    the next row's loads before the current row's reduction, 5-15% faster
-//    at M = 2048 ... 8192 (H = 5120) and 1-6% at 16384.  A thread owns 8-element chunks (16 bytes) at chunk index
-//    tid, tid + nthr, ..., so every load and store instruction of a wave
+//    the next row's loads before the current row's reduction: 5-15% faster
+//    at M = 2048 ... 8192 (H = 5120), -1 ... +6% at 16384.  A thread owns
+//    8-element chunks (16 bytes) at chunk index tid, tid + nthr, ..., so
+//    every load and store instruction of a wave
 //    covers contiguous memory: 1 KB of x / residual / y, 512 B of FP8 codes,
 //    256 B of FP4 codes.  1, 2 or 4 chunks per thread (chunks_per_thread:
 //    one up to H = 4096 and at H = 6144, 8192; else two up to 16384, four up

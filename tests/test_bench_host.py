@@ -120,3 +120,12 @@ def test_cpu_baseline_single_and_all_threads(monkeypatch):
     if bench.host_threads() > 1:
         par = out["all_threads"]
         assert par["cores"] == 2 and par["value"] > 0 and par["unit"] == "GB/s"
+
+
+def test_kernel_hash_ignores_comments_only():
+    """Traffic counters stay attached to the fused kernel's code across
+    comment and layout edits, and not across code edits."""
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* no\n overflow check */\n}\n"
+    assert bench._code_only(a) == bench._code_only("int f(int x) {\n\n return 2 * x;\n}")
+    assert bench._code_only(a) != bench._code_only("int f(int x) { return 3 * x; }")
+    assert len(bench.kernel_sha()) == 16
