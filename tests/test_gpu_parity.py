@@ -117,39 +117,49 @@ def test_edge_shapes(dt, nvfp4, M, H, res, wy):
 
 
 PREFETCH = [
-    # dtype, nvfp4, M, H, residual, write_y: rows of 4096 < H < 6144 at
+    # dtype, output, M, H, residual, write_y: rows of 4096 < H < 6144 at
     # 2048 <= M <= 16384 loop 1024 workgroups over the rows
-    (torch.float16, True, 2100, 5120, True, True),
-    (torch.bfloat16, False, 3000, 4160, False, False),
-    (torch.float16, True, 4096, 6080, False, False),
-    (torch.bfloat16, True, 16384, 5120, True, False),
+    (torch.float16, "nvfp4", 2100, 5120, True, True),
+    (torch.bfloat16, "fp8", 3000, 4160, False, False),
+    (torch.float16, "nvfp4", 4096, 6080, False, False),
+    (torch.bfloat16, "nvfp4", 16384, 5120, True, False),
+    (torch.bfloat16, "mxfp8", 2100, 5120, True, False),
+    (torch.float16, "none", 2048, 4608, True, True),      # add + plain norm alone
 ]
 
 
-@pytest.mark.parametrize("dt,nvfp4,M,H,res,wy", PREFETCH)
-def test_row_loop_matches_one_workgroup_per_row(dt, nvfp4, M, H, res, wy):
+@pytest.mark.parametrize("dt,out,M,H,res,wy", PREFETCH)
+def test_row_loop_matches_one_workgroup_per_row(dt, out, M, H, res, wy):
     """Rows are independent, so every byte the looping launch writes (the
     whole residual, y, codes and scale buffer) must equal that of 1024-row
     slices, which launch one workgroup per row; sampled rows of both launch
     forms are checked against the oracle by the other tests."""
-    print(f"prefetch loop {dt} nvfp4={nvfp4} M={M} H={H} res={res} write_y={wy}", flush=True)
+    print(f"prefetch loop {dt} {out} M={M} H={H} res={res} write_y={wy}", flush=True)
     g = torch.Generator().manual_seed(M * 31 + H)
     x = torch.randn(M, H, generator=g).to(dt)
     r = (torch.randn(M, H, generator=g) * 2).to(dt) if res else None
     w = (torch.randn(H, generator=g) * 0.2).to(dt)
+    nvfp4 = out == "nvfp4"
     scale = 0.03 if not nvfp4 else 448 * 6 / 5.0
-    full = P.run_gpu(x, r.clone() if res else None, w, 1e-6, scale, nvfp4, wy)
+    kw = dict(mxfp8=out == "mxfp8", quant=out != "none", norm="plain" if out == "none" else "gemma")
+
+    def run(a, b):
+        return P.run_gpu(x[a:b], r[a:b].clone() if res else None, w, 1e-6, scale, nvfp4, wy, **kw)
+
+    full = run(0, M)
     assert full["guards_ok"]
     tile_row = ops.block_scale_bytes(128, H)      # bytes of one 128-row band of scale tiles
     for a in range(0, M, 1024):
         b = min(M, a + 1024)
-        part = P.run_gpu(x[a:b], r[a:b].clone() if res else None, w, 1e-6, scale, nvfp4, wy)
+        part = run(a, b)
         for k in ("residual", "y", "q"):
             if full[k] is not None:
                 assert np.array_equal(full[k][a:b], part[k]), (k, a)
         if nvfp4:
             o = a // 128 * tile_row
             assert np.array_equal(full["bs"][o:o + part["bs"].size], part["bs"]), a
+        elif out == "mxfp8":
+            assert np.array_equal(full["bs"].reshape(M, H // 32)[a:b].ravel(), part["bs"]), a
 
 
 @pytest.mark.parametrize("nvfp4", [False, True])
