@@ -55,6 +55,14 @@ __global__ void convert_probe(int kind, const uint32_t *__restrict__ in, int64_t
     case 6: out[i] = (uint8_t)nvfp4_scale_code(f, param); break;
     case 7: out[i] = (uint8_t)mx_scale_code(fabsf(f)); break;
     case 8: out[i] = (uint8_t)e4m3_one(f * mx_elem_scale((uint32_t)param)); break;
+    case 9: {
+      // NVFP4 element step: bf16 y in bits 0..15, the block's E4M3 scale
+      // code in bits 16..23, global scale `param`.
+      const float o = nvfp4_elem_scale((bits >> 16) & 0xffu, param);
+      float v[8] = {Bf16::lo(bits & 0xffffu) * o, 0, 0, 0, 0, 0, 0, 0};
+      out[i] = (uint8_t)(e2m1x8(v) & 0xfu);
+      break;
+    }
     default: break;
   }
 }
@@ -257,7 +265,7 @@ nq_status nq_gemm_nvfp4(const void *a, const void *a_scales, const float *a_gs, 
 
 nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,
                            void *stream) {
-  if (kind < 0 || kind > 8 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in)))
+  if (kind < 0 || kind > 9 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in)))
     return NQ_EINVAL;
   // kind 8 takes an E8M0 code the kernels can produce (0..247) as param.
   if (kind == 8 && !(param >= 0.0f && param <= 247.0f && param == (float)(int)param))

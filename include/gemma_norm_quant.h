@@ -257,7 +257,11 @@ int nq_abi_version(void);
  *   kind 8: MXFP8 element code of the fp32 pattern in a block whose E8M0
  *           scale code is `param` (an integer in [0, 247], else
  *           NQ_EINVAL) -> 1 byte each
- *   out  device buffer of n (kinds 0, 1, 4..8) or 2n (kinds 2, 3) bytes.
+ *   kind 9: NVFP4 element code of bf16 y = bits 0..15 of the pattern in a
+ *           block whose E4M3FN scale code is bits 16..23, global scale
+ *           `param` (the E2M1(y * gs / decode(S)) step) -> 1 byte each
+ *           (code in the low nibble)
+ *   out  device buffer of n (kinds 0, 1, 4..9) or 2n (kinds 2, 3) bytes.
  *   n    in [0, 2^31).
  */
 nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,

@@ -34,6 +34,7 @@ from .formats import (  # noqa: F401
 )
 from .norm_quant import (  # noqa: F401
     add_residual, gemma_rms_norm, rms_norm, quant_fp8_static, quant_nvfp4,
+    nvfp4_block_scale_codes, nvfp4_element_codes,
     mxfp8_block_exponent, quant_mxfp8,
     swizzle_128x4_offset, block_scale_buffer_shape, scatter_block_scales,
     gemma_add_rms_norm_quant, add_rms_norm_quant,

@@ -33,6 +33,28 @@ design notes):
     types and shapes) per 32-element block, with the OCP MX scale rule:
         a = max|y|;  e = max(floor(log2 a) - 8, -127)  (-127 when a = 0);
         scale code = e + 127 (E8M0);  q = E4M3FN_RNE(clamp(y * 2^-e, +-448)).
+
+Parity (tests/test_oracle_norm.py, tests/test_oracle_quant.py):
+  * add_residual: torch's native bf16/fp16 add and the fp32-then-round sum;
+  * rms_norm / gemma_rms_norm: closed forms (constant rows, eps placement,
+    zero weight = torch's rms_norm, w = -1 gives signed zeros, power-of-two
+    row scaling) and an exact rational evaluation of the correctly rounded y;
+  * quant_fp8_static: hand-derived examples, two of which tell y / s from
+    y * fl(1 / s) apart, a brute-force nearest-code search and the E4M3
+    error bound;
+  * nvfp4_block_scale_codes / nvfp4_element_codes / quant_nvfp4: a
+    hand-derived example with gs = 1 and one with gs = 9868951 / 2^15 whose
+    inputs sit on ties where (gs * a) / 6, gs * fl(1 / sigma), 1 /
+    fl(sigma / gs) and y / fl(sigma / gs) each give other codes (the
+    arithmetic order is a reading of the pages, fixed by this fixture, not
+    a parity result against another implementation); brute-force nearest
+    codes, the block-max-gets-code-7 invariant, nibble order;
+  * quant_mxfp8: ten hand-derived blocks, the block exponent against a
+    linear search over every finite bf16 and fp16 magnitude, brute-force
+    element codes;
+  * swizzle_128x4_offset: hand-derived offsets, bijection, untouched padding.
+    The layout itself is named but not defined by the pages: its agreement
+    with an outside consumer is parity unpinned.
 """
 
 import numpy as np
@@ -41,6 +63,7 @@ from .formats import BF16, FP16, E4M3FN, E2M1, Format, bits_to_f64, f64_to_bits,
 
 __all__ = [
     "add_residual", "gemma_rms_norm", "rms_norm", "quant_fp8_static", "quant_nvfp4",
+    "nvfp4_block_scale_codes", "nvfp4_element_codes",
     "mxfp8_block_exponent", "quant_mxfp8",
     "swizzle_128x4_offset", "block_scale_buffer_shape", "scatter_block_scales",
     "gemma_add_rms_norm_quant", "add_rms_norm_quant",
@@ -122,6 +145,49 @@ def quant_fp8_static(y_bits, fmt: Format, scale: float) -> np.ndarray:
     return encode(v.astype(np.float64), E4M3FN)
 
 
+def nvfp4_block_scale_codes(amax, global_scale) -> np.ndarray:
+    """E4M3FN block-scale codes S from block amax values (fp32, >= 0).
+
+    The block's decode scale is amax / 6 (6 is E2M1's largest magnitude),
+    mapped into E4M3's range by the global scale gs: u = fl(gs * fl(amax / 6)),
+    then S = E4M3FN_RNE(min(u, 448)).  The pages state only that the fused
+    kernel uses the standalone NVFP4 quant's scale arithmetic
+    (``fused_norm_quant`` page, module docstring); this order of fp32
+    operations is the reading taken, and a hand-derived fixture with a
+    global scale other than 1 fixes it (the order (gs * amax) / 6 gives
+    another code there).
+    """
+    a = np.asarray(amax, dtype=np.float32)
+    gs = np.float32(global_scale)
+    t = a / np.float32(E2M1_MAX)                                   # fp32
+    with np.errstate(over="ignore"):
+        u = gs * t                                                 # fp32
+    u = np.minimum(u, np.float32(E4M3_MAX))
+    return encode(u.astype(np.float64), E4M3FN).astype(np.uint8)
+
+
+def nvfp4_element_codes(y, S, global_scale) -> np.ndarray:
+    """E2M1 codes (one per element, sign in bit 3) of fp32 values y in a
+    block whose E4M3FN scale code is S (broadcast against y).
+
+    The element multiplier is o = fl(gs / decode(S)), 0 for a zero scale;
+    each code is E2M1_RNE(clamp(fl(y * o), -6, 6)) (the ``_cvt_e2m1x2``
+    helper's ``cvt.rn.satfinite``).  As for the block scale, this order
+    (gs divided by the decoded scale, not multiplied by its rounded
+    reciprocal) is a reading, fixed by the same fixture.
+    """
+    y = np.asarray(y, dtype=np.float32)
+    gs = np.float32(global_scale)
+    sigma = decode(np.asarray(S, dtype=np.uint8), E4M3FN).astype(np.float32)
+    o = np.zeros_like(sigma)
+    nz = sigma != 0
+    o[nz] = gs / sigma[nz]                                         # fp32
+    with np.errstate(over="ignore", invalid="ignore"):
+        v = y * o                                                  # fp32
+    v = np.minimum(np.maximum(v, np.float32(-E2M1_MAX)), np.float32(E2M1_MAX))
+    return encode(v.astype(np.float64), E2M1).astype(np.uint8)
+
+
 def quant_nvfp4(y_bits, fmt: Format, global_scale: float):
     """NVFP4: E2M1 codes with one E4M3FN scale per 16-element block.
 
@@ -133,6 +199,8 @@ def quant_nvfp4(y_bits, fmt: Format, global_scale: float):
     round-to-nearest-even with saturation (the page's ``_cvt_e2m1x2`` helper
     uses ``cvt.rn.satfinite.e2m1x2.f32``), and each byte holds the
     even-index element in its low nibble (that helper's operand order).
+    Per block: ``nvfp4_block_scale_codes`` of its amax, then
+    ``nvfp4_element_codes`` of its elements.
 
     Returns ``(q, S)``: q is (M, H/2) uint8 packed codes; S is the (M, H/16)
     uint8 block-scale codes in row-major order (not yet swizzled).
@@ -142,24 +210,12 @@ def quant_nvfp4(y_bits, fmt: Format, global_scale: float):
     M, H = y.shape
     if H % NVFP4_BLOCK:
         raise ValueError("H must be a multiple of 16")
-    gs = np.float32(global_scale)
     blk = y.reshape(M, H // NVFP4_BLOCK, NVFP4_BLOCK)
     a = np.max(np.abs(blk), axis=2)                                # exact
-    t = a / np.float32(E2M1_MAX)                                   # fp32
-    with np.errstate(over="ignore"):
-        u = gs * t                                                 # fp32
-    u = np.minimum(u, np.float32(E4M3_MAX))
-    S = encode(u.astype(np.float64), E4M3FN)
-    sigma = decode(S, E4M3FN).astype(np.float32)
-    o = np.zeros_like(sigma)
-    nz = sigma != 0
-    o[nz] = gs / sigma[nz]                                         # fp32
-    with np.errstate(over="ignore", invalid="ignore"):
-        v = blk * o[:, :, None]                                    # fp32
-    v = np.minimum(np.maximum(v, np.float32(-E2M1_MAX)), np.float32(E2M1_MAX))
-    c = encode(v.astype(np.float64), E2M1).astype(np.uint8).reshape(M, H)
+    S = nvfp4_block_scale_codes(a, global_scale)
+    c = nvfp4_element_codes(blk, S[:, :, None], global_scale).reshape(M, H)
     q = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
-    return q, S.astype(np.uint8)
+    return q, S
 
 
 def mxfp8_block_exponent(amax) -> np.ndarray:

@@ -175,7 +175,8 @@ def test_standalone_mxfp8_validation(over, want):
 
 
 def test_probe_validation():
-    assert _lib.nq_convert_probe(9, 0x1000, 4, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
+    assert _lib.nq_convert_probe(10, 0x1000, 4, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
+    assert _lib.nq_convert_probe(-1, 0x1000, 4, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
     for bad in (-1.0, 248.0, 12.5, float("nan"), float("inf")):
         assert _lib.nq_convert_probe(8, 0x1000, 4, bad, 0x2000, 0) == _lib.NQ_EINVAL, bad
     assert _lib.nq_convert_probe(8, 0x1000, 0, 247.0, 0x2000, 0) == _lib.NQ_OK

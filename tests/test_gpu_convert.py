@@ -2,7 +2,8 @@
 oracle's encoders: every rounding tie of every fp32 binade with its two
 neighbours plus random patterns for the format encoders, every 16-bit y for
 the static FP8 quant step, and tie-heavy amax values for the NVFP4 block
-scale."""
+scale, every bf16 y for the NVFP4 element step, and the hand-derived NVFP4
+example with a global scale other than 1."""
 
 import numpy as np
 import pytest
@@ -91,14 +92,54 @@ def test_fp8_quant_step_every_16bit_y(kind, fmt):
         assert n == 0, (s32, ex)
 
 
-@pytest.mark.parametrize("gs", [1.0, 441.1076965332031, 360.0879211425781, 1e5, 1.0 / 7.0])
+GLOBAL_SCALES = [1.0, 441.1076965332031, 360.0879211425781, 1e5, 1.0 / 7.0, 301.176483154296875,
+                 448 * 6 / 8.925]
+
+
+@pytest.mark.parametrize("gs", GLOBAL_SCALES)
 def test_nvfp4_block_scale_step(gs):
+    """The kernel's block-scale code against the oracle's step on tie-heavy
+    fp32 amax values over 60 binades."""
     v = _tie_heavy_f32(exp_lo=-30, exp_hi=30, n_random=200_000)
     v = np.abs(v)
     got = probe(6, v.view(np.uint32), gs)
-    gs32 = np.float32(gs)
-    with np.errstate(over="ignore"):
-        u = np.minimum(gs32 * (v / np.float32(6)), np.float32(448))
-    want = O.encode(u.astype(np.float64), O.E4M3FN)
+    want = O.nvfp4_block_scale_codes(v, gs)
     n, ex = _mismatch(got, want, v)
     assert n == 0, ex
+
+
+@pytest.mark.parametrize("gs", GLOBAL_SCALES)
+def test_nvfp4_element_step_every_bf16_y(gs):
+    """The kernel's element code against the oracle's step: every finite bf16
+    y against 24 block-scale codes (zero, subnormal, normal, 448)."""
+    ycodes = np.arange(1 << 16, dtype=np.uint32)
+    ok = np.isfinite(O.decode(ycodes, O.BF16))
+    ycodes = ycodes[ok]
+    scodes = [0x00, 0x01, 0x05, 0x07, 0x08, 0x0F, 0x1C, 0x29, 0x2D, 0x30, 0x38, 0x3B, 0x41, 0x4E,
+              0x55, 0x5A, 0x60, 0x66, 0x6C, 0x6D, 0x73, 0x78, 0x7D, 0x7E]
+    for sc in scodes:
+        got = probe(9, ycodes | (sc << 16), gs)
+        y = O.bits_to_f64(ycodes.astype(np.uint16), O.BF16).astype(np.float32)
+        want = O.nvfp4_element_codes(y, np.full(y.shape, sc, np.uint8), gs)
+        n, ex = _mismatch(got, want, ycodes)
+        assert n == 0, (hex(sc), ex)
+
+
+def test_nvfp4_global_scale_fixture_on_gpu():
+    """The hand-derived gs != 1 example through the standalone NVFP4 quant
+    kernel (the fused kernel's quant routine): codes and scales as derived,
+    padding rows of the scale buffer untouched."""
+    from fp4_activation_quant_amd import ops
+    from tests.test_oracle_quant import _gs_fixture
+    from tests.golden import num
+    d, y, gs = _gs_fixture()
+    dev = torch.device("cuda")
+    yd = torch.tensor([y], dtype=torch.float64).to(torch.bfloat16).to(dev)
+    q = torch.full((1, 32), 0xA5, dtype=torch.uint8, device=dev)
+    bs = torch.full((128 * 4,), 0xA5, dtype=torch.uint8, device=dev)
+    ops.quant_nvfp4(yd, torch.tensor([gs], dtype=torch.float32, device=dev), q, bs)
+    torch.cuda.synchronize()
+    assert [int(b) for b in q[0].cpu()] == [num(t) for t in d["q"]]
+    b = bs.cpu().numpy()
+    assert [int(v) for v in b[:4]] == [num(t) for t in d["scales"]]
+    assert np.all(b[4:] == 0xA5)

@@ -86,6 +86,77 @@ def test_nvfp4_worked_example():
     assert np.all(buf[4:] == 0xA5)
 
 
+def _gs_fixture():
+    d = {}
+    for k, v in read_fixture("nvfp4_global_scale_example.txt"):
+        d.setdefault(k, []).extend(v)
+    y = [num(t) for t in d["y"]]
+    assert len(y) == int(num(d["H"][0])) == 64
+    return d, y, num(d["gscale"][0])
+
+
+def test_nvfp4_global_scale_example():
+    """Hand-derived NVFP4 quant with gs = 9868951 / 2^15: the block scale is
+    fl(gs * fl(a / 6)) rounded to E4M3 and the element multiplier fl(gs /
+    sigma) (the fixture's inputs sit on ties where other orders differ)."""
+    d, y, gs = _gs_fixture()
+    yb = vals_to_bits([y], O.BF16)
+    assert np.array_equal(O.bits_to_f64(yb, O.BF16)[0], np.array(y))   # exact bf16 values
+    q, S = O.quant_nvfp4(yb, O.BF16, gs)
+    assert [int(b) for b in q[0]] == [num(t) for t in d["q"]]
+    assert [int(b) for b in S[0]] == [num(t) for t in d["scales"]]
+    buf = np.full(128 * 4, 0xA5, np.uint8)
+    O.scatter_block_scales(S, 1, 64, buf)
+    assert [int(b) for b in buf[:4]] == [num(t) for t in d["scales"]]
+    assert np.all(buf[4:] == 0xA5)
+
+
+def test_nvfp4_global_scale_example_tells_orders_apart():
+    """The other plausible fp32 orders, evaluated here directly, give the
+    codes the fixture lists as theirs, all different from the fixture's:
+    (gs * a) / 6 for the block scale (blocks A and D); gs * fl(1 / sigma),
+    1 / fl(sigma / gs) and y / fl(sigma / gs) for the elements (block B)."""
+    d, y, gs = _gs_fixture()
+    f32 = np.float32
+    g = f32(gs)
+    yv = np.array(y, dtype=f32).reshape(4, 16)
+    a = np.abs(yv).max(axis=1)
+    alt_S = O.encode(np.minimum((g * a) / f32(6), f32(448)).astype(np.float64), O.E4M3FN)
+    want_alt = [num(t) for t in d["alt_gs_times_a_scales"]]
+    assert [int(v) for v in alt_S] == want_alt
+    assert want_alt != [num(t) for t in d["scales"]]
+    # block A's codes under the alternative block scale
+    sig_a = f32(O.decode(np.array([alt_S[0]]), O.E4M3FN)[0])
+    ca = O.encode(np.clip(yv[0] * f32(g / sig_a), -6, 6).astype(np.float64), O.E2M1)
+    assert [int(ca[2 * k] | (ca[2 * k + 1] << 4)) for k in range(8)] == [num(t) for t in d["alt_gs_times_a_q"]]
+    # block B's element codes under each alternative element multiplier
+    sig = f32(O.decode(np.array([num(d["scales"][1])]), O.E4M3FN)[0])
+    yb_ = yv[1]
+    alts = {
+        "gs * fl(1/sigma)": yb_ * f32(g * f32(f32(1) / sig)),
+        "1 / fl(sigma/gs)": yb_ * f32(f32(1) / f32(sig / g)),
+        "y / fl(sigma/gs)": yb_ / f32(sig / g),
+    }
+    want = [num(t) for t in d["alt_elem_scale_block_b_q"]]
+    for name, v in alts.items():
+        c = O.encode(np.clip(v.astype(f32), -6, 6).astype(np.float64), O.E2M1)
+        got = [int(c[2 * k] | (c[2 * k + 1] << 4)) for k in range(8)]
+        assert got == want, name
+    assert want != [num(t) for t in d["q"][8:16]]
+
+
+def test_nvfp4_steps_compose_quant():
+    """quant_nvfp4 is its two steps: the block-scale code of each block's
+    amax, then the element codes against that scale."""
+    yb = _random_y(4, 256, 41, spread=2.0)
+    gs = 448 * 6 / 11.0
+    q, S = O.quant_nvfp4(yb, O.BF16, gs)
+    y = O.bits_to_f64(yb, O.BF16).astype(np.float32).reshape(4, 16, 16)
+    assert np.array_equal(S, O.nvfp4_block_scale_codes(np.abs(y).max(axis=2), gs))
+    c = O.nvfp4_element_codes(y, S[:, :, None], gs).reshape(4, 256)
+    assert np.array_equal(q, (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8))
+
+
 def _random_y(M, H, seed, fmt=O.BF16, spread=1.0):
     g = torch.Generator().manual_seed(seed)
     y = torch.randn(M, H, generator=g) * torch.exp(torch.randn(M, H // 16, 1, generator=g).expand(M, H // 16, 16).reshape(M, H) * spread)
