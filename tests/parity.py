@@ -3,10 +3,9 @@
 The HIP op runs on device copies of CPU inputs, into output buffers that are
 pre-filled with a sentinel byte and followed by guard bytes, so that writes
 outside an output (or into the unwritten padding rows of the NVFP4 scale
-buffer) show up.  The oracle runs on a set of rows (all rows for small
-inputs, a seeded sample plus the first and the last 128-row tile for large
-ones); rows are independent, so a sampled row is compared exactly as in a
-full run.
+buffer) show up.  The oracle runs on every row, in 128-row chunks over a
+thread pool (rows are independent), so whole tensors are compared at every
+size.
 
 Acceptance, per element of the compared rows:
   residual     bit-exact;
@@ -22,6 +21,9 @@ Acceptance, per element of the compared rows:
                applied to the GPU's own y, bit for bit (needs the GPU's y);
   padding      scale-buffer rows >= M and all guard bytes keep the sentinel.
 """
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -108,16 +110,17 @@ def run_gpu(x, r, w, eps, scale, nvfp4, write_y, device="cuda", misalign=False, 
     return out
 
 
-def sample_rows(M, max_full=512, n_random=192, extra=(), seed=0):
-    """All rows when M is small, else the first and last 128-row tiles, a
-    seeded random sample and ``extra`` rows."""
-    if M <= max_full:
-        return np.arange(M)
-    rng = np.random.default_rng(seed)
-    last0 = (M - 1) // 128 * 128
-    rows = np.concatenate([np.arange(128), np.arange(last0, M), rng.choice(M, n_random, replace=False),
-                           np.asarray(list(extra), dtype=np.int64)])
-    return np.unique(rows)
+def all_rows(M):
+    """Every row: the oracle checks whole tensors (on 128-row chunks over a
+    thread pool, so the largest workload takes seconds)."""
+    return np.arange(M)
+
+
+def oracle_threads():
+    """Host threads for the oracle: the process's CPU affinity, at most 16
+    (the GPU machine's CPU share per GPU)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, n))
 
 
 def _ord16(b):
@@ -140,70 +143,120 @@ def gather_scales(bs_flat, rows, H):
     return bs_flat[O.swizzle_128x4_offset(mm, bb, H)]
 
 
-def compare(gpu, x, r, w, eps, scale, rows, y_gpu=None):
-    """Compare a GPU run with the oracle on ``rows``.  ``y_gpu`` (full (M, H)
-    uint16) is the GPU's y when the run itself did not write it."""
+CHUNK_ROWS = 128
+
+
+def _compare_chunk(gpu, xb_all, rb_all, wb, eps, scale, rows, yg_all, fmt):
+    """Raw counts for one chunk of rows (aggregated by ``compare``)."""
     M, H, nvfp4 = gpu["M"], gpu["H"], gpu["nvfp4"]
     mode, norm = gpu.get("mode", "nvfp4" if nvfp4 else "fp8"), gpu.get("norm", "gemma")
-    fmt = FMT[x.dtype]
-    rows = np.asarray(rows, dtype=np.int64)
-    xb = bits16(x)[rows]
-    rb = bits16(r)[rows] if r is not None else None
-    ref = O.add_rms_norm_quant(xb, rb, bits16(w), eps, scale, mode, norm, fmt)
-    rep = {"rows": len(rows), "elements": len(rows) * H, "guards_ok": gpu["guards_ok"],
-           "x_unchanged": gpu["x_unchanged"]}
-    if r is not None:
-        rep["residual_mismatch"] = int(np.count_nonzero(gpu["residual"][rows] != ref["residual"]))
-    yg = gpu["y"] if gpu["y"] is not None else y_gpu
-    if yg is not None:
-        yg = yg[rows]
+    xb = xb_all[rows]
+    rb = rb_all[rows] if rb_all is not None else None
+    ref = O.add_rms_norm_quant(xb, rb, wb, eps, scale, mode, norm, fmt)
+    c = {"elements": len(rows) * H}
+    if rb is not None:
+        c["residual_mismatch"] = int(np.count_nonzero(gpu["residual"][rows] != ref["residual"]))
+    y_equal = None
+    yg = None
+    if yg_all is not None:
+        yg = yg_all[rows]
         dy = np.abs(_ord16(yg) - _ord16(ref["y"]))
-        rep["y_max_ulp"] = int(dy.max()) if dy.size else 0
-        rep["y_diff_fraction"] = float(np.count_nonzero(dy) / max(dy.size, 1))
+        c["y_max_ulp"] = int(dy.max()) if dy.size else 0
+        c["y_diff"] = int(np.count_nonzero(dy))
         y_equal = yg == ref["y"]
         # +0 and -0 are one ulp step apart in no ordering: count them apart
-        rep["y_zero_sign_mismatch"] = int(np.count_nonzero((dy == 0) & ~y_equal))
-    else:
-        y_equal = None
+        c["y_zero_sign_mismatch"] = int(np.count_nonzero((dy == 0) & ~y_equal))
     if mode is None:
-        rep["code_max_step"] = 0
-        rep["code_diff_fraction"] = 0.0
-        return rep
+        return c
     if mode == "mxfp8":
         cg = gpu["q"][rows]
         cr = ref["q"]
         sg = gpu["bs"].reshape(M, H // 32)[rows]
         sr = ref["scales"]
-        rep["scale_match_fraction"] = float(np.count_nonzero(sg == sr) / max(sr.size, 1))
+        c["scale_match"], c["scales"] = int(np.count_nonzero(sg == sr)), int(sr.size)
         same_scale = np.repeat(sg == sr, 32, axis=1)
         step = np.where(same_scale, np.abs(_ord_code(cg, 0x80) - _ord_code(cr, 0x80)), 0)
-        rep["codes_in_rescaled_blocks"] = int(np.count_nonzero(~same_scale))
+        c["codes_in_rescaled_blocks"] = int(np.count_nonzero(~same_scale))
         if y_equal is not None:
             blk_eq = y_equal.reshape(len(rows), -1, 32).all(axis=2)
-            rep["scale_mismatch_where_y_equal"] = int(np.count_nonzero((sg != sr) & blk_eq))
-            rep["code_mismatch_where_y_equal"] = int(np.count_nonzero(
+            c["scale_mismatch_where_y_equal"] = int(np.count_nonzero((sg != sr) & blk_eq))
+            c["code_mismatch_where_y_equal"] = int(np.count_nonzero(
                 (cg != cr).reshape(len(rows), -1, 32).any(axis=2) & blk_eq))
             q2, s2 = O.quant_mxfp8(yg, fmt)
-            rep["requant_code_mismatch"] = int(np.count_nonzero(q2 != cg))
-            rep["requant_scale_mismatch"] = int(np.count_nonzero(s2 != sg))
-        rep["code_diff_fraction"] = float(np.count_nonzero(cg != cr) / max(cg.size, 1))
-        rep["code_max_step"] = int(step.max()) if step.size else 0
-        return rep
-    if nvfp4:
+            c["requant_code_mismatch"] = int(np.count_nonzero(q2 != cg))
+            c["requant_scale_mismatch"] = int(np.count_nonzero(s2 != sg))
+    elif nvfp4:
         cg = _unpack_e2m1(gpu["q"][rows])
         cr = _unpack_e2m1(ref["q"])
         step = np.abs(_ord_code(cg, 8) - _ord_code(cr, 8))
         sg = gather_scales(gpu["bs"], rows, H)
         sr = ref["scales"]
-        rep["scale_match_fraction"] = float(np.count_nonzero(sg == sr) / max(sr.size, 1))
+        c["scale_match"], c["scales"] = int(np.count_nonzero(sg == sr)), int(sr.size)
         if y_equal is not None:
             blk_eq = y_equal.reshape(len(rows), -1, 16).all(axis=2)
-            rep["scale_mismatch_where_y_equal"] = int(np.count_nonzero((sg != sr) & blk_eq))
-            rep["code_mismatch_where_y_equal"] = int(np.count_nonzero(
+            c["scale_mismatch_where_y_equal"] = int(np.count_nonzero((sg != sr) & blk_eq))
+            c["code_mismatch_where_y_equal"] = int(np.count_nonzero(
                 (cg != cr).reshape(len(rows), -1, 16).any(axis=2) & blk_eq))
             q2, s2 = O.quant_nvfp4(yg, fmt, scale)
-            rep["requant_code_mismatch"] = int(np.count_nonzero(q2 != gpu["q"][rows]))
-            rep["requant_scale_mismatch"] = int(np.count_nonzero(s2 != sg))
+            c["requant_code_mismatch"] = int(np.count_nonzero(q2 != gpu["q"][rows]))
+            c["requant_scale_mismatch"] = int(np.count_nonzero(s2 != sg))
+    else:
+        cg = gpu["q"][rows]
+        cr = ref["q"]
+        step = np.abs(_ord_code(cg, 0x80) - _ord_code(cr, 0x80))
+        if y_equal is not None:
+            c["code_mismatch_where_y_equal"] = int(np.count_nonzero((cg != cr) & y_equal))
+            q2 = O.quant_fp8_static(yg, fmt, scale)
+            c["requant_code_mismatch"] = int(np.count_nonzero(q2 != cg))
+    c["code_max_step"] = int(step.max()) if step.size else 0
+    c["code_diff"] = int(np.count_nonzero(cg != cr))
+    c["codes"] = int(cg.size)
+    return c
+
+
+_MAX_KEYS = ("y_max_ulp", "code_max_step")
+
+
+def compare(gpu, x, r, w, eps, scale, rows, y_gpu=None, threads=None):
+    """Compare a GPU run with the oracle on ``rows`` (normally every row).
+    ``y_gpu`` (full (M, H) uint16) is the GPU's y when the run itself did not
+    write it.  The oracle runs on chunks of at most 128 of these rows on a
+    thread pool (rows are independent; numpy releases the interpreter lock
+    inside its array loops)."""
+    M, H, nvfp4 = gpu["M"], gpu["H"], gpu["nvfp4"]
+    mode = gpu.get("mode", "nvfp4" if nvfp4 else "fp8")
+    fmt = FMT[x.dtype]
+    rows = np.asarray(rows, dtype=np.int64)
+    xb_all = bits16(x)
+    rb_all = bits16(r) if r is not None else None
+    wb = bits16(w)
+    yg_all = gpu["y"] if gpu["y"] is not None else y_gpu
+    chunks = [rows[i:i + CHUNK_ROWS] for i in range(0, len(rows), CHUNK_ROWS)]
+    with ThreadPoolExecutor(threads or oracle_threads()) as ex:
+        parts = list(ex.map(lambda c: _compare_chunk(gpu, xb_all, rb_all, wb, eps, scale, c, yg_all, fmt),
+                            chunks))
+    tot = {}
+    for p in parts:
+        for k, v in p.items():
+            tot[k] = max(tot.get(k, 0), v) if k in _MAX_KEYS else tot.get(k, 0) + v
+    rep = {"rows": len(rows), "elements": len(rows) * H, "guards_ok": gpu["guards_ok"],
+           "x_unchanged": gpu["x_unchanged"]}
+    for k in ("residual_mismatch", "y_max_ulp", "y_zero_sign_mismatch", "codes_in_rescaled_blocks",
+              "scale_mismatch_where_y_equal", "code_mismatch_where_y_equal", "requant_code_mismatch",
+              "requant_scale_mismatch"):
+        if k in tot:
+            rep[k] = tot[k]
+    if "y_diff" in tot:
+        rep["y_diff_fraction"] = float(tot["y_diff"] / max(rep["elements"], 1))
+    if mode is None:
+        rep["code_max_step"] = 0
+        rep["code_diff_fraction"] = 0.0
+        return rep
+    rep["code_max_step"] = tot.get("code_max_step", 0)
+    rep["code_diff_fraction"] = float(tot.get("code_diff", 0) / max(tot.get("codes", 0), 1))
+    if "scales" in tot:
+        rep["scale_match_fraction"] = float(tot["scale_match"] / max(tot["scales"], 1))
+    if nvfp4:
         # padding rows of the scale buffer keep the sentinel
         R = O.block_scale_buffer_shape(M, H)[0]
         if R > M:
@@ -211,16 +264,6 @@ def compare(gpu, x, r, w, eps, scale, rows, y_gpu=None):
             rep["padding_written"] = int(np.count_nonzero(pr != SENTINEL))
         else:
             rep["padding_written"] = 0
-    else:
-        cg = gpu["q"][rows]
-        cr = ref["q"]
-        step = np.abs(_ord_code(cg, 0x80) - _ord_code(cr, 0x80))
-        if y_equal is not None:
-            rep["code_mismatch_where_y_equal"] = int(np.count_nonzero((cg != cr) & y_equal))
-            q2 = O.quant_fp8_static(yg, fmt, scale)
-            rep["requant_code_mismatch"] = int(np.count_nonzero(q2 != cg))
-    rep["code_max_step"] = int(step.max()) if step.size else 0
-    rep["code_diff_fraction"] = float(np.count_nonzero(cg != cr) / max(cg.size, 1))
     return rep
 
 

@@ -33,7 +33,7 @@ def _run_and_compare(x, r, w, eps, write_y, rows=None, misalign=False, norm="gem
     if not write_y:
         y_gpu = P.run_gpu(x, r.clone() if r is not None else None, w, eps, 1.0, False, True,
                           misalign=misalign, norm=norm, mxfp8=True)["y"]
-    rows = P.sample_rows(x.shape[0]) if rows is None else rows
+    rows = P.all_rows(x.shape[0]) if rows is None else rows
     rep = P.compare(gpu, x, r, w, eps, 1.0, rows, y_gpu=y_gpu)
     if r is not None:
         assert np.array_equal(gpu["residual"], P.bits16(x + r))
@@ -49,10 +49,7 @@ def test_mxfp8_workload_parity(name):
     wl = WORKLOADS[name]
     print(f"mxfp8 workload {name}", flush=True)
     x, r, w = make_inputs(wl)
-    extra = ()
-    if wl.row_outliers:
-        extra = (x.float().abs().amax(dim=1) > 20).nonzero().flatten().tolist()
-    _run_and_compare(x, r, w, wl.eps, wl.write_y, rows=P.sample_rows(wl.M, extra=extra))
+    _run_and_compare(x, r, w, wl.eps, wl.write_y, rows=P.all_rows(wl.M))
 
 
 EDGE = [

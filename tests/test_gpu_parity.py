@@ -1,9 +1,9 @@
 """GPU parity: the HIP op against the CPU oracle, through the C ABI.
 
 Every workload runs at its full size in the launch configuration the
-benchmark uses; the oracle checks a row sample (rows are independent) and
-cheap whole-tensor properties cover the rest (residual == x + residual by
-torch's CPU add, guard bytes, untouched scale padding).  Edge cases cover
+benchmark uses; the oracle checks every row of every output (threaded over
+128-row chunks), plus residual == x + residual by torch's CPU add, guard
+bytes and untouched scale padding.  Edge cases cover
 ragged tiles, the scalar path (H % 16 != 0, H > 32768, unaligned views),
 1, 2 and 4 chunks per thread, the looping launch with early loads (4096 < H
 < 6144 at 2048 <= M <= 16384), several rows per wave (H <= 512),
@@ -39,7 +39,7 @@ def _run_and_compare(x, r, w, eps, scale, nvfp4, write_y, rows=None, misalign=Fa
         y_gpu = P.run_gpu(x, r.clone() if r is not None else None, w, eps, scale, nvfp4, True,
                           misalign=misalign, mxfp8=mxfp8)["y"]
     M = x.shape[0]
-    rows = P.sample_rows(M) if rows is None else rows
+    rows = P.all_rows(M) if rows is None else rows
     rep = P.compare(gpu, x, r, w, eps, scale, rows, y_gpu=y_gpu)
     if r is not None:
         rep["residual_full_mismatch"] = int(np.count_nonzero(gpu["residual"] != P.bits16(x + r)))
@@ -53,12 +53,7 @@ def test_workload_parity(name):
     wl = WORKLOADS[name]
     print(f"workload {name}", flush=True)
     x, r, w = make_inputs(wl)
-    extra = ()
-    if wl.row_outliers:
-        big = (x.float().abs().amax(dim=1) > 20).nonzero().flatten().tolist()
-        extra = big
-    rows = P.sample_rows(wl.M, extra=extra)
-    _run_and_compare(x, r, w, wl.eps, load_scale(wl), wl.nvfp4, wl.write_y, rows=rows,
+    _run_and_compare(x, r, w, wl.eps, load_scale(wl), wl.nvfp4, wl.write_y, rows=P.all_rows(wl.M),
                      mxfp8=wl.mode == "mxfp8")
 
 
@@ -132,8 +127,8 @@ PREFETCH = [
 def test_row_loop_matches_one_workgroup_per_row(dt, out, M, H, res, wy):
     """Rows are independent, so every byte the looping launch writes (the
     whole residual, y, codes and scale buffer) must equal that of 1024-row
-    slices, which launch one workgroup per row; sampled rows of both launch
-    forms are checked against the oracle by the other tests."""
+    slices, which launch one workgroup per row; both launch forms are
+    checked against the oracle, every row, by the other tests."""
     print(f"prefetch loop {dt} {out} M={M} H={H} res={res} write_y={wy}", flush=True)
     g = torch.Generator().manual_seed(M * 31 + H)
     x = torch.randn(M, H, generator=g).to(dt)
