@@ -119,11 +119,19 @@ nq_status nq_add_rms_norm_quant(const void *x, void *residual, const void *weigh
   const void *qq = none ? nullptr : q;
   const void *bb = (nv || mx) ? block_scale : nullptr;
   if (residual == x) return NQ_EINVAL;
-  const void *bufs[5] = {x, residual, qq, yy, bb};
-  const size_t lens[5] = {act, act, qbytes, act, bsbytes};
-  for (int i = 0; i < 5; ++i)
-    for (int j = i + 1; j < 5; ++j)
-      if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return NQ_EINVAL;
+  // Written buffers may overlap nothing; read-only inputs (x, weight, the
+  // scale) may overlap each other.
+  const void *ss = (mode == NQ_MODE_FP8_STATIC || nv) ? (const void *)scale : nullptr;
+  const void *wr[4] = {residual, qq, yy, bb};
+  const size_t wlen[4] = {act, qbytes, act, bsbytes};
+  const void *rd[3] = {x, weight, ss};
+  const size_t rlen[3] = {act, (size_t)H * 2, 4};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(wr[i], wlen[i], wr[j], wlen[j])) return NQ_EINVAL;
+    for (int k = 0; k < 3; ++k)
+      if (overlaps(wr[i], wlen[i], rd[k], rlen[k])) return NQ_EINVAL;
+  }
   if (M == 0) return NQ_OK;
 
   FusedArgs a{x,
@@ -171,8 +179,10 @@ static nq_status quant_common(const void *y, const float *scale, int64_t M, int6
   const size_t act = (size_t)M * (size_t)H * 2;
   const size_t qbytes = nv ? (size_t)M * (size_t)(H / 2) : (size_t)M * (size_t)H;
   const size_t bsbytes = nv ? block_scale_bytes(M, H) : mx ? (size_t)M * (size_t)(H / kMxBlock) : 0;
-  if (overlaps(y, act, q, qbytes) || ((nv || mx) && (overlaps(y, act, block_scale, bsbytes) ||
-                                                     overlaps(q, qbytes, block_scale, bsbytes))))
+  const void *ss = mx ? nullptr : (const void *)scale;
+  const void *bb = (nv || mx) ? block_scale : nullptr;
+  if (overlaps(y, act, q, qbytes) || overlaps(y, act, bb, bsbytes) || overlaps(q, qbytes, bb, bsbytes) ||
+      overlaps(ss, 4, q, qbytes) || overlaps(ss, 4, bb, bsbytes))
     return NQ_EINVAL;
   if (M == 0) return NQ_OK;
   QuantArgs a{y, mx ? nullptr : scale, M, H, q, (nv || mx) ? block_scale : nullptr,
@@ -273,9 +283,8 @@ nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, voi
   if (n == 0) return NQ_OK;
   const int threads = 256;
   const int64_t blocks = (n + threads - 1) / threads;
-  hipLaunchKernelGGL(convert_probe, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,
-                     kind, (const uint32_t *)in, n, param, (uint8_t *)out);
-  return status_of(hipGetLastError());
+  return status_of(launch(convert_probe, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,
+                          kind, (const uint32_t *)in, n, param, (uint8_t *)out));
 }
 
 }  // extern "C"

@@ -18,6 +18,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gnq_launch.hpp"
+
 namespace gnq {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -341,37 +341,33 @@ hipError_t run_fused(const FusedArgs &a) {
   if (vector_path_ok(a, MODE)) {
     const int nchunk = (int)(a.H / kVec);
     if (a.H <= 512 && a.M <= kMaxGrid) {
-#define GNQ_SMALL(L)                                                                              \
-  hipLaunchKernelGGL((fused_rows_small<D, MODE, RES, WY, GEMMA, L>),                              \
-                     dim3((unsigned)((a.M + kSmallThreads / L - 1) / (kSmallThreads / L))),       \
-                     dim3(kSmallThreads), 0, a.st, x, res, w, a.scale, a.eps, a.M, nchunk, q, bs, \
-                     y, ktiles)
+#define GNQ_SMALL(L)                                                                               \
+  return launch(fused_rows_small<D, MODE, RES, WY, GEMMA, L>,                                       \
+                dim3((unsigned)((a.M + kSmallThreads / L - 1) / (kSmallThreads / L))),            \
+                dim3(kSmallThreads), 0, a.st, x, res, w, a.scale, a.eps, a.M, nchunk, q, bs, y, ktiles)
       if (nchunk <= 2) GNQ_SMALL(2);
-      else if (nchunk <= 4) GNQ_SMALL(4);
-      else if (nchunk <= 8) GNQ_SMALL(8);
-      else if (nchunk <= 16) GNQ_SMALL(16);
-      else if (nchunk <= 32) GNQ_SMALL(32);
-      else GNQ_SMALL(64);
+      if (nchunk <= 4) GNQ_SMALL(4);
+      if (nchunk <= 8) GNQ_SMALL(8);
+      if (nchunk <= 16) GNQ_SMALL(16);
+      if (nchunk <= 32) GNQ_SMALL(32);
+      GNQ_SMALL(64);
 #undef GNQ_SMALL
-      return hipGetLastError();
     }
     const int cpt = chunks_per_thread(a.H);
     const int per_thread = (nchunk + cpt - 1) / cpt;
     const dim3 block(((per_thread + kWave - 1) / kWave) * kWave);
-#define GNQ_VEC(C, P, G)                                                                       \
-  hipLaunchKernelGGL((fused_rows<D, MODE, RES, WY, GEMMA, C, P>), G, block, 0, a.st, x, res, w, \
-                     a.scale, a.eps, a.M, nchunk, q, bs, y, ktiles)
+#define GNQ_VEC(C, P, G)                                                                         \
+  return launch(fused_rows<D, MODE, RES, WY, GEMMA, C, P>, G, block, 0, a.st, x, res, w, a.scale, \
+                a.eps, a.M, nchunk, q, bs, y, ktiles)
     if (cpt == 1) GNQ_VEC(1, false, grid);
-    else if (cpt == 2 && prefetch_rows(a.M, a.H)) GNQ_VEC(2, true, dim3(kPrefetchGrid));
-    else if (cpt == 2) GNQ_VEC(2, false, grid);
-    else GNQ_VEC(4, false, grid);
+    if (cpt == 2 && prefetch_rows(a.M, a.H)) GNQ_VEC(2, true, dim3(kPrefetchGrid));
+    if (cpt == 2) GNQ_VEC(2, false, grid);
+    GNQ_VEC(4, false, grid);
 #undef GNQ_VEC
-    return hipGetLastError();
   }
-  hipLaunchKernelGGL((fused_rows_scalar<D, MODE, RES, WY, GEMMA>), grid, dim3(256), 0, a.st,
-                     (const uint16_t *)a.x, (uint16_t *)a.res, (const uint16_t *)a.w, a.scale,
-                     a.eps, a.M, (int)a.H, q, bs, (uint16_t *)a.y, ktiles);
-  return hipGetLastError();
+  return launch(fused_rows_scalar<D, MODE, RES, WY, GEMMA>, grid, dim3(256), 0, a.st,
+                (const uint16_t *)a.x, (uint16_t *)a.res, (const uint16_t *)a.w, a.scale, a.eps, a.M,
+                (int)a.H, q, bs, (uint16_t *)a.y, ktiles);
 }
 
 template <class D, int MODE>

@@ -473,9 +473,8 @@ hipError_t launch_dma(const uint8_t *A, const uint8_t *SA, const uint8_t *B, con
   const hipError_t e = allow_dynamic_lds((const void *)gemm_fp8_tn_dma<MX, NW, TM, TN, T>, lds, lds_set);
   if (e != hipSuccess) return e;
   const int tiles_m = (M + T - 1) / T, tiles = tiles_m * ((N + T - 1) / T);
-  hipLaunchKernelGGL((gemm_fp8_tn_dma<MX, NW, TM, TN, T>), dim3(tiles), dim3(64 * NW), lds, st, A, SA,
-                     B, SB, a_scale, b_scale, M, N, K, C, tiles_m, tiles, 127);
-  return hipGetLastError();
+  return launch(gemm_fp8_tn_dma<MX, NW, TM, TN, T>, dim3(tiles), dim3(64 * NW), lds, st, A, SA, B, SB,
+                a_scale, b_scale, M, N, K, C, tiles_m, tiles, 127);
 }
 
 
@@ -577,9 +576,8 @@ hipError_t launch_skinny(const uint8_t *A, const uint8_t *SA, const uint8_t *B, 
   const hipError_t e = allow_dynamic_lds((const void *)gemm_fp8_skinny<MX>, kSkinnyLds, lds_set);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + kSkinnyRows - 1) / kSkinnyRows));
-  hipLaunchKernelGGL((gemm_fp8_skinny<MX>), grid, dim3(64 * kSkinnyWaves), kSkinnyLds, st, A, SA, B, SB,
-                     a_scale, b_scale, M, N, K, C, 127);
-  return hipGetLastError();
+  return launch(gemm_fp8_skinny<MX>, grid, dim3(64 * kSkinnyWaves), kSkinnyLds, st, A, SA, B, SB,
+                a_scale, b_scale, M, N, K, C, 127);
 }
 
 // Decode-size GEMM (few activation rows, K % 2048 == 0, K <= 16384): a
@@ -780,9 +778,8 @@ hipError_t launch_decode_tile(const uint8_t *A, const uint8_t *SA, const uint8_t
   const hipError_t e = allow_dynamic_lds((const void *)gemm_fp8_decode<MX, NW, MT, NT, S>, kDecLdsMax, lds_set);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((N + NT - 1) / NT), (unsigned)((M + MT - 1) / MT));
-  hipLaunchKernelGGL((gemm_fp8_decode<MX, NW, MT, NT, S>), grid, dim3(64 * NW), dec_lds_bytes(K, MT, NT), st, A,
-                     SA, B, SB, a_scale, b_scale, M, N, K, C, 127);
-  return hipGetLastError();
+  return launch(gemm_fp8_decode<MX, NW, MT, NT, S>, grid, dim3(64 * NW), dec_lds_bytes(K, MT, NT), st, A,
+                SA, B, SB, a_scale, b_scale, M, N, K, C, 127);
 }
 
 // Tile choice (measured on 4096- and 8192-wide weights, K 4096 and 8192):
@@ -1182,9 +1179,8 @@ hipError_t launch_nvfp4_big(const uint8_t *A, const uint8_t *SA, const float *a_
   if (e != hipSuccess) return e;
   const int tiles_m = (M + kFp4BigRows - 1) / kFp4BigRows, tiles_n = (N + kFp4BigRows - 1) / kFp4BigRows;
   const int tiles = tiles_m * tiles_n;
-  hipLaunchKernelGGL(gemm_nvfp4_big, dim3((unsigned)tiles), dim3(256), kFp4BigLds, st, A, SA, a_gs, B, SB, b_gs, M,
-                     N, K, C, tiles_m, tiles);
-  return hipGetLastError();
+  return launch(gemm_nvfp4_big, dim3((unsigned)tiles), dim3(256), kFp4BigLds, st, A, SA, a_gs, B, SB, b_gs, M,
+                N, K, C, tiles_m, tiles);
 }
 
 template <int NW, int MT, int NT, int S>
@@ -1199,9 +1195,8 @@ hipError_t launch_nvfp4(const uint8_t *A, const uint8_t *SA, const float *a_gs, 
   if (e != hipSuccess) return e;
   const int tiles_n = (N + NT - 1) / NT;
   const long tiles = (long)((M + MT - 1) / MT) * tiles_n;
-  hipLaunchKernelGGL((gemm_nvfp4_k<NW, MT, NT, S>), dim3((unsigned)tiles), dim3(64 * NW), lds, st, A, SA, a_gs, B,
-                     SB, b_gs, M, N, K, C, tiles_n);
-  return hipGetLastError();
+  return launch(gemm_nvfp4_k<NW, MT, NT, S>, dim3((unsigned)tiles), dim3(64 * NW), lds, st, A, SA, a_gs, B,
+                SB, b_gs, M, N, K, C, tiles_n);
 }
 
 // Few activation rows (up to 8): a dot-product kernel, since 32-row MFMA
@@ -1339,9 +1334,8 @@ hipError_t launch_nvfp4_gemv(const uint8_t *A, const uint8_t *SA, const float *a
   const hipError_t e = allow_dynamic_lds((const void *)gemm_nvfp4_gemv<MR>, kGemvMaxLds, lds_set);
   if (e != hipSuccess) return e;
   const int lds = M * (K / 32) * kGemvChunk;
-  hipLaunchKernelGGL((gemm_nvfp4_gemv<MR>), dim3((unsigned)((N + kGemvRows - 1) / kGemvRows)), dim3(512), lds, st,
-                     A, SA, a_gs, B, SB, b_gs, M, N, K, C);
-  return hipGetLastError();
+  return launch(gemm_nvfp4_gemv<MR>, dim3((unsigned)((N + kGemvRows - 1) / kGemvRows)), dim3(512), lds, st,
+                A, SA, a_gs, B, SB, b_gs, M, N, K, C);
 }
 
 // Caller guarantees K % 64 == 0, 0 < M, N, and that the 32 x 32 tile count
@@ -1421,13 +1415,8 @@ hipError_t gemm_fp8(bool mx, const void *a, const void *sa, const void *b, const
               : launch_skinny<false>(A, SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, st);
   const int tiles_m = (int)((M + kGemmTile - 1) / kGemmTile);
   const int tiles = tiles_m * (int)((N + kGemmTile - 1) / kGemmTile);
-  if (mx)
-    hipLaunchKernelGGL((gemm_fp8_tn<true>), dim3(tiles), dim3(kGemmThreads), 0, st, A, SA, B, SB,
-                       a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m, tiles, 127);
-  else
-    hipLaunchKernelGGL((gemm_fp8_tn<false>), dim3(tiles), dim3(kGemmThreads), 0, st, A, SA, B, SB,
-                       a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m, tiles, 127);
-  return hipGetLastError();
+  return launch(mx ? gemm_fp8_tn<true> : gemm_fp8_tn<false>, dim3(tiles), dim3(kGemmThreads), 0, st, A,
+                SA, B, SB, a_scale, b_scale, (int)M, (int)N, (int)K, (uint16_t *)c, tiles_m, tiles, 127);
 }
 
 }  // namespace gnq

@@ -97,18 +97,16 @@ hipError_t run_quant(const QuantArgs &a) {
     const int cpt = nchunk <= kMaxThreads ? 1 : (nchunk <= 2 * kMaxThreads ? 2 : 4);
     const int per_thread = (nchunk + cpt - 1) / cpt;
     const dim3 block(((per_thread + kWave - 1) / kWave) * kWave);
-#define GNQ_QV(C)                                                                               \
-  hipLaunchKernelGGL((quant_rows<D, MODE, C>), grid, block, 0, a.st, (const u32x4 *)a.y, a.scale, \
-                     a.M, nchunk, (uint8_t *)a.q, (uint8_t *)a.bs, ktiles)
+#define GNQ_QV(C)                                                                              \
+  return launch(quant_rows<D, MODE, C>, grid, block, 0, a.st, (const u32x4 *)a.y, a.scale, a.M, \
+                nchunk, (uint8_t *)a.q, (uint8_t *)a.bs, ktiles)
     if (cpt == 1) GNQ_QV(1);
-    else if (cpt == 2) GNQ_QV(2);
-    else GNQ_QV(4);
+    if (cpt == 2) GNQ_QV(2);
+    GNQ_QV(4);
 #undef GNQ_QV
-    return hipGetLastError();
   }
-  hipLaunchKernelGGL((quant_rows_scalar<D, MODE>), grid, dim3(256), 0, a.st, (const uint16_t *)a.y,
-                     a.scale, a.M, (int)a.H, (uint8_t *)a.q, (uint8_t *)a.bs, ktiles);
-  return hipGetLastError();
+  return launch(quant_rows_scalar<D, MODE>, grid, dim3(256), 0, a.st, (const uint16_t *)a.y, a.scale,
+                a.M, (int)a.H, (uint8_t *)a.q, (uint8_t *)a.bs, ktiles);
 }
 
 }  // namespace gnq

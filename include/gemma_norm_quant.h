@@ -39,7 +39,15 @@
  * The library allocates nothing, keeps no pointer past the call and launches
  * asynchronously on `stream` (a hipStream_t; NULL is the null stream).  On
  * any error nothing is launched and nothing is written.  No C++ exception
- * crosses this boundary.
+ * crosses this boundary.  NQ_EHIP is the status of this call's own HIP
+ * calls (the launch's return value): an error an earlier call left on the
+ * thread is neither reported nor cleared.
+ *
+ * Library state: none for the norm / quant entry points.  The GEMM entry
+ * points raise their kernels' dynamic-LDS limit (hipFuncSetAttribute) on
+ * the first call on each device and remember that in a process-wide atomic
+ * bit set per kernel (devices 0..63); concurrent first calls may both set
+ * the attribute, which is harmless.  Nothing else persists between calls.
  */
 #ifndef GEMMA_NORM_QUANT_H
 #define GEMMA_NORM_QUANT_H
@@ -101,7 +109,9 @@ typedef enum { NQ_NORM_GEMMA = 0, NQ_NORM_PLAIN = 1 } nq_norm;
  *   y          (M, H) dtype when write_y, else ignored (may be NULL).
  *   stream     hipStream_t to launch on.
  *
- * Outputs must not overlap inputs or each other (residual is both).
+ * Outputs (residual, q, block_scale, y) must not overlap each other or an
+ * input (x, weight, and the fp32 scale in FP8 / NVFP4 modes); read-only
+ * inputs may overlap each other (NQ_EINVAL otherwise, nothing written).
  * x, residual, weight and y must be 2-byte aligned and scale 4-byte aligned
  * (NQ_EINVAL otherwise); any H is accepted.  The fast path needs 16-byte
  * aligned pointers and H % 16 == 0, other cases take a slower correct path.

@@ -86,6 +86,15 @@ def call(**over):
     (dict(w=W + 1), _lib.NQ_EINVAL),
     (dict(wy=1, y=Y + 3), _lib.NQ_EINVAL),
     (dict(s=S + 2), _lib.NQ_EINVAL),                 # fp32 scale must be 4-byte aligned
+    # outputs overlapping the weight (H * 2 bytes) or the fp32 scale
+    (dict(q=W + 64), _lib.NQ_EINVAL),
+    (dict(r=W - 1024 + 2), _lib.NQ_EINVAL),          # residual's last bytes reach the weight
+    (dict(wy=1, y=W + 254), _lib.NQ_EINVAL),
+    (dict(mode=1, bs=W + 16), _lib.NQ_EINVAL),
+    (dict(q=S - 508), _lib.NQ_EINVAL),               # codes (512 bytes) end inside the scale
+    (dict(mode=1, bs=S), _lib.NQ_EINVAL),
+    (dict(r=S + 0), _lib.NQ_EINVAL),
+    (dict(wy=1, y=S - 1022), _lib.NQ_EINVAL),
     # M == 0: valid, returns before any launch
     (dict(M=0), _lib.NQ_OK),
     (dict(M=0, mode=1, wy=1), _lib.NQ_OK),
@@ -119,6 +128,8 @@ def call_ex(**over):
     (dict(mode=2, wy=1, y=0), _lib.NQ_EINVAL),
     (dict(mode=2, wy=1, y=X + 64), _lib.NQ_EINVAL),  # y overlaps x
     (dict(mode=2, wy=1, s=0, q=0, bs=0, M=0), _lib.NQ_OK),   # scale/q ignored in no-quant mode
+    (dict(mode=3, bs=W + 2), _lib.NQ_EINVAL),         # MXFP8 scales overlap the weight
+    (dict(mode=2, wy=1, y=W - 1000), _lib.NQ_EINVAL),  # y overlaps the weight
     (dict(norm=1, mode=1, H=96), _lib.NQ_EUNSUPPORTED),
     (dict(norm=1, M=0), _lib.NQ_OK),
     (dict(x=0, norm=1), _lib.NQ_EINVAL),
@@ -146,6 +157,9 @@ def test_gemma_entry_rejects_no_quant_and_mxfp8_modes():
     (True, dict(H=24), _lib.NQ_EUNSUPPORTED),
     (True, dict(H=48, M=0), _lib.NQ_OK),             # H % 16 == 0 suffices standalone
     (True, dict(bs=Q + 4), _lib.NQ_EINVAL),
+    (False, dict(s=Q + 4), _lib.NQ_EINVAL),           # scale inside the codes
+    (True, dict(s=B + 8), _lib.NQ_EINVAL),            # global scale inside the scale buffer
+    (True, dict(s=Q + 252), _lib.NQ_EINVAL),          # global scale inside the codes
 ])
 def test_standalone_quant_validation(nv, over, want):
     a = dict(y=X, s=S, M=4, H=128, dtype=0, q=Q, bs=B)

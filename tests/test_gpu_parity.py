@@ -249,6 +249,12 @@ def test_invalid_arguments_write_nothing():
         (dict(mode=1, H=80), _lib.NQ_EUNSUPPORTED),
         (dict(r=p), _lib.NQ_EINVAL),                 # residual aliases x
         (dict(q=p + 4096 + 512), _lib.NQ_EINVAL),    # q overlaps residual
+        (dict(q=p + 8192 + 64), _lib.NQ_EINVAL),     # q overlaps the weight
+        (dict(r=p + 8192 - 1022), _lib.NQ_EINVAL),   # residual reaches into the weight
+        (dict(wy=1, y=p + 8192 + 200), _lib.NQ_EINVAL),
+        (dict(mode=1, bs=p + 8192), _lib.NQ_EINVAL),
+        (dict(s=p + 12288 + 8), _lib.NQ_EINVAL),     # the scale inside q
+        (dict(mode=1, s=p + 16384 + 4), _lib.NQ_EINVAL),  # the global scale inside the scales
     ]
     for over, want in cases:
         a = dict(x=x, r=r, w=w, s=s.data_ptr(), M=M, H=H, dtype=0, mode=0, wy=0, q=q, bs=bs, y=y)
@@ -258,6 +264,34 @@ def test_invalid_arguments_write_nothing():
         assert st == want, (over, st)
     torch.cuda.synchronize()
     assert bool((buf == P.SENTINEL).all())
+
+
+def test_read_only_inputs_may_share_memory():
+    """x, the weight and the scale are only read, so they may overlap: the
+    weight here is x's first row and the fp32 scale is two bf16 elements of
+    x's row 5."""
+    M, H = 64, 1024
+    g = torch.Generator().manual_seed(77)
+    x = torch.randn(M, H, generator=g).to(torch.bfloat16)
+    r = torch.randn(M, H, generator=g).to(torch.bfloat16)
+    sv = torch.tensor([0.04], dtype=torch.float32)
+    x[5, 10:12] = sv.view(torch.bfloat16)               # the scale's bytes inside x
+    dev = torch.device("cuda")
+    xd, rd = x.to(dev), r.to(dev)
+    q = torch.empty((M, H), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    st = _lib.nq_gemma_add_rms_norm_quant(xd.data_ptr(), rd.data_ptr(), xd.data_ptr(), 1e-6,
+                                          xd.data_ptr() + (5 * H + 10) * 2, M, H, 0, 0, 1,
+                                          q.data_ptr(), 0, y.data_ptr(), 0)
+    assert st == _lib.NQ_OK
+    torch.cuda.synchronize()
+    ref = O.gemma_add_rms_norm_quant(P.bits16(x), P.bits16(r), P.bits16(x[0].clone()), 1e-6,
+                                     float(sv[0]), False, True)
+    assert np.array_equal(P.bits16(rd), ref["residual"])
+    dy = np.abs(P._ord16(P.bits16(y)) - P._ord16(ref["y"]))
+    assert dy.max() <= 1
+    same = P.bits16(y) == ref["y"]
+    assert np.array_equal(q.cpu().numpy()[same], ref["q"][same])
 
 
 def test_runs_on_the_callers_stream():
