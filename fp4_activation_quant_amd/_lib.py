@@ -16,7 +16,8 @@ NQ_MODE_FP8_STATIC, NQ_MODE_NVFP4, NQ_MODE_NONE, NQ_MODE_MXFP8 = 0, 1, 2, 3
 NQ_NORM_GEMMA, NQ_NORM_PLAIN = 0, 1
 EXPORTS = ("nq_gemma_add_rms_norm_quant", "nq_add_rms_norm_quant", "nq_quant_fp8_static",
            "nq_quant_nvfp4", "nq_quant_mxfp8", "nq_gemm_mxfp8", "nq_gemm_fp8_static", "nq_gemm_nvfp4",
-           "nq_block_scale_bytes", "nq_status_string", "nq_abi_version", "nq_convert_probe")
+           "nq_block_scale_bytes", "nq_status_string", "nq_abi_version", "nq_convert_probe",
+           "nq_traffic_probe")
 
 _lib = None
 
@@ -62,6 +63,10 @@ def lib():
         L.nq_abi_version.restype = i32
         L.nq_convert_probe.argtypes = [i32, vp, i64, f32, vp, vp]
         L.nq_convert_probe.restype = i32
+        pp = ctypes.POINTER(ctypes.c_void_p)
+        pi64 = ctypes.POINTER(ctypes.c_int64)
+        L.nq_traffic_probe.argtypes = [pp, pi64, i32, pp, pi64, i32, i64, i32, i32, i32, vp]
+        L.nq_traffic_probe.restype = i32
         _lib = L
     return _lib
 
@@ -130,3 +135,15 @@ def nq_convert_probe(kind, inp, n, param, out, stream):
     """Raw call: ``inp``/``out`` are device addresses (see the header)."""
     return lib().nq_convert_probe(int(kind), inp or None, int(n), float(param), out or None,
                                   stream or None)
+
+
+def nq_traffic_probe(src, src_row_bytes, dst, dst_row_bytes, rows, threads, grid, prefetch, stream):
+    """Raw call: ``src`` / ``dst`` are lists of device addresses, the row
+    byte counts lists of ints (see the header)."""
+    vpa = ctypes.c_void_p * max(1, len(src))
+    vpd = ctypes.c_void_p * max(1, len(dst))
+    i64a = ctypes.c_int64 * max(1, len(src))
+    i64d = ctypes.c_int64 * max(1, len(dst))
+    return lib().nq_traffic_probe(vpa(*src), i64a(*src_row_bytes), len(src), vpd(*dst) if dst else None,
+                                  i64d(*dst_row_bytes) if dst else None, len(dst), int(rows), int(threads),
+                                  int(grid), int(prefetch), stream or None)

@@ -13,24 +13,11 @@
 #include "gemma_norm_quant.h"
 #include "gnq_common.hpp"
 #include "gnq_gemm.hpp"
+#include "gnq_traffic.hpp"
+#include "gnq_validate.hpp"
 
 namespace gnq {
 namespace {
-
-bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
-  if (!a || !b || !na || !nb) return false;
-  const uintptr_t x0 = (uintptr_t)a, x1 = x0 + na, y0 = (uintptr_t)b, y1 = y0 + nb;
-  return x0 < y1 && y0 < x1;
-}
-
-bool valid_dtype(int dtype) { return dtype == NQ_BF16 || dtype == NQ_FP16; }
-
-size_t block_scale_bytes(int64_t M, int64_t H) {
-  if (M <= 0 || H < kBlock) return 0;
-  const int64_t rows = (M + 127) / 128 * 128;
-  const int64_t cols = ((H / kBlock) + 3) / 4 * 4;
-  return (size_t)rows * (size_t)cols;
-}
 
 nq_status status_of(hipError_t e) { return e == hipSuccess ? NQ_OK : NQ_EHIP; }
 
@@ -92,48 +79,9 @@ nq_status nq_add_rms_norm_quant(const void *x, void *residual, const void *weigh
                                 const float *scale, int64_t M, int64_t H, int dtype, int norm,
                                 int mode, int write_y, void *q, void *block_scale, void *y,
                                 void *stream) {
-  if (!valid_dtype(dtype)) return NQ_EINVAL;
-  if (norm != NQ_NORM_GEMMA && norm != NQ_NORM_PLAIN) return NQ_EINVAL;
-  if (mode != NQ_MODE_FP8_STATIC && mode != NQ_MODE_NVFP4 && mode != NQ_MODE_NONE &&
-      mode != NQ_MODE_MXFP8)
-    return NQ_EINVAL;
-  // H <= 2^30 and M * H <= 2^60: every byte count below fits 64 bits
-  if (M < 0 || H <= 0 || H > ((int64_t)1 << 30) || M > ((int64_t)1 << 60) / H) return NQ_EINVAL;
+  const nq_status v = check_op(x, residual, weight, scale, M, H, dtype, norm, mode, write_y, q, block_scale, y);
+  if (v != NQ_OK || M == 0) return v;
   const bool nv = mode == NQ_MODE_NVFP4, none = mode == NQ_MODE_NONE, mx = mode == NQ_MODE_MXFP8;
-  if (!x || !weight) return NQ_EINVAL;
-  if (!none && !q) return NQ_EINVAL;
-  if ((mode == NQ_MODE_FP8_STATIC || nv) && !scale) return NQ_EINVAL;
-  if ((nv || mx) && !block_scale) return NQ_EINVAL;
-  if ((write_y || none) && !y) return NQ_EINVAL;
-  if (none && !write_y) return NQ_EINVAL;
-  if (nv && H % 64 != 0) return NQ_EUNSUPPORTED;
-  if (mx && H % kMxBlock != 0) return NQ_EUNSUPPORTED;
-  // 16-bit elements need 2-byte alignment, the fp32 scale 4-byte.
-  if (((uintptr_t)x | (uintptr_t)residual | (uintptr_t)weight | (uintptr_t)((write_y || none) ? y : nullptr)) % 2 != 0)
-    return NQ_EINVAL;
-  if ((mode == NQ_MODE_FP8_STATIC || nv) && (uintptr_t)scale % 4 != 0) return NQ_EINVAL;
-  const size_t act = (size_t)M * (size_t)H * 2;
-  const size_t qbytes = none ? 0 : nv ? (size_t)M * (size_t)(H / 2) : (size_t)M * (size_t)H;
-  const size_t bsbytes = nv ? block_scale_bytes(M, H) : mx ? (size_t)M * (size_t)(H / kMxBlock) : 0;
-  const void *yy = write_y ? y : nullptr;
-  const void *qq = none ? nullptr : q;
-  const void *bb = (nv || mx) ? block_scale : nullptr;
-  if (residual == x) return NQ_EINVAL;
-  // Written buffers may overlap nothing; read-only inputs (x, weight, the
-  // scale) may overlap each other.
-  const void *ss = (mode == NQ_MODE_FP8_STATIC || nv) ? (const void *)scale : nullptr;
-  const void *wr[4] = {residual, qq, yy, bb};
-  const size_t wlen[4] = {act, qbytes, act, bsbytes};
-  const void *rd[3] = {x, weight, ss};
-  const size_t rlen[3] = {act, (size_t)H * 2, 4};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(wr[i], wlen[i], wr[j], wlen[j])) return NQ_EINVAL;
-    for (int k = 0; k < 3; ++k)
-      if (overlaps(wr[i], wlen[i], rd[k], rlen[k])) return NQ_EINVAL;
-  }
-  if (M == 0) return NQ_OK;
-
   FusedArgs a{x,
               residual,
               weight,
@@ -168,23 +116,9 @@ nq_status nq_gemma_add_rms_norm_quant(const void *x, void *residual, const void 
 
 static nq_status quant_common(const void *y, const float *scale, int64_t M, int64_t H, int dtype,
                               int mode, void *q, void *block_scale, void *stream) {
+  const nq_status v = check_quant(y, scale, M, H, dtype, mode, q, block_scale);
+  if (v != NQ_OK || M == 0) return v;
   const bool nv = mode == NQ_MODE_NVFP4, mx = mode == NQ_MODE_MXFP8;
-  if (!valid_dtype(dtype)) return NQ_EINVAL;
-  // H <= 2^30 and M * H <= 2^60: every byte count below fits 64 bits
-  if (M < 0 || H <= 0 || H > ((int64_t)1 << 30) || M > ((int64_t)1 << 60) / H) return NQ_EINVAL;
-  if (!y || !q || (!mx && !scale) || ((nv || mx) && !block_scale)) return NQ_EINVAL;
-  if (nv && H % kBlock != 0) return NQ_EUNSUPPORTED;
-  if (mx && H % kMxBlock != 0) return NQ_EUNSUPPORTED;
-  if ((uintptr_t)y % 2 != 0 || (!mx && (uintptr_t)scale % 4 != 0)) return NQ_EINVAL;
-  const size_t act = (size_t)M * (size_t)H * 2;
-  const size_t qbytes = nv ? (size_t)M * (size_t)(H / 2) : (size_t)M * (size_t)H;
-  const size_t bsbytes = nv ? block_scale_bytes(M, H) : mx ? (size_t)M * (size_t)(H / kMxBlock) : 0;
-  const void *ss = mx ? nullptr : (const void *)scale;
-  const void *bb = (nv || mx) ? block_scale : nullptr;
-  if (overlaps(y, act, q, qbytes) || overlaps(y, act, bb, bsbytes) || overlaps(q, qbytes, bb, bsbytes) ||
-      overlaps(ss, 4, q, qbytes) || overlaps(ss, 4, bb, bsbytes))
-    return NQ_EINVAL;
-  if (M == 0) return NQ_OK;
   QuantArgs a{y, mx ? nullptr : scale, M, H, q, (nv || mx) ? block_scale : nullptr,
               (hipStream_t)stream};
   const bool bf = dtype == NQ_BF16;
@@ -216,25 +150,8 @@ nq_status nq_quant_mxfp8(const void *y, int64_t M, int64_t H, int dtype, void *q
 static nq_status gemm_common(bool mx, const void *a, const void *sa, const float *a_scale,
                              const void *b, const void *sb, const float *b_scale, int64_t M,
                              int64_t N, int64_t K, void *out, void *stream) {
-  if (M < 0 || N < 0 || K <= 0 || M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30) ||
-      K > ((int64_t)1 << 24))
-    return NQ_EINVAL;
-  if (!a || !b || !out) return NQ_EINVAL;
-  if (mx ? (!sa || !sb) : (!a_scale || !b_scale)) return NQ_EINVAL;
-  if (K % kMxBlock != 0) return NQ_EUNSUPPORTED;
-  if (((uintptr_t)a | (uintptr_t)b) % 16 != 0 || (uintptr_t)out % 2 != 0) return NQ_EINVAL;
-  if (!mx && ((uintptr_t)a_scale | (uintptr_t)b_scale) % 4 != 0) return NQ_EINVAL;
-  // one workgroup per 256 x 256 output tile: the count must fit a grid
-  if (((M + 255) / 256) * ((N + 255) / 256) > (int64_t)INT32_MAX) return NQ_EINVAL;
-  const size_t obytes = (size_t)M * (size_t)N * 2;
-  const size_t abytes = (size_t)M * (size_t)K, bbytes = (size_t)N * (size_t)K;
-  const size_t sab = mx ? (size_t)M * (size_t)(K / kMxBlock) : 4;
-  const size_t sbb = mx ? (size_t)N * (size_t)(K / kMxBlock) : 4;
-  const void *sap = mx ? sa : (const void *)a_scale, *sbp = mx ? sb : (const void *)b_scale;
-  if (overlaps(out, obytes, a, abytes) || overlaps(out, obytes, b, bbytes) ||
-      overlaps(out, obytes, sap, sab) || overlaps(out, obytes, sbp, sbb))
-    return NQ_EINVAL;
-  if (M == 0 || N == 0) return NQ_OK;
+  const nq_status v = check_gemm_fp8(mx, a, sa, a_scale, b, sb, b_scale, M, N, K, out);
+  if (v != NQ_OK || M == 0 || N == 0) return v;
   return status_of(gemm_fp8(mx, a, mx ? sa : nullptr, b, mx ? sb : nullptr, mx ? nullptr : a_scale,
                             mx ? nullptr : b_scale, M, N, K, out, (hipStream_t)stream));
 }
@@ -253,34 +170,33 @@ nq_status nq_gemm_fp8_static(const void *a, const float *a_scale, const void *b,
 nq_status nq_gemm_nvfp4(const void *a, const void *a_scales, const float *a_gs, const void *b,
                         const void *b_scales, const float *b_gs, int64_t M, int64_t N, int64_t K, void *out,
                         void *stream) {
-  if (M < 0 || N < 0 || K <= 0 || M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30) ||
-      K > ((int64_t)1 << 24))
-    return NQ_EINVAL;
-  if (!a || !b || !a_scales || !b_scales || !a_gs || !b_gs || !out) return NQ_EINVAL;
-  if (K % 64 != 0) return NQ_EUNSUPPORTED;
-  if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)a_scales | (uintptr_t)b_scales) % 16 != 0 ||
-      (uintptr_t)out % 2 != 0 || ((uintptr_t)a_gs | (uintptr_t)b_gs) % 4 != 0)
-    return NQ_EINVAL;
-  // one workgroup per 32 x 32 (or larger) output tile: the count must fit a grid
-  if (((M + 31) / 32) * ((N + 31) / 32) > (int64_t)INT32_MAX) return NQ_EINVAL;
-  const size_t obytes = (size_t)M * (size_t)N * 2;
-  if (overlaps(out, obytes, a, (size_t)M * (size_t)(K / 2)) || overlaps(out, obytes, b, (size_t)N * (size_t)(K / 2)) ||
-      overlaps(out, obytes, a_scales, block_scale_bytes(M, K)) ||
-      overlaps(out, obytes, b_scales, block_scale_bytes(N, K)) || overlaps(out, obytes, a_gs, 4) ||
-      overlaps(out, obytes, b_gs, 4))
-    return NQ_EINVAL;
-  if (M == 0 || N == 0) return NQ_OK;
+  const nq_status v = check_gemm_nvfp4(a, a_scales, a_gs, b, b_scales, b_gs, M, N, K, out);
+  if (v != NQ_OK || M == 0 || N == 0) return v;
   return status_of(gemm_nvfp4(a, a_scales, a_gs, b, b_scales, b_gs, M, N, K, out, (hipStream_t)stream));
+}
+
+nq_status nq_traffic_probe(const void *const *src, const int64_t *src_row_bytes, int nsrc,
+                           void *const *dst, const int64_t *dst_row_bytes, int ndst, int64_t rows,
+                           int threads, int grid, int prefetch, void *stream) {
+  const nq_status v = check_traffic(src, src_row_bytes, nsrc, dst, dst_row_bytes, ndst, rows, threads, grid);
+  if (v != NQ_OK || rows == 0) return v;
+  TrafficStreams t{};
+  t.ndst = ndst;
+  for (int i = 0; i < nsrc; ++i) {
+    t.src[i] = src[i];
+    t.src_chunks[i] = (unsigned)(src_row_bytes[i] / 16);
+  }
+  for (int i = 0; i < ndst; ++i) {
+    t.dst[i] = dst[i];
+    t.dst_chunks[i] = (unsigned)(dst_row_bytes[i] / 16);
+  }
+  return status_of(traffic_probe(t, nsrc, rows, threads, grid, prefetch != 0, (hipStream_t)stream));
 }
 
 nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,
                            void *stream) {
-  if (kind < 0 || kind > 9 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in)))
-    return NQ_EINVAL;
-  // kind 8 takes an E8M0 code the kernels can produce (0..247) as param.
-  if (kind == 8 && !(param >= 0.0f && param <= 247.0f && param == (float)(int)param))
-    return NQ_EINVAL;
-  if (n == 0) return NQ_OK;
+  const nq_status v = check_convert_probe(kind, in, n, param, out);
+  if (v != NQ_OK || n == 0) return v;
   const int threads = 256;
   const int64_t blocks = (n + threads - 1) / threads;
   return status_of(launch(convert_probe, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,

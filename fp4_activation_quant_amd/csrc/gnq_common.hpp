@@ -18,6 +18,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gnq_consts.hpp"
 #include "gnq_launch.hpp"
 
 namespace gnq {
@@ -28,11 +29,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kVec = 8;           // elements per thread chunk (16 bytes)
-constexpr int kBlock = 16;        // elements per NVFP4 block scale
-constexpr int kMxBlock = 32;      // elements per MXFP8 (E8M0) block scale
-constexpr int kWave = 64;
-constexpr int kMaxThreads = 1024;
 constexpr float kE4M3Max = 448.0f;
 constexpr float kE2M1Max = 6.0f;
 

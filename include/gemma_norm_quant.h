@@ -237,7 +237,8 @@ nq_status nq_gemm_nvfp4(const void *a, const void *a_scales, const float *a_gs, 
 
 /* Size in bytes of the NVFP4 block-scale buffer:
  * round_up(M, 128) * round_up(H / 16, 4) (the wrapper's allocation on the
- * `fused_norm_quant` page).  0 for M <= 0 or H < 16. */
+ * `fused_norm_quant` page).  0 for M <= 0, H < 16, or sizes the entry points
+ * reject (H > 2^30 or M * H > 2^60). */
 size_t nq_block_scale_bytes(int64_t M, int64_t H);
 
 /* Static description of a status code; never NULL. */
@@ -276,6 +277,34 @@ int nq_abi_version(void);
  */
 nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,
                            void *stream);
+
+/*
+ * nq_traffic_probe -- diagnostic: a kernel with the op's access structure
+ * and none of its arithmetic, to measure the bandwidth a launch that moves
+ * the op's bytes can reach (the practical ceiling the op's figures are
+ * compared with).  Per row, every thread loads its 16-byte chunks (index
+ * thread, thread + threads, ...) of each read stream with non-temporal
+ * loads, folds them into one value and stores that value to its chunks of
+ * each write stream with non-temporal stores.
+ *
+ *   src, src_row_bytes, nsrc   host arrays: 1 or 2 device read streams of
+ *                              rows * src_row_bytes[i] bytes;
+ *   dst, dst_row_bytes, ndst   host arrays: 0..4 device write streams of
+ *                              rows * dst_row_bytes[i] bytes;
+ *   rows                       >= 0 (0: NQ_OK, nothing launched);
+ *   threads                    workgroup size, a multiple of 64 in [64, 1024];
+ *   grid                       0: one workgroup per row; else that many
+ *                              workgroups taking rows round-robin;
+ *   prefetch                   nonzero: issue the next row's loads before
+ *                              the current row's stores.
+ * Row bytes must be positive multiples of 16 (a read row at most
+ * 64 * threads bytes), pointers 16-byte aligned, and no write stream may
+ * overlap another stream (NQ_EINVAL otherwise).  The written bytes are
+ * meaningless.
+ */
+nq_status nq_traffic_probe(const void *const *src, const int64_t *src_row_bytes, int nsrc,
+                           void *const *dst, const int64_t *dst_row_bytes, int ndst, int64_t rows,
+                           int threads, int grid, int prefetch, void *stream);
 
 #ifdef __cplusplus
 }

@@ -271,3 +271,38 @@ def test_gemm_nvfp4_validation(over, want):
     a.update(over)
     assert _lib.nq_gemm_nvfp4(a["a"], a["sa"], a["ga"], a["b"], a["sb"], a["gb"], a["M"], a["N"], a["K"],
                               a["out"], 0) == want
+
+
+SA, SB, DA, DB = (0x30000000 + i * 0x1000000 for i in range(4))
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(), None),                                         # valid: only M = 0 returns before a launch
+    (dict(src=[]), _lib.NQ_EINVAL),                         # 1 or 2 read streams
+    (dict(src=[SA, SB, SA + 0x100000], srb=[1024] * 3), _lib.NQ_EINVAL),
+    (dict(dst=[DA] * 5, drb=[64] * 5), _lib.NQ_EINVAL),     # at most 4 write streams
+    (dict(srb=[1000]), _lib.NQ_EINVAL),                     # row bytes a multiple of 16
+    (dict(drb=[0]), _lib.NQ_EINVAL),
+    (dict(srb=[64 * 256 + 16]), _lib.NQ_EINVAL),            # a read row beyond 4 chunks per thread
+    (dict(threads=96), _lib.NQ_EINVAL),
+    (dict(threads=2048), _lib.NQ_EINVAL),
+    (dict(grid=-1), _lib.NQ_EINVAL),
+    (dict(src=[SA + 8]), _lib.NQ_EINVAL),                   # 16-byte alignment
+    (dict(dst=[0]), _lib.NQ_EINVAL),
+    (dict(dst=[SA + 512], rows=8), _lib.NQ_EINVAL),         # a write stream over a read stream
+    (dict(dst=[DA, DA + 256], drb=[64, 64], rows=8), _lib.NQ_EINVAL),   # write streams overlapping
+    (dict(rows=-1), _lib.NQ_EINVAL),
+])
+def test_traffic_probe_validation(over, want):
+    a = dict(src=[SA], srb=[1024], dst=[DA], drb=[512], rows=0, threads=256, grid=0, pf=0)
+    a.update(over)
+    if want is None:
+        want = _lib.NQ_OK
+    assert _lib.nq_traffic_probe(a["src"], a["srb"], a["dst"], a["drb"], a["rows"], a["threads"],
+                                 a["grid"], a["pf"], 0) == want
+
+
+def test_traffic_probe_nonzero_rows_still_validated():
+    # rows > 0 with a bad stream is rejected before any launch
+    assert _lib.nq_traffic_probe([SA], [1000], [DA], [512], 8, 256, 0, 0, 0) == _lib.NQ_EINVAL
+    assert _lib.nq_traffic_probe([SA], [1024], [SA], [512], 8, 256, 0, 0, 0) == _lib.NQ_EINVAL
