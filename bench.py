@@ -247,25 +247,56 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA
 def _time_graph(launch, steps, warmup, stream):
     """Warm up, capture `steps` launches in one HIP graph, replay once;
     returns (wall seconds, kernel ms per launch from events on `stream`)."""
+    t = _time_graphs(launch, steps, warmup, stream)
+    return t["wall_s"], t["span_ms"]
+
+
+def _time_graphs(launch, steps, warmup, stream, differenced=False):
+    """Warm up, capture `steps` launches (launch(warmup + i)) in one HIP graph
+    and, if `differenced`, `2 * steps` launches in a second one; replay each
+    once untimed, then once between HIP events recorded on `stream` (the
+    launch stream).  Returns a dict:
+
+      wall_s    host wall time of the timed replay of `steps` launches
+                (synchronised on both sides);
+      span_ms   event span of that replay / steps;
+      diff_ms   (span of the 2 * steps replay - span of the steps replay)
+                / steps: the per-launch time with the replay's fixed start
+                cost (a few hundred us) cancelled, which is what sets the
+                figure for launches of a few us.
+    """
     import torch
     with torch.cuda.stream(stream):
         for i in range(warmup):
             launch(i)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(steps):
-            launch(warmup + i)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
+    graphs = []
+    for n in ((steps, 2 * steps) if differenced else (steps,)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                launch(warmup + i)
         g.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    return time.perf_counter() - t0, e0.elapsed_time(e1) / steps
+        torch.cuda.synchronize()
+        graphs.append(g)
+    spans = []
+    wall = 0.0
+    for k, g in enumerate(graphs):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        if k == 0:
+            wall = time.perf_counter() - t0
+        spans.append(e0.elapsed_time(e1))
+    out = {"wall_s": wall, "span_ms": spans[0] / steps}
+    if differenced:
+        out["diff_ms"] = (spans[1] - spans[0]) / steps
+    return out
 
 
 def gemm_cpu_baseline(gw, a, sa, b, sb, budget_s):
@@ -499,6 +530,79 @@ def chain_main(args):
     print(json.dumps(line), flush=True)
 
 
+def block_threads(H):
+    """The fused kernel's workgroup size for rows of H elements (its launch
+    rule: chunks per thread, rounded up to whole waves)."""
+    nchunk = H // 8
+    cpt = chunks_per_thread(H)
+    return -(-(-(-nchunk // cpt)) // 64) * 64
+
+
+def traffic_streams(wl):
+    """Per-row bytes of the op's read and write streams for a workload: reads
+    x (and the residual); writes the residual, y, the codes and the scale
+    bytes (row-major here: the probe measures bytes, not the tiled layout)."""
+    H = wl.H
+    src = [2 * H] + ([2 * H] if wl.has_residual else [])
+    dst = ([2 * H] if wl.has_residual else []) + ([2 * H] if wl.write_y else [])
+    dst += {"fp8": [H], "nvfp4": [H // 2, H // 16], "mxfp8": [H, H // 32]}[wl.mode]
+    return src, dst
+
+
+def ceiling_main(args):
+    """The traffic probe (the op's access structure and byte mix, no
+    arithmetic) for each named workload, in several launch forms, timed like
+    the op: graph replay, buffer sets rotated through >= 2 GiB, per-launch
+    time from the difference of a K- and a 2K-launch replay.  One JSON line
+    per workload with every form and the best (the practical ceiling the
+    op's figure is compared with)."""
+    import torch
+    from fp4_activation_quant_amd import _lib
+    from fp4_activation_quant_amd.workloads import WORKLOADS
+    _lib.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    names = list(WORKLOADS) if args.ceiling == "all" else args.ceiling.split(",")
+    for name in names:
+        wl = WORKLOADS[name]
+        src_rb, dst_rb = traffic_streams(wl)
+        if any(b % 16 for b in src_rb + dst_rb):
+            print(json.dumps({"ceiling": name, "skipped": "row bytes not a multiple of 16"}), flush=True)
+            continue
+        M = wl.M
+        per_launch = M * (sum(src_rb) + sum(dst_rb))
+        n_sets = max(1, min(64, -(-ROTATE_BYTES // per_launch)))
+        sets = [([torch.ones(M * b // 4, dtype=torch.int32, device=dev) for b in src_rb],
+                 [torch.empty(M * b // 4, dtype=torch.int32, device=dev) for b in dst_rb])
+                for _ in range(n_sets)]
+        op_threads = block_threads(wl.H)
+        forms = [(op_threads, 0, 0)]
+        forms += [(op_threads, g, 1) for g in (256, 512, 768, 1024, 1536, 2048) if g < M]
+        forms += [(t, 0, 0) for t in (256, 512, 1024) if t != op_threads and 2 * wl.H <= 64 * t]
+        stream = torch.cuda.Stream(device=dev)
+        results = []
+        for threads, grid, pf in forms:
+            def launch(i, threads=threads, grid=grid, pf=pf):
+                srcs, dsts = sets[i % n_sets]
+                st = _lib.nq_traffic_probe([t.data_ptr() for t in srcs], src_rb, [t.data_ptr() for t in dsts],
+                                           dst_rb, M, threads, grid, pf, stream.cuda_stream)
+                if st != _lib.NQ_OK:
+                    raise RuntimeError(f"nq_traffic_probe: status {st}")
+            t = _time_graphs(launch, args.steps, args.warmup, stream, differenced=True)
+            us = t["diff_ms"] * 1e3
+            results.append({"threads": threads, "grid": grid, "prefetch": pf, "us": round(us, 3),
+                            "GBps": round(per_launch / (us * 1e-6) / 1e9, 1),
+                            "span_us": round(t["span_ms"] * 1e3, 3)})
+        best = max(results, key=lambda r: r["GBps"])
+        print(json.dumps({"ceiling": name, "bytes_per_launch": per_launch, "rows": M,
+                          "src_row_bytes": src_rb, "dst_row_bytes": dst_rb, "buffer_sets": n_sets,
+                          "steps": args.steps, "best_GBps": best["GBps"],
+                          "best_frac_of_peak": round(best["GBps"] / HBM_PEAK_GBS, 4), "forms": results}),
+              flush=True)
+        del sets
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -527,6 +631,9 @@ def main():
     ap.add_argument("--write-y", action="store_true",
                     help="also write y for a workload whose default is write_y=False (the "
                          "decode sweep with the normed output, 9H bytes per row)")
+    ap.add_argument("--ceiling", default=None, metavar="WORKLOADS",
+                    help="time the traffic probe (the op's byte mix and access structure, no "
+                         "arithmetic) for these workloads (comma-separated, or 'all') instead of the op")
     ap.add_argument("--overlap", type=int, default=1, metavar="CHUNKS",
                     help="with --chain: also time the fused op and the GEMM on row chunks, the op "
                          "of chunk j + 1 on a second stream beside the GEMM of chunk j")
@@ -546,6 +653,8 @@ def main():
         return gemm_main(args)
     if args.chain:
         return chain_main(args)
+    if args.ceiling:
+        return ceiling_main(args)
     _lib.lib()
     wl = WORKLOADS[args.workload or DEFAULT_BENCH]
     if args.write_y and not wl.write_y:
@@ -609,33 +718,23 @@ def main():
         ops.gemma_add_rms_norm_quant_out(xi, st["r"], wd, wl.eps, sd, wl.nvfp4, st["q"], st["bs"],
                                          st["y"])
 
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            launch(i)
-    torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps, {n_sets} buffer sets); timing {args.steps} steps"
-          f" ({'graph' if (not args.eager) else 'eager'})", file=sys.stderr, flush=True)
-
+    print(f"# timing {args.steps} steps after {args.warmup} warm-up steps ({n_sets} buffer sets, "
+          f"{'graph' if (not args.eager) else 'eager'})", file=sys.stderr, flush=True)
     if not args.eager:
         # The K launches captured once as a HIP graph and replayed: launch
-        # overhead off the critical path.  Kernel time = event span / K.
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(args.steps):
-                launch(args.warmup + i)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        kern_ms = [e0.elapsed_time(e1) / args.steps]
+        # overhead off the critical path.  Kernel time per launch = (span of
+        # a 2K-launch replay - span of the K-launch replay) / K, which cancels
+        # the replay's fixed start cost; the K-launch replay is the timed
+        # region of `value`.
+        t = _time_graphs(launch, args.steps, args.warmup, stream, differenced=True)
+        wall = t["wall_s"]
+        kern_ms = [t["diff_ms"]]
+        span_ms = t["span_ms"]
     else:
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                launch(i)
+        torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -648,6 +747,7 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         kern_ms = [a.elapsed_time(b) for a, b in ev]
+        span_ms = None
     kern_ms.sort()
     avg_ms = sum(kern_ms) / len(kern_ms)
     med_ms = kern_ms[len(kern_ms) // 2]
@@ -678,8 +778,11 @@ def main():
         "launch": "graph" if (not args.eager) else "eager",
         "path": "unfused (2 kernels)" if args.unfused else "fused",
         "buffer_sets": n_sets,
-        "kernel_ms": {"avg": round(avg_ms, 5), "median": round(med_ms, 5),
-                      "min": round(kern_ms[0], 5), "max": round(kern_ms[-1], 5)},
+        "kernel_ms": ({"avg": round(avg_ms, 5), "span_per_launch": round(span_ms, 5),
+                       "method": "(span of 2K launches - span of K launches) / K, graph replays"}
+                      if span_ms is not None else
+                      {"avg": round(avg_ms, 5), "median": round(med_ms, 5), "min": round(kern_ms[0], 5),
+                       "max": round(kern_ms[-1], 5), "method": "event pair per eager launch"}),
         "roofline": {"bound": "hbm", "kernel": kernel_name(wl), "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

@@ -90,6 +90,15 @@ WORKLOADS = {w.name: w for w in [
     _wl(name="nvfp4_m32768_h8192_bf16_y", M=32768, H=8192, dtype="bf16", mode="nvfp4",
         has_residual=True, write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1),
         seed_base=5000, scale_rule="nvfp4_amax"),
+    # Static FP8 at the prefill and the largest shape (bf16, residual, y
+    # written): the FP8 mode at sizes where bandwidth, not launch latency,
+    # sets the time.
+    _wl(name="fp8_prefill_m8192_h4096_bf16_y", M=8192, H=4096, dtype="bf16", mode="fp8",
+        has_residual=True, write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1),
+        seed_base=3100, scale_rule="fp8_amax"),
+    _wl(name="fp8_m32768_h8192_bf16_y", M=32768, H=8192, dtype="bf16", mode="fp8",
+        has_residual=True, write_y=True, eps=1e-6, x_std=1.0, r_std=1.0, w_dist=("normal", 0.1),
+        seed_base=5100, scale_rule="fp8_amax"),
     # MXFP8 output (scales from the data, no scale argument) at the prefill
     # and the largest shape.
     _wl(name="mxfp8_prefill_m8192_h4096_bf16_y", M=8192, H=4096, dtype="bf16", mode="mxfp8",
