@@ -115,10 +115,23 @@ __device__ __forceinline__ float div_by_scale(float y, float s, float r) {
   return __builtin_fmaf(-__builtin_fmaf(q, s, -y), r, q);
 }
 
+// fl32(a / 6), correctly rounded, for a block amax a >= 0: the reciprocal
+// r = fl32(1/6) and two remainder corrections, as in div_by_scale (q0 within
+// 1.5 ulp, the first correction within 1 ulp, the second exact; the
+// remainder a - 6q is exact).  5 VALU instructions instead of the ~10 of
+// an IEEE division; the probe tests compare the block-scale code over every
+// 16-bit amax (the only values a block of rounded y can have) and over
+// tie-heavy fp32 patterns against the oracle's division.
+__device__ __forceinline__ float div6(float a) {
+  const float r = 1.0f / kE2M1Max;
+  float q = a * r;
+  q = __builtin_fmaf(-__builtin_fmaf(q, kE2M1Max, -a), r, q);
+  return __builtin_fmaf(-__builtin_fmaf(q, kE2M1Max, -a), r, q);
+}
+
 // NVFP4 block scale: S = E4M3(min(gs * (amax / 6), 448)).
 __device__ __forceinline__ uint32_t nvfp4_scale_code(float amax, float gs) {
-  const float t = amax / kE2M1Max;
-  const float u = fminf(gs * t, kE4M3Max);
+  const float u = fminf(gs * div6(amax), kE4M3Max);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false) & 0xffu;
 }
 
@@ -126,6 +139,27 @@ __device__ __forceinline__ uint32_t nvfp4_scale_code(float amax, float gs) {
 __device__ __forceinline__ float nvfp4_elem_scale(uint32_t s_code, float gs) {
   const float sigma = __builtin_amdgcn_cvt_f32_fp8((int)s_code, 0);
   return sigma == 0.0f ? 0.0f : gs / sigma;
+}
+
+// The element multiplier of every E4M3 code a block scale can take (0 ..
+// 0x7F), filled once per workgroup into LDS by its threads (visible to all
+// after the next barrier): a block then looks o up instead of dividing.
+constexpr int kNvfp4Codes = 128;
+__device__ __forceinline__ void nvfp4_fill_table(float *tab, float gs, unsigned tid, unsigned nthr) {
+  for (unsigned i = tid; i < (unsigned)kNvfp4Codes; i += nthr) tab[i] = nvfp4_elem_scale(i, gs);
+}
+
+// rstd = 1 / sqrt(sum(h^2) / H + eps) in fp32 from the row's sum of squares
+// and inv_h = 1 / H: a multiply, an add and the hardware reciprocal square
+// root (1 ulp), a few fp32 ulps from the exact value like any fp32
+// evaluation order, far inside the one unit of the 16-bit output the
+// result is rounded to.  Arguments below 2^-100 (eps = 0 and tiny rows) are
+// scaled by 2^64 first so the instruction never sees a subnormal.
+__device__ __forceinline__ float row_rstd(float sum_sq, float inv_h, float eps) {
+  const float v = __builtin_fmaf(sum_sq, inv_h, eps);
+  const bool tiny = v < 0x1p-100f;
+  const float r = __builtin_amdgcn_rsqf(tiny ? v * 0x1p64f : v);
+  return tiny ? r * 0x1p32f : r;
 }
 
 // MXFP8 block scale: 2^e with e = floor(log2(amax)) - 8 (8 is the exponent
@@ -211,9 +245,14 @@ __device__ __forceinline__ float group_sum(float v) {
 // every zero y the sign of h * rstd * (1 + w): fl(1 + w) is +0 for w = -1,
 // and t keeps the sign of h.
 template <bool GEMMA>
+__device__ __forceinline__ float norm_factor(float w) {
+  if constexpr (GEMMA) return 1.0f + w;
+  return w;
+}
+
+template <bool GEMMA>
 __device__ __forceinline__ float norm_scale(float t, float w) {
-  if constexpr (GEMMA) return t * (1.0f + w);
-  return t * w;
+  return t * norm_factor<GEMMA>(w);
 }
 
 // Quantize one 8-element chunk of y (already rounded to the activation dtype)
@@ -223,17 +262,22 @@ __device__ __forceinline__ float norm_scale(float t, float w) {
 // other half of the 16-element block and to run this too; MXFP8 likewise
 // needs the aligned quad of lanes (4 x 8 = 32 elements) to hold chunks
 // 4k..4k+3 and all run it.
-template <int MODE>
+// TABLE: NVFP4 looks the element multiplier up in otab, the workgroup's
+// table (nvfp4_fill_table), instead of dividing.
+template <int MODE, bool TABLE = false>
 __device__ __forceinline__ void quant_store_chunk(const float (&yv)[kVec], float s, float r_s,
                                                   uint8_t *__restrict__ q, uint8_t *__restrict__ bs,
-                                                  int64_t row, unsigned ch, int nchunk, int ktiles) {
+                                                  int64_t row, unsigned ch, int nchunk, int ktiles,
+                                                  const float *otab = nullptr) {
   if constexpr (MODE == kModeNvfp4) {
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < kVec; ++k) amax = fmaxf(amax, fabsf(yv[k]));
     amax = fmaxf(amax, dpp_swap_adjacent(amax));
     const uint32_t sc = nvfp4_scale_code(amax, s);
-    const float o = nvfp4_elem_scale(sc, s);
+    float o;
+    if constexpr (TABLE) o = otab[sc & (kNvfp4Codes - 1)];
+    else o = nvfp4_elem_scale(sc, s);
     float v[kVec];
 #pragma unroll
     for (int k = 0; k < kVec; ++k) v[k] = yv[k] * o;

@@ -44,11 +44,12 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
            const float *__restrict__ scale_ptr, float eps, int64_t M, int nchunk,
            uint8_t *__restrict__ q, uint8_t *__restrict__ bs, u32x4 *__restrict__ y, int ktiles) {
   __shared__ float partial[2][kMaxThreads / kWave];
+  __shared__ float otab[MODE == kModeNvfp4 ? kNvfp4Codes : 1];
   const unsigned tid = threadIdx.x;
   const unsigned nthr = blockDim.x;
   const unsigned nch = (unsigned)nchunk;
   const int nwaves = nthr / kWave;
-  const float Hf = (float)(nchunk * kVec);
+  const float inv_h = __builtin_amdgcn_rcpf((float)(nchunk * kVec));
   // The row loads: x and residual stream from HBM (non-temporal).
   u32x4 xa[CPT], ra[CPT], wa[CPT];
   auto load_row = [&](int64_t b) {
@@ -74,6 +75,20 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
   }
   const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
   const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+  // NVFP4: the multiplier table, read after the first row's barrier.
+  if constexpr (MODE == kModeNvfp4) nvfp4_fill_table(otab, s, tid, nthr);
+  // The looping launch keeps the norm's per-element factor fl(1 + w) (or w)
+  // in registers across its rows.
+  float g[PF ? CPT : 1][PF ? kVec : 1];
+  if constexpr (PF) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        g[c][2 * k] = norm_factor<GEMMA>(D::lo(wa[c][k]));
+        g[c][2 * k + 1] = norm_factor<GEMMA>(D::hi(wa[c][k]));
+      }
+  }
   int parity = 0;
   for (; blk < M; blk += gridDim.x, parity ^= 1) {
     const int64_t row = MODE == kModeNvfp4 ? nvfp4_row_of_block(blk, M) : blk;
@@ -114,7 +129,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
     __syncthreads();
     float tot = 0.0f;
     for (int i = 0; i < nwaves; ++i) tot += partial[parity][i];
-    const float rstd = 1.0f / __builtin_sqrtf(tot / Hf + eps);
+    const float rstd = row_rstd(tot, inv_h, eps);
 
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -127,7 +142,10 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float ta = D::lo(hb[c][k]) * rstd, tb = D::hi(hb[c][k]) * rstd;
-          yb[k] = D::pack(norm_scale<GEMMA>(ta, D::lo(wa[c][k])), norm_scale<GEMMA>(tb, D::hi(wa[c][k])));
+          if constexpr (PF)
+            yb[k] = D::pack(ta * g[c][2 * k], tb * g[c][2 * k + 1]);
+          else
+            yb[k] = D::pack(norm_scale<GEMMA>(ta, D::lo(wa[c][k])), norm_scale<GEMMA>(tb, D::hi(wa[c][k])));
           yv[2 * k] = D::lo(yb[k]);
           yv[2 * k + 1] = D::hi(yb[k]);
         }
@@ -135,7 +153,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
           const u32x4 o = {yb[0], yb[1], yb[2], yb[3]};
           __builtin_nontemporal_store(o, &yr[ch]);
         }
-        quant_store_chunk<MODE>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles);
+        quant_store_chunk<MODE, MODE == kModeNvfp4>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles, otab);
       }
     }
     if constexpr (!PF)
@@ -188,7 +206,7 @@ fused_rows_small(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32
     ss = __builtin_fmaf(b, b, ss);
   }
   ss = group_sum<LPR>(ss);
-  const float rstd = 1.0f / __builtin_sqrtf(ss / (float)(nchunk * kVec) + eps);
+  const float rstd = row_rstd(ss, __builtin_amdgcn_rcpf((float)(nchunk * kVec)), eps);
   float yv[kVec];
   uint32_t yb[4];
 #pragma unroll
@@ -240,7 +258,7 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
     __syncthreads();
     float tot = 0.0f;
     for (int i = 0; i < nwaves; ++i) tot += partial[parity][i];
-    const float rstd = 1.0f / __builtin_sqrtf(tot / (float)H + eps);
+    const float rstd = row_rstd(tot, __builtin_amdgcn_rcpf((float)H), eps);
     // After the barrier every thread may read h written by the others.
     const uint16_t *hsrc = HAS_RES ? res : x;
     if constexpr (MODE == kModeNvfp4) {

@@ -16,6 +16,12 @@ quant_rows(const u32x4 *__restrict__ y, const float *__restrict__ scale_ptr, int
   const unsigned tid = threadIdx.x;
   const unsigned nthr = blockDim.x;
   const unsigned nch = (unsigned)nchunk;
+  // NVFP4: the fused kernel's multiplier table (same values as dividing).
+  __shared__ float otab[MODE == kModeNvfp4 ? kNvfp4Codes : 1];
+  if constexpr (MODE == kModeNvfp4) {
+    nvfp4_fill_table(otab, *scale_ptr, tid, nthr);
+    __syncthreads();
+  }
   for (int64_t blk = blockIdx.x; blk < M; blk += gridDim.x) {
     const int64_t row = MODE == kModeNvfp4 ? nvfp4_row_of_block(blk, M) : blk;
     const u32x4 *__restrict__ yr = y + (size_t)row * (size_t)nchunk;
@@ -37,7 +43,7 @@ quant_rows(const u32x4 *__restrict__ y, const float *__restrict__ scale_ptr, int
           yv[2 * k] = D::lo(ya[c][k]);
           yv[2 * k + 1] = D::hi(ya[c][k]);
         }
-        quant_store_chunk<MODE>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles);
+        quant_store_chunk<MODE, MODE == kModeNvfp4>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles, otab);
       }
     }
   }

@@ -108,6 +108,20 @@ def test_nvfp4_block_scale_step(gs):
     assert n == 0, ex
 
 
+@pytest.mark.parametrize("gs", GLOBAL_SCALES + [2.0 ** 100, 3.0e-30])
+@pytest.mark.parametrize("fmt", [O.BF16, O.FP16])
+def test_nvfp4_block_scale_every_16bit_amax(gs, fmt):
+    """Every non-negative finite bf16 / fp16 value as the block amax (the
+    values a block of rounded y can have), against the oracle's step."""
+    codes = np.arange(1 << 15, dtype=np.uint32)
+    a = O.decode(codes, fmt)
+    a = a[np.isfinite(a)].astype(np.float32)
+    got = probe(6, a.view(np.uint32), gs)
+    want = O.nvfp4_block_scale_codes(a, gs)
+    n, ex = _mismatch(got, want, a)
+    assert n == 0, ex
+
+
 @pytest.mark.parametrize("gs", GLOBAL_SCALES)
 def test_nvfp4_element_step_every_bf16_y(gs):
     """The kernel's element code against the oracle's step: every finite bf16
