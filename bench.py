@@ -530,6 +530,56 @@ def chain_main(args):
     print(json.dumps(line), flush=True)
 
 
+def decode_main(args):
+    """A decode step at H = N = 4096 (the decode sweep's rows; an FP8
+    weight of random finite codes): the op (static FP8) and its consumer
+    linear as one fused launch against the two launches (the op, then the
+    decode GEMM), per row count.  Weights rotate through >= 2 GiB, so each
+    step fetches its weight from HBM as a layer of a real decode step does.
+    One JSON line per M: us per step (graph replay, differenced)."""
+    import numpy as np
+    import torch
+    from fp4_activation_quant_amd import _lib, ops
+    from fp4_activation_quant_amd.workloads import WORKLOADS, make_inputs, load_scale
+    _lib.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS["fp8_decode_m256_h4096_bf16"]
+    x, r, w = make_inputs(wl)
+    H = N = wl.H
+    s = torch.tensor([load_scale(wl)], dtype=torch.float32, device=dev)
+    bs = torch.tensor([0.004], dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(9700)
+    b0 = (rng.integers(0, 8, size=(N, H)) | (rng.integers(0, 8, size=(N, H)) << 3)
+          | (rng.integers(0, 2, size=(N, H)) << 7)).astype(np.uint8)
+    n_sets = max(1, ROTATE_BYTES // (N * H))
+    bsets = [torch.from_numpy(b0).to(dev) for _ in range(n_sets)]
+    wd = w.to(dev)
+    for M in [int(v) for v in args.decode.split(",")]:
+        xs = [x[:M].to(dev), (-x[:M]).to(dev)]
+        rd = r[:M].to(dev)
+        rout = torch.empty_like(rd)
+        q = torch.empty((M, H), dtype=torch.uint8, device=dev)
+        qf = q.view(torch.float8_e4m3fn)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        res = {}
+        for path in ("fused", "two_launches"):
+            def launch(i, path=path):
+                xi, b = xs[(i // n_sets) & 1], bsets[i % n_sets]
+                if path == "fused":
+                    ops.gemma_add_rms_norm_quant_gemm_fp8_out(xi, rd, rout, wd, wl.eps, s, b, bs, q, None, out)
+                else:
+                    ops.gemma_add_rms_norm_quant_out(xi, rout, wd, wl.eps, s, False, qf, None, None)
+                    ops.gemm_fp8_static(q, s, b, bs, out=out)
+            stream = torch.cuda.Stream(device=dev)
+            t = _time_graphs(launch, args.steps, args.warmup, stream, differenced=True)
+            res[path] = t["diff_ms"] * 1e3
+        print(json.dumps({"metric": "decode step: add + Gemma RMSNorm + FP8 quant + FP8 linear, us per step",
+                          "M": M, "H": H, "N": N, "weight_sets": n_sets, "steps": args.steps,
+                          "fused_us": round(res["fused"], 3), "two_launches_us": round(res["two_launches"], 3),
+                          "speedup": round(res["two_launches"] / res["fused"], 3)}), flush=True)
+
+
 def block_threads(H):
     """The fused kernel's workgroup size for rows of H elements (its launch
     rule: chunks per thread, rounded up to whole waves)."""
@@ -631,6 +681,9 @@ def main():
     ap.add_argument("--write-y", action="store_true",
                     help="also write y for a workload whose default is write_y=False (the "
                          "decode sweep with the normed output, 9H bytes per row)")
+    ap.add_argument("--decode", default=None, metavar="ROWS",
+                    help="time the fused decode step (op + FP8 linear in one launch) against the two "
+                         "launches for these row counts (comma-separated, each <= 8), H = N = 4096")
     ap.add_argument("--ceiling", default=None, metavar="WORKLOADS",
                     help="time the traffic probe (the op's byte mix and access structure, no "
                          "arithmetic) for these workloads (comma-separated, or 'all') instead of the op")
@@ -655,6 +708,8 @@ def main():
         return chain_main(args)
     if args.ceiling:
         return ceiling_main(args)
+    if args.decode:
+        return decode_main(args)
     _lib.lib()
     wl = WORKLOADS[args.workload or DEFAULT_BENCH]
     if args.write_y and not wl.write_y:

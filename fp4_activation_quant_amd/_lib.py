@@ -17,7 +17,7 @@ NQ_NORM_GEMMA, NQ_NORM_PLAIN = 0, 1
 EXPORTS = ("nq_gemma_add_rms_norm_quant", "nq_add_rms_norm_quant", "nq_quant_fp8_static",
            "nq_quant_nvfp4", "nq_quant_mxfp8", "nq_gemm_mxfp8", "nq_gemm_fp8_static", "nq_gemm_nvfp4",
            "nq_block_scale_bytes", "nq_status_string", "nq_abi_version", "nq_convert_probe",
-           "nq_traffic_probe")
+           "nq_traffic_probe", "nq_gemma_add_rms_norm_quant_gemm_fp8")
 
 _lib = None
 
@@ -67,6 +67,9 @@ def lib():
         pi64 = ctypes.POINTER(ctypes.c_int64)
         L.nq_traffic_probe.argtypes = [pp, pi64, i32, pp, pi64, i32, i64, i32, i32, i32, vp]
         L.nq_traffic_probe.restype = i32
+        L.nq_gemma_add_rms_norm_quant_gemm_fp8.argtypes = [vp, vp, vp, vp, f32, vp, i64, i64, i32, i32, vp, vp,
+                                                           vp, vp, i64, vp, vp]
+        L.nq_gemma_add_rms_norm_quant_gemm_fp8.restype = i32
         _lib = L
     return _lib
 
@@ -147,3 +150,11 @@ def nq_traffic_probe(src, src_row_bytes, dst, dst_row_bytes, rows, threads, grid
     return lib().nq_traffic_probe(vpa(*src), i64a(*src_row_bytes), len(src), vpd(*dst) if dst else None,
                                   i64d(*dst_row_bytes) if dst else None, len(dst), int(rows), int(threads),
                                   int(grid), int(prefetch), stream or None)
+
+
+def nq_gemma_add_rms_norm_quant_gemm_fp8(x, residual, residual_out, weight, eps, scale, M, H, dtype,
+                                         write_y, q, y, b, b_scale, N, out, stream):
+    return lib().nq_gemma_add_rms_norm_quant_gemm_fp8(x or None, residual or None, residual_out or None,
+                                                      weight or None, float(eps), scale or None, int(M), int(H),
+                                                      int(dtype), int(write_y), q or None, y or None, b or None,
+                                                      b_scale or None, int(N), out or None, stream or None)

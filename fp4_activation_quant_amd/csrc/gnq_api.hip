@@ -12,6 +12,7 @@
 
 #include "gemma_norm_quant.h"
 #include "gnq_common.hpp"
+#include "gnq_decode.hpp"
 #include "gnq_gemm.hpp"
 #include "gnq_traffic.hpp"
 #include "gnq_validate.hpp"
@@ -37,8 +38,8 @@ __global__ void convert_probe(int kind, const uint32_t *__restrict__ in, int64_t
     }
     case 2: reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)(Bf16::pack(f, 0.0f) & 0xffffu); break;
     case 3: reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)(Fp16::pack(f, 0.0f) & 0xffffu); break;
-    case 4: out[i] = (uint8_t)e4m3_one(div_by_scale(Bf16::lo(bits & 0xffffu), param, 1.0f / param)); break;
-    case 5: out[i] = (uint8_t)e4m3_one(div_by_scale(Fp16::lo(bits & 0xffffu), param, 1.0f / param)); break;
+    case 4: out[i] = (uint8_t)e4m3_one(div_by_scale(Bf16::lo(bits & 0xffffu), quant_scale(param, true))); break;
+    case 5: out[i] = (uint8_t)e4m3_one(div_by_scale(Fp16::lo(bits & 0xffffu), quant_scale(param, true))); break;
     case 6: out[i] = (uint8_t)nvfp4_scale_code(f, param); break;
     case 7: out[i] = (uint8_t)mx_scale_code(fabsf(f)); break;
     case 8: out[i] = (uint8_t)e4m3_one(f * mx_elem_scale((uint32_t)param)); break;
@@ -173,6 +174,18 @@ nq_status nq_gemm_nvfp4(const void *a, const void *a_scales, const float *a_gs, 
   const nq_status v = check_gemm_nvfp4(a, a_scales, a_gs, b, b_scales, b_gs, M, N, K, out);
   if (v != NQ_OK || M == 0 || N == 0) return v;
   return status_of(gemm_nvfp4(a, a_scales, a_gs, b, b_scales, b_gs, M, N, K, out, (hipStream_t)stream));
+}
+
+nq_status nq_gemma_add_rms_norm_quant_gemm_fp8(const void *x, const void *residual, void *residual_out,
+                                               const void *weight, float eps, const float *scale, int64_t M,
+                                               int64_t H, int dtype, int write_y, void *q, void *y, const void *b,
+                                               const float *b_scale, int64_t N, void *out, void *stream) {
+  const nq_status v = check_fused_decode(x, residual, residual_out, weight, scale, M, H, dtype, write_y, q, y, b,
+                                         b_scale, N, out);
+  if (v != NQ_OK || M == 0) return v;
+  FusedDecodeArgs a{x, residual, residual_out, weight, scale, eps, M, H, q, write_y ? y : nullptr,
+                    b, b_scale, N, out, (hipStream_t)stream};
+  return status_of(fused_decode(a, dtype == NQ_BF16));
 }
 
 nq_status nq_traffic_probe(const void *const *src, const int64_t *src_row_bytes, int nsrc,

@@ -99,6 +99,15 @@ __device__ __forceinline__ uint32_t e2m1x8(const float *v) {
   return w;
 }
 
+// The quant step's per-tensor constants, formed once per thread: the
+// scale s (FP8: the static scale; NVFP4: the global scale), r = fl32(1 / s)
+// and, for FP8, lim = fl32(1024 s) (+inf when that overflows).
+struct QuantScale {
+  float s, r, lim, nz;
+};
+
+__device__ __forceinline__ QuantScale quant_scale(float s, bool fp8);
+
 // fl32(y / s), correctly rounded, from r = fl32(1 / s) (one IEEE division
 // per thread instead of one per element).  q0 = fl(y * r) lies within 1.5
 // ulp of y / s; a correction step q + (y - q*s) * r (FMA, one rounding)
@@ -106,13 +115,73 @@ __device__ __forceinline__ uint32_t e2m1x8(const float *v) {
 // rounded quotient (Markstein's theorem: reciprocal within half an ulp,
 // quotient within one ulp, exact remainder).  The remainder is exact for
 // |y| >= 2^-103, i.e. for every scale >= 2^-90 wherever the FP8 code is not
-// zero.  Quotients beyond +-1024 saturate to +-448 either way; clamping them
-// between steps keeps every intermediate finite.  The remainder is formed as
-// q*s - y and subtracted, so a zero quotient keeps the sign of y.
-__device__ __forceinline__ float div_by_scale(float y, float s, float r) {
-  float q = clampf(y * r, 1024.0f);
-  q = clampf(__builtin_fmaf(-__builtin_fmaf(q, s, -y), r, q), 1024.0f);
-  return __builtin_fmaf(-__builtin_fmaf(q, s, -y), r, q);
+// zero.  y is first clamped to +-fl(1024 s): quotients beyond +-1024
+// saturate to +-448 either way, and every intermediate stays finite (one
+// clamp instead of one per step).  The remainder is formed as q*s - y and
+// subtracted, so a zero quotient keeps the sign of y.
+__device__ __forceinline__ float div_by_scale(float y, const QuantScale &d) {
+  y = clampf(y, d.lim);
+  float q = y * d.r;
+  q = __builtin_fmaf(-__builtin_fmaf(q, d.s, -y), d.r, q);
+  return __builtin_fmaf(-__builtin_fmaf(q, d.s, -y), d.r, q);
+}
+
+// Static FP8 codes of one 8-element chunk of rounded y (four words of two
+// activation-dtype values), little-endian.
+template <class D>
+__device__ __forceinline__ u32x2 fp8_codes(const uint32_t (&yb)[4], const QuantScale &d) {
+  float v[kVec];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = div_by_scale(D::lo(yb[k]), d);
+    v[2 * k + 1] = div_by_scale(D::hi(yb[k]), d);
+  }
+  return u32x2{e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
+}
+
+// -0.0 in a register the optimizer cannot see into.  fma(a, b, -0) is the
+// same single rounding of the exact product as a * b (signed zeros
+// included); written with this addend it is not folded back into a
+// multiply, so an fp16 operand is read straight from its packed half
+// (v_fma_mix_f32) instead of being unpacked first.
+__device__ __forceinline__ float opaque_neg_zero() {
+  float z;
+  asm("v_mov_b32 %0, 0x80000000" : "=v"(z));
+  return z;
+}
+
+__device__ __forceinline__ QuantScale quant_scale(float s, bool fp8) {
+  return QuantScale{s, fp8 ? 1.0f / s : 0.0f, fp8 ? 1024.0f * s : 0.0f, opaque_neg_zero()};
+}
+
+// fl32(y * o) for each value of a chunk (nz: opaque_neg_zero()).
+template <class D>
+__device__ __forceinline__ void scale_chunk(const uint32_t (&yb)[4], float o, float nz, float (&v)[kVec]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = __builtin_fmaf(D::lo(yb[k]), o, nz);
+    v[2 * k + 1] = __builtin_fmaf(D::hi(yb[k]), o, nz);
+  }
+}
+
+// max |y| over a chunk of rounded y.
+template <class D>
+__device__ __forceinline__ float chunk_amax(const uint32_t (&yb)[4]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a = fmaxf(a, fmaxf(fabsf(D::lo(yb[k])), fabsf(D::hi(yb[k]))));
+  return a;
+}
+
+// The same max from the fp32 values before their rounding to the
+// activation dtype: rounding to nearest is monotone in magnitude, so the
+// largest rounded magnitude is the rounding of the largest magnitude.
+template <class D>
+__device__ __forceinline__ float rounded_amax(const float (&y32)[kVec]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kVec; ++k) a = fmaxf(a, fabsf(y32[k]));
+  return D::lo(D::pack(a, 0.0f));
 }
 
 // fl32(a / 6), correctly rounded, for a block amax a >= 0: the reciprocal
@@ -255,57 +324,44 @@ __device__ __forceinline__ float norm_scale(float t, float w) {
   return t * norm_factor<GEMMA>(w);
 }
 
-// Quantize one 8-element chunk of y (already rounded to the activation dtype)
-// of row `row`, chunk `ch`, and store its codes (and, for NVFP4, from the
-// even lane of the pair, the block scale; for MXFP8, from the first lane of
-// the quad, the E8M0 scale).  NVFP4 needs the neighbouring lane to hold the
-// other half of the 16-element block and to run this too; MXFP8 likewise
-// needs the aligned quad of lanes (4 x 8 = 32 elements) to hold chunks
-// 4k..4k+3 and all run it.
-// TABLE: NVFP4 looks the element multiplier up in otab, the workgroup's
-// table (nvfp4_fill_table), instead of dividing.
-template <int MODE, bool TABLE = false>
-__device__ __forceinline__ void quant_store_chunk(const float (&yv)[kVec], float s, float r_s,
+// Quantize one 8-element chunk of y (yb: four words of two values already
+// rounded to the activation dtype D; amax: max |y| over the chunk) of row
+// `row`, chunk `ch`, and store its codes (and, for NVFP4, from the even lane
+// of the pair, the block scale; for MXFP8, from the first lane of the quad,
+// the E8M0 scale).  NVFP4 needs the neighbouring lane to hold the other half
+// of the 16-element block and to run this too; MXFP8 likewise needs the
+// aligned quad of lanes (4 x 8 = 32 elements) to hold chunks 4k..4k+3 and
+// all run it.  TABLE: NVFP4 looks the element multiplier up in otab, the
+// workgroup's table (nvfp4_fill_table), instead of dividing.
+template <class D, int MODE, bool TABLE = false>
+__device__ __forceinline__ void quant_store_chunk(const uint32_t (&yb)[4], float amax, const QuantScale &qs,
                                                   uint8_t *__restrict__ q, uint8_t *__restrict__ bs,
                                                   int64_t row, unsigned ch, int nchunk, int ktiles,
                                                   const float *otab = nullptr) {
   if constexpr (MODE == kModeNvfp4) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) amax = fmaxf(amax, fabsf(yv[k]));
     amax = fmaxf(amax, dpp_swap_adjacent(amax));
-    const uint32_t sc = nvfp4_scale_code(amax, s);
+    const uint32_t sc = nvfp4_scale_code(amax, qs.s);
     float o;
     if constexpr (TABLE) o = otab[sc & (kNvfp4Codes - 1)];
-    else o = nvfp4_elem_scale(sc, s);
+    else o = nvfp4_elem_scale(sc, qs.s);
     float v[kVec];
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) v[k] = yv[k] * o;
+    scale_chunk<D>(yb, o, qs.nz, v);
     uint32_t *qrow = reinterpret_cast<uint32_t *>(q + (size_t)row * (size_t)nchunk * 4);
     __builtin_nontemporal_store(e2m1x8(v), &qrow[ch]);
     if ((ch & 1) == 0) bs[swz128x4(row, (int)(ch >> 1), ktiles)] = (uint8_t)sc;
   } else if constexpr (MODE == kModeMxfp8) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) amax = fmaxf(amax, fabsf(yv[k]));
     amax = fmaxf(amax, dpp<0xB1>(amax));   // lane ^ 1
     amax = fmaxf(amax, dpp<0x4E>(amax));   // lane ^ 2
     const uint32_t sc = mx_scale_code(amax);
-    const float o = mx_elem_scale(sc);
     float v[kVec];
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) v[k] = yv[k] * o;
+    scale_chunk<D>(yb, mx_elem_scale(sc), qs.nz, v);
     const u32x2 packed = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
     u32x2 *qrow = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8);
     __builtin_nontemporal_store(packed, &qrow[ch]);
     if ((ch & 3) == 0) bs[(size_t)row * (size_t)(nchunk >> 2) + (ch >> 2)] = (uint8_t)sc;
   } else if constexpr (MODE == kModeFp8) {
-    float v[kVec];
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) v[k] = div_by_scale(yv[k], s, r_s);
-    const u32x2 packed = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
     u32x2 *qrow = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8);
-    __builtin_nontemporal_store(packed, &qrow[ch]);
+    __builtin_nontemporal_store(fp8_codes<D>(yb, qs), &qrow[ch]);
   }
 }
 

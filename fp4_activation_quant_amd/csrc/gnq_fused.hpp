@@ -73,10 +73,9 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
     const unsigned ch = tid + c * nthr;
     if (ch < nch) wa[c] = w[ch];
   }
-  const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
-  const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+  const QuantScale qs = quant_scale(mode_reads_scale(MODE) ? *scale_ptr : 1.0f, MODE == kModeFp8);
   // NVFP4: the multiplier table, read after the first row's barrier.
-  if constexpr (MODE == kModeNvfp4) nvfp4_fill_table(otab, s, tid, nthr);
+  if constexpr (MODE == kModeNvfp4) nvfp4_fill_table(otab, qs.s, tid, nthr);
   // The looping launch keeps the norm's per-element factor fl(1 + w) (or w)
   // in registers across its rows.
   float g[PF ? CPT : 1][PF ? kVec : 1];
@@ -135,25 +134,30 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
     for (int c = 0; c < CPT; ++c) {
       const unsigned ch = tid + c * nthr;
       if (ch < nch) {
-        // y = RN(t * (1 + w)) (Gemma) or RN(t * w), t = h * rstd; the quant
-        // reads the rounded y.
-        float yv[kVec];
+        // y = RN(t * (1 + w)) (Gemma) or RN(t * w), t = h * rstd (as
+        // fma(h, rstd, -0): the same rounding); the quant reads the rounded y.
+        float y32[kVec];
         uint32_t yb[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float ta = D::lo(hb[c][k]) * rstd, tb = D::hi(hb[c][k]) * rstd;
-          if constexpr (PF)
-            yb[k] = D::pack(ta * g[c][2 * k], tb * g[c][2 * k + 1]);
-          else
-            yb[k] = D::pack(norm_scale<GEMMA>(ta, D::lo(wa[c][k])), norm_scale<GEMMA>(tb, D::hi(wa[c][k])));
-          yv[2 * k] = D::lo(yb[k]);
-          yv[2 * k + 1] = D::hi(yb[k]);
+          const float ta = __builtin_fmaf(D::lo(hb[c][k]), rstd, qs.nz);
+          const float tb = __builtin_fmaf(D::hi(hb[c][k]), rstd, qs.nz);
+          if constexpr (PF) {
+            y32[2 * k] = ta * g[c][2 * k];
+            y32[2 * k + 1] = tb * g[c][2 * k + 1];
+          } else {
+            y32[2 * k] = norm_scale<GEMMA>(ta, D::lo(wa[c][k]));
+            y32[2 * k + 1] = norm_scale<GEMMA>(tb, D::hi(wa[c][k]));
+          }
+          yb[k] = D::pack(y32[2 * k], y32[2 * k + 1]);
         }
         if constexpr (WRITE_Y) {
           const u32x4 o = {yb[0], yb[1], yb[2], yb[3]};
           __builtin_nontemporal_store(o, &yr[ch]);
         }
-        quant_store_chunk<MODE, MODE == kModeNvfp4>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles, otab);
+        if constexpr (MODE != kModeNone)
+          quant_store_chunk<D, MODE, MODE == kModeNvfp4>(yb, MODE == kModeFp8 ? 0.0f : rounded_amax<D>(y32), qs,
+                                                         q, bs, row, ch, nchunk, ktiles, otab);
       }
     }
     if constexpr (!PF)
@@ -184,8 +188,7 @@ fused_rows_small(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32
     if constexpr (HAS_RES) ra = __builtin_nontemporal_load(&res[rbase + ch]);
     wa = w[ch];
   }
-  const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
-  const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+  const QuantScale qs = quant_scale(mode_reads_scale(MODE) ? *scale_ptr : 1.0f, MODE == kModeFp8);
   uint32_t hb[4];
   float ss = 0.0f;
   if constexpr (HAS_RES) {
@@ -207,14 +210,13 @@ fused_rows_small(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32
   }
   ss = group_sum<LPR>(ss);
   const float rstd = row_rstd(ss, __builtin_amdgcn_rcpf((float)(nchunk * kVec)), eps);
-  float yv[kVec];
+  float y32[kVec];
   uint32_t yb[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float ta = D::lo(hb[k]) * rstd, tb = D::hi(hb[k]) * rstd;
-    yb[k] = D::pack(norm_scale<GEMMA>(ta, D::lo(wa[k])), norm_scale<GEMMA>(tb, D::hi(wa[k])));
-    yv[2 * k] = D::lo(yb[k]);
-    yv[2 * k + 1] = D::hi(yb[k]);
+    y32[2 * k] = norm_scale<GEMMA>(__builtin_fmaf(D::lo(hb[k]), rstd, qs.nz), D::lo(wa[k]));
+    y32[2 * k + 1] = norm_scale<GEMMA>(__builtin_fmaf(D::hi(hb[k]), rstd, qs.nz), D::hi(wa[k]));
+    yb[k] = D::pack(y32[2 * k], y32[2 * k + 1]);
   }
   if constexpr (WRITE_Y) {
     if (active) {
@@ -225,7 +227,10 @@ fused_rows_small(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32
   // NVFP4 has H % 64 == 0 and MXFP8 H % 32 == 0, so the lanes of a row group
   // into whole blocks (LPR >= 4 for MXFP8) and an inactive lane shares a
   // block only with inactive lanes.
-  if (active) quant_store_chunk<MODE>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles);
+  if constexpr (MODE != kModeNone)
+    if (active)
+      quant_store_chunk<D, MODE>(yb, MODE == kModeFp8 ? 0.0f : rounded_amax<D>(y32), qs, q, bs, row, ch, nchunk,
+                                 ktiles);
 }
 
 // Any H and any alignment: element loads, same arithmetic.
@@ -238,8 +243,8 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
   __shared__ float partial[2][256 / kWave];
   const int tid = threadIdx.x;
   const int nwaves = blockDim.x / kWave;
-  const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
-  const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+  const QuantScale qs = quant_scale(mode_reads_scale(MODE) ? *scale_ptr : 1.0f, MODE == kModeFp8);
+  const float s = qs.s;
   int parity = 0;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x, parity ^= 1) {
     const size_t rb = (size_t)row * (size_t)H;
@@ -304,7 +309,7 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
         const uint32_t yq =
             D::pack(norm_scale<GEMMA>(D::lo(hsrc[rb + j]) * rstd, D::lo(w[j])), 0.0f) & 0xffffu;
         if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
-        if constexpr (MODE == kModeFp8) q[rb + j] = (uint8_t)e4m3_one(div_by_scale(D::lo(yq), s, r_s));
+        if constexpr (MODE == kModeFp8) q[rb + j] = (uint8_t)e4m3_one(div_by_scale(D::lo(yq), qs));
       }
     }
   }

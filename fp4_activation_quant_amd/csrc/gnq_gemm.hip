@@ -40,11 +40,9 @@
 
 #include "gnq_common.hpp"
 #include "gnq_gemm.hpp"
+#include "gnq_mfma.hpp"
 
 namespace gnq {
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmThreads = 256;
 constexpr int kGemmTile = 256;                // output rows and columns per workgroup
@@ -237,17 +235,6 @@ __host__ __device__ constexpr int dma_scale_win(int T) { return T * 2 * kGemmSca
 __host__ __device__ constexpr int dma_scale_off(int T) { return kGemmStages * dma_stage_bytes(T); }
 __host__ __device__ constexpr int dma_lds_bytes(int T) { return dma_scale_off(T) + 2 * 2 * dma_scale_win(T); }
 
-// Global -> LDS DMA of 16 bytes per lane (lane l writes lds + 16 l).
-__device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // NW waves per workgroup, each owning TM x TN MFMA tiles (32 x 32) of the
 // T x T workgroup tile; the T / 8 one-KB data segments (16 rows each, T / 16
 // per operand) and T / 32 scale segments (64 rows each) of a step are split
@@ -330,7 +317,12 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{0};
   i32x8 af[2][TM], bf[2][TN];
-  int sa[2][TM], sb[2][TN];
+  // MXFP8: this lane's E8M0 codes of the current 8-step scale window, for
+  // each operand unit (B tiles, then A tiles): the byte of step j at byte
+  // j % 4 of word j / 4.  Loaded once per window by a 16-byte LDS read per
+  // unit (16-byte rows: no bank conflicts; per-step byte reads of 32 rows
+  // 16 bytes apart conflicted two-way) and packed to this lane's half.
+  uint32_t swin[kUnits][2];
   // LDS byte offsets of this lane's fragment rows, one per (stage pair,
   // operand, 16-byte half).  The swizzle of rows wm + 32 i + r depends on r
   // only, so tile, stage-in-pair and slot constants become immediate offsets
@@ -352,26 +344,36 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
   uint32_t sbase[2];
 #pragma unroll
   for (int op = 0; op < 2; ++op) {
-    sbase[op] = (uint32_t)(kScaleOff + op * kScaleWin + ((op ? wn : wm) + r) * 16 + h);
+    sbase[op] = (uint32_t)(kScaleOff + op * kScaleWin + ((op ? wn : wm) + r) * 16);
     asm volatile("" : "+v"(sbase[op]));
   }
+  // bytes h, h + 2, h + 4, h + 6 of a pair of window words (steps 0..3 or
+  // 4..7 of this lane's half: lanes 32..63 take the odd blocks)
+  const uint32_t sel = 0x06040200u + 0x01010101u * (uint32_t)h;
+  auto load_window = [&](uint32_t wofs) {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int op = u < TN ? 1 : 0, t = u < TN ? u : u - TN;
+      const u32x4 w4 = *reinterpret_cast<const u32x4 *>(smem + sbase[op] + wofs + t * 32 * 16);
+      swin[u][0] = __builtin_amdgcn_perm(w4[1], w4[0], sel);
+      swin[u][1] = __builtin_amdgcn_perm(w4[3], w4[2], sel);
+    }
+  };
+  // the E8M0 code of unit u for step j (0..7) of the window
+  auto code_of = [&](int u, int j) -> int {
+    return (int)__builtin_amdgcn_ubfe(swin[u][j >> 2], 8 * (j & 3), 8);
+  };
   // Read unit u of step ks into register set p: B tile u for u < TN, else
-  // A tile u - TN, each with its scale code (window buffer offset `wofs`).
-  auto read_unit = [&](int ks, int p, int u, uint32_t wofs) {
+  // A tile u - TN.
+  auto read_unit = [&](int ks, int p, int u) {
     const int stg = ks % kGemmStages;
     const int op = u < TN ? 1 : 0, t = u < TN ? u : u - TN;
     const uint32_t imm = (uint32_t)((stg & 1) * kStageBytes + t * 32 * kGemmK);
     const u32x4 lo = *reinterpret_cast<const u32x4 *>(smem + fbase[stg >> 1][op][0] + imm);
     const u32x4 hi = *reinterpret_cast<const u32x4 *>(smem + fbase[stg >> 1][op][1] + imm);
     const i32x8 f = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    const int sc = MX ? (int)smem[sbase[op] + wofs + (ks % kGemmScaleSteps) * 2 + t * 32 * 16] : unit_scale;
-    if (op) {
-      bf[p][t] = f;
-      sb[p][t] = sc;
-    } else {
-      af[p][t] = f;
-      sa[p][t] = sc;
-    }
+    if (op) bf[p][t] = f;
+    else af[p][t] = f;
   };
 
   // One K step: MFMAs of step ks from register set ks % 2, interleaved with
@@ -382,11 +384,19 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
   // (inside LDS) that nothing uses.
   auto step = [&](int ks, int u8, int c) {
     const int p = u8 & 1;
-    const uint32_t wofs = (uint32_t)((((ks + 1) / kGemmScaleSteps) & 1) * 2 * kScaleWin);
     // step ks + 1's segments of this wave: at most step ks + 2's (and a
     // scale window issued after them) may still be in flight
     wait_vmcnt<kSegs>();
     asm volatile("s_barrier" ::: "memory");
+    // this step's scale codes, before the last step of a window loads the
+    // next window's (the barrier above certifies its DMA has landed)
+    int sa[TM], sb[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] = MX ? code_of(j, u8) : unit_scale;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = MX ? code_of(TN + i, u8) : unit_scale;
+    if (MX && u8 == kGemmScaleSteps - 1)
+      load_window((uint32_t)(((c + 1) & 1) * 2 * kScaleWin));
     const int nk = ks + kGemmStages - 1, from = min(nk, ksteps - 1);
     // The DMA of step ks + 3 (each instruction holds the wave for many
     // cycles) and the reads of step ks + 1 are spread between the MFMAs
@@ -395,13 +405,13 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
     for (int q = 0; q < kMfma; ++q) {
       const int i = q / TN, j = q % TN;
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[p][i], bf[p][j], acc[i][j], 0, 0, 0,
-                                                                  sa[p][i], 0, sb[p][j]);
+                                                                  sa[i], 0, sb[j]);
       __builtin_amdgcn_sched_barrier(0);
       // unit u of the next step is read after MFMA u * kMfma / kUnits,
       // DMA segment g after MFMA g * kMfma / kSegs + kMfma / (2 kSegs)
 #pragma unroll
       for (int u = 0; u < kUnits; ++u)
-        if ((u * kMfma) / kUnits == q) read_unit(ks + 1, p ^ 1, u, wofs);
+        if ((u * kMfma) / kUnits == q) read_unit(ks + 1, p ^ 1, u);
 #pragma unroll
       for (int g = 0; g < kSegs; ++g)
         if ((g * kMfma) / kSegs + kMfma / (2 * kSegs) == q) issue_seg(nk, from, g);
@@ -417,8 +427,9 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
   for (int p = 0; p < kGemmStages - 1; ++p) issue(p, p);
   wait_vmcnt<kSegs * (kGemmStages - 2)>();
   asm volatile("s_barrier" ::: "memory");
+  if (MX) load_window(0);
 #pragma unroll
-  for (int u = 0; u < kUnits; ++u) read_unit(0, 0, u, 0);
+  for (int u = 0; u < kUnits; ++u) read_unit(0, 0, u);
   for (int c = 0; c < chunks; ++c) {
 #pragma unroll
     for (int u8 = 0; u8 < 8; ++u8) step(8 * c + u8, u8, c);
@@ -438,18 +449,6 @@ gemm_fp8_tn_dma(const uint8_t *__restrict__ A, const uint8_t *__restrict__ SA,
           C[(size_t)row * (size_t)N + col] = (uint16_t)(Bf16::pack(acc[i][j][v] * s, 0.0f) & 0xffffu);
       }
     }
-}
-
-// Raise a kernel's dynamic-LDS limit once per device (bit d of `done`).
-inline hipError_t allow_dynamic_lds(const void *kernel, int bytes, std::atomic<uint64_t> &done) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
-  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
-  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
-  return e;
 }
 
 // Explicit instantiations: the kernels are referenced only from the launch

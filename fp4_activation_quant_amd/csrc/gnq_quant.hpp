@@ -31,19 +31,14 @@ quant_rows(const u32x4 *__restrict__ y, const float *__restrict__ scale_ptr, int
       const unsigned ch = tid + c * nthr;
       if (ch < nch) ya[c] = __builtin_nontemporal_load(&yr[ch]);
     }
-    const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
-    const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+    const QuantScale qs = quant_scale(mode_reads_scale(MODE) ? *scale_ptr : 1.0f, MODE == kModeFp8);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const unsigned ch = tid + c * nthr;
       if (ch < nch) {
-        float yv[kVec];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          yv[2 * k] = D::lo(ya[c][k]);
-          yv[2 * k + 1] = D::hi(ya[c][k]);
-        }
-        quant_store_chunk<MODE, MODE == kModeNvfp4>(yv, s, r_s, q, bs, row, ch, nchunk, ktiles, otab);
+        const uint32_t yb[4] = {ya[c][0], ya[c][1], ya[c][2], ya[c][3]};
+        quant_store_chunk<D, MODE, MODE == kModeNvfp4>(yb, MODE == kModeFp8 ? 0.0f : chunk_amax<D>(yb), qs, q, bs,
+                                                       row, ch, nchunk, ktiles, otab);
       }
     }
   }
@@ -53,8 +48,8 @@ template <class D, int MODE>
 __global__ void __launch_bounds__(256)
 quant_rows_scalar(const uint16_t *__restrict__ y, const float *__restrict__ scale_ptr, int64_t M,
                   int H, uint8_t *__restrict__ q, uint8_t *__restrict__ bs, int ktiles) {
-  const float s = mode_reads_scale(MODE) ? *scale_ptr : 1.0f;
-  const float r_s = MODE == kModeFp8 ? 1.0f / s : 0.0f;
+  const QuantScale qs = quant_scale(mode_reads_scale(MODE) ? *scale_ptr : 1.0f, MODE == kModeFp8);
+  const float s = qs.s;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
     const size_t rb = (size_t)row * (size_t)H;
     if constexpr (MODE == kModeNvfp4) {
@@ -87,7 +82,7 @@ quant_rows_scalar(const uint16_t *__restrict__ y, const float *__restrict__ scal
       }
     } else {
       for (int j = threadIdx.x; j < H; j += blockDim.x)
-        q[rb + j] = (uint8_t)e4m3_one(div_by_scale(D::lo(y[rb + j]), s, r_s));
+        q[rb + j] = (uint8_t)e4m3_one(div_by_scale(D::lo(y[rb + j]), qs));
     }
   }
 }

@@ -162,6 +162,40 @@ inline nq_status check_gemm_nvfp4(const void *a, const void *a_scales, const flo
   return NQ_OK;
 }
 
+// nq_gemma_add_rms_norm_quant_gemm_fp8: the op in static FP8 mode on M <= 8
+// rows with H in {1024, 2048, 4096} (NQ_EUNSUPPORTED otherwise, also for
+// N == 0: the two-launch path covers those), and its consumer GEMM.  The
+// updated residual goes to residual_out, which must not overlap anything
+// (in particular not residual).
+inline nq_status check_fused_decode(const void *x, const void *residual, const void *residual_out,
+                                    const void *weight, const float *scale, int64_t M, int64_t H, int dtype,
+                                    int write_y, const void *q, const void *y, const void *b,
+                                    const float *b_scale, int64_t N, const void *out) {
+  if (!valid_dtype(dtype)) return NQ_EINVAL;
+  if (M < 0 || H <= 0 || N < 0 || N > ((int64_t)1 << 30) || H > ((int64_t)1 << 30)) return NQ_EINVAL;
+  if (!x || !weight || !scale || !q || !b || !b_scale || !out) return NQ_EINVAL;
+  if ((residual != nullptr) != (residual_out != nullptr)) return NQ_EINVAL;
+  if (write_y && !y) return NQ_EINVAL;
+  if (M == 0) return NQ_OK;
+  if (M > 8 || N == 0 || !(H == 1024 || H == 2048 || H == 4096)) return NQ_EUNSUPPORTED;
+  if (((uintptr_t)x | (uintptr_t)residual | (uintptr_t)residual_out | (uintptr_t)weight |
+       (uintptr_t)(write_y ? y : nullptr) | (uintptr_t)b) % 16 != 0 ||
+      (uintptr_t)q % 8 != 0 || (uintptr_t)out % 2 != 0 || ((uintptr_t)scale | (uintptr_t)b_scale) % 4 != 0)
+    return NQ_EINVAL;
+  const size_t act = (size_t)M * (size_t)H * 2;
+  const void *wr[4] = {residual_out, q, write_y ? y : nullptr, out};
+  const size_t wlen[4] = {act, (size_t)M * (size_t)H, act, (size_t)M * (size_t)N * 2};
+  const void *rd[6] = {x, residual, weight, scale, b, b_scale};
+  const size_t rlen[6] = {act, act, (size_t)H * 2, 4, (size_t)N * (size_t)H, 4};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(wr[i], wlen[i], wr[j], wlen[j])) return NQ_EINVAL;
+    for (int k = 0; k < 6; ++k)
+      if (overlaps(wr[i], wlen[i], rd[k], rlen[k])) return NQ_EINVAL;
+  }
+  return NQ_OK;
+}
+
 // nq_traffic_probe: 1..2 read and 0..4 write streams of 16-byte chunks, a
 // read row within 4 chunks per thread; no write stream overlaps another
 // stream.

@@ -322,6 +322,36 @@ def gemm_fp8_static(a, a_scale, b, b_scale, out=None):
     return out
 
 
+def gemma_add_rms_norm_quant_gemm_fp8_out(x, residual, residual_out, weight, eps, scale, b, b_scale, q, y,
+                                          out):
+    """A decode step in one launch: the op in static FP8 mode (codes into
+    ``q``, ``y`` if given, x + ``residual`` into ``residual_out``) and the
+    consumer linear ``out`` (M, N) bf16 = dq(q) @ dq(b)^T of the FP8 weight
+    ``b`` (N, H) with its float32 scale.  For 1 <= M <= 8 and H in {1024,
+    2048, 4096}; other shapes raise (call the op and ``gemm_fp8_static``).
+    The residual is not updated in place (``residual_out`` is its own
+    buffer)."""
+    _validate(x, residual, weight, scale)
+    M, H = x.shape
+    dev = x.device
+    if residual is not None:
+        _buf(residual_out, "residual_out", dev, shape=(M, H), dtype=x.dtype)
+    _validate_codes(b, "b", dev)
+    _require(b.shape[1] == H, "b: (N, H)")
+    _scalar(b_scale, "b_scale", dev)
+    _buf(q, "q", dev, nbytes=M * H, itemsize=1)
+    if y is not None:
+        _buf(y, "y", dev, nbytes=M * H * x.element_size(), dtype=x.dtype)
+    N = b.shape[0]
+    _buf(out, "out", dev, shape=(M, N), dtype=torch.bfloat16)
+    with torch.cuda.device(dev):
+        st = _lib.nq_gemma_add_rms_norm_quant_gemm_fp8(
+            x.data_ptr(), _ptr(residual), _ptr(residual_out) if residual is not None else 0, weight.data_ptr(),
+            eps, scale.data_ptr(), M, H, _DT[x.dtype], y is not None, q.data_ptr(), _ptr(y), b.data_ptr(),
+            b_scale.data_ptr(), N, out.data_ptr(), _stream(dev))
+    _check(st, "nq_gemma_add_rms_norm_quant_gemm_fp8")
+
+
 def gemm_nvfp4(a, a_block_scale, a_global_scale, b, b_block_scale, b_global_scale, out=None):
     """The consumer linear on an NVFP4 activation: out (M, N) bf16 =
     dq(a) @ dq(b)^T, with a (M, K // 2) / b (N, K // 2) packed E2M1 codes,

@@ -235,6 +235,40 @@ nq_status nq_gemm_nvfp4(const void *a, const void *a_scales, const float *a_gs, 
                         const void *b_scales, const float *b_gs, int64_t M, int64_t N, int64_t K, void *out,
                         void *stream);
 
+/*
+ * nq_gemma_add_rms_norm_quant_gemm_fp8 -- a decode step: the op in static
+ * FP8 mode on a few token rows and its consumer linear, in one launch.  The
+ * `fused_norm_quant` page overlaps the consumer GEMM's launch with the op at
+ * small batches (its launch comment: an early trigger, ~2% at up to 128
+ * rows); here every GEMM workgroup fetches its weight tile and forms the
+ * rows' norm and FP8 codes itself, so no second launch waits on the first.
+ *
+ *   x, weight, eps, scale, M, H, dtype, write_y, q, y
+ *              as nq_gemma_add_rms_norm_quant in NQ_MODE_FP8_STATIC; the
+ *              results (q, y, the updated residual) are bit-for-bit those
+ *              of that call.
+ *   residual   (M, H) dtype or NULL, read only;
+ *   residual_out (M, H) dtype, required with residual: x + residual
+ *              (not in place: the launch's workgroups read the residual
+ *              while one of them writes the result).
+ *   b, b_scale the linear's weight: (N, H) E4M3FN codes, row-major, and its
+ *              static fp32 scale (DEVICE pointer).
+ *   N          output features >= 1.
+ *   out        (M, N) bf16 = dq(q) dq(b)^T, the result of
+ *              nq_gemm_fp8_static(q, scale, b, b_scale) for the same codes.
+ *
+ * Shapes: 1 <= M <= 8 and H in {1024, 2048, 4096}; other M, H and N == 0
+ * return NQ_EUNSUPPORTED (run the op and the GEMM as two calls); M == 0
+ * returns NQ_OK without launching.  x, residual, residual_out, weight, y and
+ * b 16-byte aligned, q 8-byte, out 2-byte, the scales 4-byte; outputs
+ * (residual_out, q, y, out) overlap nothing (NQ_EINVAL otherwise, nothing
+ * launched).
+ */
+nq_status nq_gemma_add_rms_norm_quant_gemm_fp8(const void *x, const void *residual, void *residual_out,
+                                               const void *weight, float eps, const float *scale, int64_t M,
+                                               int64_t H, int dtype, int write_y, void *q, void *y, const void *b,
+                                               const float *b_scale, int64_t N, void *out, void *stream);
+
 /* Size in bytes of the NVFP4 block-scale buffer:
  * round_up(M, 128) * round_up(H / 16, 4) (the wrapper's allocation on the
  * `fused_norm_quant` page).  0 for M <= 0, H < 16, or sizes the entry points

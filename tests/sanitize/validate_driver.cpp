@@ -8,6 +8,7 @@
 //   gemm4 a sa ags b sb bgs M N K out
 //   traffic nsrc ndst rows threads grid src0 src1 srb0 srb1 dst0..dst3 drb0..drb3
 //   probe kind in n param out
+//   fdec x r ro w s M H dtype write_y q y b bs N out
 //   bsb M H                       (prints nq_block_scale_bytes)
 // Addresses and sizes are decimal 64-bit integers; param is a decimal float.
 #include <cinttypes>
@@ -87,6 +88,13 @@ int main() {
       p += k;
       next(out);
       std::printf("%d\n", (int)check_convert_probe((int)kind, P(in), n, param, P(out)));
+    } else if (c == "fdec") {
+      uint64_t x, r, ro, w, s, q, y, b, bs, out;
+      int64_t M, H, dt, wy, N;
+      next(x), next(r), next(ro), next(w), next(s), nexti(M), nexti(H), nexti(dt), nexti(wy), next(q), next(y);
+      next(b), next(bs), nexti(N), next(out);
+      std::printf("%d\n", (int)check_fused_decode(P(x), P(r), P(ro), P(w), (const float *)P(s), M, H, (int)dt,
+                                                  (int)wy, P(q), P(y), P(b), (const float *)P(bs), N, P(out)));
     } else if (c == "bsb") {
       int64_t M, H;
       nexti(M), nexti(H);

@@ -306,3 +306,34 @@ def test_traffic_probe_nonzero_rows_still_validated():
     # rows > 0 with a bad stream is rejected before any launch
     assert _lib.nq_traffic_probe([SA], [1000], [DA], [512], 8, 256, 0, 0, 0) == _lib.NQ_EINVAL
     assert _lib.nq_traffic_probe([SA], [1024], [SA], [512], 8, 256, 0, 0, 0) == _lib.NQ_EINVAL
+
+
+FX, FR, FRO, FW, FS, FQ, FY, FB, FBS, FO = (0x40000000 + i * 0x1000000 for i in range(10))
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(M=0), _lib.NQ_OK),                          # nothing to do
+    (dict(M=9), _lib.NQ_EUNSUPPORTED),                # more than 8 rows
+    (dict(H=5120), _lib.NQ_EUNSUPPORTED),
+    (dict(N=0), _lib.NQ_EUNSUPPORTED),
+    (dict(M=-1), _lib.NQ_EINVAL),
+    (dict(dtype=3), _lib.NQ_EINVAL),
+    (dict(x=0), _lib.NQ_EINVAL),
+    (dict(b=0), _lib.NQ_EINVAL),
+    (dict(ro=0), _lib.NQ_EINVAL),                     # residual without residual_out
+    (dict(r=0), _lib.NQ_EINVAL),                      # residual_out without residual
+    (dict(ro=FR), _lib.NQ_EINVAL),                    # in place
+    (dict(wy=1, y=0), _lib.NQ_EINVAL),
+    (dict(x=FX + 8), _lib.NQ_EINVAL),                 # 16-byte alignment
+    (dict(q=FQ + 4), _lib.NQ_EINVAL),
+    (dict(o=FB + 100), _lib.NQ_EINVAL),               # out over the weight
+    (dict(q=FW), _lib.NQ_EINVAL),                     # q over the norm weight
+    (dict(o=FS - 8), _lib.NQ_EINVAL),                 # out over the scale
+])
+def test_fused_decode_validation(over, want):
+    a = dict(x=FX, r=FR, ro=FRO, w=FW, s=FS, M=4, H=4096, dtype=0, wy=0, q=FQ, y=FY, b=FB, bs=FBS, N=4096, o=FO)
+    a.update(over)
+    st = _lib.nq_gemma_add_rms_norm_quant_gemm_fp8(a["x"], a["r"], a["ro"], a["w"], 1e-6, a["s"], a["M"], a["H"],
+                                                   a["dtype"], a["wy"], a["q"], a["y"], a["b"], a["bs"], a["N"],
+                                                   a["o"], 0)
+    assert st == want

@@ -61,6 +61,10 @@ def _u(v):
 
 
 def _line(cmd, a):
+    if cmd == "fdec":
+        x, r, ro, w, sc, M, H, dt, wy, q, y, b, bs, N, out = a
+        return "fdec " + " ".join(str(v) for v in (_u(x), _u(r), _u(ro), _u(w), _u(sc), M, H, dt, wy, _u(q), _u(y),
+                                                   _u(b), _u(bs), N, _u(out)))
     if cmd in ("op", "quant", "gemm", "gemm4"):
         return cmd + " " + " ".join(str(_u(v)) for v in a)
     if cmd == "traffic":
@@ -79,7 +83,7 @@ def _fuzz(n, seed):
     pick = rng.choice
     out = []
     for _ in range(n):
-        k = rng.randrange(7)
+        k = rng.randrange(8)
         if k == 0:       # x r w s M H dtype norm mode write_y q bs y
             out.append(("op", [pick(ADDRS) for _ in range(4)] +
                         [pick(I64), pick(I64), pick([-1, 0, 1, 2]), pick([-1, 0, 1, 2]),
@@ -99,8 +103,12 @@ def _fuzz(n, seed):
                         [pick(ADDRS) for _ in range(4)] + [pick(ROW_BYTES) for _ in range(4)]))
         elif k == 5:     # kind in n param out
             out.append(("probe", [pick([-1, 0, 5, 8, 9, 10]), pick(ADDRS), pick(I64), pick(PARAMS), pick(ADDRS)]))
-        else:            # M H
+        elif k == 6:     # M H
             out.append(("bsb", [pick(I64), pick(I64)]))
+        else:            # x r ro w s M H dtype write_y q y b bs N out
+            out.append(("fdec", [pick(ADDRS) for _ in range(5)] +
+                        [pick(I64 + [1, 3, 8, 9]), pick(I64 + [1024, 2048, 4096]), pick([-1, 0, 1, 2]),
+                         pick([0, 1])] + [pick(ADDRS) for _ in range(4)] + [pick(I64), pick(ADDRS)]))
     return out
 
 
@@ -153,6 +161,12 @@ def _library(cmd, a, st):
         if st == _lib.NQ_OK and n != 0:
             return None
         return L.nq_convert_probe(kind, _u(inp), n, float(param), _u(out), None)
+    if cmd == "fdec":
+        x, r, ro, w, sc, M, H, dt, wy, q, y, b, bs, N, out = a
+        if st == _lib.NQ_OK and M != 0:
+            return None
+        return L.nq_gemma_add_rms_norm_quant_gemm_fp8(_u(x), _u(r), _u(ro), _u(w), 1e-6, _u(sc), M, H, dt, wy,
+                                                      _u(q), _u(y), _u(b), _u(bs), N, _u(out), None)
     return L.nq_block_scale_bytes(*a)
 
 
