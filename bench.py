@@ -576,6 +576,7 @@ def decode_main(args):
             res[path] = t["diff_ms"] * 1e3
         print(json.dumps({"metric": "decode step: add + Gemma RMSNorm + FP8 quant + FP8 linear, us per step",
                           "M": M, "H": H, "N": N, "weight_sets": n_sets, "steps": args.steps,
+                          "fused_call_runs": "one launch" if M <= 3 else "op + decode GEMM",
                           "fused_us": round(res["fused"], 3), "two_launches_us": round(res["two_launches"], 3),
                           "speedup": round(res["two_launches"] / res["fused"], 3)}), flush=True)
 

@@ -94,7 +94,8 @@ nq_status nq_add_rms_norm_quant(const void *x, void *residual, const void *weigh
               (nv || mx) ? block_scale : nullptr,
               (write_y || none) ? y : nullptr,
               norm == NQ_NORM_GEMMA,
-              (hipStream_t)stream};
+              (hipStream_t)stream,
+              nullptr};
   const bool bf = dtype == NQ_BF16;
   hipError_t e;
   switch (mode) {

@@ -48,6 +48,9 @@ constexpr bool mode_reads_scale(int mode) { return mode == kModeFp8 || mode == k
 struct Bf16 {
   static __device__ __forceinline__ float lo(uint32_t p) { return __uint_as_float(p << 16); }
   static __device__ __forceinline__ float hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+  // fl32(v * b + c), one rounding, for the low / high value v of p.
+  static __device__ __forceinline__ float fma_lo(uint32_t p, float b, float c) { return __builtin_fmaf(lo(p), b, c); }
+  static __device__ __forceinline__ float fma_hi(uint32_t p, float b, float c) { return __builtin_fmaf(hi(p), b, c); }
   static __device__ __forceinline__ uint32_t pack(float a, float b) {
     f32x2 v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
@@ -60,6 +63,20 @@ struct Fp16 {
   }
   static __device__ __forceinline__ float hi(uint32_t p) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+  }
+  // fl32(v * b + c), one rounding, for the low / high value v of p, with v
+  // read from its half of p by v_fma_mix_f32 (whose widening of v is exact).
+  // Written out because the compiler does not form the instruction where
+  // the widening is shared with other uses of v.
+  static __device__ __forceinline__ float fma_lo(uint32_t p, float b, float c) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(p), "v"(b), "v"(c));
+    return d;
+  }
+  static __device__ __forceinline__ float fma_hi(uint32_t p, float b, float c) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(p), "v"(b), "v"(c));
+    return d;
   }
   static __device__ __forceinline__ uint32_t pack(float a, float b) {
     f32x2 v = {a, b};
@@ -332,12 +349,14 @@ __device__ __forceinline__ float norm_scale(float t, float w) {
 // of the 16-element block and to run this too; MXFP8 likewise needs the
 // aligned quad of lanes (4 x 8 = 32 elements) to hold chunks 4k..4k+3 and
 // all run it.  TABLE: NVFP4 looks the element multiplier up in otab, the
-// workgroup's table (nvfp4_fill_table), instead of dividing.
+// workgroup's table (nvfp4_fill_table), instead of dividing.  active =
+// false: the lane computes (its DPP partners may need its values) but
+// stores nothing.
 template <class D, int MODE, bool TABLE = false>
 __device__ __forceinline__ void quant_store_chunk(const uint32_t (&yb)[4], float amax, const QuantScale &qs,
                                                   uint8_t *__restrict__ q, uint8_t *__restrict__ bs,
                                                   int64_t row, unsigned ch, int nchunk, int ktiles,
-                                                  const float *otab = nullptr) {
+                                                  const float *otab = nullptr, bool active = true) {
   if constexpr (MODE == kModeNvfp4) {
     amax = fmaxf(amax, dpp_swap_adjacent(amax));
     const uint32_t sc = nvfp4_scale_code(amax, qs.s);
@@ -346,9 +365,10 @@ __device__ __forceinline__ void quant_store_chunk(const uint32_t (&yb)[4], float
     else o = nvfp4_elem_scale(sc, qs.s);
     float v[kVec];
     scale_chunk<D>(yb, o, qs.nz, v);
+    const uint32_t codes = e2m1x8(v);
     uint32_t *qrow = reinterpret_cast<uint32_t *>(q + (size_t)row * (size_t)nchunk * 4);
-    __builtin_nontemporal_store(e2m1x8(v), &qrow[ch]);
-    if ((ch & 1) == 0) bs[swz128x4(row, (int)(ch >> 1), ktiles)] = (uint8_t)sc;
+    if (active) __builtin_nontemporal_store(codes, &qrow[ch]);
+    if (active && (ch & 1) == 0) bs[swz128x4(row, (int)(ch >> 1), ktiles)] = (uint8_t)sc;
   } else if constexpr (MODE == kModeMxfp8) {
     amax = fmaxf(amax, dpp<0xB1>(amax));   // lane ^ 1
     amax = fmaxf(amax, dpp<0x4E>(amax));   // lane ^ 2
@@ -357,11 +377,12 @@ __device__ __forceinline__ void quant_store_chunk(const uint32_t (&yb)[4], float
     scale_chunk<D>(yb, mx_elem_scale(sc), qs.nz, v);
     const u32x2 packed = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
     u32x2 *qrow = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8);
-    __builtin_nontemporal_store(packed, &qrow[ch]);
-    if ((ch & 3) == 0) bs[(size_t)row * (size_t)(nchunk >> 2) + (ch >> 2)] = (uint8_t)sc;
+    if (active) __builtin_nontemporal_store(packed, &qrow[ch]);
+    if (active && (ch & 3) == 0) bs[(size_t)row * (size_t)(nchunk >> 2) + (ch >> 2)] = (uint8_t)sc;
   } else if constexpr (MODE == kModeFp8) {
+    const u32x2 codes = fp8_codes<D>(yb, qs);
     u32x2 *qrow = reinterpret_cast<u32x2 *>(q + (size_t)row * (size_t)nchunk * 8);
-    __builtin_nontemporal_store(fp8_codes<D>(yb, qs), &qrow[ch]);
+    if (active) __builtin_nontemporal_store(codes, &qrow[ch]);
   }
 }
 
@@ -398,6 +419,7 @@ struct FusedArgs {
   void *y;          // nullptr: y not written
   bool gemma;       // (1 + w) if true, w if false
   hipStream_t st;
+  void *res_out;    // nullptr: the updated residual goes back into res
 };
 
 struct QuantArgs {

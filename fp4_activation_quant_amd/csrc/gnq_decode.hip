@@ -1,6 +1,10 @@
 // Fused decode step: the op in static FP8 mode (residual add + Gemma
 // RMSNorm + FP8 quant of a few token rows) and its consumer linear (the
-// quantized activation times an FP8 weight) in one launch.
+// quantized activation times an FP8 weight) in one launch, up to 3 rows.
+// From 4 rows on, the step runs the op and the decode GEMM as two launches:
+// the one-launch kernel's per-workgroup norm of every row (about 18 VALU
+// operations per element) then costs more than the second launch (at
+// H = N = 4096: 8.9 against 8.6 us at 4 rows, 11.7 against 8.7 at 8).
 //
 // The `fused_norm_quant` page launches the op with an early trigger so the
 // consumer GEMM's weight fetch overlaps the norm at small batches (its launch
@@ -34,6 +38,7 @@
 //    M - 1, weight rows repeated modulo 16) and its fixed-order reduction.
 #include "gnq_common.hpp"
 #include "gnq_decode.hpp"
+#include "gnq_gemm.hpp"
 #include "gnq_mfma.hpp"
 
 namespace gnq {
@@ -238,8 +243,18 @@ template <class D>
 hipError_t fd_rows(const FusedDecodeArgs &a) {
   if (a.M <= 1) return fd_k<D, 1>(a);
   if (a.M <= 2) return fd_k<D, 2>(a);
-  if (a.M <= 4) return fd_k<D, 4>(a);
-  return fd_k<D, 8>(a);
+  return fd_k<D, 4>(a);
+}
+
+// From 4 rows on, the two launches: the op (its updated residual written to
+// residual_out) and the decode GEMM, the same kernels the two separate calls
+// run.
+hipError_t two_launches(const FusedDecodeArgs &a, bool bf16) {
+  FusedArgs op{a.x,  const_cast<void *>(a.res), a.w, a.scale, a.eps, a.M, a.H, a.q, nullptr, a.y,
+               true, a.st, a.res ? a.res_out : nullptr};
+  const hipError_t e = bf16 ? fused_bf16_fp8(op) : fused_fp16_fp8(op);
+  if (e != hipSuccess) return e;
+  return gemm_fp8(false, a.q, nullptr, a.b, nullptr, a.scale, a.b_scale, a.M, a.N, a.H, a.out, a.st);
 }
 
 }  // namespace
@@ -248,6 +263,9 @@ bool fused_decode_supported(int64_t M, int64_t H) {
   return M >= 1 && M <= kFusedDecodeMaxRows && (H == 1024 || H == 2048 || H == 4096);
 }
 
-hipError_t fused_decode(const FusedDecodeArgs &a, bool bf16) { return bf16 ? fd_rows<Bf16>(a) : fd_rows<Fp16>(a); }
+hipError_t fused_decode(const FusedDecodeArgs &a, bool bf16) {
+  if (a.M > kFusedDecodeOneLaunchRows) return two_launches(a, bf16);
+  return bf16 ? fd_rows<Bf16>(a) : fd_rows<Fp16>(a);
+}
 
 }  // namespace gnq

@@ -8,6 +8,10 @@
 namespace gnq {
 
 constexpr int kFusedDecodeMaxRows = 8;
+// Up to this many rows the step is one launch; above, the op and the decode
+// GEMM as two launches (every workgroup of the one-launch kernel normalises
+// all rows itself, which from 4 rows on costs more than the second launch).
+constexpr int kFusedDecodeOneLaunchRows = 3;
 
 struct FusedDecodeArgs {
   const void *x;

@@ -38,9 +38,11 @@
 
 namespace gnq {
 
-template <class D, int MODE, bool HAS_RES, bool WRITE_Y, bool GEMMA, int CPT, bool PF>
+// RES_OUT: the updated residual goes to res_out instead of back into res.
+template <class D, int MODE, bool HAS_RES, bool WRITE_Y, bool GEMMA, int CPT, bool PF, bool RES_OUT = false>
 __global__ void __launch_bounds__(kMaxThreads)
-fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__restrict__ w,
+fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, u32x4 *__restrict__ res_out,
+           const u32x4 *__restrict__ w,
            const float *__restrict__ scale_ptr, float eps, int64_t M, int nchunk,
            uint8_t *__restrict__ q, uint8_t *__restrict__ bs, u32x4 *__restrict__ y, int ktiles) {
   __shared__ float partial[2][kMaxThreads / kWave];
@@ -50,18 +52,20 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
   const unsigned nch = (unsigned)nchunk;
   const int nwaves = nthr / kWave;
   const float inv_h = __builtin_amdgcn_rcpf((float)(nchunk * kVec));
-  // The row loads: x and residual stream from HBM (non-temporal).
+  // The row loads: x and residual stream from HBM (non-temporal).  They are
+  // unconditional (a thread past the row's end re-reads its last chunk and
+  // drops it), so the compiler's wait before the next row's loads into the
+  // same registers counts only those loads, not the row's stores still in
+  // flight.
   u32x4 xa[CPT], ra[CPT], wa[CPT];
   auto load_row = [&](int64_t b) {
     const int64_t rw = MODE == kModeNvfp4 ? nvfp4_row_of_block(b, M) : b;
     const size_t rb = (size_t)rw * (size_t)nchunk;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const unsigned ch = tid + c * nthr;
-      if (ch < nch) {
-        xa[c] = __builtin_nontemporal_load(&x[rb + ch]);
-        if constexpr (HAS_RES) ra[c] = __builtin_nontemporal_load(&res[rb + ch]);
-      }
+      const unsigned ch = min(tid + c * nthr, nch - 1);
+      xa[c] = __builtin_nontemporal_load(&x[rb + ch]);
+      if constexpr (HAS_RES) ra[c] = __builtin_nontemporal_load(&res[rb + ch]);
     }
   };
   int64_t blk = blockIdx.x;
@@ -69,10 +73,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
   // The weight and the scale come from L2, once per workgroup; the scale's
   // reciprocal is formed while the first row's loads are in flight.
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const unsigned ch = tid + c * nthr;
-    if (ch < nch) wa[c] = w[ch];
-  }
+  for (int c = 0; c < CPT; ++c) wa[c] = w[min(tid + c * nthr, nch - 1)];
   const QuantScale qs = quant_scale(mode_reads_scale(MODE) ? *scale_ptr : 1.0f, MODE == kModeFp8);
   // NVFP4: the multiplier table, read after the first row's barrier.
   if constexpr (MODE == kModeNvfp4) nvfp4_fill_table(otab, qs.s, tid, nthr);
@@ -92,7 +93,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
   for (; blk < M; blk += gridDim.x, parity ^= 1) {
     const int64_t row = MODE == kModeNvfp4 ? nvfp4_row_of_block(blk, M) : blk;
     const size_t rbase = (size_t)row * (size_t)nchunk;
-    u32x4 *__restrict__ rr = res + rbase;
+    u32x4 *__restrict__ rr = (RES_OUT ? res_out : res) + rbase;
     u32x4 *__restrict__ yr = y + rbase;
     // h = RN(x + r), written back; sum of squares of the rounded h.
     uint32_t hb[CPT][4];
@@ -100,24 +101,28 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const unsigned ch = tid + c * nthr;
-      if (ch < nch) {
-        if constexpr (HAS_RES) {
+      if constexpr (HAS_RES) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            hb[c][k] = D::pack(D::lo(xa[c][k]) + D::lo(ra[c][k]), D::hi(xa[c][k]) + D::hi(ra[c][k]));
+        for (int k = 0; k < 4; ++k)
+          hb[c][k] = D::pack(D::lo(xa[c][k]) + D::lo(ra[c][k]), D::hi(xa[c][k]) + D::hi(ra[c][k]));
+        if (ch < nch) {
           const u32x4 o = {hb[c][0], hb[c][1], hb[c][2], hb[c][3]};
           __builtin_nontemporal_store(o, &rr[ch]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) hb[c][k] = xa[c][k];
         }
+      } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float a = D::lo(hb[c][k]), b = D::hi(hb[c][k]);
-          ss = __builtin_fmaf(a, a, ss);
-          ss = __builtin_fmaf(b, b, ss);
-        }
+        for (int k = 0; k < 4; ++k) hb[c][k] = xa[c][k];
       }
+      // the chunk's squares, added in element order (nothing for a chunk
+      // past the row's end)
+      float sc = ss;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float a = D::lo(hb[c][k]), b = D::hi(hb[c][k]);
+        sc = __builtin_fmaf(a, a, sc);
+        sc = __builtin_fmaf(b, b, sc);
+      }
+      ss = ch < nch ? sc : ss;
     }
     // x and residual are dead once h is formed: with PF the next row's loads
     // go out now, behind this row's reduction and stores.
@@ -132,33 +137,35 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, const u32x4 *__
 
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
+      // With PF every thread computes (a chunk past the row's end holds a
+      // re-read chunk and stores nothing), so no branch separates the
+      // conversions of h from their FMAs (measured: 3% faster there, 1%
+      // slower without PF, where the threads past the row skip it).
       const unsigned ch = tid + c * nthr;
-      if (ch < nch) {
-        // y = RN(t * (1 + w)) (Gemma) or RN(t * w), t = h * rstd (as
-        // fma(h, rstd, -0): the same rounding); the quant reads the rounded y.
-        float y32[kVec];
-        uint32_t yb[4];
+      const bool active = ch < nch;
+      if (!PF && !active) continue;
+      // y = RN(t * (1 + w)) (Gemma) or RN(t * w), t = h * rstd (as
+      // fma(h, rstd, -0): the same rounding); the quant reads the rounded y.
+      float y32[kVec];
+      uint32_t yb[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float ta = __builtin_fmaf(D::lo(hb[c][k]), rstd, qs.nz);
-          const float tb = __builtin_fmaf(D::hi(hb[c][k]), rstd, qs.nz);
-          if constexpr (PF) {
-            y32[2 * k] = ta * g[c][2 * k];
-            y32[2 * k + 1] = tb * g[c][2 * k + 1];
-          } else {
-            y32[2 * k] = norm_scale<GEMMA>(ta, D::lo(wa[c][k]));
-            y32[2 * k + 1] = norm_scale<GEMMA>(tb, D::hi(wa[c][k]));
-          }
-          yb[k] = D::pack(y32[2 * k], y32[2 * k + 1]);
+      for (int k = 0; k < 4; ++k) {
+        const float ta = D::fma_lo(hb[c][k], rstd, qs.nz);
+        const float tb = D::fma_hi(hb[c][k], rstd, qs.nz);
+        if constexpr (PF) {
+          y32[2 * k] = ta * g[c][2 * k];
+          y32[2 * k + 1] = tb * g[c][2 * k + 1];
+        } else {
+          y32[2 * k] = norm_scale<GEMMA>(ta, D::lo(wa[c][k]));
+          y32[2 * k + 1] = norm_scale<GEMMA>(tb, D::hi(wa[c][k]));
         }
-        if constexpr (WRITE_Y) {
-          const u32x4 o = {yb[0], yb[1], yb[2], yb[3]};
-          __builtin_nontemporal_store(o, &yr[ch]);
-        }
-        if constexpr (MODE != kModeNone)
-          quant_store_chunk<D, MODE, MODE == kModeNvfp4>(yb, MODE == kModeFp8 ? 0.0f : rounded_amax<D>(y32), qs,
-                                                         q, bs, row, ch, nchunk, ktiles, otab);
+        yb[k] = D::pack(y32[2 * k], y32[2 * k + 1]);
       }
+      if constexpr (WRITE_Y)
+        if (active) __builtin_nontemporal_store(u32x4{yb[0], yb[1], yb[2], yb[3]}, &yr[ch]);
+      if constexpr (MODE != kModeNone)
+        quant_store_chunk<D, MODE, MODE == kModeNvfp4>(yb, MODE == kModeFp8 ? 0.0f : rounded_amax<D>(y32), qs, q,
+                                                       bs, row, ch, nchunk, ktiles, otab, active);
     }
     if constexpr (!PF)
       if (blk + gridDim.x < M) load_row(blk + gridDim.x);
@@ -361,6 +368,20 @@ hipError_t run_fused(const FusedArgs &a) {
   const u32x4 *w = (const u32x4 *)a.w;
   u32x4 *y = (u32x4 *)a.y;
   uint8_t *q = (uint8_t *)a.q, *bs = (uint8_t *)a.bs;
+  if (a.res_out != nullptr) {
+    // The out-of-place residual exists for the decode step's two-launch
+    // form only: FP8, Gemma, rows of one chunk per thread.
+    if constexpr (MODE == kModeFp8 && RES && GEMMA) {
+      if (vector_path_ok(a, MODE) && aligned_to(a.res_out, 16) && a.H > 512 && chunks_per_thread(a.H) == 1 &&
+          a.M <= kMaxGrid) {
+        const int nchunk = (int)(a.H / kVec);
+        const dim3 block(((nchunk + kWave - 1) / kWave) * kWave);
+        return launch(fused_rows<D, MODE, RES, WY, GEMMA, 1, false, true>, grid, block, 0, a.st, x, res,
+                      (u32x4 *)a.res_out, w, a.scale, a.eps, a.M, nchunk, q, bs, y, ktiles);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   if (vector_path_ok(a, MODE)) {
     const int nchunk = (int)(a.H / kVec);
     if (a.H <= 512 && a.M <= kMaxGrid) {
@@ -379,8 +400,8 @@ hipError_t run_fused(const FusedArgs &a) {
     const int cpt = chunks_per_thread(a.H);
     const int per_thread = (nchunk + cpt - 1) / cpt;
     const dim3 block(((per_thread + kWave - 1) / kWave) * kWave);
-#define GNQ_VEC(C, P, G)                                                                         \
-  return launch(fused_rows<D, MODE, RES, WY, GEMMA, C, P>, G, block, 0, a.st, x, res, w, a.scale, \
+#define GNQ_VEC(C, P, G)                                                                               \
+  return launch(fused_rows<D, MODE, RES, WY, GEMMA, C, P>, G, block, 0, a.st, x, res, nullptr, w, a.scale, \
                 a.eps, a.M, nchunk, q, bs, y, ktiles)
     if (cpt == 1) GNQ_VEC(1, false, grid);
     if (cpt == 2 && prefetch_rows(a.M, a.H)) GNQ_VEC(2, true, dim3(kPrefetchGrid));

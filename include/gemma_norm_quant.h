@@ -237,11 +237,14 @@ nq_status nq_gemm_nvfp4(const void *a, const void *a_scales, const float *a_gs, 
 
 /*
  * nq_gemma_add_rms_norm_quant_gemm_fp8 -- a decode step: the op in static
- * FP8 mode on a few token rows and its consumer linear, in one launch.  The
+ * FP8 mode on a few token rows and its consumer linear.  The
  * `fused_norm_quant` page overlaps the consumer GEMM's launch with the op at
  * small batches (its launch comment: an early trigger, ~2% at up to 128
- * rows); here every GEMM workgroup fetches its weight tile and forms the
- * rows' norm and FP8 codes itself, so no second launch waits on the first.
+ * rows).  Here, for M <= 3, the step is one launch: every GEMM workgroup
+ * fetches its weight tile while it forms the rows' norm and FP8 codes
+ * itself, so no second launch waits on the first.  For 4 <= M <= 8 the
+ * redundant per-workgroup norm costs more than a launch, and the call runs
+ * the op and the decode GEMM as two launches on the stream.
  *
  *   x, weight, eps, scale, M, H, dtype, write_y, q, y
  *              as nq_gemma_add_rms_norm_quant in NQ_MODE_FP8_STATIC; the
@@ -254,8 +257,11 @@ nq_status nq_gemm_nvfp4(const void *a, const void *a_scales, const float *a_gs, 
  *   b, b_scale the linear's weight: (N, H) E4M3FN codes, row-major, and its
  *              static fp32 scale (DEVICE pointer).
  *   N          output features >= 1.
- *   out        (M, N) bf16 = dq(q) dq(b)^T, the result of
- *              nq_gemm_fp8_static(q, scale, b, b_scale) for the same codes.
+ *   out        (M, N) bf16 = dq(q) dq(b)^T: bit-for-bit the result of
+ *              nq_gemm_fp8_static(q, scale, b, b_scale) for 4 <= M <= 8, and
+ *              for M <= 3 where that call runs its 32 x 16 decode tiles
+ *              (H 2048 or 4096, N < 6144); elsewhere within that call's
+ *              error bound (another K split).
  *
  * Shapes: 1 <= M <= 8 and H in {1024, 2048, 4096}; other M, H and N == 0
  * return NQ_EUNSUPPORTED (run the op and the GEMM as two calls); M == 0

@@ -1,14 +1,16 @@
 """The fused decode step (nq_gemma_add_rms_norm_quant_gemm_fp8: the op in
-static FP8 mode on a few rows and its consumer linear in one launch) against
-the two calls it replaces, through the C ABI:
+static FP8 mode on a few rows and its consumer linear; one launch up to 3
+rows, the op and the decode GEMM from 4) against the two calls it replaces,
+through the C ABI:
 
   * the op's outputs (x + residual, FP8 codes, y) bit-for-bit those of
     nq_gemma_add_rms_norm_quant (which the parity tests check against the
     oracle);
   * the linear's bf16 output bit-for-bit that of nq_gemm_fp8_static on the
-    same codes where that call runs the decode GEMM on 32 x 16 tiles (K 2048
-    or 4096, N < 6144: the same K split, MFMA sequence and reduction order),
-    and everywhere within the GEMM bar against the oracle's exact product
+    same codes from 4 rows, and up to 3 rows where that call runs the
+    decode GEMM on 32 x 16 tiles (K 2048 or 4096, N < 6144: the same K
+    split, MFMA sequence and reduction order), and everywhere within the
+    GEMM bar against the oracle's exact product
     (|out - exact| <= 2^-8 |exact| + 2^-10 sum |a b|);
   * x and residual unchanged; nothing written past any output."""
 
@@ -42,6 +44,8 @@ CASES = [
     (torch.bfloat16, 1, 4096, 4096, True, False),
     (torch.bfloat16, 2, 4096, 4096, True, True),
     (torch.bfloat16, 3, 4096, 1000, True, False),
+    (torch.bfloat16, 3, 2048, 4096, True, True),     # the largest one-launch case, 4-row kernel
+    (torch.float16, 3, 1024, 4100, False, True),
     (torch.bfloat16, 4, 4096, 4096, False, True),
     (torch.bfloat16, 8, 4096, 4096, True, True),
     (torch.float16, 5, 2048, 4096, True, False),
@@ -98,7 +102,7 @@ def test_fused_decode_matches_the_two_calls(dt, M, H, N, res, wy):
     if wy:
         assert torch.equal(y.cpu(), y2.cpu())
     got = P.bits16(out)
-    if H in (2048, 4096) and N < 6144:
+    if M >= 4 or (H in (2048, 4096) and N < 6144):
         assert np.array_equal(got, P.bits16(out2))
     else:
         print(f"  output equal to the two-call GEMM: {np.array_equal(got, P.bits16(out2))}", flush=True)

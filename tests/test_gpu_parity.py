@@ -115,6 +115,9 @@ PREFETCH = [
     # dtype, output, M, H, residual, write_y: rows of 4096 < H < 6144 at
     # 2048 <= M <= 16384 loop 1024 workgroups over the rows
     (torch.float16, "nvfp4", 2100, 5120, True, True),
+    (torch.bfloat16, "nvfp4", 2049, 4864, True, True),    # one row past the last full 1024-row span
+    (torch.float16, "mxfp8", 2050, 4224, False, True),    # some threads own one chunk
+    (torch.bfloat16, "fp8", 4096, 5120, True, True),
     (torch.bfloat16, "fp8", 3000, 4160, False, False),
     (torch.float16, "nvfp4", 4096, 6080, False, False),
     (torch.bfloat16, "nvfp4", 16384, 5120, True, False),
