@@ -78,10 +78,10 @@ def _code_only(src):
     return " ".join(src.split())
 
 
-def chunks_per_thread(H):
+def chunks_per_thread(H, res=False):
     """The fused kernel's 8-element chunks per thread (its launcher's rule)."""
     nchunk = H // 8
-    if H <= 4096 or (nchunk <= 1024 and nchunk % 256 == 0):
+    if H <= 4096 or (res and H <= 5120) or (nchunk <= 1024 and nchunk % 256 == 0):
         return 1
     return 2 if nchunk <= 2048 else 4
 
@@ -122,15 +122,16 @@ def nvfp4_kernel(M, N, K):
 
 
 def prefetch_rows(M, H):
-    """Whether the fused kernel loops 1024 workgroups over the rows, loading
-    the next row early (its launcher's rule)."""
+    """Whether the fused kernel loops workgroups over the rows, loading the
+    next row early (its launcher's rule; 1024 workgroups with two chunks per
+    thread, 512 with one)."""
     return 4096 < H < 6144 and 2048 <= M <= 16384
 
 
 def kernel_name(wl):
     return "fused_rows<{},{},{},{},{}{}>".format(
         wl.dtype, wl.mode, "res" if wl.has_residual else "nores",
-        "y" if wl.write_y else "noy", chunks_per_thread(wl.H),
+        "y" if wl.write_y else "noy", chunks_per_thread(wl.H, wl.has_residual),
         ",prefetch" if prefetch_rows(wl.M, wl.H) else "")
 
 
@@ -581,11 +582,11 @@ def decode_main(args):
                           "speedup": round(res["two_launches"] / res["fused"], 3)}), flush=True)
 
 
-def block_threads(H):
+def block_threads(H, res=False):
     """The fused kernel's workgroup size for rows of H elements (its launch
     rule: chunks per thread, rounded up to whole waves)."""
     nchunk = H // 8
-    cpt = chunks_per_thread(H)
+    cpt = chunks_per_thread(H, res)
     return -(-(-(-nchunk // cpt)) // 64) * 64
 
 
@@ -626,7 +627,7 @@ def ceiling_main(args):
         sets = [([torch.ones(M * b // 4, dtype=torch.int32, device=dev) for b in src_rb],
                  [torch.empty(M * b // 4, dtype=torch.int32, device=dev) for b in dst_rb])
                 for _ in range(n_sets)]
-        op_threads = block_threads(wl.H)
+        op_threads = block_threads(wl.H, wl.has_residual)
         forms = [(op_threads, 0, 0)]
         forms += [(op_threads, g, 1) for g in (256, 512, 768, 1024, 1536, 2048) if g < M]
         forms += [(t, 0, 0) for t in (256, 512, 1024) if t != op_threads and 2 * wl.H <= 64 * t]

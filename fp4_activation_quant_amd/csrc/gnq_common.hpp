@@ -266,10 +266,17 @@ __device__ __forceinline__ float mx_elem_scale(uint32_t code) {
 }
 
 // Byte offset of block scale (row m, block b) in the 128x4-tiled layout;
-// ktiles = round_up(H/16, 4) / 4.
+// ktiles = round_up(H/16, 4) / 4.  It is the sum of a part that depends on
+// the row only (its 128-row tile band, its 16-byte line inside the tile and
+// its 4-byte slot in that line) and one that depends on the block only (its
+// 512-byte tile along the row and its byte in the slot), so a row loop can
+// keep the block part in a register and form the row part in scalars.
+__device__ __forceinline__ size_t swz128x4_row(int64_t m, int ktiles) {
+  return (size_t)(m >> 7) * (size_t)ktiles * 512u + (size_t)(m & 31) * 16u + (size_t)((m >> 5) & 3) * 4u;
+}
+__device__ __forceinline__ uint32_t swz128x4_col(int b) { return (uint32_t)(b >> 2) * 512u + (uint32_t)(b & 3); }
 __device__ __forceinline__ size_t swz128x4(int64_t m, int b, int ktiles) {
-  return ((size_t)(m >> 7) * (size_t)ktiles + (size_t)(b >> 2)) * 512u + (size_t)(m & 31) * 16u +
-         (size_t)((m >> 5) & 3) * 4u + (size_t)(b & 3);
+  return swz128x4_row(m, ktiles) + swz128x4_col(b);
 }
 
 // Workgroup -> row for NVFP4.  Workgroups are dispatched round-robin over the
@@ -368,7 +375,7 @@ __device__ __forceinline__ void quant_store_chunk(const uint32_t (&yb)[4], float
     const uint32_t codes = e2m1x8(v);
     uint32_t *qrow = reinterpret_cast<uint32_t *>(q + (size_t)row * (size_t)nchunk * 4);
     if (active) __builtin_nontemporal_store(codes, &qrow[ch]);
-    if (active && (ch & 1) == 0) bs[swz128x4(row, (int)(ch >> 1), ktiles)] = (uint8_t)sc;
+    if (active && (ch & 1) == 0) (bs + swz128x4_row(row, ktiles))[swz128x4_col((int)(ch >> 1))] = (uint8_t)sc;
   } else if constexpr (MODE == kModeMxfp8) {
     amax = fmaxf(amax, dpp<0xB1>(amax));   // lane ^ 1
     amax = fmaxf(amax, dpp<0x4E>(amax));   // lane ^ 2

@@ -331,10 +331,16 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
 // 8192: its waves spread evenly over the 4 SIMDs; measured 1-3.5% faster
 // than two chunks at H = 8192, while the 10-wave workgroups of H = 5120 ran
 // 3-22% slower than 5-wave ones with two chunks); otherwise two up to
-// H = 16384, four up to H = 32768.
-inline int chunks_per_thread(int64_t H) {
+// H = 16384, four up to H = 32768.  The exception: rows with a residual at
+// 4096 < H <= 5120 take one chunk (10-wave workgroups, two per CU on the
+// looping launch: 2.7% faster there than two chunks at 4096 x 5120, with
+// or without y; without a residual, 25% slower).  Every launch form of such
+// a row then uses the same chunk split, so its sum of squares is formed in
+// the same order whatever M is.
+inline int chunks_per_thread(int64_t H, bool res) {
   const int64_t nchunk = H / kVec;
   if (H <= 4096) return 1;
+  if (res && H <= 5120) return 1;
   if (nchunk <= kMaxThreads && nchunk % (4 * kWave) == 0) return 1;
   if (nchunk <= 2 * kMaxThreads) return 2;
   return 4;
@@ -342,12 +348,15 @@ inline int chunks_per_thread(int64_t H) {
 
 inline bool aligned_to(const void *p, uintptr_t n) { return p == nullptr || ((uintptr_t)p % n) == 0; }
 
-// Whether fused_rows runs as 1024 workgroups looping over rows with the next
-// row's loads issued early (PF): rows of 4096 < H < 6144 (two chunks per
-// thread, 5- or 6-wave workgroups) at 2048 <= M <= 16384, where it measured
-// faster than one workgroup per row.  A multiple of 8 workgroups keeps each
-// workgroup's NVFP4 rows on its own XCD.
+// Whether fused_rows runs as workgroups looping over rows with the next
+// row's loads issued early (PF): rows of 4096 < H < 6144 at 2048 <= M <=
+// 16384, where it measured faster than one workgroup per row.  1024
+// workgroups of two chunks per thread (5- or 6-wave, four per CU), 512 of
+// one chunk (10-wave, two per CU; 768 and 384 measured 17% and 13% slower).
+// A multiple of 8 workgroups keeps each workgroup's NVFP4 rows on its own
+// XCD.
 constexpr int kPrefetchGrid = 1024;
+constexpr int kPrefetchGridOneChunk = 512;
 inline bool prefetch_rows(int64_t M, int64_t H) {
   return H > 4096 && H < 6144 && M >= 2048 && M <= 16384;
 }
@@ -372,7 +381,7 @@ hipError_t run_fused(const FusedArgs &a) {
     // The out-of-place residual exists for the decode step's two-launch
     // form only: FP8, Gemma, rows of one chunk per thread.
     if constexpr (MODE == kModeFp8 && RES && GEMMA) {
-      if (vector_path_ok(a, MODE) && aligned_to(a.res_out, 16) && a.H > 512 && chunks_per_thread(a.H) == 1 &&
+      if (vector_path_ok(a, MODE) && aligned_to(a.res_out, 16) && a.H > 512 && chunks_per_thread(a.H, true) == 1 &&
           a.M <= kMaxGrid) {
         const int nchunk = (int)(a.H / kVec);
         const dim3 block(((nchunk + kWave - 1) / kWave) * kWave);
@@ -397,12 +406,13 @@ hipError_t run_fused(const FusedArgs &a) {
       GNQ_SMALL(64);
 #undef GNQ_SMALL
     }
-    const int cpt = chunks_per_thread(a.H);
+    const int cpt = chunks_per_thread(a.H, RES);
     const int per_thread = (nchunk + cpt - 1) / cpt;
     const dim3 block(((per_thread + kWave - 1) / kWave) * kWave);
 #define GNQ_VEC(C, P, G)                                                                               \
   return launch(fused_rows<D, MODE, RES, WY, GEMMA, C, P>, G, block, 0, a.st, x, res, nullptr, w, a.scale, \
                 a.eps, a.M, nchunk, q, bs, y, ktiles)
+    if (cpt == 1 && prefetch_rows(a.M, a.H)) GNQ_VEC(1, true, dim3(kPrefetchGridOneChunk));
     if (cpt == 1) GNQ_VEC(1, false, grid);
     if (cpt == 2 && prefetch_rows(a.M, a.H)) GNQ_VEC(2, true, dim3(kPrefetchGrid));
     if (cpt == 2) GNQ_VEC(2, false, grid);

@@ -72,11 +72,22 @@ def test_kernel_name_follows_the_launchers_chunk_rule(H, cpt):
                                     (4096, 6144, False), (32768, 8192, False), (1, 5120, False)])
 def test_prefetch_rule(M, H, pf):
     """Rows of 4096 < H < 6144 at 2048 <= M <= 16384 take the looping
-    prefetch launch (the fused launcher's prefetch_rows), always with two
-    chunks per thread."""
+    prefetch launch (the fused launcher's prefetch_rows): two chunks per
+    thread without a residual, and with one up to H = 5120."""
     assert bench.prefetch_rows(M, H) == pf
     if pf:
         assert bench.chunks_per_thread(H) == 2
+        assert bench.chunks_per_thread(H, res=True) == (1 if H <= 5120 else 2)
+
+
+@pytest.mark.parametrize("H,cpt", [(4096, 1), (4160, 1), (5120, 1), (5184, 2), (6144, 1), (8192, 1), (16384, 2)])
+def test_residual_rows_chunk_rule(H, cpt):
+    """Rows with a residual at 4096 < H <= 5120 take one chunk per thread in
+    every launch form."""
+    assert bench.chunks_per_thread(H, res=True) == cpt
+    assert bench.kernel_name(WORKLOADS["fp8_res_m4096_h5120_fp16"]).endswith(",1,prefetch>")
+    assert bench.kernel_name(WORKLOADS["nvfp4_nores_m4096_h5120_fp16"]).endswith(",2,prefetch>")
+    assert bench.block_threads(5120, res=True) == 640 and bench.block_threads(5120) == 320
 
 
 @pytest.mark.parametrize("M,N,K,kernel", [

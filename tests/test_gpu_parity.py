@@ -66,7 +66,8 @@ EDGE = [
     (torch.bfloat16, False, 65, 1000, True, False),      # scalar path
     (torch.bfloat16, False, 3, 16384, True, True),       # 2 chunks x 1024 threads
     (torch.bfloat16, False, 5, 20480, True, True),       # 4 chunks per thread
-    (torch.bfloat16, False, 9, 4112, True, True),        # ragged: some threads own 1 chunk
+    (torch.bfloat16, False, 9, 4112, True, True),        # one chunk per thread, a partial last wave
+    (torch.bfloat16, False, 9, 4112, False, True),       # ragged: some threads own 1 chunk
     (torch.bfloat16, False, 33, 48, True, True),         # 6 chunks, one partial wave
     (torch.bfloat16, False, 2, 40000, True, True),       # H > 32768: scalar path
     (torch.float16, False, 257, 4096, True, True),
@@ -77,7 +78,8 @@ EDGE = [
     (torch.bfloat16, True, 130, 16384, True, True),
     (torch.bfloat16, True, 3, 32768, True, True),        # 4 chunks x 1024 threads
     (torch.float16, True, 3, 32832, True, True),         # NVFP4 beyond 32768: scalar path
-    (torch.bfloat16, True, 17, 4160, True, True),        # ragged 2-chunk split
+    (torch.bfloat16, True, 17, 4160, True, True),        # one chunk per thread (residual, H <= 5120)
+    (torch.bfloat16, True, 17, 4160, False, True),       # ragged 2-chunk split
     (torch.bfloat16, True, 2100, 256, True, True),       # XCD row map: 2 spans + ragged tail
     (torch.float16, True, 3072, 64, False, True),        # XCD row map: exact spans
     (torch.float16, True, 200, 5120, True, True),
