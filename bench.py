@@ -410,32 +410,9 @@ def gemm_main(args):
         "launch": "graph", "buffer_sets": n_sets, "kernel_ms": round(kern_ms, 5),
         "roofline": dict(kernel=kernel, **roof),
     }
-    if not args.no_library and not nv:
-        out["library"] = library_gemm(sets[0], mx, M, N, K, args.steps, args.warmup, stream)
     out["cpu_baseline"] = (None if args.no_cpu_baseline else
                            gemm_cpu_baseline(gw, a, sa, b, sb, args.cpu_seconds))
     print(json.dumps(out), flush=True)
-
-
-def library_gemm(st, mx, M, N, K, steps, warmup, stream):
-    """Context, not the product: the same operands through torch._scaled_mm
-    (hipBLASLt), per-tensor FP8 or E8M0 block scales, timed the same way.
-    Only the time is reported (for the block-scaled case the library's own
-    scale layout is not checked here)."""
-    import torch
-    a = st["a"].view(torch.float8_e4m3fn)
-    b = st["b"].view(torch.float8_e4m3fn)
-    if mx:
-        sa, sb = st["sa"].view(torch.float8_e8m0fnu), st["sb"].view(torch.float8_e8m0fnu)
-    else:
-        sa, sb = st["sa"].reshape(()), st["sb"].reshape(())
-    try:
-        _, ms = _time_graph(lambda i: torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16),
-                            steps, warmup, stream)
-    except Exception as ex:   # the library may not take this configuration
-        return {"name": "torch._scaled_mm (hipBLASLt)", "error": str(ex).splitlines()[0][:160]}
-    return {"name": "torch._scaled_mm (hipBLASLt)", "kernel_ms": round(ms, 5),
-            "TFLOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
 
 
 def chain_main(args):
@@ -662,8 +639,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-library", action="store_true",
-                    help="--gemm: skip timing torch._scaled_mm on the same operands")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused chain instead: add + norm (y to HBM), then the "
