@@ -246,14 +246,15 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA
 
 
 def _time_graph(launch, steps, warmup, stream):
-    """Warm up, capture `steps` launches in one HIP graph, replay once;
-    returns (wall seconds, kernel ms per launch from events on `stream`)."""
-    t = _time_graphs(launch, steps, warmup, stream)
-    return t["wall_s"], t["span_ms"]
+    """Warm up, capture `steps` (and 2 * `steps`) launches in HIP graphs and
+    time their replays (_time_graphs); returns (wall seconds of the
+    `steps`-launch replay, kernel ms per launch: the differenced figure)."""
+    t = _time_graphs(launch, steps, warmup, stream, differenced=True)
+    return t["wall_s"], t["diff_ms"]
 
 
-PAD_BYTES = 1 << 30        # device buffer filled ahead of each event-timed replay
-PAD_FILLS = 6              # ~1.5 ms of device work
+PAD_BYTES = 1 << 30        # device buffer read ahead of each event-timed replay
+PAD_READS = 6              # ~1.5 ms of device work
 
 
 def _time_graphs(launch, steps, warmup, stream, differenced=False):
@@ -264,15 +265,19 @@ def _time_graphs(launch, steps, warmup, stream, differenced=False):
       wall_s    host wall time of a replay of the `steps` launches,
                 synchronised on both sides (the bench's timed region);
       span_ms   event span of a replay of the `steps` launches / steps.  The
-                replay is queued behind ~1.5 ms of device work (fills of a
-                1 GiB pad buffer) and its start event recorded after that
-                work, so every launch of the graph is queued before the
-                first one runs: the span holds the kernels back to back,
-                with no gap where the device has caught up with the host's
-                submission of the graph (such gaps, 50-80 us each a few
-                dozen launches into a replay, were seen under the profiler);
-      diff_ms   (span of the 2 * steps replay - span_ms * steps) / steps, a
-                cross-check: with no submission gaps the two agree.
+                replay is queued behind ~1.5 ms of device work (reads of a
+                1 GiB pad buffer: reads, so no dirty lines are left to be
+                written back while the replay runs) and its start event
+                recorded after that work, so every launch of the graph is
+                queued before the first one runs: the span holds the
+                kernels back to back, with no gap where the device has
+                caught up with the host's submission of the graph (such
+                gaps, 50-80 us each a few dozen launches into a replay, were
+                seen under the profiler);
+      diff_ms   (span of the 2 * steps replay - span of the steps replay) /
+                steps, both queued the same way: the per-launch time with
+                any fixed cost of a replay cancelled, so it does not depend
+                on `steps`.
     """
     import torch
     with torch.cuda.stream(stream):
@@ -294,14 +299,15 @@ def _time_graphs(launch, steps, warmup, stream, differenced=False):
         graphs[0].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pad = torch.empty(PAD_BYTES // 4, dtype=torch.int32, device=stream.device)
+    pad = torch.zeros(PAD_BYTES // 4, dtype=torch.int32, device=stream.device)
+    torch.cuda.synchronize()
     spans = []
     for k, g in enumerate(graphs):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
-            for _ in range(PAD_FILLS):
-                pad.fill_(k)
+            for _ in range(PAD_READS):
+                torch.sum(pad, dtype=torch.int64)
             e0.record(stream)
             g.replay()
             e1.record(stream)
@@ -528,8 +534,8 @@ def decode_main(args):
     linear as one fused launch against the two launches (the op, then the
     decode GEMM), per row count.  Weights rotate through >= 2 GiB, so each
     step fetches its weight from HBM as a layer of a real decode step does.
-    One JSON line per M: us per step (graph replay queued behind device
-    work; the differenced figure beside it as a check)."""
+    One JSON line per M: us per step (differenced graph replays queued
+    behind device work; the K-launch span / K beside it as a check)."""
     import numpy as np
     import torch
     from fp4_activation_quant_amd import _lib, ops
@@ -566,14 +572,14 @@ def decode_main(args):
                     ops.gemm_fp8_static(q, s, b, bs, out=out)
             stream = torch.cuda.Stream(device=dev)
             t = _time_graphs(launch, args.steps, args.warmup, stream, differenced=True)
-            res[path] = t["span_ms"] * 1e3
-            res[path + "_differenced"] = t["diff_ms"] * 1e3
+            res[path] = t["diff_ms"] * 1e3
+            res[path + "_span"] = t["span_ms"] * 1e3
         print(json.dumps({"metric": "decode step: add + Gemma RMSNorm + FP8 quant + FP8 linear, us per step",
                           "M": M, "H": H, "N": N, "weight_sets": n_sets, "steps": args.steps,
                           "fused_call_runs": "one launch" if M <= 3 else "op + decode GEMM",
                           "fused_us": round(res["fused"], 3), "two_launches_us": round(res["two_launches"], 3),
-                          "fused_differenced_us": round(res["fused_differenced"], 3),
-                          "two_launches_differenced_us": round(res["two_launches_differenced"], 3),
+                          "fused_span_us": round(res["fused_span"], 3),
+                          "two_launches_span_us": round(res["two_launches_span"], 3),
                           "speedup": round(res["two_launches"] / res["fused"], 3)}), flush=True)
 
 
@@ -636,10 +642,10 @@ def ceiling_main(args):
                 if st != _lib.NQ_OK:
                     raise RuntimeError(f"nq_traffic_probe: status {st}")
             t = _time_graphs(launch, args.steps, args.warmup, stream, differenced=True)
-            us = t["span_ms"] * 1e3
+            us = t["diff_ms"] * 1e3
             results.append({"threads": threads, "grid": grid, "prefetch": pf, "us": round(us, 3),
                             "GBps": round(per_launch / (us * 1e-6) / 1e9, 1),
-                            "differenced_us": round(t["diff_ms"] * 1e3, 3)})
+                            "span_us": round(t["span_ms"] * 1e3, 3)})
         best = max(results, key=lambda r: r["GBps"])
         print(json.dumps({"ceiling": name, "bytes_per_launch": per_launch, "rows": M,
                           "src_row_bytes": src_rb, "dst_row_bytes": dst_rb, "buffer_sets": n_sets,
@@ -772,14 +778,14 @@ def main():
           f"{'graph' if (not args.eager) else 'eager'})", file=sys.stderr, flush=True)
     if not args.eager:
         # The K launches captured once as a HIP graph and replayed: launch
-        # overhead off the critical path.  Kernel time per launch = event
-        # span of a K-launch replay queued behind device work / K (checked
-        # against the 2K-launch replay); the host-timed K-launch replay is
-        # the timed region of `value`.
+        # overhead off the critical path.  Kernel time per launch = (span of
+        # a 2K-launch replay - span of the K-launch replay) / K, both queued
+        # behind device work (the K-launch span / K beside it as a check);
+        # the host-timed K-launch replay is the timed region of `value`.
         t = _time_graphs(launch, args.steps, args.warmup, stream, differenced=True)
         wall = t["wall_s"]
-        kern_ms = [t["span_ms"]]
-        diff_ms = t["diff_ms"]
+        kern_ms = [t["diff_ms"]]
+        span_ms = t["span_ms"]
     else:
         with torch.cuda.stream(stream):
             for i in range(args.warmup):
@@ -797,7 +803,7 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         kern_ms = [a.elapsed_time(b) for a, b in ev]
-        diff_ms = None
+        span_ms = None
     kern_ms.sort()
     avg_ms = sum(kern_ms) / len(kern_ms)
     med_ms = kern_ms[len(kern_ms) // 2]
@@ -828,10 +834,10 @@ def main():
         "launch": "graph" if (not args.eager) else "eager",
         "path": "unfused (2 kernels)" if args.unfused else "fused",
         "buffer_sets": n_sets,
-        "kernel_ms": ({"avg": round(avg_ms, 5), "differenced": round(diff_ms, 5),
-                       "method": "event span of a K-launch graph replay queued behind device work / K; "
-                                 "differenced = (span of a 2K-launch replay - span of the K-launch replay) / K"}
-                      if diff_ms is not None else
+        "kernel_ms": ({"avg": round(avg_ms, 5), "span_per_launch": round(span_ms, 5),
+                       "method": "(span of a 2K-launch graph replay - span of a K-launch replay) / K, each "
+                                 "replay queued behind device work; span_per_launch = the K-launch span / K"}
+                      if span_ms is not None else
                       {"avg": round(avg_ms, 5), "median": round(med_ms, 5), "min": round(kern_ms[0], 5),
                        "max": round(kern_ms[-1], 5), "method": "event pair per eager launch"}),
         "roofline": {"bound": "hbm", "kernel": kernel_name(wl), "achieved": round(achieved, 2),
