@@ -267,6 +267,21 @@ def compare(gpu, x, r, w, eps, scale, rows, y_gpu=None, threads=None):
     return rep
 
 
+# Whole-tensor figures of the full-size workload comparisons, printed in the
+# test run's terminal summary (tests/conftest.py).
+SUMMARY = []
+
+
+def record(name, rep):
+    """Keep one line of a passing full-size comparison for the run's summary."""
+    parts = [f"{rep['rows']} rows", f"y differs {rep.get('y_diff_fraction', 0.0):.2e} (max {rep.get('y_max_ulp', 0)} ulp)",
+             f"codes differ {rep['code_diff_fraction']:.2e} (max {rep['code_max_step']} step)"]
+    if "scale_match_fraction" in rep:
+        parts.append(f"block scales match {rep['scale_match_fraction']:.6f}")
+    parts.append(f"residual mismatches {rep.get('residual_mismatch', 0)}")
+    SUMMARY.append(f"{name}: " + ", ".join(parts))
+
+
 def check(rep):
     """Raise AssertionError listing every bar the report misses."""
     bad = []

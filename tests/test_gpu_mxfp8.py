@@ -49,7 +49,8 @@ def test_mxfp8_workload_parity(name):
     wl = WORKLOADS[name]
     print(f"mxfp8 workload {name}", flush=True)
     x, r, w = make_inputs(wl)
-    _run_and_compare(x, r, w, wl.eps, wl.write_y, rows=P.all_rows(wl.M))
+    rep, _ = _run_and_compare(x, r, w, wl.eps, wl.write_y, rows=P.all_rows(wl.M))
+    P.record(f"{name} (as MXFP8)", rep)
 
 
 EDGE = [

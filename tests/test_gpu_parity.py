@@ -53,8 +53,9 @@ def test_workload_parity(name):
     wl = WORKLOADS[name]
     print(f"workload {name}", flush=True)
     x, r, w = make_inputs(wl)
-    _run_and_compare(x, r, w, wl.eps, load_scale(wl), wl.nvfp4, wl.write_y, rows=P.all_rows(wl.M),
-                     mxfp8=wl.mode == "mxfp8")
+    rep, _ = _run_and_compare(x, r, w, wl.eps, load_scale(wl), wl.nvfp4, wl.write_y, rows=P.all_rows(wl.M),
+                              mxfp8=wl.mode == "mxfp8")
+    P.record(name, rep)
 
 
 EDGE = [
