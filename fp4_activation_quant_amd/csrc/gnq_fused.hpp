@@ -39,7 +39,10 @@
 namespace gnq {
 
 // RES_OUT: the updated residual goes to res_out instead of back into res.
-template <class D, int MODE, bool HAS_RES, bool WRITE_Y, bool GEMMA, int CPT, bool PF, bool RES_OUT = false>
+// COVER: the launch guarantees nchunk == CPT * blockDim.x (every thread's
+// chunks lie inside the row), so no load, sum or store is guarded.
+template <class D, int MODE, bool HAS_RES, bool WRITE_Y, bool GEMMA, int CPT, bool PF, bool RES_OUT = false,
+          bool COVER = false>
 __global__ void __launch_bounds__(kMaxThreads)
 fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, u32x4 *__restrict__ res_out,
            const u32x4 *__restrict__ w,
@@ -63,7 +66,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, u32x4 *__restri
     const size_t rb = (size_t)rw * (size_t)nchunk;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const unsigned ch = min(tid + c * nthr, nch - 1);
+      const unsigned ch = COVER ? tid + c * nthr : min(tid + c * nthr, nch - 1);
       xa[c] = __builtin_nontemporal_load(&x[rb + ch]);
       if constexpr (HAS_RES) ra[c] = __builtin_nontemporal_load(&res[rb + ch]);
     }
@@ -73,7 +76,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, u32x4 *__restri
   // The weight and the scale come from L2, once per workgroup; the scale's
   // reciprocal is formed while the first row's loads are in flight.
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) wa[c] = w[min(tid + c * nthr, nch - 1)];
+  for (int c = 0; c < CPT; ++c) wa[c] = w[COVER ? tid + c * nthr : min(tid + c * nthr, nch - 1)];
   const QuantScale qs = quant_scale(mode_reads_scale(MODE) ? *scale_ptr : 1.0f, MODE == kModeFp8);
   // NVFP4: the multiplier table, read after the first row's barrier.
   if constexpr (MODE == kModeNvfp4) nvfp4_fill_table(otab, qs.s, tid, nthr);
@@ -105,7 +108,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, u32x4 *__restri
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           hb[c][k] = D::pack(D::lo(xa[c][k]) + D::lo(ra[c][k]), D::hi(xa[c][k]) + D::hi(ra[c][k]));
-        if (ch < nch) {
+        if (COVER || ch < nch) {
           const u32x4 o = {hb[c][0], hb[c][1], hb[c][2], hb[c][3]};
           __builtin_nontemporal_store(o, &rr[ch]);
         }
@@ -122,7 +125,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, u32x4 *__restri
         sc = __builtin_fmaf(a, a, sc);
         sc = __builtin_fmaf(b, b, sc);
       }
-      ss = ch < nch ? sc : ss;
+      ss = (COVER || ch < nch) ? sc : ss;
     }
     // x and residual are dead once h is formed: with PF the next row's loads
     // go out now, behind this row's reduction and stores.
@@ -142,7 +145,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, u32x4 *__restri
       // conversions of h from their FMAs (measured: 3% faster there, 1%
       // slower without PF, where the threads past the row skip it).
       const unsigned ch = tid + c * nthr;
-      const bool active = ch < nch;
+      const bool active = COVER || ch < nch;
       if (!PF && !active) continue;
       // y = RN(t * (1 + w)) (Gemma) or RN(t * w), t = h * rstd (as
       // fma(h, rstd, -0): the same rounding); the quant reads the rounded y.
@@ -414,6 +417,15 @@ hipError_t run_fused(const FusedArgs &a) {
                 a.eps, a.M, nchunk, q, bs, y, ktiles)
     if (cpt == 1 && prefetch_rows(a.M, a.H)) GNQ_VEC(1, true, dim3(kPrefetchGridOneChunk));
     if (cpt == 1) GNQ_VEC(1, false, grid);
+    if constexpr (!RES) {
+      // Residual-free rows whose chunks the threads cover exactly (H = 5120
+      // here) drop every per-chunk guard: 4-4.5% faster at 4096 x 5120 fp16
+      // (with a residual the same form measured 5% slower, so it is not
+      // used there).
+      if (cpt == 2 && prefetch_rows(a.M, a.H) && (int)block.x * 2 == nchunk)
+        return launch(fused_rows<D, MODE, RES, WY, GEMMA, 2, true, false, true>, dim3(kPrefetchGrid), block, 0,
+                      a.st, x, res, nullptr, w, a.scale, a.eps, a.M, nchunk, q, bs, y, ktiles);
+    }
     if (cpt == 2 && prefetch_rows(a.M, a.H)) GNQ_VEC(2, true, dim3(kPrefetchGrid));
     if (cpt == 2) GNQ_VEC(2, false, grid);
     GNQ_VEC(4, false, grid);

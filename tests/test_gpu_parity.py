@@ -121,6 +121,8 @@ PREFETCH = [
     (torch.bfloat16, "nvfp4", 2049, 4864, True, True),    # one row past the last full 1024-row span
     (torch.float16, "mxfp8", 2050, 4224, False, True),    # some threads own one chunk
     (torch.bfloat16, "fp8", 4096, 5120, True, True),
+    (torch.bfloat16, "mxfp8", 2100, 5120, False, True),  # no residual, threads covering the row: no guards
+    (torch.float16, "nvfp4", 16384, 5120, False, False),
     (torch.bfloat16, "fp8", 3000, 4160, False, False),
     (torch.float16, "nvfp4", 4096, 6080, False, False),
     (torch.bfloat16, "nvfp4", 16384, 5120, True, False),
