@@ -324,13 +324,13 @@ def gemm_fp8_static(a, a_scale, b, b_scale, out=None):
 
 def gemma_add_rms_norm_quant_gemm_fp8_out(x, residual, residual_out, weight, eps, scale, b, b_scale, q, y,
                                           out):
-    """A decode step in one launch: the op in static FP8 mode (codes into
-    ``q``, ``y`` if given, x + ``residual`` into ``residual_out``) and the
-    consumer linear ``out`` (M, N) bf16 = dq(q) @ dq(b)^T of the FP8 weight
-    ``b`` (N, H) with its float32 scale.  For 1 <= M <= 8 and H in {1024,
-    2048, 4096}; other shapes raise (call the op and ``gemm_fp8_static``).
-    The residual is not updated in place (``residual_out`` is its own
-    buffer)."""
+    """A decode step: the op in static FP8 mode (codes into ``q``, ``y`` if
+    given, x + ``residual`` into ``residual_out``) and the consumer linear
+    ``out`` (M, N) bf16 = dq(q) @ dq(b)^T of the FP8 weight ``b`` (N, H)
+    with its float32 scale; one launch up to 3 rows, the op and the decode
+    GEMM as two launches from 4.  For 1 <= M <= 8 and H in {1024, 2048,
+    4096}; other shapes raise (call the op and ``gemm_fp8_static``).  The
+    residual is not updated in place (``residual_out`` is its own buffer)."""
     _validate(x, residual, weight, scale)
     M, H = x.shape
     dev = x.device

@@ -116,3 +116,50 @@ def test_graph_op_and_consumer_gemm_replays_match_eager(fmt, M, H, N):
         torch.cuda.synchronize()
         assert torch.equal(outg, oute), rep
         assert torch.equal(rg, re), rep
+
+
+@pytest.mark.parametrize("M", [2, 6])
+def test_graph_decode_step_replays_match_eager(M):
+    """The decode step (one launch at M = 2, the op and the decode GEMM at
+    M = 6) captured in a graph: every replay, with eager work between them,
+    reproduces the eager outputs bit for bit."""
+    print(f"graph decode step M={M}", flush=True)
+    import numpy as np
+    dev = torch.device("cuda")
+    H = N = 4096
+    g0 = torch.Generator().manual_seed(4200 + M)
+    x = torch.randn(M, H, generator=g0).to(torch.bfloat16).to(dev)
+    r = (torch.randn(M, H, generator=g0) * 2).to(torch.bfloat16).to(dev)
+    w = (torch.randn(H, generator=g0) * 0.1).to(torch.bfloat16).to(dev)
+    s = torch.tensor([0.02], dtype=torch.float32, device=dev)
+    bs = torch.tensor([0.004], dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(M)
+    b = torch.from_numpy((rng.integers(0, 8, size=(N, H)) | (rng.integers(0, 8, size=(N, H)) << 3)
+                          | (rng.integers(0, 2, size=(N, H)) << 7)).astype(np.uint8)).to(dev)
+
+    def outputs():
+        return (torch.full((M, H), 0x5A5A, dtype=torch.int16, device=dev).view(torch.bfloat16),
+                torch.full((M, H), 0x5A, dtype=torch.uint8, device=dev),
+                torch.zeros((M, H), dtype=torch.bfloat16, device=dev),
+                torch.zeros((M, N), dtype=torch.bfloat16, device=dev))
+
+    ro, q, y, out = outputs()
+    ops.gemma_add_rms_norm_quant_gemm_fp8_out(x, r, ro, w, 1e-6, s, b, bs, q, y, out)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (ro, q, y, out)]
+
+    rog, qg, yg, outg = outputs()
+    st = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=st):
+        ops.gemma_add_rms_norm_quant_gemm_fp8_out(x, r, rog, w, 1e-6, s, b, bs, qg, yg, outg)
+    for rep in range(3):
+        for t in (rog, yg, outg):
+            t.zero_()
+        qg.fill_(0x5A)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip((rog, qg, yg, outg), want):
+            assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), rep
