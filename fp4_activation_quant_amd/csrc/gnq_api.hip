@@ -51,6 +51,23 @@ __global__ void convert_probe(int kind, const uint32_t *__restrict__ in, int64_t
       out[i] = (uint8_t)(e2m1x8(v) & 0xfu);
       break;
     }
+    case 10:
+    case 11: {
+      // static FP8 quant of the 8-element chunk i / 8 by the vector routine
+      // (n % 8 == 0): y = low 16 bits of patterns i & ~7 .. (i & ~7) + 7
+      if (i % 8) break;
+      uint32_t yb[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) yb[k] = (in[i + 2 * k] & 0xffffu) | (in[i + 2 * k + 1] << 16);
+      const u32x2 c = kind == 10 ? fp8_codes<Bf16>(yb, quant_scale(param, true))
+                                 : fp8_codes<Fp16>(yb, quant_scale(param, true));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        out[i + k] = (uint8_t)(c[0] >> (8 * k));
+        out[i + 4 + k] = (uint8_t)(c[1] >> (8 * k));
+      }
+      break;
+    }
     default: break;
   }
 }

@@ -46,6 +46,7 @@ constexpr bool mode_reads_scale(int mode) { return mode == kModeFp8 || mode == k
 // Activation dtypes: unpack two values from a 32-bit word, pack two fp32
 // values with round-to-nearest-even.
 struct Bf16 {
+  static constexpr bool kF16 = false;
   static __device__ __forceinline__ float lo(uint32_t p) { return __uint_as_float(p << 16); }
   static __device__ __forceinline__ float hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
   // fl32(v * b + c), one rounding, for the low / high value v of p.
@@ -58,6 +59,7 @@ struct Bf16 {
 };
 
 struct Fp16 {
+  static constexpr bool kF16 = true;
   static __device__ __forceinline__ float lo(uint32_t p) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xffffu));
   }
@@ -82,6 +84,14 @@ struct Fp16 {
     f32x2 v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
+  // Both values of p clamped to [-L, L], L a non-negative fp16 held in both
+  // halves of l2 (two packed instructions for two values).
+  static __device__ __forceinline__ uint32_t clamp2(uint32_t p, uint32_t l2) {
+    uint32_t t, r;
+    asm("v_pk_max_f16 %0, %1, %2 neg_lo:[0,1] neg_hi:[0,1]" : "=v"(t) : "v"(p), "v"(l2));
+    asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(t), "v"(l2));
+    return r;
+  }
 };
 
 // ----------------------------------------------------------------------------
@@ -99,6 +109,16 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
+// e4m3x4 without the clamp: exact for |v| <= 464 (values in (448, 464]
+// round to the saturated code, beyond 464 the conversion gives NaN).  (The first
+// conversion's untouched half is overwritten by the second, so it starts
+// from a's bits rather than a zero that would cost a move.)
+__device__ __forceinline__ uint32_t e4m3x4_near(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 __device__ __forceinline__ uint32_t e4m3_one(float a) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clampf(a, kE4M3Max), 0.0f, 0, false) & 0xffu;
 }
@@ -108,7 +128,8 @@ __device__ __forceinline__ uint32_t e4m3_one(float a) {
 // (including infinities) to 6 by itself, so no clamp precedes it; the
 // exhaustive probe tests check it against clamp-then-round.
 __device__ __forceinline__ uint32_t e2m1x8(const float *v) {
-  uint32_t w = 0;
+  // every byte of w is written below, so it may start from any bits
+  uint32_t w = __builtin_bit_cast(uint32_t, v[0]);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
@@ -118,9 +139,11 @@ __device__ __forceinline__ uint32_t e2m1x8(const float *v) {
 
 // The quant step's per-tensor constants, formed once per thread: the
 // scale s (FP8: the static scale; NVFP4: the global scale), r = fl32(1 / s)
-// and, for FP8, lim = fl32(1024 s) (+inf when that overflows).
+// and, for FP8, the clamp bound lim = fl32(456 s) of div_by_scale.
 struct QuantScale {
   float s, r, lim, nz;
+  uint32_t lim2;   // static FP8: fl32(456 s) rounded to fp16, in both halves
+  bool lim2_ok;    // 2^-22 <= s <= 143: lim2 is a finite normal fp16
 };
 
 __device__ __forceinline__ QuantScale quant_scale(float s, bool fp8);
@@ -132,10 +155,13 @@ __device__ __forceinline__ QuantScale quant_scale(float s, bool fp8);
 // rounded quotient (Markstein's theorem: reciprocal within half an ulp,
 // quotient within one ulp, exact remainder).  The remainder is exact for
 // |y| >= 2^-103, i.e. for every scale >= 2^-90 wherever the FP8 code is not
-// zero.  y is first clamped to +-fl(1024 s): quotients beyond +-1024
-// saturate to +-448 either way, and every intermediate stays finite (one
-// clamp instead of one per step).  The remainder is formed as q*s - y and
-// subtracted, so a zero quotient keeps the sign of y.
+// zero.  y is first clamped to +-L, L = fl(456 s): a y beyond L has
+// |y| / s > 455 and the saturated code, and so does +-L itself, whose
+// quotient lies within 0.01 of 456.  So every quotient stays within +-464,
+// where the conversion needs no clamp of its own (e4m3x4_near), and every
+// intermediate stays finite (one clamp instead of one per step).  The
+// remainder is formed as q*s - y and subtracted, so a zero quotient keeps
+// the sign of y.  (A NaN y, outside the contract, clamps to -L.)
 __device__ __forceinline__ float div_by_scale(float y, const QuantScale &d) {
   y = clampf(y, d.lim);
   float q = y * d.r;
@@ -143,17 +169,69 @@ __device__ __forceinline__ float div_by_scale(float y, const QuantScale &d) {
   return __builtin_fmaf(-__builtin_fmaf(q, d.s, -y), d.r, q);
 }
 
+// Steps of the division above for the fp16 value in half H of a word c:
+// y is read from its half by v_fma_mix_f32 each time it enters (its
+// widening is exact), so it needs no separate conversion.
+template <int H>
+__device__ __forceinline__ float mix_mul_f16(uint32_t c, float r, float nz) {   // fl(y r + nz)
+  float q;
+  if constexpr (H == 0)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(q) : "v"(c), "v"(r), "v"(nz));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(q) : "v"(c), "v"(r), "v"(nz));
+  return q;
+}
+template <int H>
+__device__ __forceinline__ float mix_rem_f16(float q, float s, uint32_t c) {   // fl(q s - y)
+  float e;
+  if constexpr (H == 0)
+    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(e) : "v"(q), "v"(s), "v"(c));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(e) : "v"(q), "v"(s), "v"(c));
+  return e;
+}
+
 // Static FP8 codes of one 8-element chunk of rounded y (four words of two
-// activation-dtype values), little-endian.
+// activation-dtype values), little-endian.  fp16 y are clamped in pairs in
+// their own format (lim2, the fp16 rounding of L: within (455.7 s,
+// 456.3 s), so the argument above holds unchanged) where that bound is a
+// finite normal fp16; other scales and bf16 y take the fp32 clamp.
 template <class D>
 __device__ __forceinline__ u32x2 fp8_codes(const uint32_t (&yb)[4], const QuantScale &d) {
   float v[kVec];
+  if constexpr (D::kF16) {
+    if (d.lim2_ok) {
+      // div_by_scale's steps, each over all eight values before the next
+      // (the inline assembly keeps its order, so this order is the issue
+      // order: eight independent instructions per step)
+      uint32_t c[4];
+      float e[kVec];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[k] = Fp16::clamp2(yb[k], d.lim2);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = mix_mul_f16<0>(c[k], d.r, d.nz);
+        v[2 * k + 1] = mix_mul_f16<1>(c[k], d.r, d.nz);
+      }
+#pragma unroll
+      for (int step = 0; step < 2; ++step) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          e[2 * k] = mix_rem_f16<0>(v[2 * k], d.s, c[k]);
+          e[2 * k + 1] = mix_rem_f16<1>(v[2 * k + 1], d.s, c[k]);
+        }
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) v[i] = __builtin_fmaf(-e[i], d.r, v[i]);
+      }
+      return u32x2{e4m3x4_near(v[0], v[1], v[2], v[3]), e4m3x4_near(v[4], v[5], v[6], v[7])};
+    }
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     v[2 * k] = div_by_scale(D::lo(yb[k]), d);
     v[2 * k + 1] = div_by_scale(D::hi(yb[k]), d);
   }
-  return u32x2{e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
+  return u32x2{e4m3x4_near(v[0], v[1], v[2], v[3]), e4m3x4_near(v[4], v[5], v[6], v[7])};
 }
 
 // -0.0 in a register the optimizer cannot see into.  fma(a, b, -0) is the
@@ -168,7 +246,9 @@ __device__ __forceinline__ float opaque_neg_zero() {
 }
 
 __device__ __forceinline__ QuantScale quant_scale(float s, bool fp8) {
-  return QuantScale{s, fp8 ? 1.0f / s : 0.0f, fp8 ? 1024.0f * s : 0.0f, opaque_neg_zero()};
+  const float lim = fp8 ? 456.0f * s : 0.0f;
+  return QuantScale{s, fp8 ? 1.0f / s : 0.0f, lim, opaque_neg_zero(), Fp16::pack(lim, lim),
+                    fp8 && s >= 0x1p-22f && s <= 143.0f};
 }
 
 // fl32(y * o) for each value of a chunk (nz: opaque_neg_zero()).
@@ -201,24 +281,23 @@ __device__ __forceinline__ float rounded_amax(const float (&y32)[kVec]) {
   return D::lo(D::pack(a, 0.0f));
 }
 
-// fl32(a / 6), correctly rounded, for a block amax a >= 0: the reciprocal
-// r = fl32(1/6) and two remainder corrections, as in div_by_scale (q0 within
-// 1.5 ulp, the first correction within 1 ulp, the second exact; the
-// remainder a - 6q is exact).  5 VALU instructions instead of the ~10 of
-// an IEEE division; the probe tests compare the block-scale code over every
-// 16-bit amax (the only values a block of rounded y can have) and over
-// tie-heavy fp32 patterns against the oracle's division.
+// fl32(a / 6), correctly rounded, for a block amax a >= 0 that a bf16 or
+// an fp16 holds (every amax the kernels pass: the max of a block of
+// rounded y): the reciprocal r = fl32(1/6), q0 = fl(a r) and one remainder
+// correction q0 + (a - 6 q0) r (FMA, one rounding).  For those 60032
+// values one correction is exact (checked in exact rational arithmetic by
+// tests/test_host_arith.py; for arbitrary fp32 a a second one would be
+// needed).  3 VALU instructions instead of the ~10 of an IEEE division.
 __device__ __forceinline__ float div6(float a) {
   const float r = 1.0f / kE2M1Max;
-  float q = a * r;
-  q = __builtin_fmaf(-__builtin_fmaf(q, kE2M1Max, -a), r, q);
+  const float q = a * r;
   return __builtin_fmaf(-__builtin_fmaf(q, kE2M1Max, -a), r, q);
 }
 
 // NVFP4 block scale: S = E4M3(min(gs * (amax / 6), 448)).
 __device__ __forceinline__ uint32_t nvfp4_scale_code(float amax, float gs) {
   const float u = fminf(gs * div6(amax), kE4M3Max);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false) & 0xffu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, __builtin_bit_cast(int, u), false) & 0xffu;
 }
 
 // Element multiplier o = gs / decode(S), 0 for a zero scale.
@@ -303,6 +382,13 @@ __device__ __forceinline__ float dpp(float v) {
 // Value of the neighbouring lane (lane ^ 1): DPP quad_perm [1, 0, 3, 2].
 __device__ __forceinline__ float dpp_swap_adjacent(float v) { return dpp<0xB1>(v); }
 
+// max of two non-negative floats (block amaxes) as integers: their bit
+// patterns order as their values, and the integer max needs none of the
+// NaN quieting fmaxf adds under IEEE rules.
+__device__ __forceinline__ float max_nonneg(float a, float b) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)));
+}
+
 // Sum over the 64 lanes of a wave (all lanes active), returned to every lane:
 // DPP exchanges inside each 16-lane row (lane ^ 1, lane ^ 2, 8-lane mirror,
 // 16-lane mirror), then the four row totals via readlane.
@@ -365,7 +451,7 @@ __device__ __forceinline__ void quant_store_chunk(const uint32_t (&yb)[4], float
                                                   int64_t row, unsigned ch, int nchunk, int ktiles,
                                                   const float *otab = nullptr, bool active = true) {
   if constexpr (MODE == kModeNvfp4) {
-    amax = fmaxf(amax, dpp_swap_adjacent(amax));
+    amax = max_nonneg(amax, dpp_swap_adjacent(amax));
     const uint32_t sc = nvfp4_scale_code(amax, qs.s);
     float o;
     if constexpr (TABLE) o = otab[sc & (kNvfp4Codes - 1)];
@@ -377,8 +463,8 @@ __device__ __forceinline__ void quant_store_chunk(const uint32_t (&yb)[4], float
     if (active) __builtin_nontemporal_store(codes, &qrow[ch]);
     if (active && (ch & 1) == 0) (bs + swz128x4_row(row, ktiles))[swz128x4_col((int)(ch >> 1))] = (uint8_t)sc;
   } else if constexpr (MODE == kModeMxfp8) {
-    amax = fmaxf(amax, dpp<0xB1>(amax));   // lane ^ 1
-    amax = fmaxf(amax, dpp<0x4E>(amax));   // lane ^ 2
+    amax = max_nonneg(amax, dpp<0xB1>(amax));   // lane ^ 1
+    amax = max_nonneg(amax, dpp<0x4E>(amax));   // lane ^ 2
     const uint32_t sc = mx_scale_code(amax);
     float v[kVec];
     scale_chunk<D>(yb, mx_elem_scale(sc), qs.nz, v);

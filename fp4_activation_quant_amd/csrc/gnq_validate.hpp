@@ -227,7 +227,8 @@ inline nq_status check_traffic(const void *const *src, const int64_t *src_row_by
 // nq_convert_probe: kinds 0..9, n in [0, 2^31); kind 8 takes an E8M0 code
 // the kernels can produce (an integer in 0..247) as its parameter.
 inline nq_status check_convert_probe(int kind, const void *in, int64_t n, float param, const void *out) {
-  if (kind < 0 || kind > 9 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in))) return NQ_EINVAL;
+  if (kind < 0 || kind > 11 || n < 0 || n >= ((int64_t)1 << 31) || (n > 0 && (!out || !in))) return NQ_EINVAL;
+  if (kind >= 10 && n % 8 != 0) return NQ_EINVAL;
   if (kind == 8 && !(param >= 0.0f && param <= 247.0f && param == (float)(int)param)) return NQ_EINVAL;
   return NQ_OK;
 }

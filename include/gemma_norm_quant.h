@@ -303,7 +303,8 @@ int nq_abi_version(void);
  *           scale `param` (the E4M3FN(y / scale) step) -> 1 byte each
  *   kind 5: kind 4 for fp16 y
  *   kind 6: NVFP4 block-scale code of amax = fp32 pattern with global scale
- *           `param` -> 1 byte each
+ *           `param` -> 1 byte each (exact for amax values a bf16 or an
+ *           fp16 holds, the only ones the kernels pass)
  *   kind 7: MXFP8 E8M0 scale code of amax = |fp32 pattern| -> 1 byte each
  *   kind 8: MXFP8 element code of the fp32 pattern in a block whose E8M0
  *           scale code is `param` (an integer in [0, 247], else
@@ -312,7 +313,11 @@ int nq_abi_version(void);
  *           block whose E4M3FN scale code is bits 16..23, global scale
  *           `param` (the E2M1(y * gs / decode(S)) step) -> 1 byte each
  *           (code in the low nibble)
- *   out  device buffer of n (kinds 0, 1, 4..9) or 2n (kinds 2, 3) bytes.
+ *   kind 10: kind 4 through the vector routine the kernels use on 8-element
+ *           chunks: patterns 8j .. 8j + 7 form one chunk (n % 8 == 0, else
+ *           NQ_EINVAL) -> 1 byte each
+ *   kind 11: kind 10 for fp16 y
+ *   out  device buffer of n (kinds 0, 1, 4..11) or 2n (kinds 2, 3) bytes.
  *   n    in [0, 2^31).
  */
 nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,

@@ -189,7 +189,10 @@ def test_standalone_mxfp8_validation(over, want):
 
 
 def test_probe_validation():
-    assert _lib.nq_convert_probe(10, 0x1000, 4, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
+    assert _lib.nq_convert_probe(12, 0x1000, 4, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
+    for kind in (10, 11):
+        assert _lib.nq_convert_probe(kind, 0x1000, 12, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
+        assert _lib.nq_convert_probe(kind, 0x1000, 0, 1.0, 0x2000, 0) == _lib.NQ_OK
     assert _lib.nq_convert_probe(-1, 0x1000, 4, 1.0, 0x2000, 0) == _lib.NQ_EINVAL
     for bad in (-1.0, 248.0, 12.5, float("nan"), float("inf")):
         assert _lib.nq_convert_probe(8, 0x1000, 4, bad, 0x2000, 0) == _lib.NQ_EINVAL, bad

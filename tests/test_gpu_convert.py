@@ -92,6 +92,50 @@ def test_fp8_quant_step_every_16bit_y(kind, fmt):
         assert n == 0, (s32, ex)
 
 
+@pytest.mark.parametrize("kind,fmt", [(10, O.BF16), (11, O.FP16)])
+def test_fp8_quant_chunks_every_16bit_y(kind, fmt):
+    """The vector routine the kernels run on 8-element chunks (for fp16 y the
+    clamp in packed fp16 and the division reading y from its half): every
+    finite 16-bit y for the same 75 scales, in code order and in a seeded
+    shuffle, against the oracle's step."""
+    codes = np.arange(1 << 16, dtype=np.uint32)
+    codes = codes[np.isfinite(O.decode(codes, fmt))]
+    codes = codes[: codes.size // 8 * 8]
+    rng = np.random.default_rng(3)
+    scales = SCALES + list(rng.uniform(1e-3, 10, 8)) + list(2.0 ** rng.uniform(-20, 20, 48))
+    shuffled = np.random.default_rng(11).permutation(codes)
+    for s in scales:
+        s32 = float(np.float32(s))
+        for order in (codes, shuffled):
+            got = probe(kind, order, s32)
+            want = O.quant_fp8_static(order.astype(np.uint16)[None, :], fmt, s32)[0]
+            n, ex = _mismatch(got, want, order)
+            assert n == 0, (s32, ex)
+
+
+@pytest.mark.parametrize("kind,fmt", [(10, O.BF16), (11, O.FP16)])
+def test_fp8_quant_chunks_scale_range_ends(kind, fmt):
+    """Scales at and next to the ends of the packed-fp16 clamp's range (2^-22
+    .. 143, where the fp16 rounding of 456 s is a finite normal fp16) and at
+    the far ends of the division's range (bf16 only from 2^-90 on, the
+    division's own exact range for the tiny bf16 y; every nonzero fp16 y is
+    at least 2^-24)."""
+    codes = np.arange(1 << 16, dtype=np.uint32)
+    codes = codes[np.isfinite(O.decode(codes, fmt))]
+    codes = codes[: codes.size // 8 * 8]
+    for e in (-121, -90, -23, -22, -21, 6, 7, 8, 100):
+        if fmt is O.BF16 and e < -90:
+            continue
+        for f in (1.0, 1.5, 0.75, 1.1171875, 143.0 / 128, 144.0 / 128):
+            s32 = float(np.float32(f * 2.0 ** e))
+            if s32 == 0.0 or not np.isfinite(s32):
+                continue
+            got = probe(kind, codes, s32)
+            want = O.quant_fp8_static(codes.astype(np.uint16)[None, :], fmt, s32)[0]
+            n, ex = _mismatch(got, want, codes)
+            assert n == 0, (s32, ex)
+
+
 GLOBAL_SCALES = [1.0, 441.1076965332031, 360.0879211425781, 1e5, 1.0 / 7.0, 301.176483154296875,
                  448 * 6 / 8.925]
 
@@ -99,9 +143,12 @@ GLOBAL_SCALES = [1.0, 441.1076965332031, 360.0879211425781, 1e5, 1.0 / 7.0, 301.
 @pytest.mark.parametrize("gs", GLOBAL_SCALES)
 def test_nvfp4_block_scale_step(gs):
     """The kernel's block-scale code against the oracle's step on tie-heavy
-    fp32 amax values over 60 binades."""
-    v = _tie_heavy_f32(exp_lo=-30, exp_hi=30, n_random=200_000)
-    v = np.abs(v)
+    amax values over 60 binades, rounded to bf16 and to fp16 (the values a
+    block of rounded y can have; the routine's division of amax by 6 is
+    exact for those)."""
+    v = np.abs(_tie_heavy_f32(exp_lo=-30, exp_hi=30, n_random=200_000)).astype(np.float64)
+    v = np.concatenate([O.decode(O.f64_to_bits(v, fmt), fmt) for fmt in (O.BF16, O.FP16)])
+    v = v[np.isfinite(v)].astype(np.float32)
     got = probe(6, v.view(np.uint32), gs)
     want = O.nvfp4_block_scale_codes(v, gs)
     n, ex = _mismatch(got, want, v)
