@@ -74,7 +74,7 @@ SCALES = [0.05, 7.0, 0.9, 1.0, 2.0 ** -20, 3.0e4, 0.0560825876891613, 0.01666259
 
 @pytest.mark.parametrize("kind,fmt", [(4, O.BF16), (5, O.FP16)])
 def test_fp8_quant_step_every_16bit_y(kind, fmt):
-    """All 65536 patterns of y (NaN/Inf excluded) for 75 scales, including the
+    """All 65536 patterns of y (NaN/Inf excluded) for 67 scales, including the
     workloads' calibrated ones."""
     codes = np.arange(1 << 16, dtype=np.uint32)
     yv = O.decode(codes, fmt)
@@ -96,7 +96,7 @@ def test_fp8_quant_step_every_16bit_y(kind, fmt):
 def test_fp8_quant_chunks_every_16bit_y(kind, fmt):
     """The vector routine the kernels run on 8-element chunks (for fp16 y the
     clamp in packed fp16 and the division reading y from its half): every
-    finite 16-bit y for the same 75 scales, in code order and in a seeded
+    finite 16-bit y for the same 67 scales, in code order and in a seeded
     shuffle, against the oracle's step."""
     codes = np.arange(1 << 16, dtype=np.uint32)
     codes = codes[np.isfinite(O.decode(codes, fmt))]
