@@ -136,6 +136,29 @@ def test_fp8_quant_chunks_scale_range_ends(kind, fmt):
             assert n == 0, (s32, ex)
 
 
+@pytest.mark.parametrize("chunk_kind,scalar_kind,fmt", [(10, 4, O.BF16), (11, 5, O.FP16)])
+def test_fp8_quant_infinite_y(chunk_kind, scalar_kind, fmt):
+    """An infinite y (the fp16 or bf16 rounding of t (1 + w) overflowed)
+    saturates to +-448 like any y beyond 448 s: every lane position of a
+    chunk, mixed with finite values, for scales inside and outside the
+    packed-fp16 clamp's range, through both routines."""
+    inf, ninf = (0x7C00, 0xFC00) if fmt is O.FP16 else (0x7F80, 0xFF80)
+    rng = np.random.default_rng(17)
+    finite = np.arange(1 << 16, dtype=np.uint32)
+    finite = finite[np.isfinite(O.decode(finite, fmt))]
+    codes = rng.choice(finite, 8 * 4096).astype(np.uint32)
+    pos = rng.random(codes.size) < 0.1
+    codes[pos] = np.where(rng.random(pos.sum()) < 0.5, inf, ninf)
+    for s in (0.0157645083963871, 1.0, 3.0e-7, 100.0, 200.0, 3.0e4):
+        s32 = float(np.float32(s))
+        want = O.quant_fp8_static(codes.astype(np.uint16)[None, :], fmt, s32)[0]
+        assert np.all(want[codes == inf] == 0x7E) and np.all(want[codes == ninf] == 0xFE)
+        for kind in (chunk_kind, scalar_kind):
+            got = probe(kind, codes, s32)
+            n, ex = _mismatch(got, want, codes)
+            assert n == 0, (kind, s32, ex)
+
+
 GLOBAL_SCALES = [1.0, 441.1076965332031, 360.0879211425781, 1e5, 1.0 / 7.0, 301.176483154296875,
                  448 * 6 / 8.925]
 
