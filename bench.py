@@ -15,10 +15,12 @@ one JSON line:
                wall time of the K steps (synchronised on both sides).  The K
                launches are captured once in a HIP graph and the timed region
                is one replay of it (--eager: one Python launch per step);
-  roofline     the kernel's average duration from HIP events recorded on the
-               launch stream around the timed region (graph: span / K; eager:
-               one event pair per launch), algorithmic bytes / that duration against the
-               8 TB/s HBM peak; traffic = measured HBM bytes per launch
+  roofline     the kernel's duration per launch from HIP events recorded on
+               the launch stream: (span of a replay of 2K launches - span of
+               a replay of K) / K, each replay queued behind device work so
+               no launch waits for the host (eager: one event pair per
+               launch); algorithmic bytes / that duration against the 8 TB/s
+               HBM peak; traffic = measured HBM bytes per launch
                (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel's
                reading) from profiles/traffic.json when it was taken on the
                current kernel source, else null;
