@@ -128,6 +128,8 @@ PREFETCH = [
     (torch.bfloat16, "nvfp4", 16384, 5120, True, False),
     (torch.bfloat16, "mxfp8", 2100, 5120, True, False),
     (torch.float16, "none", 2048, 4608, True, True),      # add + plain norm alone
+    (torch.bfloat16, "fp8", 2048, 5120, False, True),     # no guards; static FP8 by the fp32 division
+    (torch.float16, "fp8", 2049, 5120, False, False),     # no guards; static FP8 on packed fp16 halves
 ]
 
 
