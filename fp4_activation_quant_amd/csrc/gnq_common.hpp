@@ -144,6 +144,7 @@ struct QuantScale {
   float s, r, lim, nz;
   uint32_t lim2;   // static FP8: fl32(456 s) rounded to fp16, in both halves
   bool lim2_ok;    // 2^-22 <= s <= 143: lim2 is a finite normal fp16
+  double r64;      // static FP8: RN64(1 / s)
 };
 
 __device__ __forceinline__ QuantScale quant_scale(float s, bool fp8);
@@ -169,67 +170,49 @@ __device__ __forceinline__ float div_by_scale(float y, const QuantScale &d) {
   return __builtin_fmaf(-__builtin_fmaf(q, d.s, -y), d.r, q);
 }
 
-// Steps of the division above for the fp16 value in half H of a word c:
-// y is read from its half by v_fma_mix_f32 each time it enters (its
-// widening is exact), so it needs no separate conversion.
-template <int H>
-__device__ __forceinline__ float mix_mul_f16(uint32_t c, float r, float nz) {   // fl(y r + nz)
-  float q;
-  if constexpr (H == 0)
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(q) : "v"(c), "v"(r), "v"(nz));
-  else
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(q) : "v"(c), "v"(r), "v"(nz));
-  return q;
-}
-template <int H>
-__device__ __forceinline__ float mix_rem_f16(float q, float s, uint32_t c) {   // fl(q s - y)
-  float e;
-  if constexpr (H == 0)
-    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(e) : "v"(q), "v"(s), "v"(c));
-  else
-    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(e) : "v"(q), "v"(s), "v"(c));
-  return e;
+// fl32(y / s) for a y that a bf16 or an fp16 holds (at most 11
+// significant bits), as RN32(RN64(y * RN64(1/s))): the double product is
+// within 2^-52 relative of y / s (two roundings of 2^-53), while y / s is
+// never within 2^-49 relative of a point halfway between two floats (that
+// midpoint has a 25-bit odd significand m; y = Y 2^a, s = S 2^b with Y and
+// S odd of at most 11 and 24 bits, so y - m 2^c s is a nonzero multiple of
+// 2^min(a, b + c), at least 2^-49 of m S 2^(b + c)), so both round to the
+// same float (quotients below 2^-126, where that spacing argument ends,
+// take the code +-0 either way).  Five instructions per value with the two
+// widenings, against
+// six for div_by_scale's reciprocal and corrections (the fp64 multiply runs
+// at the fp32 rate on this part).  Bit-identical to div_by_scale wherever
+// both apply.  y clamped as in div_by_scale (the clamp bound L may have
+// more bits than y, but its quotient lies next to 456, far from any code
+// boundary, so its code is the saturated one either way).
+__device__ __forceinline__ float div_by_scale_f64(float y, const QuantScale &d) {
+  return (float)((double)y * d.r64);
 }
 
 // Static FP8 codes of one 8-element chunk of rounded y (four words of two
 // activation-dtype values), little-endian.  fp16 y are clamped in pairs in
 // their own format (lim2, the fp16 rounding of L: within (455.7 s,
-// 456.3 s), so the argument above holds unchanged) where that bound is a
-// finite normal fp16; other scales and bf16 y take the fp32 clamp.
+// 456.3 s), so the argument of div_by_scale holds unchanged) where that
+// bound is a finite normal fp16; other scales and bf16 y take the fp32
+// clamp.
 template <class D>
 __device__ __forceinline__ u32x2 fp8_codes(const uint32_t (&yb)[4], const QuantScale &d) {
   float v[kVec];
   if constexpr (D::kF16) {
     if (d.lim2_ok) {
-      // div_by_scale's steps, each over all eight values before the next
-      // (the inline assembly keeps its order, so this order is the issue
-      // order: eight independent instructions per step)
-      uint32_t c[4];
-      float e[kVec];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = Fp16::clamp2(yb[k], d.lim2);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        v[2 * k] = mix_mul_f16<0>(c[k], d.r, d.nz);
-        v[2 * k + 1] = mix_mul_f16<1>(c[k], d.r, d.nz);
-      }
-#pragma unroll
-      for (int step = 0; step < 2; ++step) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          e[2 * k] = mix_rem_f16<0>(v[2 * k], d.s, c[k]);
-          e[2 * k + 1] = mix_rem_f16<1>(v[2 * k + 1], d.s, c[k]);
-        }
-#pragma unroll
-        for (int i = 0; i < kVec; ++i) v[i] = __builtin_fmaf(-e[i], d.r, v[i]);
+        const uint32_t c = Fp16::clamp2(yb[k], d.lim2);
+        v[2 * k] = div_by_scale_f64(Fp16::lo(c), d);
+        v[2 * k + 1] = div_by_scale_f64(Fp16::hi(c), d);
       }
       return u32x2{e4m3x4_near(v[0], v[1], v[2], v[3]), e4m3x4_near(v[4], v[5], v[6], v[7])};
     }
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    v[2 * k] = div_by_scale(D::lo(yb[k]), d);
-    v[2 * k + 1] = div_by_scale(D::hi(yb[k]), d);
+    v[2 * k] = div_by_scale_f64(clampf(D::lo(yb[k]), d.lim), d);
+    v[2 * k + 1] = div_by_scale_f64(clampf(D::hi(yb[k]), d.lim), d);
   }
   return u32x2{e4m3x4_near(v[0], v[1], v[2], v[3]), e4m3x4_near(v[4], v[5], v[6], v[7])};
 }
@@ -248,7 +231,7 @@ __device__ __forceinline__ float opaque_neg_zero() {
 __device__ __forceinline__ QuantScale quant_scale(float s, bool fp8) {
   const float lim = fp8 ? 456.0f * s : 0.0f;
   return QuantScale{s, fp8 ? 1.0f / s : 0.0f, lim, opaque_neg_zero(), Fp16::pack(lim, lim),
-                    fp8 && s >= 0x1p-22f && s <= 143.0f};
+                    fp8 && s >= 0x1p-22f && s <= 143.0f, fp8 ? 1.0 / (double)s : 0.0};
 }
 
 // fl32(y * o) for each value of a chunk (nz: opaque_neg_zero()).

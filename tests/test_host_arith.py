@@ -66,3 +66,36 @@ def test_div6_needs_the_correction():
     r = rn32(F(1, 6))
     vals = _nonneg_16bit_values()
     assert sum(rn32(F(v) * r) != rn32(F(v) / 6) for v in vals[::7]) > 1000
+
+
+def _finite_16bit(fmt):
+    if fmt == "fp16":
+        v = np.arange(0, 1 << 16, dtype=np.uint16).view(np.float16).astype(np.float32)
+    else:
+        v = (np.arange(0, 1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    return v[np.isfinite(v)]
+
+
+def test_fp8_division_in_fp64_is_fl32():
+    """Static FP8: the kernels form fl32(y / s) as RN32(RN64(y * RN64(1/s)))
+    for y that a bf16 or an fp16 holds.  Against numpy's correctly rounded
+    fp32 division, every finite 16-bit y of both formats, 300 scales over 80
+    binades plus amax / 448 scales of short amax values (whose quotients
+    land on fp32 values that are E4M3 rounding ties): equal wherever the
+    quotient is a normal fp32, and below 2^-10 (the code +-0) with the same
+    sign where it is not."""
+    rng = np.random.default_rng(23)
+    scales = list(2.0 ** rng.uniform(-40, 40, 300))
+    scales += [a / 448 for a in (7.0625, 6.96875, 6.1875, 25.125, 7.46484375, 1.0, 3.0, 113.0, 0.75)]
+    for fmt in ("fp16", "bf16"):
+        y = _finite_16bit(fmt)
+        for s in scales:
+            s32 = np.float32(s)
+            with np.errstate(over="ignore"):       # infinite quotients on both sides
+                want = y / s32
+                got = (y.astype(np.float64) * (1.0 / np.float64(s32))).astype(np.float32)
+            normal = np.abs(want) >= np.float32(2.0 ** -126)
+            assert np.array_equal(got[normal], want[normal]), (fmt, float(s32))
+            sub = ~normal
+            assert np.all(np.abs(got[sub]) < 2.0 ** -10)
+            assert np.array_equal(np.signbit(got[sub]), np.signbit(want[sub]))
