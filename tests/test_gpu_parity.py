@@ -116,7 +116,7 @@ def test_edge_shapes(dt, nvfp4, M, H, res, wy):
 
 PREFETCH = [
     # dtype, output, M, H, residual, write_y: rows of 4096 < H < 6144 at
-    # 2048 <= M <= 16384 loop 1024 workgroups over the rows
+    # 2048 <= M <= 16384 loop 1024 (or 512) workgroups over the rows
     (torch.float16, "nvfp4", 2100, 5120, True, True),
     (torch.bfloat16, "nvfp4", 2049, 4864, True, True),    # one row past the last full 1024-row span
     (torch.float16, "mxfp8", 2050, 4224, False, True),    # some threads own one chunk
@@ -130,6 +130,9 @@ PREFETCH = [
     (torch.float16, "none", 2048, 4608, True, True),      # add + plain norm alone
     (torch.bfloat16, "fp8", 2048, 5120, False, True),     # no guards; static FP8 by the fp32 division
     (torch.float16, "fp8", 2049, 5120, False, False),     # no guards; static FP8 on packed fp16 halves
+    (torch.bfloat16, "nvfp4", 2048, 5120, True, False),   # 512 workgroups, 4 rows each
+    (torch.float16, "nvfp4", 8192, 4352, True, True),     # 512 workgroups, 16 rows each
+    (torch.float16, "nvfp4", 6144, 5120, False, True),    # 1024 workgroups, 6 rows each
 ]
 
 
