@@ -596,7 +596,8 @@ def block_threads(H, res=False):
 def traffic_streams(wl):
     """Per-row bytes of the op's read and write streams for a workload: reads
     x (and the residual); writes the residual, y, the codes and the scale
-    bytes (row-major here: the probe measures bytes, not the tiled layout)."""
+    bytes (NVFP4's last: the probe writes them as a plain row stream, or in
+    its tiled form at their 128x4-tiled offsets as the op does)."""
     H = wl.H
     src = [2 * H] + ([2 * H] if wl.has_residual else [])
     dst = ([2 * H] if wl.has_residual else []) + ([2 * H] if wl.write_y else [])
@@ -610,7 +611,10 @@ def ceiling_main(args):
     the op: graph replay, buffer sets rotated through >= 2 GiB, per-launch
     time from the difference of a K- and a 2K-launch replay.  One JSON line
     per workload with every form and the best (the practical ceiling the
-    op's figure is compared with)."""
+    op's figure is compared with).  NVFP4 workloads (M a multiple of 128)
+    are also probed with the scale bytes stored at their 128x4-tiled offsets
+    in the op's row order, as the op must store them: best_tiled is the best
+    of those forms."""
     import torch
     from fp4_activation_quant_amd import _lib
     from fp4_activation_quant_amd.workloads import WORKLOADS
@@ -634,6 +638,8 @@ def ceiling_main(args):
         forms = [(op_threads, 0, 0)]
         forms += [(op_threads, g, 1) for g in (256, 512, 768, 1024, 1536, 2048) if g < M]
         forms += [(t, 0, 0) for t in (256, 512, 1024) if t != op_threads and 2 * wl.H <= 64 * t]
+        if wl.mode == "nvfp4" and M % 128 == 0:
+            forms += [(t, g, f | _lib.NQ_PROBE_TILED_SCALES) for t, g, f in forms]
         stream = torch.cuda.Stream(device=dev)
         results = []
         for threads, grid, pf in forms:
@@ -645,15 +651,23 @@ def ceiling_main(args):
                     raise RuntimeError(f"nq_traffic_probe: status {st}")
             t = _time_graphs(launch, args.steps, args.warmup, stream, differenced=True)
             us = t["diff_ms"] * 1e3
-            results.append({"threads": threads, "grid": grid, "prefetch": pf, "us": round(us, 3),
+            results.append({"threads": threads, "grid": grid,
+                            "prefetch": int(bool(pf & _lib.NQ_PROBE_PREFETCH)),
+                            "tiled_scales": int(bool(pf & _lib.NQ_PROBE_TILED_SCALES)), "us": round(us, 3),
                             "GBps": round(per_launch / (us * 1e-6) / 1e9, 1),
                             "span_us": round(t["span_ms"] * 1e3, 3)})
         best = max(results, key=lambda r: r["GBps"])
-        print(json.dumps({"ceiling": name, "bytes_per_launch": per_launch, "rows": M,
-                          "src_row_bytes": src_rb, "dst_row_bytes": dst_rb, "buffer_sets": n_sets,
-                          "steps": args.steps, "best_GBps": best["GBps"],
-                          "best_frac_of_peak": round(best["GBps"] / HBM_PEAK_GBS, 4), "forms": results}),
-              flush=True)
+        line = {"ceiling": name, "bytes_per_launch": per_launch, "rows": M,
+                "src_row_bytes": src_rb, "dst_row_bytes": dst_rb, "buffer_sets": n_sets,
+                "steps": args.steps, "best_GBps": best["GBps"], "best_us": best["us"],
+                "best_frac_of_peak": round(best["GBps"] / HBM_PEAK_GBS, 4)}
+        tiled = [r for r in results if r["tiled_scales"]]
+        if tiled:
+            bt = max(tiled, key=lambda r: r["GBps"])
+            line.update(best_tiled_GBps=bt["GBps"], best_tiled_us=bt["us"],
+                        best_tiled_frac_of_peak=round(bt["GBps"] / HBM_PEAK_GBS, 4))
+        line["forms"] = results
+        print(json.dumps(line), flush=True)
         del sets
         torch.cuda.empty_cache()
 

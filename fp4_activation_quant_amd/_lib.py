@@ -140,16 +140,19 @@ def nq_convert_probe(kind, inp, n, param, out, stream):
                                   stream or None)
 
 
-def nq_traffic_probe(src, src_row_bytes, dst, dst_row_bytes, rows, threads, grid, prefetch, stream):
+NQ_PROBE_PREFETCH, NQ_PROBE_TILED_SCALES = 1, 2
+
+
+def nq_traffic_probe(src, src_row_bytes, dst, dst_row_bytes, rows, threads, grid, flags, stream):
     """Raw call: ``src`` / ``dst`` are lists of device addresses, the row
-    byte counts lists of ints (see the header)."""
+    byte counts lists of ints, ``flags`` NQ_PROBE_* bits (see the header)."""
     vpa = ctypes.c_void_p * max(1, len(src))
     vpd = ctypes.c_void_p * max(1, len(dst))
     i64a = ctypes.c_int64 * max(1, len(src))
     i64d = ctypes.c_int64 * max(1, len(dst))
     return lib().nq_traffic_probe(vpa(*src), i64a(*src_row_bytes), len(src), vpd(*dst) if dst else None,
                                   i64d(*dst_row_bytes) if dst else None, len(dst), int(rows), int(threads),
-                                  int(grid), int(prefetch), stream or None)
+                                  int(grid), int(flags), stream or None)
 
 
 def nq_gemma_add_rms_norm_quant_gemm_fp8(x, residual, residual_out, weight, eps, scale, M, H, dtype,

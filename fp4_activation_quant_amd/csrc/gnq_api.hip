@@ -208,8 +208,8 @@ nq_status nq_gemma_add_rms_norm_quant_gemm_fp8(const void *x, const void *residu
 
 nq_status nq_traffic_probe(const void *const *src, const int64_t *src_row_bytes, int nsrc,
                            void *const *dst, const int64_t *dst_row_bytes, int ndst, int64_t rows,
-                           int threads, int grid, int prefetch, void *stream) {
-  const nq_status v = check_traffic(src, src_row_bytes, nsrc, dst, dst_row_bytes, ndst, rows, threads, grid);
+                           int threads, int grid, int flags, void *stream) {
+  const nq_status v = check_traffic(src, src_row_bytes, nsrc, dst, dst_row_bytes, ndst, rows, threads, grid, flags);
   if (v != NQ_OK || rows == 0) return v;
   TrafficStreams t{};
   t.ndst = ndst;
@@ -221,7 +221,8 @@ nq_status nq_traffic_probe(const void *const *src, const int64_t *src_row_bytes,
     t.dst[i] = dst[i];
     t.dst_chunks[i] = (unsigned)(dst_row_bytes[i] / 16);
   }
-  return status_of(traffic_probe(t, nsrc, rows, threads, grid, prefetch != 0, (hipStream_t)stream));
+  return status_of(traffic_probe(t, nsrc, rows, threads, grid, (flags & NQ_PROBE_PREFETCH) != 0,
+                                 (flags & NQ_PROBE_TILED_SCALES) != 0, (hipStream_t)stream));
 }
 
 nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, void *out,

@@ -16,7 +16,9 @@ struct TrafficStreams {
   int ndst;
 };
 
+// tiled: the last write stream is the 128x4-tiled NVFP4 block-scale layout
+// (one byte per 16 elements), written as the op writes it.
 hipError_t traffic_probe(const TrafficStreams &t, int nsrc, int64_t rows, int threads, int grid, bool pf,
-                         hipStream_t st);
+                         bool tiled, hipStream_t st);
 
 }  // namespace gnq

@@ -198,13 +198,16 @@ inline nq_status check_fused_decode(const void *x, const void *residual, const v
 
 // nq_traffic_probe: 1..2 read and 0..4 write streams of 16-byte chunks, a
 // read row within 4 chunks per thread; no write stream overlaps another
-// stream.
+// stream; flags from NQ_PROBE_PREFETCH | NQ_PROBE_TILED_SCALES, the tiled
+// scale stream (the last write stream) on whole 128-row tiles.
 inline nq_status check_traffic(const void *const *src, const int64_t *src_row_bytes, int nsrc,
                                void *const *dst, const int64_t *dst_row_bytes, int ndst, int64_t rows,
-                               int threads, int grid) {
+                               int threads, int grid, int flags) {
   if (nsrc < 1 || nsrc > 2 || ndst < 0 || ndst > 4 || rows < 0 || !src || !src_row_bytes ||
       (ndst > 0 && (!dst || !dst_row_bytes)))
     return NQ_EINVAL;
+  if ((flags & ~(NQ_PROBE_PREFETCH | NQ_PROBE_TILED_SCALES)) != 0) return NQ_EINVAL;
+  if ((flags & NQ_PROBE_TILED_SCALES) != 0 && (ndst < 1 || rows % 128 != 0)) return NQ_EINVAL;
   if (threads < kWave || threads > kMaxThreads || threads % kWave != 0 || grid < 0) return NQ_EINVAL;
   const void *bufs[6];
   size_t lens[6];

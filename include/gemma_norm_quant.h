@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define NQ_ABI_VERSION 6
+#define NQ_ABI_VERSION 7
 
 typedef enum {
   NQ_OK = 0,
@@ -340,16 +340,27 @@ nq_status nq_convert_probe(int kind, const void *in, int64_t n, float param, voi
  *   threads                    workgroup size, a multiple of 64 in [64, 1024];
  *   grid                       0: one workgroup per row; else that many
  *                              workgroups taking rows round-robin;
- *   prefetch                   nonzero: issue the next row's loads before
- *                              the current row's stores.
+ *   flags                      NQ_PROBE_PREFETCH: issue the next row's loads
+ *                              before the current row's stores;
+ *                              NQ_PROBE_TILED_SCALES: the last write stream
+ *                              holds one byte per 16 elements in the 128x4-
+ *                              tiled NVFP4 block-scale layout (byte of block b
+ *                              of row m at the offset nq_gemma_add_rms_norm_quant
+ *                              stores it, with row_bytes / 4 four-block
+ *                              tiles per 128 rows), stored one byte at a
+ *                              time as the op stores its scales, and rows go
+ *                              to workgroups in the op's NVFP4 row order;
+ *                              rows must be a multiple of 128.
  * Row bytes must be positive multiples of 16 (a read row at most
  * 64 * threads bytes), pointers 16-byte aligned, and no write stream may
- * overlap another stream (NQ_EINVAL otherwise).  The written bytes are
- * meaningless.
+ * overlap another stream (NQ_EINVAL otherwise, as for any other flag bit).
+ * The written bytes are meaningless.
  */
+#define NQ_PROBE_PREFETCH 1
+#define NQ_PROBE_TILED_SCALES 2
 nq_status nq_traffic_probe(const void *const *src, const int64_t *src_row_bytes, int nsrc,
                            void *const *dst, const int64_t *dst_row_bytes, int ndst, int64_t rows,
-                           int threads, int grid, int prefetch, void *stream);
+                           int threads, int grid, int flags, void *stream);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,7 @@
 //   quant y s M H dtype mode q bs
 //   gemm mx a sa as b sb bs M N K out
 //   gemm4 a sa ags b sb bgs M N K out
-//   traffic nsrc ndst rows threads grid src0 src1 srb0 srb1 dst0..dst3 drb0..drb3
+//   traffic nsrc ndst rows threads grid flags src0 src1 srb0 srb1 dst0..dst3 drb0..drb3
 //   probe kind in n param out
 //   fdec x r ro w s M H dtype write_y q y b bs N out
 //   bsb M H                       (prints nq_block_scale_bytes)
@@ -66,8 +66,8 @@ int main() {
       std::printf("%d\n", (int)check_gemm_nvfp4(P(a), P(sa), (const float *)P(ags), P(b), P(sb),
                                                 (const float *)P(bgs), M, N, K, P(out)));
     } else if (c == "traffic") {
-      int64_t nsrc, ndst, rows, threads, grid;
-      nexti(nsrc), nexti(ndst), nexti(rows), nexti(threads), nexti(grid);
+      int64_t nsrc, ndst, rows, threads, grid, flags;
+      nexti(nsrc), nexti(ndst), nexti(rows), nexti(threads), nexti(grid), nexti(flags);
       uint64_t src[2], dst[4];
       int64_t srb[2], drb[4];
       next(src[0]), next(src[1]), nexti(srb[0]), nexti(srb[1]);
@@ -77,7 +77,7 @@ int main() {
       void *dp[4] = {(void *)P(dst[0]), (void *)P(dst[1]), (void *)P(dst[2]), (void *)P(dst[3])};
       // the counts index these fixed arrays only after the check bounds them
       std::printf("%d\n", (int)check_traffic(sp, srb, (int)nsrc, dp, drb, (int)ndst, rows, (int)threads,
-                                             (int)grid));
+                                             (int)grid, (int)flags));
     } else if (c == "probe") {
       int64_t kind, n;
       uint64_t in, out;

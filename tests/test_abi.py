@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert _lib.nq_abi_version() == 6
+    assert _lib.nq_abi_version() == 7
     assert _lib.nq_status_string(0) == "ok"
     for s in range(0, 6):
         assert isinstance(_lib.nq_status_string(s), str)
@@ -295,6 +295,11 @@ SA, SB, DA, DB = (0x30000000 + i * 0x1000000 for i in range(4))
     (dict(dst=[SA + 512], rows=8), _lib.NQ_EINVAL),         # a write stream over a read stream
     (dict(dst=[DA, DA + 256], drb=[64, 64], rows=8), _lib.NQ_EINVAL),   # write streams overlapping
     (dict(rows=-1), _lib.NQ_EINVAL),
+    (dict(pf=4), _lib.NQ_EINVAL),                           # unknown flag bit
+    (dict(pf=-1), _lib.NQ_EINVAL),
+    (dict(pf=3), None),                                     # prefetch + tiled scales (M = 0: no launch)
+    (dict(pf=2, rows=130), _lib.NQ_EINVAL),                 # tiled scales on whole 128-row tiles only
+    (dict(pf=2, dst=[], drb=[], rows=128), _lib.NQ_EINVAL), # and a write stream to hold them
 ])
 def test_traffic_probe_validation(over, want):
     a = dict(src=[SA], srb=[1024], dst=[DA], drb=[512], rows=0, threads=256, grid=0, pf=0)

@@ -68,7 +68,7 @@ def _line(cmd, a):
     if cmd in ("op", "quant", "gemm", "gemm4"):
         return cmd + " " + " ".join(str(_u(v)) for v in a)
     if cmd == "traffic":
-        nums = a[:5] + [_u(v) for v in a[5:7]] + a[7:9] + [_u(v) for v in a[9:13]] + a[13:17]
+        nums = a[:6] + [_u(v) for v in a[6:8]] + a[8:10] + [_u(v) for v in a[10:14]] + a[14:18]
         return "traffic " + " ".join(str(v) for v in nums)
     if cmd == "probe":
         kind, inp, n, param, out = a
@@ -96,9 +96,10 @@ def _fuzz(n, seed):
                         [pick(I64), pick(I64), pick(I64), pick(ADDRS)]))
         elif k == 3:     # a sa ags b sb bgs M N K out
             out.append(("gemm4", [pick(ADDRS) for _ in range(6)] + [pick(I64), pick(I64), pick(I64), pick(ADDRS)]))
-        elif k == 4:     # nsrc ndst rows threads grid src0 src1 srb0 srb1 dst0..3 drb0..3
-            out.append(("traffic", [pick([-1, 0, 1, 2, 3]), pick([-1, 0, 1, 4, 5]), pick(I64),
-                                    pick([0, 32, 64, 96, 256, 1024, 2048]), pick([-1, 0, 8, 2**31 - 1])] +
+        elif k == 4:     # nsrc ndst rows threads grid flags src0 src1 srb0 srb1 dst0..3 drb0..3
+            out.append(("traffic", [pick([-1, 0, 1, 2, 3]), pick([-1, 0, 1, 4, 5]), pick(I64 + [128, 256]),
+                                    pick([0, 32, 64, 96, 256, 1024, 2048]), pick([-1, 0, 8, 2**31 - 1]),
+                                    pick([-1, 0, 1, 2, 3, 4])] +
                         [pick(ADDRS), pick(ADDRS), pick(ROW_BYTES), pick(ROW_BYTES)] +
                         [pick(ADDRS) for _ in range(4)] + [pick(ROW_BYTES) for _ in range(4)]))
         elif k == 5:     # kind in n param out
@@ -148,14 +149,14 @@ def _library(cmd, a, st):
             return None
         return L.nq_gemm_nvfp4(_u(A), _u(sa), _u(ags), _u(B), _u(sb), _u(bgs), M, N, K, _u(out), None)
     if cmd == "traffic":
-        nsrc, ndst, rows, threads, grid = a[:5]
+        nsrc, ndst, rows, threads, grid, flags = a[:6]
         if st == _lib.NQ_OK and rows != 0:
             return None
         if not (1 <= nsrc <= 2 and 0 <= ndst <= 4):
             return None          # the raw call takes the stream lists' own lengths
-        src, srb = [_u(v) for v in a[5:5 + nsrc]], a[7:7 + nsrc]
-        dst, drb = [_u(v) for v in a[9:9 + ndst]], a[13:13 + ndst]
-        return _lib.nq_traffic_probe(src, srb, dst, drb, rows, threads, grid, 0, None)
+        src, srb = [_u(v) for v in a[6:6 + nsrc]], a[8:8 + nsrc]
+        dst, drb = [_u(v) for v in a[10:10 + ndst]], a[14:14 + ndst]
+        return _lib.nq_traffic_probe(src, srb, dst, drb, rows, threads, grid, flags, None)
     if cmd == "probe":
         kind, inp, n, param, out = a
         if st == _lib.NQ_OK and n != 0:
