@@ -56,6 +56,11 @@ struct Bf16 {
     f32x2 v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
+  // One value rounded to bf16, in the low 16 bits (as Fp16::round1).
+  static __device__ __forceinline__ uint32_t round1(float a) {
+    asm("" : "+v"(a));
+    return pack(a, 0.0f) & 0xffffu;
+  }
 };
 
 struct Fp16 {
@@ -83,6 +88,14 @@ struct Fp16 {
   static __device__ __forceinline__ uint32_t pack(float a, float b) {
     f32x2 v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  // One value rounded to fp16, in the low 16 bits.  The value passes an
+  // empty asm first: without it the compiler folds a product feeding a lone
+  // conversion into v_fma_mixlo_f16 with a +0 addend, which rounds the exact
+  // product once (not to fp32, then to fp16) and turns a -0 product into +0.
+  static __device__ __forceinline__ uint32_t round1(float a) {
+    asm("" : "+v"(a));
+    return pack(a, 0.0f) & 0xffffu;
   }
   // Both values of p clamped to [-L, L], L a non-negative fp16 held in both
   // halves of l2 (two packed instructions for two values).

@@ -262,7 +262,7 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
     for (int j = tid; j < H; j += blockDim.x) {
       uint32_t h = x[rb + j];
       if constexpr (HAS_RES) {
-        h = D::pack(D::lo(h) + D::lo(res[rb + j]), 0.0f) & 0xffffu;
+        h = D::round1(D::lo(h) + D::lo(res[rb + j]));
         res[rb + j] = (uint16_t)h;
       }
       const float hf = D::lo(h);
@@ -283,7 +283,7 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
         for (int k = 0; k < kBlock; ++k) {
           const int j = b * kBlock + k;
           const uint32_t yq =
-              D::pack(norm_scale<GEMMA>(D::lo(hsrc[rb + j]) * rstd, D::lo(w[j])), 0.0f) & 0xffffu;
+              D::round1(norm_scale<GEMMA>(D::lo(hsrc[rb + j]) * rstd, D::lo(w[j])));
           if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
           yv[k] = D::lo(yq);
         }
@@ -308,7 +308,7 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
         for (int k = 0; k < kMxBlock; ++k) {
           const int j = b * kMxBlock + k;
           const uint32_t yq =
-              D::pack(norm_scale<GEMMA>(D::lo(hsrc[rb + j]) * rstd, D::lo(w[j])), 0.0f) & 0xffffu;
+              D::round1(norm_scale<GEMMA>(D::lo(hsrc[rb + j]) * rstd, D::lo(w[j])));
           if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
           yv[k] = D::lo(yq);
         }
@@ -317,7 +317,7 @@ fused_rows_scalar(const uint16_t *__restrict__ x, uint16_t *__restrict__ res,
     } else {
       for (int j = tid; j < H; j += blockDim.x) {
         const uint32_t yq =
-            D::pack(norm_scale<GEMMA>(D::lo(hsrc[rb + j]) * rstd, D::lo(w[j])), 0.0f) & 0xffffu;
+            D::round1(norm_scale<GEMMA>(D::lo(hsrc[rb + j]) * rstd, D::lo(w[j])));
         if constexpr (WRITE_Y) y[rb + j] = (uint16_t)yq;
         if constexpr (MODE == kModeFp8) q[rb + j] = (uint8_t)e4m3_one(div_by_scale(D::lo(yq), qs));
       }

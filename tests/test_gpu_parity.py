@@ -208,6 +208,43 @@ def test_special_values(nvfp4, dt):
         _run_and_compare(x, torch.flip(x, [0]).contiguous(), w, 1e-5, scale, nvfp4, True)
 
 
+ZERO_SIGN_SHAPES = [
+    # M, H, misaligned views: every launch form
+    (9, 256, False),       # several rows per wave
+    (9, 1024, False),      # one workgroup per row
+    (2048, 5120, False),   # the looping launch
+    (9, 1000, False),      # element-wise path (H % 16 != 0)
+    (9, 1024, True),       # element-wise path (unaligned views)
+]
+
+
+@pytest.mark.parametrize("M,H,misalign", ZERO_SIGN_SHAPES)
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("norm", ["gemma", "plain"])
+def test_zero_products_keep_their_sign(M, H, misalign, dt, norm):
+    """y = t * g is an exact zero where the norm factor g is (w = -1 for
+    Gemma's 1 + w, w = 0 for the plain norm) or where h is (x = -residual
+    gives h = +0): IEEE gives it the product's sign, and the codes keep it
+    (0x80 / 0x8 for -0).  The fp16 element-wise kernel once rounded such a
+    product with a fused multiply-add of +0, which returns +0 for a -0
+    product."""
+    print(f"zero products M={M} H={H} misalign={misalign} {dt} {norm}", flush=True)
+    g = torch.Generator().manual_seed(M * 17 + H + (1 if norm == "plain" else 0))
+    x = torch.randn(M, H, generator=g).to(dt)
+    r = (torch.randn(M, H, generator=g) * 2).to(dt)
+    r[0] = -x[0]                                        # h = +0 across row 0
+    w = (torch.randn(H, generator=g) * 0.3).to(dt)
+    w[::5] = -1.0 if norm == "gemma" else 0.0           # zero norm factor
+    for mode in ("fp8", "nvfp4", "mxfp8", "none"):
+        if (mode == "nvfp4" and H % 64) or (mode == "mxfp8" and H % 32):
+            continue
+        scale = {"fp8": 0.02, "nvfp4": 448 * 6 / 8.0}.get(mode, 1.0)
+        for res in (r, None):
+            gpu = P.run_gpu(x, res.clone() if res is not None else None, w, 1e-6, scale, mode == "nvfp4", True,
+                            misalign=misalign, norm=norm, quant=mode != "none", mxfp8=mode == "mxfp8")
+            P.check(P.compare(gpu, x, res, w, 1e-6, scale, P.all_rows(M)))
+
+
 def test_empty_batch_launches_nothing():
     dev = torch.device("cuda")
     for nvfp4 in (False, True):
