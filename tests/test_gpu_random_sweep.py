@@ -231,3 +231,23 @@ def test_random_gemm_matches_oracle_exactly(case):
     got = P.bits16(o)
     bad = np.nonzero(got != want)
     assert bad[0].size == 0, (bad[0][:5], bad[1][:5], got[bad][:5], want[bad][:5])
+
+
+def _draw_decode_cases(n=24):
+    rng = np.random.default_rng(SEED + 3)
+    return [dict(i=i, dt=[torch.bfloat16, torch.float16][int(rng.integers(2))], M=int(rng.integers(1, 9)),
+                 H=[1024, 2048, 4096][int(rng.integers(3))], N=int(np.exp(rng.uniform(0.0, np.log(9000.0)))),
+                 res=bool(rng.integers(2)), wy=bool(rng.integers(2))) for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _draw_decode_cases(), ids=lambda c: "{i}-{M}x{H}x{N}".format(**c))
+def test_random_decode_step_matches_the_two_calls(case):
+    """The fused decode step over random row counts, hidden sizes and weight
+    heights, to the bars of the fixed decode cases (the op's outputs bit for
+    bit those of the separate op call; the linear within the GEMM bar of the
+    oracle's exact product, bit for bit the two-call GEMM where both run the
+    same reduction)."""
+    from tests.test_gpu_decode import test_fused_decode_matches_the_two_calls as check
+    c = case
+    print(f"random decode case {c['i']}", flush=True)
+    check(c["dt"], c["M"], c["H"], c["N"], c["res"], c["wy"])
