@@ -130,3 +130,41 @@ def test_fused_decode_rejects_and_passes_through():
                                                   torch.empty(9, 4096, dtype=torch.uint8, device=dev), None,
                                                   torch.empty(9, 64, dtype=torch.bfloat16, device=dev))
     assert e.value.status == _lib.NQ_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("M,H", [(1, 4096), (3, 2048), (5, 1024)])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_fused_decode_zero_products_keep_their_sign(M, H, dt):
+    """Columns with w = -1 (Gemma's 1 + w is +0) and half a row with x =
+    -residual (h = +0): y is a zero product with the product's sign, and the decode
+    step's codes and y must equal the separate op's, sign of zero included
+    (which the op's own tests check against the oracle)."""
+    print(f"fused decode zero products M={M} H={H} {dt}", flush=True)
+    dev = torch.device("cuda")
+    g = torch.Generator().manual_seed(M * 7 + H)
+    x = torch.randn(M, H, generator=g).to(dt)
+    r = (torch.randn(M, H, generator=g) * 2).to(dt)
+    r[0, : H // 2] = -x[0, : H // 2]
+    w = (torch.randn(H, generator=g) * 0.1).to(dt)
+    w[::7] = -1.0
+    s = torch.tensor([0.02], dtype=torch.float32, device=dev)
+    N = 256
+    rng = np.random.default_rng(M + H)
+    bq = torch.from_numpy(_finite_codes(rng, (N, H))).to(dev)
+    bs = torch.tensor([0.004], dtype=torch.float32, device=dev)
+    xd, wd, rd = x.to(dev), w.to(dev), r.to(dev)
+    rout = torch.empty_like(rd)
+    q = torch.empty((M, H), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, H), dtype=dt, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ops.gemma_add_rms_norm_quant_gemm_fp8_out(xd, rd, rout, wd, 1e-6, s, bq, bs, q, y, out)
+    r2 = rd.clone()
+    q2 = torch.empty((M, H), dtype=torch.float8_e4m3fn, device=dev)
+    y2 = torch.empty((M, H), dtype=dt, device=dev)
+    ops.gemma_add_rms_norm_quant_out(xd, r2, wd, 1e-6, s, False, q2, None, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(rout.cpu().view(torch.int16), r2.cpu().view(torch.int16))
+    assert torch.equal(y.cpu().view(torch.int16), y2.cpu().view(torch.int16))
+    assert torch.equal(q.cpu(), q2.view(torch.uint8).cpu())
+    yb = P.bits16(y)
+    assert np.count_nonzero(yb == 0x8000) > 0 and np.count_nonzero(yb == 0x0000) > 0
