@@ -54,6 +54,9 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, u32x4 *__restri
   const unsigned nthr = blockDim.x;
   const unsigned nch = (unsigned)nchunk;
   const int nwaves = nthr / kWave;
+  // NVFP4 rows in line-group order on the looping launch of one chunk per
+  // thread (residual rows: 512 workgroups, half a 1024-row span per pass).
+  constexpr bool kLines = PF && CPT == 1;
   const float inv_h = __builtin_amdgcn_rcpf((float)(nchunk * kVec));
   // The row loads: x and residual stream from HBM (non-temporal).  They are
   // unconditional (a thread past the row's end re-reads its last chunk and
@@ -62,7 +65,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, u32x4 *__restri
   // flight.
   u32x4 xa[CPT], ra[CPT], wa[CPT];
   auto load_row = [&](int64_t b) {
-    const int64_t rw = MODE == kModeNvfp4 ? nvfp4_row_of_block(b, M) : b;
+    const int64_t rw = MODE == kModeNvfp4 ? nvfp4_row_of_block<kLines>(b, M) : b;
     const size_t rb = (size_t)rw * (size_t)nchunk;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -94,7 +97,7 @@ fused_rows(const u32x4 *__restrict__ x, u32x4 *__restrict__ res, u32x4 *__restri
   }
   int parity = 0;
   for (; blk < M; blk += gridDim.x, parity ^= 1) {
-    const int64_t row = MODE == kModeNvfp4 ? nvfp4_row_of_block(blk, M) : blk;
+    const int64_t row = MODE == kModeNvfp4 ? nvfp4_row_of_block<kLines>(blk, M) : blk;
     const size_t rbase = (size_t)row * (size_t)nchunk;
     u32x4 *__restrict__ rr = (RES_OUT ? res_out : res) + rbase;
     u32x4 *__restrict__ yr = y + rbase;
