@@ -4,16 +4,17 @@
 //
 // Design (memory-bound; no MFMA -- nothing here is a contraction):
 //  * fused_rows: one workgroup per row, grid = M (at 32768 x 8192 a grid of
-//    512 to 2048 looping workgroups took 426-461 us against 380).  The
-//    exception (PF): rows of 4096 < H < 6144 (5- or 6-wave workgroups) at
-//    2048 <= M <= 16384 run on 1024 workgroups that loop over rows and issue
-//    the next row's loads before the current row's reduction: 5-15% faster
-//    at M = 2048 ... 8192 (H = 5120), -1 ... +6% at 16384.  A thread owns
-//    8-element chunks (16 bytes) at chunk index tid, tid + nthr, ..., so
-//    every load and store instruction of a wave
-//    covers contiguous memory: 1 KB of x / residual / y, 512 B of FP8 codes,
-//    256 B of FP4 codes.  1, 2 or 4 chunks per thread (chunks_per_thread:
-//    one up to H = 4096 and at H = 6144, 8192; else two up to 16384, four up
+//    512 to 2048 looping workgroups took 426-461 us against ~370).  The
+//    exception (PF): rows of 4096 < H < 6144 at 2048 <= M <= 16384 run on
+//    1024 workgroups of two chunks per thread (512 of one chunk, for rows
+//    with a residual up to H = 5120) that loop over rows and issue the next
+//    row's loads before the current row's reduction: 5-15% faster at M =
+//    2048 ... 8192 (H = 5120), -1 ... +6% at 16384.  A thread owns 8-element
+//    chunks (16 bytes) at chunk index tid, tid + nthr, ..., so every load and
+//    store instruction of a wave covers contiguous memory: 1 KB of x /
+//    residual / y, 512 B of FP8 codes, 256 B of FP4 codes.  1, 2 or 4 chunks
+//    per thread (chunks_per_thread: one up to H = 4096, at H = 6144, 8192 and
+//    for rows with a residual up to H = 5120; else two up to 16384, four up
 //    to 32768).  x and residual are streamed with non-temporal loads, all
 //    outputs with non-temporal stores; weight and scale are plain (L2-cached)
 //    loads.  All loads of a row are issued before the first wait.  Sum of
@@ -23,7 +24,8 @@
 //    lanes; the block amax is combined with a DPP lane swap and the even lane
 //    stores the block's scale byte at its 128x4-tiled offset.  NVFP4 rows are
 //    assigned to workgroups so that each 128-row scale tile is written
-//    through a single XCD.
+//    through a single XCD (nvfp4_row_of_block; in line-group order on the
+//    one-chunk looping launch).
 //  * An MXFP8 block (32 elements) is the chunk quad of four adjacent lanes
 //    (DPP quad permutations combine the amax); the quad's first lane stores
 //    the E8M0 scale byte, row-major.
@@ -31,7 +33,8 @@
 //    lane groups with DPP, no LDS and no barrier.
 //  * fused_rows_scalar: shapes or pointers the vector path cannot take
 //    (H % 16 != 0, H > 32768, unaligned views); same arithmetic, one thread
-//    per element (FP8, none) or per scale block (NVFP4, MXFP8).
+//    per element (FP8, none) or per scale block (NVFP4, MXFP8); each value
+//    rounded to the activation dtype through round1 (no fused multiply-round).
 #pragma once
 
 #include "gnq_common.hpp"
