@@ -363,10 +363,10 @@ __device__ __forceinline__ size_t swz128x4(int64_t m, int b, int ktiles) {
 // Inside a tile the rows go in order, except with LINES: then the 32 rows of
 // each line group (rows 8 g .. 8 g + 7 and their partners 32, 64 and 96
 // rows on) come one after another, so a looping launch that covers half a
-// span per pass completes each scale line in one pass (2% faster for rows
-// with a residual at 4096 x 5120 on 512 workgroups; 2% slower on 1024, and
-// 8% slower with one workgroup per row, where rows in order read memory in
-// order).
+// span per pass completes each scale line in one pass (1.3-5% faster for
+// rows with a residual at M = 2048 ... 16384, H = 5120, on 512 workgroups;
+// 2% slower on 1024, and 8% slower with one workgroup per row, where rows
+// in order read memory in order).
 template <bool LINES = false>
 __device__ __forceinline__ int64_t nvfp4_row_of_block(int64_t b, int64_t M) {
   if ((((b >> 10) + 1) << 10) > M) return b;
