@@ -118,7 +118,7 @@ def all_rows(M):
 
 def oracle_threads():
     """Host threads for the oracle: the process's CPU affinity, at most 16
-    (the GPU machine's CPU share per GPU)."""
+    (the host cores a machine typically gives one GPU's process)."""
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     return max(1, min(16, n))
 
