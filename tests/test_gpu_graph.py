@@ -72,12 +72,17 @@ def test_graph_replays_match_eager(name):
 
 @pytest.mark.parametrize("fmt,M,H,N", [("nvfp4", 4, 1024, 320), ("nvfp4", 40, 1152, 200),
                                        ("nvfp4", 300, 1024, 384), ("nvfp4", 300, 1024, 4096),
-                                       ("nvfp4", 2100, 256, 4096), ("mxfp8", 300, 1024, 384)])
+                                       ("nvfp4", 2100, 256, 4096), ("mxfp8", 300, 1024, 384),
+                                       ("mxfp8", 2100, 512, 4096), ("mxfp8", 8, 2048, 4096),
+                                       ("fp8", 8, 2048, 4096), ("fp8", 40, 1088, 200),
+                                       ("fp8", 300, 1056, 384), ("fp8", 300, 1024, 384),
+                                       ("fp8", 2100, 512, 4096)])
 def test_graph_op_and_consumer_gemm_replays_match_eager(fmt, M, H, N):
     """The op and its consumer GEMM captured together (the NVFP4 dot-product,
-    32 x 32, 128 x 64 and 256 x 256 tile kernels, and the MXFP8 one): every replay, with
-    eager resets and synchronisations between, gives the eager result bit for
-    bit."""
+    32 x 32, 128 x 64 and 256 x 256 tile kernels; the MXFP8 and static-FP8
+    decode, 128 x 128 and 256 x 256 LDS-DMA kernels; the static-FP8 skinny
+    and register-staged kernels): every replay, with eager resets and
+    synchronisations between, gives the eager result bit for bit."""
     print(f"graph chain {fmt} M={M} H={H} N={N}", flush=True)
     dev = torch.device("cuda")
     g = torch.Generator().manual_seed(M + H + N)
@@ -86,17 +91,25 @@ def test_graph_op_and_consumer_gemm_replays_match_eager(fmt, M, H, N):
     w = (torch.randn(H, generator=g) * 0.1).to(torch.bfloat16).to(dev)
     W = torch.randn(N, H, generator=g).to(torch.bfloat16).to(dev)
     gs = torch.tensor([448.0 * 6.0 / 9.0], dtype=torch.float32, device=dev)
+    # static FP8: about 5 / 448 for the activation and the weight alike
+    sa = torch.tensor([0.0125], dtype=torch.float32, device=dev)
+    sb = torch.tensor([0.011], dtype=torch.float32, device=dev)
     if fmt == "nvfp4":
         wq, wbs = ops.quant_nvfp4(W, gs)
-    else:
+    elif fmt == "mxfp8":
         wq, wbs = ops.quant_mxfp8(W)
+    else:
+        wq = ops.quant_fp8_static(W, sb)
 
     def chain(r):
         if fmt == "nvfp4":
             q, bs, _ = ops.gemma_add_rms_norm_quant(x, r, w, 1e-6, gs, True)
             return ops.gemm_nvfp4(q, bs, gs, wq, wbs, gs)
-        q, s, _, _ = ops.gemma_add_rms_norm_mxfp8(x, r, w, 1e-6)
-        return ops.gemm_mxfp8(q, s, wq, wbs)
+        if fmt == "mxfp8":
+            q, s, _, _ = ops.gemma_add_rms_norm_mxfp8(x, r, w, 1e-6)
+            return ops.gemm_mxfp8(q, s, wq, wbs)
+        q, _, _ = ops.gemma_add_rms_norm_quant(x, r, w, 1e-6, sa, False)
+        return ops.gemm_fp8_static(q, sa, wq, sb)
 
     re = r0.clone()
     oute = chain(re)
@@ -116,6 +129,64 @@ def test_graph_op_and_consumer_gemm_replays_match_eager(fmt, M, H, N):
         torch.cuda.synchronize()
         assert torch.equal(outg, oute), rep
         assert torch.equal(rg, re), rep
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("M,H", [(130, 2080), (7, 4096)])
+def test_graph_unfused_chain_replays_match_eager(M, H, dtype):
+    """The unfused chain (add + Gemma norm with no quant, then each standalone
+    quant kernel) captured together: every replay, with eager resets and
+    synchronisations between, writes the eager result bit for bit, NVFP4's
+    untouched scale padding included."""
+    print(f"graph unfused M={M} H={H} {dtype}", flush=True)
+    dev = torch.device("cuda")
+    g = torch.Generator().manual_seed(M * 3 + H)
+    x = torch.randn(M, H, generator=g).to(dtype).to(dev)
+    r0 = torch.randn(M, H, generator=g).to(dtype).to(dev)
+    w = (torch.randn(H, generator=g) * 0.1).to(dtype).to(dev)
+    s8 = torch.tensor([0.0125], dtype=torch.float32, device=dev)
+    gs = torch.tensor([448.0 * 6.0 / 9.0], dtype=torch.float32, device=dev)
+
+    def outputs():
+        return {"q8": torch.empty((M, H), dtype=torch.uint8, device=dev),
+                "q4": torch.empty((M, H // 2), dtype=torch.uint8, device=dev),
+                "bs4": torch.empty((_lib.nq_block_scale_bytes(M, H),), dtype=torch.uint8, device=dev),
+                "qmx": torch.empty((M, H), dtype=torch.uint8, device=dev),
+                "smx": torch.empty((M, H // 32), dtype=torch.uint8, device=dev)}
+
+    def chain(r, o):
+        _, _, y = ops.add_rms_norm_quant(x, r, w, 1e-6, None, None)
+        ops.quant_fp8_static(y, s8, o["q8"].view(torch.float8_e4m3fn))
+        ops.quant_nvfp4(y, gs, o["q4"], o["bs4"].view(torch.float8_e4m3fn))
+        ops.quant_mxfp8(y, o["qmx"].view(torch.float8_e4m3fn), o["smx"].view(torch.float8_e8m0fnu))
+        return y
+
+    def reset(r, o):
+        r.copy_(r0)
+        for t in o.values():
+            t.fill_(0xA5)
+
+    re, oe = r0.clone(), outputs()
+    reset(re, oe)
+    ye = chain(re, oe)
+    torch.cuda.synchronize()
+
+    rg, og = r0.clone(), outputs()
+    st = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=st):
+        yg = chain(rg, og)
+    for rep in range(3):
+        reset(rg, og)
+        yg.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ye), rep
+        assert torch.equal(rg, re), rep
+        for k in oe:
+            assert torch.equal(og[k], oe[k]), (rep, k)
 
 
 @pytest.mark.parametrize("M", [2, 6])
